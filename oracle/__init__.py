@@ -1,0 +1,19 @@
+"""CPU oracle for the identity Hyper-Connections residual path.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the GPU library.
+"""
+from .oracle import (  # noqa: F401
+    block_tanh,
+    build,
+    get_threads,
+    load,
+    post_mix,
+    pre_mix,
+    round_bf16,
+    round_f32,
+    set_threads,
+    sinkhorn,
+    weights,
+    widen,
+)

@@ -1,0 +1,31 @@
+"""The byte model used for the roofline reproduces the pages' worked example
+(tests/golden/state_bytes.txt)."""
+import os
+
+from hyper_connections_amd import traffic
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "state_bytes.txt")
+
+
+def rows():
+    for line in open(GOLDEN):
+        line = line.split("#")[0].strip()
+        if line:
+            yield tuple(int(v) for v in line.split())
+
+
+def test_state_bytes_worked_example():
+    got = list(rows())
+    assert len(got) == 3
+    for n, d, s, tokens, expect in got:
+        assert traffic.state_bytes(n, d, s, tokens) == expect
+    # "a 4x increase, and 48 KB more per token per boundary"
+    one, four = traffic.state_bytes(1, 8192, 2), traffic.state_bytes(4, 8192, 2)
+    assert four == 4 * one and four - one == 48 * 1024
+
+
+def test_layer_bytes_are_14_state_units_at_n4():
+    """pre reads the state and writes one stream; post reads state and F and
+    writes the state: (n+1) + (2n+1) = 3n+2 hidden-width vectors per token."""
+    n, d, s = 4, 4096, 2
+    assert traffic.pre_bytes(n, d, s) + traffic.post_bytes(n, d, s) == 14 * d * s == 114688
