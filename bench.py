@@ -1,0 +1,341 @@
+#!/usr/bin/env python3
+"""Benchmark of the Hyper-Connections residual path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the path over one batch of synthetic tokens whose
+inputs are already resident in HBM:
+  static-bf16   pre (read-mix + RMSNorm) then post (stream-mix + write-back)
+                with shared static weights; F is a given tensor (default)
+  dynamic-bf16  per-token weights (MFMA projection + tanh), then pre, post
+  mhc-bf16      Sinkhorn records from per-token logits, then pre, post
+  chain-bf16    78 layers of pre, tanh block, post (reported, not graded)
+  tiny-f32      one small fp32 layer
+
+Timing: W untimed steps, then K timed steps between device synchronisations,
+with HIP events recorded on the launch stream around every kernel.  Each step
+uses the next of several buffer sets whose total size is at least twice the
+256 MB Infinity Cache, so that re-reads cannot come from it.  Prints one JSON
+line; details go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s + achieved HBM GB/s (% roofline), fused HC pre+post, n=4 d=4096 bf16"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MALL_BYTES = 256 * 2 ** 20      # Infinity Cache
+PROFILES = os.path.join(ROOT, "profiles")
+
+KERNEL_SOURCES = {
+    "pre_mix": "hc_rows.hip", "post_mix": "hc_rows.hip", "post_pre_mix": "hc_rows.hip",
+    "block_tanh": "hc_rows.hip", "weights": "hc_weights.hip", "sinkhorn": "hc_weights.hip",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(kernel: str) -> str:
+    """Hash of the sources a kernel is built from (its file + the shared
+    device header), used to invalidate stale counter summaries."""
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "hc_device.h"):
+        with open(os.path.join(ROOT, "hyper_connections_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha") != source_sha(kernel):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+class Timer:
+    """Events around every launch on the current stream; per-kernel averages."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, name, fn):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        r = fn()
+        b.record()
+        self.pairs.setdefault(name, []).append((a, b))
+        return r
+
+    def avg_ms(self):
+        return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in self.pairs.items()}
+
+    def clear(self):
+        self.pairs = {}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="static-bf16")
+    ap.add_argument("--sets", type=int, default=0, help="buffer sets (0 = enough to defeat the cache)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle CPU-baseline budget")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--fused", action="store_true",
+                    help="chain: fuse each write-back with the next read-mix")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this path runs on one GPU "
+              "(tokens shard across GPUs with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from hyper_connections_amd import hc, traffic, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    hc.lib()   # raises if the library is not built
+
+    wl = workloads.workload(args.workload)
+    n, d, T, s = wl.n, wl.d, wl.T, wl.elem_bytes
+    K = wl.K
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a.astype(np.float32)).cuda()
+
+    t0 = time.time()
+    inp = workloads.make_inputs(wl)
+    log(f"[bench] inputs for {wl.name} generated in {time.time() - t0:.1f}s")
+    gamma = dev(inp["gamma"])
+
+    # ---------------------------------------------------------------- sets
+    per_tok = wl.kind in ("dynamic", "mhc")
+    set_bytes = T * d * s * (2 * n + 2)   # H, F, u, H_out
+    sets = args.sets or max(3, math.ceil(2 * MALL_BYTES / set_bytes))
+    if wl.kind == "chain":
+        sets = 1
+    log(f"[bench] {sets} buffer set(s) of {set_bytes / 2 ** 20:.0f} MiB")
+    H0 = dev(inp["H"])
+    bufs = []
+    for i in range(sets):
+        b = {"H": H0 if i == 0 else H0.clone(),
+             "u": torch.empty((T, d), dtype=H0.dtype, device="cuda"),
+             "O": torch.empty_like(H0)}
+        if "F" in inp:
+            b["F"] = dev(inp["F"]) if i == 0 else bufs[0]["F"].clone()
+        else:
+            b["F"] = torch.empty((T, d), dtype=H0.dtype, device="cuda")
+        if wl.kind == "mhc":
+            b["logits"] = dev(inp["logits"]) if i == 0 else bufs[0]["logits"].clone()
+        if per_tok:
+            b["w"] = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        bufs.append(b)
+    if wl.kind == "static" or wl.kind == "chain":
+        w_static = dev(inp["w"]) if "w" in inp else None
+    if wl.kind == "dynamic":
+        Wp, ws = dev(inp["W"]), dev(inp["w_static"])
+    if wl.kind == "chain":
+        recs = [dev(workloads.layer_record(wl, l)) for l in range(wl.layers + 1)]
+
+    # algorithmic bytes per launch
+    launch_bytes = {
+        "pre_mix": traffic.pre_bytes(n, d, s, per_tok) * T,
+        "post_mix": traffic.post_bytes(n, d, s, per_tok) * T,
+        "post_pre_mix": traffic.post_pre_bytes(n, d, s) * T,
+        "weights": traffic.weights_bytes(n, d, s) * T,
+        "sinkhorn": traffic.sinkhorn_bytes(n) * T,
+        "block_tanh": 2 * d * s * T,
+    }
+
+    def step(tm: Timer, i: int):
+        b = bufs[i % sets]
+        if wl.kind == "static":
+            tm.run("pre_mix", lambda: hc.pre_mix(b["H"], w_static, gamma, wl.eps, out=b["u"]))
+            tm.run("post_mix", lambda: hc.post_mix(b["H"], b["F"], w_static, out=b["O"]))
+        elif wl.kind == "dynamic":
+            tm.run("weights", lambda: hc.weights(b["H"], Wp, ws, wl.scale, wl.eps, 0, out=b["w"]))
+            tm.run("pre_mix", lambda: hc.pre_mix(b["H"], b["w"], gamma, wl.eps, out=b["u"]))
+            tm.run("post_mix", lambda: hc.post_mix(b["H"], b["F"], b["w"], out=b["O"]))
+        elif wl.kind == "mhc":
+            tm.run("sinkhorn", lambda: hc.sinkhorn(b["logits"], n, wl.iters, out=b["w"]))
+            tm.run("pre_mix", lambda: hc.pre_mix(b["H"], b["w"], gamma, wl.eps, out=b["u"]))
+            tm.run("post_mix", lambda: hc.post_mix(b["H"], b["F"], b["w"], out=b["O"]))
+        else:   # chain: H ping-pongs between b["H"] and b["O"]
+            Ha, Hb = b["H"], b["O"]
+            if args.fused:
+                tm.run("pre_mix", lambda: hc.pre_mix(Ha, recs[0], gamma, wl.eps, out=b["u"]))
+                for l in range(wl.layers):
+                    tm.run("block_tanh", lambda: hc.block_tanh(b["u"], out=b["F"]))
+                    tm.run("post_pre_mix", lambda: hc.post_pre_mix(
+                        Ha, b["F"], recs[l], recs[l + 1], gamma, wl.eps, out=Hb, u_out=b["u"]))
+                    Ha, Hb = Hb, Ha
+            else:
+                for l in range(wl.layers):
+                    tm.run("pre_mix", lambda: hc.pre_mix(Ha, recs[l], gamma, wl.eps, out=b["u"]))
+                    tm.run("block_tanh", lambda: hc.block_tanh(b["u"], out=b["F"]))
+                    tm.run("post_mix", lambda: hc.post_mix(Ha, b["F"], recs[l], out=Hb))
+                    Ha, Hb = Hb, Ha
+
+    # -------------------------------------------------------- copy probe
+    cp_n = 512 * 2 ** 20
+    src = torch.empty(cp_n // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * cp_n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    log(f"[bench] device copy (512 MiB read + 512 MiB write): {copy_gbps:.0f} GB/s")
+
+    # ------------------------------------------------------------- timing
+    tm = Timer(torch)
+    for i in range(args.warmup):
+        step(tm, i)
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warmup steps done")
+    tm.clear()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(tm, args.warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    kms = tm.avg_ms()
+    log(f"[bench] {args.steps} timed steps: {ms_step * 1e3:.1f} us/step")
+
+    hc_kernels = [k for k in kms if k != "block_tanh"]
+    launches = {k: len(v) // args.steps for k, v in tm.pairs.items()}
+    step_bytes = sum(launch_bytes[k] * launches[k] for k in hc_kernels)
+    kernels = {}
+    for k, ms in kms.items():
+        gbps = launch_bytes[k] / (ms * 1e-3) / 1e9
+        kernels[k] = {"us": round(ms * 1e3, 2), "launches_per_step": launches[k],
+                      "algorithmic_bytes": launch_bytes[k], "gbps": round(gbps, 1),
+                      "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+        log(f"[bench]   {k:13s} {ms * 1e3:9.2f} us  {gbps:8.0f} GB/s  "
+            f"{100 * gbps / HBM_PEAK_GBPS:5.1f}% of 8 TB/s")
+    # dominant kernel = largest share of step time
+    dom = max(kms, key=lambda k: kms[k] * launches[k])
+    dom_gbps = launch_bytes[dom] / (kms[dom] * 1e-3) / 1e9
+    traffic_b = counter_traffic(dom, wl.name)
+
+    tokens_per_s = T / (ms_step * 1e-3)
+    step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, identity-init weights + noise)",
+        "config": {"workload": wl.name, "T": T, "n": n, "d": d, "weights": wl.kind,
+                   "layers": wl.layers, "buffer_sets": sets, "fused": bool(args.fused)},
+        "hbm_gbps": round(step_gbps, 1),
+        "frac_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "copy_gbps": round(copy_gbps, 1),
+        "kernels": kernels,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_b},
+        "cpu_baseline": None,
+    }
+
+    # ------------------------------------------------ oracle CPU baseline
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, inp, budget_s: float):
+    """The oracle, as it stands, on the host cores: whole passes over the
+    workload's tokens (chunks of 1024) until the time budget is used."""
+    import numpy as np
+
+    import oracle
+    from hyper_connections_amd import workloads
+
+    threads = oracle.get_threads()
+    chunk = 1024
+    done, t0 = 0, time.perf_counter()
+    layers = 0
+    while True:
+        for c0 in range(0, wl.T, chunk):
+            sl = slice(c0, min(wl.T, c0 + chunk))
+            H = inp["H"][sl]
+            if wl.kind == "static":
+                w = inp["w"].astype(np.float64)
+                oracle.pre_mix(H, w, inp["gamma"], wl.eps)
+                oracle.post_mix(H, inp["F"][sl], w)
+            elif wl.kind == "dynamic":
+                w = oracle.weights(H, inp["W"], inp["w_static"].astype(np.float64), wl.scale, wl.eps, 0)
+                oracle.pre_mix(H, w, inp["gamma"], wl.eps)
+                oracle.post_mix(H, inp["F"][sl], w)
+            elif wl.kind == "mhc":
+                w = oracle.sinkhorn(inp["logits"][sl].astype(np.float64), wl.n, wl.iters)
+                oracle.pre_mix(H, w, inp["gamma"], wl.eps)
+                oracle.post_mix(H, inp["F"][sl], w)
+            else:
+                w = workloads.layer_record(wl, layers % wl.layers).astype(np.float64)
+                u = oracle.pre_mix(H, w, inp["gamma"], wl.eps)
+                oracle.post_mix(H, oracle.round_bf16(np.tanh(u)), w)
+            done += sl.stop - sl.start
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        layers += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    rate = done / el
+    if wl.kind == "chain":
+        rate /= wl.layers   # one token through all layers
+    log(f"[bench] oracle CPU baseline: {done} token passes in {el:.1f}s on {threads} threads")
+    return {"value": round(rate, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} token passes of {wl.name} ({wl.T} tokens per full pass, chunks of "
+                      f"1024), fp64 oracle, {el:.1f}s wall"}
+
+
+if __name__ == "__main__":
+    main()

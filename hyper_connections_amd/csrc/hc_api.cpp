@@ -1,0 +1,195 @@
+// hc_api.cpp -- the extern "C" boundary of libhc.so (declared in include/hc.h).
+//
+// Every entry point validates all arguments before it launches anything, so
+// a failed check leaves the stream untouched.  Validation uses only pointer
+// values and sizes (no HIP calls), which also lets it run on hosts without a
+// GPU.  No exception crosses the boundary and nothing is printed.
+#include "hc.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "hc_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxBytes = int64_t(1) << 52;   // any single buffer (4 PiB)
+
+struct Span {
+    const void* p;
+    int64_t bytes;
+};
+
+bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+bool overlap(Span a, Span b) {
+    if (a.bytes <= 0 || b.bytes <= 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a.p), y = reinterpret_cast<uintptr_t>(b.p);
+    return x < y + static_cast<uintptr_t>(b.bytes) && y < x + static_cast<uintptr_t>(a.bytes);
+}
+
+int elem_bytes(hc_dtype dt) { return dt == HC_F32 ? 4 : 2; }
+int vec_elems(hc_dtype dt) { return dt == HC_F32 ? 4 : 8; }
+
+bool dtype_ok(hc_dtype dt) { return dt == HC_F32 || dt == HC_BF16; }
+
+int record_len(int n) { return 2 * n + n * n; }
+
+// Bytes of T records read through a stride (0 = one shared record).
+int64_t record_span(int64_t T, int64_t stride, int K) {
+    return (stride == 0 ? int64_t(K) : (T - 1) * stride + K) * 4;
+}
+
+// Shape checks shared by the row kernels.  Order of checks: dtype, n, d, T.
+hc_status check_nd(int32_t n, int32_t d, int64_t T, hc_dtype dt) {
+    if (!dtype_ok(dt)) return HC_ERR_DTYPE;
+    if (n < 1 || n > HC_MAX_STREAMS) return HC_ERR_SHAPE;
+    if (d < 1 || d > HC_MAX_HIDDEN || d % vec_elems(dt) != 0) return HC_ERR_SHAPE;
+    if (T < 0) return HC_ERR_ARG;
+    if (T > kMaxBytes / (int64_t(n) * d * elem_bytes(dt))) return HC_ERR_ARG;
+    return HC_OK;
+}
+
+hc_status check_stride(int64_t stride, int K, int64_t T) {
+    if (stride != 0 && stride < K) return HC_ERR_SHAPE;
+    if (stride > 0 && T > kMaxBytes / 4 / stride) return HC_ERR_ARG;
+    return HC_OK;
+}
+
+bool eps_ok(float eps) { return std::isfinite(eps) && eps > 0.0f; }
+
+hc_status from_hip(hipError_t e) { return e == hipSuccess ? HC_OK : HC_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* hc_status_str(hc_status s) {
+    switch (s) {
+        case HC_OK: return "HC_OK: success";
+        case HC_ERR_NULL: return "HC_ERR_NULL: a required pointer is NULL";
+        case HC_ERR_SHAPE: return "HC_ERR_SHAPE: n, d or a stride is outside the supported set";
+        case HC_ERR_DTYPE: return "HC_ERR_DTYPE: unknown storage dtype";
+        case HC_ERR_ALIGN: return "HC_ERR_ALIGN: a pointer is not aligned as required";
+        case HC_ERR_ALIAS: return "HC_ERR_ALIAS: an output overlaps an input or another output";
+        case HC_ERR_ARG: return "HC_ERR_ARG: T, eps or iters out of range";
+        case HC_ERR_HIP: return "HC_ERR_HIP: the HIP runtime reported a launch error";
+    }
+    return "HC_ERR_UNKNOWN: unknown status code";
+}
+
+int32_t hc_abi_version(void) { return 1; }
+
+hc_status hc_pre_mix(const void* H, const float* w, int64_t w_stride, const float* gamma, float eps,
+                     void* u, int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream) {
+    if (!H || !w || !gamma || !u) return HC_ERR_NULL;
+    hc_status st = check_nd(n, d, T, dt);
+    if (st != HC_OK) return st;
+    const int K = record_len(n);
+    if ((st = check_stride(w_stride, K, T)) != HC_OK) return st;
+    if (!eps_ok(eps)) return HC_ERR_ARG;
+    if (misaligned(H, 16) || misaligned(u, 16) || misaligned(gamma, 16) || misaligned(w, 4))
+        return HC_ERR_ALIGN;
+    if (T == 0) return HC_OK;
+    const int64_t s = elem_bytes(dt);
+    const Span sH{H, T * n * d * s}, sU{u, T * d * s}, sW{w, record_span(T, w_stride, K)},
+        sG{gamma, int64_t(d) * 4};
+    if (overlap(sU, sH) || overlap(sU, sW) || overlap(sU, sG)) return HC_ERR_ALIAS;
+    return from_hip(hc::launch_pre_mix(H, w, w_stride, gamma, eps, u, T, n, d, dt,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+hc_status hc_post_mix(const void* H, const void* F, const float* w, int64_t w_stride, void* H_out,
+                      int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream) {
+    if (!H || !F || !w || !H_out) return HC_ERR_NULL;
+    hc_status st = check_nd(n, d, T, dt);
+    if (st != HC_OK) return st;
+    const int K = record_len(n);
+    if ((st = check_stride(w_stride, K, T)) != HC_OK) return st;
+    if (misaligned(H, 16) || misaligned(F, 16) || misaligned(H_out, 16) || misaligned(w, 4))
+        return HC_ERR_ALIGN;
+    if (T == 0) return HC_OK;
+    const int64_t s = elem_bytes(dt);
+    const Span sH{H, T * n * d * s}, sF{F, T * d * s}, sO{H_out, T * n * d * s},
+        sW{w, record_span(T, w_stride, K)};
+    if ((H_out != H && overlap(sO, sH)) || overlap(sO, sF) || overlap(sO, sW)) return HC_ERR_ALIAS;
+    return from_hip(hc::launch_post_mix(H, F, w, w_stride, H_out, T, n, d, dt,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+hc_status hc_post_pre_mix(const void* H, const void* F, const float* w, int64_t w_stride,
+                          const float* w_next, int64_t w_next_stride, const float* gamma_next,
+                          float eps, void* H_out, void* u_next, int64_t T, int32_t n, int32_t d,
+                          hc_dtype dt, void* stream) {
+    if (!H || !F || !w || !w_next || !gamma_next || !H_out || !u_next) return HC_ERR_NULL;
+    hc_status st = check_nd(n, d, T, dt);
+    if (st != HC_OK) return st;
+    const int K = record_len(n);
+    if ((st = check_stride(w_stride, K, T)) != HC_OK) return st;
+    if ((st = check_stride(w_next_stride, K, T)) != HC_OK) return st;
+    if (!eps_ok(eps)) return HC_ERR_ARG;
+    if (misaligned(H, 16) || misaligned(F, 16) || misaligned(H_out, 16) || misaligned(u_next, 16) ||
+        misaligned(gamma_next, 16) || misaligned(w, 4) || misaligned(w_next, 4))
+        return HC_ERR_ALIGN;
+    if (T == 0) return HC_OK;
+    const int64_t s = elem_bytes(dt);
+    const Span sH{H, T * n * d * s}, sF{F, T * d * s}, sO{H_out, T * n * d * s},
+        sU{u_next, T * d * s}, sW{w, record_span(T, w_stride, K)},
+        sW2{w_next, record_span(T, w_next_stride, K)}, sG{gamma_next, int64_t(d) * 4};
+    if ((H_out != H && overlap(sO, sH)) || overlap(sO, sF) || overlap(sO, sW) || overlap(sO, sW2) ||
+        overlap(sO, sG) || overlap(sU, sH) || overlap(sU, sF) || overlap(sU, sW) ||
+        overlap(sU, sW2) || overlap(sU, sG) || overlap(sU, sO))
+        return HC_ERR_ALIAS;
+    return from_hip(hc::launch_post_pre_mix(H, F, w, w_stride, w_next, w_next_stride, gamma_next,
+                                            eps, H_out, u_next, T, n, d, dt,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+hc_status hc_weights(const void* H, const void* W, const float* w_static, float scale, float eps,
+                     int32_t sinkhorn_iters, float* w_out, int64_t T, int32_t n, int32_t d,
+                     hc_dtype dt, void* stream) {
+    if (!H || !W || !w_static || !w_out) return HC_ERR_NULL;
+    hc_status st = check_nd(n, d, T, dt);
+    if (st != HC_OK) return st;
+    if (!eps_ok(eps) || !std::isfinite(scale)) return HC_ERR_ARG;
+    if (sinkhorn_iters < 0 || sinkhorn_iters > HC_MAX_SINKHORN_ITERS) return HC_ERR_ARG;
+    if (misaligned(H, 16) || misaligned(W, 16) || misaligned(w_static, 4) || misaligned(w_out, 4))
+        return HC_ERR_ALIGN;
+    if (T == 0) return HC_OK;
+    const int K = record_len(n);
+    const int64_t s = elem_bytes(dt);
+    const Span sH{H, T * n * d * s}, sW{W, int64_t(K) * d * s}, sS{w_static, int64_t(K) * 4},
+        sO{w_out, T * K * 4};
+    if (overlap(sO, sH) || overlap(sO, sW) || overlap(sO, sS)) return HC_ERR_ALIAS;
+    return from_hip(hc::launch_weights(H, W, w_static, scale, eps, sinkhorn_iters, w_out, T, n, d,
+                                       dt, static_cast<hipStream_t>(stream)));
+}
+
+hc_status hc_sinkhorn(const float* logits, float* w_out, int32_t iters, int64_t T, int32_t n,
+                      void* stream) {
+    if (!logits || !w_out) return HC_ERR_NULL;
+    if (n < 1 || n > HC_MAX_STREAMS) return HC_ERR_SHAPE;
+    if (T < 0 || iters < 0 || iters > HC_MAX_SINKHORN_ITERS) return HC_ERR_ARG;
+    const int K = record_len(n);
+    if (T > kMaxBytes / (4 * K)) return HC_ERR_ARG;
+    if (misaligned(logits, 4) || misaligned(w_out, 4)) return HC_ERR_ALIGN;
+    if (T == 0) return HC_OK;
+    if (overlap(Span{logits, T * K * 4}, Span{w_out, T * K * 4})) return HC_ERR_ALIAS;
+    return from_hip(hc::launch_sinkhorn(logits, w_out, iters, T, n, static_cast<hipStream_t>(stream)));
+}
+
+hc_status hc_block_tanh(const void* u, void* F, int64_t count, hc_dtype dt, void* stream) {
+    if (!u || !F) return HC_ERR_NULL;
+    if (!dtype_ok(dt)) return HC_ERR_DTYPE;
+    if (count < 0 || count > kMaxBytes / 4) return HC_ERR_ARG;
+    if (count % vec_elems(dt) != 0) return HC_ERR_SHAPE;
+    if (misaligned(u, 16) || misaligned(F, 16)) return HC_ERR_ALIGN;
+    if (count == 0) return HC_OK;
+    const int64_t bytes = count * elem_bytes(dt);
+    if (overlap(Span{u, bytes}, Span{F, bytes})) return HC_ERR_ALIAS;
+    return from_hip(hc::launch_block_tanh(u, F, count, dt, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// hc_launch.h -- internal (C++) launchers behind the C ABI.  The ABI layer
+// validates every argument before calling these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+namespace hc {
+
+// Launch `kernel` with arguments converted to its exact parameter types and
+// return the runtime's verdict on the launch itself.
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                  hipStream_t stream, Args&&... args) {
+    std::tuple<KArgs...> params(std::forward<Args>(args)...);
+    void* argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+    std::apply([&](auto&... p) {
+        int i = 0;
+        ((argv[i++] = static_cast<void*>(&p)), ...);
+    }, params);
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, shmem, stream);
+}
+
+// Row kernels (one workgroup per token row): block size and 16-byte vectors
+// per thread for a row of `nvec` vectors.  Shared by pre, post and the fused
+// post+pre so that their reductions over d run in the same order.
+struct RowCfg { int block; int vpt; };
+inline RowCfg row_config(int nvec) {
+    if (nvec <= 64) return {64, 1};
+    if (nvec <= 1024) return {256, (nvec + 255) / 256};
+    return {1024, (nvec + 1023) / 1024};
+}
+
+hipError_t launch_pre_mix(const void* H, const float* w, int64_t w_stride, const float* gamma,
+                          float eps, void* u, int64_t T, int n, int d, int dt, hipStream_t s);
+hipError_t launch_post_mix(const void* H, const void* F, const float* w, int64_t w_stride,
+                           void* H_out, int64_t T, int n, int d, int dt, hipStream_t s);
+hipError_t launch_post_pre_mix(const void* H, const void* F, const float* w, int64_t w_stride,
+                               const float* w_next, int64_t w_next_stride, const float* gamma,
+                               float eps, void* H_out, void* u_next, int64_t T, int n, int d,
+                               int dt, hipStream_t s);
+hipError_t launch_block_tanh(const void* u, void* F, int64_t count, int dt, hipStream_t s);
+hipError_t launch_weights(const void* H, const void* W, const float* w_static, float scale,
+                          float eps, int iters, float* w_out, int64_t T, int n, int d, int dt,
+                          hipStream_t s);
+hipError_t launch_sinkhorn(const float* logits, float* w_out, int iters, int64_t T, int n,
+                           hipStream_t s);
+
+}  // namespace hc

@@ -1,0 +1,305 @@
+// hc_weights.hip -- per-token mixing weights: the projection of the
+// normalised streams on the matrix cores, tanh, and the Sinkhorn (mHC) step.
+//
+// Sources: hfviewer.com glossary "Hyper-connections (mHC)", definition (the
+// mHC variant makes the stream mixing doubly stochastic with a few Sinkhorn
+// iterations); llm-atlas "Tencent Hy4-preview (770B-A49B)", "Architecture
+// concepts" (constrained mixing between parallel streams).  The pages give no
+// rule for computing weights per token; the reading implemented is
+//   r_i = 1/sqrt(mean_k H_ik^2 + eps), hbar = (1/n) sum_i r_i H_i,
+//   z = W hbar (W is K x d, K = 2n + n^2),
+//   w = w_static + scale * tanh(z)            (sinkhorn_iters == 0)
+//   w = mhc(w_static + scale * z)             (sinkhorn_iters  > 0)
+// where mhc(l) = [sigmoid(l_alpha) | sigmoid(l_beta) | Sinkhorn(exp(l_A))].
+//
+// Projection as a GEMM.  Because z is linear in the streams,
+//   z_c = (1/n) sum_i r_i P_ic,   P_ic = sum_k H_ik W_ck,
+// so the kernel multiplies the raw stream rows (H viewed as a (T*n) x d
+// matrix) by W^T on MFMA while the same registers feed the per-row sums of
+// squares; r_i is applied in the epilogue.  One HBM pass over H.
+//
+// Tiling (one wave = 16 matrix rows = 16/n tokens; 4 waves per workgroup):
+//  - A operand: the wave's 16 rows.  Lane l supplies row l % 16; its lane
+//    group g = l / 16 supplies the k-slice the MFMA assigns to that group.
+//    The physical k of every slice is our choice as long as the B operand
+//    uses the same one: at step s group g takes vector 4s + g of the chunk,
+//    so the four lanes of a row read 64 contiguous bytes per instruction.
+//  - B operand: W staged through LDS one k-chunk at a time (shared by the
+//    four waves; rows >= K and k >= d are zero), 16 bytes of row padding.
+//  - C: one 16x16 tile per 16 outputs (two tiles for K = 24).
+//  - Epilogue through LDS: the C tile and the row sums of squares are
+//    combined per token, then tanh or the mHC transform, then stored.
+#include "hc_device.h"
+#include "hc_launch.h"
+
+namespace hc {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kLV = 8;         // 16-byte vectors per lane per k-chunk
+constexpr int64_t kMaxGrid = 1 << 20;
+
+// ------------------------------------------------------------ mHC record
+
+// Logit record l (K = 2N + N^2) -> weight record out.  With iters >= 1 the
+// largest logit of A is subtracted before exp; the first row division
+// removes any common factor, so the result is unchanged in exact arithmetic.
+template <int N>
+__device__ __forceinline__ void mhc_record(const float* l, float* out, int iters) {
+#pragma unroll
+    for (int i = 0; i < 2 * N; ++i) out[i] = 1.0f / (1.0f + expf(-l[i]));
+    float M[N * N];
+    float m = 0.0f;
+    if (iters > 0) {
+        m = l[2 * N];
+#pragma unroll
+        for (int e = 1; e < N * N; ++e) m = fmaxf(m, l[2 * N + e]);
+    }
+#pragma unroll
+    for (int e = 0; e < N * N; ++e) M[e] = expf(l[2 * N + e] - m);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            float s = M[i * N];
+#pragma unroll
+            for (int j = 1; j < N; ++j) s += M[i * N + j];
+#pragma unroll
+            for (int j = 0; j < N; ++j) M[i * N + j] = M[i * N + j] / s;
+        }
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            float s = M[j];
+#pragma unroll
+            for (int i = 1; i < N; ++i) s += M[i * N + j];
+#pragma unroll
+            for (int i = 0; i < N; ++i) M[i * N + j] = M[i * N + j] / s;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < N * N; ++e) out[2 * N + e] = M[e];
+}
+
+// --------------------------------------------------------------- sinkhorn
+
+// One thread per token; records staged through LDS so that global traffic is
+// coalesced (records are K floats, K = 3, 8, 15 or 24, not 16-byte multiples).
+template <int N>
+__global__ __launch_bounds__(256) void sinkhorn_kernel(const float* __restrict__ logits,
+                                                       float* __restrict__ w_out, int iters,
+                                                       int64_t T) {
+    constexpr int K = 2 * N + N * N;
+    constexpr int KP = K + 1;   // odd pitch: lanes hit distinct banks
+    __shared__ float rec[256 * KP];
+    for (int64_t t0 = (int64_t)blockIdx.x * 256; t0 < T; t0 += (int64_t)gridDim.x * 256) {
+        const int ntok = (int)((T - t0) < 256 ? (T - t0) : 256);
+        const float* src = logits + t0 * K;
+        for (int e = threadIdx.x; e < ntok * K; e += 256) rec[(e / K) * KP + e % K] = src[e];
+        __syncthreads();
+        if ((int)threadIdx.x < ntok) {
+            float l[K], o[K];
+#pragma unroll
+            for (int c = 0; c < K; ++c) l[c] = rec[threadIdx.x * KP + c];
+            mhc_record<N>(l, o, iters);
+#pragma unroll
+            for (int c = 0; c < K; ++c) rec[threadIdx.x * KP + c] = o[c];
+        }
+        __syncthreads();
+        float* dst = w_out + t0 * K;
+        for (int e = threadIdx.x; e < ntok * K; e += 256) dst[e] = rec[(e / K) * KP + e % K];
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- weights
+
+template <typename S> struct Mfma;
+template <> struct Mfma<bf16_t> {
+    // one 16-byte vector (8 bf16) is one K = 32 step across the 4 lane groups
+    static __device__ __forceinline__ f32x4 step(uint4 a, uint4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+template <> struct Mfma<f32_t> {
+    // one 16-byte vector (4 fp32) is four K = 4 steps
+    static __device__ __forceinline__ f32x4 step(uint4 a, uint4 b, f32x4 c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+        return c;
+    }
+};
+
+template <int N, typename S>
+struct WeightsGeom {
+    static constexpr int K = 2 * N + N * N;           // outputs per token
+    static constexpr int NT = (K + 15) / 16;          // 16-wide C tiles
+    static constexpr int TPW = 16 / N;                // tokens per wave
+    static constexpr int V = Store<S>::kElems;        // elements per vector
+    static constexpr int KC = 4 * kLV * V;            // k per chunk
+    static constexpr int RS = KC * Store<S>::kBytes + 16;  // LDS row pitch (bytes)
+    static constexpr int WBYTES = NT * 16 * RS;       // one W chunk in LDS
+    static constexpr int PIECES = KC * Store<S>::kBytes / 16;  // 16-byte pieces per W row
+    static constexpr int CPITCH = NT * 16 + 1;        // epilogue C row pitch (floats)
+    static constexpr int EPI = 16 * CPITCH + 16 + TPW * K;  // floats per wave
+};
+
+template <int N, typename S>
+__global__ __launch_bounds__(256) void weights_kernel(
+    const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, const float* __restrict__ w_static,
+    float scale, float eps, int iters, float* __restrict__ w_out, int64_t T, int d) {
+    using G = WeightsGeom<N, S>;
+    constexpr int V = G::V, KC = G::KC, NT = G::NT, K = G::K, TPW = G::TPW;
+    constexpr int SB = Store<S>::kBytes;
+    __shared__ __attribute__((aligned(16))) uint8_t wlds[G::WBYTES];
+    __shared__ float epi[kWaves * G::EPI];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rho = lane & 15, grp = lane >> 4;
+    const int64_t row_bytes = (int64_t)d * SB;
+    const int nchunks = (d + KC - 1) / KC;
+    const int tok_per_block = kWaves * TPW;
+
+    // zero the padding rows (>= K) of the W tile once; chunks never write them
+    for (int p = threadIdx.x; p < (NT * 16 - K) * G::PIECES; p += 256) {
+        const int r = K + p / G::PIECES, c = p % G::PIECES;
+        *reinterpret_cast<uint4*>(wlds + r * G::RS + c * 16) = make_uint4(0, 0, 0, 0);
+    }
+
+    for (int64_t b = blockIdx.x; b * tok_per_block < T; b += gridDim.x) {
+        const int64_t tok0 = b * tok_per_block + wave * TPW;    // first token of this wave
+        const int tok_local = rho / N;
+        const bool row_ok = rho < TPW * N && tok0 + tok_local < T;
+        const uint8_t* arow = H + (tok0 * N + rho) * row_bytes;
+
+        f32x4 acc[NT];
+#pragma unroll
+        for (int q = 0; q < NT; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float ss = 0.0f;
+
+        for (int c = 0; c < nchunks; ++c) {
+            const int k0 = c * KC;
+            // this lane's stream vectors for the chunk (zero past d or past T)
+            uint4 a[kLV];
+#pragma unroll
+            for (int s = 0; s < kLV; ++s) {
+                const int k = k0 + (4 * s + grp) * V;
+                a[s] = (row_ok && k < d) ? ld16_stream(arow + (int64_t)k * SB) : make_uint4(0, 0, 0, 0);
+            }
+            // W chunk -> LDS (rows < K; zero past d)
+            __syncthreads();   // previous chunk's readers are done
+            for (int p = threadIdx.x; p < K * G::PIECES; p += 256) {
+                const int r = p / G::PIECES, pc = p % G::PIECES;
+                const int k = k0 + pc * (16 / SB);
+                uint4 v = k < d ? ld16(W + ((int64_t)r * d + k) * SB) : make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4*>(wlds + r * G::RS + pc * 16) = v;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < kLV; ++s) {
+                float f[V];
+                unpack<S>(a[s], f);
+#pragma unroll
+                for (int e = 0; e < V; ++e) ss = fmaf(f[e], f[e], ss);
+                const int kb = (4 * s + grp) * 16;   // byte offset of this slice in the chunk
+#pragma unroll
+                for (int q = 0; q < NT; ++q) {
+                    const uint4 bv = *reinterpret_cast<const uint4*>(wlds + (q * 16 + rho) * G::RS + kb);
+                    acc[q] = Mfma<S>::step(a[s], bv, acc[q]);
+                }
+            }
+        }
+
+        // row sums of squares: the 4 lane groups of a row hold partials
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+
+        float* E = epi + wave * G::EPI;
+        float* Cs = E;                          // [16][CPITCH]
+        float* rs = E + 16 * G::CPITCH;         // [16]
+        float* ls = rs + 16;                    // [TPW][K]
+#pragma unroll
+        for (int q = 0; q < NT; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Cs[(4 * grp + r) * G::CPITCH + q * 16 + rho] = acc[q][r];
+        if (grp == 0) rs[rho] = 1.0f / sqrtf(ss / (float)d + eps);
+        __syncthreads();
+
+        for (int o = lane; o < TPW * K; o += 64) {
+            const int tl = o / K, col = o % K;
+            float z = rs[tl * N] * Cs[(tl * N) * G::CPITCH + col];
+#pragma unroll
+            for (int i = 1; i < N; ++i) z = fmaf(rs[tl * N + i], Cs[(tl * N + i) * G::CPITCH + col], z);
+            z = z / (float)N;
+            if (iters == 0) {
+                if (tok0 + tl < T) w_out[(tok0 + tl) * K + col] = w_static[col] + scale * tanhf(z);
+            } else {
+                ls[tl * K + col] = fmaf(scale, z, w_static[col]);
+            }
+        }
+        if (iters > 0) {
+            __syncthreads();
+            if (lane < TPW && tok0 + lane < T) {
+                float l[K], out[K];
+#pragma unroll
+                for (int col = 0; col < K; ++col) l[col] = ls[lane * K + col];
+                mhc_record<N>(l, out, iters);
+#pragma unroll
+                for (int col = 0; col < K; ++col) w_out[(tok0 + lane) * K + col] = out[col];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_sinkhorn(const float* logits, float* w_out, int iters, int64_t T, int n,
+                           hipStream_t s) {
+    const int64_t blocks = (T + 255) / 256;
+    const dim3 grid((unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid));
+    switch (n) {
+        case 1: return launch(sinkhorn_kernel<1>, grid, dim3(256), 0, s, logits, w_out, iters, T);
+        case 2: return launch(sinkhorn_kernel<2>, grid, dim3(256), 0, s, logits, w_out, iters, T);
+        case 3: return launch(sinkhorn_kernel<3>, grid, dim3(256), 0, s, logits, w_out, iters, T);
+        case 4: return launch(sinkhorn_kernel<4>, grid, dim3(256), 0, s, logits, w_out, iters, T);
+    }
+    return hipErrorInvalidValue;
+}
+
+namespace {
+template <int N, typename S>
+hipError_t weights_go(const void* H, const void* W, const float* w_static, float scale, float eps,
+                      int iters, float* w_out, int64_t T, int d, hipStream_t s) {
+    const int64_t per_block = kWaves * WeightsGeom<N, S>::TPW;
+    const int64_t blocks = (T + per_block - 1) / per_block;
+    const dim3 grid((unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid));
+    return launch(weights_kernel<N, S>, grid, dim3(256), 0, s, static_cast<const uint8_t*>(H),
+                  static_cast<const uint8_t*>(W), w_static, scale, eps, iters, w_out, T, d);
+}
+template <typename S>
+hipError_t weights_by_n(int n, const void* H, const void* W, const float* w_static, float scale,
+                        float eps, int iters, float* w_out, int64_t T, int d, hipStream_t s) {
+    switch (n) {
+        case 1: return weights_go<1, S>(H, W, w_static, scale, eps, iters, w_out, T, d, s);
+        case 2: return weights_go<2, S>(H, W, w_static, scale, eps, iters, w_out, T, d, s);
+        case 3: return weights_go<3, S>(H, W, w_static, scale, eps, iters, w_out, T, d, s);
+        case 4: return weights_go<4, S>(H, W, w_static, scale, eps, iters, w_out, T, d, s);
+    }
+    return hipErrorInvalidValue;
+}
+}  // namespace
+
+hipError_t launch_weights(const void* H, const void* W, const float* w_static, float scale,
+                          float eps, int iters, float* w_out, int64_t T, int n, int d, int dt,
+                          hipStream_t s) {
+    if (dt == 0) return weights_by_n<f32_t>(n, H, W, w_static, scale, eps, iters, w_out, T, d, s);
+    return weights_by_n<bf16_t>(n, H, W, w_static, scale, eps, iters, w_out, T, d, s);
+}
+
+}  // namespace hc

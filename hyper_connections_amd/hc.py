@@ -1,0 +1,228 @@
+"""Thin ctypes binding of libhc.so (declared in include/hc.h).
+
+Argument marshalling only: every function checks the torch tensors it is
+given (device, dtype, contiguity, shape), passes raw device pointers and the
+current HIP stream to the C entry point of the same name, and raises
+``HCError`` with the library's status text when the call is rejected.  All
+work runs in the library's kernels; there is no CPU fallback, and the module
+raises on first use if the library is not built.
+
+Tensor conventions (storage dtype torch.bfloat16 or torch.float32):
+  H      (T, n, d)      residual streams
+  u, F   (T, d)         block input / block output
+  w      (K,) float32   one weight record shared by all tokens, or
+         (T, K) float32 one record per token; K = 2n + n^2 laid out as
+                        [alpha (n) | beta (n) | A (n x n, row-major)]
+  gamma  (d,) float32   RMSNorm gain
+  W      (K, d)         projection for per-token weights
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhc.so")
+
+HC_F32, HC_BF16 = 0, 1
+MAX_STREAMS = 4
+MAX_HIDDEN = 16384
+MAX_SINKHORN_ITERS = 10000
+
+# (name, argtypes); every entry point returns hc_status (int)
+_vp, _fp = ctypes.c_void_p, ctypes.c_void_p
+_i64, _i32, _f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+_SIGS = {
+    "hc_pre_mix": [_vp, _fp, _i64, _fp, _f32, _vp, _i64, _i32, _i32, _i32, _vp],
+    "hc_post_mix": [_vp, _vp, _fp, _i64, _vp, _i64, _i32, _i32, _i32, _vp],
+    "hc_post_pre_mix": [_vp, _vp, _fp, _i64, _fp, _i64, _fp, _f32, _vp, _vp, _i64, _i32, _i32,
+                        _i32, _vp],
+    "hc_weights": [_vp, _vp, _fp, _f32, _f32, _i32, _fp, _i64, _i32, _i32, _i32, _vp],
+    "hc_sinkhorn": [_fp, _fp, _i32, _i64, _i32, _vp],
+    "hc_block_tanh": [_vp, _vp, _i64, _i32, _vp],
+}
+EXPORTS = tuple(_SIGS) + ("hc_status_str", "hc_abi_version")
+
+_lib = None
+
+
+class HCError(RuntimeError):
+    def __init__(self, func: str, status: int, text: str):
+        super().__init__(f"{func}: {text}")
+        self.func, self.status = func, status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libhc.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built: run `python -m hyper_connections_amd.build` "
+                "(or __graft_entry__.build()); there is no CPU fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.hc_status_str.argtypes = [ctypes.c_int]
+        L.hc_status_str.restype = ctypes.c_char_p
+        L.hc_abi_version.argtypes = []
+        L.hc_abi_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().hc_status_str(int(status)).decode()
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise HCError(name, st, status_str(st))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return HC_BF16
+    if t.dtype == torch.float32:
+        return HC_F32
+    raise TypeError(f"storage dtype must be bfloat16 or float32, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, what: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be on a GPU, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t
+
+
+def _record(w: torch.Tensor, T: int, K: int, what: str = "w") -> int:
+    """Validate a weight-record tensor; returns its token stride."""
+    _dev(w, what)
+    if w.dtype != torch.float32:
+        raise TypeError(f"{what} must be float32")
+    if tuple(w.shape) == (K,):
+        return 0
+    if tuple(w.shape) == (T, K):
+        return K
+    raise ValueError(f"{what} must have shape ({K},) or ({T}, {K}), got {tuple(w.shape)}")
+
+
+def _H(H: torch.Tensor):
+    _dev(H, "H")
+    if H.dim() != 3:
+        raise ValueError(f"H must be (T, n, d), got {tuple(H.shape)}")
+    T, n, d = H.shape
+    return T, n, d, 2 * n + n * n
+
+
+def pre_mix(H, w, gamma, eps: float = 1e-6, out=None, stream=None) -> torch.Tensor:
+    """Block input u = RMSNorm_gamma(sum_i alpha_i H_i), shape (T, d)."""
+    T, n, d, K = _H(H)
+    ws = _record(w, T, K)
+    _dev(gamma, "gamma")
+    if gamma.dtype != torch.float32 or tuple(gamma.shape) != (d,):
+        raise ValueError("gamma must be float32 of shape (d,)")
+    u = torch.empty((T, d), dtype=H.dtype, device=H.device) if out is None else _dev(out, "out")
+    if u.dtype != H.dtype or tuple(u.shape) != (T, d):
+        raise ValueError("out must match H's dtype and have shape (T, d)")
+    _call("hc_pre_mix", H.data_ptr(), w.data_ptr(), ws, gamma.data_ptr(), float(eps), u.data_ptr(),
+          T, n, d, _dt(H), _stream(stream))
+    return u
+
+
+def post_mix(H, F, w, out=None, stream=None) -> torch.Tensor:
+    """H'_i = sum_j A[i][j] H_j + beta_i F, shape (T, n, d).  ``out=H`` runs in place."""
+    T, n, d, K = _H(H)
+    ws = _record(w, T, K)
+    _dev(F, "F")
+    if F.dtype != H.dtype or tuple(F.shape) != (T, d):
+        raise ValueError("F must match H's dtype and have shape (T, d)")
+    o = torch.empty_like(H) if out is None else _dev(out, "out")
+    if o.dtype != H.dtype or o.shape != H.shape:
+        raise ValueError("out must match H")
+    _call("hc_post_mix", H.data_ptr(), F.data_ptr(), w.data_ptr(), ws, o.data_ptr(), T, n, d,
+          _dt(H), _stream(stream))
+    return o
+
+
+def post_pre_mix(H, F, w, w_next, gamma_next, eps: float = 1e-6, out=None, u_out=None,
+                 stream=None):
+    """Fused write-back of one layer and read-mix + RMSNorm of the next.
+    Returns (H', u_next); bitwise equal to post_mix followed by pre_mix."""
+    T, n, d, K = _H(H)
+    ws = _record(w, T, K)
+    ws2 = _record(w_next, T, K, "w_next")
+    _dev(F, "F")
+    _dev(gamma_next, "gamma_next")
+    if F.dtype != H.dtype or tuple(F.shape) != (T, d):
+        raise ValueError("F must match H's dtype and have shape (T, d)")
+    if gamma_next.dtype != torch.float32 or tuple(gamma_next.shape) != (d,):
+        raise ValueError("gamma_next must be float32 of shape (d,)")
+    o = torch.empty_like(H) if out is None else _dev(out, "out")
+    u = torch.empty((T, d), dtype=H.dtype, device=H.device) if u_out is None else _dev(u_out, "u_out")
+    if o.dtype != H.dtype or o.shape != H.shape or u.dtype != H.dtype or tuple(u.shape) != (T, d):
+        raise ValueError("out / u_out do not match H")
+    _call("hc_post_pre_mix", H.data_ptr(), F.data_ptr(), w.data_ptr(), ws, w_next.data_ptr(), ws2,
+          gamma_next.data_ptr(), float(eps), o.data_ptr(), u.data_ptr(), T, n, d, _dt(H),
+          _stream(stream))
+    return o, u
+
+
+def weights(H, W, w_static, scale: float, eps: float = 1e-6, sinkhorn_iters: int = 0,
+            out=None, stream=None) -> torch.Tensor:
+    """Per-token weight records (T, K) float32 from the streams (see include/hc.h)."""
+    T, n, d, K = _H(H)
+    _dev(W, "W")
+    if W.dtype != H.dtype or tuple(W.shape) != (K, d):
+        raise ValueError(f"W must match H's dtype and have shape ({K}, {d})")
+    _dev(w_static, "w_static")
+    if w_static.dtype != torch.float32 or tuple(w_static.shape) != (K,):
+        raise ValueError(f"w_static must be float32 of shape ({K},)")
+    o = torch.empty((T, K), dtype=torch.float32, device=H.device) if out is None else _dev(out, "out")
+    if o.dtype != torch.float32 or tuple(o.shape) != (T, K):
+        raise ValueError(f"out must be float32 of shape ({T}, {K})")
+    _call("hc_weights", H.data_ptr(), W.data_ptr(), w_static.data_ptr(), float(scale), float(eps),
+          int(sinkhorn_iters), o.data_ptr(), T, n, d, _dt(H), _stream(stream))
+    return o
+
+
+def sinkhorn(logits, n: int, iters: int, out=None, stream=None) -> torch.Tensor:
+    """mHC transform of per-token logit records (T, K) -> weight records (T, K)."""
+    _dev(logits, "logits")
+    K = 2 * n + n * n
+    if logits.dtype != torch.float32 or logits.dim() != 2 or logits.shape[1] != K:
+        raise ValueError(f"logits must be float32 of shape (T, {K})")
+    T = logits.shape[0]
+    o = torch.empty_like(logits) if out is None else _dev(out, "out")
+    if o.dtype != torch.float32 or o.shape != logits.shape:
+        raise ValueError("out must match logits")
+    _call("hc_sinkhorn", logits.data_ptr(), o.data_ptr(), int(iters), T, int(n), _stream(stream))
+    return o
+
+
+def block_tanh(u, out=None, stream=None) -> torch.Tensor:
+    """Stand-in block F = tanh(u) (not part of the method)."""
+    _dev(u, "u")
+    F = torch.empty_like(u) if out is None else _dev(out, "out")
+    if F.dtype != u.dtype or F.shape != u.shape:
+        raise ValueError("out must match u")
+    _call("hc_block_tanh", u.data_ptr(), F.data_ptr(), u.numel(), _dt(u), _stream(stream))
+    return F
+
+
+def abi_version() -> int:
+    return int(lib().hc_abi_version())

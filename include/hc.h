@@ -1,0 +1,156 @@
+/*
+ * hc.h -- C ABI of libhc.so, the identity Hyper-Connections residual path on
+ * MI355X (gfx950).
+ *
+ * Sources (web pages; cited by title and section):
+ *   [EXPL]  learnaivisually.com, "Tencent open-sources Hy4 Preview at 770B --
+ *           Identity Hyper-Connections -- What does it mean?"
+ *   [GLOSS] hfviewer.com glossary entry "Hyper-connections (mHC)"
+ *   [ATLAS] llm-atlas model card "Tencent Hy4-preview (770B-A49B)"
+ *
+ * The residual stream is widened to n parallel streams that a block reads
+ * from and writes to separately ([EXPL] "Jargon", Hyper-Connections); learned
+ * matrices mix them before and after the block ([GLOSS] definition).  Around
+ * a user's block the path is therefore two calls: hc_pre_mix before it (the
+ * block's input) and hc_post_mix after it (write-back into the streams), plus
+ * the producers of per-token mixing weights (hc_weights, hc_sinkhorn).
+ *
+ * Common conventions
+ * ------------------
+ *  - Residual state H: [T][n][d] contiguous, token-major; T tokens in flight,
+ *    n streams (1..4; Hy4 uses 4 per [EXPL] TL;DR), hidden width d.
+ *  - Block input u and block output F: [T][d] contiguous.
+ *  - Storage dtype (hc_dtype) applies to H, F, u, H_out and W.  Arithmetic is
+ *    fp32; results are rounded once to the storage type (nearest, ties to
+ *    even; subnormals kept).
+ *  - Weight record: K = 2n + n^2 fp32 values
+ *        [alpha_0..alpha_{n-1} | beta_0..beta_{n-1} | A row-major]
+ *    A[i][j] (at 2n + i*n + j) weighs input stream j into output stream i.
+ *    Record of token t is at w + t * w_stride; w_stride = 0 shares one record
+ *    (static weights), otherwise w_stride >= K.
+ *  - Identity weights (alpha = e_0, beta = 1, A = I) on n copies of one
+ *    stream reproduce the ordinary residual x + f(x) bitwise ([EXPL]
+ *    "Jargon", Identity initialization).
+ *  - Every pointer is device memory owned by the caller.  The library
+ *    allocates nothing and keeps no state; calls are thread-safe.
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  Work
+ *    is enqueued and the call returns without synchronising.
+ *  - All arguments are validated before anything is launched; a failed check
+ *    returns its code with nothing enqueued.  A launch failure reported by the
+ *    HIP runtime returns HC_ERR_HIP.  No exception crosses the ABI and the
+ *    library never prints.
+ *  - Sizes: 1 <= n <= 4; 1 <= d <= HC_MAX_HIDDEN; d % 8 == 0 for bf16 and
+ *    d % 4 == 0 for fp32 (16-byte vectors) else HC_ERR_SHAPE.  T == 0 is a
+ *    no-op returning HC_OK; T < 0 is HC_ERR_ARG.
+ *  - Alignment: H, F, u, H_out, W and gamma 16 bytes; weight records and
+ *    logits 4 bytes (HC_ERR_ALIGN).
+ *  - Aliasing: outputs may not overlap any input or each other
+ *    (HC_ERR_ALIAS), except H_out == H exactly in hc_post_mix (in place).
+ */
+#ifndef HC_H
+#define HC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hc_status {
+    HC_OK = 0,
+    HC_ERR_NULL = 1,   /* a required pointer is NULL                        */
+    HC_ERR_SHAPE = 2,  /* n, d or a stride outside the supported set       */
+    HC_ERR_DTYPE = 3,  /* unknown hc_dtype                                  */
+    HC_ERR_ALIGN = 4,  /* pointer not aligned as required                   */
+    HC_ERR_ALIAS = 5,  /* an output overlaps an input or another output     */
+    HC_ERR_ARG = 6,    /* T < 0, eps not positive/finite, iters out of range */
+    HC_ERR_HIP = 7     /* the HIP runtime reported a launch error           */
+} hc_status;
+
+typedef enum hc_dtype { HC_F32 = 0, HC_BF16 = 1 } hc_dtype;
+
+#define HC_MAX_STREAMS 4
+#define HC_MAX_HIDDEN 16384
+#define HC_MAX_SINKHORN_ITERS 10000
+#define HC_RECORD_LEN(n) (2 * (n) + (n) * (n))
+
+/* Pre (read-mix + RMSNorm): u = gamma * x / sqrt(mean_k x_k^2 + eps) with
+ * x = sum_i alpha_i H_i.  [GLOSS] definition (mixing before the block);
+ * [EXPL] "Jargon", Pre-norm (the block input is normalised); RMSNorm per
+ * [GLOSS] "Related concepts".
+ *   H      [T][n][d] dt          w  records (only alpha is read)
+ *   gamma  [d] fp32              eps > 0
+ *   u      [T][d] dt, output (may not overlap H, w or gamma)
+ * The reduction over d is done in an order that depends only on d, so alpha =
+ * e_0 gives u bitwise equal to the n = 1 call on stream 0. */
+hc_status hc_pre_mix(const void* H, const float* w, int64_t w_stride,
+                     const float* gamma, float eps, void* u,
+                     int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream);
+
+/* Post (stream-mix + write-back): H_out_i = sum_j A[i][j] H_j + beta_i F.
+ * [GLOSS] definition (mixing after the block); [EXPL] "Jargon", Residual
+ * connection (the block output is added to what came in).
+ *   H      [T][n][d] dt          F  [T][d] dt
+ *   w      records (beta and A are read)
+ *   H_out  [T][n][d] dt, output; H_out == H is allowed (in place: every
+ *          element is read before the same thread writes it), any other
+ *          overlap is HC_ERR_ALIAS. */
+hc_status hc_post_mix(const void* H, const void* F, const float* w, int64_t w_stride,
+                      void* H_out, int64_t T, int32_t n, int32_t d, hc_dtype dt,
+                      void* stream);
+
+/* Per-token weights computed from the streams.  The pages publish no rule for
+ * per-token weights ([EXPL], the paragraph on what the model card leaves
+ * out); the reading implemented: r_i = 1/sqrt(mean_k H_ik^2 + eps),
+ * hbar = (1/n) sum_i r_i H_i, z_c = sum_k hbar_k W[c][k] (c < K), then
+ *   sinkhorn_iters == 0:  w = w_static + scale * tanh(z)
+ *   sinkhorn_iters  > 0:  l = w_static + scale * z, w = the hc_sinkhorn
+ *                         transform of l with that many iterations.
+ * The projection runs on the matrix cores (MFMA), fp32 accumulation.
+ *   H        [T][n][d] dt        W  [K][d] dt (row c = output c; the layout
+ *                                   of a linear layer's weight)
+ *   w_static [K] fp32            w_out [T][K] fp32, output (stride K)
+ *   0 <= sinkhorn_iters <= HC_MAX_SINKHORN_ITERS, eps > 0. */
+hc_status hc_weights(const void* H, const void* W, const float* w_static, float scale,
+                     float eps, int32_t sinkhorn_iters, float* w_out,
+                     int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream);
+
+/* mHC step: make the stream mix doubly stochastic with Sinkhorn iterations
+ * ([GLOSS] definition; [ATLAS] "Architecture concepts", mHC).  Per token:
+ * alpha = sigmoid(l_alpha), beta = sigmoid(l_beta), A = exp(l_A) then `iters`
+ * times {divide every row by its sum; divide every column by its sum}.  With
+ * iters >= 1 the largest logit of A is subtracted before exp (equal after the
+ * first row division in exact arithmetic).  After the last iteration columns
+ * sum to 1 to fp32 rounding; rows approach 1 as iters grows.
+ *   logits [T][K] fp32, w_out [T][K] fp32 output (may not overlap logits),
+ *   0 <= iters <= HC_MAX_SINKHORN_ITERS. */
+hc_status hc_sinkhorn(const float* logits, float* w_out, int32_t iters, int64_t T,
+                      int32_t n, void* stream);
+
+/* Cross-layer fusion: the write-back of one layer and the read-mix + RMSNorm
+ * of the next in one pass over the streams.  Equivalent to hc_post_mix(H, F,
+ * w, w_stride, H_out) followed by hc_pre_mix(H_out, w_next, w_next_stride,
+ * gamma_next, eps, u_next) with H_out rounded to dt in between, but H_out is
+ * read back from registers instead of HBM.  H_out == H is allowed; u_next may
+ * not overlap anything else. */
+hc_status hc_post_pre_mix(const void* H, const void* F, const float* w, int64_t w_stride,
+                          const float* w_next, int64_t w_next_stride,
+                          const float* gamma_next, float eps, void* H_out, void* u_next,
+                          int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream);
+
+/* Stand-in block used by the benchmarks and tests, not part of the method:
+ * F = tanh(u) elementwise ([EXPL] "Jargon", Residual connection: the block
+ * computes f(x)).  count % 8 == 0 (bf16) or count % 4 == 0 (fp32). */
+hc_status hc_block_tanh(const void* u, void* F, int64_t count, hc_dtype dt, void* stream);
+
+/* Static string naming a status code; never NULL. */
+const char* hc_status_str(hc_status s);
+
+/* Version of this ABI (incremented on any signature change). */
+int32_t hc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HC_H */

@@ -1,0 +1,84 @@
+"""Helpers for the GPU parity tests: host <-> device transfer of storage
+arrays and the error metric.
+
+Error metric: for every element, |gpu - ref| / max(|ref|, rms(ref row)), where
+the row is the d-vector (or weight record) the element belongs to; the
+maximum over elements is compared with the tolerance.  Dividing by the row
+RMS stops cancellation near zero from failing a correct result.
+
+Tolerances: 1e-5 for fp32 storage; 2e-2 for bf16 storage with fp32
+arithmetic.  For bf16 the tests also require one bf16 unit in the last place
+(2^-8 of the row scale), which a correctly rounded store plus fp32 arithmetic
+meets with margin."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+TOL_BF16_ULP = 2.0 ** -8
+TOL_RECORD = 1e-5      # fp32 weight records (any storage dtype of H)
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    """Storage array (float32 or uint16 bf16 bits) -> device tensor."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    if a.dtype in (np.float32, np.float64):
+        return torch.from_numpy(a.astype(np.float32)).cuda()
+    raise TypeError(a.dtype)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> storage array (uint16 bits for bf16)."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """Max over elements of |got - ref| / max(|ref|, rms(ref row)); rows are
+    the last axis.  NaNs must match position for position."""
+    g = oracle.widen(got) if got.dtype in (np.uint16, np.float32) else np.asarray(got, np.float64)
+    r = np.asarray(ref, np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    if g.size == 0:
+        return 0.0
+    gn, rn = np.isnan(g), np.isnan(r)
+    assert np.array_equal(gn, rn), "NaN positions differ"
+    g, r = np.where(gn, 0.0, g), np.where(rn, 0.0, r)
+    inf = np.isinf(r) | np.isinf(g)
+    if inf.any():
+        assert np.array_equal(g[inf], r[inf]), "infinities differ"
+        g, r = np.where(inf, 0.0, g), np.where(inf, 0.0, r)
+    rms = np.sqrt(np.mean(r * r, axis=-1, keepdims=True))
+    scale = np.maximum(np.abs(r), rms)
+    scale = np.where(scale == 0, 1.0, scale)
+    return float(np.max(np.abs(g - r) / scale))
+
+
+def check(got: np.ndarray, ref: np.ndarray, what: str = "") -> float:
+    """Assert the storage-dtype tolerance; returns the error."""
+    e = rel_err(got, ref)
+    if got.dtype == np.uint16:
+        assert e <= TOL_BF16, f"{what}: max rel err {e:.3g} > {TOL_BF16}"
+        assert e <= TOL_BF16_ULP, f"{what}: max rel err {e:.3g} > one bf16 ulp"
+    else:
+        assert e <= TOL_F32, f"{what}: max rel err {e:.3g} > {TOL_F32}"
+    return e
+
+
+def rounded(ref64: np.ndarray, like: np.ndarray) -> np.ndarray:
+    """The oracle's value stored in the storage dtype of `like`."""
+    return oracle.round_bf16(ref64) if like.dtype == np.uint16 else oracle.round_f32(ref64)

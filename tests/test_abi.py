@@ -1,0 +1,140 @@
+"""The C ABI: the built library loads and exports every function include/hc.h
+declares, and argument validation rejects bad calls before anything is
+launched (these calls never reach the GPU, so they run on any host)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from hyper_connections_amd import hc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hc.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, ARG = 0, 1, 2, 3, 4, 5, 6
+BF16, F32 = hc.HC_BF16, hc.HC_F32
+
+# fake, never dereferenced device addresses (16-byte aligned, far apart)
+P = [0x10000000 * (i + 1) for i in range(8)]
+MiB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(hc.LIB_PATH):
+        from hyper_connections_amd import build
+        build.build()
+    return hc.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:hc_status|const char\*|int32_t)\s+(hc_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(hc.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", hc.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(hc_\w+)$", out, re.M))
+    for n in names:
+        assert n in exported, n
+        assert getattr(L, n) is not None
+
+
+def test_status_strings(L):
+    for code in range(8):
+        s = hc.status_str(code)
+        assert s.startswith("HC_")
+    assert hc.status_str(99).startswith("HC_ERR_UNKNOWN")
+    assert hc.abi_version() == 1
+
+
+def pre(L, H=P[0], w=P[1], ws=0, g=P[2], eps=1e-6, u=P[3], T=16, n=4, d=4096, dt=BF16):
+    return L.hc_pre_mix(H, w, ws, g, eps, u, T, n, d, dt, None)
+
+
+def post(L, H=P[0], F=P[1], w=P[2], ws=0, O=P[3], T=16, n=4, d=4096, dt=BF16):
+    return L.hc_post_mix(H, F, w, ws, O, T, n, d, dt, None)
+
+
+def test_pre_validation(L):
+    assert pre(L, T=0) == OK                       # empty: no-op, nothing launched
+    assert pre(L, H=None) == NULL and pre(L, u=None) == NULL and pre(L, g=None) == NULL
+    assert pre(L, n=0) == SHAPE and pre(L, n=5) == SHAPE
+    assert pre(L, d=4092) == SHAPE                 # bf16 needs d % 8 == 0
+    assert pre(L, d=4092, dt=F32, T=0) == OK       # fp32 needs d % 4 == 0
+    assert pre(L, d=0) == SHAPE and pre(L, d=hc.MAX_HIDDEN + 8) == SHAPE
+    assert pre(L, dt=2) == DTYPE
+    assert pre(L, T=-1) == ARG
+    assert pre(L, eps=0.0) == ARG and pre(L, eps=-1.0) == ARG and pre(L, eps=float("inf")) == ARG
+    assert pre(L, ws=5) == SHAPE                   # stride must be 0 or >= K = 24
+    assert pre(L, H=P[0] + 8) == ALIGN and pre(L, u=P[3] + 4) == ALIGN
+    assert pre(L, g=P[2] + 4) == ALIGN and pre(L, w=P[1] + 2) == ALIGN
+    assert pre(L, u=P[0] + 16 * 4096) == ALIAS     # u inside H
+    assert pre(L, u=P[1] - 64) == ALIAS            # u runs into w
+
+
+def test_post_validation(L):
+    assert post(L, T=0) == OK
+    assert post(L, F=None) == NULL and post(L, O=None) == NULL
+    assert post(L, n=7) == SHAPE and post(L, d=12) == SHAPE
+    assert post(L, T=-3) == ARG and post(L, dt=9) == DTYPE
+    assert post(L, O=P[3] + 8) == ALIGN
+    assert post(L, O=P[0] + 16) == ALIAS           # partial overlap with H
+    assert post(L, O=P[1]) == ALIAS                # H_out on F
+    assert post(L, O=P[2] - 16) == ALIAS           # H_out runs into w
+    assert post(L, T=0, O=P[0]) == OK              # exact in-place is allowed
+    assert post(L, ws=23) == SHAPE
+
+
+def test_fused_validation(L):
+    f = lambda **k: L.hc_post_pre_mix(  # noqa: E731
+        k.get("H", P[0]), k.get("F", P[1]), k.get("w", P[2]), k.get("ws", 0), k.get("w2", P[3]),
+        k.get("ws2", 0), k.get("g", P[4]), k.get("eps", 1e-6), k.get("O", P[5]), k.get("u", P[6]),
+        k.get("T", 4), 4, 4096, BF16, None)
+    assert f(T=0) == OK
+    assert f(w2=None) == NULL and f(u=None) == NULL
+    assert f(ws2=3) == SHAPE and f(eps=0.0) == ARG
+    assert f(u=P[5]) == ALIAS                      # u_next on H_out
+    assert f(u=P[0]) == ALIAS                      # u_next on H
+    assert f(O=P[0], T=0) == OK
+
+
+def test_weights_validation(L):
+    f = lambda **k: L.hc_weights(  # noqa: E731
+        k.get("H", P[0]), k.get("W", P[1]), k.get("ws", P[2]), k.get("scale", 0.01),
+        k.get("eps", 1e-6), k.get("it", 0), k.get("o", P[3]), k.get("T", 64), k.get("n", 4),
+        k.get("d", 4096), k.get("dt", BF16), None)
+    assert f(T=0) == OK
+    assert f(W=None) == NULL
+    assert f(it=-1) == ARG and f(it=hc.MAX_SINKHORN_ITERS + 1) == ARG
+    assert f(scale=float("nan")) == ARG and f(eps=0.0) == ARG
+    assert f(W=P[1] + 8) == ALIGN and f(o=P[3] + 2) == ALIGN
+    assert f(o=P[0] + 64) == ALIAS and f(o=P[1]) == ALIAS
+    assert f(n=0) == SHAPE and f(d=100) == SHAPE and f(dt=5) == DTYPE
+
+
+def test_sinkhorn_validation(L):
+    f = lambda **k: L.hc_sinkhorn(k.get("l", P[0]), k.get("o", P[1]), k.get("it", 20),  # noqa: E731
+                                  k.get("T", 100), k.get("n", 4), None)
+    assert f(T=0) == OK
+    assert f(l=None) == NULL and f(n=5) == SHAPE and f(it=-2) == ARG and f(T=-1) == ARG
+    assert f(o=P[0] + 4) == ALIAS and f(o=P[0] + 2) == ALIGN
+
+
+def test_block_tanh_validation(L):
+    f = lambda **k: L.hc_block_tanh(k.get("u", P[0]), k.get("F", P[1]), k.get("c", 4096),  # noqa: E731
+                                    k.get("dt", BF16), None)
+    assert f(c=0) == OK and f(c=-8) == ARG and f(c=12) == SHAPE and f(c=12, dt=F32, F=P[0] + 16) == ALIAS
+    assert f(u=None) == NULL and f(dt=4) == DTYPE and f(F=P[1] + 4) == ALIGN
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    H = torch.zeros(2, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        hc.pre_mix(H, torch.zeros(24), torch.ones(64))

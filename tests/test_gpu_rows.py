@@ -1,0 +1,217 @@
+"""GPU parity of the streaming kernels (pre, post, fused post+pre, tanh block)
+against the fp64 oracle, through the C ABI.
+
+Cases span every launch shape of the row kernels (64-thread rows, 256-thread
+rows with 1-4 vectors per thread, 1024-thread rows with 2-4), ragged rows
+(d not a multiple of the block's vector count), T = 1 and small odd T, both
+storage dtypes, n = 1..4, shared and per-token weight records."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import check, dev, host, need_gpu, rel_err, rounded
+from hyper_connections_amd import hc
+from hyper_connections_amd.workloads import (f32_to_bf16_bits, identity_record, make_inputs,
+                                             workload)
+
+pytestmark = pytest.mark.gpu
+
+# d values per dtype: covers every (block, vectors-per-thread) launch shape
+D_BF16 = [8, 40, 520, 2048, 4096, 6144, 8192, 8200, 16384]
+D_F32 = [4, 36, 516, 1024, 3072, 4096, 4100, 12288, 16384]
+SHAPES = [("bf16", d) for d in D_BF16] + [("f32", d) for d in D_F32]
+
+
+def storage(x: np.ndarray, dt: str) -> np.ndarray:
+    return f32_to_bf16_bits(x) if dt == "bf16" else x.astype(np.float32)
+
+
+def case(rng, dt, T, n, d, per_token):
+    K = 2 * n + n * n
+    H = storage(rng.standard_normal((T, n, d)).astype(np.float32), dt)
+    F = storage(rng.standard_normal((T, d)).astype(np.float32), dt)
+    if per_token:
+        w = (identity_record(n)[None, :] + 0.3 * rng.standard_normal((T, K))).astype(np.float32)
+    else:
+        w = (identity_record(n) + 0.3 * rng.standard_normal(K)).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    return H, F, w, g
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+@pytest.mark.parametrize("dt,d", SHAPES)
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_pre_parity(dt, d, n):
+    rng = np.random.default_rng(1000 * n + d)
+    T = 3 if d >= 8192 else 7
+    H, F, w, g = case(rng, dt, T, n, d, per_token=(d % 3 == 0))
+    u = host(hc.pre_mix(dev(H), dev(w), dev(g), 1e-6))
+    ref = oracle.pre_mix(H, w.astype(np.float64), g, 1e-6)
+    check(u, ref, f"pre n={n} d={d} {dt}")
+
+
+@pytest.mark.parametrize("dt,d", SHAPES)
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_post_parity(dt, d, n):
+    rng = np.random.default_rng(2000 * n + d)
+    T = 3 if d >= 8192 else 7
+    H, F, w, g = case(rng, dt, T, n, d, per_token=(d % 3 != 0))
+    out = host(hc.post_mix(dev(H), dev(F), dev(w)))
+    ref = oracle.post_mix(H, F, w.astype(np.float64))
+    check(out, ref, f"post n={n} d={d} {dt}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("n", [1, 4])
+def test_post_in_place(dt, n):
+    rng = np.random.default_rng(7)
+    H, F, w, g = case(rng, dt, 33, n, 4096, per_token=True)
+    Hd = dev(H)
+    ptr = Hd.data_ptr()
+    hc.post_mix(Hd, dev(F), dev(w), out=Hd)
+    assert Hd.data_ptr() == ptr
+    check(host(Hd), oracle.post_mix(H, F, w.astype(np.float64)), "post in place")
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 8), ("bf16", 4096), ("bf16", 6144), ("bf16", 16384),
+                                  ("f32", 1024), ("f32", 16384)])
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_identity_post_is_plain_residual_bitwise(dt, d, n):
+    """alpha = e_0, beta = 1, A = I on n copies of x: every stream is the
+    stored x + F, bitwise, and equals the oracle's rounded value bitwise."""
+    rng = np.random.default_rng(d + n)
+    T = 9
+    x = storage(rng.standard_normal((T, 1, d)).astype(np.float32), dt)
+    F = storage(rng.standard_normal((T, d)).astype(np.float32), dt)
+    H = np.repeat(x, n, axis=1)
+    out = host(hc.post_mix(dev(H), dev(F), dev(identity_record(n))))
+    plain = rounded(oracle.widen(x)[:, 0, :] + oracle.widen(F), out)
+    for i in range(n):
+        assert np.array_equal(out[:, i, :], plain)
+    # the n = 1 layer is the ordinary residual (x + f(x)) stored once
+    one = host(hc.post_mix(dev(x), dev(F), dev(identity_record(1))))
+    assert np.array_equal(one[:, 0, :], plain)
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 8), ("bf16", 4096), ("bf16", 6144), ("bf16", 16384),
+                                  ("f32", 1024), ("f32", 4100)])
+@pytest.mark.parametrize("n", [2, 3, 4])
+def test_identity_pre_bitwise_equals_single_stream(dt, d, n):
+    """alpha = e_0: u is bitwise the n = 1 call on stream 0 (the reduction
+    order over d does not depend on n)."""
+    rng = np.random.default_rng(d * n)
+    H, F, w, g = case(rng, dt, 11, n, d, per_token=False)
+    u_n = host(hc.pre_mix(dev(H), dev(identity_record(n)), dev(g)))
+    u_1 = host(hc.pre_mix(dev(np.ascontiguousarray(H[:, :1, :])), dev(identity_record(1)), dev(g)))
+    assert np.array_equal(u_n, u_1)
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 40), ("bf16", 4096), ("bf16", 6144), ("bf16", 8200),
+                                  ("f32", 516), ("f32", 16384)])
+@pytest.mark.parametrize("n", [1, 3, 4])
+def test_fused_post_pre_bitwise(dt, d, n):
+    rng = np.random.default_rng(31 * d + n)
+    T = 13
+    H, F, w, g = case(rng, dt, T, n, d, per_token=True)
+    w2 = (identity_record(n) + 0.3 * rng.standard_normal(2 * n + n * n)).astype(np.float32)
+    Hd, Fd, wd, w2d, gd = dev(H), dev(F), dev(w), dev(w2), dev(g)
+    Hp, u = hc.post_pre_mix(Hd, Fd, wd, w2d, gd, 1e-6)
+    Hp_ref = hc.post_mix(Hd, Fd, wd)
+    u_ref = hc.pre_mix(Hp_ref, w2d, gd, 1e-6)
+    assert np.array_equal(host(Hp), host(Hp_ref))
+    assert np.array_equal(host(u), host(u_ref))
+    # and against the oracle, fed the stored H'
+    check(host(u), oracle.pre_mix(host(Hp), w2.astype(np.float64), g, 1e-6), "fused u")
+    # in place
+    Hd2 = dev(H)
+    hc.post_pre_mix(Hd2, Fd, wd, w2d, gd, 1e-6, out=Hd2)
+    assert np.array_equal(host(Hd2), host(Hp_ref))
+
+
+def test_deterministic():
+    rng = np.random.default_rng(5)
+    H, F, w, g = case(rng, "bf16", 257, 4, 4096, per_token=True)
+    Hd, Fd, wd, gd = dev(H), dev(F), dev(w), dev(g)
+    a = [host(hc.pre_mix(Hd, wd, gd)) for _ in range(3)]
+    b = [host(hc.post_mix(Hd, Fd, wd)) for _ in range(3)]
+    assert all(np.array_equal(a[0], x) for x in a[1:])
+    assert all(np.array_equal(b[0], x) for x in b[1:])
+
+
+def test_nan_and_inf_propagate_like_the_oracle():
+    rng = np.random.default_rng(9)
+    H, F, w, g = case(rng, "bf16", 6, 4, 64, per_token=False)
+    Hn = oracle.widen(H)
+    Hn[1, 2, 5] = np.nan
+    Hn[3, 0, 7] = np.inf
+    H2 = oracle.round_bf16(Hn)
+    Fn = oracle.widen(F)
+    Fn[4, 9] = -np.inf
+    F2 = oracle.round_bf16(Fn)
+    wd = w.astype(np.float64)
+    check(host(hc.pre_mix(dev(H2), dev(w), dev(g))), oracle.pre_mix(H2, wd, g), "pre nan")
+    check(host(hc.post_mix(dev(H2), dev(F2), dev(w))), oracle.post_mix(H2, F2, wd), "post nan")
+
+
+def test_zero_tokens_is_a_noop():
+    e = torch.empty((0, 4, 4096), dtype=torch.bfloat16, device="cuda")
+    u = hc.pre_mix(e, dev(identity_record(4)), torch.ones(4096, device="cuda"))
+    assert u.shape == (0, 4096)
+    o = hc.post_mix(e, torch.empty((0, 4096), dtype=torch.bfloat16, device="cuda"),
+                    dev(identity_record(4)))
+    assert o.shape == (0, 4, 4096)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_block_tanh(dt):
+    rng = np.random.default_rng(3)
+    u = storage(3 * rng.standard_normal((17, 1024)).astype(np.float32), dt)
+    F = host(hc.block_tanh(dev(u)))
+    check(F, oracle.block_tanh(u), "tanh")
+
+
+def test_tiny_f32_workload():
+    """T=256, n=4, d=1024 fp32, identity + N(0, 0.02) weights; F is the host
+    tanh of the oracle's block input, fed to both post paths."""
+    wl = workload("tiny-f32")
+    inp = make_inputs(wl)
+    H, w, g = inp["H"], inp["w"], inp["gamma"]
+    Hd, wd = dev(H), dev(w)
+    u = host(hc.pre_mix(Hd, wd, dev(g), wl.eps))
+    u_ref = oracle.pre_mix(H, w.astype(np.float64), g, wl.eps)
+    check(u, u_ref, "tiny pre")
+    F = oracle.round_f32(np.tanh(u_ref))
+    out = host(hc.post_mix(Hd, dev(F), wd))
+    check(out, oracle.post_mix(H, F, w.astype(np.float64)), "tiny post")
+    # unperturbed identity run: the ordinary residual, bitwise
+    out_id = host(hc.post_mix(dev(np.repeat(H[:, :1], 4, axis=1)), dev(F), dev(identity_record(4))))
+    assert np.array_equal(out_id[:, 3, :], oracle.round_f32(oracle.widen(H[:, 0, :]) + F))
+
+
+def sample_tokens(T: int, k: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=k, replace=False)]))
+
+
+def test_static_bf16_full_size_sampled():
+    """T=8192, n=4, d=4096 bf16, in the launch configuration the benchmark
+    times; 256 sampled tokens (plus the first and last) checked by the oracle."""
+    wl = workload("static-bf16")
+    inp = make_inputs(wl)
+    Hd, Fd, wd, gd = dev(inp["H"]), dev(inp["F"]), dev(inp["w"]), dev(inp["gamma"])
+    u = hc.pre_mix(Hd, wd, gd, wl.eps)
+    Hp = hc.post_mix(Hd, Fd, wd)
+    torch.cuda.synchronize()
+    idx = sample_tokens(wl.T, 256, 11)
+    sub = make_inputs(wl, tokens=idx)
+    assert np.array_equal(sub["H"], inp["H"][idx])
+    w64 = inp["w"].astype(np.float64)
+    check(host(u[torch.from_numpy(idx).cuda()]), oracle.pre_mix(sub["H"], w64, inp["gamma"], wl.eps),
+          "static pre")
+    check(host(Hp[torch.from_numpy(idx).cuda()]), oracle.post_mix(sub["H"], sub["F"], w64),
+          "static post")
