@@ -70,13 +70,19 @@ def counter_traffic(kernel: str, workload: str):
 
 
 class Timer:
-    """Events around every launch on the current stream; per-kernel averages."""
+    """Counts launches per kernel; with `per_kernel`, also records HIP events
+    on the launch stream around every launch."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, per_kernel: bool):
         self.torch = torch
+        self.per_kernel = per_kernel
         self.pairs = {}
+        self.counts = {}
 
     def run(self, name, fn):
+        self.counts[name] = self.counts.get(name, 0) + 1
+        if not self.per_kernel:
+            return fn()
         t = self.torch
         a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
         a.record()
@@ -90,6 +96,81 @@ class Timer:
 
     def clear(self):
         self.pairs = {}
+        self.counts = {}
+
+
+COPY_PROBE_BYTES = 512 * 2 ** 20   # bytes read (and written) by the calibration copy
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, kernel: str, workload: str, cmds: list):
+    """Turn two rocprofv3 --pmc runs of this benchmark (FETCH_SIZE, then
+    WRITE_SIZE; KiB per dispatch) into HBM bytes per launch of `kernel`.
+
+    Each counter is scaled by what it reads for the benchmark's calibration
+    copy (torch copy_ of COPY_PROBE_BYTES, a blit kernel that reads and writes
+    exactly that many bytes).  Writes profiles/<kernel>_<workload>_counters.json
+    (read by the benchmark for roofline.traffic) and a .md next to it."""
+    import csv
+
+    def rows(path, counter):
+        out = []
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    out.append(r)
+        return out
+
+    fetch, write = rows(fetch_csv, "FETCH_SIZE"), rows(write_csv, "WRITE_SIZE")
+    probe_kib = COPY_PROBE_BYTES / 1024
+    wprobe = [r for r in write if "copyBuffer" in r["Kernel_Name"]
+              and abs(float(r["Counter_Value"]) - probe_kib) < 0.01 * probe_kib]
+    ids = {r["Dispatch_Id"] for r in wprobe}
+    fprobe = [r for r in fetch if r["Dispatch_Id"] in ids and "copyBuffer" in r["Kernel_Name"]]
+    if not wprobe or not fprobe:
+        raise SystemExit("calibration copy not found in the counter runs")
+    mean = lambda rs: sum(float(r["Counter_Value"]) for r in rs) / len(rs)  # noqa: E731
+    f_scale, w_scale = probe_kib / mean(fprobe), probe_kib / mean(wprobe)
+    tag = f"{kernel}_kernel<"
+    fk, wk = [r for r in fetch if tag in r["Kernel_Name"]], [r for r in write if tag in r["Kernel_Name"]]
+    if not fk or not wk:
+        raise SystemExit(f"no {kernel} dispatches in the counter runs")
+    fetch_kib, write_kib = mean(fk), mean(wk)
+    traffic = (fetch_kib * f_scale + write_kib * w_scale) * 1024
+    from hyper_connections_amd import traffic as tr
+    from hyper_connections_amd import workloads
+    wl = workloads.workload(workload)
+    per_tok = wl.kind in ("dynamic", "mhc")
+    alg = {"pre_mix": tr.pre_bytes(wl.n, wl.d, wl.elem_bytes, per_tok),
+           "post_mix": tr.post_bytes(wl.n, wl.d, wl.elem_bytes, per_tok),
+           "weights": tr.weights_bytes(wl.n, wl.d, wl.elem_bytes),
+           "post_pre_mix": tr.post_pre_bytes(wl.n, wl.d, wl.elem_bytes)}[kernel] * wl.T
+    rec = {"kernel": kernel, "workload": workload, "source_sha": source_sha(kernel),
+           "dispatches": {"FETCH_SIZE": len(fk), "WRITE_SIZE": len(wk)},
+           "fetch_kib_per_dispatch": round(fetch_kib, 3), "write_kib_per_dispatch": round(write_kib, 3),
+           "copy_probe_bytes": COPY_PROBE_BYTES, "fetch_scale": round(f_scale, 5),
+           "write_scale": round(w_scale, 5), "traffic_bytes_per_launch": int(round(traffic)),
+           "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": round(traffic / alg, 5),
+           "commands": cmds}
+    base = os.path.join(PROFILES, f"{kernel}_{workload}_counters")
+    with open(base + ".json", "w") as fh:
+        json.dump(rec, fh, indent=1)
+    with open(base + ".md", "w") as fh:
+        fh.write(f"# HBM traffic of {kernel}, workload {workload}\n\n")
+        fh.write("Commands (run as `cd /tmp && export TMPDIR=/tmp` first; paths are relative to the repository root):\n\n")
+        for c in cmds:
+            fh.write(f"    {c}\n")
+        fh.write(f"\nSummarised with `python bench.py --summarize-counters FETCH_CSV WRITE_CSV "
+                 f"--kernel {kernel} --workload {workload}`.\n\n")
+        fh.write("| quantity | value |\n|---|---|\n")
+        for k in ("fetch_kib_per_dispatch", "write_kib_per_dispatch", "fetch_scale", "write_scale",
+                  "traffic_bytes_per_launch", "algorithmic_bytes_per_launch",
+                  "traffic_over_algorithmic", "source_sha"):
+            fh.write(f"| {k} | {rec[k]} |\n")
+        fh.write(f"\nCalibration: the benchmark's {COPY_PROBE_BYTES >> 20} MiB device copy reads "
+                 f"FETCH_SIZE x {f_scale:.4f} and WRITE_SIZE x {w_scale:.4f} of its true size; the "
+                 "kernel's counters are scaled by the same factors.\n")
+    log(f"[bench] wrote {base}.json: traffic {traffic / 1e6:.2f} MB/launch, "
+        f"{traffic / alg:.4f} x algorithmic")
 
 
 def main():
@@ -103,7 +184,16 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--fused", action="store_true",
                     help="chain: fuse each write-back with the next read-mix")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
+    ap.add_argument("--kernel", default="post_mix", help="kernel for --summarize-counters")
+    ap.add_argument("--command", action="append", default=[],
+                    help="profiling command to record in the summary (repeatable)")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.kernel, args.workload, args.command)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this path runs on one GPU "
@@ -175,37 +265,42 @@ def main():
         "block_tanh": 2 * d * s * T,
     }
 
+    # the kernels of one step, in order: (name, launch on buffer set b)
+    if wl.kind == "static":
+        ops = [("pre_mix", lambda b: hc.pre_mix(b["H"], w_static, gamma, wl.eps, out=b["u"])),
+               ("post_mix", lambda b: hc.post_mix(b["H"], b["F"], w_static, out=b["O"]))]
+    elif wl.kind == "dynamic":
+        ops = [("weights", lambda b: hc.weights(b["H"], Wp, ws, wl.scale, wl.eps, 0, out=b["w"])),
+               ("pre_mix", lambda b: hc.pre_mix(b["H"], b["w"], gamma, wl.eps, out=b["u"])),
+               ("post_mix", lambda b: hc.post_mix(b["H"], b["F"], b["w"], out=b["O"]))]
+    elif wl.kind == "mhc":
+        ops = [("sinkhorn", lambda b: hc.sinkhorn(b["logits"], n, wl.iters, out=b["w"])),
+               ("pre_mix", lambda b: hc.pre_mix(b["H"], b["w"], gamma, wl.eps, out=b["u"])),
+               ("post_mix", lambda b: hc.post_mix(b["H"], b["F"], b["w"], out=b["O"]))]
+    else:   # chain: H ping-pongs between b["H"] and b["O"] (an even layer count returns it)
+        ops = []
+        if args.fused:
+            ops.append(("pre_mix", lambda b: hc.pre_mix(b["H"], recs[0], gamma, wl.eps, out=b["u"])))
+        for l in range(wl.layers):
+            src, dst = ("H", "O") if l % 2 == 0 else ("O", "H")
+            ops.append(("block_tanh", lambda b: hc.block_tanh(b["u"], out=b["F"])) if args.fused else
+                       ("pre_mix", lambda b, l=l, src=src: hc.pre_mix(b[src], recs[l], gamma, wl.eps,
+                                                                       out=b["u"])))
+            if args.fused:
+                ops.append(("post_pre_mix", lambda b, l=l, src=src, dst=dst: hc.post_pre_mix(
+                    b[src], b["F"], recs[l], recs[l + 1], gamma, wl.eps, out=b[dst], u_out=b["u"])))
+            else:
+                ops.append(("block_tanh", lambda b: hc.block_tanh(b["u"], out=b["F"])))
+                ops.append(("post_mix", lambda b, l=l, src=src, dst=dst: hc.post_mix(
+                    b[src], b["F"], recs[l], out=b[dst])))
+
     def step(tm: Timer, i: int):
         b = bufs[i % sets]
-        if wl.kind == "static":
-            tm.run("pre_mix", lambda: hc.pre_mix(b["H"], w_static, gamma, wl.eps, out=b["u"]))
-            tm.run("post_mix", lambda: hc.post_mix(b["H"], b["F"], w_static, out=b["O"]))
-        elif wl.kind == "dynamic":
-            tm.run("weights", lambda: hc.weights(b["H"], Wp, ws, wl.scale, wl.eps, 0, out=b["w"]))
-            tm.run("pre_mix", lambda: hc.pre_mix(b["H"], b["w"], gamma, wl.eps, out=b["u"]))
-            tm.run("post_mix", lambda: hc.post_mix(b["H"], b["F"], b["w"], out=b["O"]))
-        elif wl.kind == "mhc":
-            tm.run("sinkhorn", lambda: hc.sinkhorn(b["logits"], n, wl.iters, out=b["w"]))
-            tm.run("pre_mix", lambda: hc.pre_mix(b["H"], b["w"], gamma, wl.eps, out=b["u"]))
-            tm.run("post_mix", lambda: hc.post_mix(b["H"], b["F"], b["w"], out=b["O"]))
-        else:   # chain: H ping-pongs between b["H"] and b["O"]
-            Ha, Hb = b["H"], b["O"]
-            if args.fused:
-                tm.run("pre_mix", lambda: hc.pre_mix(Ha, recs[0], gamma, wl.eps, out=b["u"]))
-                for l in range(wl.layers):
-                    tm.run("block_tanh", lambda: hc.block_tanh(b["u"], out=b["F"]))
-                    tm.run("post_pre_mix", lambda: hc.post_pre_mix(
-                        Ha, b["F"], recs[l], recs[l + 1], gamma, wl.eps, out=Hb, u_out=b["u"]))
-                    Ha, Hb = Hb, Ha
-            else:
-                for l in range(wl.layers):
-                    tm.run("pre_mix", lambda: hc.pre_mix(Ha, recs[l], gamma, wl.eps, out=b["u"]))
-                    tm.run("block_tanh", lambda: hc.block_tanh(b["u"], out=b["F"]))
-                    tm.run("post_mix", lambda: hc.post_mix(Ha, b["F"], recs[l], out=Hb))
-                    Ha, Hb = Hb, Ha
+        for name, fn in ops:
+            tm.run(name, lambda: fn(b))
 
     # -------------------------------------------------------- copy probe
-    cp_n = 512 * 2 ** 20
+    cp_n = COPY_PROBE_BYTES
     src = torch.empty(cp_n // 2, dtype=torch.bfloat16, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -222,26 +317,43 @@ def main():
     log(f"[bench] device copy (512 MiB read + 512 MiB write): {copy_gbps:.0f} GB/s")
 
     # ------------------------------------------------------------- timing
-    tm = Timer(torch)
+    # pass 1: the timed steps, launches back to back (value, ms_per_step)
+    # pass 2: the same steps again with events around every launch (per-kernel
+    #         durations for the roofline; events add gaps between kernels)
+    bare = Timer(torch, per_kernel=False)
     for i in range(args.warmup):
-        step(tm, i)
+        step(bare, i)
     torch.cuda.synchronize()
     log(f"[bench] {args.warmup} warmup steps done")
-    tm.clear()
+    bare.clear()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        step(tm, args.warmup + i)
+        step(bare, args.warmup + i)
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
-    kms = tm.avg_ms()
     log(f"[bench] {args.steps} timed steps: {ms_step * 1e3:.1f} us/step")
 
+    # pass 2: every kernel of the step on its own, `steps` launches back to
+    # back (rotating buffer sets) between one pair of events on the stream
+    kms = {}
+    for name in dict.fromkeys(k for k, _ in ops):
+        fn = next(f for k, f in ops if k == name)
+        fn(bufs[0])
+        torch.cuda.synchronize()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(args.steps):
+            fn(bufs[i % sets])
+        z.record()
+        torch.cuda.synchronize()
+        kms[name] = a.elapsed_time(z) / args.steps
+
     hc_kernels = [k for k in kms if k != "block_tanh"]
-    launches = {k: len(v) // args.steps for k, v in tm.pairs.items()}
+    launches = {k: c // args.steps for k, c in bare.counts.items()}
     step_bytes = sum(launch_bytes[k] * launches[k] for k in hc_kernels)
     kernels = {}
     for k, ms in kms.items():
@@ -276,6 +388,7 @@ def main():
         "hbm_gbps": round(step_gbps, 1),
         "frac_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "copy_gbps": round(copy_gbps, 1),
+        "gaps_us_per_step": round(ms_step * 1e3 - sum(kms[k] * 1e3 * launches[k] for k in kms), 2),
         "kernels": kernels,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),

@@ -84,15 +84,15 @@ int32_t hc_abi_version(void) { return 1; }
 
 hc_status hc_pre_mix(const void* H, const float* w, int64_t w_stride, const float* gamma, float eps,
                      void* u, int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream) {
-    if (!H || !w || !gamma || !u) return HC_ERR_NULL;
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
     const int K = record_len(n);
     if ((st = check_stride(w_stride, K, T)) != HC_OK) return st;
     if (!eps_ok(eps)) return HC_ERR_ARG;
+    if (T == 0) return HC_OK;
+    if (!H || !w || !gamma || !u) return HC_ERR_NULL;
     if (misaligned(H, 16) || misaligned(u, 16) || misaligned(gamma, 16) || misaligned(w, 4))
         return HC_ERR_ALIGN;
-    if (T == 0) return HC_OK;
     const int64_t s = elem_bytes(dt);
     const Span sH{H, T * n * d * s}, sU{u, T * d * s}, sW{w, record_span(T, w_stride, K)},
         sG{gamma, int64_t(d) * 4};
@@ -103,14 +103,14 @@ hc_status hc_pre_mix(const void* H, const float* w, int64_t w_stride, const floa
 
 hc_status hc_post_mix(const void* H, const void* F, const float* w, int64_t w_stride, void* H_out,
                       int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream) {
-    if (!H || !F || !w || !H_out) return HC_ERR_NULL;
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
     const int K = record_len(n);
     if ((st = check_stride(w_stride, K, T)) != HC_OK) return st;
+    if (T == 0) return HC_OK;
+    if (!H || !F || !w || !H_out) return HC_ERR_NULL;
     if (misaligned(H, 16) || misaligned(F, 16) || misaligned(H_out, 16) || misaligned(w, 4))
         return HC_ERR_ALIGN;
-    if (T == 0) return HC_OK;
     const int64_t s = elem_bytes(dt);
     const Span sH{H, T * n * d * s}, sF{F, T * d * s}, sO{H_out, T * n * d * s},
         sW{w, record_span(T, w_stride, K)};
@@ -123,17 +123,17 @@ hc_status hc_post_pre_mix(const void* H, const void* F, const float* w, int64_t 
                           const float* w_next, int64_t w_next_stride, const float* gamma_next,
                           float eps, void* H_out, void* u_next, int64_t T, int32_t n, int32_t d,
                           hc_dtype dt, void* stream) {
-    if (!H || !F || !w || !w_next || !gamma_next || !H_out || !u_next) return HC_ERR_NULL;
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
     const int K = record_len(n);
     if ((st = check_stride(w_stride, K, T)) != HC_OK) return st;
     if ((st = check_stride(w_next_stride, K, T)) != HC_OK) return st;
     if (!eps_ok(eps)) return HC_ERR_ARG;
+    if (T == 0) return HC_OK;
+    if (!H || !F || !w || !w_next || !gamma_next || !H_out || !u_next) return HC_ERR_NULL;
     if (misaligned(H, 16) || misaligned(F, 16) || misaligned(H_out, 16) || misaligned(u_next, 16) ||
         misaligned(gamma_next, 16) || misaligned(w, 4) || misaligned(w_next, 4))
         return HC_ERR_ALIGN;
-    if (T == 0) return HC_OK;
     const int64_t s = elem_bytes(dt);
     const Span sH{H, T * n * d * s}, sF{F, T * d * s}, sO{H_out, T * n * d * s},
         sU{u_next, T * d * s}, sW{w, record_span(T, w_stride, K)},
@@ -150,14 +150,14 @@ hc_status hc_post_pre_mix(const void* H, const void* F, const float* w, int64_t 
 hc_status hc_weights(const void* H, const void* W, const float* w_static, float scale, float eps,
                      int32_t sinkhorn_iters, float* w_out, int64_t T, int32_t n, int32_t d,
                      hc_dtype dt, void* stream) {
-    if (!H || !W || !w_static || !w_out) return HC_ERR_NULL;
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
     if (!eps_ok(eps) || !std::isfinite(scale)) return HC_ERR_ARG;
     if (sinkhorn_iters < 0 || sinkhorn_iters > HC_MAX_SINKHORN_ITERS) return HC_ERR_ARG;
+    if (T == 0) return HC_OK;
+    if (!H || !W || !w_static || !w_out) return HC_ERR_NULL;
     if (misaligned(H, 16) || misaligned(W, 16) || misaligned(w_static, 4) || misaligned(w_out, 4))
         return HC_ERR_ALIGN;
-    if (T == 0) return HC_OK;
     const int K = record_len(n);
     const int64_t s = elem_bytes(dt);
     const Span sH{H, T * n * d * s}, sW{W, int64_t(K) * d * s}, sS{w_static, int64_t(K) * 4},
@@ -169,24 +169,24 @@ hc_status hc_weights(const void* H, const void* W, const float* w_static, float 
 
 hc_status hc_sinkhorn(const float* logits, float* w_out, int32_t iters, int64_t T, int32_t n,
                       void* stream) {
-    if (!logits || !w_out) return HC_ERR_NULL;
     if (n < 1 || n > HC_MAX_STREAMS) return HC_ERR_SHAPE;
     if (T < 0 || iters < 0 || iters > HC_MAX_SINKHORN_ITERS) return HC_ERR_ARG;
     const int K = record_len(n);
     if (T > kMaxBytes / (4 * K)) return HC_ERR_ARG;
-    if (misaligned(logits, 4) || misaligned(w_out, 4)) return HC_ERR_ALIGN;
     if (T == 0) return HC_OK;
+    if (!logits || !w_out) return HC_ERR_NULL;
+    if (misaligned(logits, 4) || misaligned(w_out, 4)) return HC_ERR_ALIGN;
     if (overlap(Span{logits, T * K * 4}, Span{w_out, T * K * 4})) return HC_ERR_ALIAS;
     return from_hip(hc::launch_sinkhorn(logits, w_out, iters, T, n, static_cast<hipStream_t>(stream)));
 }
 
 hc_status hc_block_tanh(const void* u, void* F, int64_t count, hc_dtype dt, void* stream) {
-    if (!u || !F) return HC_ERR_NULL;
     if (!dtype_ok(dt)) return HC_ERR_DTYPE;
     if (count < 0 || count > kMaxBytes / 4) return HC_ERR_ARG;
     if (count % vec_elems(dt) != 0) return HC_ERR_SHAPE;
-    if (misaligned(u, 16) || misaligned(F, 16)) return HC_ERR_ALIGN;
     if (count == 0) return HC_OK;
+    if (!u || !F) return HC_ERR_NULL;
+    if (misaligned(u, 16) || misaligned(F, 16)) return HC_ERR_ALIGN;
     const int64_t bytes = count * elem_bytes(dt);
     if (overlap(Span{u, bytes}, Span{F, bytes})) return HC_ERR_ALIAS;
     return from_hip(hc::launch_block_tanh(u, F, count, dt, static_cast<hipStream_t>(stream)));

@@ -25,13 +25,16 @@ hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
 }
 
 // Row kernels (one workgroup per token row): block size and 16-byte vectors
-// per thread for a row of `nvec` vectors.  Shared by pre, post and the fused
-// post+pre so that their reductions over d run in the same order.
+// per thread for a row of `nvec` vectors.  As few vectors per thread as a
+// 1024-thread block allows (one up to d = 8192 bf16): measured on MI355X, one
+// vector per thread in 512-thread blocks streams faster than two in 256.
+// Shared by pre, post and the fused post+pre so that their reductions over d
+// run in the same order; the order depends on d only.
 struct RowCfg { int block; int vpt; };
 inline RowCfg row_config(int nvec) {
-    if (nvec <= 64) return {64, 1};
-    if (nvec <= 1024) return {256, (nvec + 255) / 256};
-    return {1024, (nvec + 1023) / 1024};
+    const int vpt = (nvec + 1023) / 1024;                    // 1..4 for d <= 16384
+    const int block = ((nvec + vpt - 1) / vpt + 63) / 64 * 64;
+    return {block, vpt};
 }
 
 hipError_t launch_pre_mix(const void* H, const float* w, int64_t w_stride, const float* gamma,

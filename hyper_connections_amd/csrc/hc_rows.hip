@@ -12,9 +12,9 @@
 //
 // Design (HBM-bound, 1.9 flop/byte at n = 4 bf16):
 //  - One workgroup per token row; a thread owns VPT 16-byte vectors of the
-//    row at positions tid, tid + B, ... and the same positions of every
-//    stream, so each wave instruction touches 1 KiB of contiguous memory and
-//    every HBM byte is read or written exactly once.
+//    row at positions tid, tid + B, ... (B = blockDim) and the same positions
+//    of every stream, so each wave instruction touches 1 KiB of contiguous
+//    memory and every HBM byte is read or written exactly once.
 //  - All loads of a row are issued before any arithmetic (n*VPT + VPT
 //    outstanding 16-byte loads per thread) to keep enough bytes in flight.
 //  - The token's weights are wave-uniform and live in scalar registers.
@@ -33,12 +33,13 @@ constexpr int64_t kMaxGrid = 1 << 20;
 
 // ------------------------------------------------------------------- pre
 
-template <int N, typename S, int B, int VPT>
-__global__ __launch_bounds__(B) void pre_mix_kernel(
+template <int N, typename S, int VPT>
+__global__ __launch_bounds__(1024) void pre_mix_kernel(
     const uint8_t* __restrict__ H, const float* __restrict__ w, int64_t w_stride,
     const float* __restrict__ gamma, float eps, uint8_t* __restrict__ u, int64_t T, int d) {
     constexpr int V = Store<S>::kElems;
-    __shared__ float red[B / 64];
+    __shared__ float red[16];
+    const int B = blockDim.x;
     const int nvec = d / V;
     const int64_t row_bytes = (int64_t)d * Store<S>::kBytes;
 
@@ -114,11 +115,12 @@ __global__ __launch_bounds__(B) void pre_mix_kernel(
 
 // H and H_out may be the same buffer: a thread reads every stream at its
 // positions before it writes them, and no other thread touches them.
-template <int N, typename S, int B, int VPT>
-__global__ __launch_bounds__(B) void post_mix_kernel(
+template <int N, typename S, int VPT>
+__global__ __launch_bounds__(1024) void post_mix_kernel(
     const uint8_t* H, const uint8_t* __restrict__ F, const float* __restrict__ w,
     int64_t w_stride, uint8_t* H_out, int64_t T, int d) {
     constexpr int V = Store<S>::kElems;
+    const int B = blockDim.x;
     const int nvec = d / V;
     const int64_t row_bytes = (int64_t)d * Store<S>::kBytes;
 
@@ -177,14 +179,15 @@ __global__ __launch_bounds__(B) void post_mix_kernel(
 // next layer's input is formed from the rounded H_out values exactly as
 // pre_mix_kernel would form it after reading them back, so the fused result
 // is bitwise that of the two separate calls.
-template <int N, typename S, int B, int VPT>
-__global__ __launch_bounds__(B) void post_pre_mix_kernel(
+template <int N, typename S, int VPT>
+__global__ __launch_bounds__(1024) void post_pre_mix_kernel(
     const uint8_t* H, const uint8_t* __restrict__ F, const float* __restrict__ w,
     int64_t w_stride, const float* __restrict__ w_next, int64_t w_next_stride,
     const float* __restrict__ gamma, float eps, uint8_t* H_out, uint8_t* __restrict__ u_next,
     int64_t T, int d) {
     constexpr int V = Store<S>::kElems;
-    __shared__ float red[B / 64];
+    __shared__ float red[16];
+    const int B = blockDim.x;
     const int nvec = d / V;
     const int64_t row_bytes = (int64_t)d * Store<S>::kBytes;
 
@@ -303,41 +306,31 @@ __global__ __launch_bounds__(256) void block_tanh_kernel(const uint8_t* __restri
 inline dim3 row_grid(int64_t T) { return dim3((unsigned)(T < kMaxGrid ? T : kMaxGrid)); }
 
 struct PreL {
-    template <int N, typename S, int B, int VPT, typename... A>
-    static hipError_t go(int64_t T, hipStream_t s, A... a) {
-        return launch(pre_mix_kernel<N, S, B, VPT>, row_grid(T), dim3(B), 0, s, a...);
+    template <int N, typename S, int VPT, typename... A>
+    static hipError_t go(RowCfg c, int64_t T, hipStream_t s, A... a) {
+        return launch(pre_mix_kernel<N, S, VPT>, row_grid(T), dim3(c.block), 0, s, a...);
     }
 };
 struct PostL {
-    template <int N, typename S, int B, int VPT, typename... A>
-    static hipError_t go(int64_t T, hipStream_t s, A... a) {
-        return launch(post_mix_kernel<N, S, B, VPT>, row_grid(T), dim3(B), 0, s, a...);
+    template <int N, typename S, int VPT, typename... A>
+    static hipError_t go(RowCfg c, int64_t T, hipStream_t s, A... a) {
+        return launch(post_mix_kernel<N, S, VPT>, row_grid(T), dim3(c.block), 0, s, a...);
     }
 };
 struct PostPreL {
-    template <int N, typename S, int B, int VPT, typename... A>
-    static hipError_t go(int64_t T, hipStream_t s, A... a) {
-        return launch(post_pre_mix_kernel<N, S, B, VPT>, row_grid(T), dim3(B), 0, s, a...);
+    template <int N, typename S, int VPT, typename... A>
+    static hipError_t go(RowCfg c, int64_t T, hipStream_t s, A... a) {
+        return launch(post_pre_mix_kernel<N, S, VPT>, row_grid(T), dim3(c.block), 0, s, a...);
     }
 };
 
 template <class L, int N, typename S, typename... A>
 hipError_t by_cfg(RowCfg c, int64_t T, hipStream_t s, A... a) {
-    if (c.block == 64) return L::template go<N, S, 64, 1>(T, s, a...);
-    if (c.block == 256) {
-        switch (c.vpt) {
-            case 1: return L::template go<N, S, 256, 1>(T, s, a...);
-            case 2: return L::template go<N, S, 256, 2>(T, s, a...);
-            case 3: return L::template go<N, S, 256, 3>(T, s, a...);
-            case 4: return L::template go<N, S, 256, 4>(T, s, a...);
-        }
-    }
-    if (c.block == 1024) {
-        switch (c.vpt) {
-            case 2: return L::template go<N, S, 1024, 2>(T, s, a...);
-            case 3: return L::template go<N, S, 1024, 3>(T, s, a...);
-            case 4: return L::template go<N, S, 1024, 4>(T, s, a...);
-        }
+    switch (c.vpt) {
+        case 1: return L::template go<N, S, 1>(c, T, s, a...);
+        case 2: return L::template go<N, S, 2>(c, T, s, a...);
+        case 3: return L::template go<N, S, 3>(c, T, s, a...);
+        case 4: return L::template go<N, S, 4>(c, T, s, a...);
     }
     return hipErrorInvalidConfiguration;
 }

@@ -40,8 +40,10 @@
  *    HIP runtime returns HC_ERR_HIP.  No exception crosses the ABI and the
  *    library never prints.
  *  - Sizes: 1 <= n <= 4; 1 <= d <= HC_MAX_HIDDEN; d % 8 == 0 for bf16 and
- *    d % 4 == 0 for fp32 (16-byte vectors) else HC_ERR_SHAPE.  T == 0 is a
- *    no-op returning HC_OK; T < 0 is HC_ERR_ARG.
+ *    d % 4 == 0 for fp32 (16-byte vectors) else HC_ERR_SHAPE.  T < 0 is
+ *    HC_ERR_ARG.  T == 0 (count == 0 for hc_block_tanh) is a no-op returning
+ *    HC_OK once the scalar arguments are valid; the data pointers are then
+ *    not checked and may be NULL (an empty tensor has no storage).
  *  - Alignment: H, F, u, H_out, W and gamma 16 bytes; weight records and
  *    logits 4 bytes (HC_ERR_ALIGN).
  *  - Aliasing: outputs may not overlap any input or each other

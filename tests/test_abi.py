@@ -63,6 +63,8 @@ def post(L, H=P[0], F=P[1], w=P[2], ws=0, O=P[3], T=16, n=4, d=4096, dt=BF16):
 
 def test_pre_validation(L):
     assert pre(L, T=0) == OK                       # empty: no-op, nothing launched
+    assert pre(L, T=0, H=None, u=None) == OK       # empty tensors have no storage
+    assert pre(L, T=0, eps=0.0) == ARG and pre(L, T=0, ws=3) == SHAPE
     assert pre(L, H=None) == NULL and pre(L, u=None) == NULL and pre(L, g=None) == NULL
     assert pre(L, n=0) == SHAPE and pre(L, n=5) == SHAPE
     assert pre(L, d=4092) == SHAPE                 # bf16 needs d % 8 == 0

@@ -1,10 +1,10 @@
 """GPU parity of the streaming kernels (pre, post, fused post+pre, tanh block)
 against the fp64 oracle, through the C ABI.
 
-Cases span every launch shape of the row kernels (64-thread rows, 256-thread
-rows with 1-4 vectors per thread, 1024-thread rows with 2-4), ragged rows
-(d not a multiple of the block's vector count), T = 1 and small odd T, both
-storage dtypes, n = 1..4, shared and per-token weight records."""
+Cases span every launch shape of the row kernels (blocks of 64..1024 threads
+with 1, 2, 3 and 4 vectors per thread), ragged rows (d not a multiple of the
+block's vector count), small odd T, both storage dtypes, n = 1..4, shared and
+per-token weight records."""
 import numpy as np
 import pytest
 import torch
@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 # d values per dtype: covers every (block, vectors-per-thread) launch shape
 D_BF16 = [8, 40, 520, 2048, 4096, 6144, 8192, 8200, 16384]
-D_F32 = [4, 36, 516, 1024, 3072, 4096, 4100, 12288, 16384]
+D_F32 = [4, 36, 516, 1024, 3072, 4096, 4100, 8196, 12288, 12296, 16384]
 SHAPES = [("bf16", d) for d in D_BF16] + [("f32", d) for d in D_F32]
 
 
