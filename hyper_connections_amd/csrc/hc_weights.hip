@@ -39,77 +39,105 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;    // waves per weights workgroup
 constexpr int kLV = 8;         // 16-byte vectors per lane per k-chunk
 constexpr int64_t kMaxGrid = 1 << 20;
 
 // ------------------------------------------------------------ mHC record
 
-// Logit record l (K = 2N + N^2) -> weight record out.  With iters >= 1 the
-// largest logit of A is subtracted before exp; the first row division
-// removes any common factor, so the result is unchanged in exact arithmetic.
+// DPP quad permutes: swap neighbours (1,0,3,2) and pairs (2,3,0,1).
+__device__ __forceinline__ float quad_swap1(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_swap2(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+// Sum / max over the 4 lanes of a quad; every lane gets the same value (each
+// step adds the same two operands on both partners).
+__device__ __forceinline__ float quad_sum(float v) {
+    v += quad_swap1(v);
+    return v + quad_swap2(v);
+}
+__device__ __forceinline__ float quad_max(float v) {
+    v = fmaxf(v, quad_swap1(v));
+    return fmaxf(v, quad_swap2(v));
+}
+
+// The mHC transform of one token, spread over the 4 lanes of a quad: lane r
+// owns alpha_r, beta_r and row r of the n x n mix (lanes r >= N hold zeros
+// and take part only in the column sums).  On entry a, b and row[] are the
+// logits, on exit the weights:
+//   alpha = sigmoid(l_alpha), beta = sigmoid(l_beta),
+//   A = exp(l_A) normalised `iters` times, rows then columns.
+// With iters >= 1 the largest logit of A is subtracted before exp; the first
+// row division removes any common factor, so exact results are unchanged.
+// Must be called by all 4 lanes of the quad (no divergence around DPP).
 template <int N>
-__device__ __forceinline__ void mhc_record(const float* l, float* out, int iters) {
-#pragma unroll
-    for (int i = 0; i < 2 * N; ++i) out[i] = 1.0f / (1.0f + expf(-l[i]));
-    float M[N * N];
+__device__ __forceinline__ void mhc_quad(int r, float& a, float& b, float (&row)[N], int iters) {
+    const bool live = r < N;
+    a = 1.0f / (1.0f + expf(-a));
+    b = 1.0f / (1.0f + expf(-b));
     float m = 0.0f;
     if (iters > 0) {
-        m = l[2 * N];
+        m = live ? row[0] : -INFINITY;
 #pragma unroll
-        for (int e = 1; e < N * N; ++e) m = fmaxf(m, l[2 * N + e]);
+        for (int j = 1; j < N; ++j) m = live ? fmaxf(m, row[j]) : m;
+        m = quad_max(m);
     }
 #pragma unroll
-    for (int e = 0; e < N * N; ++e) M[e] = expf(l[2 * N + e] - m);
+    for (int j = 0; j < N; ++j) row[j] = live ? expf(row[j] - m) : 0.0f;
     for (int it = 0; it < iters; ++it) {
+        float s = row[0];
 #pragma unroll
-        for (int i = 0; i < N; ++i) {
-            float s = M[i * N];
+        for (int j = 1; j < N; ++j) s += row[j];
+        const float sd = live ? s : 1.0f;
 #pragma unroll
-            for (int j = 1; j < N; ++j) s += M[i * N + j];
-#pragma unroll
-            for (int j = 0; j < N; ++j) M[i * N + j] = M[i * N + j] / s;
-        }
+        for (int j = 0; j < N; ++j) row[j] = row[j] / sd;
 #pragma unroll
         for (int j = 0; j < N; ++j) {
-            float s = M[j];
-#pragma unroll
-            for (int i = 1; i < N; ++i) s += M[i * N + j];
-#pragma unroll
-            for (int i = 0; i < N; ++i) M[i * N + j] = M[i * N + j] / s;
+            const float c = quad_sum(row[j]);
+            row[j] = row[j] / c;
         }
     }
-#pragma unroll
-    for (int e = 0; e < N * N; ++e) out[2 * N + e] = M[e];
 }
 
 // --------------------------------------------------------------- sinkhorn
 
-// One thread per token; records staged through LDS so that global traffic is
-// coalesced (records are K floats, K = 3, 8, 15 or 24, not 16-byte multiples).
+// Four lanes per token (lane r owns row r); 64 tokens per 256-thread block.
+// Records are staged through LDS so that global traffic is coalesced (a
+// record is K floats, K = 3, 8, 15 or 24: not a multiple of 16 bytes).
 template <int N>
 __global__ __launch_bounds__(256) void sinkhorn_kernel(const float* __restrict__ logits,
                                                        float* __restrict__ w_out, int iters,
                                                        int64_t T) {
     constexpr int K = 2 * N + N * N;
-    constexpr int KP = K + 1;   // odd pitch: lanes hit distinct banks
-    __shared__ float rec[256 * KP];
-    for (int64_t t0 = (int64_t)blockIdx.x * 256; t0 < T; t0 += (int64_t)gridDim.x * 256) {
-        const int ntok = (int)((T - t0) < 256 ? (T - t0) : 256);
+    constexpr int TB = 64;      // tokens per block
+    __shared__ float rec[TB * K];
+    const int tl = threadIdx.x >> 2, r = threadIdx.x & 3;
+    for (int64_t t0 = (int64_t)blockIdx.x * TB; t0 < T; t0 += (int64_t)gridDim.x * TB) {
+        const int ntok = (int)((T - t0) < TB ? (T - t0) : TB);
         const float* src = logits + t0 * K;
-        for (int e = threadIdx.x; e < ntok * K; e += 256) rec[(e / K) * KP + e % K] = src[e];
+        for (int e = threadIdx.x; e < ntok * K; e += 256) rec[e] = src[e];
         __syncthreads();
-        if ((int)threadIdx.x < ntok) {
-            float l[K], o[K];
+        const bool mine = tl < ntok && r < N;
+        float a = 0.0f, b = 0.0f, row[N];
+        if (mine) {
+            a = rec[tl * K + r];
+            b = rec[tl * K + N + r];
+        }
 #pragma unroll
-            for (int c = 0; c < K; ++c) l[c] = rec[threadIdx.x * KP + c];
-            mhc_record<N>(l, o, iters);
+        for (int j = 0; j < N; ++j) row[j] = mine ? rec[tl * K + 2 * N + r * N + j] : 0.0f;
+        mhc_quad<N>(r, a, b, row, iters);
+        __syncthreads();
+        if (mine) {
+            rec[tl * K + r] = a;
+            rec[tl * K + N + r] = b;
 #pragma unroll
-            for (int c = 0; c < K; ++c) rec[threadIdx.x * KP + c] = o[c];
+            for (int j = 0; j < N; ++j) rec[tl * K + 2 * N + r * N + j] = row[j];
         }
         __syncthreads();
         float* dst = w_out + t0 * K;
-        for (int e = threadIdx.x; e < ntok * K; e += 256) dst[e] = rec[(e / K) * KP + e % K];
+        for (int e = threadIdx.x; e < ntok * K; e += 256) dst[e] = rec[e];
         __syncthreads();
     }
 }
@@ -135,6 +163,8 @@ template <> struct Mfma<f32_t> {
     }
 };
 
+constexpr int kWThreads = kWaves * 64;
+
 template <int N, typename S>
 struct WeightsGeom {
     static constexpr int K = 2 * N + N * N;           // outputs per token
@@ -150,7 +180,7 @@ struct WeightsGeom {
 };
 
 template <int N, typename S>
-__global__ __launch_bounds__(256) void weights_kernel(
+__global__ __launch_bounds__(kWThreads) void weights_kernel(
     const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, const float* __restrict__ w_static,
     float scale, float eps, int iters, float* __restrict__ w_out, int64_t T, int d) {
     using G = WeightsGeom<N, S>;
@@ -166,7 +196,7 @@ __global__ __launch_bounds__(256) void weights_kernel(
     const int tok_per_block = kWaves * TPW;
 
     // zero the padding rows (>= K) of the W tile once; chunks never write them
-    for (int p = threadIdx.x; p < (NT * 16 - K) * G::PIECES; p += 256) {
+    for (int p = threadIdx.x; p < (NT * 16 - K) * G::PIECES; p += kWThreads) {
         const int r = K + p / G::PIECES, c = p % G::PIECES;
         *reinterpret_cast<uint4*>(wlds + r * G::RS + c * 16) = make_uint4(0, 0, 0, 0);
     }
@@ -193,7 +223,7 @@ __global__ __launch_bounds__(256) void weights_kernel(
             }
             // W chunk -> LDS (rows < K; zero past d)
             __syncthreads();   // previous chunk's readers are done
-            for (int p = threadIdx.x; p < K * G::PIECES; p += 256) {
+            for (int p = threadIdx.x; p < K * G::PIECES; p += kWThreads) {
                 const int r = p / G::PIECES, pc = p % G::PIECES;
                 const int k = k0 + pc * (16 / SB);
                 uint4 v = k < d ? ld16(W + ((int64_t)r * d + k) * SB) : make_uint4(0, 0, 0, 0);
@@ -244,13 +274,23 @@ __global__ __launch_bounds__(256) void weights_kernel(
         }
         if (iters > 0) {
             __syncthreads();
-            if (lane < TPW && tok0 + lane < T) {
-                float l[K], out[K];
+            // four lanes per token, lane r owns row r (TPW * 4 <= 64)
+            const int tl = lane >> 2, r = lane & 3;
+            const bool mine = tl < TPW && tok0 + tl < T && r < N;
+            float a = 0.0f, bb = 0.0f, row[N];
+            if (mine) {
+                a = ls[tl * K + r];
+                bb = ls[tl * K + N + r];
+            }
 #pragma unroll
-                for (int col = 0; col < K; ++col) l[col] = ls[lane * K + col];
-                mhc_record<N>(l, out, iters);
+            for (int j = 0; j < N; ++j) row[j] = mine ? ls[tl * K + 2 * N + r * N + j] : 0.0f;
+            mhc_quad<N>(r, a, bb, row, iters);
+            if (mine) {
+                float* o = w_out + (tok0 + tl) * K;
+                o[r] = a;
+                o[N + r] = bb;
 #pragma unroll
-                for (int col = 0; col < K; ++col) w_out[(tok0 + lane) * K + col] = out[col];
+                for (int j = 0; j < N; ++j) o[2 * N + r * N + j] = row[j];
             }
         }
         __syncthreads();
@@ -261,7 +301,7 @@ __global__ __launch_bounds__(256) void weights_kernel(
 
 hipError_t launch_sinkhorn(const float* logits, float* w_out, int iters, int64_t T, int n,
                            hipStream_t s) {
-    const int64_t blocks = (T + 255) / 256;
+    const int64_t blocks = (T + 63) / 64;
     const dim3 grid((unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid));
     switch (n) {
         case 1: return launch(sinkhorn_kernel<1>, grid, dim3(256), 0, s, logits, w_out, iters, T);
@@ -279,7 +319,7 @@ hipError_t weights_go(const void* H, const void* W, const float* w_static, float
     const int64_t per_block = kWaves * WeightsGeom<N, S>::TPW;
     const int64_t blocks = (T + per_block - 1) / per_block;
     const dim3 grid((unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid));
-    return launch(weights_kernel<N, S>, grid, dim3(256), 0, s, static_cast<const uint8_t*>(H),
+    return launch(weights_kernel<N, S>, grid, dim3(kWThreads), 0, s, static_cast<const uint8_t*>(H),
                   static_cast<const uint8_t*>(W), w_static, scale, eps, iters, w_out, T, d);
 }
 template <typename S>
