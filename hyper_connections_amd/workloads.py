@@ -30,7 +30,12 @@ static-bf16         8192   4  4096  bf16   static identity + N(0, 0.05)
 dynamic-bf16        16384  4  4096  bf16   per token: W ~ N(0, 0.02), scale 0.01
 mhc-bf16            32768  4  4096  bf16   per token logits ~ N(0, 1), 20 iters
 chain-bf16 (x78)    4096   4  6144  bf16   per layer identity + N(0, 0.02)
+decode-bf16 (x78)   64     4  8192  bf16   per layer identity + N(0, 0.02)
 ==================  =====  =  ====  =====  =====================================
+
+The decode workload is the explainer's worked shape (section "What four
+streams cost per token"): 64 tokens in flight, hidden width 8192, four
+streams, about 4 MB of residual state.
 """
 from __future__ import annotations
 
@@ -80,6 +85,8 @@ WORKLOADS = {
                  proj_sd=0.02, scale=0.01),
         Workload("mhc-bf16", 32768, 4, 4096, "bf16", 404, "mhc", gamma_sd=0.1, iters=20),
         Workload("chain-bf16", 4096, 4, 6144, "bf16", 505, "chain", weight_sd=0.02, layers=78,
+                 F_kind="tanh"),
+        Workload("decode-bf16", 64, 4, 8192, "bf16", 606, "chain", weight_sd=0.02, layers=78,
                  F_kind="tanh"),
     ]
 }
