@@ -9,7 +9,9 @@ from .oracle import (  # noqa: F401
     get_threads,
     load,
     post_mix,
+    post_mix_backward,
     pre_mix,
+    pre_mix_backward,
     round_bf16,
     round_f32,
     set_threads,

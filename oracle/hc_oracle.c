@@ -297,3 +297,99 @@ void orc_block_tanh(const void* u, int dt, double* F, int64_t count)
 #pragma omp parallel for schedule(static)
     for (int64_t e = 0; e < count; ++e) F[e] = tanh(orc_load(u, e, dt));
 }
+
+/* ------------------------------------------------------------ backward */
+
+/* Gradients of the post step H'_i = sum_j A[i][j] H_j + beta_i F, given dHo =
+ * dL/dH' (chain rule on a linear map):
+ *   dH_j = sum_i A[i][j] dHo_i        dF = sum_i beta_i dHo_i
+ *   dA[i][j] = sum_k dHo_ik H_jk      dbeta_i = sum_k dHo_ik F_k
+ * dw receives one gradient record per token in the weight-record layout
+ * [dalpha | dbeta | dA]; dalpha is 0 (post does not read alpha).
+ *   dHo, H [T][n][d], F [T][d] storage dt; dH [T][n][d], dF [T][d], dw [T][K]. */
+void orc_post_mix_backward(const void* dHo, const void* H, const void* F, int dt,
+                           const double* w, int64_t w_stride, double* dH, double* dF,
+                           double* dw, int64_t T, int n, int d)
+{
+    const int K = 2 * n + n * n;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const double* rec = w + t * w_stride;
+        const double* beta = rec + n;
+        const double* A = rec + 2 * n;
+        const int64_t row0 = t * (int64_t)n * d;
+        double* g = dw + t * K;
+        for (int c = 0; c < K; ++c) g[c] = 0.0;
+        for (int k = 0; k < d; ++k) {
+            const double f = orc_load(F, t * (int64_t)d + k, dt);
+            double df = 0.0;
+            for (int i = 0; i < n; ++i) {
+                const double go = orc_load(dHo, row0 + (int64_t)i * d + k, dt);
+                df += beta[i] * go;
+                g[n + i] += go * f;
+                for (int j = 0; j < n; ++j)
+                    g[2 * n + i * n + j] += go * orc_load(H, row0 + (int64_t)j * d + k, dt);
+            }
+            dF[t * (int64_t)d + k] = df;
+            for (int j = 0; j < n; ++j) {
+                double s = 0.0;
+                for (int i = 0; i < n; ++i)
+                    s += A[i * n + j] * orc_load(dHo, row0 + (int64_t)i * d + k, dt);
+                dH[row0 + (int64_t)j * d + k] = s;
+            }
+        }
+    }
+}
+
+/* Gradients of the pre step u = gamma * x * r, r = 1/sqrt(mean_k x_k^2 + eps),
+ * x = sum_i alpha_i H_i, given du = dL/du:
+ *   dy = gamma * du;  dx = r * (dy - x * r^2 * (sum_k dy_k x_k) / d)
+ *   dH_i = alpha_i dx;  dalpha_i = sum_k dx_k H_ik;  dgamma_k = sum_t du_k x_k r
+ * (the derivative of the root-mean-square normalisation written out).
+ * dH_in (may be NULL) is added to dH: a layer's H feeds both pre and post.
+ *   du [T][d], H [T][n][d] storage dt; dH [T][n][d], dw [T][K] (only dalpha
+ *   nonzero), dgamma [d] (summed over tokens). */
+void orc_pre_mix_backward(const void* du, const void* H, int dt, const double* w,
+                          int64_t w_stride, const double* gamma, double eps,
+                          const double* dH_in, double* dH, double* dw, double* dgamma,
+                          int64_t T, int n, int d)
+{
+    const int K = 2 * n + n * n;
+    for (int k = 0; k < d; ++k) dgamma[k] = 0.0;
+    for (int64_t t = 0; t < T; ++t) {   /* serial: dgamma sums over tokens in order */
+        const double* alpha = w + t * w_stride;
+        const int64_t row0 = t * (int64_t)n * d;
+        double* x = (double*)malloc((size_t)d * sizeof(double));
+        double* dx = (double*)malloc((size_t)d * sizeof(double));
+        double ss = 0.0, sdx = 0.0;
+        for (int k = 0; k < d; ++k) {
+            double v = alpha[0] * orc_load(H, row0 + k, dt);
+            for (int i = 1; i < n; ++i) v += alpha[i] * orc_load(H, row0 + (int64_t)i * d + k, dt);
+            x[k] = v;
+            ss += v * v;
+        }
+        const double r = 1.0 / sqrt(ss / d + eps);
+        for (int k = 0; k < d; ++k) {
+            const double g = orc_load(du, t * (int64_t)d + k, dt);
+            sdx += gamma[k] * g * x[k];
+            dgamma[k] += g * x[k] * r;
+        }
+        for (int k = 0; k < d; ++k) {
+            const double dy = gamma[k] * orc_load(du, t * (int64_t)d + k, dt);
+            dx[k] = r * (dy - x[k] * r * r * sdx / d);
+        }
+        double* g = dw + t * K;
+        for (int c = 0; c < K; ++c) g[c] = 0.0;
+        for (int i = 0; i < n; ++i) {
+            double s = 0.0;
+            for (int k = 0; k < d; ++k) {
+                const int64_t e = row0 + (int64_t)i * d + k;
+                s += dx[k] * orc_load(H, e, dt);
+                dH[e] = alpha[i] * dx[k] + (dH_in ? dH_in[e] : 0.0);
+            }
+            g[i] = s;
+        }
+        free(x);
+        free(dx);
+    }
+}

@@ -60,11 +60,14 @@ def load():
     lib.orc_round_bf16_array.argtypes = [dp, ctypes.POINTER(ctypes.c_uint16), i64]
     lib.orc_round_f32_array.argtypes = [dp, ctypes.POINTER(ctypes.c_float), i64]
     lib.orc_widen_array.argtypes = [vp, i32, dp, i64]
+    lib.orc_post_mix_backward.argtypes = [vp, vp, vp, i32, dp, i64, dp, dp, dp, i64, i32, i32]
+    lib.orc_pre_mix_backward.argtypes = [vp, vp, i32, dp, i64, dp, dbl, dp, dp, dp, dp, i64, i32, i32]
     lib.orc_round_bf16.argtypes = [dbl]
     lib.orc_round_bf16.restype = ctypes.c_uint16
     lib.orc_set_threads.argtypes = [i32]
     lib.orc_get_threads.restype = i32
     for f in ("orc_pre_mix", "orc_post_mix", "orc_weights", "orc_sinkhorn",
+              "orc_post_mix_backward", "orc_pre_mix_backward",
               "orc_block_tanh", "orc_round_bf16_array", "orc_round_f32_array",
               "orc_widen_array", "orc_set_threads"):
         getattr(lib, f).restype = None
@@ -197,3 +200,45 @@ def widen(x: np.ndarray) -> np.ndarray:
     out = np.empty(x.shape, np.float64)
     lib.orc_widen_array(x.ctypes.data, _dt(x), _dp(out), x.size)
     return out
+
+
+def post_mix_backward(dHo: np.ndarray, H: np.ndarray, F: np.ndarray, w: np.ndarray):
+    """Gradients of post given dL/dH': returns (dH, dF, dw) in float64; dw is
+    one gradient record per token [dalpha (0) | dbeta | dA]."""
+    lib = load()
+    dHo, H, F = _c(dHo), _c(H), _c(F)
+    T, n, d = H.shape
+    assert dHo.shape == H.shape and F.shape == (T, d) and dHo.dtype == H.dtype == F.dtype
+    K = 2 * n + n * n
+    w, ws = _record(w, T, K)
+    dH = np.empty((T, n, d), np.float64)
+    dF = np.empty((T, d), np.float64)
+    dw = np.empty((T, K), np.float64)
+    lib.orc_post_mix_backward(dHo.ctypes.data, H.ctypes.data, F.ctypes.data, _dt(H), _dp(w), ws,
+                              _dp(dH), _dp(dF), _dp(dw), T, n, d)
+    return dH, dF, dw
+
+
+def pre_mix_backward(du: np.ndarray, H: np.ndarray, w: np.ndarray, gamma: np.ndarray,
+                     eps: float = 1e-6, dH_in: np.ndarray | None = None):
+    """Gradients of pre given dL/du: returns (dH, dw, dgamma) in float64; dH
+    includes dH_in when given; dw is one record per token [dalpha | 0 | 0];
+    dgamma is summed over tokens."""
+    lib = load()
+    du, H = _c(du), _c(H)
+    T, n, d = H.shape
+    assert du.shape == (T, d) and du.dtype == H.dtype
+    K = 2 * n + n * n
+    w, ws = _record(w, T, K)
+    gamma = _c(gamma, np.float64)
+    dH = np.empty((T, n, d), np.float64)
+    dw = np.empty((T, K), np.float64)
+    dg = np.empty(d, np.float64)
+    acc = None
+    if dH_in is not None:
+        acc = _c(dH_in, np.float64)
+        assert acc.shape == (T, n, d)
+    lib.orc_pre_mix_backward(du.ctypes.data, H.ctypes.data, _dt(H), _dp(w), ws, _dp(gamma),
+                             float(eps), _dp(acc) if acc is not None else None, _dp(dH), _dp(dw),
+                             _dp(dg), T, n, d)
+    return dH, dw, dg

@@ -14,7 +14,7 @@ SRC = os.path.join(ROOT, "oracle", "hc_oracle.c")
 
 PIN_TESTS = [os.path.join(ROOT, "tests", f) for f in (
     "test_oracle_storage.py", "test_oracle_pre.py", "test_oracle_post.py",
-    "test_oracle_weights.py", "test_oracle_sinkhorn.py")]
+    "test_oracle_weights.py", "test_oracle_sinkhorn.py", "test_oracle_backward.py")]
 
 MUTANTS = {
     "post: A transposed": ("y += A[i * n + j] * orc_load", "y += A[j * n + i] * orc_load"),
@@ -36,6 +36,13 @@ MUTANTS = {
     "sinkhorn: beta from alpha logits": ("out[n + i] = orc_sigmoid(l[n + i]);", "out[n + i] = orc_sigmoid(l[i]);"),
     "storage: truncating bf16": ("double m = rint(ldexp(a, -q));", "double m = floor(ldexp(a, -q));"),
     "block: tanh replaced": ("F[e] = tanh(orc_load(u, e, dt));", "F[e] = sin(orc_load(u, e, dt));"),
+    "post bwd: dH not transposed": ("s += A[i * n + j] * orc_load(dHo", "s += A[j * n + i] * orc_load(dHo"),
+    "post bwd: dbeta from H": ("g[n + i] += go * f;", "g[n + i] += go;"),
+    "post bwd: dF unweighted": ("df += beta[i] * go;", "df += go;"),
+    "pre bwd: no projection term": ("dx[k] = r * (dy - x[k] * r * r * sdx / d);", "dx[k] = r * dy;"),
+    "pre bwd: dgamma missing r": ("dgamma[k] += g * x[k] * r;", "dgamma[k] += g * x[k];"),
+    "pre bwd: dalpha from x": ("s += dx[k] * orc_load(H, e, dt);", "s += dx[k];"),
+    "pre bwd: accumulation dropped": ("dH[e] = alpha[i] * dx[k] + (dH_in ? dH_in[e] : 0.0);", "dH[e] = alpha[i] * dx[k];"),
     "storage: no subnormal range": ("int q = (e - 1 >= -126) ? e - 8 : -133;", "int q = e - 8;"),
 }
 
