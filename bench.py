@@ -41,6 +41,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "pre_mix": "hc_rows.hip", "post_mix": "hc_rows.hip", "post_pre_mix": "hc_rows.hip",
     "block_tanh": "hc_rows.hip", "weights": "hc_weights.hip", "sinkhorn": "hc_weights.hip",
+    "post_mix_backward": "hc_backward.hip", "pre_mix_backward": "hc_backward.hip",
+    "sum_records": "hc_backward.hip",
 }
 
 
@@ -186,6 +188,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--fused", action="store_true",
                     help="chain: fuse each write-back with the next read-mix")
+    ap.add_argument("--backward", action="store_true",
+                    help="static workload: time the layer's gradients (post backward, pre "
+                         "backward accumulating into the same dH, shared-weight sums)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph (torch.cuda.CUDAGraph) and time replays")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -274,10 +279,38 @@ def main():
         "weights": traffic.weights_bytes(n, d, s) * T,
         "sinkhorn": traffic.sinkhorn_bytes(n) * T,
         "block_tanh": 2 * d * s * T,
+        "post_mix_backward": traffic.post_bwd_bytes(n, d, s) * T,
+        "pre_mix_backward": traffic.pre_bwd_bytes(n, d, s, True) * T,
     }
 
+    if args.backward:
+        if wl.kind != "static":
+            raise SystemExit("--backward is defined for the static workloads")
+        rng = np.random.default_rng(wl.seed + 1)
+        G0 = dev(workloads.to_storage(rng.standard_normal((T, n, d), dtype=np.float32), wl.dtype))
+        du0 = dev(workloads.to_storage(rng.standard_normal((T, d), dtype=np.float32), wl.dtype))
+        ws_bytes = hc.backward_workspace(T, n, d)
+        for i, b in enumerate(bufs):
+            b["G"] = G0 if i == 0 else G0.clone()
+            b["du"] = du0 if i == 0 else du0.clone()
+            b["dF"] = torch.empty((T, d), dtype=H0.dtype, device="cuda")
+            b["dwp"] = torch.empty(K, dtype=torch.float32, device="cuda")
+            b["dwq"] = torch.empty(K, dtype=torch.float32, device="cuda")
+            b["dg"] = torch.empty(d, dtype=torch.float32, device="cuda")
+            b["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+
+        def post_bwd(b):
+            # dH lands in b["O"]; the pre backward then accumulates into it
+            hc.post_mix_backward(b["G"], b["H"], b["F"], w_static, dH=b["O"], dF=b["dF"],
+                                 dw=b["dwp"], workspace=b["ws"])
+
+        def pre_bwd(b):
+            hc.pre_mix_backward(b["du"], b["H"], w_static, gamma, wl.eps, dH_in=b["O"],
+                                out=b["O"], dw=b["dwq"], dgamma=b["dg"], workspace=b["ws"])
+
+        ops = [("post_mix_backward", post_bwd), ("pre_mix_backward", pre_bwd)]
     # the kernels of one step, in order: (name, launch on buffer set b)
-    if wl.kind == "static":
+    elif wl.kind == "static":
         ops = [("pre_mix", lambda b: hc.pre_mix(b["H"], w_static, gamma, wl.eps, out=b["u"])),
                ("post_mix", lambda b: hc.post_mix(b["H"], b["F"], w_static, out=b["O"]))]
     elif wl.kind == "dynamic":
@@ -412,7 +445,7 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs, identity-init weights + noise)",
         "config": {"workload": wl.name, "T": T, "n": n, "d": d, "weights": wl.kind,
                    "layers": wl.layers, "buffer_sets": sets, "fused": bool(args.fused),
-                   "graph": bool(args.graph)},
+                   "graph": bool(args.graph), "backward": bool(args.backward)},
         "us_per_layer": round(ms_step * 1e3 / wl.layers, 3),
         "hbm_gbps": round(step_gbps, 1),
         "frac_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),

@@ -180,6 +180,90 @@ hc_status hc_sinkhorn(const float* logits, float* w_out, int32_t iters, int64_t 
     return from_hip(hc::launch_sinkhorn(logits, w_out, iters, T, n, static_cast<hipStream_t>(stream)));
 }
 
+int64_t hc_backward_workspace(int64_t T, int32_t n, int32_t d) {
+    if (n < 1 || n > HC_MAX_STREAMS || d < 1 || d > HC_MAX_HIDDEN) return 0;
+    return hc::backward_workspace_bytes(T, n, d);
+}
+
+hc_status hc_post_mix_backward(const void* dH_out, const void* H, const void* F, const float* w,
+                               int64_t w_stride, void* dH, void* dF, float* dw, void* workspace,
+                               int64_t workspace_bytes, int64_t T, int32_t n, int32_t d,
+                               hc_dtype dt, void* stream) {
+    hc_status st = check_nd(n, d, T, dt);
+    if (st != HC_OK) return st;
+    const int K = record_len(n);
+    if ((st = check_stride(w_stride, K, T)) != HC_OK) return st;
+    if (T == 0) return HC_OK;
+    if (!dH_out || !H || !F || !w || !dH || !dF || !dw) return HC_ERR_NULL;
+    const bool shared = w_stride == 0;
+    if (shared && !workspace) return HC_ERR_NULL;
+    if (shared && workspace_bytes < hc_backward_workspace(T, n, d)) return HC_ERR_ARG;
+    if (misaligned(dH_out, 16) || misaligned(H, 16) || misaligned(F, 16) || misaligned(dH, 16) ||
+        misaligned(dF, 16) || misaligned(w, 4) || misaligned(dw, 4) ||
+        (shared && misaligned(workspace, 16)))
+        return HC_ERR_ALIGN;
+    const int64_t s = elem_bytes(dt);
+    const Span sG{dH_out, T * n * d * s}, sH{H, T * n * d * s}, sF{F, T * d * s},
+        sW{w, record_span(T, w_stride, K)}, sdH{dH, T * n * d * s}, sdF{dF, T * d * s},
+        sdw{dw, (shared ? 1 : T) * K * 4},
+        sws{workspace, shared ? hc_backward_workspace(T, n, d) : 0};
+    const Span ins[] = {sG, sH, sF, sW};
+    for (const Span& o : {sdH, sdF, sdw, sws})
+        for (const Span& i : ins)
+            if (overlap(o, i)) return HC_ERR_ALIAS;
+    if (overlap(sdH, sdF) || overlap(sdH, sdw) || overlap(sdF, sdw) || overlap(sws, sdH) ||
+        overlap(sws, sdF) || overlap(sws, sdw))
+        return HC_ERR_ALIAS;
+    return from_hip(hc::launch_post_mix_backward(dH_out, H, F, w, w_stride, dH, dF, dw, workspace,
+                                                 T, n, d, dt, static_cast<hipStream_t>(stream)));
+}
+
+hc_status hc_pre_mix_backward(const void* du, const void* H, const float* w, int64_t w_stride,
+                              const float* gamma, float eps, const void* dH_in, void* dH,
+                              float* dw, float* dgamma, void* workspace, int64_t workspace_bytes,
+                              int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream) {
+    hc_status st = check_nd(n, d, T, dt);
+    if (st != HC_OK) return st;
+    const int K = record_len(n);
+    if ((st = check_stride(w_stride, K, T)) != HC_OK) return st;
+    if (!eps_ok(eps)) return HC_ERR_ARG;
+    if (T == 0) return HC_OK;
+    if (!du || !H || !w || !gamma || !dH || !dw || !dgamma || !workspace) return HC_ERR_NULL;
+    if (workspace_bytes < hc_backward_workspace(T, n, d)) return HC_ERR_ARG;
+    if (misaligned(du, 16) || misaligned(H, 16) || misaligned(gamma, 16) || misaligned(dH, 16) ||
+        misaligned(dH_in, 16) || misaligned(workspace, 16) || misaligned(w, 4) ||
+        misaligned(dw, 4) || misaligned(dgamma, 4))
+        return HC_ERR_ALIGN;
+    const int64_t s = elem_bytes(dt);
+    const bool shared = w_stride == 0;
+    const Span su{du, T * d * s}, sH{H, T * n * d * s}, sW{w, record_span(T, w_stride, K)},
+        sg{gamma, int64_t(d) * 4}, sin{dH_in, dH_in ? T * n * d * s : 0}, sdH{dH, T * n * d * s},
+        sdw{dw, (shared ? 1 : T) * K * 4}, sdg{dgamma, int64_t(d) * 4},
+        sws{workspace, hc_backward_workspace(T, n, d)};
+    const Span ins[] = {su, sH, sW, sg};
+    for (const Span& o : {sdH, sdw, sdg, sws})
+        for (const Span& i : ins)
+            if (overlap(o, i)) return HC_ERR_ALIAS;
+    if (dH_in && dH_in != dH && overlap(sdH, sin)) return HC_ERR_ALIAS;
+    for (const Span& o : {sdw, sdg, sws})
+        if (overlap(o, sin)) return HC_ERR_ALIAS;
+    if (overlap(sdH, sdw) || overlap(sdH, sdg) || overlap(sdH, sws) || overlap(sdw, sdg) ||
+        overlap(sdw, sws) || overlap(sdg, sws))
+        return HC_ERR_ALIAS;
+    return from_hip(hc::launch_pre_mix_backward(du, H, w, w_stride, gamma, eps, dH_in, dH, dw,
+                                                dgamma, workspace, T, n, d, dt,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+hc_status hc_sum_records(const float* rec, int64_t T, int32_t K, float* out, void* stream) {
+    if (K < 1 || K > 1024) return HC_ERR_SHAPE;
+    if (T < 0 || T > kMaxBytes / 4 / K) return HC_ERR_ARG;
+    if (!rec || !out) return HC_ERR_NULL;
+    if (misaligned(rec, 4) || misaligned(out, 4)) return HC_ERR_ALIGN;
+    if (overlap(Span{rec, T * K * 4}, Span{out, int64_t(K) * 4})) return HC_ERR_ALIAS;
+    return from_hip(hc::launch_sum_records(rec, T, K, out, static_cast<hipStream_t>(stream)));
+}
+
 hc_status hc_block_tanh(const void* u, void* F, int64_t count, hc_dtype dt, void* stream) {
     if (!dtype_ok(dt)) return HC_ERR_DTYPE;
     if (count < 0 || count > kMaxBytes / 4) return HC_ERR_ARG;

@@ -1,0 +1,540 @@
+// hc_backward.hip -- gradients of the Hyper-Connections residual path: the
+// write-back (post) and the read-mix + RMSNorm (pre), and the deterministic
+// sums that turn per-block partial gradients into gradients of shared
+// parameters.
+//
+// Sources: hfviewer.com glossary "Hyper-connections (mHC)", definition (the
+// mixing before and after the block is learned, so its weights need
+// gradients; "richer gradient routing than one shared residual");
+// learnaivisually.com "Tencent open-sources Hy4 Preview at 770B -- Identity
+// Hyper-Connections", section "Jargon", Residual connection (gradients take
+// the short path back through the residual).
+//
+// Post:  H'_i = sum_j A[i][j] H_j + beta_i F is linear, so
+//   dH_j = sum_i A[i][j] dH'_i,  dF = sum_i beta_i dH'_i,
+//   dA[i][j] = sum_k dH'_ik H_jk,  dbeta_i = sum_k dH'_ik F_k.
+// Pre:   u = gamma * x * r, r = (mean x^2 + eps)^(-1/2), x = sum_i alpha_i H_i:
+//   dy = gamma * du,  dx = r * (dy - x * r^2 * mean(dy * x)),
+//   dH_i = alpha_i dx,  dalpha_i = sum_k dx_k H_ik,  dgamma = sum_t du x r.
+//
+// Weight gradients take the shape of the weights: one record per token for
+// per-token weights (a block reduction per token), one record in total for
+// shared weights.  Shared-record gradients and dgamma are summed over the
+// tokens of a block in registers, written once per block to the caller's
+// workspace, and summed over blocks by sum_rows_kernel in a fixed order
+// (two levels), so every result is deterministic.
+//
+// Both kernels stream rows like the forward ones (one 16-byte vector per
+// thread per stream, all loads of a token issued first).
+#include "hc_device.h"
+#include "hc_launch.h"
+
+namespace hc {
+
+namespace {
+
+constexpr int64_t kMaxGridB = 1 << 20;
+constexpr int kSumRows = 64;            // rows summed per block in sum_rows_kernel
+
+// Sum M values over the block at once; every thread gets all M sums.  `red`
+// holds 16 * M floats.
+template <int M>
+__device__ __forceinline__ void block_sum_vec(float (&v)[M], float* red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        v[m] = wave_sum(v[m]);
+        if (lane == 0) red[wave * M + m] = v[m];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        float s = red[m];
+        for (int w = 1; w < nw; ++w) s += red[w * M + m];
+        v[m] = s;
+    }
+    __syncthreads();
+}
+
+// Tokens per block for shared-record gradients: enough blocks to fill the
+// chip several times over, at least 8 tokens each.
+inline int64_t group_of(int64_t T) {
+    const int64_t g = T / 2048;
+    return g < 8 ? 8 : g;
+}
+
+// ------------------------------------------------------------ post backward
+
+// PER_TOKEN: dw is [T][K], one block reduction per token.  Otherwise the
+// block's tokens are summed in registers and one partial record per block
+// goes to part[blk][M] (M = n + n^2: dbeta then dA).
+template <int N, typename S, int VPT, bool PER_TOKEN>
+__global__ __launch_bounds__(1024) void post_bwd_kernel(
+    const uint8_t* __restrict__ dHo, const uint8_t* __restrict__ H, const uint8_t* __restrict__ F,
+    const float* __restrict__ w, int64_t w_stride, uint8_t* __restrict__ dH,
+    uint8_t* __restrict__ dF, float* __restrict__ dw, float* __restrict__ part, int64_t T, int d,
+    int group) {
+    constexpr int V = Store<S>::kElems;
+    constexpr int K = 2 * N + N * N;
+    constexpr int M = N + N * N;            // dbeta, dA
+    __shared__ float red[16 * M];
+    const int B = blockDim.x;
+    const int nvec = d / V;
+    const int64_t row_bytes = (int64_t)d * Store<S>::kBytes;
+
+    for (int64_t blk = blockIdx.x; blk * group < T; blk += gridDim.x) {
+        float acc[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+        const int64_t t_end = (blk + 1) * group < T ? (blk + 1) * group : T;
+        for (int64_t t = blk * group; t < t_end; ++t) {
+            const float* rec = w + t * w_stride;
+            float beta[N], A[N][N];
+#pragma unroll
+            for (int i = 0; i < N; ++i) beta[i] = rec[N + i];
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+#pragma unroll
+                for (int j = 0; j < N; ++j) A[i][j] = rec[2 * N + i * N + j];
+
+            const int64_t r0 = t * N * row_bytes;
+            uint4 rg[N][VPT], rh[N][VPT], rf[VPT];
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+                const int v = threadIdx.x + j * B;
+                if (v < nvec) {
+#pragma unroll
+                    for (int i = 0; i < N; ++i) {
+                        rg[i][j] = ld16_stream(dHo + r0 + i * row_bytes + v * 16);
+                        rh[i][j] = ld16_stream(H + r0 + i * row_bytes + v * 16);
+                    }
+                    rf[j] = ld16_stream(F + t * row_bytes + v * 16);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+                const int v = threadIdx.x + j * B;
+                if (v < nvec) {
+                    float g[N][V], f[V];
+#pragma unroll
+                    for (int i = 0; i < N; ++i) unpack<S>(rg[i][j], g[i]);
+                    unpack<S>(rf[j], f);
+                    // dH_j = sum_i A[i][j] dH'_i
+#pragma unroll
+                    for (int jj = 0; jj < N; ++jj) {
+                        float o[V];
+#pragma unroll
+                        for (int e = 0; e < V; ++e) {
+                            float s = A[0][jj] * g[0][e];
+#pragma unroll
+                            for (int i = 1; i < N; ++i) s = fmaf(A[i][jj], g[i][e], s);
+                            o[e] = s;
+                        }
+                        st16_stream(dH + r0 + jj * row_bytes + v * 16, pack<S>(o));
+                    }
+                    // dF = sum_i beta_i dH'_i
+                    float o[V];
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        float s = beta[0] * g[0][e];
+#pragma unroll
+                        for (int i = 1; i < N; ++i) s = fmaf(beta[i], g[i][e], s);
+                        o[e] = s;
+                    }
+                    st16_stream(dF + t * row_bytes + v * 16, pack<S>(o));
+                    // partials of dbeta_i and dA[i][j]
+#pragma unroll
+                    for (int jj = 0; jj < N; ++jj) {
+                        float h[V];
+                        unpack<S>(rh[jj][j], h);
+#pragma unroll
+                        for (int i = 0; i < N; ++i)
+#pragma unroll
+                            for (int e = 0; e < V; ++e)
+                                acc[N + i * N + jj] = fmaf(g[i][e], h[e], acc[N + i * N + jj]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < N; ++i)
+#pragma unroll
+                        for (int e = 0; e < V; ++e) acc[i] = fmaf(g[i][e], f[e], acc[i]);
+                }
+            }
+            if constexpr (PER_TOKEN) {
+                block_sum_vec<M>(acc, red);
+                if (threadIdx.x < K) {
+                    const int c = threadIdx.x;
+                    float val = 0.0f;
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+                        if (c == N + m) val = acc[m];
+                    dw[t * K + c] = val;      // dalpha = 0 (post does not read alpha)
+                }
+#pragma unroll
+                for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+            }
+        }
+        if constexpr (!PER_TOKEN) {
+            block_sum_vec<M>(acc, red);
+            if (threadIdx.x < M) {
+                float val = 0.0f;
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    if ((int)threadIdx.x == m) val = acc[m];
+                part[blk * M + threadIdx.x] = val;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- pre backward
+
+// A block walks `group` consecutive tokens.  The dgamma partial of each
+// thread's columns stays in registers and goes to dg_part[blk][d] once;
+// dalpha goes to dw[t] per token (PER_TOKEN) or is summed over the block's
+// tokens into da_part[blk][N].
+template <int N, typename S, int VPT, bool PER_TOKEN>
+__global__ __launch_bounds__(1024) void pre_bwd_kernel(
+    const uint8_t* __restrict__ du, const uint8_t* __restrict__ H, const float* __restrict__ w,
+    int64_t w_stride, const float* __restrict__ gamma, float eps, const uint8_t* dH_in,
+    uint8_t* dH, float* __restrict__ dw, float* __restrict__ dg_part,
+    float* __restrict__ da_part, int64_t T, int d, int group) {
+    constexpr int V = Store<S>::kElems;
+    constexpr int K = 2 * N + N * N;
+    __shared__ float red[16 * (N > 2 ? N : 2)];   // block_sum_vec<2> and <N>
+    const int B = blockDim.x;
+    const int nvec = d / V;
+    const int64_t row_bytes = (int64_t)d * Store<S>::kBytes;
+
+    for (int64_t blk = blockIdx.x; blk * group < T; blk += gridDim.x) {
+        float dgp[VPT][V];
+#pragma unroll
+        for (int j = 0; j < VPT; ++j)
+#pragma unroll
+            for (int e = 0; e < V; ++e) dgp[j][e] = 0.0f;
+        float dab[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) dab[i] = 0.0f;
+
+        const int64_t t_end = (blk + 1) * group < T ? (blk + 1) * group : T;
+        for (int64_t t = blk * group; t < t_end; ++t) {
+            const float* a = w + t * w_stride;
+            float alpha[N];
+#pragma unroll
+            for (int i = 0; i < N; ++i) alpha[i] = a[i];
+            const int64_t r0 = t * N * row_bytes;
+            uint4 rh[N][VPT], ru[VPT];
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+                const int v = threadIdx.x + j * B;
+                if (v < nvec) {
+#pragma unroll
+                    for (int i = 0; i < N; ++i) rh[i][j] = ld16_stream(H + r0 + i * row_bytes + v * 16);
+                    ru[j] = ld16_stream(du + t * row_bytes + v * 16);
+                }
+            }
+            // x (kept), mean square and mean(gamma * du * x)
+            float x[VPT][V];
+            float s2[2] = {0.0f, 0.0f};
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+                const int v = threadIdx.x + j * B;
+                if (v < nvec) {
+                    float h[V], ug[V], g[V];
+                    unpack<S>(rh[0][j], h);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) x[j][e] = alpha[0] * h[e];
+#pragma unroll
+                    for (int i = 1; i < N; ++i) {
+                        unpack<S>(rh[i][j], h);
+#pragma unroll
+                        for (int e = 0; e < V; ++e) x[j][e] = fmaf(alpha[i], h[e], x[j][e]);
+                    }
+                    unpack<S>(ru[j], ug);
+#pragma unroll
+                    for (int q = 0; q < V / 4; ++q) unpack<f32_t>(ld16(gamma + v * V + 4 * q), &g[4 * q]);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        s2[0] = fmaf(x[j][e], x[j][e], s2[0]);
+                        s2[1] = fmaf(g[e] * ug[e], x[j][e], s2[1]);
+                    }
+                }
+            }
+            // both sums in one reduction: the mean square of x does not
+            // depend on r, and mean(dy * x) is needed only after r is known
+            block_sum_vec<2>(s2, red);
+            const float r = 1.0f / sqrtf(s2[0] / (float)d + eps);
+            const float c2 = r * r * s2[1] / (float)d;
+            float da[N];
+#pragma unroll
+            for (int i = 0; i < N; ++i) da[i] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+                const int v = threadIdx.x + j * B;
+                if (v < nvec) {
+                    float ug[V], g[V], dx[V];
+                    unpack<S>(ru[j], ug);
+#pragma unroll
+                    for (int q = 0; q < V / 4; ++q) unpack<f32_t>(ld16(gamma + v * V + 4 * q), &g[4 * q]);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        dx[e] = r * (g[e] * ug[e] - x[j][e] * c2);
+                        dgp[j][e] = fmaf(ug[e], x[j][e] * r, dgp[j][e]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < N; ++i) {
+                        float h[V], o[V];
+                        unpack<S>(rh[i][j], h);
+#pragma unroll
+                        for (int e = 0; e < V; ++e) {
+                            da[i] = fmaf(dx[e], h[e], da[i]);
+                            o[e] = alpha[i] * dx[e];
+                        }
+                        if (dH_in) {
+                            float p[V];
+                            unpack<S>(ld16_stream(dH_in + r0 + i * row_bytes + v * 16), p);
+#pragma unroll
+                            for (int e = 0; e < V; ++e) o[e] += p[e];
+                        }
+                        st16_stream(dH + r0 + i * row_bytes + v * 16, pack<S>(o));
+                    }
+                }
+            }
+            if constexpr (PER_TOKEN) {
+                block_sum_vec<N>(da, red);
+                if (threadIdx.x < K) {
+                    const int c = threadIdx.x;
+                    float val = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < N; ++i)
+                        if (c == i) val = da[i];
+                    dw[t * K + c] = val;      // dbeta = dA = 0 (pre does not read them)
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < N; ++i) dab[i] += da[i];
+            }
+        }
+        // the block's partials: dgamma of its columns, dalpha (shared record)
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int v = threadIdx.x + j * B;
+            if (v < nvec) {
+#pragma unroll
+                for (int q = 0; q < V / 4; ++q)
+                    st16(dg_part + blk * (int64_t)d + v * V + 4 * q,
+                         make_uint4(__float_as_uint(dgp[j][4 * q]), __float_as_uint(dgp[j][4 * q + 1]),
+                                    __float_as_uint(dgp[j][4 * q + 2]), __float_as_uint(dgp[j][4 * q + 3])));
+            }
+        }
+        if constexpr (!PER_TOKEN) {
+            block_sum_vec<N>(dab, red);
+            if (threadIdx.x < N) {
+                float val = 0.0f;
+#pragma unroll
+                for (int i = 0; i < N; ++i)
+                    if ((int)threadIdx.x == i) val = dab[i];
+                da_part[blk * N + threadIdx.x] = val;
+            }
+        }
+    }
+}
+
+// out[s][c] = sum of in[r][c] over rows r of segment s (kSumRows rows each),
+// in row order; a thread per column.
+__global__ __launch_bounds__(256) void sum_rows_kernel(const float* __restrict__ in, int64_t rows,
+                                                       int cols, float* __restrict__ out) {
+    const int64_t r0 = (int64_t)blockIdx.y * kSumRows;
+    const int64_t r1 = r0 + kSumRows < rows ? r0 + kSumRows : rows;
+    for (int c = blockIdx.x * 256 + threadIdx.x; c < cols; c += gridDim.x * 256) {
+        float s = 0.0f;
+#pragma unroll 8
+        for (int64_t r = r0; r < r1; ++r) s += in[r * cols + c];
+        out[(int64_t)blockIdx.y * cols + c] = s;
+    }
+}
+
+// out[c] = sum_t rec[t * K + c] for c < K: one 1024-thread block per column,
+// a strided per-thread sum in token order, then the block reduction.
+__global__ __launch_bounds__(1024) void sum_records_kernel(const float* __restrict__ rec, int64_t T,
+                                                           int K, float* __restrict__ out) {
+    __shared__ float red[16];
+    const int c = blockIdx.x;
+    float s = 0.0f;
+    for (int64_t t = threadIdx.x; t < T; t += 1024) s += rec[t * K + c];
+    s = block_sum(s, red);
+    if (threadIdx.x == 0) out[c] = s;
+}
+
+// ----------------------------------------------------------------- dispatch
+
+inline dim3 grid_of(int64_t blocks) { return dim3((unsigned)(blocks < kMaxGridB ? blocks : kMaxGridB)); }
+
+// Two-level deterministic column sum: rows -> ceil(rows / 64) segment rows in
+// tmp -> out.  tmp holds ceil(rows / 64) * cols floats.
+hipError_t sum_rows(const float* in, int64_t rows, int cols, float* tmp, float* out, hipStream_t s) {
+    const int64_t segs = (rows + kSumRows - 1) / kSumRows;
+    const dim3 gx((unsigned)((cols + 255) / 256));
+    if (segs <= 1) return launch(sum_rows_kernel, dim3(gx.x, 1), dim3(256), 0, s, in, rows, cols, out);
+    hipError_t e = launch(sum_rows_kernel, dim3(gx.x, (unsigned)segs), dim3(256), 0, s, in, rows, cols, tmp);
+    if (e != hipSuccess) return e;
+    return sum_rows(tmp, segs, cols, tmp + segs * cols, out, s);
+}
+
+template <int N, typename S, int VPT>
+hipError_t post_bwd_go(RowCfg c, const void* dHo, const void* H, const void* F, const float* w,
+                       int64_t ws, void* dH, void* dF, float* dw, float* part, int64_t T, int d,
+                       int group, hipStream_t s) {
+    const dim3 grid = grid_of((T + group - 1) / group);
+    if (ws != 0)
+        return launch(post_bwd_kernel<N, S, VPT, true>, grid, dim3(c.block), 0, s,
+                      static_cast<const uint8_t*>(dHo), static_cast<const uint8_t*>(H),
+                      static_cast<const uint8_t*>(F), w, ws, static_cast<uint8_t*>(dH),
+                      static_cast<uint8_t*>(dF), dw, part, T, d, group);
+    return launch(post_bwd_kernel<N, S, VPT, false>, grid, dim3(c.block), 0, s,
+                  static_cast<const uint8_t*>(dHo), static_cast<const uint8_t*>(H),
+                  static_cast<const uint8_t*>(F), w, ws, static_cast<uint8_t*>(dH),
+                  static_cast<uint8_t*>(dF), dw, part, T, d, group);
+}
+
+template <int N, typename S, int VPT>
+hipError_t pre_bwd_go(RowCfg c, const void* du, const void* H, const float* w, int64_t ws,
+                      const float* gamma, float eps, const void* dH_in, void* dH, float* dw,
+                      float* dg_part, float* da_part, int64_t T, int d, int group, hipStream_t s) {
+    const dim3 grid = grid_of((T + group - 1) / group);
+    if (ws != 0)
+        return launch(pre_bwd_kernel<N, S, VPT, true>, grid, dim3(c.block), 0, s,
+                      static_cast<const uint8_t*>(du), static_cast<const uint8_t*>(H), w, ws, gamma,
+                      eps, static_cast<const uint8_t*>(dH_in), static_cast<uint8_t*>(dH), dw,
+                      dg_part, da_part, T, d, group);
+    return launch(pre_bwd_kernel<N, S, VPT, false>, grid, dim3(c.block), 0, s,
+                  static_cast<const uint8_t*>(du), static_cast<const uint8_t*>(H), w, ws, gamma,
+                  eps, static_cast<const uint8_t*>(dH_in), static_cast<uint8_t*>(dH), dw, dg_part,
+                  da_part, T, d, group);
+}
+
+#define HC_BWD_VPT(FN, ...)                                  \
+    switch (c.vpt) {                                         \
+        case 1: return FN<N, S, 1>(c, __VA_ARGS__);          \
+        case 2: return FN<N, S, 2>(c, __VA_ARGS__);          \
+        case 3: return FN<N, S, 3>(c, __VA_ARGS__);          \
+        case 4: return FN<N, S, 4>(c, __VA_ARGS__);          \
+    }                                                        \
+    return hipErrorInvalidConfiguration;
+
+template <int N, typename S>
+hipError_t post_bwd_vpt(RowCfg c, const void* dHo, const void* H, const void* F, const float* w,
+                        int64_t ws, void* dH, void* dF, float* dw, float* part, int64_t T, int d,
+                        int group, hipStream_t s) {
+    HC_BWD_VPT(post_bwd_go, dHo, H, F, w, ws, dH, dF, dw, part, T, d, group, s)
+}
+
+template <int N, typename S>
+hipError_t pre_bwd_vpt(RowCfg c, const void* du, const void* H, const float* w, int64_t ws,
+                       const float* gamma, float eps, const void* dH_in, void* dH, float* dw,
+                       float* dg_part, float* da_part, int64_t T, int d, int group, hipStream_t s) {
+    HC_BWD_VPT(pre_bwd_go, du, H, w, ws, gamma, eps, dH_in, dH, dw, dg_part, da_part, T, d, group, s)
+}
+#undef HC_BWD_VPT
+
+template <typename S, typename... A>
+hipError_t post_bwd_n(int n, A... a) {
+    switch (n) {
+        case 1: return post_bwd_vpt<1, S>(a...);
+        case 2: return post_bwd_vpt<2, S>(a...);
+        case 3: return post_bwd_vpt<3, S>(a...);
+        case 4: return post_bwd_vpt<4, S>(a...);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename S, typename... A>
+hipError_t pre_bwd_n(int n, A... a) {
+    switch (n) {
+        case 1: return pre_bwd_vpt<1, S>(a...);
+        case 2: return pre_bwd_vpt<2, S>(a...);
+        case 3: return pre_bwd_vpt<3, S>(a...);
+        case 4: return pre_bwd_vpt<4, S>(a...);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Workspace layout for T tokens of width d with n streams (floats):
+//   [rows][d]   dgamma partials         (rows = blocks = ceil(T / group))
+//   [rows][M]   record partials         (M = n + n^2 >= the n of dalpha)
+//   tmp         second-level rows of either sum (ceil(rows / 64) * max(d, M),
+//               plus a third level, bounded by 2 * ceil(rows / 64) * max(d, M))
+struct BwdSpace {
+    int64_t rows, dg, rec, tmp, total;   // offsets and total, in floats
+};
+inline BwdSpace bwd_space(int64_t T, int n, int d) {
+    BwdSpace b;
+    const int64_t g = group_of(T);
+    b.rows = (T + g - 1) / g;
+    const int64_t M = n + int64_t(n) * n;
+    const int64_t segs = (b.rows + kSumRows - 1) / kSumRows;
+    const int64_t wide = d > M ? d : M;
+    b.dg = 0;
+    b.rec = b.rows * d;
+    b.tmp = b.rec + b.rows * M;
+    b.total = b.tmp + 2 * (segs + 1) * wide;
+    return b;
+}
+
+}  // namespace
+
+int64_t backward_workspace_bytes(int64_t T, int n, int d) {
+    if (T <= 0 || d <= 0 || n <= 0) return 0;
+    return bwd_space(T, n, d).total * 4;
+}
+
+hipError_t launch_post_mix_backward(const void* dHo, const void* H, const void* F, const float* w,
+                                    int64_t w_stride, void* dH, void* dF, float* dw, void* work,
+                                    int64_t T, int n, int d, int dt, hipStream_t s) {
+    const BwdSpace sp = bwd_space(T, n, d);
+    float* ws = static_cast<float*>(work);
+    const int group = w_stride != 0 ? 1 : (int)group_of(T);
+    float* part = w_stride != 0 ? nullptr : ws + sp.rec;
+    hipError_t e =
+        dt == 0 ? post_bwd_n<f32_t>(n, row_config(d / Store<f32_t>::kElems), dHo, H, F, w, w_stride,
+                                    dH, dF, dw, part, T, d, group, s)
+                : post_bwd_n<bf16_t>(n, row_config(d / Store<bf16_t>::kElems), dHo, H, F, w, w_stride,
+                                     dH, dF, dw, part, T, d, group, s);
+    if (e != hipSuccess || w_stride != 0) return e;
+    // shared record: dw = [0 (dalpha) | sum of the block partials]
+    const int M = n + n * n;
+    e = launch(sum_rows_kernel, dim3(1, 1), dim3(256), 0, s, static_cast<const float*>(ws), int64_t(0),
+               n, dw);   // zero rows: writes dalpha = 0
+    if (e != hipSuccess) return e;
+    return sum_rows(part, sp.rows, M, ws + sp.tmp, dw + n, s);
+}
+
+hipError_t launch_pre_mix_backward(const void* du, const void* H, const float* w, int64_t w_stride,
+                                   const float* gamma, float eps, const void* dH_in, void* dH,
+                                   float* dw, float* dgamma, void* work, int64_t T, int n, int d,
+                                   int dt, hipStream_t s) {
+    const BwdSpace sp = bwd_space(T, n, d);
+    float* ws = static_cast<float*>(work);
+    const int group = (int)group_of(T);
+    float* dg_part = ws + sp.dg;
+    float* da_part = ws + sp.rec;
+    hipError_t e =
+        dt == 0 ? pre_bwd_n<f32_t>(n, row_config(d / Store<f32_t>::kElems), du, H, w, w_stride,
+                                   gamma, eps, dH_in, dH, dw, dg_part, da_part, T, d, group, s)
+                : pre_bwd_n<bf16_t>(n, row_config(d / Store<bf16_t>::kElems), du, H, w, w_stride,
+                                    gamma, eps, dH_in, dH, dw, dg_part, da_part, T, d, group, s);
+    if (e != hipSuccess) return e;
+    e = sum_rows(dg_part, sp.rows, d, ws + sp.tmp, dgamma, s);
+    if (e != hipSuccess || w_stride != 0) return e;
+    // shared record: dw = [sum of the dalpha partials | 0 (dbeta, dA)]
+    const int K = 2 * n + n * n;
+    e = sum_rows(da_part, sp.rows, n, ws + sp.tmp, dw, s);
+    if (e != hipSuccess) return e;
+    return launch(sum_rows_kernel, dim3(1, 1), dim3(256), 0, s, static_cast<const float*>(ws),
+                  int64_t(0), K - n, dw + n);   // zero rows: writes 0
+}
+
+hipError_t launch_sum_records(const float* rec, int64_t T, int K, float* out, hipStream_t s) {
+    return launch(sum_records_kernel, dim3(K), dim3(1024), 0, s, rec, T, K, out);
+}
+
+}  // namespace hc

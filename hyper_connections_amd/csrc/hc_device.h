@@ -71,13 +71,22 @@ template <> __device__ __forceinline__ uint4 pack<f32_t>(const float* f) {
                       __float_as_uint(f[2]), __float_as_uint(f[3]));
 }
 
-// Butterfly sum over the 64 lanes of a wave.  Every lane ends with the same
-// value: at each step a lane and its partner add the same two operands.
+// Sum over the 64 lanes of a wave with DPP row shifts and row broadcasts (no
+// LDS traffic): prefix sums of 4, 8 and 16 inside each row, then rows 0+1
+// and 2+3, then the two halves; the total lands in lane 63 and is broadcast
+// from there, so every lane returns the same value in a fixed order.
+#define HC_DPP(v, ctrl, rm, bm)                                                         \
+    __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), (ctrl), (rm), (bm), false))
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
+    v += HC_DPP(v, 0x111, 0xF, 0xF);    // row_shr:1
+    v += HC_DPP(v, 0x112, 0xF, 0xF);    // row_shr:2
+    v += HC_DPP(v, 0x114, 0xF, 0xE);    // row_shr:4, lanes 4..15 of each row
+    v += HC_DPP(v, 0x118, 0xF, 0xC);    // row_shr:8, lanes 8..15 of each row
+    v += HC_DPP(v, 0x142, 0xA, 0xF);    // row_bcast:15 into rows 1 and 3
+    v += HC_DPP(v, 0x143, 0xC, 0xF);    // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+#undef HC_DPP
 
 // Sum over the block: waves reduce, then every thread adds the per-wave
 // partials in wave order.  The order depends only on blockDim.  `red` holds

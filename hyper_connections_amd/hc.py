@@ -42,8 +42,13 @@ _SIGS = {
     "hc_weights": [_vp, _vp, _fp, _f32, _f32, _i32, _fp, _i64, _i32, _i32, _i32, _vp],
     "hc_sinkhorn": [_fp, _fp, _i32, _i64, _i32, _vp],
     "hc_block_tanh": [_vp, _vp, _i64, _i32, _vp],
+    "hc_post_mix_backward": [_vp, _vp, _vp, _fp, _i64, _vp, _vp, _fp, _vp, _i64, _i64, _i32, _i32,
+                             _i32, _vp],
+    "hc_pre_mix_backward": [_vp, _vp, _fp, _i64, _fp, _f32, _vp, _vp, _fp, _fp, _vp, _i64, _i64,
+                            _i32, _i32, _i32, _vp],
+    "hc_sum_records": [_fp, _i64, _i32, _fp, _vp],
 }
-EXPORTS = tuple(_SIGS) + ("hc_status_str", "hc_abi_version")
+EXPORTS = tuple(_SIGS) + ("hc_status_str", "hc_abi_version", "hc_backward_workspace")
 
 _lib = None
 
@@ -71,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.hc_status_str.restype = ctypes.c_char_p
         L.hc_abi_version.argtypes = []
         L.hc_abi_version.restype = ctypes.c_int32
+        L.hc_backward_workspace.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+        L.hc_backward_workspace.restype = ctypes.c_int64
         _lib = L
     return _lib
 
@@ -226,3 +233,93 @@ def block_tanh(u, out=None, stream=None) -> torch.Tensor:
 
 def abi_version() -> int:
     return int(lib().hc_abi_version())
+
+
+def backward_workspace(T: int, n: int, d: int) -> int:
+    """Bytes of workspace the backward calls need (hc_backward_workspace)."""
+    return int(lib().hc_backward_workspace(int(T), int(n), int(d)))
+
+
+def _workspace(ws, T, n, d, device):
+    need = backward_workspace(T, n, d)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    _dev(ws, "workspace")
+    return ws, ws.numel() * ws.element_size()
+
+
+def _grad_record(dw, T, K, ws_stride, device, what="dw"):
+    shape = (K,) if ws_stride == 0 else (T, K)
+    if dw is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    _dev(dw, what)
+    if dw.dtype != torch.float32 or tuple(dw.shape) != shape:
+        raise ValueError(f"{what} must be float32 of shape {shape} (the shape of the weights)")
+    return dw
+
+
+def post_mix_backward(dH_out, H, F, w, dH=None, dF=None, dw=None, workspace=None, stream=None):
+    """Gradients of post_mix: returns (dH, dF, dw).  dw has the shape of the
+    weights: (K,) for a shared record (summed over tokens), (T, K) for
+    per-token records; entries [dalpha (0) | dbeta | dA]."""
+    T, n, d, K = _H(H)
+    ws = _record(w, T, K)
+    _dev(dH_out, "dH_out")
+    _dev(F, "F")
+    if dH_out.dtype != H.dtype or dH_out.shape != H.shape:
+        raise ValueError("dH_out must match H")
+    if F.dtype != H.dtype or tuple(F.shape) != (T, d):
+        raise ValueError("F must match H's dtype and have shape (T, d)")
+    dH = torch.empty_like(H) if dH is None else _dev(dH, "dH")
+    dF = torch.empty_like(F) if dF is None else _dev(dF, "dF")
+    if dH.shape != H.shape or dH.dtype != H.dtype or dF.shape != F.shape or dF.dtype != F.dtype:
+        raise ValueError("dH / dF do not match H / F")
+    dw = _grad_record(dw, T, K, ws, H.device)
+    wk, wkb = (None, 0) if ws != 0 else _workspace(workspace, T, n, d, H.device)
+    _call("hc_post_mix_backward", dH_out.data_ptr(), H.data_ptr(), F.data_ptr(), w.data_ptr(), ws,
+          dH.data_ptr(), dF.data_ptr(), dw.data_ptr(), wk.data_ptr() if wk is not None else None,
+          wkb, T, n, d, _dt(H), _stream(stream))
+    return dH, dF, dw
+
+
+def pre_mix_backward(du, H, w, gamma, eps: float = 1e-6, dH_in=None, out=None, dw=None,
+                     dgamma=None, workspace=None, stream=None):
+    """Gradients of pre_mix: returns (dH, dw, dgamma).  dH includes dH_in when
+    given (``out=dH_in`` accumulates in place); dw has the shape of the
+    weights ([dalpha | 0 | 0]); dgamma is summed over tokens.  Output
+    buffers and the workspace may be passed in."""
+    T, n, d, K = _H(H)
+    ws = _record(w, T, K)
+    _dev(du, "du")
+    _dev(gamma, "gamma")
+    if du.dtype != H.dtype or tuple(du.shape) != (T, d):
+        raise ValueError("du must match H's dtype and have shape (T, d)")
+    if gamma.dtype != torch.float32 or tuple(gamma.shape) != (d,):
+        raise ValueError("gamma must be float32 of shape (d,)")
+    if dH_in is not None:
+        _dev(dH_in, "dH_in")
+        if dH_in.dtype != H.dtype or dH_in.shape != H.shape:
+            raise ValueError("dH_in must match H")
+    dH = torch.empty_like(H) if out is None else _dev(out, "out")
+    if dH.dtype != H.dtype or dH.shape != H.shape:
+        raise ValueError("out must match H")
+    dw = _grad_record(dw, T, K, ws, H.device)
+    dg = torch.empty(d, dtype=torch.float32, device=H.device) if dgamma is None else _dev(dgamma, "dgamma")
+    if dg.dtype != torch.float32 or tuple(dg.shape) != (d,):
+        raise ValueError(f"dgamma must be float32 of shape ({d},)")
+    wk, wkb = _workspace(workspace, T, n, d, H.device)
+    _call("hc_pre_mix_backward", du.data_ptr(), H.data_ptr(), w.data_ptr(), ws, gamma.data_ptr(),
+          float(eps), dH_in.data_ptr() if dH_in is not None else None, dH.data_ptr(),
+          dw.data_ptr(), dg.data_ptr(), wk.data_ptr(), wkb, T, n, d, _dt(H), _stream(stream))
+    return dH, dw, dg
+
+
+def sum_records(rec, out=None, stream=None):
+    """Sum of per-token records over tokens: (T, K) float32 -> (K,)."""
+    _dev(rec, "rec")
+    if rec.dtype != torch.float32 or rec.dim() != 2:
+        raise ValueError("rec must be float32 of shape (T, K)")
+    T, K = rec.shape
+    o = torch.empty(K, dtype=torch.float32, device=rec.device) if out is None else _dev(out, "out")
+    _call("hc_sum_records", rec.data_ptr(), T, K, o.data_ptr(), _stream(stream))
+    return o

@@ -50,3 +50,16 @@ def post_pre_bytes(n: int, d: int, s: int, per_token_record: bool = False) -> in
     write H' and the next block input u."""
     rec = (n + n * n + n) * RECORD_BYTES_PER_ENTRY if per_token_record else 0
     return (2 * n + 2) * d * s + rec
+
+
+def post_bwd_bytes(n: int, d: int, s: int) -> int:
+    """Gradient of post: read dH', H and F, write dH and dF and one gradient
+    record."""
+    return (3 * n + 2) * d * s + record_bytes(n)
+
+
+def pre_bwd_bytes(n: int, d: int, s: int, accumulate: bool = True) -> int:
+    """Gradient of pre: read du and H (and the incoming dH when it is
+    accumulated), write dH and one gradient record (the dgamma partials,
+    d floats per group of tokens, are not counted)."""
+    return (2 * n + 1 + (n if accumulate else 0)) * d * s + record_bytes(n)

@@ -140,6 +140,52 @@ hc_status hc_post_pre_mix(const void* H, const void* F, const float* w, int64_t 
                           const float* gamma_next, float eps, void* H_out, void* u_next,
                           int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream);
 
+/* Bytes of device workspace the backward calls need for T tokens of width d
+ * with n streams (0 for T <= 0).  The caller owns it; it holds per-block
+ * partial sums and is fully rewritten by every call. */
+int64_t hc_backward_workspace(int64_t T, int32_t n, int32_t d);
+
+/* Gradients of hc_post_mix (the map is linear in H and F):
+ *   dH_j = sum_i A[i][j] dH_out_i        dF = sum_i beta_i dH_out_i
+ *   dA[i][j] = sum_k dH_out_ik H_jk      dbeta_i = sum_k dH_out_ik F_k
+ * [GLOSS] definition: the mixing is learned, so its weights take gradients.
+ *   dH_out, H [T][n][d] dt; F [T][d] dt; w records as in hc_post_mix
+ *   dH [T][n][d] dt, dF [T][d] dt: outputs (no overlap with anything)
+ *   dw fp32, the shape of the weights: one record [dalpha | dbeta | dA]
+ *      (dalpha = 0: post does not read alpha) when w_stride == 0, summed over
+ *      the tokens in a fixed order; else [T][K], one record per token.
+ *   workspace: >= hc_backward_workspace(T, n, d) bytes, 16-byte aligned
+ *      (used when w_stride == 0; may be NULL otherwise). */
+hc_status hc_post_mix_backward(const void* dH_out, const void* H, const void* F, const float* w,
+                               int64_t w_stride, void* dH, void* dF, float* dw,
+                               void* workspace, int64_t workspace_bytes, int64_t T,
+                               int32_t n, int32_t d, hc_dtype dt, void* stream);
+
+/* Gradients of hc_pre_mix (RMSNorm and read-mix written out):
+ *   dy = gamma * du, dx = r * (dy - x * r^2 * mean_k(dy_k x_k)),
+ *   dH_i = alpha_i dx (+ dH_in_i), dalpha_i = sum_k dx_k H_ik,
+ *   dgamma_k = sum_t du_tk x_tk r_t,
+ * with x and r = 1/sqrt(mean x^2 + eps) recomputed from H.
+ *   du [T][d] dt; H [T][n][d] dt; w, gamma, eps as in hc_pre_mix
+ *   dH_in [T][n][d] dt or NULL: added to dH (a layer's H feeds both pre and
+ *     post, so this is where the two gradients meet); dH_in == dH allowed
+ *   dH [T][n][d] dt
+ *   dw fp32, the shape of the weights: [dalpha | 0 | 0] summed over tokens
+ *     when w_stride == 0, else [T][K] per token
+ *   dgamma [d] fp32, summed over tokens in a fixed order (deterministic)
+ *   workspace: >= hc_backward_workspace(T, n, d) bytes, 16-byte aligned.
+ * Outputs may not overlap inputs, each other or the workspace (except
+ * dH == dH_in); a short workspace is HC_ERR_ARG. */
+hc_status hc_pre_mix_backward(const void* du, const void* H, const float* w, int64_t w_stride,
+                              const float* gamma, float eps, const void* dH_in, void* dH,
+                              float* dw, float* dgamma, void* workspace, int64_t workspace_bytes,
+                              int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream);
+
+/* out[c] = sum over t of rec[t * K + c], c < K, summed in a fixed order:
+ * turns per-token gradient records into the gradient of one shared record.
+ *   rec [T][K] fp32, out [K] fp32 (no overlap), 1 <= K <= 1024. */
+hc_status hc_sum_records(const float* rec, int64_t T, int32_t K, float* out, void* stream);
+
 /* Stand-in block used by the benchmarks and tests, not part of the method:
  * F = tanh(u) elementwise ([EXPL] "Jargon", Residual connection: the block
  * computes f(x)).  count % 8 == 0 (bf16) or count % 4 == 0 (fp32). */

@@ -68,12 +68,15 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(g - r) / scale))
 
 
-def check(got: np.ndarray, ref: np.ndarray, what: str = "") -> float:
-    """Assert the storage-dtype tolerance; returns the error."""
+def check(got: np.ndarray, ref: np.ndarray, what: str = "", one_ulp: bool = True) -> float:
+    """Assert the storage-dtype tolerance; returns the error.  `one_ulp=False`
+    drops the one-ulp bound for results stored twice (an accumulation into a
+    rounded buffer), which only the 2e-2 tolerance covers."""
     e = rel_err(got, ref)
     if got.dtype == np.uint16:
         assert e <= TOL_BF16, f"{what}: max rel err {e:.3g} > {TOL_BF16}"
-        assert e <= TOL_BF16_ULP, f"{what}: max rel err {e:.3g} > one bf16 ulp"
+        if one_ulp:
+            assert e <= TOL_BF16_ULP, f"{what}: max rel err {e:.3g} > one bf16 ulp"
     else:
         assert e <= TOL_F32, f"{what}: max rel err {e:.3g} > {TOL_F32}"
     return e

@@ -31,7 +31,8 @@ def L():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:hc_status|const char\*|int32_t)\s+(hc_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:hc_status|const char\*|int32_t|int64_t)\s+(hc_\w+)\s*\(",
+                                 text, re.M)))
 
 
 def test_exports_every_declared_symbol(L):
@@ -118,6 +119,31 @@ def test_weights_validation(L):
     assert f(W=P[1] + 8) == ALIGN and f(o=P[3] + 2) == ALIGN
     assert f(o=P[0] + 64) == ALIAS and f(o=P[1]) == ALIAS
     assert f(n=0) == SHAPE and f(d=100) == SHAPE and f(dt=5) == DTYPE
+
+
+def test_backward_validation(L):
+    ws_need = L.hc_backward_workspace(8, 4, 4096)
+    assert ws_need > 0 and L.hc_backward_workspace(0, 4, 4096) == 0
+    assert L.hc_backward_workspace(8, 5, 4096) == 0
+    pb = lambda **k: L.hc_post_mix_backward(  # noqa: E731
+        k.get("g", P[0]), k.get("H", P[1]), k.get("F", P[2]), k.get("w", P[3]), k.get("ws", 0),
+        k.get("dH", P[4]), k.get("dF", P[5]), k.get("dw", P[6]), k.get("wk", P[7]),
+        k.get("wkb", ws_need), k.get("T", 8), 4, 4096, BF16, None)
+    assert pb(T=0) == OK and pb(T=0, dH=None) == OK
+    assert pb(dF=None) == NULL and pb(ws=2) == SHAPE and pb(dH=P[4] + 8) == ALIGN
+    assert pb(wk=None) == NULL and pb(wkb=ws_need - 1) == ARG and pb(wk=P[7] + 4) == ALIGN
+    assert pb(dH=P[1]) == ALIAS and pb(dw=P[4] + 64) == ALIAS and pb(dF=P[0] + 16) == ALIAS
+    assert pb(wk=P[6]) == ALIAS
+    qb = lambda **k: L.hc_pre_mix_backward(  # noqa: E731
+        k.get("du", P[0]), k.get("H", P[1]), k.get("w", P[2]), k.get("ws", 0), k.get("g", P[3]),
+        k.get("eps", 1e-6), k.get("din", None), k.get("dH", P[4]), k.get("dw", P[5]),
+        k.get("dg", P[6]), k.get("wk", P[7]), k.get("wkb", ws_need), k.get("T", 8), 4, 4096, BF16, None)
+    assert qb(T=0) == OK and qb(eps=0.0) == ARG and qb(wkb=ws_need - 4) == ARG
+    assert qb(wk=None) == NULL and qb(dg=P[6] + 2) == ALIGN and qb(wk=P[7] + 8) == ALIGN
+    assert qb(din=P[4] + 16) == ALIAS and qb(dH=P[1]) == ALIAS and qb(wk=P[5]) == ALIAS
+    assert L.hc_sum_records(P[0], 10, 0, P[1], None) == SHAPE
+    assert L.hc_sum_records(P[0], -1, 24, P[1], None) == ARG
+    assert L.hc_sum_records(P[0], 10, 24, P[0] + 8, None) == ALIAS
 
 
 def test_sinkhorn_validation(L):

@@ -1,0 +1,168 @@
+"""GPU parity of the backward kernels (gradients of post and pre, the
+deterministic sums) against the oracle's gradients, through the C ABI.
+
+Gradient records are sums over d of products accumulated in fp32; with
+random signs they cancel, so they are held to 1e-4 of the record's RMS
+(TOL_GRAD); storage outputs (dH, dF) to the storage tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import check, dev, host, need_gpu, rel_err
+from hyper_connections_amd import hc
+from hyper_connections_amd.workloads import f32_to_bf16_bits, identity_record, make_inputs, workload
+
+pytestmark = pytest.mark.gpu
+
+TOL_GRAD = 1e-4
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def storage(x, dt):
+    return f32_to_bf16_bits(x) if dt == "bf16" else x.astype(np.float32)
+
+
+def grad_check(got, ref, what):
+    e = rel_err(np.asarray(got, np.float64), np.asarray(ref, np.float64))
+    assert e <= TOL_GRAD, f"{what}: {e:.3g} > {TOL_GRAD}"
+
+
+def dalpha_check(got, ref, du, H, w, g, eps, what):
+    """dalpha_i = sum_k dx_k H_ik cancels by construction (RMSNorm is scale
+    invariant, so sum_i alpha_i dalpha_i = sum_k dx_k x_k ~ 0; at n = 1 dalpha
+    itself is ~0), so it is compared against its Cauchy-Schwarz bound
+    |dx| |H_i| rather than its own size."""
+    Hf = oracle.widen(H)
+    T, n, d = Hf.shape
+    W = np.broadcast_to(w, (T, w.shape[-1])).astype(np.float64)
+    x = np.einsum("ti,tid->td", W[:, :n], Hf)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps)
+    dy = g[None, :] * oracle.widen(du)
+    dx = r * (dy - x * r * r * np.mean(dy * x, axis=1, keepdims=True))
+    bound = np.linalg.norm(dx, axis=1)[:, None] * np.linalg.norm(Hf, axis=2)
+    got = np.asarray(got, np.float64).reshape(-1, W.shape[1])[:, :n]
+    ref = np.asarray(ref, np.float64).reshape(-1, W.shape[1])[:, :n]
+    if got.shape[0] == 1:          # shared record: summed over tokens
+        bound = bound.sum(axis=0, keepdims=True)
+    e = np.max(np.abs(got - ref) / np.maximum(bound, 1e-30))
+    assert e <= 1e-5, f"{what}: {e:.3g} of the Cauchy-Schwarz bound"
+
+
+def case(rng, dt, T, n, d, per_token):
+    K = 2 * n + n * n
+    H = storage(rng.standard_normal((T, n, d)).astype(np.float32), dt)
+    F = storage(rng.standard_normal((T, d)).astype(np.float32), dt)
+    G = storage(rng.standard_normal((T, n, d)).astype(np.float32), dt)
+    du = storage(rng.standard_normal((T, d)).astype(np.float32), dt)
+    shape = (T, K) if per_token else (K,)
+    w = (np.broadcast_to(identity_record(n), shape) + 0.3 * rng.standard_normal(shape)).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    return H, F, G, du, w, g
+
+
+SHAPES = [("bf16", 8), ("bf16", 520), ("bf16", 4096), ("bf16", 6144), ("bf16", 8200),
+          ("f32", 4), ("f32", 1024), ("f32", 4100)]
+
+
+@pytest.mark.parametrize("dt,d", SHAPES)
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_post_backward_parity(dt, d, n):
+    rng = np.random.default_rng(d * 11 + n)
+    T = 9
+    H, F, G, du, w, g = case(rng, dt, T, n, d, per_token=(d % 3 == 0))
+    dH, dF, dw = hc.post_mix_backward(dev(G), dev(H), dev(F), dev(w))
+    rdH, rdF, rdw = oracle.post_mix_backward(G, H, F, w.astype(np.float64))
+    check(host(dH), rdH, f"post dH n={n} d={d}")
+    check(host(dF), rdF, f"post dF n={n} d={d}")
+    if w.ndim == 1:                 # shared record: the gradient is the sum over tokens
+        rdw = rdw.sum(axis=0)[None]
+        got = host(dw)[None]
+    else:
+        got = host(dw)
+    grad_check(got, rdw, f"post dw n={n} d={d}")
+
+
+@pytest.mark.parametrize("dt,d", SHAPES)
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("acc", [False, True])
+def test_pre_backward_parity(dt, d, n, acc):
+    rng = np.random.default_rng(d * 13 + n + 7 * acc)
+    T = 21          # several dgamma groups, the last one partial
+    H, F, G, du, w, g = case(rng, dt, T, n, d, per_token=(d % 3 != 0))
+    dH_in = G if acc else None
+    dH, dw, dg = hc.pre_mix_backward(dev(du), dev(H), dev(w), dev(g), 1e-6,
+                                     dH_in=dev(dH_in) if acc else None)
+    rdH, rdw, rdg = oracle.pre_mix_backward(du, H, w.astype(np.float64), g, 1e-6,
+                                            dH_in=oracle.widen(dH_in) if acc else None)
+    check(host(dH), rdH, f"pre dH n={n} d={d}")
+    if w.ndim == 1:
+        rdw = rdw.sum(axis=0)
+    dalpha_check(host(dw), rdw, du, H, w, g, 1e-6, f"pre dalpha n={n} d={d}")
+    assert np.all(host(dw).reshape(-1, 2 * n + n * n)[:, n:] == 0)
+    grad_check(host(dg)[None, :], rdg[None, :], f"pre dgamma n={n} d={d}")
+
+
+def test_pre_backward_accumulates_in_place():
+    rng = np.random.default_rng(3)
+    H, F, G, du, w, g = case(rng, "bf16", 17, 4, 4096, per_token=True)
+    ref_dH, _, _ = hc.pre_mix_backward(dev(du), dev(H), dev(w), dev(g), dH_in=dev(G))
+    acc = dev(G)
+    ptr = acc.data_ptr()
+    out, _, _ = hc.pre_mix_backward(dev(du), dev(H), dev(w), dev(g), dH_in=acc, out=acc)
+    assert out.data_ptr() == ptr
+    assert np.array_equal(host(acc), host(ref_dH))
+
+
+def test_backward_deterministic():
+    rng = np.random.default_rng(4)
+    H, F, G, du, w, g = case(rng, "bf16", 300, 4, 4096, per_token=False)
+    runs = [[host(x) for x in hc.pre_mix_backward(dev(du), dev(H), dev(w), dev(g), dH_in=dev(G))]
+            for _ in range(2)]
+    for a, b in zip(*runs):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("T,K", [(1, 24), (255, 24), (8192, 24), (1000, 3), (37, 15)])
+def test_sum_records(T, K):
+    rng = np.random.default_rng(T + K)
+    rec = rng.standard_normal((T, K)).astype(np.float32)
+    got = host(hc.sum_records(dev(rec)))
+    ref = rec.astype(np.float64).sum(axis=0)
+    np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-5 * np.sqrt(T))
+
+
+def test_static_layer_backward_full_size_sampled():
+    """T=8192, n=4, d=4096 bf16 with shared weights: post backward, then pre
+    backward accumulating into the same dH; dgamma and the shared weight
+    gradients (summed records) against the oracle over all tokens; dH and dF
+    on 256 sampled tokens."""
+    wl = workload("static-bf16")
+    inp = make_inputs(wl)
+    rng = np.random.default_rng(77)
+    T, n, d = wl.T, wl.n, wl.d
+    G = f32_to_bf16_bits(rng.standard_normal((T, n, d)).astype(np.float32))
+    du = f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    Hd, Fd, wd, gd = dev(inp["H"]), dev(inp["F"]), dev(inp["w"]), dev(inp["gamma"])
+    dH, dF, dw_post = hc.post_mix_backward(dev(G), Hd, Fd, wd)
+    dH, dw_pre, dg = hc.pre_mix_backward(dev(du), Hd, wd, gd, wl.eps, dH_in=dH, out=dH)
+    gw = host(dw_post) + host(dw_pre)
+    w64 = inp["w"].astype(np.float64)
+    oracle.set_threads(0)
+    r_post = oracle.post_mix_backward(G, inp["H"], inp["F"], w64)
+    r_pre = oracle.pre_mix_backward(du, inp["H"], w64, inp["gamma"], wl.eps,
+                                    dH_in=oracle.widen(oracle.round_bf16(r_post[0])))
+    grad_check(gw[None, n:], r_post[2].sum(0)[None, n:], "shared dbeta, dA")
+    dalpha_check(gw[None, :], r_pre[1].sum(0)[None, :], du, inp["H"], inp["w"], inp["gamma"], wl.eps,
+                 "shared dalpha")
+    grad_check(host(dg)[None, :], r_pre[2][None, :], "dgamma")
+    idx = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 256, replace=False)]))
+    ti = torch.from_numpy(idx).cuda()
+    check(host(dF[ti]), r_post[1][idx], "dF")
+    # dH on the GPU is the bf16-stored post gradient plus the pre gradient,
+    # rounded again: two roundings, so only the bf16 tolerance applies
+    check(host(dH[ti]), r_pre[0][idx], "dH", one_ulp=False)
