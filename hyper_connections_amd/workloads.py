@@ -10,7 +10,8 @@ Recipe.  Every random tensor is drawn from numpy's PCG64 with
 only on (seed, tensor, token), so any subset of tokens can be regenerated on
 its own (the sampled checks at full size rely on that).  bf16 tensors are the
 fp32 draw rounded to nearest-even bf16 and are held as ``uint16`` bit patterns
-on the host.
+on the host; fp8 tensors (E4M3, the OCP 8-bit float with 3 mantissa bits) are
+the draw rounded to the nearest code, ties to even, held as ``uint8``.
 
 The weight record of a token has K = 2n + n^2 fp32 entries laid out as
 ``[alpha_0..alpha_{n-1} | beta_0..beta_{n-1} | A row-major]``; the identity
@@ -31,6 +32,7 @@ dynamic-bf16        16384  4  4096  bf16   per token: W ~ N(0, 0.02), scale 0.01
 mhc-bf16            32768  4  4096  bf16   per token logits ~ N(0, 1), 20 iters
 chain-bf16 (x78)    4096   4  6144  bf16   per layer identity + N(0, 0.02)
 decode-bf16 (x78)   64     4  8192  bf16   per layer identity + N(0, 0.02)
+static-fp8          16384  4  4096  fp8    static identity + N(0, 0.05)
 ==================  =====  =  ====  =====  =====================================
 
 The decode workload is the explainer's worked shape (section "What four
@@ -55,7 +57,7 @@ class Workload:
     T: int
     n: int
     d: int
-    dtype: str            # "f32" | "bf16"
+    dtype: str            # "f32" | "bf16" | "fp8"
     seed: int
     kind: str             # "static" | "dynamic" | "mhc" | "chain"
     weight_sd: float = 0.0
@@ -73,7 +75,7 @@ class Workload:
 
     @property
     def elem_bytes(self) -> int:
-        return 4 if self.dtype == "f32" else 2
+        return {"f32": 4, "bf16": 2, "fp8": 1}[self.dtype]
 
 
 WORKLOADS = {
@@ -88,6 +90,7 @@ WORKLOADS = {
                  F_kind="tanh"),
         Workload("decode-bf16", 64, 4, 8192, "bf16", 606, "chain", weight_sd=0.02, layers=78,
                  F_kind="tanh"),
+        Workload("static-fp8", 16384, 4, 4096, "fp8", 707, "static", weight_sd=0.05, gamma_sd=0.1),
     ]
 }
 
@@ -114,8 +117,45 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def _fp8_table() -> np.ndarray:
+    """Values of the FP8 E4M3 codes 0..126 (the non-negative finite ones), in
+    increasing order: subnormals m * 2^-9, normals (1 + m/8) * 2^(e-7)."""
+    c = np.arange(127)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, np.ldexp(m, -9), np.ldexp(8 + m, e - 10)).astype(np.float64)
+
+
+_FP8_VALUES = _fp8_table()
+
+
+def f32_to_fp8_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to FP8 E4M3 (nearest, ties to the even code), saturating
+    at +-448; NaN -> 0x7F.  Returns uint8 codes."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    a = np.minimum(np.abs(x.astype(np.float64)), 448.0)
+    a = np.where(np.isnan(a), 0.0, a)
+    hi = np.clip(np.searchsorted(_FP8_VALUES, a), 1, 126)
+    lo = hi - 1
+    dlo, dhi = a - _FP8_VALUES[lo], _FP8_VALUES[hi] - a
+    code = np.where((dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0)), hi, lo).astype(np.uint8)
+    code = np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+    code[np.isnan(x)] = 0x7F
+    return code
+
+
+def fp8_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    v = _FP8_VALUES[np.minimum(b & 0x7F, 126)].astype(np.float32)
+    v[(b & 0x7F) == 0x7F] = np.nan
+    return np.where(b & 0x80, -v, v).astype(np.float32)
+
+
 def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
-    return f32_to_bf16_bits(x) if dtype == "bf16" else np.ascontiguousarray(x, np.float32)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "fp8":
+        return f32_to_fp8_bits(x)
+    return np.ascontiguousarray(x, np.float32)
 
 
 def identity_record(n: int) -> np.ndarray:

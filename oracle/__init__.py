@@ -14,6 +14,7 @@ from .oracle import (  # noqa: F401
     pre_mix_backward,
     round_bf16,
     round_f32,
+    round_fp8,
     set_threads,
     sinkhorn,
     weights,

@@ -10,8 +10,8 @@
  *
  * Style: every value is computed in IEEE double precision with scalar loops,
  * one token at a time, in the order the definitions below are written.  Inputs
- * arrive in their storage type (fp32, or bf16 bit patterns held in uint16_t)
- * and are widened exactly; outputs are written unrounded as doubles.  A
+ * arrive in their storage type (fp32, bf16 bit patterns held in uint16_t, or
+ * FP8 E4M3 codes held in uint8_t) and are widened exactly; outputs are written unrounded as doubles.  A
  * separate routine rounds doubles to a storage type (round to nearest, ties to
  * even, subnormals kept) so that callers can model what a bf16/fp32 store
  * does.  The only parallelism is an OpenMP loop over tokens, which are
@@ -54,7 +54,20 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2 };
+
+/* FP8 E4M3 ("fn", the OCP 8-bit float): sign, 4 exponent bits with bias 7, 3
+ * mantissa bits; no infinities; S.1111.111 is NaN; the largest finite value
+ * is 448 and the smallest subnormal 2^-9.  Value of one code. */
+static double orc_fp8_value(uint8_t b)
+{
+    const int e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7) v = NAN;
+    else if (e == 0) v = ldexp((double)m, -9);        /* subnormal: m * 2^-9 */
+    else v = ldexp((double)(8 + m), e - 10);          /* (1 + m/8) * 2^(e-7) */
+    return (b & 0x80) ? -v : v;
+}
 
 /* ---------------------------------------------------------------- storage */
 
@@ -63,6 +76,7 @@ enum { ORC_F32 = 0, ORC_BF16 = 1 };
 static double orc_load(const void* p, int64_t idx, int dt)
 {
     if (dt == ORC_F32) return (double)((const float*)p)[idx];
+    if (dt == ORC_FP8) return orc_fp8_value(((const uint8_t*)p)[idx]);
     uint32_t bits = (uint32_t)((const uint16_t*)p)[idx] << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
@@ -99,6 +113,40 @@ uint16_t orc_round_bf16(double v)
     uint16_t out = (uint16_t)(bits >> 16);
     if (neg) out |= 0x8000u;
     return out;
+}
+
+/* Round a double to FP8 E4M3, nearest with ties to even, saturating: magnitudes
+ * beyond the largest finite value (448, infinities included) store as +-448;
+ * NaN stores as NaN.  4 significant bits for normal values (e-1 >= -6),
+ * spacing 2^-9 below.  Returns the code. */
+uint8_t orc_round_fp8(double v)
+{
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v)) return (uint8_t)(sign | 0x7F);
+    double a = fabs(v);
+    if (a > 448.0) a = 448.0;
+    if (a == 0.0) return sign;
+    int e;
+    (void)frexp(a, &e);                          /* a = f * 2^e, 0.5 <= f < 1 */
+    const int q = (e - 1 >= -6) ? e - 4 : -9;    /* spacing exponent */
+    const double r = ldexp(rint(ldexp(a, -q)), q);
+    if (r == 0.0) return sign;
+    int er;
+    (void)frexp(r, &er);
+    uint8_t code;
+    if (er - 1 >= -6) {                          /* normal: r = (8 + m) 2^(E-10) */
+        const int E = er - 1 + 7;
+        const int m = (int)ldexp(r, -(E - 10)) - 8;
+        code = (uint8_t)((E << 3) | m);
+    } else {                                     /* subnormal: r = m 2^-9 */
+        code = (uint8_t)(int)ldexp(r, 9);
+    }
+    return (uint8_t)(sign | code);
+}
+
+void orc_round_fp8_array(const double* in, uint8_t* out, int64_t count)
+{
+    for (int64_t i = 0; i < count; ++i) out[i] = orc_round_fp8(in[i]);
 }
 
 void orc_round_bf16_array(const double* in, uint16_t* out, int64_t count)

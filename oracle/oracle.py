@@ -5,8 +5,8 @@ benchmark's CPU-baseline leg; the GPU library never imports it and it never
 imports the GPU library.
 
 Arrays are numpy arrays on the host.  Storage tensors (H, F, W, u) are passed
-in their storage type: ``np.float32`` for fp32 or ``np.uint16`` holding bf16
-bit patterns.  Weight records, gains and logits are ``np.float64`` (callers
+in their storage type: ``np.float32`` for fp32, ``np.uint16`` holding bf16 bit
+patterns or ``np.uint8`` holding FP8 E4M3 codes.  Weight records, gains and logits are ``np.float64`` (callers
 widen fp32 values exactly).  Every result is returned unrounded in float64;
 ``round_bf16`` / ``round_f32`` model a store to the storage type.
 
@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hc_oracle.c")
 _SO = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16 = 0, 1
+F32, BF16, FP8 = 0, 1, 2
 
 _lib = None
 
@@ -59,6 +59,7 @@ def load():
     lib.orc_block_tanh.argtypes = [vp, i32, dp, i64]
     lib.orc_round_bf16_array.argtypes = [dp, ctypes.POINTER(ctypes.c_uint16), i64]
     lib.orc_round_f32_array.argtypes = [dp, ctypes.POINTER(ctypes.c_float), i64]
+    lib.orc_round_fp8_array.argtypes = [dp, ctypes.POINTER(ctypes.c_uint8), i64]
     lib.orc_widen_array.argtypes = [vp, i32, dp, i64]
     lib.orc_post_mix_backward.argtypes = [vp, vp, vp, i32, dp, i64, dp, dp, dp, i64, i32, i32]
     lib.orc_pre_mix_backward.argtypes = [vp, vp, i32, dp, i64, dp, dbl, dp, dp, dp, dp, i64, i32, i32]
@@ -68,7 +69,7 @@ def load():
     lib.orc_get_threads.restype = i32
     for f in ("orc_pre_mix", "orc_post_mix", "orc_weights", "orc_sinkhorn",
               "orc_post_mix_backward", "orc_pre_mix_backward",
-              "orc_block_tanh", "orc_round_bf16_array", "orc_round_f32_array",
+              "orc_block_tanh", "orc_round_bf16_array", "orc_round_f32_array", "orc_round_fp8_array",
               "orc_widen_array", "orc_set_threads"):
         getattr(lib, f).restype = None
     _lib = lib
@@ -80,7 +81,10 @@ def _dt(a: np.ndarray) -> int:
         return F32
     if a.dtype == np.uint16:
         return BF16
-    raise TypeError(f"storage arrays must be float32 or uint16 (bf16 bits), got {a.dtype}")
+    if a.dtype == np.uint8:
+        return FP8
+    raise TypeError(f"storage arrays must be float32, uint16 (bf16 bits) or uint8 (fp8 e4m3 "
+                    f"codes), got {a.dtype}")
 
 
 def _c(a: np.ndarray, dtype=None) -> np.ndarray:
@@ -185,6 +189,16 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def round_fp8(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to FP8 E4M3 (nearest even, saturating at +-448);
+    returns uint8 codes."""
+    lib = load()
+    x = _c(x, np.float64)
+    out = np.empty(x.shape, np.uint8)
+    lib.orc_round_fp8_array(_dp(x), out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), x.size)
+    return out
+
+
 def round_f32(x: np.ndarray) -> np.ndarray:
     lib = load()
     x = _c(x, np.float64)
@@ -194,7 +208,7 @@ def round_f32(x: np.ndarray) -> np.ndarray:
 
 
 def widen(x: np.ndarray) -> np.ndarray:
-    """Exact float64 value of a storage array (float32 or bf16 bits)."""
+    """Exact float64 value of a storage array (float32, bf16 bits or fp8 codes)."""
     lib = load()
     x = _c(x)
     out = np.empty(x.shape, np.float64)

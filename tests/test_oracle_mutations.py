@@ -44,6 +44,10 @@ MUTANTS = {
     "pre bwd: dalpha from x": ("s += dx[k] * orc_load(H, e, dt);", "s += dx[k];"),
     "pre bwd: accumulation dropped": ("dH[e] = alpha[i] * dx[k] + (dH_in ? dH_in[e] : 0.0);", "dH[e] = alpha[i] * dx[k];"),
     "storage: no subnormal range": ("int q = (e - 1 >= -126) ? e - 8 : -133;", "int q = e - 8;"),
+    "fp8: exponent bias 8": ("else v = ldexp((double)(8 + m), e - 10);", "else v = ldexp((double)(8 + m), e - 11);"),
+    "fp8: subnormal scale": ("else if (e == 0) v = ldexp((double)m, -9);", "else if (e == 0) v = ldexp((double)m, -10);"),
+    "fp8: truncating": ("const double r = ldexp(rint(ldexp(a, -q)), q);", "const double r = ldexp(floor(ldexp(a, -q)), q);"),
+    "fp8: overflow to NaN": ("if (a > 448.0) a = 448.0;", "if (a > 464.0) return (uint8_t)(sign | 0x7F);"),
 }
 
 
