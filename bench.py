@@ -12,6 +12,8 @@ inputs are already resident in HBM:
   chain-bf16    78 layers of pre, tanh block, post (reported, not graded)
   decode-bf16   the same 78-layer loop at 64 tokens in flight (latency-bound;
                 use --graph to replay it as one HIP graph)
+  static-fp8    static-bf16's step with FP8 E4M3 storage (16384 tokens: the
+                same HBM bytes per step)
   tiny-f32      one small fp32 layer
 
 Timing: W untimed steps, then K timed steps between device synchronisations,
@@ -187,7 +189,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle CPU-baseline budget")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--fused", action="store_true",
-                    help="chain: fuse each write-back with the next read-mix")
+                    help="fuse each write-back with the next read-mix (chain: every layer; "
+                         "static: one step is one fused layer boundary)")
     ap.add_argument("--backward", action="store_true",
                     help="static workload: time the layer's gradients (post backward, pre "
                          "backward accumulating into the same dH, shared-weight sums)")
@@ -228,6 +231,8 @@ def main():
         a = np.ascontiguousarray(a)
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        if a.dtype == np.uint8:
+            return torch.from_numpy(a).view(torch.float8_e4m3fn).cuda()
         return torch.from_numpy(a.astype(np.float32)).cuda()
 
     t0 = time.time()
@@ -310,6 +315,10 @@ def main():
 
         ops = [("post_mix_backward", post_bwd), ("pre_mix_backward", pre_bwd)]
     # the kernels of one step, in order: (name, launch on buffer set b)
+    elif wl.kind == "static" and args.fused:
+        # one layer boundary: write-back of this layer fused with the next read-mix
+        ops = [("post_pre_mix", lambda b: hc.post_pre_mix(b["H"], b["F"], w_static, w_static, gamma,
+                                                          wl.eps, out=b["O"], u_out=b["u"]))]
     elif wl.kind == "static":
         ops = [("pre_mix", lambda b: hc.pre_mix(b["H"], w_static, gamma, wl.eps, out=b["u"])),
                ("post_mix", lambda b: hc.post_mix(b["H"], b["F"], w_static, out=b["O"]))]

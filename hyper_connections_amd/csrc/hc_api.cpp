@@ -30,10 +30,13 @@ bool overlap(Span a, Span b) {
     return x < y + static_cast<uintptr_t>(b.bytes) && y < x + static_cast<uintptr_t>(a.bytes);
 }
 
-int elem_bytes(hc_dtype dt) { return dt == HC_F32 ? 4 : 2; }
-int vec_elems(hc_dtype dt) { return dt == HC_F32 ? 4 : 8; }
+int elem_bytes(hc_dtype dt) { return dt == HC_F32 ? 4 : (dt == HC_FP8 ? 1 : 2); }
+int vec_elems(hc_dtype dt) { return 16 / elem_bytes(dt); }
 
-bool dtype_ok(hc_dtype dt) { return dt == HC_F32 || dt == HC_BF16; }
+// The streaming calls (pre, post, post+pre, tanh block) take every storage
+// dtype; the weight producer and the gradients take fp32 and bf16.
+bool dtype_ok(hc_dtype dt) { return dt == HC_F32 || dt == HC_BF16 || dt == HC_FP8; }
+bool dtype_wide(hc_dtype dt) { return dt == HC_F32 || dt == HC_BF16; }
 
 int record_len(int n) { return 2 * n + n * n; }
 
@@ -71,7 +74,7 @@ const char* hc_status_str(hc_status s) {
         case HC_OK: return "HC_OK: success";
         case HC_ERR_NULL: return "HC_ERR_NULL: a required pointer is NULL";
         case HC_ERR_SHAPE: return "HC_ERR_SHAPE: n, d or a stride is outside the supported set";
-        case HC_ERR_DTYPE: return "HC_ERR_DTYPE: unknown storage dtype";
+        case HC_ERR_DTYPE: return "HC_ERR_DTYPE: storage dtype unknown or not taken by this call";
         case HC_ERR_ALIGN: return "HC_ERR_ALIGN: a pointer is not aligned as required";
         case HC_ERR_ALIAS: return "HC_ERR_ALIAS: an output overlaps an input or another output";
         case HC_ERR_ARG: return "HC_ERR_ARG: T, eps or iters out of range";
@@ -150,6 +153,7 @@ hc_status hc_post_pre_mix(const void* H, const void* F, const float* w, int64_t 
 hc_status hc_weights(const void* H, const void* W, const float* w_static, float scale, float eps,
                      int32_t sinkhorn_iters, float* w_out, int64_t T, int32_t n, int32_t d,
                      hc_dtype dt, void* stream) {
+    if (!dtype_wide(dt)) return HC_ERR_DTYPE;
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
     if (!eps_ok(eps) || !std::isfinite(scale)) return HC_ERR_ARG;
@@ -189,6 +193,7 @@ hc_status hc_post_mix_backward(const void* dH_out, const void* H, const void* F,
                                int64_t w_stride, void* dH, void* dF, float* dw, void* workspace,
                                int64_t workspace_bytes, int64_t T, int32_t n, int32_t d,
                                hc_dtype dt, void* stream) {
+    if (!dtype_wide(dt)) return HC_ERR_DTYPE;
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
     const int K = record_len(n);
@@ -222,6 +227,7 @@ hc_status hc_pre_mix_backward(const void* du, const void* H, const float* w, int
                               const float* gamma, float eps, const void* dH_in, void* dH,
                               float* dw, float* dgamma, void* workspace, int64_t workspace_bytes,
                               int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream) {
+    if (!dtype_wide(dt)) return HC_ERR_DTYPE;
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
     const int K = record_len(n);

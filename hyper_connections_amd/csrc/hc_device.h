@@ -1,8 +1,8 @@
 // hc_device.h -- device helpers shared by the libhc.so kernels (gfx950).
 //
-// Storage: 16-byte vectors (8 bf16 or 4 fp32 values) are the unit of every
-// HBM access; values are widened to fp32 in registers and rounded once on the
-// way out (nearest, ties to even, via the hardware bf16 packer).
+// Storage: 16-byte vectors (4 fp32, 8 bf16 or 16 fp8 values) are the unit of
+// every HBM access; values are widened to fp32 in registers and rounded once
+// on the way out (nearest, ties to even, via the hardware packers).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -10,13 +10,16 @@
 
 namespace hc {
 
-// Tag types for the two storage formats.
+// Tag types for the storage formats.  fp8_t is E4M3 (the OCP 8-bit float:
+// 4 exponent bits, bias 7, 3 mantissa bits, no infinities, largest 448).
 struct f32_t {};
 struct bf16_t {};
+struct fp8_t {};
 
 template <typename S> struct Store;
 template <> struct Store<f32_t> { static constexpr int kElems = 4; static constexpr int kBytes = 4; };
 template <> struct Store<bf16_t> { static constexpr int kElems = 8; static constexpr int kBytes = 2; };
+template <> struct Store<fp8_t> { static constexpr int kElems = 16; static constexpr int kBytes = 1; };
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -49,6 +52,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, b);
 }
 
+// FP8 E4M3: four codes per dword, element 0 in the low byte.  Widening is
+// exact (v_cvt_pk_f32_fp8 decodes two codes).  Narrowing rounds to nearest
+// even with v_cvt_pk_fp8_f32, which turns anything beyond the largest finite
+// code into NaN; values are first saturated to [-448, 448] with the IEEE
+// maximum/minimum operations (v_maximum3/v_minimum3), which pass NaN through,
+// so NaN stays NaN and only overflow is clipped.
+__device__ __forceinline__ void unpack_fp8x4(uint32_t w, float* f) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    f[0] = lo.x; f[1] = lo.y; f[2] = hi.x; f[3] = hi.y;
+}
+__device__ __forceinline__ float sat_fp8(float x) {
+    return __builtin_elementwise_minimum(__builtin_elementwise_maximum(x, -448.0f), 448.0f);
+}
+__device__ __forceinline__ uint32_t pack_fp8x4(const float* f) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_fp8(f[0]), sat_fp8(f[1]), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_fp8(f[2]), sat_fp8(f[3]), w, true);
+    return (uint32_t)w;
+}
+
 template <typename S> __device__ __forceinline__ void unpack(uint4 v, float* f);
 template <> __device__ __forceinline__ void unpack<bf16_t>(uint4 v, float* f) {
     f[0] = lo_bf16(v.x); f[1] = hi_bf16(v.x);
@@ -61,6 +84,11 @@ template <> __device__ __forceinline__ void unpack<f32_t>(uint4 v, float* f) {
     f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
 }
 
+template <> __device__ __forceinline__ void unpack<fp8_t>(uint4 v, float* f) {
+    unpack_fp8x4(v.x, f); unpack_fp8x4(v.y, f + 4);
+    unpack_fp8x4(v.z, f + 8); unpack_fp8x4(v.w, f + 12);
+}
+
 template <typename S> __device__ __forceinline__ uint4 pack(const float* f);
 template <> __device__ __forceinline__ uint4 pack<bf16_t>(const float* f) {
     return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
@@ -69,6 +97,40 @@ template <> __device__ __forceinline__ uint4 pack<bf16_t>(const float* f) {
 template <> __device__ __forceinline__ uint4 pack<f32_t>(const float* f) {
     return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
                       __float_as_uint(f[2]), __float_as_uint(f[3]));
+}
+template <> __device__ __forceinline__ uint4 pack<fp8_t>(const float* f) {
+    return make_uint4(pack_fp8x4(f), pack_fp8x4(f + 4), pack_fp8x4(f + 8), pack_fp8x4(f + 12));
+}
+
+// Per-dword access: a 16-byte vector is 4 dwords of kWordElems values each
+// (1 fp32, 2 bf16, 4 fp8).  Kernels that work dword by dword keep fewer
+// values live at once than a whole-vector unpack.
+template <typename S> struct Word { static constexpr int kElems = 4 / Store<S>::kBytes; };
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int q) {
+    return q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
+}
+
+template <typename S> __device__ __forceinline__ void unpack_word(uint32_t w, float* f);
+template <> __device__ __forceinline__ void unpack_word<f32_t>(uint32_t w, float* f) {
+    f[0] = __uint_as_float(w);
+}
+template <> __device__ __forceinline__ void unpack_word<bf16_t>(uint32_t w, float* f) {
+    f[0] = lo_bf16(w); f[1] = hi_bf16(w);
+}
+template <> __device__ __forceinline__ void unpack_word<fp8_t>(uint32_t w, float* f) {
+    unpack_fp8x4(w, f);
+}
+
+template <typename S> __device__ __forceinline__ uint32_t pack_word(const float* f);
+template <> __device__ __forceinline__ uint32_t pack_word<f32_t>(const float* f) {
+    return __float_as_uint(f[0]);
+}
+template <> __device__ __forceinline__ uint32_t pack_word<bf16_t>(const float* f) {
+    return pack_bf16x2(f[0], f[1]);
+}
+template <> __device__ __forceinline__ uint32_t pack_word<fp8_t>(const float* f) {
+    return pack_fp8x4(f);
 }
 
 // Sum over the 64 lanes of a wave with DPP row shifts and row broadcasts (no

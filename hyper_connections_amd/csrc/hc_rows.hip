@@ -10,7 +10,7 @@
 // token" (the n-fold state handed across every layer boundary is what these
 // kernels move).
 //
-// Design (HBM-bound, 1.9 flop/byte at n = 4 bf16):
+// Design (HBM-bound, 1.9 flop/byte at n = 4 bf16, 3.8 at fp8):
 //  - One workgroup per token row; a thread owns VPT 16-byte vectors of the
 //    row at positions tid, tid + B, ... (B = blockDim) and the same positions
 //    of every stream, so each wave instruction touches 1 KiB of contiguous
@@ -37,7 +37,7 @@ template <int N, typename S, int VPT>
 __global__ __launch_bounds__(1024) void pre_mix_kernel(
     const uint8_t* __restrict__ H, const float* __restrict__ w, int64_t w_stride,
     const float* __restrict__ gamma, float eps, uint8_t* __restrict__ u, int64_t T, int d) {
-    constexpr int V = Store<S>::kElems;
+    constexpr int V = Store<S>::kElems, E = Word<S>::kElems;
     __shared__ float red[16];
     const int B = blockDim.x;
     const int nvec = d / V;
@@ -66,15 +66,19 @@ __global__ __launch_bounds__(1024) void pre_mix_kernel(
         for (int j = 0; j < VPT; ++j) {
             const int v = threadIdx.x + j * B;
             if (v < nvec) {
-                float h[V];
-                unpack<S>(raw[0][j], h);
 #pragma unroll
-                for (int e = 0; e < V; ++e) x[j][e] = alpha[0] * h[e];
+                for (int q = 0; q < 4; ++q) {
+                    float h[E];
+                    float* xq = &x[j][q * E];
+                    unpack_word<S>(word(raw[0][j], q), h);
 #pragma unroll
-                for (int i = 1; i < N; ++i) {
-                    unpack<S>(raw[i][j], h);
+                    for (int e = 0; e < E; ++e) xq[e] = alpha[0] * h[e];
 #pragma unroll
-                    for (int e = 0; e < V; ++e) x[j][e] = fmaf(alpha[i], h[e], x[j][e]);
+                    for (int i = 1; i < N; ++i) {
+                        unpack_word<S>(word(raw[i][j], q), h);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) xq[e] = fmaf(alpha[i], h[e], xq[e]);
+                    }
                 }
 #pragma unroll
                 for (int e = 0; e < V; ++e) ss = fmaf(x[j][e], x[j][e], ss);
@@ -119,7 +123,7 @@ template <int N, typename S, int VPT>
 __global__ __launch_bounds__(1024) void post_mix_kernel(
     const uint8_t* H, const uint8_t* __restrict__ F, const float* __restrict__ w,
     int64_t w_stride, uint8_t* H_out, int64_t T, int d) {
-    constexpr int V = Store<S>::kElems;
+    constexpr int V = Store<S>::kElems, E = Word<S>::kElems;
     const int B = blockDim.x;
     const int nvec = d / V;
     const int64_t row_bytes = (int64_t)d * Store<S>::kBytes;
@@ -152,22 +156,29 @@ __global__ __launch_bounds__(1024) void post_mix_kernel(
         for (int j = 0; j < VPT; ++j) {
             const int v = threadIdx.x + j * B;
             if (v < nvec) {
-                float h[N][V], f[V];
+                uint32_t o[N][4];
 #pragma unroll
-                for (int i = 0; i < N; ++i) unpack<S>(rh[i][j], h[i]);
-                unpack<S>(rf[j], f);
+                for (int q = 0; q < 4; ++q) {          // dword by dword
+                    float h[N][E], f[E];
 #pragma unroll
-                for (int i = 0; i < N; ++i) {
-                    float y[V];
+                    for (int i = 0; i < N; ++i) unpack_word<S>(word(rh[i][j], q), h[i]);
+                    unpack_word<S>(word(rf[j], q), f);
 #pragma unroll
-                    for (int e = 0; e < V; ++e) {
-                        float acc = A[i][0] * h[0][e];
+                    for (int i = 0; i < N; ++i) {
+                        float y[E];
 #pragma unroll
-                        for (int k = 1; k < N; ++k) acc = fmaf(A[i][k], h[k][e], acc);
-                        y[e] = fmaf(beta[i], f[e], acc);
+                        for (int e = 0; e < E; ++e) {
+                            float acc = A[i][0] * h[0][e];
+#pragma unroll
+                            for (int k = 1; k < N; ++k) acc = fmaf(A[i][k], h[k][e], acc);
+                            y[e] = fmaf(beta[i], f[e], acc);
+                        }
+                        o[i][q] = pack_word<S>(y);
                     }
-                    st16_stream(Ot + i * row_bytes + v * 16, pack<S>(y));
                 }
+#pragma unroll
+                for (int i = 0; i < N; ++i)
+                    st16_stream(Ot + i * row_bytes + v * 16, make_uint4(o[i][0], o[i][1], o[i][2], o[i][3]));
             }
         }
     }
@@ -185,7 +196,7 @@ __global__ __launch_bounds__(1024) void post_pre_mix_kernel(
     int64_t w_stride, const float* __restrict__ w_next, int64_t w_next_stride,
     const float* __restrict__ gamma, float eps, uint8_t* H_out, uint8_t* __restrict__ u_next,
     int64_t T, int d) {
-    constexpr int V = Store<S>::kElems;
+    constexpr int V = Store<S>::kElems, E = Word<S>::kElems;
     __shared__ float red[16];
     const int B = blockDim.x;
     const int nvec = d / V;
@@ -224,32 +235,39 @@ __global__ __launch_bounds__(1024) void post_pre_mix_kernel(
         for (int j = 0; j < VPT; ++j) {
             const int v = threadIdx.x + j * B;
             if (v < nvec) {
-                float h[N][V], f[V];
+                uint32_t o[N][4];
 #pragma unroll
-                for (int i = 0; i < N; ++i) unpack<S>(rh[i][j], h[i]);
-                unpack<S>(rf[j], f);
+                for (int q = 0; q < 4; ++q) {          // dword by dword
+                    float h[N][E], f[E];
+                    float* xq = &x[j][q * E];
 #pragma unroll
-                for (int i = 0; i < N; ++i) {
-                    float y[V];
+                    for (int i = 0; i < N; ++i) unpack_word<S>(word(rh[i][j], q), h[i]);
+                    unpack_word<S>(word(rf[j], q), f);
 #pragma unroll
-                    for (int e = 0; e < V; ++e) {
-                        float acc = A[i][0] * h[0][e];
+                    for (int i = 0; i < N; ++i) {
+                        float y[E];
 #pragma unroll
-                        for (int k = 1; k < N; ++k) acc = fmaf(A[i][k], h[k][e], acc);
-                        y[e] = fmaf(beta[i], f[e], acc);
-                    }
-                    const uint4 p = pack<S>(y);
-                    st16_stream(Ot + i * row_bytes + v * 16, p);
-                    float yr[V];
-                    unpack<S>(p, yr);             // the stored (rounded) values
-                    if (i == 0) {
+                        for (int e = 0; e < E; ++e) {
+                            float acc = A[i][0] * h[0][e];
 #pragma unroll
-                        for (int e = 0; e < V; ++e) x[j][e] = alpha[0] * yr[e];
-                    } else {
+                            for (int k = 1; k < N; ++k) acc = fmaf(A[i][k], h[k][e], acc);
+                            y[e] = fmaf(beta[i], f[e], acc);
+                        }
+                        o[i][q] = pack_word<S>(y);
+                        float yr[E];
+                        unpack_word<S>(o[i][q], yr);   // the stored (rounded) values
+                        if (i == 0) {
 #pragma unroll
-                        for (int e = 0; e < V; ++e) x[j][e] = fmaf(alpha[i], yr[e], x[j][e]);
+                            for (int e = 0; e < E; ++e) xq[e] = alpha[0] * yr[e];
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < E; ++e) xq[e] = fmaf(alpha[i], yr[e], xq[e]);
+                        }
                     }
                 }
+#pragma unroll
+                for (int i = 0; i < N; ++i)
+                    st16_stream(Ot + i * row_bytes + v * 16, make_uint4(o[i][0], o[i][1], o[i][2], o[i][3]));
 #pragma unroll
                 for (int e = 0; e < V; ++e) ss = fmaf(x[j][e], x[j][e], ss);
             }
@@ -326,13 +344,19 @@ struct PostPreL {
 
 template <class L, int N, typename S, typename... A>
 hipError_t by_cfg(RowCfg c, int64_t T, hipStream_t s, A... a) {
-    switch (c.vpt) {
-        case 1: return L::template go<N, S, 1>(c, T, s, a...);
-        case 2: return L::template go<N, S, 2>(c, T, s, a...);
-        case 3: return L::template go<N, S, 3>(c, T, s, a...);
-        case 4: return L::template go<N, S, 4>(c, T, s, a...);
+    if constexpr (Store<S>::kElems == 16) {
+        // fp8 rows hold at most HC_MAX_HIDDEN / 16 = 1024 vectors: one per thread
+        if (c.vpt == 1) return L::template go<N, S, 1>(c, T, s, a...);
+        return hipErrorInvalidConfiguration;
+    } else {
+        switch (c.vpt) {
+            case 1: return L::template go<N, S, 1>(c, T, s, a...);
+            case 2: return L::template go<N, S, 2>(c, T, s, a...);
+            case 3: return L::template go<N, S, 3>(c, T, s, a...);
+            case 4: return L::template go<N, S, 4>(c, T, s, a...);
+        }
+        return hipErrorInvalidConfiguration;
     }
-    return hipErrorInvalidConfiguration;
 }
 
 template <class L, typename S, typename... A>
@@ -349,6 +373,7 @@ hipError_t by_n(int n, RowCfg c, int64_t T, hipStream_t s, A... a) {
 template <class L, typename... A>
 hipError_t dispatch_rows(int n, int d, int dt, int64_t T, hipStream_t s, A... a) {
     if (dt == 0) return by_n<L, f32_t>(n, row_config(d / Store<f32_t>::kElems), T, s, a...);
+    if (dt == 2) return by_n<L, fp8_t>(n, row_config(d / Store<fp8_t>::kElems), T, s, a...);
     return by_n<L, bf16_t>(n, row_config(d / Store<bf16_t>::kElems), T, s, a...);
 }
 
@@ -378,12 +403,16 @@ hipError_t launch_post_pre_mix(const void* H, const void* F, const float* w, int
 }
 
 hipError_t launch_block_tanh(const void* u, void* F, int64_t count, int dt, hipStream_t s) {
-    const int V = dt == 0 ? Store<f32_t>::kElems : Store<bf16_t>::kElems;
+    const int V = dt == 0 ? Store<f32_t>::kElems
+                          : (dt == 2 ? Store<fp8_t>::kElems : Store<bf16_t>::kElems);
     const int64_t nvec = count / V;
     const int64_t blocks = (nvec + 255) / 256;
     const dim3 grid((unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid));
     if (dt == 0)
         return launch(block_tanh_kernel<f32_t>, grid, dim3(256), 0, s,
+                      static_cast<const uint8_t*>(u), static_cast<uint8_t*>(F), nvec);
+    if (dt == 2)
+        return launch(block_tanh_kernel<fp8_t>, grid, dim3(256), 0, s,
                       static_cast<const uint8_t*>(u), static_cast<uint8_t*>(F), nvec);
     return launch(block_tanh_kernel<bf16_t>, grid, dim3(256), 0, s,
                   static_cast<const uint8_t*>(u), static_cast<uint8_t*>(F), nvec);

@@ -7,7 +7,9 @@ current HIP stream to the C entry point of the same name, and raises
 work runs in the library's kernels; there is no CPU fallback, and the module
 raises on first use if the library is not built.
 
-Tensor conventions (storage dtype torch.bfloat16 or torch.float32):
+Tensor conventions (storage dtype torch.float32, torch.bfloat16 or
+torch.float8_e4m3fn; the last for pre_mix, post_mix, post_pre_mix and
+block_tanh only):
   H      (T, n, d)      residual streams
   u, F   (T, d)         block input / block output
   w      (K,) float32   one weight record shared by all tokens, or
@@ -26,7 +28,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhc.so")
 
-HC_F32, HC_BF16 = 0, 1
+HC_F32, HC_BF16, HC_FP8 = 0, 1, 2
 MAX_STREAMS = 4
 MAX_HIDDEN = 16384
 MAX_SINKHORN_ITERS = 10000
@@ -101,9 +103,11 @@ def _stream(stream) -> int:
 def _dt(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return HC_BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return HC_FP8
     if t.dtype == torch.float32:
         return HC_F32
-    raise TypeError(f"storage dtype must be bfloat16 or float32, got {t.dtype}")
+    raise TypeError(f"storage dtype must be float8_e4m3fn, bfloat16 or float32, got {t.dtype}")
 
 
 def _dev(t: torch.Tensor, what: str) -> torch.Tensor:

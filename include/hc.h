@@ -22,7 +22,8 @@
  *  - Block input u and block output F: [T][d] contiguous.
  *  - Storage dtype (hc_dtype) applies to H, F, u, H_out and W.  Arithmetic is
  *    fp32; results are rounded once to the storage type (nearest, ties to
- *    even; subnormals kept).
+ *    even; subnormals kept).  FP8 stores saturate: magnitudes beyond 448
+ *    (infinities included) store as +-448; NaN stays NaN.
  *  - Weight record: K = 2n + n^2 fp32 values
  *        [alpha_0..alpha_{n-1} | beta_0..beta_{n-1} | A row-major]
  *    A[i][j] (at 2n + i*n + j) weighs input stream j into output stream i.
@@ -39,8 +40,9 @@
  *    returns its code with nothing enqueued.  A launch failure reported by the
  *    HIP runtime returns HC_ERR_HIP.  No exception crosses the ABI and the
  *    library never prints.
- *  - Sizes: 1 <= n <= 4; 1 <= d <= HC_MAX_HIDDEN; d % 8 == 0 for bf16 and
- *    d % 4 == 0 for fp32 (16-byte vectors) else HC_ERR_SHAPE.  T < 0 is
+ *  - Sizes: 1 <= n <= 4; 1 <= d <= HC_MAX_HIDDEN; d % 16 == 0 for fp8,
+ *    d % 8 == 0 for bf16 and d % 4 == 0 for fp32 (16-byte vectors) else
+ *    HC_ERR_SHAPE.  T < 0 is
  *    HC_ERR_ARG.  T == 0 (count == 0 for hc_block_tanh) is a no-op returning
  *    HC_OK once the scalar arguments are valid; the data pointers are then
  *    not checked and may be NULL (an empty tensor has no storage).
@@ -62,14 +64,20 @@ typedef enum hc_status {
     HC_OK = 0,
     HC_ERR_NULL = 1,   /* a required pointer is NULL                        */
     HC_ERR_SHAPE = 2,  /* n, d or a stride outside the supported set       */
-    HC_ERR_DTYPE = 3,  /* unknown hc_dtype                                  */
+    HC_ERR_DTYPE = 3,  /* unknown hc_dtype, or one the call does not take   */
     HC_ERR_ALIGN = 4,  /* pointer not aligned as required                   */
     HC_ERR_ALIAS = 5,  /* an output overlaps an input or another output     */
     HC_ERR_ARG = 6,    /* T < 0, eps not positive/finite, iters out of range */
     HC_ERR_HIP = 7     /* the HIP runtime reported a launch error           */
 } hc_status;
 
-typedef enum hc_dtype { HC_F32 = 0, HC_BF16 = 1 } hc_dtype;
+/* Storage dtypes.  HC_FP8 is E4M3 (OCP 8-bit float: 4 exponent bits, bias 7,
+ * 3 mantissa bits, no infinities, largest finite 448).  The release ships
+ * BF16 and FP8 weights ([EXPL] "The news"; [MAP] "inference quantization");
+ * the pages name no 8-bit format, E4M3 is the one implemented.  FP8 is taken
+ * by hc_pre_mix, hc_post_mix, hc_post_pre_mix and hc_block_tanh; hc_weights
+ * and the gradient calls return HC_ERR_DTYPE for it. */
+typedef enum hc_dtype { HC_F32 = 0, HC_BF16 = 1, HC_FP8 = 2 } hc_dtype;
 
 #define HC_MAX_STREAMS 4
 #define HC_MAX_HIDDEN 16384
@@ -188,7 +196,8 @@ hc_status hc_sum_records(const float* rec, int64_t T, int32_t K, float* out, voi
 
 /* Stand-in block used by the benchmarks and tests, not part of the method:
  * F = tanh(u) elementwise ([EXPL] "Jargon", Residual connection: the block
- * computes f(x)).  count % 8 == 0 (bf16) or count % 4 == 0 (fp32). */
+ * computes f(x)).  count % 16 == 0 (fp8), count % 8 == 0 (bf16) or
+ * count % 4 == 0 (fp32). */
 hc_status hc_block_tanh(const void* u, void* F, int64_t count, hc_dtype dt, void* stream);
 
 /* Static string naming a status code; never NULL. */

@@ -9,7 +9,13 @@ RMS stops cancellation near zero from failing a correct result.
 Tolerances: 1e-5 for fp32 storage; 2e-2 for bf16 storage with fp32
 arithmetic.  For bf16 the tests also require one bf16 unit in the last place
 (2^-8 of the row scale), which a correctly rounded store plus fp32 arithmetic
-meets with margin."""
+meets with margin.  For FP8 E4M3 storage (3 mantissa bits) the bound is one
+FP8 unit in the last place, 2^-3 of the value (or of the row scale), and the
+stored codes must equal the oracle's rounding of its fp64 value except for
+at most 1 + 0.1% of them: fp32 arithmetic moves a value across an FP8
+rounding boundary only when it lies within about 1e-6 (relative) of one.
+FP8 stores saturate, so FP8 results are compared with the reference clipped
+to +-448."""
 from __future__ import annotations
 
 import numpy as np
@@ -21,6 +27,7 @@ import oracle
 TOL_F32 = 1e-5
 TOL_BF16 = 2e-2
 TOL_BF16_ULP = 2.0 ** -8
+TOL_FP8 = 2.0 ** -3
 TOL_RECORD = 1e-5      # fp32 weight records (any storage dtype of H)
 
 
@@ -30,27 +37,32 @@ def need_gpu():
 
 
 def dev(a: np.ndarray) -> torch.Tensor:
-    """Storage array (float32 or uint16 bf16 bits) -> device tensor."""
+    """Storage array (float32, uint16 bf16 bits or uint8 fp8 codes) -> device tensor."""
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    if a.dtype == np.uint8:
+        return torch.from_numpy(a).view(torch.float8_e4m3fn).cuda()
     if a.dtype in (np.float32, np.float64):
         return torch.from_numpy(a.astype(np.float32)).cuda()
     raise TypeError(a.dtype)
 
 
 def host(t: torch.Tensor) -> np.ndarray:
-    """Device tensor -> storage array (uint16 bits for bf16)."""
+    """Device tensor -> storage array (uint16 bits for bf16, uint8 codes for fp8)."""
     t = t.detach().contiguous().cpu()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16).copy()
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy().copy()
     return t.numpy().copy()
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     """Max over elements of |got - ref| / max(|ref|, rms(ref row)); rows are
     the last axis.  NaNs must match position for position."""
-    g = oracle.widen(got) if got.dtype in (np.uint16, np.float32) else np.asarray(got, np.float64)
+    g = (oracle.widen(got) if got.dtype in (np.uint8, np.uint16, np.float32)
+         else np.asarray(got, np.float64))
     r = np.asarray(ref, np.float64)
     assert g.shape == r.shape, (g.shape, r.shape)
     if g.size == 0:
@@ -72,8 +84,18 @@ def check(got: np.ndarray, ref: np.ndarray, what: str = "", one_ulp: bool = True
     """Assert the storage-dtype tolerance; returns the error.  `one_ulp=False`
     drops the one-ulp bound for results stored twice (an accumulation into a
     rounded buffer), which only the 2e-2 tolerance covers."""
+    if got.dtype == np.uint8:
+        # FP8 stores saturate at +-448: compare with the reference so clipped
+        ref = np.asarray(ref, np.float64)
+        ref = np.where(np.abs(ref) > 448.0, np.copysign(448.0, ref), ref)
     e = rel_err(got, ref)
-    if got.dtype == np.uint16:
+    if got.dtype == np.uint8:
+        assert e <= TOL_FP8, f"{what}: max rel err {e:.3g} > one fp8 ulp"
+        want = oracle.round_fp8(np.asarray(ref, np.float64))
+        fin = ~np.isnan(np.asarray(ref, np.float64))
+        bad = int(np.count_nonzero(want[fin] != got[fin]))
+        assert bad <= 1 + fin.sum() // 1000, f"{what}: {bad} of {fin.sum()} fp8 codes differ"
+    elif got.dtype == np.uint16:
         assert e <= TOL_BF16, f"{what}: max rel err {e:.3g} > {TOL_BF16}"
         if one_ulp:
             assert e <= TOL_BF16_ULP, f"{what}: max rel err {e:.3g} > one bf16 ulp"
@@ -84,4 +106,6 @@ def check(got: np.ndarray, ref: np.ndarray, what: str = "", one_ulp: bool = True
 
 def rounded(ref64: np.ndarray, like: np.ndarray) -> np.ndarray:
     """The oracle's value stored in the storage dtype of `like`."""
+    if like.dtype == np.uint8:
+        return oracle.round_fp8(ref64)
     return oracle.round_bf16(ref64) if like.dtype == np.uint16 else oracle.round_f32(ref64)

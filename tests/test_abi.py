@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hc.h")
 
 OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, ARG = 0, 1, 2, 3, 4, 5, 6
-BF16, F32 = hc.HC_BF16, hc.HC_F32
+BF16, F32, FP8 = hc.HC_BF16, hc.HC_F32, hc.HC_FP8
 
 # fake, never dereferenced device addresses (16-byte aligned, far apart)
 P = [0x10000000 * (i + 1) for i in range(8)]
@@ -71,7 +71,11 @@ def test_pre_validation(L):
     assert pre(L, d=4092) == SHAPE                 # bf16 needs d % 8 == 0
     assert pre(L, d=4092, dt=F32, T=0) == OK       # fp32 needs d % 4 == 0
     assert pre(L, d=0) == SHAPE and pre(L, d=hc.MAX_HIDDEN + 8) == SHAPE
-    assert pre(L, dt=2) == DTYPE
+    assert pre(L, dt=3) == DTYPE
+    assert pre(L, dt=FP8, T=0) == OK
+    assert pre(L, dt=FP8, d=4088) == SHAPE and pre(L, dt=FP8, d=4088, T=0) == SHAPE   # d % 16
+    assert pre(L, dt=FP8, u=P[3] + 8) == ALIGN
+    assert pre(L, dt=FP8, u=P[0] + 16 * 4096) == ALIAS   # u inside the fp8 H (16 x 4 x 4096 B)
     assert pre(L, T=-1) == ARG
     assert pre(L, eps=0.0) == ARG and pre(L, eps=-1.0) == ARG and pre(L, eps=float("inf")) == ARG
     assert pre(L, ws=5) == SHAPE                   # stride must be 0 or >= K = 24
@@ -119,6 +123,7 @@ def test_weights_validation(L):
     assert f(W=P[1] + 8) == ALIGN and f(o=P[3] + 2) == ALIGN
     assert f(o=P[0] + 64) == ALIAS and f(o=P[1]) == ALIAS
     assert f(n=0) == SHAPE and f(d=100) == SHAPE and f(dt=5) == DTYPE
+    assert f(dt=FP8) == DTYPE and f(dt=FP8, T=0) == DTYPE     # fp8 weights not taken
 
 
 def test_backward_validation(L):
@@ -128,7 +133,8 @@ def test_backward_validation(L):
     pb = lambda **k: L.hc_post_mix_backward(  # noqa: E731
         k.get("g", P[0]), k.get("H", P[1]), k.get("F", P[2]), k.get("w", P[3]), k.get("ws", 0),
         k.get("dH", P[4]), k.get("dF", P[5]), k.get("dw", P[6]), k.get("wk", P[7]),
-        k.get("wkb", ws_need), k.get("T", 8), 4, 4096, BF16, None)
+        k.get("wkb", ws_need), k.get("T", 8), 4, 4096, k.get("dt", BF16), None)
+    assert pb(dt=FP8) == DTYPE and pb(dt=FP8, T=0) == DTYPE
     assert pb(T=0) == OK and pb(T=0, dH=None) == OK
     assert pb(dF=None) == NULL and pb(ws=2) == SHAPE and pb(dH=P[4] + 8) == ALIGN
     assert pb(wk=None) == NULL and pb(wkb=ws_need - 1) == ARG and pb(wk=P[7] + 4) == ALIGN
@@ -137,7 +143,9 @@ def test_backward_validation(L):
     qb = lambda **k: L.hc_pre_mix_backward(  # noqa: E731
         k.get("du", P[0]), k.get("H", P[1]), k.get("w", P[2]), k.get("ws", 0), k.get("g", P[3]),
         k.get("eps", 1e-6), k.get("din", None), k.get("dH", P[4]), k.get("dw", P[5]),
-        k.get("dg", P[6]), k.get("wk", P[7]), k.get("wkb", ws_need), k.get("T", 8), 4, 4096, BF16, None)
+        k.get("dg", P[6]), k.get("wk", P[7]), k.get("wkb", ws_need), k.get("T", 8), 4, 4096,
+        k.get("dt", BF16), None)
+    assert qb(dt=FP8) == DTYPE and qb(dt=FP8, T=0) == DTYPE
     assert qb(T=0) == OK and qb(eps=0.0) == ARG and qb(wkb=ws_need - 4) == ARG
     assert qb(wk=None) == NULL and qb(dg=P[6] + 2) == ALIGN and qb(wk=P[7] + 8) == ALIGN
     assert qb(din=P[4] + 16) == ALIAS and qb(dH=P[1]) == ALIAS and qb(wk=P[5]) == ALIAS
@@ -159,6 +167,7 @@ def test_block_tanh_validation(L):
                                     k.get("dt", BF16), None)
     assert f(c=0) == OK and f(c=-8) == ARG and f(c=12) == SHAPE and f(c=12, dt=F32, F=P[0] + 16) == ALIAS
     assert f(u=None) == NULL and f(dt=4) == DTYPE and f(F=P[1] + 4) == ALIGN
+    assert f(dt=FP8, c=4104) == SHAPE and f(dt=FP8, F=P[0] + 4000) == ALIAS   # 4104 % 16 = 8
 
 
 def test_binding_rejects_host_tensors():

@@ -3,8 +3,8 @@ against the fp64 oracle, through the C ABI.
 
 Cases span every launch shape of the row kernels (blocks of 64..1024 threads
 with 1, 2, 3 and 4 vectors per thread), ragged rows (d not a multiple of the
-block's vector count), small odd T, both storage dtypes, n = 1..4, shared and
-per-token weight records."""
+block's vector count), small odd T, the three storage dtypes (fp32, bf16, FP8
+E4M3), n = 1..4, shared and per-token weight records."""
 import numpy as np
 import pytest
 import torch
@@ -12,18 +12,22 @@ import torch
 import oracle
 from gpu_util import check, dev, host, need_gpu, rel_err, rounded
 from hyper_connections_amd import hc
-from hyper_connections_amd.workloads import (f32_to_bf16_bits, identity_record, make_inputs,
-                                             workload)
+from hyper_connections_amd.workloads import (f32_to_bf16_bits, f32_to_fp8_bits, identity_record,
+                                             make_inputs, workload)
 
 pytestmark = pytest.mark.gpu
 
 # d values per dtype: covers every (block, vectors-per-thread) launch shape
 D_BF16 = [8, 40, 520, 2048, 4096, 6144, 8192, 8200, 16384]
 D_F32 = [4, 36, 516, 1024, 3072, 4096, 4100, 8196, 12288, 12296, 16384]
-SHAPES = [("bf16", d) for d in D_BF16] + [("f32", d) for d in D_F32]
+D_FP8 = [16, 48, 1040, 4096, 8192, 8208, 12288, 16384]
+SHAPES = ([("bf16", d) for d in D_BF16] + [("f32", d) for d in D_F32] +
+          [("fp8", d) for d in D_FP8])
 
 
 def storage(x: np.ndarray, dt: str) -> np.ndarray:
+    if dt == "fp8":
+        return f32_to_fp8_bits(x)
     return f32_to_bf16_bits(x) if dt == "bf16" else x.astype(np.float32)
 
 
@@ -66,7 +70,7 @@ def test_post_parity(dt, d, n):
     check(out, ref, f"post n={n} d={d} {dt}")
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("dt", ["bf16", "f32", "fp8"])
 @pytest.mark.parametrize("n", [1, 4])
 def test_post_in_place(dt, n):
     rng = np.random.default_rng(7)
@@ -79,7 +83,8 @@ def test_post_in_place(dt, n):
 
 
 @pytest.mark.parametrize("dt,d", [("bf16", 8), ("bf16", 4096), ("bf16", 6144), ("bf16", 16384),
-                                  ("f32", 1024), ("f32", 16384)])
+                                  ("f32", 1024), ("f32", 16384), ("fp8", 16), ("fp8", 4096),
+                                  ("fp8", 8208)])
 @pytest.mark.parametrize("n", [1, 2, 3, 4])
 def test_identity_post_is_plain_residual_bitwise(dt, d, n):
     """alpha = e_0, beta = 1, A = I on n copies of x: every stream is the
@@ -99,20 +104,25 @@ def test_identity_post_is_plain_residual_bitwise(dt, d, n):
 
 
 @pytest.mark.parametrize("dt,d", [("bf16", 8), ("bf16", 4096), ("bf16", 6144), ("bf16", 16384),
-                                  ("f32", 1024), ("f32", 4100)])
+                                  ("f32", 1024), ("f32", 4100), ("fp8", 48), ("fp8", 16384)])
 @pytest.mark.parametrize("n", [2, 3, 4])
 def test_identity_pre_bitwise_equals_single_stream(dt, d, n):
     """alpha = e_0: u is bitwise the n = 1 call on stream 0 (the reduction
-    order over d does not depend on n)."""
+    order over d does not depend on n), up to the sign of zero: a -0 in
+    stream 0 plus 0 * (a positive value) of another stream is +0 (FP8 draws
+    round small values to -0)."""
     rng = np.random.default_rng(d * n)
     H, F, w, g = case(rng, dt, 11, n, d, per_token=False)
     u_n = host(hc.pre_mix(dev(H), dev(identity_record(n)), dev(g)))
     u_1 = host(hc.pre_mix(dev(np.ascontiguousarray(H[:, :1, :])), dev(identity_record(1)), dev(g)))
-    assert np.array_equal(u_n, u_1)
+    zn, z1 = oracle.widen(u_n) == 0, oracle.widen(u_1) == 0
+    assert np.array_equal(zn, z1)
+    assert np.array_equal(u_n[~zn], u_1[~z1])
 
 
 @pytest.mark.parametrize("dt,d", [("bf16", 40), ("bf16", 4096), ("bf16", 6144), ("bf16", 8200),
-                                  ("f32", 516), ("f32", 16384)])
+                                  ("f32", 516), ("f32", 16384), ("fp8", 48), ("fp8", 4096),
+                                  ("fp8", 8208)])
 @pytest.mark.parametrize("n", [1, 3, 4])
 def test_fused_post_pre_bitwise(dt, d, n):
     rng = np.random.default_rng(31 * d + n)
@@ -167,7 +177,7 @@ def test_zero_tokens_is_a_noop():
     assert o.shape == (0, 4, 4096)
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("dt", ["bf16", "f32", "fp8"])
 def test_block_tanh(dt):
     rng = np.random.default_rng(3)
     u = storage(3 * rng.standard_normal((17, 1024)).astype(np.float32), dt)
@@ -215,3 +225,66 @@ def test_static_bf16_full_size_sampled():
           "static pre")
     check(host(Hp[torch.from_numpy(idx).cuda()]), oracle.post_mix(sub["H"], sub["F"], w64),
           "static post")
+
+
+def _fp8_finite_codes() -> np.ndarray:
+    c = np.arange(256, dtype=np.uint8)
+    return c[(c & 0x7F) != 0x7F]
+
+
+def test_fp8_store_rounding_exhaustive():
+    """Every sum of two finite FP8 values, stored by the identity post with
+    n = 1 (H' = H + F, exact in fp32): the stored code is the oracle's
+    nearest-even saturating rounding, bitwise.  Covers ties, the subnormal
+    range, carries into the next binade and overflow past 448."""
+    codes = _fp8_finite_codes()                      # 254 codes
+    d = 256
+    x = np.zeros(d, np.uint8)
+    x[:codes.size] = codes
+    H = np.repeat(x[None, None, :], codes.size, axis=0)              # (254, 1, 256)
+    F = np.repeat(codes[:, None], d, axis=1).astype(np.uint8)        # token t adds code t
+    out = host(hc.post_mix(dev(H), dev(F), dev(identity_record(1))))
+    want = oracle.round_fp8(oracle.widen(H)[:, 0, :] + oracle.widen(F))
+    assert np.array_equal(out[:, 0, :], want)
+    assert (want == 0x7E).any() and (want == 0x01).any()             # saturation and subnormals hit
+
+
+def test_fp8_nan_propagates_and_large_values_saturate():
+    rng = np.random.default_rng(19)
+    n, d, T = 4, 64, 5
+    H = f32_to_fp8_bits(rng.standard_normal((T, n, d)).astype(np.float32) * 100)
+    F = f32_to_fp8_bits(rng.standard_normal((T, d)).astype(np.float32) * 300)
+    H[1, 2, 5] = 0x7F                                                   # NaN
+    H[2, :, :8] = 0x7E                                                  # 448 in every stream
+    w = (identity_record(n) + 0.3 * rng.standard_normal(2 * n + n * n)).astype(np.float32)
+    w[n:2 * n] = 2.0                                                    # beta = 2 pushes past 448
+    g = np.ones(d, np.float32)
+    wd = w.astype(np.float64)
+    out = host(hc.post_mix(dev(H), dev(F), dev(w)))
+    ref = oracle.post_mix(H, F, wd)
+    check(out, ref, "post fp8 nan/sat")
+    assert (np.abs(ref) > 448).any() and ((out & 0x7F) == 0x7E).any()
+    assert np.array_equal(np.isnan(oracle.widen(out)), np.isnan(ref))
+    check(host(hc.pre_mix(dev(H), dev(w), dev(g))), oracle.pre_mix(H, wd, g), "pre fp8 nan")
+
+
+def test_static_fp8_full_size_sampled():
+    """T=16384, n=4, d=4096 FP8 E4M3, in the launch configuration the
+    benchmark times; 256 sampled tokens (plus the first and last) checked by
+    the oracle."""
+    wl = workload("static-fp8")
+    inp = make_inputs(wl)
+    Hd, Fd, wd, gd = dev(inp["H"]), dev(inp["F"]), dev(inp["w"]), dev(inp["gamma"])
+    u = hc.pre_mix(Hd, wd, gd, wl.eps)
+    Hp = hc.post_mix(Hd, Fd, wd)
+    Hp2, u2 = hc.post_pre_mix(Hd, Fd, wd, wd, gd, wl.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(Hp2.view(torch.uint8), Hp.view(torch.uint8))
+    idx = sample_tokens(wl.T, 256, 13)
+    sub = make_inputs(wl, tokens=idx)
+    assert np.array_equal(sub["H"], inp["H"][idx])
+    w64 = inp["w"].astype(np.float64)
+    ti = torch.from_numpy(idx).cuda()
+    check(host(u[ti]), oracle.pre_mix(sub["H"], w64, inp["gamma"], wl.eps), "static fp8 pre")
+    check(host(Hp[ti]), oracle.post_mix(sub["H"], sub["F"], w64), "static fp8 post")
+    check(host(u2[ti]), oracle.pre_mix(host(Hp[ti]), w64, inp["gamma"], wl.eps), "static fp8 fused u")
