@@ -214,6 +214,18 @@ __global__ __launch_bounds__(kWThreads) void weights_kernel(
 
         for (int c = 0; c < nchunks; ++c) {
             const int k0 = c * KC;
+            // W chunk pieces first (L2 hits), so that storing them to LDS waits
+            // only for these loads and not for the stream loads behind them
+            constexpr int WP = (K * G::PIECES + kWThreads - 1) / kWThreads;
+            uint4 wv[WP];
+#pragma unroll
+            for (int i = 0; i < WP; ++i) {
+                const int p = threadIdx.x + i * kWThreads;
+                const int r = p / G::PIECES, pc = p % G::PIECES;
+                const int k = k0 + pc * (16 / SB);
+                wv[i] = (p < K * G::PIECES && k < d) ? ld16(W + ((int64_t)r * d + k) * SB)
+                                                     : make_uint4(0, 0, 0, 0);
+            }
             // this lane's stream vectors for the chunk (zero past d or past T)
             uint4 a[kLV];
 #pragma unroll
@@ -221,13 +233,14 @@ __global__ __launch_bounds__(kWThreads) void weights_kernel(
                 const int k = k0 + (4 * s + grp) * V;
                 a[s] = (row_ok && k < d) ? ld16_stream(arow + (int64_t)k * SB) : make_uint4(0, 0, 0, 0);
             }
-            // W chunk -> LDS (rows < K; zero past d)
             __syncthreads();   // previous chunk's readers are done
-            for (int p = threadIdx.x; p < K * G::PIECES; p += kWThreads) {
-                const int r = p / G::PIECES, pc = p % G::PIECES;
-                const int k = k0 + pc * (16 / SB);
-                uint4 v = k < d ? ld16(W + ((int64_t)r * d + k) * SB) : make_uint4(0, 0, 0, 0);
-                *reinterpret_cast<uint4*>(wlds + r * G::RS + pc * 16) = v;
+#pragma unroll
+            for (int i = 0; i < WP; ++i) {
+                const int p = threadIdx.x + i * kWThreads;
+                if (p < K * G::PIECES) {
+                    const int r = p / G::PIECES, pc = p % G::PIECES;
+                    *reinterpret_cast<uint4*>(wlds + r * G::RS + pc * 16) = wv[i];
+                }
             }
             __syncthreads();
 #pragma unroll
