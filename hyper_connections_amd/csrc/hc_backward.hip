@@ -74,7 +74,7 @@ __global__ __launch_bounds__(1024) void post_bwd_kernel(
     const float* __restrict__ w, int64_t w_stride, uint8_t* __restrict__ dH,
     uint8_t* __restrict__ dF, float* __restrict__ dw, float* __restrict__ part, int64_t T, int d,
     int group) {
-    constexpr int V = Store<S>::kElems;
+    constexpr int V = Store<S>::kElems, E = Word<S>::kElems;
     constexpr int K = 2 * N + N * N;
     constexpr int M = N + N * N;            // dbeta, dA
     __shared__ float red[16 * M];
@@ -97,66 +97,95 @@ __global__ __launch_bounds__(1024) void post_bwd_kernel(
 #pragma unroll
                 for (int j = 0; j < N; ++j) A[i][j] = rec[2 * N + i * N + j];
 
+            // buffer resources over this token's rows (see pre_bwd_kernel)
+            const uint32_t rb = (uint32_t)row_bytes;
             const int64_t r0 = t * N * row_bytes;
+            const __amdgpu_buffer_rsrc_t rG = make_rsrc(dHo + r0, N * rb);
+            const __amdgpu_buffer_rsrc_t rH = make_rsrc(H + r0, N * rb);
+            const __amdgpu_buffer_rsrc_t rF = make_rsrc(F + t * row_bytes, rb);
+            const __amdgpu_buffer_rsrc_t rO = make_rsrc(dH + r0, N * rb);
+            const __amdgpu_buffer_rsrc_t rOF = make_rsrc(dF + t * row_bytes, rb);
             uint4 rg[N][VPT], rh[N][VPT], rf[VPT];
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
                 const int v = threadIdx.x + j * B;
-                if (v < nvec) {
+                const uint32_t vo = v < nvec ? (uint32_t)v * 16u : 0x80000000u;
 #pragma unroll
-                    for (int i = 0; i < N; ++i) {
-                        rg[i][j] = ld16_stream(dHo + r0 + i * row_bytes + v * 16);
-                        rh[i][j] = ld16_stream(H + r0 + i * row_bytes + v * 16);
-                    }
-                    rf[j] = ld16_stream(F + t * row_bytes + v * 16);
+                for (int i = 0; i < N; ++i) {
+                    rg[i][j] = bload<kNT>(rG, vo, i * rb);
+                    rh[i][j] = bload<kNT>(rH, vo, i * rb);
                 }
+                rf[j] = bload<kNT>(rF, vo, 0);
             }
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
                 const int v = threadIdx.x + j * B;
                 if (v < nvec) {
-                    float g[N][V], f[V];
-#pragma unroll
-                    for (int i = 0; i < N; ++i) unpack<S>(rg[i][j], g[i]);
-                    unpack<S>(rf[j], f);
+                    // one output row at a time, dword by dword; the unpacked
+                    // values are recomputed from the raw vectors each time
                     // dH_j = sum_i A[i][j] dH'_i
 #pragma unroll
                     for (int jj = 0; jj < N; ++jj) {
-                        float o[V];
+                        uint32_t oh[4];
 #pragma unroll
-                        for (int e = 0; e < V; ++e) {
-                            float s = A[0][jj] * g[0][e];
+                        for (int q = 0; q < 4; ++q) {
+                            float g[N][E], o[E];
 #pragma unroll
-                            for (int i = 1; i < N; ++i) s = fmaf(A[i][jj], g[i][e], s);
-                            o[e] = s;
+                            for (int i = 0; i < N; ++i) unpack_word<S>(word(rg[i][j], q), g[i]);
+#pragma unroll
+                            for (int e = 0; e < E; ++e) {
+                                float sum = A[0][jj] * g[0][e];
+#pragma unroll
+                                for (int i = 1; i < N; ++i) sum = fmaf(A[i][jj], g[i][e], sum);
+                                o[e] = sum;
+                            }
+                            oh[q] = pack_word<S>(o);
                         }
-                        st16_stream(dH + r0 + jj * row_bytes + v * 16, pack<S>(o));
+                        bstore<kNT>(make_uint4(oh[0], oh[1], oh[2], oh[3]), rO, (uint32_t)v * 16u, jj * rb);
+#pragma unroll
+                        for (int i = 0; i < N; ++i) opaque(rg[i][j]);
                     }
                     // dF = sum_i beta_i dH'_i
-                    float o[V];
+                    uint32_t of[4];
 #pragma unroll
-                    for (int e = 0; e < V; ++e) {
-                        float s = beta[0] * g[0][e];
+                    for (int q = 0; q < 4; ++q) {
+                        float g[N][E], o[E];
 #pragma unroll
-                        for (int i = 1; i < N; ++i) s = fmaf(beta[i], g[i][e], s);
-                        o[e] = s;
+                        for (int i = 0; i < N; ++i) unpack_word<S>(word(rg[i][j], q), g[i]);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            float sum = beta[0] * g[0][e];
+#pragma unroll
+                            for (int i = 1; i < N; ++i) sum = fmaf(beta[i], g[i][e], sum);
+                            o[e] = sum;
+                        }
+                        of[q] = pack_word<S>(o);
                     }
-                    st16_stream(dF + t * row_bytes + v * 16, pack<S>(o));
+                    bstore<kNT>(make_uint4(of[0], of[1], of[2], of[3]), rOF, (uint32_t)v * 16u, 0);
+#pragma unroll
+                    for (int i = 0; i < N; ++i) opaque(rg[i][j]);
                     // partials of dbeta_i and dA[i][j]
 #pragma unroll
-                    for (int jj = 0; jj < N; ++jj) {
-                        float h[V];
-                        unpack<S>(rh[jj][j], h);
+                    for (int q = 0; q < 4; ++q) {
+                        float g[N][E], f[E];
+#pragma unroll
+                        for (int i = 0; i < N; ++i) unpack_word<S>(word(rg[i][j], q), g[i]);
+                        unpack_word<S>(word(rf[j], q), f);
+#pragma unroll
+                        for (int jj = 0; jj < N; ++jj) {
+                            float h[E];
+                            unpack_word<S>(word(rh[jj][j], q), h);
+#pragma unroll
+                            for (int i = 0; i < N; ++i)
+#pragma unroll
+                                for (int e = 0; e < E; ++e)
+                                    acc[N + i * N + jj] = fmaf(g[i][e], h[e], acc[N + i * N + jj]);
+                        }
 #pragma unroll
                         for (int i = 0; i < N; ++i)
 #pragma unroll
-                            for (int e = 0; e < V; ++e)
-                                acc[N + i * N + jj] = fmaf(g[i][e], h[e], acc[N + i * N + jj]);
+                            for (int e = 0; e < E; ++e) acc[i] = fmaf(g[i][e], f[e], acc[i]);
                     }
-#pragma unroll
-                    for (int i = 0; i < N; ++i)
-#pragma unroll
-                        for (int e = 0; e < V; ++e) acc[i] = fmaf(g[i][e], f[e], acc[i]);
                 }
             }
             if constexpr (PER_TOKEN) {
@@ -198,7 +227,7 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
     int64_t w_stride, const float* __restrict__ gamma, float eps, const uint8_t* dH_in,
     uint8_t* dH, float* __restrict__ dw, float* __restrict__ dg_part,
     float* __restrict__ da_part, int64_t T, int d, int group) {
-    constexpr int V = Store<S>::kElems;
+    constexpr int V = Store<S>::kElems, E = Word<S>::kElems;
     constexpr int K = 2 * N + N * N;
     __shared__ float red[16 * (N > 2 ? N : 2)];   // block_sum_vec<2> and <N>
     const int B = blockDim.x;
@@ -221,47 +250,74 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
             float alpha[N];
 #pragma unroll
             for (int i = 0; i < N; ++i) alpha[i] = a[i];
+            // Buffer resources over this token's rows (uniform); a thread's
+            // vectors are addressed by one lane offset plus a per-stream
+            // uniform offset.  A NULL dH_in gets an empty resource (loads
+            // return zeros and are not added).
+            const uint32_t rb = (uint32_t)row_bytes;
             const int64_t r0 = t * N * row_bytes;
-            uint4 rh[N][VPT], ru[VPT];
+            const __amdgpu_buffer_rsrc_t rH = make_rsrc(H + r0, N * rb);
+            const __amdgpu_buffer_rsrc_t rU = make_rsrc(du + t * row_bytes, rb);
+            const __amdgpu_buffer_rsrc_t rIn = make_rsrc(dH_in ? dH_in + r0 : H, dH_in ? N * rb : 0u);
+            const __amdgpu_buffer_rsrc_t rO = make_rsrc(dH + r0, N * rb);
+            // every load of the token first, dH_in included (it does not
+            // depend on the reduction)
+            uint4 rh[N][VPT], ru[VPT], rin[N][VPT];
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
                 const int v = threadIdx.x + j * B;
-                if (v < nvec) {
+                const uint32_t vo = v < nvec ? (uint32_t)v * 16u : 0x80000000u;
 #pragma unroll
-                    for (int i = 0; i < N; ++i) rh[i][j] = ld16_stream(H + r0 + i * row_bytes + v * 16);
-                    ru[j] = ld16_stream(du + t * row_bytes + v * 16);
-                }
+                for (int i = 0; i < N; ++i) rh[i][j] = bload<kNT>(rH, vo, i * rb);
+                ru[j] = bload<kNT>(rU, vo, 0);
+#pragma unroll
+                for (int i = 0; i < N; ++i) rin[i][j] = bload<kNT>(rIn, vo, i * rb);
             }
-            // x (kept), mean square and mean(gamma * du * x)
-            float x[VPT][V];
+            // x = sum_i alpha_i H_i, dword by dword (recomputed the same way
+            // after the reduction instead of being kept)
+            auto mix_word = [&](int j, int q, float (&x)[E]) {
+                float h[E];
+                unpack_word<S>(word(rh[0][j], q), h);
+#pragma unroll
+                for (int e = 0; e < E; ++e) x[e] = alpha[0] * h[e];
+#pragma unroll
+                for (int i = 1; i < N; ++i) {
+                    unpack_word<S>(word(rh[i][j], q), h);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) x[e] = fmaf(alpha[i], h[e], x[e]);
+                }
+            };
+            // mean square of x and mean(gamma * du * x)
             float s2[2] = {0.0f, 0.0f};
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
                 const int v = threadIdx.x + j * B;
                 if (v < nvec) {
-                    float h[V], ug[V], g[V];
-                    unpack<S>(rh[0][j], h);
-#pragma unroll
-                    for (int e = 0; e < V; ++e) x[j][e] = alpha[0] * h[e];
-#pragma unroll
-                    for (int i = 1; i < N; ++i) {
-                        unpack<S>(rh[i][j], h);
-#pragma unroll
-                        for (int e = 0; e < V; ++e) x[j][e] = fmaf(alpha[i], h[e], x[j][e]);
-                    }
-                    unpack<S>(ru[j], ug);
+                    float g[V];
 #pragma unroll
                     for (int q = 0; q < V / 4; ++q) unpack<f32_t>(ld16(gamma + v * V + 4 * q), &g[4 * q]);
 #pragma unroll
-                    for (int e = 0; e < V; ++e) {
-                        s2[0] = fmaf(x[j][e], x[j][e], s2[0]);
-                        s2[1] = fmaf(g[e] * ug[e], x[j][e], s2[1]);
+                    for (int q = 0; q < 4; ++q) {
+                        float x[E], ug[E];
+                        mix_word(j, q, x);
+                        unpack_word<S>(word(ru[j], q), ug);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            s2[0] = fmaf(x[e], x[e], s2[0]);
+                            s2[1] = fmaf(g[q * E + e] * ug[e], x[e], s2[1]);
+                        }
                     }
                 }
             }
             // both sums in one reduction: the mean square of x does not
             // depend on r, and mean(dy * x) is needed only after r is known
             block_sum_vec<2>(s2, red);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+#pragma unroll
+                for (int i = 0; i < N; ++i) opaque(rh[i][j]);
+                opaque(ru[j]);
+            }
             const float r = 1.0f / sqrtf(s2[0] / (float)d + eps);
             const float c2 = r * r * s2[1] / (float)d;
             float da[N];
@@ -271,31 +327,42 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
             for (int j = 0; j < VPT; ++j) {
                 const int v = threadIdx.x + j * B;
                 if (v < nvec) {
-                    float ug[V], g[V], dx[V];
-                    unpack<S>(ru[j], ug);
+                    float g[V], dx[V];
 #pragma unroll
                     for (int q = 0; q < V / 4; ++q) unpack<f32_t>(ld16(gamma + v * V + 4 * q), &g[4 * q]);
 #pragma unroll
-                    for (int e = 0; e < V; ++e) {
-                        dx[e] = r * (g[e] * ug[e] - x[j][e] * c2);
-                        dgp[j][e] = fmaf(ug[e], x[j][e] * r, dgp[j][e]);
+                    for (int q = 0; q < 4; ++q) {
+                        float x[E], ug[E];
+                        mix_word(j, q, x);
+                        unpack_word<S>(word(ru[j], q), ug);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            dx[q * E + e] = r * (g[q * E + e] * ug[e] - x[e] * c2);
+                            dgp[j][q * E + e] = fmaf(ug[e], x[e] * r, dgp[j][q * E + e]);
+                        }
                     }
+                    // one output row at a time
 #pragma unroll
                     for (int i = 0; i < N; ++i) {
-                        float h[V], o[V];
-                        unpack<S>(rh[i][j], h);
+                        uint32_t oh[4];
 #pragma unroll
-                        for (int e = 0; e < V; ++e) {
-                            da[i] = fmaf(dx[e], h[e], da[i]);
-                            o[e] = alpha[i] * dx[e];
-                        }
-                        if (dH_in) {
-                            float p[V];
-                            unpack<S>(ld16_stream(dH_in + r0 + i * row_bytes + v * 16), p);
+                        for (int q = 0; q < 4; ++q) {
+                            float h[E], o[E];
+                            unpack_word<S>(word(rh[i][j], q), h);
 #pragma unroll
-                            for (int e = 0; e < V; ++e) o[e] += p[e];
+                            for (int e = 0; e < E; ++e) {
+                                da[i] = fmaf(dx[q * E + e], h[e], da[i]);
+                                o[e] = alpha[i] * dx[q * E + e];
+                            }
+                            if (dH_in) {
+                                float p[E];
+                                unpack_word<S>(word(rin[i][j], q), p);
+#pragma unroll
+                                for (int e = 0; e < E; ++e) o[e] += p[e];
+                            }
+                            oh[q] = pack_word<S>(o);
                         }
-                        st16_stream(dH + r0 + i * row_bytes + v * 16, pack<S>(o));
+                        bstore<kNT>(make_uint4(oh[0], oh[1], oh[2], oh[3]), rO, (uint32_t)v * 16u, i * rb);
                     }
                 }
             }
