@@ -8,6 +8,7 @@ inputs are already resident in HBM:
   static-bf16   pre (read-mix + RMSNorm) then post (stream-mix + write-back)
                 with shared static weights; F is a given tensor (default)
   dynamic-bf16  per-token weights (MFMA projection + tanh), then pre, post
+  dynamic-fp8   the same with FP8 E4M3 H, W and F
   mhc-bf16      Sinkhorn records from per-token logits, then pre, post
   chain-bf16    78 layers of pre, tanh block, post (reported, not graded)
   decode-bf16   the same 78-layer loop at 64 tokens in flight (latency-bound;

@@ -153,7 +153,6 @@ hc_status hc_post_pre_mix(const void* H, const void* F, const float* w, int64_t 
 hc_status hc_weights(const void* H, const void* W, const float* w_static, float scale, float eps,
                      int32_t sinkhorn_iters, float* w_out, int64_t T, int32_t n, int32_t d,
                      hc_dtype dt, void* stream) {
-    if (!dtype_wide(dt)) return HC_ERR_DTYPE;
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
     if (!eps_ok(eps) || !std::isfinite(scale)) return HC_ERR_ARG;

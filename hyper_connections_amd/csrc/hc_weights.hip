@@ -16,7 +16,9 @@
 //   z_c = (1/n) sum_i r_i P_ic,   P_ic = sum_k H_ik W_ck,
 // so the kernel multiplies the raw stream rows (H viewed as a (T*n) x d
 // matrix) by W^T on MFMA while the same registers feed the per-row sums of
-// squares; r_i is applied in the epilogue.  One HBM pass over H.
+// squares; r_i is applied in the epilogue.  One HBM pass over H.  bf16 uses
+// v_mfma_f32_16x16x32_bf16, FP8 (E4M3 H and W) the same after an exact
+// widening to bf16, fp32 v_mfma_f32_16x16x4f32.
 //
 // Tiling (one wave = 16 matrix rows = 16/n tokens; 4 waves per workgroup):
 //  - A operand: the wave's 16 rows.  Lane l supplies row l % 16; its lane
@@ -159,6 +161,26 @@ template <> struct Mfma<f32_t> {
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+        return c;
+    }
+};
+
+template <> struct Mfma<fp8_t> {
+    // one 16-byte vector (16 fp8 E4M3) is two K = 32 bf16 steps: every FP8
+    // value is exactly a bf16 value, so the operands are widened to bf16
+    // (v_cvt_scalef32_pk_bf16_fp8 with scale 1) and multiplied on the bf16
+    // matrix path, whose fp32 accumulation matches the other dtypes
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
+        const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false);
+        const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true);
+        const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false);
+        const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true);
+        return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+    }
+    static __device__ __forceinline__ f32x4 step(uint4 a, uint4 b, f32x4 c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(a.x, a.y), widen8(b.x, b.y), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(a.z, a.w), widen8(b.z, b.w), c, 0, 0, 0);
         return c;
     }
 };
@@ -352,6 +374,7 @@ hipError_t launch_weights(const void* H, const void* W, const float* w_static, f
                           float eps, int iters, float* w_out, int64_t T, int n, int d, int dt,
                           hipStream_t s) {
     if (dt == 0) return weights_by_n<f32_t>(n, H, W, w_static, scale, eps, iters, w_out, T, d, s);
+    if (dt == 2) return weights_by_n<fp8_t>(n, H, W, w_static, scale, eps, iters, w_out, T, d, s);
     return weights_by_n<bf16_t>(n, H, W, w_static, scale, eps, iters, w_out, T, d, s);
 }
 

@@ -33,6 +33,7 @@ mhc-bf16            32768  4  4096  bf16   per token logits ~ N(0, 1), 20 iters
 chain-bf16 (x78)    4096   4  6144  bf16   per layer identity + N(0, 0.02)
 decode-bf16 (x78)   64     4  8192  bf16   per layer identity + N(0, 0.02)
 static-fp8          16384  4  4096  fp8    static identity + N(0, 0.05)
+dynamic-fp8         16384  4  4096  fp8    as dynamic-bf16, H, F and W in FP8
 ==================  =====  =  ====  =====  =====================================
 
 The decode workload is the explainer's worked shape (section "What four
@@ -91,6 +92,8 @@ WORKLOADS = {
         Workload("decode-bf16", 64, 4, 8192, "bf16", 606, "chain", weight_sd=0.02, layers=78,
                  F_kind="tanh"),
         Workload("static-fp8", 16384, 4, 4096, "fp8", 707, "static", weight_sd=0.05, gamma_sd=0.1),
+        Workload("dynamic-fp8", 16384, 4, 4096, "fp8", 808, "dynamic", gamma_sd=0.1,
+                 proj_sd=0.02, scale=0.01),
     ]
 }
 

@@ -75,8 +75,9 @@ typedef enum hc_status {
  * 3 mantissa bits, no infinities, largest finite 448).  The release ships
  * BF16 and FP8 weights ([EXPL] "The news"; [MAP] "inference quantization");
  * the pages name no 8-bit format, E4M3 is the one implemented.  FP8 is taken
- * by hc_pre_mix, hc_post_mix, hc_post_pre_mix and hc_block_tanh; hc_weights
- * and the gradient calls return HC_ERR_DTYPE for it. */
+ * by hc_pre_mix, hc_post_mix, hc_post_pre_mix, hc_weights (H and W in FP8,
+ * fp32 accumulation) and hc_block_tanh; the gradient calls return
+ * HC_ERR_DTYPE for it. */
 typedef enum hc_dtype { HC_F32 = 0, HC_BF16 = 1, HC_FP8 = 2 } hc_dtype;
 
 #define HC_MAX_STREAMS 4
@@ -116,7 +117,8 @@ hc_status hc_post_mix(const void* H, const void* F, const float* w, int64_t w_st
  *   sinkhorn_iters == 0:  w = w_static + scale * tanh(z)
  *   sinkhorn_iters  > 0:  l = w_static + scale * z, w = the hc_sinkhorn
  *                         transform of l with that many iterations.
- * The projection runs on the matrix cores (MFMA), fp32 accumulation.
+ * The projection runs on the matrix cores (MFMA), fp32 accumulation; FP8
+ * operands are widened exactly to bf16 first.
  *   H        [T][n][d] dt        W  [K][d] dt (row c = output c; the layout
  *                                   of a linear layer's weight)
  *   w_static [K] fp32            w_out [T][K] fp32, output (stride K)

@@ -123,7 +123,7 @@ def test_weights_validation(L):
     assert f(W=P[1] + 8) == ALIGN and f(o=P[3] + 2) == ALIGN
     assert f(o=P[0] + 64) == ALIAS and f(o=P[1]) == ALIAS
     assert f(n=0) == SHAPE and f(d=100) == SHAPE and f(dt=5) == DTYPE
-    assert f(dt=FP8) == DTYPE and f(dt=FP8, T=0) == DTYPE     # fp8 weights not taken
+    assert f(dt=FP8, T=0) == OK and f(dt=FP8, d=4104) == SHAPE   # fp8 needs d % 16 == 0
 
 
 def test_backward_validation(L):

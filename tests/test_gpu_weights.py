@@ -7,8 +7,8 @@ import torch
 import oracle
 from gpu_util import TOL_RECORD, check, dev, host, need_gpu, rel_err
 from hyper_connections_amd import hc
-from hyper_connections_amd.workloads import (TID_LOGITS, f32_to_bf16_bits, identity_record,
-                                             make_inputs, normal_rows, workload)
+from hyper_connections_amd.workloads import (TID_LOGITS, f32_to_bf16_bits, f32_to_fp8_bits,
+                                             identity_record, make_inputs, normal_rows, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -19,6 +19,8 @@ def _gpu():
 
 
 def storage(x, dt):
+    if dt == "fp8":
+        return f32_to_fp8_bits(x)
     return f32_to_bf16_bits(x) if dt == "bf16" else x.astype(np.float32)
 
 
@@ -30,7 +32,8 @@ def record_check(got: np.ndarray, ref: np.ndarray, what: str):
 
 # d: one partial chunk, exact chunks, a ragged last chunk; T: partial tiles
 @pytest.mark.parametrize("dt,d", [("bf16", 8), ("bf16", 264), ("bf16", 4096), ("bf16", 6152),
-                                  ("f32", 4), ("f32", 132), ("f32", 1024)])
+                                  ("f32", 4), ("f32", 132), ("f32", 1024),
+                                  ("fp8", 16), ("fp8", 528), ("fp8", 4096), ("fp8", 6160)])
 @pytest.mark.parametrize("n", [1, 2, 3, 4])
 @pytest.mark.parametrize("iters", [0, 5])
 def test_weights_parity(dt, d, n, iters):
@@ -59,7 +62,7 @@ def test_weights_ragged_tokens(T):
     assert np.all(got[T:] == 7.0)
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("dt", ["bf16", "f32", "fp8"])
 def test_zero_projection_is_static_bitwise(dt):
     n, d, K = 4, 1024, 24
     rng = np.random.default_rng(2)
@@ -126,10 +129,12 @@ def test_mhc_workload_full():
     assert np.mean(np.abs(Ar.sum(axis=2) - 1).max(axis=1) <= 1e-6) > 0.97
 
 
-def test_dynamic_workload_full_size_sampled():
-    """T=16384, n=4, d=4096 bf16 with W ~ N(0, 0.02): all records checked
-    against the oracle on 256 sampled tokens, then pre/post with them."""
-    wl = workload("dynamic-bf16")
+@pytest.mark.parametrize("name", ["dynamic-bf16", "dynamic-fp8"])
+def test_dynamic_workload_full_size_sampled(name):
+    """T=16384, n=4, d=4096 (bf16, or FP8 E4M3 H, W and F) with W ~ N(0,
+    0.02): records checked against the oracle on 256 sampled tokens, then
+    pre/post with them."""
+    wl = workload(name)
     inp = make_inputs(wl)
     Hd, Fd, gd = dev(inp["H"]), dev(inp["F"]), dev(inp["gamma"])
     w = hc.weights(Hd, dev(inp["W"]), dev(inp["w_static"]), wl.scale, wl.eps, 0)
