@@ -82,12 +82,16 @@ __global__ __launch_bounds__(1024) void post_bwd_kernel(
     const int nvec = d / V;
     const int64_t row_bytes = (int64_t)d * Store<S>::kBytes;
 
-    for (int64_t blk = blockIdx.x; blk * group < T; blk += gridDim.x) {
+    // Block blk takes tokens blk, blk + nb, blk + 2 nb, ... (at most `group`
+    // of them), so the tokens in flight at any moment lie close together in
+    // memory (consecutive tokens per block spread them over the whole
+    // tensor; the pre gradient ran 8% slower that way).
+    const int64_t nb = (T + group - 1) / group;
+    for (int64_t blk = blockIdx.x; blk < nb; blk += gridDim.x) {
         float acc[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[m] = 0.0f;
-        const int64_t t_end = (blk + 1) * group < T ? (blk + 1) * group : T;
-        for (int64_t t = blk * group; t < t_end; ++t) {
+        for (int64_t t = blk; t < T; t += nb) {
             const float* rec = w + t * w_stride;
             float beta[N], A[N][N];
 #pragma unroll
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(1024) void post_bwd_kernel(
 
 // ------------------------------------------------------------- pre backward
 
-// A block walks `group` consecutive tokens.  The dgamma partial of each
+// A block walks up to `group` tokens (see post_bwd_kernel).  The dgamma partial of each
 // thread's columns stays in registers and goes to dg_part[blk][d] once;
 // dalpha goes to dw[t] per token (PER_TOKEN) or is summed over the block's
 // tokens into da_part[blk][N].
@@ -234,7 +238,12 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
     const int nvec = d / V;
     const int64_t row_bytes = (int64_t)d * Store<S>::kBytes;
 
-    for (int64_t blk = blockIdx.x; blk * group < T; blk += gridDim.x) {
+    // Block blk takes tokens blk, blk + nb, blk + 2 nb, ... (at most `group`
+    // of them), so the tokens in flight at any moment lie close together in
+    // memory (consecutive tokens per block spread them over the whole
+    // tensor; the pre gradient ran 8% slower that way).
+    const int64_t nb = (T + group - 1) / group;
+    for (int64_t blk = blockIdx.x; blk < nb; blk += gridDim.x) {
         float dgp[VPT][V];
 #pragma unroll
         for (int j = 0; j < VPT; ++j)
@@ -244,8 +253,7 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
 #pragma unroll
         for (int i = 0; i < N; ++i) dab[i] = 0.0f;
 
-        const int64_t t_end = (blk + 1) * group < T ? (blk + 1) * group : T;
-        for (int64_t t = blk * group; t < t_end; ++t) {
+        for (int64_t t = blk; t < T; t += nb) {
             const float* a = w + t * w_stride;
             float alpha[N];
 #pragma unroll
