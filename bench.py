@@ -107,6 +107,72 @@ class Timer:
 
 
 COPY_PROBE_BYTES = 512 * 2 ** 20   # bytes read (and written) by the calibration copy
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense, published
+CLOCK_GHZ = 2.4
+SIMDS = 1024                       # 256 CUs x 4
+XCDS = 8
+
+# kernel name in the traces, where it differs from "<kernel>_kernel<"
+KERNEL_TAGS = {"post_mix_backward": "post_bwd_kernel<", "pre_mix_backward": "pre_bwd_kernel<"}
+
+
+def summarize_mfma(pmc_csv: str, kernel: str, workload: str, cmds: list):
+    """Matrix-core use of `kernel` from one rocprofv3 --pmc run with
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_LDS_BANK_CONFLICT,
+    SQ_LDS_IDX_ACTIVE and GRBM_GUI_ACTIVE.  Per dispatch: MFMA busy fraction =
+    busy SIMD-cycles / (active cycles x 1024 SIMDs), where GRBM_GUI_ACTIVE
+    sums the 8 XCDs' active cycles; MFMA flops = MOPS x 512.  Writes
+    profiles/<kernel>_<workload>_mfma.{json,md}."""
+    import csv
+    from collections import defaultdict
+    tag = KERNEL_TAGS.get(kernel, f"{kernel}_kernel<")
+    per = defaultdict(dict)
+    with open(pmc_csv) as fh:
+        for r in csv.DictReader(fh):
+            if tag in r["Kernel_Name"]:
+                per[r["Dispatch_Id"]][r["Counter_Name"]] = float(r["Counter_Value"])
+    need = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_LDS_BANK_CONFLICT",
+            "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE")
+    disp = [v for v in per.values() if all(k in v for k in need)]
+    if not disp:
+        raise SystemExit(f"no {kernel} dispatches with all of {need}")
+    mean = lambda k: sum(v[k] for v in disp) / len(disp)  # noqa: E731
+    cycles = mean("GRBM_GUI_ACTIVE") / XCDS
+    busy = mean("SQ_VALU_MFMA_BUSY_CYCLES") / (cycles * SIMDS)
+    flops = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512
+    secs = cycles / (CLOCK_GHZ * 1e9)
+    from hyper_connections_amd import workloads
+    wl = workloads.workload(workload)
+    useful = 2.0 * wl.T * wl.n * wl.K * wl.d
+    rec = {"kernel": kernel, "workload": workload, "source_sha": source_sha(kernel),
+           "dispatches": len(disp), "active_cycles_per_xcd": round(cycles),
+           "duration_us_from_cycles": round(secs * 1e6, 2),
+           "mfma_busy_fraction": round(busy, 4), "mfma_flops_per_launch": int(flops),
+           "useful_flops_per_launch": int(useful),
+           "mfma_tflops": round(flops / secs / 1e12, 1),
+           "mfma_peak_tflops_bf16": MFMA_PEAK_TFLOPS["bf16"],
+           "lds_bank_conflict_over_active": round(mean("SQ_LDS_BANK_CONFLICT") /
+                                                  max(mean("SQ_LDS_IDX_ACTIVE"), 1.0), 4),
+           "commands": cmds}
+    base = os.path.join(PROFILES, f"{kernel}_{workload}_mfma")
+    with open(base + ".json", "w") as fh:
+        json.dump(rec, fh, indent=1)
+    with open(base + ".md", "w") as fh:
+        fh.write(f"# Matrix-core use of {kernel}, workload {workload}\n\n")
+        fh.write("Command (run as `cd /tmp && export TMPDIR=/tmp` first; paths are relative to the repository root):\n\n")
+        for c in cmds:
+            fh.write(f"    {c}\n")
+        fh.write(f"\nSummarised with `python bench.py --summarize-mfma PMC_CSV --kernel {kernel} "
+                 f"--workload {workload}`.\n\n| quantity | value |\n|---|---|\n")
+        for k in ("dispatches", "active_cycles_per_xcd", "duration_us_from_cycles", "mfma_busy_fraction",
+                  "mfma_flops_per_launch", "useful_flops_per_launch", "mfma_tflops",
+                  "mfma_peak_tflops_bf16", "lds_bank_conflict_over_active", "source_sha"):
+            fh.write(f"| {k} | {rec[k]} |\n")
+        fh.write("\nThe projection is 24 output columns padded to two 16-column MFMA tiles, so the "
+                 "matrix cores do 32/24 of the useful flops.  The kernel is bound by HBM: its flops per "
+                 "byte are about 12x below the bf16 MFMA ridge, and the matrix cores idle most of the "
+                 "time by design.\n")
+    log(f"[bench] wrote {base}.json: MFMA busy {busy:.1%}, {flops / secs / 1e12:.1f} TFLOP/s")
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, kernel: str, workload: str, cmds: list):
@@ -137,7 +203,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, kernel: str, workload: st
         raise SystemExit("calibration copy not found in the counter runs")
     mean = lambda rs: sum(float(r["Counter_Value"]) for r in rs) / len(rs)  # noqa: E731
     f_scale, w_scale = probe_kib / mean(fprobe), probe_kib / mean(wprobe)
-    tag = f"{kernel}_kernel<"
+    tag = KERNEL_TAGS.get(kernel, f"{kernel}_kernel<")
     fk, wk = [r for r in fetch if tag in r["Kernel_Name"]], [r for r in write if tag in r["Kernel_Name"]]
     if not fk or not wk:
         raise SystemExit(f"no {kernel} dispatches in the counter runs")
@@ -150,7 +216,9 @@ def summarize_counters(fetch_csv: str, write_csv: str, kernel: str, workload: st
     alg = {"pre_mix": tr.pre_bytes(wl.n, wl.d, wl.elem_bytes, per_tok),
            "post_mix": tr.post_bytes(wl.n, wl.d, wl.elem_bytes, per_tok),
            "weights": tr.weights_bytes(wl.n, wl.d, wl.elem_bytes),
-           "post_pre_mix": tr.post_pre_bytes(wl.n, wl.d, wl.elem_bytes)}[kernel] * wl.T
+           "post_pre_mix": tr.post_pre_bytes(wl.n, wl.d, wl.elem_bytes),
+           "post_mix_backward": tr.post_bwd_bytes(wl.n, wl.d, wl.elem_bytes, per_tok),
+           "pre_mix_backward": tr.pre_bwd_bytes(wl.n, wl.d, wl.elem_bytes, per_tok)}[kernel] * wl.T
     rec = {"kernel": kernel, "workload": workload, "source_sha": source_sha(kernel),
            "dispatches": {"FETCH_SIZE": len(fk), "WRITE_SIZE": len(wk)},
            "fetch_kib_per_dispatch": round(fetch_kib, 3), "write_kib_per_dispatch": round(write_kib, 3),
@@ -199,13 +267,18 @@ def main():
                     help="capture one step in a HIP graph (torch.cuda.CUDAGraph) and time replays")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
-    ap.add_argument("--kernel", default="post_mix", help="kernel for --summarize-counters")
+    ap.add_argument("--summarize-mfma", metavar="PMC_CSV",
+                    help="summarise a rocprofv3 --pmc run of MFMA/LDS counters into profiles/ and exit")
+    ap.add_argument("--kernel", default="post_mix", help="kernel for --summarize-counters/--summarize-mfma")
     ap.add_argument("--command", action="append", default=[],
                     help="profiling command to record in the summary (repeatable)")
     args = ap.parse_args()
 
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, args.kernel, args.workload, args.command)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, args.kernel, args.workload, args.command)
         return
 
     if args.gpus != 1:
