@@ -288,3 +288,28 @@ def test_static_fp8_full_size_sampled():
     check(host(u[ti]), oracle.pre_mix(sub["H"], w64, inp["gamma"], wl.eps), "static fp8 pre")
     check(host(Hp[ti]), oracle.post_mix(sub["H"], sub["F"], w64), "static fp8 post")
     check(host(u2[ti]), oracle.pre_mix(host(Hp[ti]), w64, inp["gamma"], wl.eps), "static fp8 fused u")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32", "fp8"])
+def test_degenerate_weights_give_exact_results(dt):
+    """Zero read weights give u = 0 exactly (x = 0, r = 1/sqrt(eps)); zero
+    write weights give H' = A H with no trace of F (bitwise the same with F =
+    0); A = 0, beta = 0 gives zeros; a zero stream state gives u = 0."""
+    n, d, T = 4, 4096, 5
+    rng = np.random.default_rng(23)
+    H, F, w, g = case(rng, dt, T, n, d, per_token=False)
+    z = w.copy()
+    z[:n] = 0.0                                           # alpha = 0
+    u = host(hc.pre_mix(dev(H), dev(z), dev(g)))
+    assert not oracle.widen(u).any()
+    u0 = host(hc.pre_mix(dev(np.zeros_like(H)), dev(w), dev(g)))
+    assert not oracle.widen(u0).any()
+    nb = w.copy()
+    nb[n:2 * n] = 0.0                                     # beta = 0: F has no effect
+    a = host(hc.post_mix(dev(H), dev(F), dev(nb)))
+    b = host(hc.post_mix(dev(H), dev(np.zeros_like(F)), dev(nb)))
+    assert np.array_equal(a, b)
+    check(a, oracle.post_mix(H, F, nb.astype(np.float64)), "beta = 0")
+    zz = np.zeros_like(w)
+    o = host(hc.post_mix(dev(H), dev(F), dev(zz)))
+    assert not oracle.widen(o).any()
