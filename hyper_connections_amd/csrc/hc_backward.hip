@@ -101,25 +101,19 @@ __global__ __launch_bounds__(1024) void post_bwd_kernel(
 #pragma unroll
                 for (int j = 0; j < N; ++j) A[i][j] = rec[2 * N + i * N + j];
 
-            // buffer resources over this token's rows (see pre_bwd_kernel)
-            const uint32_t rb = (uint32_t)row_bytes;
             const int64_t r0 = t * N * row_bytes;
-            const __amdgpu_buffer_rsrc_t rG = make_rsrc(dHo + r0, N * rb);
-            const __amdgpu_buffer_rsrc_t rH = make_rsrc(H + r0, N * rb);
-            const __amdgpu_buffer_rsrc_t rF = make_rsrc(F + t * row_bytes, rb);
-            const __amdgpu_buffer_rsrc_t rO = make_rsrc(dH + r0, N * rb);
-            const __amdgpu_buffer_rsrc_t rOF = make_rsrc(dF + t * row_bytes, rb);
             uint4 rg[N][VPT], rh[N][VPT], rf[VPT];
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
                 const int v = threadIdx.x + j * B;
-                const uint32_t vo = v < nvec ? (uint32_t)v * 16u : 0x80000000u;
+                if (v < nvec) {
 #pragma unroll
-                for (int i = 0; i < N; ++i) {
-                    rg[i][j] = bload<kNT>(rG, vo, i * rb);
-                    rh[i][j] = bload<kNT>(rH, vo, i * rb);
+                    for (int i = 0; i < N; ++i) {
+                        rg[i][j] = ld16_stream(dHo + r0 + i * row_bytes + v * 16);
+                        rh[i][j] = ld16_stream(H + r0 + i * row_bytes + v * 16);
+                    }
+                    rf[j] = ld16_stream(F + t * row_bytes + v * 16);
                 }
-                rf[j] = bload<kNT>(rF, vo, 0);
             }
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
@@ -145,7 +139,7 @@ __global__ __launch_bounds__(1024) void post_bwd_kernel(
                             }
                             oh[q] = pack_word<S>(o);
                         }
-                        bstore<kNT>(make_uint4(oh[0], oh[1], oh[2], oh[3]), rO, (uint32_t)v * 16u, jj * rb);
+                        st16_stream(dH + r0 + jj * row_bytes + v * 16, make_uint4(oh[0], oh[1], oh[2], oh[3]));
 #pragma unroll
                         for (int i = 0; i < N; ++i) opaque(rg[i][j]);
                     }
@@ -165,7 +159,7 @@ __global__ __launch_bounds__(1024) void post_bwd_kernel(
                         }
                         of[q] = pack_word<S>(o);
                     }
-                    bstore<kNT>(make_uint4(of[0], of[1], of[2], of[3]), rOF, (uint32_t)v * 16u, 0);
+                    st16_stream(dF + t * row_bytes + v * 16, make_uint4(of[0], of[1], of[2], of[3]));
 #pragma unroll
                     for (int i = 0; i < N; ++i) opaque(rg[i][j]);
                     // partials of dbeta_i and dA[i][j]
@@ -258,28 +252,21 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
             float alpha[N];
 #pragma unroll
             for (int i = 0; i < N; ++i) alpha[i] = a[i];
-            // Buffer resources over this token's rows (uniform); a thread's
-            // vectors are addressed by one lane offset plus a per-stream
-            // uniform offset.  A NULL dH_in gets an empty resource (loads
-            // return zeros and are not added).
-            const uint32_t rb = (uint32_t)row_bytes;
             const int64_t r0 = t * N * row_bytes;
-            const __amdgpu_buffer_rsrc_t rH = make_rsrc(H + r0, N * rb);
-            const __amdgpu_buffer_rsrc_t rU = make_rsrc(du + t * row_bytes, rb);
-            const __amdgpu_buffer_rsrc_t rIn = make_rsrc(dH_in ? dH_in + r0 : H, dH_in ? N * rb : 0u);
-            const __amdgpu_buffer_rsrc_t rO = make_rsrc(dH + r0, N * rb);
             // every load of the token first, dH_in included (it does not
             // depend on the reduction)
             uint4 rh[N][VPT], ru[VPT], rin[N][VPT];
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
                 const int v = threadIdx.x + j * B;
-                const uint32_t vo = v < nvec ? (uint32_t)v * 16u : 0x80000000u;
+                const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < N; ++i) rh[i][j] = bload<kNT>(rH, vo, i * rb);
-                ru[j] = bload<kNT>(rU, vo, 0);
+                for (int i = 0; i < N; ++i)
+                    rh[i][j] = v < nvec ? ld16_stream(H + r0 + i * row_bytes + v * 16) : z;
+                ru[j] = v < nvec ? ld16_stream(du + t * row_bytes + v * 16) : z;
 #pragma unroll
-                for (int i = 0; i < N; ++i) rin[i][j] = bload<kNT>(rIn, vo, i * rb);
+                for (int i = 0; i < N; ++i)
+                    rin[i][j] = (dH_in && v < nvec) ? ld16_stream(dH_in + r0 + i * row_bytes + v * 16) : z;
             }
             // x = sum_i alpha_i H_i, dword by dword (recomputed the same way
             // after the reduction instead of being kept)
@@ -370,7 +357,7 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
                             }
                             oh[q] = pack_word<S>(o);
                         }
-                        bstore<kNT>(make_uint4(oh[0], oh[1], oh[2], oh[3]), rO, (uint32_t)v * 16u, i * rb);
+                        st16_stream(dH + r0 + i * row_bytes + v * 16, make_uint4(oh[0], oh[1], oh[2], oh[3]));
                     }
                 }
             }

@@ -133,29 +133,6 @@ template <> __device__ __forceinline__ uint32_t pack_word<fp8_t>(const float* f)
     return pack_fp8x4(f);
 }
 
-// Buffer resources: a base address and a size in bytes held in scalar
-// registers.  An access is addressed by a per-lane offset (one VGPR shared by
-// all of a thread's accesses) plus a wave-uniform offset (an SGPR), so row
-// kernels need no 64-bit address registers per stream; loads past the size
-// return zeros and stores past it are dropped.  Word 3 selects untyped 32-bit
-// data on gfx9-family chips; kNT marks data used once (nontemporal).
-constexpr int kRsrcWord3 = 0x00020000;
-constexpr int kNT = 2;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kRsrcWord3);
-}
-template <int AUX>
-__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
-template <int AUX>
-__device__ __forceinline__ void bstore(uint4 v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    const u32x4 x = {v.x, v.y, v.z, v.w};
-    __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)voff, (int)soff, AUX);
-}
-
 // Makes the compiler treat v as changed here, so values it derived from v
 // before (unpacked fp32 copies) are recomputed after this point instead of
 // being kept live in registers.  Emits no instruction.
