@@ -68,7 +68,7 @@ def case(rng, dt, T, n, d, per_token):
 # every launch shape: 1..4 vectors per thread (bf16 d > 8192, fp32 d > 4096)
 SHAPES = [("bf16", 8), ("bf16", 520), ("bf16", 4096), ("bf16", 6144), ("bf16", 8200),
           ("bf16", 12288), ("bf16", 16384), ("f32", 4), ("f32", 1024), ("f32", 4100),
-          ("f32", 8192), ("f32", 12296), ("f32", 16384)]
+          ("f32", 8192), ("f32", 12288), ("f32", 12296), ("f32", 16384)]
 
 
 @pytest.mark.parametrize("dt,d", SHAPES)

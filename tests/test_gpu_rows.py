@@ -121,8 +121,8 @@ def test_identity_pre_bitwise_equals_single_stream(dt, d, n):
 
 
 @pytest.mark.parametrize("dt,d", [("bf16", 40), ("bf16", 4096), ("bf16", 6144), ("bf16", 8200),
-                                  ("f32", 516), ("f32", 16384), ("fp8", 48), ("fp8", 4096),
-                                  ("fp8", 8208)])
+                                  ("bf16", 16384), ("f32", 516), ("f32", 8196), ("f32", 12288),
+                                  ("f32", 16384), ("fp8", 48), ("fp8", 4096), ("fp8", 8208)])
 @pytest.mark.parametrize("n", [1, 3, 4])
 def test_fused_post_pre_bitwise(dt, d, n):
     rng = np.random.default_rng(31 * d + n)
