@@ -17,6 +17,8 @@ from .oracle import (  # noqa: F401
     round_fp8,
     set_threads,
     sinkhorn,
+    sinkhorn_backward,
     weights,
+    weights_backward,
     widen,
 )

@@ -441,3 +441,155 @@ void orc_pre_mix_backward(const void* du, const void* H, int dt, const double* w
         free(dx);
     }
 }
+
+/* ---------------------------------------------------------------------
+ * Gradients of the per-token weights (the chain rule through the mHC
+ * transform, tanh, the projection and the gain-free per-stream RMSNorm of
+ * orc_weights above).  The glossary's definition: the mixing is learned, so
+ * its producers take gradients too.
+ * ------------------------------------------------------------------- */
+
+/* Gradient of the mHC transform of one record, l [K] -> out [K], given
+ * dout = dL/dout; writes dl = dL/dl.  The forward is re-run keeping every
+ * intermediate matrix; each iteration is undone in reverse:
+ *   column step C = R / colsum(R):  dR_ij = (dC_ij - sum_i' dC_i'j C_i'j) / colsum_j
+ *   row step    R = M / rowsum(M):  dM_ij = (dR_ij - sum_j' dR_ij' R_ij') / rowsum_i
+ * and exp, sigmoid by their derivatives. */
+static void orc_mhc_record_backward(const double* l, const double* dout, double* dl, int n,
+                                    int iters)
+{
+    for (int i = 0; i < 2 * n; ++i) {
+        const double s = orc_sigmoid(l[i]);
+        dl[i] = dout[i] * s * (1.0 - s);
+    }
+    const int nn = n * n;
+    /* Ms[it] = matrix entering iteration it (Ms[0] = exp(l_A)), Rs[it] = after
+     * its row step; rs, cs = the row and column sums used */
+    double* Ms = (double*)malloc((size_t)(iters + 1) * nn * sizeof(double));
+    double* Rs = (double*)malloc((size_t)(iters > 0 ? iters : 1) * nn * sizeof(double));
+    double* rs = (double*)malloc((size_t)(iters > 0 ? iters : 1) * n * sizeof(double));
+    double* cs = (double*)malloc((size_t)(iters > 0 ? iters : 1) * n * sizeof(double));
+    for (int e = 0; e < nn; ++e) Ms[e] = exp(l[2 * n + e]);
+    for (int it = 0; it < iters; ++it) {
+        const double* M = Ms + (size_t)it * nn;
+        double* R = Rs + (size_t)it * nn;
+        double* C = Ms + (size_t)(it + 1) * nn;
+        for (int i = 0; i < n; ++i) {
+            double s = 0.0;
+            for (int j = 0; j < n; ++j) s += M[i * n + j];
+            rs[it * n + i] = s;
+            for (int j = 0; j < n; ++j) R[i * n + j] = M[i * n + j] / s;
+        }
+        for (int j = 0; j < n; ++j) {
+            double s = 0.0;
+            for (int i = 0; i < n; ++i) s += R[i * n + j];
+            cs[it * n + j] = s;
+            for (int i = 0; i < n; ++i) C[i * n + j] = R[i * n + j] / s;
+        }
+    }
+    double g[16], gr[16];
+    for (int e = 0; e < nn; ++e) g[e] = dout[2 * n + e];
+    for (int it = iters - 1; it >= 0; --it) {
+        const double* R = Rs + (size_t)it * nn;
+        const double* C = Ms + (size_t)(it + 1) * nn;
+        for (int j = 0; j < n; ++j) {
+            double s = 0.0;
+            for (int i = 0; i < n; ++i) s += g[i * n + j] * C[i * n + j];
+            for (int i = 0; i < n; ++i) gr[i * n + j] = (g[i * n + j] - s) / cs[it * n + j];
+        }
+        for (int i = 0; i < n; ++i) {
+            double s = 0.0;
+            for (int j = 0; j < n; ++j) s += gr[i * n + j] * R[i * n + j];
+            for (int j = 0; j < n; ++j) g[i * n + j] = (gr[i * n + j] - s) / rs[it * n + i];
+        }
+    }
+    for (int e = 0; e < nn; ++e) dl[2 * n + e] = g[e] * Ms[e];
+    free(Ms);
+    free(Rs);
+    free(rs);
+    free(cs);
+}
+
+/* dlogits [T][K] from dw [T][K] through the Sinkhorn step on logits [T][K]. */
+void orc_sinkhorn_backward(const double* logits, const double* dw, double* dlogits, int iters,
+                           int64_t T, int n)
+{
+    const int K = 2 * n + n * n;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        orc_mhc_record_backward(logits + t * K, dw + t * K, dlogits + t * K, n, iters);
+}
+
+/* Gradients of orc_weights given dw [T][K] = dL/dw:
+ *   dz = scale * (1 - tanh(z)^2) * dw                      (iters == 0)
+ *   dz = scale * dl,  dl = the mHC backward of dw at l    (iters  > 0)
+ *   dW[c][k] = sum_t dz_c hbar_k,   dw_static = sum_t (dw or dl),
+ *   dhbar = sum_c dz_c W[c],  s_i = H_i . dhbar,
+ *   dH_i = (r_i dhbar - r_i^3 s_i H_i / d) / n.
+ * dH [T][n][d], dW [K][d], dws [K] are written (not accumulated).  Tokens are
+ * taken in order, so the sums over tokens are reproducible. */
+void orc_weights_backward(const void* H, const void* W, int dt, const double* w_static,
+                          double scale, double eps, int iters, const double* dw, double* dH,
+                          double* dW, double* dws, int64_t T, int n, int d)
+{
+    const int K = 2 * n + n * n;
+    for (int64_t e = 0; e < (int64_t)K * d; ++e) dW[e] = 0.0;
+    for (int c = 0; c < K; ++c) dws[c] = 0.0;
+    double* hbar = (double*)malloc((size_t)d * sizeof(double));
+    double* dhbar = (double*)malloc((size_t)d * sizeof(double));
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t row0 = t * (int64_t)n * d;
+        double r[4];
+        for (int i = 0; i < n; ++i) {
+            double ss = 0.0;
+            for (int k = 0; k < d; ++k) {
+                const double h = orc_load(H, row0 + (int64_t)i * d + k, dt);
+                ss += h * h;
+            }
+            r[i] = 1.0 / sqrt(ss / d + eps);
+        }
+        for (int k = 0; k < d; ++k) {
+            double s = 0.0;
+            for (int i = 0; i < n; ++i) s += r[i] * orc_load(H, row0 + (int64_t)i * d + k, dt);
+            hbar[k] = s / n;
+        }
+        double z[24], dz[24], dl[24];
+        for (int c = 0; c < K; ++c) {
+            double acc = 0.0;
+            for (int k = 0; k < d; ++k) acc += hbar[k] * orc_load(W, (int64_t)c * d + k, dt);
+            z[c] = acc;
+        }
+        const double* g = dw + t * K;
+        if (iters == 0) {
+            for (int c = 0; c < K; ++c) {
+                const double th = tanh(z[c]);
+                dl[c] = g[c];
+                dz[c] = g[c] * scale * (1.0 - th * th);
+            }
+        } else {
+            double l[24];
+            for (int c = 0; c < K; ++c) l[c] = w_static[c] + scale * z[c];
+            orc_mhc_record_backward(l, g, dl, n, iters);
+            for (int c = 0; c < K; ++c) dz[c] = scale * dl[c];
+        }
+        for (int c = 0; c < K; ++c) {
+            dws[c] += dl[c];
+            for (int k = 0; k < d; ++k) dW[(int64_t)c * d + k] += dz[c] * hbar[k];
+        }
+        for (int k = 0; k < d; ++k) {
+            double s = 0.0;
+            for (int c = 0; c < K; ++c) s += dz[c] * orc_load(W, (int64_t)c * d + k, dt);
+            dhbar[k] = s;
+        }
+        for (int i = 0; i < n; ++i) {
+            double s = 0.0;
+            for (int k = 0; k < d; ++k) s += orc_load(H, row0 + (int64_t)i * d + k, dt) * dhbar[k];
+            for (int k = 0; k < d; ++k) {
+                const int64_t e = row0 + (int64_t)i * d + k;
+                dH[e] = (r[i] * dhbar[k] - r[i] * r[i] * r[i] * s * orc_load(H, e, dt) / d) / n;
+            }
+        }
+    }
+    free(hbar);
+    free(dhbar);
+}

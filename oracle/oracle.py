@@ -63,12 +63,15 @@ def load():
     lib.orc_widen_array.argtypes = [vp, i32, dp, i64]
     lib.orc_post_mix_backward.argtypes = [vp, vp, vp, i32, dp, i64, dp, dp, dp, i64, i32, i32]
     lib.orc_pre_mix_backward.argtypes = [vp, vp, i32, dp, i64, dp, dbl, dp, dp, dp, dp, i64, i32, i32]
+    lib.orc_sinkhorn_backward.argtypes = [dp, dp, dp, i32, i64, i32]
+    lib.orc_weights_backward.argtypes = [vp, vp, i32, dp, dbl, dbl, i32, dp, dp, dp, dp, i64, i32, i32]
     lib.orc_round_bf16.argtypes = [dbl]
     lib.orc_round_bf16.restype = ctypes.c_uint16
     lib.orc_set_threads.argtypes = [i32]
     lib.orc_get_threads.restype = i32
     for f in ("orc_pre_mix", "orc_post_mix", "orc_weights", "orc_sinkhorn",
-              "orc_post_mix_backward", "orc_pre_mix_backward",
+              "orc_post_mix_backward", "orc_pre_mix_backward", "orc_sinkhorn_backward",
+              "orc_weights_backward",
               "orc_block_tanh", "orc_round_bf16_array", "orc_round_f32_array", "orc_round_fp8_array",
               "orc_widen_array", "orc_set_threads"):
         getattr(lib, f).restype = None
@@ -256,3 +259,35 @@ def pre_mix_backward(du: np.ndarray, H: np.ndarray, w: np.ndarray, gamma: np.nda
                              float(eps), _dp(acc) if acc is not None else None, _dp(dH), _dp(dw),
                              _dp(dg), T, n, d)
     return dH, dw, dg
+
+
+def sinkhorn_backward(logits: np.ndarray, dw: np.ndarray, n: int, iters: int) -> np.ndarray:
+    """Gradient of the mHC transform: dL/dlogits (T, K) from dL/dw (T, K)."""
+    lib = load()
+    lg, g = _c(logits, np.float64), _c(dw, np.float64)
+    K = 2 * n + n * n
+    T = lg.shape[0]
+    assert lg.shape == (T, K) and g.shape == (T, K)
+    out = np.empty((T, K), np.float64)
+    lib.orc_sinkhorn_backward(_dp(lg), _dp(g), _dp(out), int(iters), T, n)
+    return out
+
+
+def weights_backward(H: np.ndarray, W: np.ndarray, w_static: np.ndarray, scale: float,
+                     dw: np.ndarray, eps: float = 1e-6, iters: int = 0):
+    """Gradients of `weights` given dL/dw (T, K): returns (dH (T, n, d),
+    dW (K, d), dw_static (K,)) in float64; dH is this path's part only."""
+    lib = load()
+    H, W = _c(H), _c(W)
+    T, n, d = H.shape
+    K = 2 * n + n * n
+    assert W.shape == (K, d) and W.dtype == H.dtype
+    ws = _c(w_static, np.float64)
+    g = _c(dw, np.float64)
+    assert ws.shape == (K,) and g.shape == (T, K)
+    dH = np.empty((T, n, d), np.float64)
+    dW = np.empty((K, d), np.float64)
+    dws = np.empty(K, np.float64)
+    lib.orc_weights_backward(H.ctypes.data, W.ctypes.data, _dt(H), _dp(ws), float(scale), float(eps),
+                             int(iters), _dp(g), _dp(dH), _dp(dW), _dp(dws), T, n, d)
+    return dH, dW, dws
