@@ -260,6 +260,77 @@ hc_status hc_pre_mix_backward(const void* du, const void* H, const float* w, int
                                                 static_cast<hipStream_t>(stream)));
 }
 
+int64_t hc_weights_backward_workspace(int64_t T, int32_t n, int32_t d, int32_t sinkhorn_iters) {
+    if (n < 1 || n > HC_MAX_STREAMS || d < 1 || d > HC_MAX_HIDDEN) return 0;
+    if (sinkhorn_iters < 0 || sinkhorn_iters > HC_MAX_SINKHORN_ITERS) return 0;
+    return hc::weights_backward_workspace_bytes(T, n, d, sinkhorn_iters);
+}
+
+hc_status hc_weights_backward(const void* H, const void* W, const float* w_static, float scale,
+                              float eps, int32_t sinkhorn_iters, const float* dw, const void* dH_in,
+                              void* dH, float* dW, float* dw_static, void* workspace,
+                              int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
+                              void* stream) {
+    if (!dtype_wide(dt)) return HC_ERR_DTYPE;
+    hc_status st = check_nd(n, d, T, dt);
+    if (st != HC_OK) return st;
+    if (!eps_ok(eps) || !std::isfinite(scale)) return HC_ERR_ARG;
+    if (sinkhorn_iters < 0 || sinkhorn_iters > HC_MAX_SINKHORN_ITERS) return HC_ERR_ARG;
+    if (T == 0) return HC_OK;
+    if (!H || !W || !w_static || !dw || !dH || !dW || !dw_static || !workspace) return HC_ERR_NULL;
+    const int64_t need = hc_weights_backward_workspace(T, n, d, sinkhorn_iters);
+    if (workspace_bytes < need) return HC_ERR_ARG;
+    if (misaligned(H, 16) || misaligned(W, 16) || misaligned(dH, 16) || misaligned(dH_in, 16) ||
+        misaligned(workspace, 16) || misaligned(w_static, 4) || misaligned(dw, 4) ||
+        misaligned(dW, 4) || misaligned(dw_static, 4))
+        return HC_ERR_ALIGN;
+    const int K = record_len(n);
+    const int64_t s = elem_bytes(dt);
+    const Span sH{H, T * n * d * s}, sW{W, int64_t(K) * d * s}, sS{w_static, int64_t(K) * 4},
+        sg{dw, T * K * 4}, sin{dH_in, dH_in ? T * n * d * s : 0}, sdH{dH, T * n * d * s},
+        sdW{dW, int64_t(K) * d * 4}, sds{dw_static, int64_t(K) * 4}, sws{workspace, need};
+    const Span ins[] = {sH, sW, sS, sg};
+    for (const Span& o : {sdH, sdW, sds, sws})
+        for (const Span& i : ins)
+            if (overlap(o, i)) return HC_ERR_ALIAS;
+    if (dH_in && dH_in != dH && overlap(sdH, sin)) return HC_ERR_ALIAS;
+    for (const Span& o : {sdW, sds, sws})
+        if (overlap(o, sin)) return HC_ERR_ALIAS;
+    if (overlap(sdH, sdW) || overlap(sdH, sds) || overlap(sdH, sws) || overlap(sdW, sds) ||
+        overlap(sdW, sws) || overlap(sds, sws))
+        return HC_ERR_ALIAS;
+    return from_hip(hc::launch_weights_backward(H, W, w_static, scale, eps, sinkhorn_iters, dw,
+                                                dH_in, dH, dW, dw_static, workspace, T, n, d, dt,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int64_t hc_sinkhorn_backward_workspace(int64_t T, int32_t iters) {
+    if (iters < 0 || iters > HC_MAX_SINKHORN_ITERS) return 0;
+    return hc::sinkhorn_backward_workspace_bytes(T, iters);
+}
+
+hc_status hc_sinkhorn_backward(const float* logits, const float* dw, float* dlogits, int32_t iters,
+                               void* workspace, int64_t workspace_bytes, int64_t T, int32_t n,
+                               void* stream) {
+    if (n < 1 || n > HC_MAX_STREAMS) return HC_ERR_SHAPE;
+    if (T < 0 || iters < 0 || iters > HC_MAX_SINKHORN_ITERS) return HC_ERR_ARG;
+    const int K = record_len(n);
+    if (T > kMaxBytes / (4 * K)) return HC_ERR_ARG;
+    if (T == 0) return HC_OK;
+    if (!logits || !dw || !dlogits) return HC_ERR_NULL;
+    const int64_t need = hc_sinkhorn_backward_workspace(T, iters);
+    if (need > 0 && !workspace) return HC_ERR_NULL;
+    if (workspace_bytes < need) return HC_ERR_ARG;
+    if (misaligned(logits, 4) || misaligned(dw, 4) || misaligned(dlogits, 4) ||
+        (need > 0 && misaligned(workspace, 4)))
+        return HC_ERR_ALIGN;
+    const Span sl{logits, T * K * 4}, sg{dw, T * K * 4}, so{dlogits, T * K * 4}, sws{workspace, need};
+    if (overlap(so, sl) || overlap(so, sg) || overlap(sws, sl) || overlap(sws, sg) || overlap(sws, so))
+        return HC_ERR_ALIAS;
+    return from_hip(hc::launch_sinkhorn_backward(logits, dw, dlogits, iters, workspace, T, n,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 hc_status hc_sum_records(const float* rec, int64_t T, int32_t K, float* out, void* stream) {
     if (K < 1 || K > 1024) return HC_ERR_SHAPE;
     if (T < 0 || T > kMaxBytes / 4 / K) return HC_ERR_ARG;

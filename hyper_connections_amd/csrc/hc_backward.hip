@@ -595,6 +595,16 @@ hipError_t launch_pre_mix_backward(const void* du, const void* H, const float* w
                   int64_t(0), K - n, dw + n);   // zero rows: writes 0
 }
 
+int64_t sum_rows_tmp_floats(int64_t rows, int64_t cols) {
+    const int64_t segs = (rows + kSumRows - 1) / kSumRows;
+    return 2 * (segs + 1) * cols;
+}
+
+hipError_t launch_sum_rows(const float* in, int64_t rows, int cols, float* tmp, float* out,
+                           hipStream_t s) {
+    return sum_rows(in, rows, cols, tmp, out, s);
+}
+
 hipError_t launch_sum_records(const float* rec, int64_t T, int K, float* out, hipStream_t s) {
     return launch(sum_records_kernel, dim3(K), dim3(1024), 0, s, rec, T, K, out);
 }

@@ -1,0 +1,460 @@
+// hc_weights_bwd.hip -- gradients of the per-token weight producer: the mHC
+// (Sinkhorn) transform, tanh, the projection W and the gain-free per-stream
+// RMSNorm that feeds it.
+//
+// Sources: hfviewer.com glossary "Hyper-connections (mHC)", definition (the
+// mixing weights are learned and the mHC variant normalises them with a few
+// Sinkhorn iterations), so every producer of the weights takes gradients.
+// The forward being differentiated (the reading implemented by hc_weights):
+//   r_i = 1/sqrt(mean_k H_ik^2 + eps), hbar = (1/n) sum_i r_i H_i,
+//   z = W hbar, w = w_static + scale tanh(z)      or      w = mhc(w_static + scale z).
+// Chain rule, per token:
+//   dz = scale (1 - tanh(z)^2) dw                  or      dz = scale dl, dl = mhc'(dw)
+//   dW += dz hbar^T,   dhbar = W^T dz,   s_i = H_i . dhbar = P_i . dz  (P_i = W H_i)
+//   dH_i = a_i dhbar + b_i H_i,  a_i = r_i / n,  b_i = -r_i^3 s_i / (n d)
+//   dw_static = sum over tokens of dw (tanh) or dl (mHC).
+// Passes: (1) the forward projection again, keeping P_i and r_i per token
+// (hc_weights.hip, raw mode); (2) one thread per token turns them and dw
+// into dz, a_i, b_i (and dl); (3) one streaming pass over H computes dH and
+// partial sums of dW on the matrix cores; (4) fixed-order sums of the
+// partials.  Everything is deterministic.
+#include "hc_device.h"
+#include "hc_launch.h"
+
+namespace hc {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int64_t kMaxGrid = 1 << 20;
+constexpr int kSlot = 16;      // floats per token per iteration in the Sinkhorn scratch
+
+// ------------------------------------------------------ mHC transform backward
+
+// Gradient of the mHC record transform for one token, one thread:
+// l [K] logits, g [K] = dL/dw in, dl [K] = dL/dl out.  The forward is re-run
+// (with the largest A logit subtracted, as the forward kernels do; the row
+// normalisation removes it exactly) and the matrix entering every iteration
+// is kept in `scr` (iteration it at scr + it * stride, kSlot floats); the
+// iterations are then undone in reverse:
+//   column step C = R / colsum:  dR_ij = (dC_ij - sum_i' dC_i'j C_i'j) / colsum_j
+//   row step    R = M / rowsum:  dM_ij = (dR_ij - sum_j' dR_ij' R_ij') / rowsum_i
+template <int N>
+__device__ void mhc_record_bwd(const float* l, const float* g, float* dl, int iters, float* scr,
+                               int64_t stride) {
+    constexpr int NN = N * N;
+    for (int i = 0; i < 2 * N; ++i) {
+        const float s = 1.0f / (1.0f + expf(-l[i]));
+        dl[i] = g[i] * s * (1.0f - s);
+    }
+    float M[NN], M0[NN];
+    float m = 0.0f;
+    if (iters > 0) {
+        m = l[2 * N];
+#pragma unroll
+        for (int e = 1; e < NN; ++e) m = fmaxf(m, l[2 * N + e]);
+    }
+#pragma unroll
+    for (int e = 0; e < NN; ++e) M0[e] = M[e] = expf(l[2 * N + e] - m);
+    for (int it = 0; it < iters; ++it) {
+        float* dst = scr + it * stride;
+#pragma unroll
+        for (int e = 0; e < NN; ++e) dst[e] = M[e];
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            float s = M[i * N];
+#pragma unroll
+            for (int j = 1; j < N; ++j) s += M[i * N + j];
+#pragma unroll
+            for (int j = 0; j < N; ++j) M[i * N + j] = M[i * N + j] / s;
+        }
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            float s = M[j];
+#pragma unroll
+            for (int i = 1; i < N; ++i) s += M[i * N + j];
+#pragma unroll
+            for (int i = 0; i < N; ++i) M[i * N + j] = M[i * N + j] / s;
+        }
+    }
+    float G[NN];
+#pragma unroll
+    for (int e = 0; e < NN; ++e) G[e] = g[2 * N + e];
+    for (int it = iters - 1; it >= 0; --it) {
+        const float* src = scr + it * stride;
+        float R[NN], rs[N], cs[N];
+#pragma unroll
+        for (int e = 0; e < NN; ++e) R[e] = src[e];
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            float s = R[i * N];
+#pragma unroll
+            for (int j = 1; j < N; ++j) s += R[i * N + j];
+            rs[i] = s;
+#pragma unroll
+            for (int j = 0; j < N; ++j) R[i * N + j] = R[i * N + j] / s;
+        }
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            float s = R[j];
+#pragma unroll
+            for (int i = 1; i < N; ++i) s += R[i * N + j];
+            cs[j] = s;
+        }
+        // column step: C_ij = R_ij / cs_j
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < N; ++i) s = fmaf(G[i * N + j], R[i * N + j] / cs[j], s);
+#pragma unroll
+            for (int i = 0; i < N; ++i) G[i * N + j] = (G[i * N + j] - s) / cs[j];
+        }
+        // row step: R_ij = M_ij / rs_i
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            float s = 0.0f;
+#pragma unroll
+            for (int j = 0; j < N; ++j) s = fmaf(G[i * N + j], R[i * N + j], s);
+#pragma unroll
+            for (int j = 0; j < N; ++j) G[i * N + j] = (G[i * N + j] - s) / rs[i];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < NN; ++e) dl[2 * N + e] = G[e] * M0[e];
+}
+
+template <int N>
+__global__ __launch_bounds__(256) void sinkhorn_bwd_kernel(const float* __restrict__ logits,
+                                                           const float* __restrict__ dw,
+                                                           float* __restrict__ dlogits, int iters,
+                                                           float* __restrict__ scr, int64_t T) {
+    constexpr int K = 2 * N + N * N;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < T;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        float l[K], g[K], out[K];
+#pragma unroll
+        for (int c = 0; c < K; ++c) {
+            l[c] = logits[t * K + c];
+            g[c] = dw[t * K + c];
+        }
+        mhc_record_bwd<N>(l, g, out, iters, scr + t * kSlot, T * kSlot);
+#pragma unroll
+        for (int c = 0; c < K; ++c) dlogits[t * K + c] = out[c];
+    }
+}
+
+// ----------------------------------------------------- per-token coefficients
+
+// From P [T][N][K], r [T][N] (the forward projection pass) and dw [T][K]:
+// dz [T][K], dl [T][K] (the gradient at the logits / records that
+// w_static receives) and ab [T][2][N] = (a_i, b_i).  One thread per token.
+template <int N>
+__global__ __launch_bounds__(256) void wgrad_coef_kernel(
+    const float* __restrict__ P, const float* __restrict__ r, const float* __restrict__ dw,
+    const float* __restrict__ w_static, float scale, int iters, float* __restrict__ scr,
+    float* __restrict__ dz, float* __restrict__ dl, float* __restrict__ ab, int64_t T, int d) {
+    constexpr int K = 2 * N + N * N;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < T;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const float* p = P + t * N * K;
+        float ri[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) ri[i] = r[t * N + i];
+        float z[K], g[K], gl[K], gz[K];
+#pragma unroll
+        for (int c = 0; c < K; ++c) {
+            // z as the forward kernel forms it: sum_i r_i P_ic in stream order, / n
+            float v = ri[0] * p[c];
+#pragma unroll
+            for (int i = 1; i < N; ++i) v = fmaf(ri[i], p[i * K + c], v);
+            z[c] = v / (float)N;
+            g[c] = dw[t * K + c];
+        }
+        if (iters == 0) {
+#pragma unroll
+            for (int c = 0; c < K; ++c) {
+                const float th = tanhf(z[c]);
+                gl[c] = g[c];
+                gz[c] = g[c] * scale * (1.0f - th * th);
+            }
+        } else {
+            float l[K];
+#pragma unroll
+            for (int c = 0; c < K; ++c) l[c] = fmaf(scale, z[c], w_static[c]);
+            mhc_record_bwd<N>(l, g, gl, iters, scr + t * kSlot, T * kSlot);
+#pragma unroll
+            for (int c = 0; c < K; ++c) gz[c] = scale * gl[c];
+        }
+#pragma unroll
+        for (int c = 0; c < K; ++c) {
+            dz[t * K + c] = gz[c];
+            dl[t * K + c] = gl[c];
+        }
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            float s = 0.0f;
+#pragma unroll
+            for (int c = 0; c < K; ++c) s = fmaf(p[i * K + c], gz[c], s);
+            ab[t * 2 * N + i] = ri[i] / (float)N;
+            ab[t * 2 * N + N + i] = -(ri[i] * ri[i] * ri[i]) * s / ((float)N * (float)d);
+        }
+    }
+}
+
+// ---------------------------------------------------- streaming dH and dW pass
+
+// One workgroup owns a slice of CB = 16 V columns (16 lanes x one 16-byte
+// vector) and a range of tokens.  Each wave takes 4 tokens per step: lane l
+// works on token l / 16 of the step and columns (slice + l % 16) * V .. + V-1,
+// so every load is 16 lanes x 16 contiguous bytes of one row.  Per element:
+//   hbar = (1/n) sum_i r_i H_i,  dhbar = sum_c dz_c W[c] (W slice in LDS),
+//   dH_i = dH_in_i + a_i dhbar + b_i H_i.
+// dW: the 4 tokens of a step are the contraction of v_mfma_f32_16x16x4f32:
+// A[m = c][k = token] = dz (c = l % 16 + 16 q), B[k = token][n] = the lane's
+// hbar element e, so "virtual tile" e has output column (slice + n) V + e --
+// the lane's own columns, no shuffles.  Each wave keeps its partial dW
+// (2 x V tiles) and writes it to part[(split * 4 + wave)][K][d] at the end.
+template <int N, typename S>
+__global__ __launch_bounds__(256) void wgrad_stream_kernel(
+    const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, const float* __restrict__ dz,
+    const float* __restrict__ ab, const float* __restrict__ r, const uint8_t* dH_in,
+    uint8_t* dH, float* __restrict__ part, int64_t T, int d, int64_t tok_per_split) {
+    constexpr int V = Store<S>::kElems, SB = Store<S>::kBytes;
+    constexpr int K = 2 * N + N * N;
+    constexpr int CB = 16 * V;                       // columns per workgroup
+    __shared__ __attribute__((aligned(16))) uint8_t wl[K * CB * SB];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, cl = lane & 15;
+    const int nvec = d / V;
+    const int cv = blockIdx.x * 16 + cl;             // this lane's vector column
+    const bool col_ok = cv < nvec;
+    const int64_t row_bytes = (int64_t)d * SB;
+
+    // the W slice: K rows x CB columns
+    for (int p = threadIdx.x; p < K * 16; p += 256) {
+        const int c = p / 16, v = blockIdx.x * 16 + p % 16;
+        *reinterpret_cast<uint4*>(wl + (c * 16 + p % 16) * 16) =
+            v < nvec ? ld16(W + ((int64_t)c * d + (int64_t)v * V) * SB) : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+
+    f32x4 acc[2][V];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[q][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t t_begin = (int64_t)blockIdx.y * tok_per_split;
+    const int64_t t_end = t_begin + tok_per_split < T ? t_begin + tok_per_split : T;
+    for (int64_t t0 = t_begin + 4 * wave; t0 < t_end; t0 += 16) {
+        const int64_t t = t0 + g;
+        const bool ok = t < t_end;
+        const bool live = ok && col_ok;
+        const int64_t r0 = (ok ? t : t_begin) * N * row_bytes + (int64_t)cv * 16;
+        uint4 rh[N], rin[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            rh[i] = live ? ld16_stream(H + r0 + i * row_bytes) : make_uint4(0, 0, 0, 0);
+            rin[i] = (live && dH_in) ? ld16_stream(dH_in + r0 + i * row_bytes) : make_uint4(0, 0, 0, 0);
+        }
+        const int64_t tt = ok ? t : t_begin;
+        float gz[K];
+#pragma unroll
+        for (int c = 0; c < K; ++c) gz[c] = ok ? dz[tt * K + c] : 0.0f;
+        float ri[N], ai[N], bi[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            ri[i] = ok ? r[tt * N + i] : 0.0f;
+            ai[i] = ok ? ab[tt * 2 * N + i] : 0.0f;
+            bi[i] = ok ? ab[tt * 2 * N + N + i] : 0.0f;
+        }
+        // dhbar for the lane's V columns
+        float dhb[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) dhb[e] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < K; ++c) {
+            float wv[V];
+            unpack<S>(*reinterpret_cast<const uint4*>(wl + (c * 16 + cl) * 16), wv);
+#pragma unroll
+            for (int e = 0; e < V; ++e) dhb[e] = fmaf(gz[c], wv[e], dhb[e]);
+        }
+        float hb[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) hb[e] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            float h[V], o[V];
+            unpack<S>(rh[i], h);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                hb[e] = fmaf(ri[i], h[e], hb[e]);
+                o[e] = fmaf(ai[i], dhb[e], bi[i] * h[e]);
+            }
+            if (dH_in) {
+                float p[V];
+                unpack<S>(rin[i], p);
+#pragma unroll
+                for (int e = 0; e < V; ++e) o[e] += p[e];
+            }
+            if (live) st16_stream(dH + r0 + i * row_bytes, pack<S>(o));
+        }
+#pragma unroll
+        for (int e = 0; e < V; ++e) hb[e] = hb[e] / (float)N;
+        // dW partial on the matrix cores
+        float a0 = 0.0f, a1 = 0.0f;
+        if (ok) {
+            a0 = cl < K ? dz[tt * K + cl] : 0.0f;
+            a1 = cl + 16 < K ? dz[tt * K + 16 + cl] : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const float bv = col_ok ? hb[e] : 0.0f;
+            acc[0][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bv, acc[0][e], 0, 0, 0);
+            acc[1][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bv, acc[1][e], 0, 0, 0);
+        }
+    }
+    // this wave's partial: C[m = 4 g + j][n = cl] of tile (q, e) is
+    // dW[c = 16 q + 4 g + j][column cv * V + e]
+    float* out = part + ((int64_t)blockIdx.y * 4 + wave) * K * (int64_t)d;
+    if (col_ok) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = 16 * q + 4 * g + j;
+                if (c < K) {
+#pragma unroll
+                    for (int e = 0; e < V; ++e) out[(int64_t)c * d + (int64_t)cv * V + e] = acc[q][e][j];
+                }
+            }
+    }
+}
+
+template <int N>
+hipError_t coef_go(const float* P, const float* r, const float* dw, const float* ws, float scale,
+                   int iters, float* scr, float* dz, float* dl, float* ab, int64_t T, int d,
+                   hipStream_t s) {
+    const int64_t blocks = (T + 255) / 256;
+    return launch(wgrad_coef_kernel<N>, dim3((unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid)),
+                  dim3(256), 0, s, P, r, dw, ws, scale, iters, scr, dz, dl, ab, T, d);
+}
+
+template <int N, typename S>
+hipError_t stream_go(const void* H, const void* W, const float* dz, const float* ab, const float* r,
+                     const void* dH_in, void* dH, float* part, int64_t T, int d, int splits,
+                     int64_t tps, hipStream_t s) {
+    const int nvec = d / Store<S>::kElems;
+    const dim3 grid((unsigned)((nvec + 15) / 16), (unsigned)splits);
+    return launch(wgrad_stream_kernel<N, S>, grid, dim3(256), 0, s, static_cast<const uint8_t*>(H),
+                  static_cast<const uint8_t*>(W), dz, ab, r, static_cast<const uint8_t*>(dH_in),
+                  static_cast<uint8_t*>(dH), part, T, d, tps);
+}
+
+template <typename S>
+hipError_t stream_by_n(int n, const void* H, const void* W, const float* dz, const float* ab,
+                       const float* r, const void* dH_in, void* dH, float* part, int64_t T, int d,
+                       int splits, int64_t tps, hipStream_t s) {
+    switch (n) {
+        case 1: return stream_go<1, S>(H, W, dz, ab, r, dH_in, dH, part, T, d, splits, tps, s);
+        case 2: return stream_go<2, S>(H, W, dz, ab, r, dH_in, dH, part, T, d, splits, tps, s);
+        case 3: return stream_go<3, S>(H, W, dz, ab, r, dH_in, dH, part, T, d, splits, tps, s);
+        case 4: return stream_go<4, S>(H, W, dz, ab, r, dH_in, dH, part, T, d, splits, tps, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Tokens per dW split: enough workgroups (columns x splits) to fill the chip,
+// at least 64 tokens each; at most 64 splits.
+inline int64_t splits_of(int64_t T) {
+    int64_t s = (T + 511) / 512;
+    if (s > 64) s = 64;
+    return s < 1 ? 1 : s;
+}
+
+// Workspace layout (floats): P [T][n][K] | r [T][n] | dz [T][K] | dl [T][K] |
+// ab [T][2n] | Sinkhorn scratch [iters][T][16] | dW partials [4 splits][K][d] |
+// sum scratch.  Every region starts 16-byte aligned.
+struct WgSpace {
+    int64_t P, r, dz, dl, ab, scr, part, tmp, total;
+};
+inline int64_t up4(int64_t x) { return (x + 3) / 4 * 4; }
+inline WgSpace wg_space(int64_t T, int n, int d, int iters) {
+    const int64_t K = 2 * n + int64_t(n) * n;
+    WgSpace w;
+    w.P = 0;
+    w.r = w.P + up4(T * n * K);
+    w.dz = w.r + up4(T * n);
+    w.dl = w.dz + up4(T * K);
+    w.ab = w.dl + up4(T * K);
+    w.scr = w.ab + up4(T * 2 * n);
+    w.part = w.scr + up4(int64_t(iters) * T * kSlot);
+    const int64_t rows = splits_of(T) * 4;
+    w.tmp = w.part + up4(rows * K * d);
+    w.total = w.tmp + sum_rows_tmp_floats(rows, K * d);
+    return w;
+}
+
+}  // namespace
+
+int64_t weights_backward_workspace_bytes(int64_t T, int n, int d, int iters) {
+    if (T <= 0 || n <= 0 || d <= 0 || iters < 0) return 0;
+    return wg_space(T, n, d, iters).total * 4;
+}
+
+int64_t sinkhorn_backward_workspace_bytes(int64_t T, int iters) {
+    if (T <= 0 || iters <= 0) return 0;
+    return int64_t(iters) * T * kSlot * 4;
+}
+
+hipError_t launch_sinkhorn_backward(const float* logits, const float* dw, float* dlogits, int iters,
+                                    void* work, int64_t T, int n, hipStream_t s) {
+    const int64_t blocks = (T + 255) / 256;
+    const dim3 grid((unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid));
+    float* scr = static_cast<float*>(work);
+    switch (n) {
+        case 1: return launch(sinkhorn_bwd_kernel<1>, grid, dim3(256), 0, s, logits, dw, dlogits, iters, scr, T);
+        case 2: return launch(sinkhorn_bwd_kernel<2>, grid, dim3(256), 0, s, logits, dw, dlogits, iters, scr, T);
+        case 3: return launch(sinkhorn_bwd_kernel<3>, grid, dim3(256), 0, s, logits, dw, dlogits, iters, scr, T);
+        case 4: return launch(sinkhorn_bwd_kernel<4>, grid, dim3(256), 0, s, logits, dw, dlogits, iters, scr, T);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_weights_backward(const void* H, const void* W, const float* w_static, float scale,
+                                   float eps, int iters, const float* dw, const void* dH_in,
+                                   void* dH, float* dW, float* dws, void* work, int64_t T, int n,
+                                   int d, int dt, hipStream_t s) {
+    const WgSpace sp = wg_space(T, n, d, iters);
+    float* ws = static_cast<float*>(work);
+    const int K = 2 * n + n * n;
+    // (1) per-stream projections and row norms
+    hipError_t e = launch_weights_raw(H, W, eps, ws + sp.P, ws + sp.r, T, n, d, dt, s);
+    if (e != hipSuccess) return e;
+    // (2) per-token coefficients
+    switch (n) {
+        case 1: e = coef_go<1>(ws + sp.P, ws + sp.r, dw, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
+        case 2: e = coef_go<2>(ws + sp.P, ws + sp.r, dw, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
+        case 3: e = coef_go<3>(ws + sp.P, ws + sp.r, dw, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
+        case 4: e = coef_go<4>(ws + sp.P, ws + sp.r, dw, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    // (3) dH and the dW partials
+    const int64_t splits = splits_of(T);
+    const int64_t tps = (T + splits - 1) / splits;
+    e = dt == 0 ? stream_by_n<f32_t>(n, H, W, ws + sp.dz, ws + sp.ab, ws + sp.r, dH_in, dH, ws + sp.part,
+                                     T, d, (int)splits, tps, s)
+                : stream_by_n<bf16_t>(n, H, W, ws + sp.dz, ws + sp.ab, ws + sp.r, dH_in, dH,
+                                      ws + sp.part, T, d, (int)splits, tps, s);
+    if (e != hipSuccess) return e;
+    // (4) fixed-order sums: dW over the partials, dw_static over the tokens
+    e = launch_sum_rows(ws + sp.part, splits * 4, K * d, ws + sp.tmp, dW, s);
+    if (e != hipSuccess) return e;
+    return launch_sum_records(ws + sp.dl, T, K, dws, s);
+}
+
+}  // namespace hc

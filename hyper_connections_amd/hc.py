@@ -49,8 +49,12 @@ _SIGS = {
     "hc_pre_mix_backward": [_vp, _vp, _fp, _i64, _fp, _f32, _vp, _vp, _fp, _fp, _vp, _i64, _i64,
                             _i32, _i32, _i32, _vp],
     "hc_sum_records": [_fp, _i64, _i32, _fp, _vp],
+    "hc_weights_backward": [_vp, _vp, _fp, _f32, _f32, _i32, _fp, _vp, _vp, _fp, _fp, _vp, _i64,
+                            _i64, _i32, _i32, _i32, _vp],
+    "hc_sinkhorn_backward": [_fp, _fp, _fp, _i32, _vp, _i64, _i64, _i32, _vp],
 }
-EXPORTS = tuple(_SIGS) + ("hc_status_str", "hc_abi_version", "hc_backward_workspace")
+EXPORTS = tuple(_SIGS) + ("hc_status_str", "hc_abi_version", "hc_backward_workspace",
+                          "hc_weights_backward_workspace", "hc_sinkhorn_backward_workspace")
 
 _lib = None
 
@@ -80,6 +84,11 @@ def lib() -> ctypes.CDLL:
         L.hc_abi_version.restype = ctypes.c_int32
         L.hc_backward_workspace.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
         L.hc_backward_workspace.restype = ctypes.c_int64
+        L.hc_weights_backward_workspace.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.c_int32]
+        L.hc_weights_backward_workspace.restype = ctypes.c_int64
+        L.hc_sinkhorn_backward_workspace.argtypes = [ctypes.c_int64, ctypes.c_int32]
+        L.hc_sinkhorn_backward_workspace.restype = ctypes.c_int64
         _lib = L
     return _lib
 
@@ -326,4 +335,66 @@ def sum_records(rec, out=None, stream=None):
     T, K = rec.shape
     o = torch.empty(K, dtype=torch.float32, device=rec.device) if out is None else _dev(out, "out")
     _call("hc_sum_records", rec.data_ptr(), T, K, o.data_ptr(), _stream(stream))
+    return o
+
+
+def weights_backward(H, W, w_static, scale: float, dw, eps: float = 1e-6, sinkhorn_iters: int = 0,
+                     dH_in=None, out=None, dW=None, dw_static=None, workspace=None, stream=None):
+    """Gradients of weights: returns (dH, dW, dw_static).  dw is dL/d(records)
+    (T, K) float32; dH includes dH_in when given (``out=dH_in`` accumulates in
+    place); dW (K, d) and dw_static (K,) are float32."""
+    T, n, d, K = _H(H)
+    _dev(W, "W")
+    _dev(w_static, "w_static")
+    _dev(dw, "dw")
+    if W.dtype != H.dtype or tuple(W.shape) != (K, d):
+        raise ValueError(f"W must match H's dtype and have shape ({K}, {d})")
+    if w_static.dtype != torch.float32 or tuple(w_static.shape) != (K,):
+        raise ValueError(f"w_static must be float32 of shape ({K},)")
+    if dw.dtype != torch.float32 or tuple(dw.shape) != (T, K):
+        raise ValueError(f"dw must be float32 of shape ({T}, {K})")
+    if dH_in is not None:
+        _dev(dH_in, "dH_in")
+        if dH_in.dtype != H.dtype or dH_in.shape != H.shape:
+            raise ValueError("dH_in must match H")
+    dH = torch.empty_like(H) if out is None else _dev(out, "out")
+    if dH.dtype != H.dtype or dH.shape != H.shape:
+        raise ValueError("out must match H")
+    dW = torch.empty((K, d), dtype=torch.float32, device=H.device) if dW is None else _dev(dW, "dW")
+    dws = (torch.empty(K, dtype=torch.float32, device=H.device) if dw_static is None
+           else _dev(dw_static, "dw_static"))
+    if dW.dtype != torch.float32 or tuple(dW.shape) != (K, d):
+        raise ValueError(f"dW must be float32 of shape ({K}, {d})")
+    if dws.dtype != torch.float32 or tuple(dws.shape) != (K,):
+        raise ValueError(f"dw_static must be float32 of shape ({K},)")
+    need = int(lib().hc_weights_backward_workspace(T, n, d, int(sinkhorn_iters)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=H.device)
+    _dev(workspace, "workspace")
+    _call("hc_weights_backward", H.data_ptr(), W.data_ptr(), w_static.data_ptr(), float(scale),
+          float(eps), int(sinkhorn_iters), dw.data_ptr(),
+          dH_in.data_ptr() if dH_in is not None else None, dH.data_ptr(), dW.data_ptr(),
+          dws.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+          T, n, d, _dt(H), _stream(stream))
+    return dH, dW, dws
+
+
+def sinkhorn_backward(logits, dw, n: int, iters: int, out=None, workspace=None, stream=None):
+    """Gradient of sinkhorn: dL/dlogits (T, K) float32 from dL/dw (T, K)."""
+    _dev(logits, "logits")
+    _dev(dw, "dw")
+    K = 2 * n + n * n
+    if logits.dtype != torch.float32 or logits.dim() != 2 or logits.shape[1] != K:
+        raise ValueError(f"logits must be float32 of shape (T, {K})")
+    if dw.dtype != torch.float32 or dw.shape != logits.shape:
+        raise ValueError("dw must match logits")
+    T = logits.shape[0]
+    o = torch.empty_like(logits) if out is None else _dev(out, "out")
+    need = int(lib().hc_sinkhorn_backward_workspace(T, int(iters)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=logits.device)
+    _dev(workspace, "workspace")
+    _call("hc_sinkhorn_backward", logits.data_ptr(), dw.data_ptr(), o.data_ptr(), int(iters),
+          workspace.data_ptr(), workspace.numel() * workspace.element_size(), T, n,
+          _stream(stream))
     return o

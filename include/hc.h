@@ -76,8 +76,8 @@ typedef enum hc_status {
  * BF16 and FP8 weights ([EXPL] "The news"; [MAP] "inference quantization");
  * the pages name no 8-bit format, E4M3 is the one implemented.  FP8 is taken
  * by hc_pre_mix, hc_post_mix, hc_post_pre_mix, hc_weights (H and W in FP8,
- * fp32 accumulation) and hc_block_tanh; the gradient calls return
- * HC_ERR_DTYPE for it. */
+ * fp32 accumulation) and hc_block_tanh; the gradient calls (the *_backward
+ * entry points) return HC_ERR_DTYPE for it. */
 typedef enum hc_dtype { HC_F32 = 0, HC_BF16 = 1, HC_FP8 = 2 } hc_dtype;
 
 #define HC_MAX_STREAMS 4
@@ -190,6 +190,44 @@ hc_status hc_pre_mix_backward(const void* du, const void* H, const float* w, int
                               const float* gamma, float eps, const void* dH_in, void* dH,
                               float* dw, float* dgamma, void* workspace, int64_t workspace_bytes,
                               int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream);
+
+/* Bytes of device workspace hc_weights_backward needs (0 for T <= 0 or
+ * arguments out of range).  It holds the per-stream projections, per-token
+ * coefficients, Sinkhorn intermediates (16 floats per token per iteration)
+ * and partial sums; every call rewrites it. */
+int64_t hc_weights_backward_workspace(int64_t T, int32_t n, int32_t d, int32_t sinkhorn_iters);
+
+/* Gradients of hc_weights ([GLOSS] definition: the weight producers are
+ * learned too).  With z = W hbar as in hc_weights and dw = dL/dw_out:
+ *   sinkhorn_iters == 0:  dz = scale (1 - tanh(z)^2) dw,   dw_static = sum_t dw
+ *   sinkhorn_iters  > 0:  dl = the mHC backward of dw at l = w_static + scale z,
+ *                         dz = scale dl,                    dw_static = sum_t dl
+ *   dW = sum_t dz hbar^T   (fp32, [K][d], summed in a fixed order)
+ *   dH_i = dH_in_i + (r_i dhbar - r_i^3 (H_i . dhbar) H_i / d) / n,  dhbar = W^T dz
+ *   H [T][n][d] dt, W [K][d] dt, w_static [K], scale, eps, sinkhorn_iters as in
+ *     hc_weights; dw [T][K] fp32 (records of stride K)
+ *   dH_in [T][n][d] dt or NULL; dH [T][n][d] dt (dH == dH_in allowed)
+ *   dW [K][d] fp32, dw_static [K] fp32 outputs
+ *   workspace >= hc_weights_backward_workspace(T, n, d, sinkhorn_iters), 16-byte
+ *     aligned.  fp32 and bf16 storage only (HC_ERR_DTYPE for HC_FP8). */
+hc_status hc_weights_backward(const void* H, const void* W, const float* w_static, float scale,
+                              float eps, int32_t sinkhorn_iters, const float* dw, const void* dH_in,
+                              void* dH, float* dW, float* dw_static, void* workspace,
+                              int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
+                              void* stream);
+
+/* Bytes of device workspace hc_sinkhorn_backward needs: 64 per token per
+ * iteration (0 for iters == 0). */
+int64_t hc_sinkhorn_backward_workspace(int64_t T, int32_t iters);
+
+/* Gradient of hc_sinkhorn: dlogits [T][K] from dw = dL/dw [T][K] (both fp32,
+ * stride K).  Each token's forward is re-run keeping the matrix entering
+ * every iteration in the workspace; the row and column steps are undone in
+ * reverse, then exp and the sigmoids.  dlogits may not overlap the inputs or
+ * the workspace. */
+hc_status hc_sinkhorn_backward(const float* logits, const float* dw, float* dlogits, int32_t iters,
+                               void* workspace, int64_t workspace_bytes, int64_t T, int32_t n,
+                               void* stream);
 
 /* out[c] = sum over t of rec[t * K + c], c < K, summed in a fixed order:
  * turns per-token gradient records into the gradient of one shared record.

@@ -175,3 +175,37 @@ def test_binding_rejects_host_tensors():
     H = torch.zeros(2, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         hc.pre_mix(H, torch.zeros(24), torch.ones(64))
+
+
+def test_weights_backward_validation(L):
+    need = L.hc_weights_backward_workspace(64, 4, 4096, 0)
+    assert need > 0 and L.hc_weights_backward_workspace(0, 4, 4096, 0) == 0
+    assert L.hc_weights_backward_workspace(64, 5, 4096, 0) == 0
+    assert L.hc_weights_backward_workspace(64, 4, 4096, -1) == 0
+    assert L.hc_weights_backward_workspace(64, 4, 4096, 20) > need      # Sinkhorn scratch
+    f = lambda **k: L.hc_weights_backward(  # noqa: E731
+        k.get("H", P[0]), k.get("W", P[1]), k.get("ws", P[2]), k.get("scale", 0.01),
+        k.get("eps", 1e-6), k.get("it", 0), k.get("g", P[3]), k.get("din", None), k.get("dH", P[4]),
+        k.get("dW", P[5]), k.get("dws", P[6]), k.get("wk", P[7]), k.get("wkb", need),
+        k.get("T", 64), k.get("n", 4), k.get("d", 4096), k.get("dt", BF16), None)
+    assert f(T=0) == OK and f(T=0, dH=None) == OK
+    assert f(dt=FP8) == DTYPE and f(dt=7) == DTYPE
+    assert f(n=0) == SHAPE and f(d=100) == SHAPE
+    assert f(eps=0.0) == ARG and f(scale=float("inf")) == ARG and f(it=-1) == ARG
+    assert f(T=-1) == ARG and f(wkb=need - 1) == ARG
+    assert f(dW=None) == NULL and f(wk=None) == NULL and f(g=None) == NULL
+    assert f(dH=P[4] + 8) == ALIGN and f(wk=P[7] + 4) == ALIGN and f(dws=P[6] + 2) == ALIGN
+    assert f(dH=P[0]) == ALIAS and f(dW=P[1] + 64) == ALIAS and f(wk=P[3]) == ALIAS
+    assert f(din=P[4] + 16) == ALIAS and f(dws=P[5] + 64) == ALIAS
+
+
+def test_sinkhorn_backward_validation(L):
+    need = L.hc_sinkhorn_backward_workspace(100, 20)
+    assert need == 100 * 20 * 64 and L.hc_sinkhorn_backward_workspace(100, 0) == 0
+    f = lambda **k: L.hc_sinkhorn_backward(  # noqa: E731
+        k.get("l", P[0]), k.get("g", P[1]), k.get("o", P[2]), k.get("it", 20), k.get("wk", P[3]),
+        k.get("wkb", need), k.get("T", 100), k.get("n", 4), None)
+    assert f(T=0) == OK
+    assert f(n=5) == SHAPE and f(it=-1) == ARG and f(T=-2) == ARG and f(wkb=need - 4) == ARG
+    assert f(l=None) == NULL and f(wk=None) == NULL
+    assert f(o=P[0] + 4) == ALIAS and f(wk=P[1]) == ALIAS and f(o=P[2] + 2) == ALIGN

@@ -1,0 +1,134 @@
+"""GPU parity of the gradients of the per-token weight producer (tanh and
+mHC modes) and of the Sinkhorn step against the oracle, through the C ABI.
+
+dH is a storage output (storage tolerance); dW, dw_static and dlogits are
+fp32 sums of products with mixed signs, held to 1e-4 of their RMS like the
+other gradient records."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import check, dev, host, need_gpu, rel_err
+from hyper_connections_amd import hc
+from hyper_connections_amd.workloads import f32_to_bf16_bits, identity_record, make_inputs, workload
+
+pytestmark = pytest.mark.gpu
+
+TOL_GRAD = 1e-4
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def storage(x, dt):
+    return f32_to_bf16_bits(x) if dt == "bf16" else x.astype(np.float32)
+
+
+def grad_check(got, ref, what):
+    e = rel_err(np.asarray(got, np.float64), np.asarray(ref, np.float64))
+    assert e <= TOL_GRAD, f"{what}: {e:.3g} > {TOL_GRAD}"
+
+
+def case(rng, dt, T, n, d, wsd=0.05):
+    K = 2 * n + n * n
+    H = storage(rng.standard_normal((T, n, d)).astype(np.float32), dt)
+    W = storage((wsd * rng.standard_normal((K, d))).astype(np.float32), dt)
+    ws = (identity_record(n) + 0.1 * rng.standard_normal(K)).astype(np.float32)
+    dw = rng.standard_normal((T, K)).astype(np.float32)
+    return H, W, ws, dw
+
+
+# d: a single column group, ragged groups, the workload width; T: one token,
+# partial tiles, several dW splits
+@pytest.mark.parametrize("dt,d", [("bf16", 8), ("bf16", 264), ("bf16", 4096), ("f32", 4),
+                                  ("f32", 132), ("f32", 1024)])
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("iters", [0, 5])
+def test_weights_backward_parity(dt, d, n, iters):
+    rng = np.random.default_rng(d * 7 + n * 3 + iters)
+    T = 37
+    H, W, ws, dw = case(rng, dt, T, n, d)
+    scale = 0.5
+    dH, dW, dws = hc.weights_backward(dev(H), dev(W), dev(ws), scale, dev(dw), 1e-6, iters)
+    rdH, rdW, rdws = oracle.weights_backward(H, W, ws.astype(np.float64), scale,
+                                             dw.astype(np.float64), 1e-6, iters)
+    check(host(dH), rdH, f"dH n={n} d={d} {dt} iters={iters}")
+    grad_check(host(dW), rdW, f"dW n={n} d={d} {dt} iters={iters}")
+    grad_check(host(dws)[None], rdws[None], f"dw_static n={n} d={d} iters={iters}")
+
+
+@pytest.mark.parametrize("T", [1, 3, 17, 600, 1100])
+def test_weights_backward_token_counts(T):
+    n, d = 4, 512
+    rng = np.random.default_rng(T + 5)
+    H, W, ws, dw = case(rng, "bf16", T, n, d)
+    dH, dW, dws = hc.weights_backward(dev(H), dev(W), dev(ws), 0.01, dev(dw))
+    rdH, rdW, rdws = oracle.weights_backward(H, W, ws.astype(np.float64), 0.01,
+                                             dw.astype(np.float64))
+    check(host(dH), rdH, f"dH T={T}")
+    grad_check(host(dW), rdW, f"dW T={T}")
+    grad_check(host(dws)[None], rdws[None], f"dws T={T}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_weights_backward_accumulates(dt):
+    """dH = dH_in + this path, also in place."""
+    n, d, T = 4, 1024, 21
+    rng = np.random.default_rng(31)
+    H, W, ws, dw = case(rng, dt, T, n, d)
+    G = storage(rng.standard_normal((T, n, d)).astype(np.float32), dt)
+    a, _, _ = hc.weights_backward(dev(H), dev(W), dev(ws), 0.3, dev(dw), dH_in=dev(G))
+    acc = dev(G)
+    b, _, _ = hc.weights_backward(dev(H), dev(W), dev(ws), 0.3, dev(dw), dH_in=acc, out=acc)
+    assert np.array_equal(host(a), host(b))
+    rdH, _, _ = oracle.weights_backward(H, W, ws.astype(np.float64), 0.3, dw.astype(np.float64))
+    check(host(a), rdH + oracle.widen(G), "dH + dH_in", one_ulp=False)
+
+
+def test_weights_backward_deterministic():
+    n, d, T = 4, 2048, 700
+    rng = np.random.default_rng(8)
+    H, W, ws, dw = case(rng, "bf16", T, n, d)
+    runs = [[host(x) for x in hc.weights_backward(dev(H), dev(W), dev(ws), 0.01, dev(dw), 1e-6, 3)]
+            for _ in range(3)]
+    for r in runs[1:]:
+        assert all(np.array_equal(a, b) for a, b in zip(runs[0], r))
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("iters", [0, 1, 20])
+def test_sinkhorn_backward_parity(n, iters):
+    rng = np.random.default_rng(n * 100 + iters)
+    T, K = 1000, 2 * n + n * n
+    lg = rng.standard_normal((T, K)).astype(np.float32)
+    dw = rng.standard_normal((T, K)).astype(np.float32)
+    got = host(hc.sinkhorn_backward(dev(lg), dev(dw), n, iters))
+    ref = oracle.sinkhorn_backward(lg.astype(np.float64), dw.astype(np.float64), n, iters)
+    grad_check(got, ref, f"dlogits n={n} iters={iters}")
+
+
+def test_dynamic_workload_backward_full_size():
+    """T=16384, n=4, d=4096 bf16 (the dynamic workload): dH on 64 sampled
+    tokens against the oracle; dW and dw_static of the first 1024 tokens (a
+    separate call, the same kernels) against the oracle."""
+    wl = workload("dynamic-bf16")
+    inp = make_inputs(wl)
+    rng = np.random.default_rng(41)
+    dw = (rng.standard_normal((wl.T, wl.K)) * 0.1).astype(np.float32)
+    Hd, Wd, wsd = dev(inp["H"]), dev(inp["W"]), dev(inp["w_static"])
+    dH, dW, dws = hc.weights_backward(Hd, Wd, wsd, wl.scale, dev(dw), wl.eps)
+    torch.cuda.synchronize()
+    idx = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 64, replace=False)]))
+    sub = make_inputs(wl, tokens=idx)
+    rdH, _, _ = oracle.weights_backward(sub["H"], inp["W"], inp["w_static"].astype(np.float64),
+                                        wl.scale, dw[idx].astype(np.float64), wl.eps)
+    check(host(dH[torch.from_numpy(idx).cuda()]), rdH, "dynamic dH (sampled)")
+    m = 1024
+    _, dW1, dws1 = hc.weights_backward(Hd[:m].contiguous(), Wd, wsd, wl.scale, dev(dw[:m]), wl.eps)
+    _, rdW, rdws = oracle.weights_backward(inp["H"][:m], inp["W"], inp["w_static"].astype(np.float64),
+                                           wl.scale, dw[:m].astype(np.float64), wl.eps)
+    grad_check(host(dW1), rdW, "dynamic dW (1024 tokens)")
+    grad_check(host(dws1)[None], rdws[None], "dynamic dw_static (1024 tokens)")
