@@ -217,8 +217,9 @@ def summarize_counters(fetch_csv: str, write_csv: str, kernel: str, workload: st
            "post_mix": tr.post_bytes(wl.n, wl.d, wl.elem_bytes, per_tok),
            "weights": tr.weights_bytes(wl.n, wl.d, wl.elem_bytes),
            "post_pre_mix": tr.post_pre_bytes(wl.n, wl.d, wl.elem_bytes),
-           "post_mix_backward": tr.post_bwd_bytes(wl.n, wl.d, wl.elem_bytes, per_tok),
-           "pre_mix_backward": tr.pre_bwd_bytes(wl.n, wl.d, wl.elem_bytes, per_tok)}[kernel] * wl.T
+           "post_mix_backward": tr.post_bwd_bytes(wl.n, wl.d, wl.elem_bytes),
+           "pre_mix_backward": tr.pre_bwd_bytes(wl.n, wl.d, wl.elem_bytes, True),
+           "weights_backward": tr.weights_bwd_bytes(wl.n, wl.d, wl.elem_bytes)}[kernel] * wl.T
     rec = {"kernel": kernel, "workload": workload, "source_sha": source_sha(kernel),
            "dispatches": {"FETCH_SIZE": len(fk), "WRITE_SIZE": len(wk)},
            "fetch_kib_per_dispatch": round(fetch_kib, 3), "write_kib_per_dispatch": round(write_kib, 3),
@@ -261,8 +262,9 @@ def main():
                     help="fuse each write-back with the next read-mix (chain: every layer; "
                          "static: one step is one fused layer boundary)")
     ap.add_argument("--backward", action="store_true",
-                    help="static workload: time the layer's gradients (post backward, pre "
-                         "backward accumulating into the same dH, shared-weight sums)")
+                    help="time the layer's gradients: post backward, pre backward accumulating "
+                         "into the same dH, shared-weight sums (static workloads); per-token "
+                         "records and the weight producer's gradient as well (dynamic)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph (torch.cuda.CUDAGraph) and time replays")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -360,11 +362,12 @@ def main():
         "block_tanh": 2 * d * s * T,
         "post_mix_backward": traffic.post_bwd_bytes(n, d, s) * T,
         "pre_mix_backward": traffic.pre_bwd_bytes(n, d, s, True) * T,
+        "weights_backward": traffic.weights_bwd_bytes(n, d, s) * T,
     }
 
     if args.backward:
-        if wl.kind != "static":
-            raise SystemExit("--backward is defined for the static workloads")
+        if wl.kind not in ("static", "dynamic") or wl.dtype == "fp8":
+            raise SystemExit("--backward is defined for the static and dynamic bf16/fp32 workloads")
         rng = np.random.default_rng(wl.seed + 1)
         G0 = dev(workloads.to_storage(rng.standard_normal((T, n, d), dtype=np.float32), wl.dtype))
         du0 = dev(workloads.to_storage(rng.standard_normal((T, d), dtype=np.float32), wl.dtype))
@@ -378,16 +381,37 @@ def main():
             b["dg"] = torch.empty(d, dtype=torch.float32, device="cuda")
             b["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
 
+        if wl.kind == "dynamic":
+            # per-token records from the forward (untimed), gradient records per token
+            wws_bytes = int(hc.lib().hc_weights_backward_workspace(T, n, d, 0))
+            for b in bufs:
+                hc.weights(b["H"], Wp, ws, wl.scale, wl.eps, 0, out=b["w"])
+                b["dwp"] = torch.empty((T, K), dtype=torch.float32, device="cuda")
+                b["dwq"] = torch.empty((T, K), dtype=torch.float32, device="cuda")
+                b["dW"] = torch.empty((K, d), dtype=torch.float32, device="cuda")
+                b["dws"] = torch.empty(K, dtype=torch.float32, device="cuda")
+                b["wws"] = torch.empty(wws_bytes, dtype=torch.uint8, device="cuda")
+            torch.cuda.synchronize()
+        rec = (lambda b: b["w"]) if wl.kind == "dynamic" else (lambda b: w_static)
+
         def post_bwd(b):
             # dH lands in b["O"]; the pre backward then accumulates into it
-            hc.post_mix_backward(b["G"], b["H"], b["F"], w_static, dH=b["O"], dF=b["dF"],
+            hc.post_mix_backward(b["G"], b["H"], b["F"], rec(b), dH=b["O"], dF=b["dF"],
                                  dw=b["dwp"], workspace=b["ws"])
 
         def pre_bwd(b):
-            hc.pre_mix_backward(b["du"], b["H"], w_static, gamma, wl.eps, dH_in=b["O"],
+            hc.pre_mix_backward(b["du"], b["H"], rec(b), gamma, wl.eps, dH_in=b["O"],
                                 out=b["O"], dw=b["dwq"], dgamma=b["dg"], workspace=b["ws"])
 
+        def weights_bwd(b):
+            # the records' gradient from post and pre, through the weight producer
+            hc.weights_backward(b["H"], Wp, ws, wl.scale, b["dwp"], wl.eps, 0, dH_in=b["O"],
+                                out=b["O"], dW=b["dW"], dw_static=b["dws"], workspace=b["wws"],
+                                dw2=b["dwq"])
+
         ops = [("post_mix_backward", post_bwd), ("pre_mix_backward", pre_bwd)]
+        if wl.kind == "dynamic":
+            ops.append(("weights_backward", weights_bwd))
     # the kernels of one step, in order: (name, launch on buffer set b)
     elif wl.kind == "static" and args.fused:
         # one layer boundary: write-back of this layer fused with the next read-mix

@@ -267,7 +267,8 @@ int64_t hc_weights_backward_workspace(int64_t T, int32_t n, int32_t d, int32_t s
 }
 
 hc_status hc_weights_backward(const void* H, const void* W, const float* w_static, float scale,
-                              float eps, int32_t sinkhorn_iters, const float* dw, const void* dH_in,
+                              float eps, int32_t sinkhorn_iters, const float* dw, const float* dw2,
+                              const void* dH_in,
                               void* dH, float* dW, float* dw_static, void* workspace,
                               int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
                               void* stream) {
@@ -282,14 +283,15 @@ hc_status hc_weights_backward(const void* H, const void* W, const float* w_stati
     if (workspace_bytes < need) return HC_ERR_ARG;
     if (misaligned(H, 16) || misaligned(W, 16) || misaligned(dH, 16) || misaligned(dH_in, 16) ||
         misaligned(workspace, 16) || misaligned(w_static, 4) || misaligned(dw, 4) ||
-        misaligned(dW, 4) || misaligned(dw_static, 4))
+        misaligned(dW, 4) || misaligned(dw_static, 4) || misaligned(dw2, 4))
         return HC_ERR_ALIGN;
     const int K = record_len(n);
     const int64_t s = elem_bytes(dt);
     const Span sH{H, T * n * d * s}, sW{W, int64_t(K) * d * s}, sS{w_static, int64_t(K) * 4},
-        sg{dw, T * K * 4}, sin{dH_in, dH_in ? T * n * d * s : 0}, sdH{dH, T * n * d * s},
-        sdW{dW, int64_t(K) * d * 4}, sds{dw_static, int64_t(K) * 4}, sws{workspace, need};
-    const Span ins[] = {sH, sW, sS, sg};
+        sg{dw, T * K * 4}, sg2{dw2, dw2 ? T * K * 4 : 0}, sin{dH_in, dH_in ? T * n * d * s : 0},
+        sdH{dH, T * n * d * s}, sdW{dW, int64_t(K) * d * 4}, sds{dw_static, int64_t(K) * 4},
+        sws{workspace, need};
+    const Span ins[] = {sH, sW, sS, sg, sg2};
     for (const Span& o : {sdH, sdW, sds, sws})
         for (const Span& i : ins)
             if (overlap(o, i)) return HC_ERR_ALIAS;
@@ -299,7 +301,7 @@ hc_status hc_weights_backward(const void* H, const void* W, const float* w_stati
     if (overlap(sdH, sdW) || overlap(sdH, sds) || overlap(sdH, sws) || overlap(sdW, sds) ||
         overlap(sdW, sws) || overlap(sds, sws))
         return HC_ERR_ALIAS;
-    return from_hip(hc::launch_weights_backward(H, W, w_static, scale, eps, sinkhorn_iters, dw,
+    return from_hip(hc::launch_weights_backward(H, W, w_static, scale, eps, sinkhorn_iters, dw, dw2,
                                                 dH_in, dH, dW, dw_static, workspace, T, n, d, dt,
                                                 static_cast<hipStream_t>(stream)));
 }

@@ -68,7 +68,8 @@ hipError_t launch_sum_rows(const float* in, int64_t rows, int cols, float* tmp, 
 int64_t weights_backward_workspace_bytes(int64_t T, int n, int d, int iters);
 int64_t sinkhorn_backward_workspace_bytes(int64_t T, int iters);
 hipError_t launch_weights_backward(const void* H, const void* W, const float* w_static, float scale,
-                                   float eps, int iters, const float* dw, const void* dH_in,
+                                   float eps, int iters, const float* dw, const float* dw2,
+                                   const void* dH_in,
                                    void* dH, float* dW, float* dws, void* work, int64_t T, int n,
                                    int d, int dt, hipStream_t s);
 hipError_t launch_sinkhorn_backward(const float* logits, const float* dw, float* dlogits, int iters,

@@ -147,13 +147,15 @@ __global__ __launch_bounds__(256) void sinkhorn_bwd_kernel(const float* __restri
 
 // ----------------------------------------------------- per-token coefficients
 
-// From P [T][N][K], r [T][N] (the forward projection pass) and dw [T][K]:
+// From P [T][N][K], r [T][N] (the forward projection pass) and dw [T][K]
+// (plus dw2 when given: the records' gradient from a second consumer):
 // dz [T][K], dl [T][K] (the gradient at the logits / records that
 // w_static receives) and ab [T][2][N] = (a_i, b_i).  One thread per token.
 template <int N>
 __global__ __launch_bounds__(256) void wgrad_coef_kernel(
     const float* __restrict__ P, const float* __restrict__ r, const float* __restrict__ dw,
-    const float* __restrict__ w_static, float scale, int iters, float* __restrict__ scr,
+    const float* __restrict__ dw2, const float* __restrict__ w_static, float scale, int iters,
+    float* __restrict__ scr,
     float* __restrict__ dz, float* __restrict__ dl, float* __restrict__ ab, int64_t T, int d) {
     constexpr int K = 2 * N + N * N;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < T;
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(256) void wgrad_coef_kernel(
 #pragma unroll
             for (int i = 1; i < N; ++i) v = fmaf(ri[i], p[i * K + c], v);
             z[c] = v / (float)N;
-            g[c] = dw[t * K + c];
+            g[c] = dw2 ? dw[t * K + c] + dw2[t * K + c] : dw[t * K + c];
         }
         if (iters == 0) {
 #pragma unroll
@@ -335,12 +337,12 @@ __global__ __launch_bounds__(256) void wgrad_stream_kernel(
 }
 
 template <int N>
-hipError_t coef_go(const float* P, const float* r, const float* dw, const float* ws, float scale,
-                   int iters, float* scr, float* dz, float* dl, float* ab, int64_t T, int d,
-                   hipStream_t s) {
+hipError_t coef_go(const float* P, const float* r, const float* dw, const float* dw2, const float* ws,
+                   float scale, int iters, float* scr, float* dz, float* dl, float* ab, int64_t T,
+                   int d, hipStream_t s) {
     const int64_t blocks = (T + 255) / 256;
     return launch(wgrad_coef_kernel<N>, dim3((unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid)),
-                  dim3(256), 0, s, P, r, dw, ws, scale, iters, scr, dz, dl, ab, T, d);
+                  dim3(256), 0, s, P, r, dw, dw2, ws, scale, iters, scr, dz, dl, ab, T, d);
 }
 
 template <int N, typename S>
@@ -425,7 +427,8 @@ hipError_t launch_sinkhorn_backward(const float* logits, const float* dw, float*
 }
 
 hipError_t launch_weights_backward(const void* H, const void* W, const float* w_static, float scale,
-                                   float eps, int iters, const float* dw, const void* dH_in,
+                                   float eps, int iters, const float* dw, const float* dw2,
+                                   const void* dH_in,
                                    void* dH, float* dW, float* dws, void* work, int64_t T, int n,
                                    int d, int dt, hipStream_t s) {
     const WgSpace sp = wg_space(T, n, d, iters);
@@ -436,10 +439,10 @@ hipError_t launch_weights_backward(const void* H, const void* W, const float* w_
     if (e != hipSuccess) return e;
     // (2) per-token coefficients
     switch (n) {
-        case 1: e = coef_go<1>(ws + sp.P, ws + sp.r, dw, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
-        case 2: e = coef_go<2>(ws + sp.P, ws + sp.r, dw, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
-        case 3: e = coef_go<3>(ws + sp.P, ws + sp.r, dw, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
-        case 4: e = coef_go<4>(ws + sp.P, ws + sp.r, dw, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
+        case 1: e = coef_go<1>(ws + sp.P, ws + sp.r, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
+        case 2: e = coef_go<2>(ws + sp.P, ws + sp.r, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
+        case 3: e = coef_go<3>(ws + sp.P, ws + sp.r, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
+        case 4: e = coef_go<4>(ws + sp.P, ws + sp.r, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;

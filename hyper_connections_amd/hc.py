@@ -49,8 +49,8 @@ _SIGS = {
     "hc_pre_mix_backward": [_vp, _vp, _fp, _i64, _fp, _f32, _vp, _vp, _fp, _fp, _vp, _i64, _i64,
                             _i32, _i32, _i32, _vp],
     "hc_sum_records": [_fp, _i64, _i32, _fp, _vp],
-    "hc_weights_backward": [_vp, _vp, _fp, _f32, _f32, _i32, _fp, _vp, _vp, _fp, _fp, _vp, _i64,
-                            _i64, _i32, _i32, _i32, _vp],
+    "hc_weights_backward": [_vp, _vp, _fp, _f32, _f32, _i32, _fp, _fp, _vp, _vp, _fp, _fp, _vp,
+                            _i64, _i64, _i32, _i32, _i32, _vp],
     "hc_sinkhorn_backward": [_fp, _fp, _fp, _i32, _vp, _i64, _i64, _i32, _vp],
 }
 EXPORTS = tuple(_SIGS) + ("hc_status_str", "hc_abi_version", "hc_backward_workspace",
@@ -339,9 +339,11 @@ def sum_records(rec, out=None, stream=None):
 
 
 def weights_backward(H, W, w_static, scale: float, dw, eps: float = 1e-6, sinkhorn_iters: int = 0,
-                     dH_in=None, out=None, dW=None, dw_static=None, workspace=None, stream=None):
+                     dH_in=None, out=None, dW=None, dw_static=None, workspace=None, dw2=None,
+                     stream=None):
     """Gradients of weights: returns (dH, dW, dw_static).  dw is dL/d(records)
-    (T, K) float32; dH includes dH_in when given (``out=dH_in`` accumulates in
+    (T, K) float32 (plus dw2 when given, e.g. the pre and post gradients of the
+    same records); dH includes dH_in when given (``out=dH_in`` accumulates in
     place); dW (K, d) and dw_static (K,) are float32."""
     T, n, d, K = _H(H)
     _dev(W, "W")
@@ -353,6 +355,10 @@ def weights_backward(H, W, w_static, scale: float, dw, eps: float = 1e-6, sinkho
         raise ValueError(f"w_static must be float32 of shape ({K},)")
     if dw.dtype != torch.float32 or tuple(dw.shape) != (T, K):
         raise ValueError(f"dw must be float32 of shape ({T}, {K})")
+    if dw2 is not None:
+        _dev(dw2, "dw2")
+        if dw2.dtype != torch.float32 or tuple(dw2.shape) != (T, K):
+            raise ValueError(f"dw2 must be float32 of shape ({T}, {K})")
     if dH_in is not None:
         _dev(dH_in, "dH_in")
         if dH_in.dtype != H.dtype or dH_in.shape != H.shape:
@@ -373,6 +379,7 @@ def weights_backward(H, W, w_static, scale: float, dw, eps: float = 1e-6, sinkho
     _dev(workspace, "workspace")
     _call("hc_weights_backward", H.data_ptr(), W.data_ptr(), w_static.data_ptr(), float(scale),
           float(eps), int(sinkhorn_iters), dw.data_ptr(),
+          dw2.data_ptr() if dw2 is not None else None,
           dH_in.data_ptr() if dH_in is not None else None, dH.data_ptr(), dW.data_ptr(),
           dws.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
           T, n, d, _dt(H), _stream(stream))

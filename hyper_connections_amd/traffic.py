@@ -63,3 +63,12 @@ def pre_bwd_bytes(n: int, d: int, s: int, accumulate: bool = True) -> int:
     accumulated), write dH and one gradient record (the dgamma partials,
     d floats per group of tokens, are not counted)."""
     return (2 * n + 1 + (n if accumulate else 0)) * d * s + record_bytes(n)
+
+
+def weights_bwd_bytes(n: int, d: int, s: int) -> int:
+    """Gradient of the per-token weights: read H, read the incoming dH and
+    write dH once each, plus two gradient records read (from pre and post).
+    The projection pass that recomputes W H_i re-reads H as well; that pass is
+    an implementation choice (the forward could keep P_i) and is not
+    counted."""
+    return 3 * n * d * s + 2 * record_bytes(n)

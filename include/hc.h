@@ -205,13 +205,16 @@ int64_t hc_weights_backward_workspace(int64_t T, int32_t n, int32_t d, int32_t s
  *   dW = sum_t dz hbar^T   (fp32, [K][d], summed in a fixed order)
  *   dH_i = dH_in_i + (r_i dhbar - r_i^3 (H_i . dhbar) H_i / d) / n,  dhbar = W^T dz
  *   H [T][n][d] dt, W [K][d] dt, w_static [K], scale, eps, sinkhorn_iters as in
- *     hc_weights; dw [T][K] fp32 (records of stride K)
+ *     hc_weights; dw [T][K] fp32 (records of stride K); dw2 [T][K] fp32 or NULL,
+ *     added to dw (the records feed both pre and post, whose backward calls
+ *     each return a per-token gradient record)
  *   dH_in [T][n][d] dt or NULL; dH [T][n][d] dt (dH == dH_in allowed)
  *   dW [K][d] fp32, dw_static [K] fp32 outputs
  *   workspace >= hc_weights_backward_workspace(T, n, d, sinkhorn_iters), 16-byte
  *     aligned.  fp32 and bf16 storage only (HC_ERR_DTYPE for HC_FP8). */
 hc_status hc_weights_backward(const void* H, const void* W, const float* w_static, float scale,
-                              float eps, int32_t sinkhorn_iters, const float* dw, const void* dH_in,
+                              float eps, int32_t sinkhorn_iters, const float* dw, const float* dw2,
+                              const void* dH_in,
                               void* dH, float* dW, float* dw_static, void* workspace,
                               int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
                               void* stream);

@@ -185,7 +185,8 @@ def test_weights_backward_validation(L):
     assert L.hc_weights_backward_workspace(64, 4, 4096, 20) > need      # Sinkhorn scratch
     f = lambda **k: L.hc_weights_backward(  # noqa: E731
         k.get("H", P[0]), k.get("W", P[1]), k.get("ws", P[2]), k.get("scale", 0.01),
-        k.get("eps", 1e-6), k.get("it", 0), k.get("g", P[3]), k.get("din", None), k.get("dH", P[4]),
+        k.get("eps", 1e-6), k.get("it", 0), k.get("g", P[3]), k.get("g2", None), k.get("din", None),
+        k.get("dH", P[4]),
         k.get("dW", P[5]), k.get("dws", P[6]), k.get("wk", P[7]), k.get("wkb", need),
         k.get("T", 64), k.get("n", 4), k.get("d", 4096), k.get("dt", BF16), None)
     assert f(T=0) == OK and f(T=0, dH=None) == OK
@@ -197,6 +198,7 @@ def test_weights_backward_validation(L):
     assert f(dH=P[4] + 8) == ALIGN and f(wk=P[7] + 4) == ALIGN and f(dws=P[6] + 2) == ALIGN
     assert f(dH=P[0]) == ALIAS and f(dW=P[1] + 64) == ALIAS and f(wk=P[3]) == ALIAS
     assert f(din=P[4] + 16) == ALIAS and f(dws=P[5] + 64) == ALIAS
+    assert f(g2=P[3] + 2) == ALIGN and f(g2=P[4]) == ALIAS             # dw2 under dH
 
 
 def test_sinkhorn_backward_validation(L):

@@ -132,3 +132,16 @@ def test_dynamic_workload_backward_full_size():
                                            wl.scale, dw[:m].astype(np.float64), wl.eps)
     grad_check(host(dW1), rdW, "dynamic dW (1024 tokens)")
     grad_check(host(dws1)[None], rdws[None], "dynamic dw_static (1024 tokens)")
+
+
+def test_weights_backward_two_gradient_records():
+    """dw + dw2 (the gradients from pre and post) give the same as their sum
+    passed as one record."""
+    n, d, T = 4, 1024, 50
+    rng = np.random.default_rng(12)
+    H, W, ws, dw = case(rng, "bf16", T, n, d)
+    dw2 = rng.standard_normal(dw.shape).astype(np.float32)
+    a = hc.weights_backward(dev(H), dev(W), dev(ws), 0.2, dev(dw), dw2=dev(dw2))
+    b = hc.weights_backward(dev(H), dev(W), dev(ws), 0.2, dev(dw + dw2))
+    for x, y in zip(a, b):
+        assert np.array_equal(host(x), host(y))
