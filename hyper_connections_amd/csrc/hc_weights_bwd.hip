@@ -18,6 +18,8 @@
 // into dz, a_i, b_i (and dl); (3) one streaming pass over H computes dH and
 // partial sums of dW on the matrix cores; (4) fixed-order sums of the
 // partials.  Everything is deterministic.
+#include <type_traits>
+
 #include "hc_device.h"
 #include "hc_launch.h"
 
@@ -336,6 +338,191 @@ __global__ __launch_bounds__(256) void wgrad_stream_kernel(
     }
 }
 
+// bf16 storage: both contractions on the matrix cores, with dz (and hbar)
+// split into a bf16 pair hi + lo (hi = dz rounded to bf16, lo = the rest
+// rounded again), so a product keeps about 16 mantissa bits (the lo x lo term
+// is below fp32 resolution of the sum and dropped; W is exact in bf16).
+// Each wave takes 16 tokens per step; lane l = 16 g + cl works on tokens
+// 4 g + j (j = 0..3) of the step, columns 8 (slice + cl) .. + 7.
+//   dhbar: v_mfma_f32_16x16x32_bf16 with A[m = token][k = c] = dz and
+//     B[k = c][n = cl] = W[c][8 (slice + n) + q] for tile q = 0..7, so tile q
+//     lands as dhbar[token 4 g + j][column 8 (slice + cl) + q] in element j
+//     of lane l: exactly the lane's own tokens and columns.
+//   dW: v_mfma_f32_16x16x16_bf16 with A[m = c][k = token] = dz and
+//     B[k = token][n = cl] = hbar[token][8 (slice + n) + q]: the lane holds
+//     B for k = 4 g + j, its own tokens.
+// Per element: hbar = sum_i a_i H_i (a_i = r_i / n), dH_i = dH_in_i + a_i dhbar + b_i H_i.
+// Loads are unconditional from clamped (valid) addresses, and values of tokens
+// past the range are zeroed after the fact: no branches in the loop.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+struct Split2 { uint32_t hi, lo; };
+// (x0, x1) -> hi and lo bf16 pairs, element 0 in the low half.
+__device__ __forceinline__ Split2 split_bf16x2(float x0, float x1) {
+    const uint32_t h = pack_bf16x2(x0, x1);
+    return {h, pack_bf16x2(x0 - lo_bf16(h), x1 - hi_bf16(h))};
+}
+
+template <int N>
+__global__ __launch_bounds__(256) void wgrad_mfma_kernel(
+    const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, const float* __restrict__ dz,
+    const float* __restrict__ ab, const float* __restrict__ r, const uint8_t* dH_in,
+    uint8_t* dH, float* __restrict__ part, int64_t T, int d, int64_t tok_per_split) {
+    constexpr int K = 2 * N + N * N;                 // <= 24
+    constexpr int MT = (K + 15) / 16;                // 16-row tiles of dW
+    // B operands of the dhbar product: wl[(q * 16 + cl) * 32 + c] = W[c][8 (slice + cl) + q],
+    // zero for c >= K and for columns past d
+    __shared__ __attribute__((aligned(16))) uint16_t wl[8 * 16 * 32];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, cl = lane & 15;
+    const int nvec = d / 8;
+    const int cv = blockIdx.x * 16 + cl;
+    const bool col_ok = cv < nvec;
+    const int64_t row_bytes = (int64_t)d * 2;
+
+    for (int p = threadIdx.x; p < 32 * 16; p += 256) {
+        const int c = p / 16, l = p % 16, v = blockIdx.x * 16 + l;
+        const uint4 x = (c < K && v < nvec) ? ld16(W + ((int64_t)c * d + (int64_t)v * 8) * 2)
+                                            : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            wl[(q * 16 + l) * 32 + c] = (uint16_t)(word(x, q / 2) >> (16 * (q & 1)));
+    }
+    __syncthreads();
+
+    f32x4 acc[MT][8];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[m][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t t_begin = (int64_t)blockIdx.y * tok_per_split;
+    const int64_t t_end = t_begin + tok_per_split < T ? t_begin + tok_per_split : T;
+    for (int64_t t0 = t_begin + 16 * wave; t0 < t_end; t0 += 64) {
+        // dhbar for the 16 tokens of the step
+        f32x4 dhb[8];
+        {
+            const int64_t t = t0 + cl;
+            const bool ok = t < t_end;
+            const int64_t tt = ok ? t : t_begin;
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int c = 8 * g + i;
+                const float v = dz[tt * K + (c < K ? c : K - 1)];
+                x[i] = (ok && c < K) ? v : 0.0f;
+            }
+            uint32_t ah[4], al[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const Split2 s = split_bf16x2(x[2 * i], x[2 * i + 1]);
+                ah[i] = s.hi;
+                al[i] = s.lo;
+            }
+            const bf16x8_t Ah = __builtin_bit_cast(bf16x8_t, make_uint4(ah[0], ah[1], ah[2], ah[3]));
+            const bf16x8_t Al = __builtin_bit_cast(bf16x8_t, make_uint4(al[0], al[1], al[2], al[3]));
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const bf16x8_t B =
+                    __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(wl + (q * 16 + cl) * 32 + 8 * g));
+                dhb[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, B, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                dhb[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, B, dhb[q], 0, 0, 0);
+            }
+        }
+        // the lane's 4 tokens: dH, and hbar for the dW product
+        float hb[4][8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t t = t0 + 4 * g + j;
+            const bool ok = t < t_end;
+            const bool live = ok && col_ok;
+            const int64_t tt = ok ? t : t_begin;
+            const int64_t r0 = tt * N * row_bytes + (int64_t)(col_ok ? cv : 0) * 16;
+            uint4 rh[N], rin[N];
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                rh[i] = ld16_stream(H + r0 + i * row_bytes);
+                if (dH_in) rin[i] = ld16_stream(dH_in + r0 + i * row_bytes);
+            }
+            float ai[N], bi[N];
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                ai[i] = ab[tt * 2 * N + i];
+                bi[i] = ab[tt * 2 * N + N + i];
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) hb[j][q] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                float h[8], o[8];
+                unpack<bf16_t>(rh[i], h);
+                if (dH_in) {
+                    unpack<bf16_t>(rin[i], o);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) o[q] = 0.0f;
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    hb[j][q] = fmaf(ai[i], h[q], hb[j][q]);
+                    o[q] = fmaf(bi[i], h[q], fmaf(ai[i], dhb[q][j], o[q]));
+                }
+                if (live) st16_stream(dH + r0 + i * row_bytes, pack<bf16_t>(o));
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) hb[j][q] = ok ? hb[j][q] : 0.0f;
+        }
+        // dW += dz^T hbar over the 16 tokens
+        i16x4_t Ah[MT], Al[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int c = 16 * m + cl;
+            float x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t t = t0 + 4 * g + j;
+                const float v = dz[(t < t_end ? t : t_begin) * K + (c < K ? c : K - 1)];
+                x[j] = (t < t_end && c < K) ? v : 0.0f;
+            }
+            const Split2 s0 = split_bf16x2(x[0], x[1]), s1 = split_bf16x2(x[2], x[3]);
+            Ah[m] = __builtin_bit_cast(i16x4_t, make_uint2(s0.hi, s1.hi));
+            Al[m] = __builtin_bit_cast(i16x4_t, make_uint2(s0.lo, s1.lo));
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const Split2 s0 = split_bf16x2(hb[0][q], hb[1][q]), s1 = split_bf16x2(hb[2][q], hb[3][q]);
+            const i16x4_t Bh = __builtin_bit_cast(i16x4_t, make_uint2(s0.hi, s1.hi));
+            const i16x4_t Bl = __builtin_bit_cast(i16x4_t, make_uint2(s0.lo, s1.lo));
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                acc[m][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Ah[m], Bh, acc[m][q], 0, 0, 0);
+                acc[m][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Ah[m], Bl, acc[m][q], 0, 0, 0);
+                acc[m][q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(Al[m], Bh, acc[m][q], 0, 0, 0);
+            }
+        }
+    }
+    // this wave's partial: element j of tile (m, q) is dW[c = 16 m + 4 g + j][8 cv + q]
+    float* out = part + ((int64_t)blockIdx.y * 4 + wave) * K * (int64_t)d;
+    if (col_ok) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = 16 * m + 4 * g + j;
+                if (c < K) {
+                    float v[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) v[q] = acc[m][q][j];
+                    float* o = out + (int64_t)c * d + (int64_t)cv * 8;
+                    *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+                    *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+                }
+            }
+    }
+}
+
 template <int N>
 hipError_t coef_go(const float* P, const float* r, const float* dw, const float* dw2, const float* ws,
                    float scale, int iters, float* scr, float* dz, float* dl, float* ab, int64_t T,
@@ -351,7 +538,10 @@ hipError_t stream_go(const void* H, const void* W, const float* dz, const float*
                      int64_t tps, hipStream_t s) {
     const int nvec = d / Store<S>::kElems;
     const dim3 grid((unsigned)((nvec + 15) / 16), (unsigned)splits);
-    return launch(wgrad_stream_kernel<N, S>, grid, dim3(256), 0, s, static_cast<const uint8_t*>(H),
+    void (*kernel)(const uint8_t*, const uint8_t*, const float*, const float*, const float*,
+                   const uint8_t*, uint8_t*, float*, int64_t, int, int64_t) =
+        std::is_same<S, bf16_t>::value ? wgrad_mfma_kernel<N> : wgrad_stream_kernel<N, S>;
+    return launch(kernel, grid, dim3(256), 0, s, static_cast<const uint8_t*>(H),
                   static_cast<const uint8_t*>(W), dz, ab, r, static_cast<const uint8_t*>(dH_in),
                   static_cast<uint8_t*>(dH), part, T, d, tps);
 }
