@@ -342,18 +342,23 @@ __global__ __launch_bounds__(256) void wgrad_stream_kernel(
 // split into a bf16 pair hi + lo (hi = dz rounded to bf16, lo = the rest
 // rounded again), so a product keeps about 16 mantissa bits (the lo x lo term
 // is below fp32 resolution of the sum and dropped; W is exact in bf16).
-// Each wave takes 16 tokens per step; lane l = 16 g + cl works on tokens
-// 4 g + j (j = 0..3) of the step, columns 8 (slice + cl) .. + 7.
-//   dhbar: v_mfma_f32_16x16x32_bf16 with A[m = token][k = c] = dz and
-//     B[k = c][n = cl] = W[c][8 (slice + n) + q] for tile q = 0..7, so tile q
-//     lands as dhbar[token 4 g + j][column 8 (slice + cl) + q] in element j
-//     of lane l: exactly the lane's own tokens and columns.
-//   dW: v_mfma_f32_16x16x16_bf16 with A[m = c][k = token] = dz and
-//     B[k = token][n = cl] = hbar[token][8 (slice + n) + q]: the lane holds
-//     B for k = 4 g + j, its own tokens.
+// A wave takes 16 tokens per step; lane l = 16 g + cl works on tokens
+// g + 4 j (j = 0..3) of the step, columns 8 (slice + cl) .. + 7, so one load
+// instruction covers 4 neighbouring tokens x 256 contiguous bytes.
+//   dhbar: v_mfma_f32_16x16x32_bf16 with A[m][k = c] = dz of token
+//     sigma(m) = m / 4 + 4 (m % 4) and B[k = c][n = cl] = W[c][8 (slice + n) + q]
+//     for tile q = 0..7, so element j of tile q in lane l is
+//     dhbar[token g + 4 j][column 8 (slice + cl) + q]: the lane's own tokens
+//     and columns.
+//   dW: v_mfma_f32_16x16x16_bf16 with A[m = c][k] = dz and
+//     B[k][n = cl] = hbar[token][8 (slice + n) + q], k = 4 g + j standing for
+//     token g + 4 j, which the lane holds.
 // Per element: hbar = sum_i a_i H_i (a_i = r_i / n), dH_i = dH_in_i + a_i dhbar + b_i H_i.
-// Loads are unconditional from clamped (valid) addresses, and values of tokens
-// past the range are zeroed after the fact: no branches in the loop.
+// The 16-token steps are dealt round robin to the waves of the grid's rows,
+// so the tokens in flight across the chip stay close together; the loads of
+// a lane's next token are in flight while one is computed.  Loads are
+// unconditional from valid addresses (tokens past T read the step's first
+// token and are zeroed after the fact): no branches in the loop.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
@@ -364,11 +369,13 @@ __device__ __forceinline__ Split2 split_bf16x2(float x0, float x1) {
     return {h, pack_bf16x2(x0 - lo_bf16(h), x1 - hi_bf16(h))};
 }
 
-template <int N>
+template <int N, bool IN>
 __global__ __launch_bounds__(256) void wgrad_mfma_kernel(
     const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, const float* __restrict__ dz,
     const float* __restrict__ ab, const float* __restrict__ r, const uint8_t* dH_in,
     uint8_t* dH, float* __restrict__ part, int64_t T, int d, int64_t tok_per_split) {
+    (void)r;
+    (void)tok_per_split;
     constexpr int K = 2 * N + N * N;                 // <= 24
     constexpr int MT = (K + 15) / 16;                // 16-row tiles of dW
     // B operands of the dhbar product: wl[(q * 16 + cl) * 32 + c] = W[c][8 (slice + cl) + q],
@@ -381,6 +388,7 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(
     const int cv = blockIdx.x * 16 + cl;
     const bool col_ok = cv < nvec;
     const int64_t row_bytes = (int64_t)d * 2;
+    const int64_t col_off = (int64_t)(col_ok ? cv : 0) * 16;
 
     for (int p = threadIdx.x; p < 32 * 16; p += 256) {
         const int c = p / 16, l = p % 16, v = blockIdx.x * 16 + l;
@@ -398,15 +406,38 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[m][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int64_t t_begin = (int64_t)blockIdx.y * tok_per_split;
-    const int64_t t_end = t_begin + tok_per_split < T ? t_begin + tok_per_split : T;
-    for (int64_t t0 = t_begin + 16 * wave; t0 < t_end; t0 += 64) {
+    const int64_t nsteps = (T + 15) / 16, sstride = (int64_t)gridDim.y * 4;
+    for (int64_t st = (int64_t)blockIdx.y * 4 + wave; st < nsteps; st += sstride) {
+        const int64_t t0 = st * 16;
+        struct Tok { uint32_t h[N][4], din[N][4]; float a[N], b[N]; };
+        auto fetch = [&](int j, Tok& L) {
+            const int64_t t = t0 + g + 4 * j;
+            const int64_t r0 = (t < T ? t : t0) * N * row_bytes + col_off;
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(H + r0 + i * row_bytes));
+                L.h[i][0] = v.x; L.h[i][1] = v.y; L.h[i][2] = v.z; L.h[i][3] = v.w;
+                if constexpr (IN) {
+                    const u32x4 u =
+                        __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dH_in + r0 + i * row_bytes));
+                    L.din[i][0] = u.x; L.din[i][1] = u.y; L.din[i][2] = u.z; L.din[i][3] = u.w;
+                }
+            }
+            const float* abt = ab + (t < T ? t : t0) * 2 * N;
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                L.a[i] = abt[i];
+                L.b[i] = abt[N + i];
+            }
+        };
+        Tok L0, L1;
+        fetch(0, L0);
         // dhbar for the 16 tokens of the step
         f32x4 dhb[8];
         {
-            const int64_t t = t0 + cl;
-            const bool ok = t < t_end;
-            const int64_t tt = ok ? t : t_begin;
+            const int64_t t = t0 + (cl >> 2) + 4 * (cl & 3);
+            const bool ok = t < T;
+            const int64_t tt = ok ? t : t0;
             float x[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -435,44 +466,36 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(
         float hb[4][8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t t = t0 + 4 * g + j;
-            const bool ok = t < t_end;
-            const bool live = ok && col_ok;
-            const int64_t tt = ok ? t : t_begin;
-            const int64_t r0 = tt * N * row_bytes + (int64_t)(col_ok ? cv : 0) * 16;
-            uint4 rh[N], rin[N];
-#pragma unroll
-            for (int i = 0; i < N; ++i) {
-                rh[i] = ld16_stream(H + r0 + i * row_bytes);
-                if (dH_in) rin[i] = ld16_stream(dH_in + r0 + i * row_bytes);
-            }
-            float ai[N], bi[N];
-#pragma unroll
-            for (int i = 0; i < N; ++i) {
-                ai[i] = ab[tt * 2 * N + i];
-                bi[i] = ab[tt * 2 * N + N + i];
-            }
+            Tok& L = (j & 1) ? L1 : L0;
+            if (j < 3) fetch(j + 1, (j & 1) ? L0 : L1);
+            __builtin_amdgcn_sched_barrier(0);
+            const int64_t t = t0 + g + 4 * j;
+            const bool ok = t < T;
+            const int64_t r0 = (ok ? t : t0) * N * row_bytes + col_off;
 #pragma unroll
             for (int q = 0; q < 8; ++q) hb[j][q] = 0.0f;
 #pragma unroll
             for (int i = 0; i < N; ++i) {
-                float h[8], o[8];
-                unpack<bf16_t>(rh[i], h);
-                if (dH_in) {
-                    unpack<bf16_t>(rin[i], o);
-                } else {
+                uint32_t ow[4];
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) o[q] = 0.0f;
+                for (int k = 0; k < 4; ++k) {
+                    const float h0 = lo_bf16(L.h[i][k]), h1 = hi_bf16(L.h[i][k]);
+                    float o0 = 0.0f, o1 = 0.0f;
+                    if constexpr (IN) {
+                        o0 = lo_bf16(L.din[i][k]);
+                        o1 = hi_bf16(L.din[i][k]);
+                    }
+                    hb[j][2 * k] = fmaf(L.a[i], h0, hb[j][2 * k]);
+                    hb[j][2 * k + 1] = fmaf(L.a[i], h1, hb[j][2 * k + 1]);
+                    o0 = fmaf(L.b[i], h0, fmaf(L.a[i], dhb[2 * k][j], o0));
+                    o1 = fmaf(L.b[i], h1, fmaf(L.a[i], dhb[2 * k + 1][j], o1));
+                    ow[k] = pack_bf16x2(o0, o1);
                 }
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    hb[j][q] = fmaf(ai[i], h[q], hb[j][q]);
-                    o[q] = fmaf(bi[i], h[q], fmaf(ai[i], dhb[q][j], o[q]));
-                }
-                if (live) st16_stream(dH + r0 + i * row_bytes, pack<bf16_t>(o));
+                if (ok && col_ok) st16_stream(dH + r0 + i * row_bytes, make_uint4(ow[0], ow[1], ow[2], ow[3]));
             }
 #pragma unroll
             for (int q = 0; q < 8; ++q) hb[j][q] = ok ? hb[j][q] : 0.0f;
+            __builtin_amdgcn_sched_barrier(0);
         }
         // dW += dz^T hbar over the 16 tokens
         i16x4_t Ah[MT], Al[MT];
@@ -482,9 +505,9 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(
             float x[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int64_t t = t0 + 4 * g + j;
-                const float v = dz[(t < t_end ? t : t_begin) * K + (c < K ? c : K - 1)];
-                x[j] = (t < t_end && c < K) ? v : 0.0f;
+                const int64_t t = t0 + g + 4 * j;
+                const float v = dz[(t < T ? t : t0) * K + (c < K ? c : K - 1)];
+                x[j] = (t < T && c < K) ? v : 0.0f;
             }
             const Split2 s0 = split_bf16x2(x[0], x[1]), s1 = split_bf16x2(x[2], x[3]);
             Ah[m] = __builtin_bit_cast(i16x4_t, make_uint2(s0.hi, s1.hi));
@@ -512,12 +535,11 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(
             for (int j = 0; j < 4; ++j) {
                 const int c = 16 * m + 4 * g + j;
                 if (c < K) {
-                    float v[8];
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) v[q] = acc[m][q][j];
                     float* o = out + (int64_t)c * d + (int64_t)cv * 8;
-                    *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
-                    *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+                    *reinterpret_cast<float4*>(o) =
+                        make_float4(acc[m][0][j], acc[m][1][j], acc[m][2][j], acc[m][3][j]);
+                    *reinterpret_cast<float4*>(o + 4) =
+                        make_float4(acc[m][4][j], acc[m][5][j], acc[m][6][j], acc[m][7][j]);
                 }
             }
     }
@@ -540,7 +562,9 @@ hipError_t stream_go(const void* H, const void* W, const float* dz, const float*
     const dim3 grid((unsigned)((nvec + 15) / 16), (unsigned)splits);
     void (*kernel)(const uint8_t*, const uint8_t*, const float*, const float*, const float*,
                    const uint8_t*, uint8_t*, float*, int64_t, int, int64_t) =
-        std::is_same<S, bf16_t>::value ? wgrad_mfma_kernel<N> : wgrad_stream_kernel<N, S>;
+        !std::is_same<S, bf16_t>::value ? wgrad_stream_kernel<N, S>
+        : dH_in                          ? wgrad_mfma_kernel<N, true>
+                                         : wgrad_mfma_kernel<N, false>;
     return launch(kernel, grid, dim3(256), 0, s, static_cast<const uint8_t*>(H),
                   static_cast<const uint8_t*>(W), dz, ab, r, static_cast<const uint8_t*>(dH_in),
                   static_cast<uint8_t*>(dH), part, T, d, tps);
