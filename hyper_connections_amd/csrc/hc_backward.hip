@@ -91,18 +91,9 @@ __global__ __launch_bounds__(1024) void post_bwd_kernel(
         float acc[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[m] = 0.0f;
-        for (int64_t t = blk; t < T; t += nb) {
-            const float* rec = w + t * w_stride;
-            float beta[N], A[N][N];
-#pragma unroll
-            for (int i = 0; i < N; ++i) beta[i] = rec[N + i];
-#pragma unroll
-            for (int i = 0; i < N; ++i)
-#pragma unroll
-                for (int j = 0; j < N; ++j) A[i][j] = rec[2 * N + i * N + j];
-
+        uint4 rg[N][VPT], rh[N][VPT], rf[VPT];
+        auto fetch = [&](int64_t t) {
             const int64_t r0 = t * N * row_bytes;
-            uint4 rg[N][VPT], rh[N][VPT], rf[VPT];
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
                 const int v = threadIdx.x + j * B;
@@ -115,6 +106,28 @@ __global__ __launch_bounds__(1024) void post_bwd_kernel(
                     rf[j] = ld16_stream(F + t * row_bytes + v * 16);
                 }
             }
+        };
+        // Per-token records with one vector per thread: a token's loads are
+        // issued before the previous token's block-wide sums.  (Measured at
+        // n = 4: this form also compiles to 77 registers instead of 85, six
+        // waves per SIMD instead of five, and runs 16% faster; with more
+        // vectors per thread it needs more registers, so it is not used there.)
+        constexpr bool kAhead = PER_TOKEN && VPT == 1;
+        if constexpr (kAhead) {
+            if (blk < T) fetch(blk);
+        }
+        for (int64_t t = blk; t < T; t += nb) {
+            if constexpr (!kAhead) fetch(t);
+            const float* rec = w + t * w_stride;
+            float beta[N], A[N][N];
+#pragma unroll
+            for (int i = 0; i < N; ++i) beta[i] = rec[N + i];
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+#pragma unroll
+                for (int j = 0; j < N; ++j) A[i][j] = rec[2 * N + i * N + j];
+
+            const int64_t r0 = t * N * row_bytes;
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
                 const int v = threadIdx.x + j * B;
@@ -187,6 +200,9 @@ __global__ __launch_bounds__(1024) void post_bwd_kernel(
                 }
             }
             if constexpr (PER_TOKEN) {
+                if constexpr (kAhead) {
+                    if (t + nb < T) fetch(t + nb);
+                }
                 block_sum_vec<M>(acc, red);
                 if (threadIdx.x < K) {
                     const int c = threadIdx.x;
@@ -421,8 +437,20 @@ __global__ __launch_bounds__(1024) void sum_records_kernel(const float* __restri
                                                            int K, float* __restrict__ out) {
     __shared__ float red[16];
     const int c = blockIdx.x;
-    float s = 0.0f;
-    for (int64_t t = threadIdx.x; t < T; t += 1024) s += rec[t * K + c];
+    // eight independent partial sums keep eight loads in flight per thread;
+    // they are combined in a fixed order
+    float p[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p[k] = 0.0f;
+    int64_t t = threadIdx.x;
+    for (; t + 7 * 1024 < T; t += 8 * 1024) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) p[k] += rec[(t + k * 1024) * K + c];
+    }
+#pragma unroll
+    for (int k = 0; k < 7; ++k)
+        if (t + k * 1024 < T) p[k] += rec[(t + k * 1024) * K + c];
+    float s = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     s = block_sum(s, red);
     if (threadIdx.x == 0) out[c] = s;
 }

@@ -549,9 +549,10 @@ template <int N>
 hipError_t coef_go(const float* P, const float* r, const float* dw, const float* dw2, const float* ws,
                    float scale, int iters, float* scr, float* dz, float* dl, float* ab, int64_t T,
                    int d, hipStream_t s) {
-    const int64_t blocks = (T + 255) / 256;
+    // one wave per workgroup: 16384 tokens still reach every CU
+    const int64_t blocks = (T + 63) / 64;
     return launch(wgrad_coef_kernel<N>, dim3((unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid)),
-                  dim3(256), 0, s, P, r, dw, dw2, ws, scale, iters, scr, dz, dl, ab, T, d);
+                  dim3(64), 0, s, P, r, dw, dw2, ws, scale, iters, scr, dz, dl, ab, T, d);
 }
 
 template <int N, typename S>
@@ -628,14 +629,14 @@ int64_t sinkhorn_backward_workspace_bytes(int64_t T, int iters) {
 
 hipError_t launch_sinkhorn_backward(const float* logits, const float* dw, float* dlogits, int iters,
                                     void* work, int64_t T, int n, hipStream_t s) {
-    const int64_t blocks = (T + 255) / 256;
+    const int64_t blocks = (T + 63) / 64;
     const dim3 grid((unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid));
     float* scr = static_cast<float*>(work);
     switch (n) {
-        case 1: return launch(sinkhorn_bwd_kernel<1>, grid, dim3(256), 0, s, logits, dw, dlogits, iters, scr, T);
-        case 2: return launch(sinkhorn_bwd_kernel<2>, grid, dim3(256), 0, s, logits, dw, dlogits, iters, scr, T);
-        case 3: return launch(sinkhorn_bwd_kernel<3>, grid, dim3(256), 0, s, logits, dw, dlogits, iters, scr, T);
-        case 4: return launch(sinkhorn_bwd_kernel<4>, grid, dim3(256), 0, s, logits, dw, dlogits, iters, scr, T);
+        case 1: return launch(sinkhorn_bwd_kernel<1>, grid, dim3(64), 0, s, logits, dw, dlogits, iters, scr, T);
+        case 2: return launch(sinkhorn_bwd_kernel<2>, grid, dim3(64), 0, s, logits, dw, dlogits, iters, scr, T);
+        case 3: return launch(sinkhorn_bwd_kernel<3>, grid, dim3(64), 0, s, logits, dw, dlogits, iters, scr, T);
+        case 4: return launch(sinkhorn_bwd_kernel<4>, grid, dim3(64), 0, s, logits, dw, dlogits, iters, scr, T);
     }
     return hipErrorInvalidValue;
 }
