@@ -382,10 +382,11 @@ def main():
             b["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
 
         if wl.kind == "dynamic":
-            # per-token records from the forward (untimed), gradient records per token
+            # per-token records from a training forward (untimed) that keeps the
+            # projections for the backward; gradient records per token
             wws_bytes = int(hc.lib().hc_weights_backward_workspace(T, n, d, 0))
             for b in bufs:
-                hc.weights(b["H"], Wp, ws, wl.scale, wl.eps, 0, out=b["w"])
+                _, b["saved"] = hc.weights_save(b["H"], Wp, ws, wl.scale, wl.eps, 0, out=b["w"])
                 b["dwp"] = torch.empty((T, K), dtype=torch.float32, device="cuda")
                 b["dwq"] = torch.empty((T, K), dtype=torch.float32, device="cuda")
                 b["dW"] = torch.empty((K, d), dtype=torch.float32, device="cuda")
@@ -407,7 +408,7 @@ def main():
             # the records' gradient from post and pre, through the weight producer
             hc.weights_backward(b["H"], Wp, ws, wl.scale, b["dwp"], wl.eps, 0, dH_in=b["O"],
                                 out=b["O"], dW=b["dW"], dw_static=b["dws"], workspace=b["wws"],
-                                dw2=b["dwq"])
+                                dw2=b["dwq"], saved=b["saved"])
 
         ops = [("post_mix_backward", post_bwd), ("pre_mix_backward", pre_bwd)]
         if wl.kind == "dynamic":

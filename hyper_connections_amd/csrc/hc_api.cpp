@@ -83,7 +83,7 @@ const char* hc_status_str(hc_status s) {
     return "HC_ERR_UNKNOWN: unknown status code";
 }
 
-int32_t hc_abi_version(void) { return 1; }
+int32_t hc_abi_version(void) { return 2; }
 
 hc_status hc_pre_mix(const void* H, const float* w, int64_t w_stride, const float* gamma, float eps,
                      void* u, int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream) {
@@ -168,6 +168,38 @@ hc_status hc_weights(const void* H, const void* W, const float* w_static, float 
     if (overlap(sO, sH) || overlap(sO, sW) || overlap(sO, sS)) return HC_ERR_ALIAS;
     return from_hip(hc::launch_weights(H, W, w_static, scale, eps, sinkhorn_iters, w_out, T, n, d,
                                        dt, static_cast<hipStream_t>(stream)));
+}
+
+int64_t hc_weights_saved_bytes(int64_t T, int32_t n) {
+    if (T <= 0 || n < 1 || n > HC_MAX_STREAMS) return 0;
+    return hc::saved_floats(T, n) * 4;
+}
+
+hc_status hc_weights_save(const void* H, const void* W, const float* w_static, float scale,
+                          float eps, int32_t sinkhorn_iters, float* w_out, float* saved,
+                          int64_t saved_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
+                          void* stream) {
+    hc_status st = check_nd(n, d, T, dt);
+    if (st != HC_OK) return st;
+    if (!eps_ok(eps) || !std::isfinite(scale)) return HC_ERR_ARG;
+    if (sinkhorn_iters < 0 || sinkhorn_iters > HC_MAX_SINKHORN_ITERS) return HC_ERR_ARG;
+    if (T == 0) return HC_OK;
+    if (!H || !W || !w_static || !w_out || !saved) return HC_ERR_NULL;
+    const int64_t need = hc_weights_saved_bytes(T, n);
+    if (saved_bytes < need) return HC_ERR_ARG;
+    if (misaligned(H, 16) || misaligned(W, 16) || misaligned(w_static, 4) || misaligned(w_out, 4) ||
+        misaligned(saved, 16))
+        return HC_ERR_ALIGN;
+    const int K = record_len(n);
+    const int64_t s = elem_bytes(dt);
+    const Span sH{H, T * n * d * s}, sW{W, int64_t(K) * d * s}, sS{w_static, int64_t(K) * 4},
+        sO{w_out, T * K * 4}, sv{saved, need};
+    for (const Span& o : {sO, sv})
+        if (overlap(o, sH) || overlap(o, sW) || overlap(o, sS)) return HC_ERR_ALIAS;
+    if (overlap(sO, sv)) return HC_ERR_ALIAS;
+    return from_hip(hc::launch_weights_save(H, W, w_static, scale, eps, sinkhorn_iters, w_out, saved,
+                                            saved + hc::saved_r_offset(T, n), T, n, d, dt,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 hc_status hc_sinkhorn(const float* logits, float* w_out, int32_t iters, int64_t T, int32_t n,
@@ -268,7 +300,7 @@ int64_t hc_weights_backward_workspace(int64_t T, int32_t n, int32_t d, int32_t s
 
 hc_status hc_weights_backward(const void* H, const void* W, const float* w_static, float scale,
                               float eps, int32_t sinkhorn_iters, const float* dw, const float* dw2,
-                              const void* dH_in,
+                              const float* saved, const void* dH_in,
                               void* dH, float* dW, float* dw_static, void* workspace,
                               int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
                               void* stream) {
@@ -283,15 +315,15 @@ hc_status hc_weights_backward(const void* H, const void* W, const float* w_stati
     if (workspace_bytes < need) return HC_ERR_ARG;
     if (misaligned(H, 16) || misaligned(W, 16) || misaligned(dH, 16) || misaligned(dH_in, 16) ||
         misaligned(workspace, 16) || misaligned(w_static, 4) || misaligned(dw, 4) ||
-        misaligned(dW, 4) || misaligned(dw_static, 4) || misaligned(dw2, 4))
+        misaligned(dW, 4) || misaligned(dw_static, 4) || misaligned(dw2, 4) || misaligned(saved, 16))
         return HC_ERR_ALIGN;
     const int K = record_len(n);
     const int64_t s = elem_bytes(dt);
     const Span sH{H, T * n * d * s}, sW{W, int64_t(K) * d * s}, sS{w_static, int64_t(K) * 4},
         sg{dw, T * K * 4}, sg2{dw2, dw2 ? T * K * 4 : 0}, sin{dH_in, dH_in ? T * n * d * s : 0},
         sdH{dH, T * n * d * s}, sdW{dW, int64_t(K) * d * 4}, sds{dw_static, int64_t(K) * 4},
-        sws{workspace, need};
-    const Span ins[] = {sH, sW, sS, sg, sg2};
+        sws{workspace, need}, ssv{saved, saved ? hc_weights_saved_bytes(T, n) : 0};
+    const Span ins[] = {sH, sW, sS, sg, sg2, ssv};
     for (const Span& o : {sdH, sdW, sds, sws})
         for (const Span& i : ins)
             if (overlap(o, i)) return HC_ERR_ALIAS;
@@ -302,7 +334,7 @@ hc_status hc_weights_backward(const void* H, const void* W, const float* w_stati
         overlap(sdW, sws) || overlap(sds, sws))
         return HC_ERR_ALIAS;
     return from_hip(hc::launch_weights_backward(H, W, w_static, scale, eps, sinkhorn_iters, dw, dw2,
-                                                dH_in, dH, dW, dw_static, workspace, T, n, d, dt,
+                                                saved, dH_in, dH, dW, dw_static, workspace, T, n, d, dt,
                                                 static_cast<hipStream_t>(stream)));
 }
 

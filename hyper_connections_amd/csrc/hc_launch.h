@@ -62,6 +62,13 @@ hipError_t launch_sinkhorn(const float* logits, float* w_out, int iters, int64_t
                            hipStream_t s);
 hipError_t launch_weights_raw(const void* H, const void* W, float eps, float* P, float* r, int64_t T,
                               int n, int d, int dt, hipStream_t s);
+hipError_t launch_weights_save(const void* H, const void* W, const float* w_static, float scale,
+                               float eps, int iters, float* w_out, float* P, float* r, int64_t T,
+                               int n, int d, int dt, hipStream_t s);
+// The per-stream projections P [T][n][K] and norms r [T][n] the forward keeps
+// for the gradient pass: floats, r at saved_r_offset(T, n).
+int64_t saved_r_offset(int64_t T, int n);
+int64_t saved_floats(int64_t T, int n);
 int64_t sum_rows_tmp_floats(int64_t rows, int64_t cols);
 hipError_t launch_sum_rows(const float* in, int64_t rows, int cols, float* tmp, float* out,
                            hipStream_t s);
@@ -69,7 +76,7 @@ int64_t weights_backward_workspace_bytes(int64_t T, int n, int d, int iters);
 int64_t sinkhorn_backward_workspace_bytes(int64_t T, int iters);
 hipError_t launch_weights_backward(const void* H, const void* W, const float* w_static, float scale,
                                    float eps, int iters, const float* dw, const float* dw2,
-                                   const void* dH_in,
+                                   const float* saved, const void* dH_in,
                                    void* dH, float* dW, float* dws, void* work, int64_t T, int n,
                                    int d, int dt, hipStream_t s);
 hipError_t launch_sinkhorn_backward(const float* logits, const float* dw, float* dlogits, int iters,

@@ -210,14 +210,16 @@ struct WeightsGeom {
     static_assert(EPI * 4 <= TBYTES, "the epilogue reuses the transpose buffer");
 };
 
-// RAW: instead of records, write the per-stream projections P_i = W H_i
-// ([T][n][K] into w_out) and the row norms r_i ([T][n] into r_out), the
-// quantities the gradient pass needs.
-template <int N, typename S, bool RAW>
+// MODE kRecord: the records into w_out.  kRaw: instead of records, the
+// per-stream projections P_i = W H_i ([T][n][K] into p_out) and the row norms
+// r_i ([T][n] into r_out), the quantities the gradient pass needs.  kSave:
+// both (the records, and P and r kept for the gradient pass).
+enum WeightsMode { kRecord = 0, kRaw = 1, kSave = 2 };
+template <int N, typename S, int MODE>
 __global__ __launch_bounds__(kWThreads) void weights_kernel(
     const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, const float* __restrict__ w_static,
-    float scale, float eps, int iters, float* __restrict__ w_out, float* __restrict__ r_out,
-    int64_t T, int d) {
+    float scale, float eps, int iters, float* __restrict__ w_out, float* __restrict__ p_out,
+    float* __restrict__ r_out, int64_t T, int d) {
     using G = WeightsGeom<N, S>;
     constexpr int V = G::V, KC = G::KC, NT = G::NT, K = G::K, TPW = G::TPW;
     constexpr int SB = Store<S>::kBytes;
@@ -336,12 +338,14 @@ __global__ __launch_bounds__(kWThreads) void weights_kernel(
         if (grp == 0) rs[rho] = 1.0f / sqrtf(ss / (float)d + eps);
         __syncthreads();
 
-        if constexpr (RAW) {
+        if constexpr (MODE != kRecord) {
             for (int o = lane; o < TPW * N * K; o += 64) {
                 const int row = o / K, col = o % K;
-                if (tok0 + row / N < T) w_out[(tok0 * N + row) * K + col] = Cs[row * G::CPITCH + col];
+                if (tok0 + row / N < T) p_out[(tok0 * N + row) * K + col] = Cs[row * G::CPITCH + col];
             }
             if (lane < TPW * N && tok0 + lane / N < T) r_out[tok0 * N + lane] = rs[lane];
+        }
+        if constexpr (MODE == kRaw) {
             __syncthreads();
             continue;
         }
@@ -400,45 +404,55 @@ hipError_t launch_sinkhorn(const float* logits, float* w_out, int iters, int64_t
 namespace {
 template <int N, typename S>
 hipError_t weights_go(const void* H, const void* W, const float* w_static, float scale, float eps,
-                      int iters, float* w_out, float* r_out, int64_t T, int d, hipStream_t s) {
+                      int iters, float* w_out, float* p_out, float* r_out, int64_t T, int d,
+                      hipStream_t s) {
     const int64_t per_block = kWaves * WeightsGeom<N, S>::TPW;
     const int64_t blocks = (T + per_block - 1) / per_block;
     const dim3 grid((unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid));
-    if (r_out)
-        return launch(weights_kernel<N, S, true>, grid, dim3(kWThreads), 0, s,
-                      static_cast<const uint8_t*>(H), static_cast<const uint8_t*>(W), w_static, scale,
-                      eps, iters, w_out, r_out, T, d);
-    return launch(weights_kernel<N, S, false>, grid, dim3(kWThreads), 0, s,
-                  static_cast<const uint8_t*>(H), static_cast<const uint8_t*>(W), w_static, scale, eps,
-                  iters, w_out, r_out, T, d);
+    void (*kernel)(const uint8_t*, const uint8_t*, const float*, float, float, int, float*, float*,
+                   float*, int64_t, int) = !p_out ? weights_kernel<N, S, kRecord>
+                                           : w_out ? weights_kernel<N, S, kSave>
+                                                   : weights_kernel<N, S, kRaw>;
+    return launch(kernel, grid, dim3(kWThreads), 0, s, static_cast<const uint8_t*>(H),
+                  static_cast<const uint8_t*>(W), w_static, scale, eps, iters, w_out, p_out, r_out, T,
+                  d);
 }
 template <typename S>
 hipError_t weights_by_n(int n, const void* H, const void* W, const float* w_static, float scale,
-                        float eps, int iters, float* w_out, float* r_out, int64_t T, int d,
-                        hipStream_t s) {
+                        float eps, int iters, float* w_out, float* p_out, float* r_out, int64_t T,
+                        int d, hipStream_t s) {
     switch (n) {
-        case 1: return weights_go<1, S>(H, W, w_static, scale, eps, iters, w_out, r_out, T, d, s);
-        case 2: return weights_go<2, S>(H, W, w_static, scale, eps, iters, w_out, r_out, T, d, s);
-        case 3: return weights_go<3, S>(H, W, w_static, scale, eps, iters, w_out, r_out, T, d, s);
-        case 4: return weights_go<4, S>(H, W, w_static, scale, eps, iters, w_out, r_out, T, d, s);
+        case 1: return weights_go<1, S>(H, W, w_static, scale, eps, iters, w_out, p_out, r_out, T, d, s);
+        case 2: return weights_go<2, S>(H, W, w_static, scale, eps, iters, w_out, p_out, r_out, T, d, s);
+        case 3: return weights_go<3, S>(H, W, w_static, scale, eps, iters, w_out, p_out, r_out, T, d, s);
+        case 4: return weights_go<4, S>(H, W, w_static, scale, eps, iters, w_out, p_out, r_out, T, d, s);
     }
     return hipErrorInvalidValue;
+}
+hipError_t weights_by_dt(int dt, int n, const void* H, const void* W, const float* w_static,
+                         float scale, float eps, int iters, float* w_out, float* p_out, float* r_out,
+                         int64_t T, int d, hipStream_t s) {
+    if (dt == 0) return weights_by_n<f32_t>(n, H, W, w_static, scale, eps, iters, w_out, p_out, r_out, T, d, s);
+    if (dt == 2) return weights_by_n<fp8_t>(n, H, W, w_static, scale, eps, iters, w_out, p_out, r_out, T, d, s);
+    return weights_by_n<bf16_t>(n, H, W, w_static, scale, eps, iters, w_out, p_out, r_out, T, d, s);
 }
 }  // namespace
 
 hipError_t launch_weights(const void* H, const void* W, const float* w_static, float scale,
                           float eps, int iters, float* w_out, int64_t T, int n, int d, int dt,
                           hipStream_t s) {
-    if (dt == 0) return weights_by_n<f32_t>(n, H, W, w_static, scale, eps, iters, w_out, nullptr, T, d, s);
-    if (dt == 2) return weights_by_n<fp8_t>(n, H, W, w_static, scale, eps, iters, w_out, nullptr, T, d, s);
-    return weights_by_n<bf16_t>(n, H, W, w_static, scale, eps, iters, w_out, nullptr, T, d, s);
+    return weights_by_dt(dt, n, H, W, w_static, scale, eps, iters, w_out, nullptr, nullptr, T, d, s);
 }
 
 hipError_t launch_weights_raw(const void* H, const void* W, float eps, float* P, float* r, int64_t T,
                               int n, int d, int dt, hipStream_t s) {
-    if (dt == 0) return weights_by_n<f32_t>(n, H, W, nullptr, 0.0f, eps, 0, P, r, T, d, s);
-    if (dt == 2) return weights_by_n<fp8_t>(n, H, W, nullptr, 0.0f, eps, 0, P, r, T, d, s);
-    return weights_by_n<bf16_t>(n, H, W, nullptr, 0.0f, eps, 0, P, r, T, d, s);
+    return weights_by_dt(dt, n, H, W, nullptr, 0.0f, eps, 0, nullptr, P, r, T, d, s);
+}
+
+hipError_t launch_weights_save(const void* H, const void* W, const float* w_static, float scale,
+                               float eps, int iters, float* w_out, float* P, float* r, int64_t T,
+                               int n, int d, int dt, hipStream_t s) {
+    return weights_by_dt(dt, n, H, W, w_static, scale, eps, iters, w_out, P, r, T, d, s);
 }
 
 }  // namespace hc

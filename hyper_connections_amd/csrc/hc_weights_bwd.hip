@@ -617,6 +617,12 @@ inline WgSpace wg_space(int64_t T, int n, int d, int iters) {
 
 }  // namespace
 
+int64_t saved_r_offset(int64_t T, int n) {
+    const int64_t K = 2 * n + int64_t(n) * n;
+    return up4(T * n * K);
+}
+int64_t saved_floats(int64_t T, int n) { return saved_r_offset(T, n) + up4(T * n); }
+
 int64_t weights_backward_workspace_bytes(int64_t T, int n, int d, int iters) {
     if (T <= 0 || n <= 0 || d <= 0 || iters < 0) return 0;
     return wg_space(T, n, d, iters).total * 4;
@@ -643,30 +649,36 @@ hipError_t launch_sinkhorn_backward(const float* logits, const float* dw, float*
 
 hipError_t launch_weights_backward(const void* H, const void* W, const float* w_static, float scale,
                                    float eps, int iters, const float* dw, const float* dw2,
-                                   const void* dH_in,
+                                   const float* saved, const void* dH_in,
                                    void* dH, float* dW, float* dws, void* work, int64_t T, int n,
                                    int d, int dt, hipStream_t s) {
     const WgSpace sp = wg_space(T, n, d, iters);
     float* ws = static_cast<float*>(work);
     const int K = 2 * n + n * n;
-    // (1) per-stream projections and row norms
-    hipError_t e = launch_weights_raw(H, W, eps, ws + sp.P, ws + sp.r, T, n, d, dt, s);
-    if (e != hipSuccess) return e;
+    // (1) per-stream projections and row norms: kept by the forward, or
+    // computed again
+    const float* Pp = saved ? saved : ws + sp.P;
+    const float* rp = saved ? saved + saved_r_offset(T, n) : ws + sp.r;
+    hipError_t e = hipSuccess;
+    if (!saved) {
+        e = launch_weights_raw(H, W, eps, ws + sp.P, ws + sp.r, T, n, d, dt, s);
+        if (e != hipSuccess) return e;
+    }
     // (2) per-token coefficients
     switch (n) {
-        case 1: e = coef_go<1>(ws + sp.P, ws + sp.r, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
-        case 2: e = coef_go<2>(ws + sp.P, ws + sp.r, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
-        case 3: e = coef_go<3>(ws + sp.P, ws + sp.r, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
-        case 4: e = coef_go<4>(ws + sp.P, ws + sp.r, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
+        case 1: e = coef_go<1>(Pp, rp, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
+        case 2: e = coef_go<2>(Pp, rp, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
+        case 3: e = coef_go<3>(Pp, rp, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
+        case 4: e = coef_go<4>(Pp, rp, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
     // (3) dH and the dW partials
     const int64_t splits = splits_of(T);
     const int64_t tps = (T + splits - 1) / splits;
-    e = dt == 0 ? stream_by_n<f32_t>(n, H, W, ws + sp.dz, ws + sp.ab, ws + sp.r, dH_in, dH, ws + sp.part,
+    e = dt == 0 ? stream_by_n<f32_t>(n, H, W, ws + sp.dz, ws + sp.ab, rp, dH_in, dH, ws + sp.part,
                                      T, d, (int)splits, tps, s)
-                : stream_by_n<bf16_t>(n, H, W, ws + sp.dz, ws + sp.ab, ws + sp.r, dH_in, dH,
+                : stream_by_n<bf16_t>(n, H, W, ws + sp.dz, ws + sp.ab, rp, dH_in, dH,
                                       ws + sp.part, T, d, (int)splits, tps, s);
     if (e != hipSuccess) return e;
     // (4) fixed-order sums: dW over the partials, dw_static over the tokens

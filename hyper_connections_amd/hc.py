@@ -49,12 +49,15 @@ _SIGS = {
     "hc_pre_mix_backward": [_vp, _vp, _fp, _i64, _fp, _f32, _vp, _vp, _fp, _fp, _vp, _i64, _i64,
                             _i32, _i32, _i32, _vp],
     "hc_sum_records": [_fp, _i64, _i32, _fp, _vp],
-    "hc_weights_backward": [_vp, _vp, _fp, _f32, _f32, _i32, _fp, _fp, _vp, _vp, _fp, _fp, _vp,
-                            _i64, _i64, _i32, _i32, _i32, _vp],
+    "hc_weights_save": [_vp, _vp, _fp, _f32, _f32, _i32, _fp, _fp, _i64, _i64, _i32, _i32, _i32,
+                        _vp],
+    "hc_weights_backward": [_vp, _vp, _fp, _f32, _f32, _i32, _fp, _fp, _fp, _vp, _vp, _fp, _fp,
+                            _vp, _i64, _i64, _i32, _i32, _i32, _vp],
     "hc_sinkhorn_backward": [_fp, _fp, _fp, _i32, _vp, _i64, _i64, _i32, _vp],
 }
 EXPORTS = tuple(_SIGS) + ("hc_status_str", "hc_abi_version", "hc_backward_workspace",
-                          "hc_weights_backward_workspace", "hc_sinkhorn_backward_workspace")
+                          "hc_weights_backward_workspace", "hc_sinkhorn_backward_workspace",
+                          "hc_weights_saved_bytes")
 
 _lib = None
 
@@ -89,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.hc_weights_backward_workspace.restype = ctypes.c_int64
         L.hc_sinkhorn_backward_workspace.argtypes = [ctypes.c_int64, ctypes.c_int32]
         L.hc_sinkhorn_backward_workspace.restype = ctypes.c_int64
+        L.hc_weights_saved_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32]
+        L.hc_weights_saved_bytes.restype = ctypes.c_int64
         _lib = L
     return _lib
 
@@ -202,9 +207,7 @@ def post_pre_mix(H, F, w, w_next, gamma_next, eps: float = 1e-6, out=None, u_out
     return o, u
 
 
-def weights(H, W, w_static, scale: float, eps: float = 1e-6, sinkhorn_iters: int = 0,
-            out=None, stream=None) -> torch.Tensor:
-    """Per-token weight records (T, K) float32 from the streams (see include/hc.h)."""
+def _weights_args(H, W, w_static, out):
     T, n, d, K = _H(H)
     _dev(W, "W")
     if W.dtype != H.dtype or tuple(W.shape) != (K, d):
@@ -215,9 +218,34 @@ def weights(H, W, w_static, scale: float, eps: float = 1e-6, sinkhorn_iters: int
     o = torch.empty((T, K), dtype=torch.float32, device=H.device) if out is None else _dev(out, "out")
     if o.dtype != torch.float32 or tuple(o.shape) != (T, K):
         raise ValueError(f"out must be float32 of shape ({T}, {K})")
+    return T, n, d, K, o
+
+
+def weights(H, W, w_static, scale: float, eps: float = 1e-6, sinkhorn_iters: int = 0,
+            out=None, stream=None) -> torch.Tensor:
+    """Per-token weight records (T, K) float32 from the streams (see include/hc.h)."""
+    T, n, d, K, o = _weights_args(H, W, w_static, out)
     _call("hc_weights", H.data_ptr(), W.data_ptr(), w_static.data_ptr(), float(scale), float(eps),
           int(sinkhorn_iters), o.data_ptr(), T, n, d, _dt(H), _stream(stream))
     return o
+
+
+def weights_save(H, W, w_static, scale: float, eps: float = 1e-6, sinkhorn_iters: int = 0,
+                 out=None, saved=None, stream=None):
+    """weights() for a training forward: returns (records, saved), where saved
+    (a float32 device buffer of hc_weights_saved_bytes) holds what
+    weights_backward(..., saved=saved) would otherwise recompute."""
+    T, n, d, K, o = _weights_args(H, W, w_static, out)
+    need = int(lib().hc_weights_saved_bytes(T, n))
+    if saved is None:
+        saved = torch.empty(max(need, 16) // 4, dtype=torch.float32, device=H.device)
+    _dev(saved, "saved")
+    if saved.dtype != torch.float32:
+        raise ValueError("saved must be float32")
+    _call("hc_weights_save", H.data_ptr(), W.data_ptr(), w_static.data_ptr(), float(scale),
+          float(eps), int(sinkhorn_iters), o.data_ptr(), saved.data_ptr(),
+          saved.numel() * 4, T, n, d, _dt(H), _stream(stream))
+    return o, saved
 
 
 def sinkhorn(logits, n: int, iters: int, out=None, stream=None) -> torch.Tensor:
@@ -340,11 +368,12 @@ def sum_records(rec, out=None, stream=None):
 
 def weights_backward(H, W, w_static, scale: float, dw, eps: float = 1e-6, sinkhorn_iters: int = 0,
                      dH_in=None, out=None, dW=None, dw_static=None, workspace=None, dw2=None,
-                     stream=None):
+                     saved=None, stream=None):
     """Gradients of weights: returns (dH, dW, dw_static).  dw is dL/d(records)
     (T, K) float32 (plus dw2 when given, e.g. the pre and post gradients of the
     same records); dH includes dH_in when given (``out=dH_in`` accumulates in
-    place); dW (K, d) and dw_static (K,) are float32."""
+    place); dW (K, d) and dw_static (K,) are float32.  ``saved`` is the buffer
+    weights_save filled for the same H, W and eps (else recomputed)."""
     T, n, d, K = _H(H)
     _dev(W, "W")
     _dev(w_static, "w_static")
@@ -363,6 +392,10 @@ def weights_backward(H, W, w_static, scale: float, dw, eps: float = 1e-6, sinkho
         _dev(dH_in, "dH_in")
         if dH_in.dtype != H.dtype or dH_in.shape != H.shape:
             raise ValueError("dH_in must match H")
+    if saved is not None:
+        _dev(saved, "saved")
+        if saved.dtype != torch.float32 or saved.numel() * 4 < int(lib().hc_weights_saved_bytes(T, n)):
+            raise ValueError("saved must be the float32 buffer weights_save filled")
     dH = torch.empty_like(H) if out is None else _dev(out, "out")
     if dH.dtype != H.dtype or dH.shape != H.shape:
         raise ValueError("out must match H")
@@ -380,6 +413,7 @@ def weights_backward(H, W, w_static, scale: float, dw, eps: float = 1e-6, sinkho
     _call("hc_weights_backward", H.data_ptr(), W.data_ptr(), w_static.data_ptr(), float(scale),
           float(eps), int(sinkhorn_iters), dw.data_ptr(),
           dw2.data_ptr() if dw2 is not None else None,
+          saved.data_ptr() if saved is not None else None,
           dH_in.data_ptr() if dH_in is not None else None, dH.data_ptr(), dW.data_ptr(),
           dws.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
           T, n, d, _dt(H), _stream(stream))

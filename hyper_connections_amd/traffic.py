@@ -68,7 +68,7 @@ def pre_bwd_bytes(n: int, d: int, s: int, accumulate: bool = True) -> int:
 def weights_bwd_bytes(n: int, d: int, s: int) -> int:
     """Gradient of the per-token weights: read H, read the incoming dH and
     write dH once each, plus two gradient records read (from pre and post).
-    The projection pass that recomputes W H_i re-reads H as well; that pass is
-    an implementation choice (the forward could keep P_i) and is not
-    counted."""
+    Not counted: the projections P_i = W H_i and norms r_i, read from what
+    the forward kept (n (K + 1) floats per token), or recomputed with a second
+    read of H when it kept nothing."""
     return 3 * n * d * s + 2 * record_bytes(n)

@@ -127,6 +127,22 @@ hc_status hc_weights(const void* H, const void* W, const float* w_static, float 
                      float eps, int32_t sinkhorn_iters, float* w_out,
                      int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream);
 
+/* Bytes of the state hc_weights_save keeps for hc_weights_backward (0 for
+ * T <= 0 or n out of range): the per-stream projections P_i = W H_i
+ * ([T][n][K] fp32) and norms r_i ([T][n] fp32, starting at float offset
+ * T*n*K rounded up to a multiple of 4). */
+int64_t hc_weights_saved_bytes(int64_t T, int32_t n);
+
+/* hc_weights for a training forward: the same records in w_out (bitwise the
+ * same as hc_weights), and in `saved` (saved_bytes >= hc_weights_saved_bytes,
+ * 16-byte aligned, no overlap with anything) the projections and norms that
+ * hc_weights_backward would otherwise recompute with a second read of H.
+ * Arguments otherwise as hc_weights. */
+hc_status hc_weights_save(const void* H, const void* W, const float* w_static, float scale,
+                          float eps, int32_t sinkhorn_iters, float* w_out, float* saved,
+                          int64_t saved_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
+                          void* stream);
+
 /* mHC step: make the stream mix doubly stochastic with Sinkhorn iterations
  * ([GLOSS] definition; [ATLAS] "Architecture concepts", mHC).  Per token:
  * alpha = sigmoid(l_alpha), beta = sigmoid(l_beta), A = exp(l_A) then `iters`
@@ -208,13 +224,16 @@ int64_t hc_weights_backward_workspace(int64_t T, int32_t n, int32_t d, int32_t s
  *     hc_weights; dw [T][K] fp32 (records of stride K); dw2 [T][K] fp32 or NULL,
  *     added to dw (the records feed both pre and post, whose backward calls
  *     each return a per-token gradient record)
+ *   saved: the state hc_weights_save kept for these H, W and eps, or NULL
+ *     (then the projections and norms are recomputed from H: one more read
+ *     of H); 16-byte aligned, an input
  *   dH_in [T][n][d] dt or NULL; dH [T][n][d] dt (dH == dH_in allowed)
  *   dW [K][d] fp32, dw_static [K] fp32 outputs
  *   workspace >= hc_weights_backward_workspace(T, n, d, sinkhorn_iters), 16-byte
  *     aligned.  fp32 and bf16 storage only (HC_ERR_DTYPE for HC_FP8). */
 hc_status hc_weights_backward(const void* H, const void* W, const float* w_static, float scale,
                               float eps, int32_t sinkhorn_iters, const float* dw, const float* dw2,
-                              const void* dH_in,
+                              const float* saved, const void* dH_in,
                               void* dH, float* dW, float* dw_static, void* workspace,
                               int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
                               void* stream);

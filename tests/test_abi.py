@@ -51,7 +51,7 @@ def test_status_strings(L):
         s = hc.status_str(code)
         assert s.startswith("HC_")
     assert hc.status_str(99).startswith("HC_ERR_UNKNOWN")
-    assert hc.abi_version() == 1
+    assert hc.abi_version() == 2
 
 
 def pre(L, H=P[0], w=P[1], ws=0, g=P[2], eps=1e-6, u=P[3], T=16, n=4, d=4096, dt=BF16):
@@ -185,8 +185,8 @@ def test_weights_backward_validation(L):
     assert L.hc_weights_backward_workspace(64, 4, 4096, 20) > need      # Sinkhorn scratch
     f = lambda **k: L.hc_weights_backward(  # noqa: E731
         k.get("H", P[0]), k.get("W", P[1]), k.get("ws", P[2]), k.get("scale", 0.01),
-        k.get("eps", 1e-6), k.get("it", 0), k.get("g", P[3]), k.get("g2", None), k.get("din", None),
-        k.get("dH", P[4]),
+        k.get("eps", 1e-6), k.get("it", 0), k.get("g", P[3]), k.get("g2", None), k.get("sv", None),
+        k.get("din", None), k.get("dH", P[4]),
         k.get("dW", P[5]), k.get("dws", P[6]), k.get("wk", P[7]), k.get("wkb", need),
         k.get("T", 64), k.get("n", 4), k.get("d", 4096), k.get("dt", BF16), None)
     assert f(T=0) == OK and f(T=0, dH=None) == OK
@@ -199,6 +199,23 @@ def test_weights_backward_validation(L):
     assert f(dH=P[0]) == ALIAS and f(dW=P[1] + 64) == ALIAS and f(wk=P[3]) == ALIAS
     assert f(din=P[4] + 16) == ALIAS and f(dws=P[5] + 64) == ALIAS
     assert f(g2=P[3] + 2) == ALIGN and f(g2=P[4]) == ALIAS             # dw2 under dH
+    assert f(sv=P[3] + 4) == ALIGN and f(sv=P[4] + 64) == ALIAS and f(sv=P[7]) == ALIAS
+
+
+def test_weights_save_validation(L):
+    need = L.hc_weights_saved_bytes(64, 4)
+    assert need == (64 * 4 * 24 + 64 * 4) * 4 and L.hc_weights_saved_bytes(0, 4) == 0
+    assert L.hc_weights_saved_bytes(64, 5) == 0 and L.hc_weights_saved_bytes(63, 3) == (63 * 3 * 15 + 1 + 63 * 3 + 3) * 4
+    f = lambda **k: L.hc_weights_save(  # noqa: E731
+        k.get("H", P[0]), k.get("W", P[1]), k.get("ws", P[2]), k.get("scale", 0.01),
+        k.get("eps", 1e-6), k.get("it", 0), k.get("o", P[3]), k.get("sv", P[4]), k.get("svb", need),
+        k.get("T", 64), k.get("n", 4), k.get("d", 4096), k.get("dt", BF16), None)
+    assert f(T=0) == OK and f(T=0, sv=None, o=None) == OK
+    assert f(dt=7) == DTYPE and f(n=0) == SHAPE and f(d=100) == SHAPE
+    assert f(eps=0.0) == ARG and f(it=-1) == ARG and f(T=-1) == ARG and f(svb=need - 4) == ARG
+    assert f(sv=None) == NULL and f(o=None) == NULL
+    assert f(sv=P[4] + 4) == ALIGN and f(o=P[3] + 2) == ALIGN
+    assert f(sv=P[0]) == ALIAS and f(o=P[4] + 64) == ALIAS and f(sv=P[1] + 16) == ALIAS
 
 
 def test_sinkhorn_backward_validation(L):

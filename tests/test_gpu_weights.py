@@ -173,3 +173,25 @@ def test_mhc_workload_pre_post_sampled():
     w64 = w_got.astype(np.float64)
     check(host(u[ti]), oracle.pre_mix(sub["H"], w64, inp["gamma"], wl.eps), "mhc pre")
     check(host(Hp[ti]), oracle.post_mix(sub["H"], sub["F"], w64), "mhc post")
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 264), ("bf16", 4096), ("f32", 132), ("fp8", 528)])
+@pytest.mark.parametrize("n", [1, 3, 4])
+@pytest.mark.parametrize("iters", [0, 5])
+def test_weights_save_records_equal_weights(dt, d, n, iters):
+    """The training forward's records are bitwise those of hc_weights; the
+    saved norms are the per-stream 1/rms of H."""
+    K = 2 * n + n * n
+    rng = np.random.default_rng(d + 11 * n + iters)
+    T = 45
+    H = storage(rng.standard_normal((T, n, d)).astype(np.float32), dt)
+    W = storage((0.05 * rng.standard_normal((K, d))).astype(np.float32), dt)
+    ws = (identity_record(n) + 0.1 * rng.standard_normal(K)).astype(np.float32)
+    Hd, Wd, wsd = dev(H), dev(W), dev(ws)
+    a = host(hc.weights(Hd, Wd, wsd, 0.5, 1e-6, iters))
+    b, saved = hc.weights_save(Hd, Wd, wsd, 0.5, 1e-6, iters)
+    assert np.array_equal(a, host(b))
+    off = (T * n * K + 3) // 4 * 4
+    r = host(saved)[off:off + T * n].reshape(T, n).astype(np.float64)
+    Hw = oracle.widen(H)
+    np.testing.assert_allclose(r, 1 / np.sqrt((Hw * Hw).mean(axis=2) + 1e-6), rtol=1e-5)

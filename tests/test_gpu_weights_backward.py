@@ -145,3 +145,20 @@ def test_weights_backward_two_gradient_records():
     b = hc.weights_backward(dev(H), dev(W), dev(ws), 0.2, dev(dw + dw2))
     for x, y in zip(a, b):
         assert np.array_equal(host(x), host(y))
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 264), ("bf16", 4096), ("f32", 132)])
+@pytest.mark.parametrize("n", [1, 2, 4])
+@pytest.mark.parametrize("iters", [0, 5])
+def test_weights_backward_with_saved_state(dt, d, n, iters):
+    """The state hc_weights_save keeps gives bitwise the gradients of the
+    recomputing path (the same kernel forms P and r either way)."""
+    rng = np.random.default_rng(d + 5 * n + iters)
+    T = 53
+    H, W, ws, dw = case(rng, dt, T, n, d)
+    Hd, Wd, wsd, dwd = dev(H), dev(W), dev(ws), dev(dw)
+    _, saved = hc.weights_save(Hd, Wd, wsd, 0.3, 1e-6, iters)
+    a = hc.weights_backward(Hd, Wd, wsd, 0.3, dwd, 1e-6, iters)
+    b = hc.weights_backward(Hd, Wd, wsd, 0.3, dwd, 1e-6, iters, saved=saved)
+    for x, y in zip(a, b):
+        assert np.array_equal(host(x), host(y))
