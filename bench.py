@@ -45,7 +45,8 @@ KERNEL_SOURCES = {
     "pre_mix": "hc_rows.hip", "post_mix": "hc_rows.hip", "post_pre_mix": "hc_rows.hip",
     "block_tanh": "hc_rows.hip", "weights": "hc_weights.hip", "sinkhorn": "hc_weights.hip",
     "post_mix_backward": "hc_backward.hip", "pre_mix_backward": "hc_backward.hip",
-    "sum_records": "hc_backward.hip",
+    "sum_records": "hc_backward.hip", "weights_backward": "hc_weights_bwd.hip",
+    "weights_backward_stream": "hc_weights_bwd.hip",
 }
 
 
@@ -113,7 +114,8 @@ SIMDS = 1024                       # 256 CUs x 4
 XCDS = 8
 
 # kernel name in the traces, where it differs from "<kernel>_kernel<"
-KERNEL_TAGS = {"post_mix_backward": "post_bwd_kernel<", "pre_mix_backward": "pre_bwd_kernel<"}
+KERNEL_TAGS = {"post_mix_backward": "post_bwd_kernel<", "pre_mix_backward": "pre_bwd_kernel<",
+               "weights_backward_stream": "wgrad_mfma_kernel<"}
 
 
 def summarize_mfma(pmc_csv: str, kernel: str, workload: str, cmds: list):
@@ -143,7 +145,21 @@ def summarize_mfma(pmc_csv: str, kernel: str, workload: str, cmds: list):
     secs = cycles / (CLOCK_GHZ * 1e9)
     from hyper_connections_amd import workloads
     wl = workloads.workload(workload)
-    useful = 2.0 * wl.T * wl.n * wl.K * wl.d
+    if kernel == "weights_backward_stream":
+        # two contractions of T x K x d: dhbar = W^T dz and dW = dz hbar^T
+        useful = 4.0 * wl.T * wl.K * wl.d
+        note = ("Two contractions of 16384 tokens x K x d each (dhbar = W^T dz, dW = sum dz hbar^T), "
+                "K = 24 padded to 32.  The split-bf16 operands (hi + lo) make dhbar two products and "
+                "dW three, so the matrix cores execute 3.3x the useful flops (five products of "
+                "32-row tiles for two contractions of 24 rows).  The pass is "
+                "bound by its memory access: a copy of the kernel with both products removed ran at "
+                "the same speed.")
+    else:
+        useful = 2.0 * wl.T * wl.n * wl.K * wl.d
+        note = ("The projection is 24 output columns padded to two 16-column MFMA tiles, so the "
+                "matrix cores do 32/24 of the useful flops.  The kernel is bound by HBM: its flops per "
+                "byte are about 12x below the bf16 MFMA ridge, and the matrix cores idle most of the "
+                "time by design.")
     rec = {"kernel": kernel, "workload": workload, "source_sha": source_sha(kernel),
            "dispatches": len(disp), "active_cycles_per_xcd": round(cycles),
            "duration_us_from_cycles": round(secs * 1e6, 2),
@@ -168,10 +184,7 @@ def summarize_mfma(pmc_csv: str, kernel: str, workload: str, cmds: list):
                   "mfma_flops_per_launch", "useful_flops_per_launch", "mfma_tflops",
                   "mfma_peak_tflops_bf16", "lds_bank_conflict_over_active", "source_sha"):
             fh.write(f"| {k} | {rec[k]} |\n")
-        fh.write("\nThe projection is 24 output columns padded to two 16-column MFMA tiles, so the "
-                 "matrix cores do 32/24 of the useful flops.  The kernel is bound by HBM: its flops per "
-                 "byte are about 12x below the bf16 MFMA ridge, and the matrix cores idle most of the "
-                 "time by design.\n")
+        fh.write("\n" + note + "\n")
     log(f"[bench] wrote {base}.json: MFMA busy {busy:.1%}, {flops / secs / 1e12:.1f} TFLOP/s")
 
 
@@ -219,7 +232,8 @@ def summarize_counters(fetch_csv: str, write_csv: str, kernel: str, workload: st
            "post_pre_mix": tr.post_pre_bytes(wl.n, wl.d, wl.elem_bytes),
            "post_mix_backward": tr.post_bwd_bytes(wl.n, wl.d, wl.elem_bytes),
            "pre_mix_backward": tr.pre_bwd_bytes(wl.n, wl.d, wl.elem_bytes, True),
-           "weights_backward": tr.weights_bwd_bytes(wl.n, wl.d, wl.elem_bytes)}[kernel] * wl.T
+           "weights_backward": tr.weights_bwd_bytes(wl.n, wl.d, wl.elem_bytes),
+           "weights_backward_stream": tr.weights_bwd_stream_bytes(wl.n, wl.d, wl.elem_bytes)}[kernel] * wl.T
     rec = {"kernel": kernel, "workload": workload, "source_sha": source_sha(kernel),
            "dispatches": {"FETCH_SIZE": len(fk), "WRITE_SIZE": len(wk)},
            "fetch_kib_per_dispatch": round(fetch_kib, 3), "write_kib_per_dispatch": round(write_kib, 3),

@@ -417,17 +417,33 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
     }
 }
 
-// out[s][c] = sum of in[r][c] over rows r of segment s (kSumRows rows each),
-// in row order; a thread per column.
-__global__ __launch_bounds__(256) void sum_rows_kernel(const float* __restrict__ in, int64_t rows,
-                                                       int cols, float* __restrict__ out) {
+// One level of a column sum: out[s][c] = sum of in[r][c] over the rows r of
+// segment s (kSumRows rows each), in row order; a thread per column.  The
+// final level of a sum may also clear `zero` (nzero floats: record entries
+// that the gradient leaves at 0).
+struct SumLevel {
+    const float* in;
+    int64_t rows;
+    int cols;
+    float* out;
+    float* zero;
+    int nzero;
+};
+
+// Up to two independent sums per launch (blockIdx.z picks one), so that the
+// short sums of a backward call share launches.
+__global__ __launch_bounds__(256) void sum_rows_kernel(SumLevel a, SumLevel b) {
+    const SumLevel& j = blockIdx.z == 0 ? a : b;
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+        for (int i = threadIdx.x; i < j.nzero; i += 256) j.zero[i] = 0.0f;
     const int64_t r0 = (int64_t)blockIdx.y * kSumRows;
-    const int64_t r1 = r0 + kSumRows < rows ? r0 + kSumRows : rows;
-    for (int c = blockIdx.x * 256 + threadIdx.x; c < cols; c += gridDim.x * 256) {
+    if (r0 >= j.rows) return;
+    const int64_t r1 = r0 + kSumRows < j.rows ? r0 + kSumRows : j.rows;
+    for (int c = blockIdx.x * 256 + threadIdx.x; c < j.cols; c += gridDim.x * 256) {
         float s = 0.0f;
 #pragma unroll 8
-        for (int64_t r = r0; r < r1; ++r) s += in[r * cols + c];
-        out[(int64_t)blockIdx.y * cols + c] = s;
+        for (int64_t r = r0; r < r1; ++r) s += j.in[r * j.cols + c];
+        j.out[(int64_t)blockIdx.y * j.cols + c] = s;
     }
 }
 
@@ -459,16 +475,49 @@ __global__ __launch_bounds__(1024) void sum_records_kernel(const float* __restri
 
 inline dim3 grid_of(int64_t blocks) { return dim3((unsigned)(blocks < kMaxGridB ? blocks : kMaxGridB)); }
 
-// Two-level deterministic column sum: rows -> ceil(rows / 64) segment rows in
-// tmp -> out.  tmp holds ceil(rows / 64) * cols floats.
-hipError_t sum_rows(const float* in, int64_t rows, int cols, float* tmp, float* out, hipStream_t s) {
-    const int64_t segs = (rows + kSumRows - 1) / kSumRows;
-    const dim3 gx((unsigned)((cols + 255) / 256));
-    if (segs <= 1) return launch(sum_rows_kernel, dim3(gx.x, 1), dim3(256), 0, s, in, rows, cols, out);
-    hipError_t e = launch(sum_rows_kernel, dim3(gx.x, (unsigned)segs), dim3(256), 0, s, in, rows, cols, tmp);
-    if (e != hipSuccess) return e;
-    return sum_rows(tmp, segs, cols, tmp + segs * cols, out, s);
+}  // namespace
+
+// Deterministic column sums, up to two at once: every level folds kSumRows
+// rows into one (rows -> ceil(rows / 64) rows in tmp -> ... -> out), so the
+// order depends only on the shapes.  Each job's tmp holds
+// sum_rows_tmp_floats(rows, cols) floats; the jobs' levels share launches.
+hipError_t launch_sum_rows2(const SumJob* jobs, int njobs, hipStream_t s) {
+    SumJob j[2] = {jobs[0], njobs > 1 ? jobs[1] : jobs[0]};
+    bool done[2] = {false, njobs < 2};
+    while (!(done[0] && done[1])) {
+        SumLevel lv[2];
+        int idx[2], nz = 0;
+        unsigned gx = 1, gy = 1;
+        for (int k = 0; k < 2; ++k) {
+            if (done[k]) continue;
+            const int64_t segs = (j[k].rows + kSumRows - 1) / kSumRows;
+            const bool last = segs <= 1;
+            lv[nz] = {j[k].in, j[k].rows, j[k].cols, last ? j[k].out : j[k].tmp,
+                      last ? j[k].zero : nullptr, last ? j[k].nzero : 0};
+            idx[nz++] = k;
+            const unsigned x = (unsigned)((j[k].cols + 255) / 256), y = (unsigned)(segs > 1 ? segs : 1);
+            gx = x > gx ? x : gx;
+            gy = y > gy ? y : gy;
+        }
+        hipError_t e = launch(sum_rows_kernel, dim3(gx, gy, (unsigned)nz), dim3(256), 0, s, lv[0],
+                              nz > 1 ? lv[1] : lv[0]);
+        if (e != hipSuccess) return e;
+        for (int q = 0; q < nz; ++q) {
+            SumJob& x = j[idx[q]];
+            const int64_t segs = (x.rows + kSumRows - 1) / kSumRows;
+            if (segs <= 1) {
+                done[idx[q]] = true;
+            } else {
+                x.in = x.tmp;
+                x.rows = segs;
+                x.tmp += segs * x.cols;
+            }
+        }
+    }
+    return hipSuccess;
 }
+
+namespace {
 
 template <int N, typename S, int VPT>
 hipError_t post_bwd_go(RowCfg c, const void* dHo, const void* H, const void* F, const float* w,
@@ -554,19 +603,18 @@ hipError_t pre_bwd_n(int n, A... a) {
 //   tmp         second-level rows of either sum (ceil(rows / 64) * max(d, M),
 //               plus a third level, bounded by 2 * ceil(rows / 64) * max(d, M))
 struct BwdSpace {
-    int64_t rows, dg, rec, tmp, total;   // offsets and total, in floats
+    int64_t rows, dg, rec, tmp, tmp2, total;   // offsets and total, in floats
 };
 inline BwdSpace bwd_space(int64_t T, int n, int d) {
     BwdSpace b;
     const int64_t g = group_of(T);
     b.rows = (T + g - 1) / g;
     const int64_t M = n + int64_t(n) * n;
-    const int64_t segs = (b.rows + kSumRows - 1) / kSumRows;
-    const int64_t wide = d > M ? d : M;
     b.dg = 0;
     b.rec = b.rows * d;
-    b.tmp = b.rec + b.rows * M;
-    b.total = b.tmp + 2 * (segs + 1) * wide;
+    b.tmp = b.rec + b.rows * M;                           // the dgamma sum's levels
+    b.tmp2 = b.tmp + sum_rows_tmp_floats(b.rows, d);      // the record sum's levels
+    b.total = b.tmp2 + sum_rows_tmp_floats(b.rows, M);
     return b;
 }
 
@@ -592,10 +640,8 @@ hipError_t launch_post_mix_backward(const void* dHo, const void* H, const void* 
     if (e != hipSuccess || w_stride != 0) return e;
     // shared record: dw = [0 (dalpha) | sum of the block partials]
     const int M = n + n * n;
-    e = launch(sum_rows_kernel, dim3(1, 1), dim3(256), 0, s, static_cast<const float*>(ws), int64_t(0),
-               n, dw);   // zero rows: writes dalpha = 0
-    if (e != hipSuccess) return e;
-    return sum_rows(part, sp.rows, M, ws + sp.tmp, dw + n, s);
+    const SumJob job = {part, sp.rows, M, ws + sp.tmp2, dw + n, dw, n};
+    return launch_sum_rows2(&job, 1, s);
 }
 
 hipError_t launch_pre_mix_backward(const void* du, const void* H, const float* w, int64_t w_stride,
@@ -613,14 +659,12 @@ hipError_t launch_pre_mix_backward(const void* du, const void* H, const float* w
                 : pre_bwd_n<bf16_t>(n, row_config(d / Store<bf16_t>::kElems), du, H, w, w_stride,
                                     gamma, eps, dH_in, dH, dw, dg_part, da_part, T, d, group, s);
     if (e != hipSuccess) return e;
-    e = sum_rows(dg_part, sp.rows, d, ws + sp.tmp, dgamma, s);
-    if (e != hipSuccess || w_stride != 0) return e;
-    // shared record: dw = [sum of the dalpha partials | 0 (dbeta, dA)]
+    // dgamma; with a shared record also dw = [sum of the dalpha partials |
+    // 0 (dbeta, dA)], in the same launches
     const int K = 2 * n + n * n;
-    e = sum_rows(da_part, sp.rows, n, ws + sp.tmp, dw, s);
-    if (e != hipSuccess) return e;
-    return launch(sum_rows_kernel, dim3(1, 1), dim3(256), 0, s, static_cast<const float*>(ws),
-                  int64_t(0), K - n, dw + n);   // zero rows: writes 0
+    const SumJob jobs[2] = {{dg_part, sp.rows, d, ws + sp.tmp, dgamma, nullptr, 0},
+                            {da_part, sp.rows, n, ws + sp.tmp2, dw, dw + n, K - n}};
+    return launch_sum_rows2(jobs, w_stride != 0 ? 1 : 2, s);
 }
 
 int64_t sum_rows_tmp_floats(int64_t rows, int64_t cols) {
@@ -628,10 +672,6 @@ int64_t sum_rows_tmp_floats(int64_t rows, int64_t cols) {
     return 2 * (segs + 1) * cols;
 }
 
-hipError_t launch_sum_rows(const float* in, int64_t rows, int cols, float* tmp, float* out,
-                           hipStream_t s) {
-    return sum_rows(in, rows, cols, tmp, out, s);
-}
 
 hipError_t launch_sum_records(const float* rec, int64_t T, int K, float* out, hipStream_t s) {
     return launch(sum_records_kernel, dim3(K), dim3(1024), 0, s, rec, T, K, out);

@@ -70,8 +70,20 @@ hipError_t launch_weights_save(const void* H, const void* W, const float* w_stat
 int64_t saved_r_offset(int64_t T, int n);
 int64_t saved_floats(int64_t T, int n);
 int64_t sum_rows_tmp_floats(int64_t rows, int64_t cols);
-hipError_t launch_sum_rows(const float* in, int64_t rows, int cols, float* tmp, float* out,
-                           hipStream_t s);
+// A deterministic column sum: out[c] = sum over r of in[r * cols + c], in a
+// fixed order of levels (tmp: sum_rows_tmp_floats(rows, cols) floats); the
+// last level also writes nzero zeros at `zero` (may be NULL).
+struct SumJob {
+    const float* in;
+    int64_t rows;
+    int cols;
+    float* tmp;
+    float* out;
+    float* zero;
+    int nzero;
+};
+// One or two independent sums; their levels share launches.
+hipError_t launch_sum_rows2(const SumJob* jobs, int njobs, hipStream_t s);
 int64_t weights_backward_workspace_bytes(int64_t T, int n, int d, int iters);
 int64_t sinkhorn_backward_workspace_bytes(int64_t T, int iters);
 hipError_t launch_weights_backward(const void* H, const void* W, const float* w_static, float scale,

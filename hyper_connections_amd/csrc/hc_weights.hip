@@ -36,6 +36,8 @@
 //  - Epilogue through LDS (the wave's transpose buffer): the C tile and the
 //    row sums of squares are combined per token, then tanh or the mHC
 //    transform, then stored.
+#include <type_traits>
+
 #include "hc_device.h"
 #include "hc_launch.h"
 
@@ -258,6 +260,22 @@ __global__ __launch_bounds__(kWThreads) void weights_kernel(
         const int lrow = lane >> 4, lpiece = lane & 15;
         for (int c = 0; c < nchunks; ++c) {
             const int k0 = c * KC;
+            // fp32 inputs: the chunk's own sums, added to the running ones at
+            // its end.  Its MFMA adds 4 products per step (against 32 for
+            // bf16 and FP8), so one running sum over a 16384-wide row would
+            // take 4096 roundings; the two-level order keeps the error near
+            // that of a 128-wide row.  (For bf16 and FP8 the single sum is
+            // within the records' tolerance, and the extra registers cost
+            // FP8 a wave per SIMD.)
+            constexpr bool kTwoLevel = std::is_same<S, f32_t>::value;
+            f32x4 cacc[NT];
+            float css = 0.0f;
+            if constexpr (kTwoLevel) {
+#pragma unroll
+                for (int q = 0; q < NT; ++q) cacc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            f32x4* const sum = kTwoLevel ? cacc : acc;
+            float& sq = kTwoLevel ? css : ss;
             // W chunk pieces first (L2 hits), so that storing them to LDS waits
             // only for these loads and not for the stream loads behind them
             constexpr int WP = (K * G::PIECES + kWThreads - 1) / kWThreads;
@@ -309,17 +327,22 @@ __global__ __launch_bounds__(kWThreads) void weights_kernel(
                     float f[V];
                     unpack<S>(av, f);
 #pragma unroll
-                    for (int e = 0; e < V; ++e) ss = fmaf(f[e], f[e], ss);
+                    for (int e = 0; e < V; ++e) sq = fmaf(f[e], f[e], sq);
                     const int kb = h * KH + sl * 16;                 // byte offset in the chunk
 #pragma unroll
                     for (int q = 0; q < NT; ++q) {
                         const uint4 bv = *reinterpret_cast<const uint4*>(wlds + (q * 16 + rho) * G::RS + kb);
-                        acc[q] = Mfma<S>::step(av, bv, acc[q]);
+                        sum[q] = Mfma<S>::step(av, bv, sum[q]);
                     }
                 }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+            if constexpr (kTwoLevel) {
+#pragma unroll
+                for (int q = 0; q < NT; ++q) acc[q] += cacc[q];
+                ss += css;
             }
         }
 

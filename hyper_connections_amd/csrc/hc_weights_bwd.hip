@@ -15,9 +15,9 @@
 //   dw_static = sum over tokens of dw (tanh) or dl (mHC).
 // Passes: (1) the forward projection again, keeping P_i and r_i per token
 // (hc_weights.hip, raw mode); (2) one thread per token turns them and dw
-// into dz, a_i, b_i (and dl); (3) one streaming pass over H computes dH and
-// partial sums of dW on the matrix cores; (4) fixed-order sums of the
-// partials.  Everything is deterministic.
+// into dz, a_i, b_i and per-workgroup partial sums of dw_static; (3) one
+// streaming pass over H computes dH and partial sums of dW on the matrix
+// cores; (4) fixed-order sums of the partials.  Everything is deterministic.
 #include <type_traits>
 
 #include "hc_device.h"
@@ -42,14 +42,27 @@ constexpr int kSlot = 16;      // floats per token per iteration in the Sinkhorn
 // iterations are then undone in reverse:
 //   column step C = R / colsum:  dR_ij = (dC_ij - sum_i' dC_i'j C_i'j) / colsum_j
 //   row step    R = M / rowsum:  dM_ij = (dR_ij - sum_j' dR_ij' R_ij') / rowsum_i
+// The derivatives of sigmoid and tanh, written without the cancellation of
+// s (1 - s) and 1 - tanh^2 where the function saturates (there 1 - s and
+// 1 - tanh^2 are tiny differences of numbers near 1; in fp32 they lose most
+// of their digits past |x| ~ 5): with e = exp(-|x|),
+//   sigmoid'(x) = e / (1 + e)^2,   tanh'(x) = 4 e^2 / (1 + e^2)^2.
+__device__ __forceinline__ float dsigmoid(float x) {
+    const float e = expf(-fabsf(x));
+    const float q = 1.0f + e;
+    return e / (q * q);
+}
+__device__ __forceinline__ float dtanh(float x) {
+    const float e = expf(-2.0f * fabsf(x));
+    const float q = 1.0f + e;
+    return 4.0f * e / (q * q);
+}
+
 template <int N>
 __device__ void mhc_record_bwd(const float* l, const float* g, float* dl, int iters, float* scr,
                                int64_t stride) {
     constexpr int NN = N * N;
-    for (int i = 0; i < 2 * N; ++i) {
-        const float s = 1.0f / (1.0f + expf(-l[i]));
-        dl[i] = g[i] * s * (1.0f - s);
-    }
+    for (int i = 0; i < 2 * N; ++i) dl[i] = g[i] * dsigmoid(l[i]);
     float M[NN], M0[NN];
     float m = 0.0f;
     if (iters > 0) {
@@ -151,15 +164,20 @@ __global__ __launch_bounds__(256) void sinkhorn_bwd_kernel(const float* __restri
 
 // From P [T][N][K], r [T][N] (the forward projection pass) and dw [T][K]
 // (plus dw2 when given: the records' gradient from a second consumer):
-// dz [T][K], dl [T][K] (the gradient at the logits / records that
-// w_static receives) and ab [T][2][N] = (a_i, b_i).  One thread per token.
+// dz [T][K], ab [T][2][N] = (a_i, b_i), and per workgroup the sum over its
+// tokens of dl (the gradient at the logits / records that w_static
+// receives): dl_part [workgroup][K].  One thread per token, one wave per
+// workgroup.
 template <int N>
 __global__ __launch_bounds__(256) void wgrad_coef_kernel(
     const float* __restrict__ P, const float* __restrict__ r, const float* __restrict__ dw,
     const float* __restrict__ dw2, const float* __restrict__ w_static, float scale, int iters,
     float* __restrict__ scr,
-    float* __restrict__ dz, float* __restrict__ dl, float* __restrict__ ab, int64_t T, int d) {
+    float* __restrict__ dz, float* __restrict__ dl_part, float* __restrict__ ab, int64_t T, int d) {
     constexpr int K = 2 * N + N * N;
+    float dls[K];
+#pragma unroll
+    for (int c = 0; c < K; ++c) dls[c] = 0.0f;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < T;
          t += (int64_t)gridDim.x * blockDim.x) {
         const float* p = P + t * N * K;
@@ -179,9 +197,8 @@ __global__ __launch_bounds__(256) void wgrad_coef_kernel(
         if (iters == 0) {
 #pragma unroll
             for (int c = 0; c < K; ++c) {
-                const float th = tanhf(z[c]);
                 gl[c] = g[c];
-                gz[c] = g[c] * scale * (1.0f - th * th);
+                gz[c] = g[c] * scale * dtanh(z[c]);
             }
         } else {
             float l[K];
@@ -194,7 +211,7 @@ __global__ __launch_bounds__(256) void wgrad_coef_kernel(
 #pragma unroll
         for (int c = 0; c < K; ++c) {
             dz[t * K + c] = gz[c];
-            dl[t * K + c] = gl[c];
+            dls[c] += gl[c];
         }
 #pragma unroll
         for (int i = 0; i < N; ++i) {
@@ -204,6 +221,12 @@ __global__ __launch_bounds__(256) void wgrad_coef_kernel(
             ab[t * 2 * N + i] = ri[i] / (float)N;
             ab[t * 2 * N + N + i] = -(ri[i] * ri[i] * ri[i]) * s / ((float)N * (float)d);
         }
+    }
+    // this wave's share of dw_static (the workgroup is one wave)
+#pragma unroll
+    for (int c = 0; c < K; ++c) {
+        const float v = wave_sum(dls[c]);
+        if (threadIdx.x == 0) dl_part[(int64_t)blockIdx.x * K + c] = v;
     }
 }
 
@@ -545,14 +568,18 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(
     }
 }
 
+inline int64_t coef_blocks(int64_t T) {
+    const int64_t b = (T + 63) / 64;
+    return b < kMaxGrid ? b : kMaxGrid;
+}
+
 template <int N>
 hipError_t coef_go(const float* P, const float* r, const float* dw, const float* dw2, const float* ws,
-                   float scale, int iters, float* scr, float* dz, float* dl, float* ab, int64_t T,
+                   float scale, int iters, float* scr, float* dz, float* dl_part, float* ab, int64_t T,
                    int d, hipStream_t s) {
     // one wave per workgroup: 16384 tokens still reach every CU
-    const int64_t blocks = (T + 63) / 64;
-    return launch(wgrad_coef_kernel<N>, dim3((unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid)),
-                  dim3(64), 0, s, P, r, dw, dw2, ws, scale, iters, scr, dz, dl, ab, T, d);
+    return launch(wgrad_coef_kernel<N>, dim3((unsigned)coef_blocks(T)), dim3(64), 0, s, P, r, dw, dw2,
+                  ws, scale, iters, scr, dz, dl_part, ab, T, d);
 }
 
 template <int N, typename S>
@@ -592,11 +619,12 @@ inline int64_t splits_of(int64_t T) {
     return s < 1 ? 1 : s;
 }
 
-// Workspace layout (floats): P [T][n][K] | r [T][n] | dz [T][K] | dl [T][K] |
-// ab [T][2n] | Sinkhorn scratch [iters][T][16] | dW partials [4 splits][K][d] |
-// sum scratch.  Every region starts 16-byte aligned.
+// Workspace layout (floats): P [T][n][K] | r [T][n] | dz [T][K] |
+// dw_static partials [coefficient workgroups][K] | ab [T][2n] | Sinkhorn
+// scratch [iters][T][16] | dW partials [4 splits][K][d] | the two sums'
+// level scratch.  Every region starts 16-byte aligned.
 struct WgSpace {
-    int64_t P, r, dz, dl, ab, scr, part, tmp, total;
+    int64_t P, r, dz, dl, ab, scr, part, tmp, tmp2, total;
 };
 inline int64_t up4(int64_t x) { return (x + 3) / 4 * 4; }
 inline WgSpace wg_space(int64_t T, int n, int d, int iters) {
@@ -606,12 +634,13 @@ inline WgSpace wg_space(int64_t T, int n, int d, int iters) {
     w.r = w.P + up4(T * n * K);
     w.dz = w.r + up4(T * n);
     w.dl = w.dz + up4(T * K);
-    w.ab = w.dl + up4(T * K);
+    w.ab = w.dl + up4(coef_blocks(T) * K);
     w.scr = w.ab + up4(T * 2 * n);
     w.part = w.scr + up4(int64_t(iters) * T * kSlot);
     const int64_t rows = splits_of(T) * 4;
     w.tmp = w.part + up4(rows * K * d);
-    w.total = w.tmp + sum_rows_tmp_floats(rows, K * d);
+    w.tmp2 = w.tmp + up4(sum_rows_tmp_floats(rows, K * d));
+    w.total = w.tmp2 + up4(sum_rows_tmp_floats(coef_blocks(T), K));
     return w;
 }
 
@@ -681,10 +710,11 @@ hipError_t launch_weights_backward(const void* H, const void* W, const float* w_
                 : stream_by_n<bf16_t>(n, H, W, ws + sp.dz, ws + sp.ab, rp, dH_in, dH,
                                       ws + sp.part, T, d, (int)splits, tps, s);
     if (e != hipSuccess) return e;
-    // (4) fixed-order sums: dW over the partials, dw_static over the tokens
-    e = launch_sum_rows(ws + sp.part, splits * 4, K * d, ws + sp.tmp, dW, s);
-    if (e != hipSuccess) return e;
-    return launch_sum_records(ws + sp.dl, T, K, dws, s);
+    // (4) fixed-order sums: dW over the partials, dw_static over the
+    // coefficient workgroups' partials, in shared launches
+    const SumJob jobs[2] = {{ws + sp.part, splits * 4, K * d, ws + sp.tmp, dW, nullptr, 0},
+                           {ws + sp.dl, coef_blocks(T), K, ws + sp.tmp2, dws, nullptr, 0}};
+    return launch_sum_rows2(jobs, 2, s);
 }
 
 }  // namespace hc

@@ -72,3 +72,10 @@ def weights_bwd_bytes(n: int, d: int, s: int) -> int:
     the forward kept (n (K + 1) floats per token), or recomputed with a second
     read of H when it kept nothing."""
     return 3 * n * d * s + 2 * record_bytes(n)
+
+
+def weights_bwd_stream_bytes(n: int, d: int, s: int) -> int:
+    """The streaming pass of the weights gradient alone: read H and the
+    incoming dH, write dH (the per-token coefficients it reads, K + 2n floats,
+    are not counted)."""
+    return 3 * n * d * s

@@ -30,10 +30,11 @@ def record_check(got: np.ndarray, ref: np.ndarray, what: str):
     return e
 
 
-# d: one partial chunk, exact chunks, a ragged last chunk; T: partial tiles
+# d: one partial chunk, exact chunks, a ragged last chunk, the largest; T: partial tiles
 @pytest.mark.parametrize("dt,d", [("bf16", 8), ("bf16", 264), ("bf16", 4096), ("bf16", 6152),
-                                  ("f32", 4), ("f32", 132), ("f32", 1024),
-                                  ("fp8", 16), ("fp8", 528), ("fp8", 4096), ("fp8", 6160)])
+                                  ("bf16", 16384), ("f32", 4), ("f32", 132), ("f32", 1024),
+                                  ("f32", 16384), ("fp8", 16), ("fp8", 528), ("fp8", 4096),
+                                  ("fp8", 6160), ("fp8", 16384)])
 @pytest.mark.parametrize("n", [1, 2, 3, 4])
 @pytest.mark.parametrize("iters", [0, 5])
 def test_weights_parity(dt, d, n, iters):

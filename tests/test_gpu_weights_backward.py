@@ -41,10 +41,10 @@ def case(rng, dt, T, n, d, wsd=0.05):
     return H, W, ws, dw
 
 
-# d: a single column group, ragged groups, the workload width; T: one token,
+# d: a single column group, ragged groups, the workload width, the largest; T: one token,
 # partial tiles, several dW splits
-@pytest.mark.parametrize("dt,d", [("bf16", 8), ("bf16", 264), ("bf16", 4096), ("f32", 4),
-                                  ("f32", 132), ("f32", 1024)])
+@pytest.mark.parametrize("dt,d", [("bf16", 8), ("bf16", 264), ("bf16", 4096), ("bf16", 16384),
+                                  ("f32", 4), ("f32", 132), ("f32", 1024), ("f32", 16384)])
 @pytest.mark.parametrize("n", [1, 2, 3, 4])
 @pytest.mark.parametrize("iters", [0, 5])
 def test_weights_backward_parity(dt, d, n, iters):
@@ -162,3 +162,26 @@ def test_weights_backward_with_saved_state(dt, d, n, iters):
     b = hc.weights_backward(Hd, Wd, wsd, 0.3, dwd, 1e-6, iters, saved=saved)
     for x, y in zip(a, b):
         assert np.array_equal(host(x), host(y))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("n", [1, 4])
+def test_weights_backward_saturated_tanh(dt, n):
+    """Projections of several units (|z| up to ~11): tanh saturates and its
+    derivative is a tiny number that 1 - tanh^2 would lose in fp32 (errors of
+    ~0.5%); whole tokens then carry only such terms.  bf16 rows are held to one
+    ulp.  fp32 rows to 1e-4: at |z| ~ 10 the derivative 4 e^(-2|z|) turns an
+    absolute error dz of z into a relative error 2 |z| dz, and fp32 forms z
+    (a sum over d of products of size ~|z|) to a few 1e-7 of |z|."""
+    rng = np.random.default_rng(77 + n)
+    T, d = 64, 1024
+    H, W, ws, dw = case(rng, dt, T, n, d, wsd=0.15 * np.sqrt(n))
+    dH, dW, dws = hc.weights_backward(dev(H), dev(W), dev(ws), 0.5, dev(dw))
+    rdH, rdW, rdws = oracle.weights_backward(H, W, ws.astype(np.float64), 0.5, dw.astype(np.float64))
+    if dt == "bf16":
+        check(host(dH), rdH, f"saturated dH n={n} {dt}")
+    else:
+        e = rel_err(host(dH), rdH)
+        assert e <= 1e-4, f"saturated dH n={n} {dt}: {e:.3g} > 1e-4"
+    grad_check(host(dW), rdW, f"saturated dW n={n} {dt}")
+    grad_check(host(dws)[None], rdws[None], f"saturated dw_static n={n} {dt}")
