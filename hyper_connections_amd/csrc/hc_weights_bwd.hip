@@ -13,8 +13,9 @@
 //   dW += dz hbar^T,   dhbar = W^T dz,   s_i = H_i . dhbar = P_i . dz  (P_i = W H_i)
 //   dH_i = a_i dhbar + b_i H_i,  a_i = r_i / n,  b_i = -r_i^3 s_i / (n d)
 //   dw_static = sum over tokens of dw (tanh) or dl (mHC).
-// Passes: (1) the forward projection again, keeping P_i and r_i per token
-// (hc_weights.hip, raw mode); (2) one thread per token turns them and dw
+// Passes: (1) P_i and r_i per token: kept by the training forward
+// (hc_weights_save), or the forward projection again (hc_weights.hip, raw
+// mode); (2) one thread per token turns them and dw
 // into dz, a_i, b_i and per-workgroup partial sums of dw_static; (3) one
 // streaming pass over H computes dH and partial sums of dW on the matrix
 // cores; (4) fixed-order sums of the partials.  Everything is deterministic.
@@ -397,6 +398,8 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(
     const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, const float* __restrict__ dz,
     const float* __restrict__ ab, const float* __restrict__ r, const uint8_t* dH_in,
     uint8_t* dH, float* __restrict__ part, int64_t T, int d, int64_t tok_per_split) {
+    // the fp32 kernel's signature: this one takes hbar's weights from ab (a_i =
+    // r_i / n) and deals its steps round robin, so r and the split size go unused
     (void)r;
     (void)tok_per_split;
     constexpr int K = 2 * N + N * N;                 // <= 24

@@ -74,8 +74,8 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
-                f"{LIB_PATH} is not built: run `python -m hyper_connections_amd.build` "
-                "(or __graft_entry__.build()); there is no CPU fallback")
+                f"{LIB_PATH} is not built: run `python -m hyper_connections_amd.build`; "
+                "there is no CPU fallback")
         L = ctypes.CDLL(LIB_PATH)
         for name, args in _SIGS.items():
             f = getattr(L, name)
