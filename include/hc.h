@@ -133,11 +133,13 @@ hc_status hc_weights(const void* H, const void* W, const float* w_static, float 
  * T*n*K rounded up to a multiple of 4). */
 int64_t hc_weights_saved_bytes(int64_t T, int32_t n);
 
-/* hc_weights for a training forward: the same records in w_out (bitwise the
- * same as hc_weights), and in `saved` (saved_bytes >= hc_weights_saved_bytes,
- * 16-byte aligned, no overlap with anything) the projections and norms that
- * hc_weights_backward would otherwise recompute with a second read of H.
- * Arguments otherwise as hc_weights. */
+/* hc_weights for a training forward ([GLOSS] definition: the weight
+ * producers are learned, so their backward needs the forward's state): the
+ * same records in w_out (bitwise the same as hc_weights), and in `saved`
+ * (saved_bytes >= hc_weights_saved_bytes, 16-byte aligned, no overlap with
+ * anything) the projections and norms that hc_weights_backward would
+ * otherwise recompute with a second read of H.  Arguments and errors
+ * otherwise as hc_weights; a short `saved` is HC_ERR_ARG. */
 hc_status hc_weights_save(const void* H, const void* W, const float* w_static, float scale,
                           float eps, int32_t sinkhorn_iters, float* w_out, float* saved,
                           int64_t saved_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
