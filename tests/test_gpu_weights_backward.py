@@ -113,13 +113,19 @@ def test_sinkhorn_backward_parity(n, iters):
 def test_dynamic_workload_backward_full_size():
     """T=16384, n=4, d=4096 bf16 (the dynamic workload): dH on 64 sampled
     tokens against the oracle; dW and dw_static of the first 1024 tokens (a
-    separate call, the same kernels) against the oracle."""
+    separate call, the same kernels) against the oracle; the benchmark's form
+    (projections kept by hc_weights_save) bitwise equal to the recomputing one."""
     wl = workload("dynamic-bf16")
     inp = make_inputs(wl)
     rng = np.random.default_rng(41)
     dw = (rng.standard_normal((wl.T, wl.K)) * 0.1).astype(np.float32)
     Hd, Wd, wsd = dev(inp["H"]), dev(inp["W"]), dev(inp["w_static"])
     dH, dW, dws = hc.weights_backward(Hd, Wd, wsd, wl.scale, dev(dw), wl.eps)
+    # the benchmark's launch: the projections kept by the training forward
+    _, saved = hc.weights_save(Hd, Wd, wsd, wl.scale, wl.eps, 0)
+    dHs, dWs, dwss = hc.weights_backward(Hd, Wd, wsd, wl.scale, dev(dw), wl.eps, saved=saved)
+    assert torch.equal(dH, dHs) and torch.equal(dW, dWs) and torch.equal(dws, dwss)
+    del dHs, dWs, dwss, saved
     torch.cuda.synchronize()
     idx = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 64, replace=False)]))
     sub = make_inputs(wl, tokens=idx)
