@@ -57,10 +57,19 @@ __device__ __forceinline__ void block_sum_vec(float (&v)[M], float* red) {
 }
 
 // Tokens per block for shared-record gradients: enough blocks to fill the
-// chip several times over, at least 8 tokens each.
+// chip several times over, at least 8 tokens each (pre: its per-block
+// partials include a d-wide dgamma row).
 inline int64_t group_of(int64_t T) {
     const int64_t g = T / 2048;
     return g < 8 ? 8 : g;
+}
+// Post's partials are only n + n^2 floats per block, so it takes fewer
+// tokens per block: about 4096 blocks, at least 2 tokens each (measured at
+// T = 8192: 2 tokens per block 176 us, 4 179 us, 8 183 us, 16 186 us, and
+// 1 token per block 196 us with its longer sum).
+inline int64_t post_group_of(int64_t T) {
+    const int64_t g = T / 4096;
+    return g < 2 ? 2 : g;
 }
 
 // ------------------------------------------------------------ post backward
@@ -603,7 +612,7 @@ hipError_t pre_bwd_n(int n, A... a) {
 //   tmp         second-level rows of either sum (ceil(rows / 64) * max(d, M),
 //               plus a third level, bounded by 2 * ceil(rows / 64) * max(d, M))
 struct BwdSpace {
-    int64_t rows, dg, rec, tmp, tmp2, total;   // offsets and total, in floats
+    int64_t rows, prows, dg, rec, tmp, tmp2, total;   // offsets and total, in floats
 };
 inline BwdSpace bwd_space(int64_t T, int n, int d) {
     BwdSpace b;
@@ -612,9 +621,12 @@ inline BwdSpace bwd_space(int64_t T, int n, int d) {
     const int64_t M = n + int64_t(n) * n;
     b.dg = 0;
     b.rec = b.rows * d;
-    b.tmp = b.rec + b.rows * M;                           // the dgamma sum's levels
-    b.tmp2 = b.tmp + sum_rows_tmp_floats(b.rows, d);      // the record sum's levels
-    b.total = b.tmp2 + sum_rows_tmp_floats(b.rows, M);
+    const int64_t pg = post_group_of(T);
+    b.prows = (T + pg - 1) / pg;                          // post's partial records
+    const int64_t rr = b.prows > b.rows ? b.prows : b.rows;
+    b.tmp = b.rec + rr * M;                               // the dgamma sum's levels
+    b.tmp2 = b.tmp + sum_rows_tmp_floats(b.rows, d);      // the record sums' levels
+    b.total = b.tmp2 + sum_rows_tmp_floats(rr, M);
     return b;
 }
 
@@ -630,7 +642,7 @@ hipError_t launch_post_mix_backward(const void* dHo, const void* H, const void* 
                                     int64_t T, int n, int d, int dt, hipStream_t s) {
     const BwdSpace sp = bwd_space(T, n, d);
     float* ws = static_cast<float*>(work);
-    const int group = w_stride != 0 ? 1 : (int)group_of(T);
+    const int group = w_stride != 0 ? 1 : (int)post_group_of(T);
     float* part = w_stride != 0 ? nullptr : ws + sp.rec;
     hipError_t e =
         dt == 0 ? post_bwd_n<f32_t>(n, row_config(d / Store<f32_t>::kElems), dHo, H, F, w, w_stride,
@@ -640,7 +652,7 @@ hipError_t launch_post_mix_backward(const void* dHo, const void* H, const void* 
     if (e != hipSuccess || w_stride != 0) return e;
     // shared record: dw = [0 (dalpha) | sum of the block partials]
     const int M = n + n * n;
-    const SumJob job = {part, sp.rows, M, ws + sp.tmp2, dw + n, dw, n};
+    const SumJob job = {part, sp.prows, M, ws + sp.tmp2, dw + n, dw, n};
     return launch_sum_rows2(&job, 1, s);
 }
 
