@@ -1,0 +1,81 @@
+"""The backward calls inside a HIP graph (torch.cuda.CUDAGraph around the
+library's launches): a layer's gradients -- post, pre accumulating into the
+same dH, and the weight producer's -- captured once and replayed, with the
+outputs and workspaces overwritten by eager work before every replay, so each
+replay must rewrite everything it produces.  Every replay equals the eager
+calls bitwise (the library enqueues kernels only: no memsets, no host work)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import dev, host, need_gpu
+from hyper_connections_amd import hc
+from hyper_connections_amd.workloads import f32_to_bf16_bits, identity_record
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def bf16(rng, shape, sd=1.0):
+    return dev(f32_to_bf16_bits((sd * rng.standard_normal(shape)).astype(np.float32)))
+
+
+@pytest.mark.parametrize("records", ["shared", "per-token"])
+def test_backward_graph_replays_equal_eager(records):
+    rng = np.random.default_rng(5 if records == "shared" else 6)
+    T, n, d = 300, 4, 1024
+    K = 2 * n + n * n
+    H, F = bf16(rng, (T, n, d)), bf16(rng, (T, d))
+    dHo, du = bf16(rng, (T, n, d)), bf16(rng, (T, d))
+    gamma = dev((1 + 0.1 * rng.standard_normal(d)).astype(np.float32))
+    ws = dev((identity_record(n) + 0.05 * rng.standard_normal(K)).astype(np.float32))
+    W = bf16(rng, (K, d), 0.02)
+    per_token = records == "per-token"
+    if per_token:
+        w, saved = hc.weights_save(H, W, ws, 0.01, 1e-6, 0)
+        dwp = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        dwq = torch.empty_like(dwp)
+    else:
+        w, saved = ws, None
+        dwp = torch.empty(K, dtype=torch.float32, device="cuda")
+        dwq = torch.empty_like(dwp)
+    dH = torch.empty_like(H)
+    dF = torch.empty_like(F)
+    dg = torch.empty(d, dtype=torch.float32, device="cuda")
+    dW = torch.empty((K, d), dtype=torch.float32, device="cuda")
+    dws = torch.empty(K, dtype=torch.float32, device="cuda")
+    wk = torch.empty(int(hc.lib().hc_backward_workspace(T, n, d)), dtype=torch.uint8, device="cuda")
+    wwk = torch.empty(int(hc.lib().hc_weights_backward_workspace(T, n, d, 0)), dtype=torch.uint8,
+                      device="cuda")
+    outs = [dH, dF, dg, dwp, dwq, dW, dws]
+
+    def step():
+        hc.post_mix_backward(dHo, H, F, w, dH=dH, dF=dF, dw=dwp, workspace=wk)
+        hc.pre_mix_backward(du, H, w, gamma, 1e-6, dH_in=dH, out=dH, dw=dwq, dgamma=dg, workspace=wk)
+        if per_token:
+            hc.weights_backward(H, W, ws, 0.01, dwp, 1e-6, 0, dH_in=dH, out=dH, dW=dW,
+                                dw_static=dws, workspace=wwk, dw2=dwq, saved=saved)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [host(t) for t in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        wk.fill_(0xFF)
+        wwk.fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, t in zip(["dH", "dF", "dgamma", "dw post", "dw pre", "dW", "dw_static"],
+                              eager, outs):
+            if per_token or name not in ("dW", "dw_static"):
+                assert np.array_equal(host(t), a, equal_nan=True), f"replay {rep}: {name} differs"
+        _ = (H.float() * 2).sum().item()   # eager work between replays
