@@ -7,6 +7,7 @@
  *           Identity Hyper-Connections -- What does it mean?"
  *   [GLOSS] hfviewer.com glossary entry "Hyper-connections (mHC)"
  *   [ATLAS] llm-atlas model card "Tencent Hy4-preview (770B-A49B)"
+ *   [MAP]   models.inteligile.com, "Hy4-preview" model techniques map
  *
  * The residual stream is widened to n parallel streams that a block reads
  * from and writes to separately ([EXPL] "Jargon", Hyper-Connections); learned
@@ -75,9 +76,9 @@ typedef enum hc_status {
  * 3 mantissa bits, no infinities, largest finite 448).  The release ships
  * BF16 and FP8 weights ([EXPL] "The news"; [MAP] "inference quantization");
  * the pages name no 8-bit format, E4M3 is the one implemented.  FP8 is taken
- * by hc_pre_mix, hc_post_mix, hc_post_pre_mix, hc_weights (H and W in FP8,
- * fp32 accumulation) and hc_block_tanh; the gradient calls (the *_backward
- * entry points) return HC_ERR_DTYPE for it. */
+ * by hc_pre_mix, hc_post_mix, hc_post_pre_mix, hc_weights and hc_weights_save
+ * (H and W in FP8, fp32 accumulation) and hc_block_tanh; the gradient calls
+ * (the *_backward entry points) return HC_ERR_DTYPE for it. */
 typedef enum hc_dtype { HC_F32 = 0, HC_BF16 = 1, HC_FP8 = 2 } hc_dtype;
 
 #define HC_MAX_STREAMS 4
