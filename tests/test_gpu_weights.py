@@ -196,3 +196,37 @@ def test_weights_save_records_equal_weights(dt, d, n, iters):
     r = host(saved)[off:off + T * n].reshape(T, n).astype(np.float64)
     Hw = oracle.widen(H)
     np.testing.assert_allclose(r, 1 / np.sqrt((Hw * Hw).mean(axis=2) + 1e-6), rtol=1e-5)
+
+
+@pytest.mark.parametrize("name", ["dynamic-bf16", "dynamic-fp8"])
+def test_dynamic_workload_full_size_every_token(name):
+    """T=16384, n=4, d=4096: every token's record against the oracle, then
+    pre and post on the GPU's records, in chunks of 2048 tokens."""
+    wl = workload(name)
+    inp = make_inputs(wl)
+    Hd, Fd, gd = dev(inp["H"]), dev(inp["F"]), dev(inp["gamma"])
+    w = hc.weights(Hd, dev(inp["W"]), dev(inp["w_static"]), wl.scale, wl.eps, 0)
+    u, Hp, w = host(hc.pre_mix(Hd, w, gd, wl.eps)), host(hc.post_mix(Hd, Fd, w)), host(w)
+    ws64 = inp["w_static"].astype(np.float64)
+    for t0 in range(0, wl.T, 2048):
+        sl = slice(t0, t0 + 2048)
+        record_check(w[sl], oracle.weights(inp["H"][sl], inp["W"], ws64, wl.scale, wl.eps, 0),
+                     f"records {t0}+")
+        w64 = w[sl].astype(np.float64)
+        check(u[sl], oracle.pre_mix(inp["H"][sl], w64, inp["gamma"], wl.eps), f"pre {t0}+")
+        check(Hp[sl], oracle.post_mix(inp["H"][sl], inp["F"][sl], w64), f"post {t0}+")
+
+
+def test_mhc_workload_full_size_every_token():
+    """T=32768, n=4, d=4096 bf16: Sinkhorn records, then pre and post with
+    them, every token against the oracle (records fed back exactly)."""
+    wl = workload("mhc-bf16")
+    inp = make_inputs(wl)
+    Hd, Fd, gd = dev(inp["H"]), dev(inp["F"]), dev(inp["gamma"])
+    w = hc.sinkhorn(dev(inp["logits"]), wl.n, wl.iters)
+    u, Hp, w = host(hc.pre_mix(Hd, w, gd, wl.eps)), host(hc.post_mix(Hd, Fd, w)), host(w)
+    for t0 in range(0, wl.T, 2048):
+        sl = slice(t0, t0 + 2048)
+        w64 = w[sl].astype(np.float64)
+        check(u[sl], oracle.pre_mix(inp["H"][sl], w64, inp["gamma"], wl.eps), f"pre {t0}+")
+        check(Hp[sl], oracle.post_mix(inp["H"][sl], inp["F"][sl], w64), f"post {t0}+")
