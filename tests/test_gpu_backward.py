@@ -138,11 +138,11 @@ def test_sum_records(T, K):
     np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-5 * np.sqrt(T))
 
 
-def test_static_layer_backward_full_size_sampled():
+def test_static_layer_backward_full_size():
     """T=8192, n=4, d=4096 bf16 with shared weights: post backward, then pre
     backward accumulating into the same dH; dgamma and the shared weight
-    gradients (summed records) against the oracle over all tokens; dH and dF
-    on 256 sampled tokens."""
+    gradients (summed records), dH and dF against the oracle over all
+    tokens."""
     wl = workload("static-bf16")
     inp = make_inputs(wl)
     rng = np.random.default_rng(77)
@@ -162,9 +162,11 @@ def test_static_layer_backward_full_size_sampled():
     dalpha_check(gw[None, :], r_pre[1].sum(0)[None, :], du, inp["H"], inp["w"], inp["gamma"], wl.eps,
                  "shared dalpha")
     grad_check(host(dg)[None, :], r_pre[2][None, :], "dgamma")
-    idx = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 256, replace=False)]))
-    ti = torch.from_numpy(idx).cuda()
-    check(host(dF[ti]), r_post[1][idx], "dF")
-    # dH on the GPU is the bf16-stored post gradient plus the pre gradient,
-    # rounded again: two roundings, so only the bf16 tolerance applies
-    check(host(dH[ti]), r_pre[0][idx], "dH", one_ulp=False)
+    # every token, in chunks; dH on the GPU is the bf16-stored post gradient
+    # plus the pre gradient, rounded again: two roundings, so only the bf16
+    # tolerance applies
+    dFh, dHh = host(dF), host(dH)
+    for t0 in range(0, T, 1024):
+        sl = slice(t0, t0 + 1024)
+        check(dFh[sl], r_post[1][sl], f"dF {t0}+")
+        check(dHh[sl], r_pre[0][sl], f"dH {t0}+", one_ulp=False)

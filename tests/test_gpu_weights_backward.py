@@ -111,10 +111,11 @@ def test_sinkhorn_backward_parity(n, iters):
 
 
 def test_dynamic_workload_backward_full_size():
-    """T=16384, n=4, d=4096 bf16 (the dynamic workload): dH on 64 sampled
-    tokens against the oracle; dW and dw_static of the first 1024 tokens (a
-    separate call, the same kernels) against the oracle; the benchmark's form
-    (projections kept by hc_weights_save) bitwise equal to the recomputing one."""
+    """T=16384, n=4, d=4096 bf16 (the dynamic workload): dH of every token,
+    dW and dw_static over all tokens, against the oracle (run in chunks of
+    2048 tokens, whose dW and dw_static are summed in fp64); the benchmark's
+    form (projections kept by hc_weights_save) bitwise equal to the
+    recomputing one."""
     wl = workload("dynamic-bf16")
     inp = make_inputs(wl)
     rng = np.random.default_rng(41)
@@ -126,18 +127,20 @@ def test_dynamic_workload_backward_full_size():
     dHs, dWs, dwss = hc.weights_backward(Hd, Wd, wsd, wl.scale, dev(dw), wl.eps, saved=saved)
     assert torch.equal(dH, dHs) and torch.equal(dW, dWs) and torch.equal(dws, dwss)
     del dHs, dWs, dwss, saved
-    torch.cuda.synchronize()
-    idx = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 64, replace=False)]))
-    sub = make_inputs(wl, tokens=idx)
-    rdH, _, _ = oracle.weights_backward(sub["H"], inp["W"], inp["w_static"].astype(np.float64),
-                                        wl.scale, dw[idx].astype(np.float64), wl.eps)
-    check(host(dH[torch.from_numpy(idx).cuda()]), rdH, "dynamic dH (sampled)")
-    m = 1024
-    _, dW1, dws1 = hc.weights_backward(Hd[:m].contiguous(), Wd, wsd, wl.scale, dev(dw[:m]), wl.eps)
-    _, rdW, rdws = oracle.weights_backward(inp["H"][:m], inp["W"], inp["w_static"].astype(np.float64),
-                                           wl.scale, dw[:m].astype(np.float64), wl.eps)
-    grad_check(host(dW1), rdW, "dynamic dW (1024 tokens)")
-    grad_check(host(dws1)[None], rdws[None], "dynamic dw_static (1024 tokens)")
+    dH, dW, dws = host(dH), host(dW), host(dws)
+    oracle.set_threads(0)
+    rdW = np.zeros(dW.shape)
+    rdws = np.zeros(dws.shape)
+    ws64 = inp["w_static"].astype(np.float64)
+    for t0 in range(0, wl.T, 2048):
+        sl = slice(t0, t0 + 2048)
+        rdH, cW, cws = oracle.weights_backward(inp["H"][sl], inp["W"], ws64, wl.scale,
+                                               dw[sl].astype(np.float64), wl.eps)
+        check(dH[sl], rdH, f"dynamic dH {t0}+")
+        rdW += cW
+        rdws += cws
+    grad_check(dW, rdW, "dynamic dW")
+    grad_check(dws[None], rdws[None], "dynamic dw_static")
 
 
 def test_weights_backward_two_gradient_records():
