@@ -230,17 +230,22 @@ def test_static_bf16_full_size_sampled():
 @pytest.mark.parametrize("name", ["static-bf16", "static-fp8"])
 def test_static_full_size_every_token(name):
     """The static workloads (T=8192 bf16, the headline, and T=16384 FP8; n=4,
-    d=4096) in the benchmark's launch configuration: every token of u and H'
-    against the oracle, in chunks of 1024 tokens."""
+    d=4096) in the benchmark's launch configuration: every token of u and H',
+    and of the fused post+pre (its H' bitwise post's, its u against the oracle
+    on that H'), in chunks of 1024 tokens."""
     wl = workload(name)
     inp = make_inputs(wl)
     Hd, Fd, wd, gd = dev(inp["H"]), dev(inp["F"]), dev(inp["w"]), dev(inp["gamma"])
     u, Hp = host(hc.pre_mix(Hd, wd, gd, wl.eps)), host(hc.post_mix(Hd, Fd, wd))
+    Hp2, u2 = hc.post_pre_mix(Hd, Fd, wd, wd, gd, wl.eps)
+    Hp2, u2 = host(Hp2), host(u2)
+    assert np.array_equal(Hp2, Hp)               # the fused write-back is the same store
     w64 = inp["w"].astype(np.float64)
     for t0 in range(0, wl.T, 1024):
         sl = slice(t0, t0 + 1024)
         check(u[sl], oracle.pre_mix(inp["H"][sl], w64, inp["gamma"], wl.eps), f"pre tokens {t0}+")
         check(Hp[sl], oracle.post_mix(inp["H"][sl], inp["F"][sl], w64), f"post tokens {t0}+")
+        check(u2[sl], oracle.pre_mix(Hp[sl], w64, inp["gamma"], wl.eps), f"fused pre {t0}+")
 
 
 def _fp8_finite_codes() -> np.ndarray:
