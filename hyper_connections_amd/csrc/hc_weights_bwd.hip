@@ -233,8 +233,9 @@ __global__ __launch_bounds__(256) void wgrad_coef_kernel(
 
 // ---------------------------------------------------- streaming dH and dW pass
 
-// One workgroup owns a slice of CB = 16 V columns (16 lanes x one 16-byte
-// vector) and a range of tokens.  Each wave takes 4 tokens per step: lane l
+// fp32 storage (bf16 takes wgrad_mfma_kernel below).  One workgroup owns a
+// slice of CB = 16 V columns (16 lanes x one 16-byte vector) and a range of
+// tokens.  Each wave takes 4 tokens per step: lane l
 // works on token l / 16 of the step and columns (slice + l % 16) * V .. + V-1,
 // so every load is 16 lanes x 16 contiguous bytes of one row.  Per element:
 //   hbar = (1/n) sum_i r_i H_i,  dhbar = sum_c dz_c W[c] (W slice in LDS),
