@@ -387,14 +387,14 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
                 }
             }
             if constexpr (PER_TOKEN) {
-                block_sum_vec<N>(da, red);
-                if (threadIdx.x < K) {
-                    const int c = threadIdx.x;
-                    float val = 0.0f;
+                // per-wave sums, no workgroup barrier: token_records_kernel
+                // adds the waves' partials in wave order, the order a
+                // workgroup reduction would take
+                const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = B >> 6;
 #pragma unroll
-                    for (int i = 0; i < N; ++i)
-                        if (c == i) val = da[i];
-                    dw[t * K + c] = val;      // dbeta = dA = 0 (pre does not read them)
+                for (int i = 0; i < N; ++i) {
+                    const float v = wave_sum(da[i]);
+                    if (lane == 0) da_part[(t * nw + wave) * N + i] = v;
                 }
             } else {
 #pragma unroll
@@ -478,6 +478,25 @@ __global__ __launch_bounds__(1024) void sum_records_kernel(const float* __restri
     float s = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     s = block_sum(s, red);
     if (threadIdx.x == 0) out[c] = s;
+}
+
+// dw[t][c] = sum over the nw waves of part[t][w][c] (c < n, in wave order),
+// 0 for c >= n: pre's per-token records from its per-wave partials.
+__global__ __launch_bounds__(256) void token_records_kernel(const float* __restrict__ part, int nw,
+                                                            int n, int K, int64_t T,
+                                                            float* __restrict__ dw) {
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < T * K;
+         e += (int64_t)gridDim.x * 256) {
+        const int64_t t = e / K;
+        const int c = (int)(e % K);
+        float s = 0.0f;
+        if (c < n) {
+            const float* p = part + t * nw * n + c;
+            s = p[0];
+            for (int w = 1; w < nw; ++w) s += p[w * n];
+        }
+        dw[e] = s;
+    }
 }
 
 // ----------------------------------------------------------------- dispatch
@@ -612,7 +631,7 @@ hipError_t pre_bwd_n(int n, A... a) {
 //   tmp         second-level rows of either sum (ceil(rows / 64) * max(d, M),
 //               plus a third level, bounded by 2 * ceil(rows / 64) * max(d, M))
 struct BwdSpace {
-    int64_t rows, prows, dg, rec, tmp, tmp2, total;   // offsets and total, in floats
+    int64_t rows, prows, dg, rec, tmp, tmp2, wp, total;   // offsets and total, in floats
 };
 inline BwdSpace bwd_space(int64_t T, int n, int d) {
     BwdSpace b;
@@ -626,7 +645,8 @@ inline BwdSpace bwd_space(int64_t T, int n, int d) {
     const int64_t rr = b.prows > b.rows ? b.prows : b.rows;
     b.tmp = b.rec + rr * M;                               // the dgamma sum's levels
     b.tmp2 = b.tmp + sum_rows_tmp_floats(b.rows, d);      // the record sums' levels
-    b.total = b.tmp2 + sum_rows_tmp_floats(rr, M);
+    b.wp = b.tmp2 + sum_rows_tmp_floats(rr, M);           // pre's per-wave partials, per token
+    b.total = b.wp + T * 16 * n;
     return b;
 }
 
@@ -664,16 +684,24 @@ hipError_t launch_pre_mix_backward(const void* du, const void* H, const float* w
     float* ws = static_cast<float*>(work);
     const int group = (int)group_of(T);
     float* dg_part = ws + sp.dg;
-    float* da_part = ws + sp.rec;
+    // dalpha: per-workgroup partials (shared record), or per token and wave
+    float* da_part = w_stride != 0 ? ws + sp.wp : ws + sp.rec;
     hipError_t e =
         dt == 0 ? pre_bwd_n<f32_t>(n, row_config(d / Store<f32_t>::kElems), du, H, w, w_stride,
                                    gamma, eps, dH_in, dH, dw, dg_part, da_part, T, d, group, s)
                 : pre_bwd_n<bf16_t>(n, row_config(d / Store<bf16_t>::kElems), du, H, w, w_stride,
                                     gamma, eps, dH_in, dH, dw, dg_part, da_part, T, d, group, s);
     if (e != hipSuccess) return e;
+    const int K = 2 * n + n * n;
+    if (w_stride != 0) {
+        const int nw = row_config(d / (dt == 0 ? Store<f32_t>::kElems : Store<bf16_t>::kElems)).block / 64;
+        const int64_t blocks = (T * K + 255) / 256;
+        e = launch(token_records_kernel, grid_of(blocks), dim3(256), 0, s,
+                   static_cast<const float*>(da_part), nw, n, K, T, dw);
+        if (e != hipSuccess) return e;
+    }
     // dgamma; with a shared record also dw = [sum of the dalpha partials |
     // 0 (dbeta, dA)], in the same launches
-    const int K = 2 * n + n * n;
     const SumJob jobs[2] = {{dg_part, sp.rows, d, ws + sp.tmp, dgamma, nullptr, 0},
                             {da_part, sp.rows, n, ws + sp.tmp2, dw, dw + n, K - n}};
     return launch_sum_rows2(jobs, w_stride != 0 ? 1 : 2, s);

@@ -170,8 +170,9 @@ hc_status hc_post_pre_mix(const void* H, const void* F, const float* w, int64_t 
                           int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream);
 
 /* Bytes of device workspace the backward calls need for T tokens of width d
- * with n streams (0 for T <= 0).  The caller owns it; it holds per-block
- * partial sums and is fully rewritten by every call. */
+ * with n streams (0 for T <= 0).  The caller owns it; it holds partial sums
+ * (per workgroup, or per token and wave for per-token records) and every
+ * call writes what it reads. */
 int64_t hc_backward_workspace(int64_t T, int32_t n, int32_t d);
 
 /* Gradients of hc_post_mix (the map is linear in H and F):
