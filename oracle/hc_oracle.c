@@ -45,6 +45,24 @@
  *   mHC   alpha = sigmoid(l_alpha), beta = sigmoid(l_beta),
  *         A = Sinkhorn_iters(exp(l_A)), one iteration = normalise every row to
  *         sum 1, then every column to sum 1.
+ *   gradients (the same formulas differentiated by the chain rule; the
+ *         learned weights take gradients, [GLOSS] definition): of post, of
+ *         pre (RMSNorm and read-mix), of the per-token weights (projection,
+ *         per-stream RMSNorm, tanh or the mHC transform) and of the mHC
+ *         transform alone.
+ *
+ * What pins each function (tests/test_oracle_*.py; none compares the oracle
+ * with itself): identity weights on copies give x + f(x) and n = 1 reduces to
+ * the plain residual (bitwise); torch's rms_norm and autograd in float64;
+ * exact-rational and 60-digit brute force on tiny inputs; closed forms
+ * (one-hot, constant, scaled copies, rank-1 Sinkhorn logits, the n = 2
+ * Sinkhorn limit, W = 0); invariants (conservation under column-stochastic A,
+ * Sinkhorn cross-ratios, scale invariance of RMSNorm); central finite
+ * differences of the forward for every gradient; and planted mistakes in
+ * copies of this file that the pins must catch.  The per-token weight rule,
+ * its tanh combination and the sigmoid alpha/beta of mHC are readings the
+ * pages do not state: the pins fix this file's arithmetic for those readings,
+ * not the readings themselves.
  */
 #include <math.h>
 #include <stdint.h>
