@@ -18,11 +18,12 @@
 //   dH_i = alpha_i dx,  dalpha_i = sum_k dx_k H_ik,  dgamma = sum_t du x r.
 //
 // Weight gradients take the shape of the weights: one record per token for
-// per-token weights (a block reduction per token), one record in total for
-// shared weights.  Shared-record gradients and dgamma are summed over the
-// tokens of a block in registers, written once per block to the caller's
-// workspace, and summed over blocks by sum_rows_kernel in a fixed order
-// (two levels), so every result is deterministic.
+// per-token weights (post: a workgroup reduction per token; pre: per-wave
+// sums in the workspace, added in wave order by token_records_kernel), one
+// record in total for shared weights.  Shared-record gradients and dgamma are
+// summed over the tokens of a block in registers, written once per block to
+// the caller's workspace, and summed over blocks by sum_rows_kernel in a
+// fixed order (64 rows per level), so every result is deterministic.
 //
 // Both kernels stream rows like the forward ones (one 16-byte vector per
 // thread per stream, all loads of a token issued first).
@@ -242,8 +243,9 @@ __global__ __launch_bounds__(1024) void post_bwd_kernel(
 
 // A block walks up to `group` tokens (see post_bwd_kernel).  The dgamma partial of each
 // thread's columns stays in registers and goes to dg_part[blk][d] once;
-// dalpha goes to dw[t] per token (PER_TOKEN) or is summed over the block's
-// tokens into da_part[blk][N].
+// dalpha goes per token and wave to da_part[t][wave][N] (PER_TOKEN; dw is
+// then filled by token_records_kernel) or is summed over the block's tokens
+// into da_part[blk][N].
 template <int N, typename S, int VPT, bool PER_TOKEN>
 __global__ __launch_bounds__(1024) void pre_bwd_kernel(
     const uint8_t* __restrict__ du, const uint8_t* __restrict__ H, const float* __restrict__ w,
