@@ -30,6 +30,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -54,13 +55,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_text(src: str) -> str:
+    """A C/HIP source without its comments and blank space: what the
+    compiler sees, so an edit to a comment leaves the hash alone."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(" ".join(l.split()) for l in src.splitlines() if l.strip())
+
+
 def source_sha(kernel: str) -> str:
-    """Hash of the sources a kernel is built from (its file + the shared
-    device header), used to invalidate stale counter summaries."""
+    """Hash of the code a kernel is built from (its file + the shared device
+    header, comments left out), used to invalidate stale counter
+    summaries."""
     h = hashlib.sha256()
     for f in (KERNEL_SOURCES[kernel], "hc_device.h"):
-        with open(os.path.join(ROOT, "hyper_connections_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "hyper_connections_amd", "csrc", f)) as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -57,6 +57,39 @@ __device__ __forceinline__ void block_sum_vec(float (&v)[M], float* red) {
     __syncthreads();
 }
 
+// Sum M values over the block for threads 0..M-1 only: thread m returns sum
+// m (the others 0), added in the same order as block_sum_vec.  `red` holds
+// 16 * M floats.
+template <int M>
+__device__ __forceinline__ float block_sum_to(float (&v)[M], float* red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        v[m] = wave_sum(v[m]);
+        if (lane == 0) red[wave * M + m] = v[m];
+    }
+    __syncthreads();
+    float s = 0.0f;
+    if ((int)threadIdx.x < M) {
+        s = red[threadIdx.x];
+        for (int w = 1; w < nw; ++w) s += red[w * M + threadIdx.x];
+    }
+    __syncthreads();
+    return s;
+}
+
+// acc + the dot product of two storage words: fp32 one product; bf16 both
+// halves at once with v_dot2_f32_bf16 (bf16 products are exact in fp32), so
+// the words need no unpacking.
+template <typename S> __device__ __forceinline__ float dot_word(uint32_t a, uint32_t b, float acc);
+template <> __device__ __forceinline__ float dot_word<f32_t>(uint32_t a, uint32_t b, float acc) {
+    return fmaf(__uint_as_float(a), __uint_as_float(b), acc);
+}
+template <> __device__ __forceinline__ float dot_word<bf16_t>(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                           acc, false);
+}
+
 // Tokens per block for shared-record gradients: enough blocks to fill the
 // chip several times over, at least 8 tokens each (pre: its per-block
 // partials include a d-wide dgamma row).
@@ -66,8 +99,8 @@ inline int64_t group_of(int64_t T) {
 }
 // Post's partials are only n + n^2 floats per block, so it takes fewer
 // tokens per block: about 4096 blocks, at least 2 tokens each (measured at
-// T = 8192: 2 tokens per block 176 us, 4 179 us, 8 183 us, 16 186 us, and
-// 1 token per block 196 us with its longer sum).
+// T = 8192, n = 4, d = 4096 bf16: 2 tokens per block 167 us, 4 171 us, and
+// 1 token per block 170 us with its longer sum).
 inline int64_t post_group_of(int64_t T) {
     const int64_t g = T / 4096;
     return g < 2 ? 2 : g;
@@ -102,6 +135,15 @@ __global__ __launch_bounds__(1024) void post_bwd_kernel(
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[m] = 0.0f;
         uint4 rg[N][VPT], rh[N][VPT], rf[VPT];
+        // Every path assigns the vectors (zeros where there is no token or
+        // column), so the last token's values are dead once used and their
+        // registers free for the next phase; otherwise they stay live
+        // around the loop.
+        auto clear = [&](int j) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) rg[i][j] = rh[i][j] = make_uint4(0, 0, 0, 0);
+            rf[j] = make_uint4(0, 0, 0, 0);
+        };
         auto fetch = [&](int64_t t) {
             const int64_t r0 = t * N * row_bytes;
 #pragma unroll
@@ -114,13 +156,15 @@ __global__ __launch_bounds__(1024) void post_bwd_kernel(
                         rh[i][j] = ld16_stream(H + r0 + i * row_bytes + v * 16);
                     }
                     rf[j] = ld16_stream(F + t * row_bytes + v * 16);
+                } else {
+                    clear(j);
                 }
             }
         };
         // Per-token records with one vector per thread: a token's loads are
         // issued before the previous token's block-wide sums.  (Measured at
-        // n = 4: this form also compiles to 77 registers instead of 85, six
-        // waves per SIMD instead of five, and runs 16% faster; with more
+        // n = 4 when it was introduced: fewer registers than loading at the
+        // top of the loop, one more wave per SIMD, and 16% faster; with more
         // vectors per thread it needs more registers, so it is not used there.)
         constexpr bool kAhead = PER_TOKEN && VPT == 1;
         if constexpr (kAhead) {
@@ -142,99 +186,74 @@ __global__ __launch_bounds__(1024) void post_bwd_kernel(
             for (int j = 0; j < VPT; ++j) {
                 const int v = threadIdx.x + j * B;
                 if (v < nvec) {
-                    // one output row at a time, dword by dword; the unpacked
-                    // values are recomputed from the raw vectors each time
-                    // dH_j = sum_i A[i][j] dH'_i
+                    // partials of dbeta_i = dH'_i . F and dA[i][jj] = dH'_i . H_jj
+                    // first, from the storage words; after them only the dH'
+                    // vectors stay live
 #pragma unroll
-                    for (int jj = 0; jj < N; ++jj) {
+                    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                        for (int i = 0; i < N; ++i) {
+                            const uint32_t gw = word(rg[i][j], q);
+#pragma unroll
+                            for (int jj = 0; jj < N; ++jj)
+                                acc[N + i * N + jj] = dot_word<S>(gw, word(rh[jj][j], q), acc[N + i * N + jj]);
+                            acc[i] = dot_word<S>(gw, word(rf[j], q), acc[i]);
+                        }
+                    }
+                    // (kept apart by the scheduler: interleaving the two phases
+                    // keeps every input and output live at once)
+                    __builtin_amdgcn_sched_barrier(0);
+                    // dH_jj = sum_i A[i][jj] dH'_i and dF = sum_i beta_i dH'_i,
+                    // one output row at a time from the dH' vectors unpacked
+                    // once (the raw words die here)
+                    float g[N][4][E];
+#pragma unroll
+                    for (int i = 0; i < N; ++i)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) unpack_word<S>(word(rg[i][j], q), g[i][q]);
+#pragma unroll
+                    for (int jj = 0; jj <= N; ++jj) {
                         uint32_t oh[4];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            float g[N][E], o[E];
-#pragma unroll
-                            for (int i = 0; i < N; ++i) unpack_word<S>(word(rg[i][j], q), g[i]);
+                            float o[E];
 #pragma unroll
                             for (int e = 0; e < E; ++e) {
-                                float sum = A[0][jj] * g[0][e];
+                                float sum = (jj < N ? A[0][jj] : beta[0]) * g[0][q][e];
 #pragma unroll
-                                for (int i = 1; i < N; ++i) sum = fmaf(A[i][jj], g[i][e], sum);
+                                for (int i = 1; i < N; ++i)
+                                    sum = fmaf(jj < N ? A[i][jj] : beta[i], g[i][q][e], sum);
                                 o[e] = sum;
                             }
                             oh[q] = pack_word<S>(o);
                         }
-                        st16_stream(dH + r0 + jj * row_bytes + v * 16, make_uint4(oh[0], oh[1], oh[2], oh[3]));
-#pragma unroll
-                        for (int i = 0; i < N; ++i) opaque(rg[i][j]);
-                    }
-                    // dF = sum_i beta_i dH'_i
-                    uint32_t of[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        float g[N][E], o[E];
-#pragma unroll
-                        for (int i = 0; i < N; ++i) unpack_word<S>(word(rg[i][j], q), g[i]);
-#pragma unroll
-                        for (int e = 0; e < E; ++e) {
-                            float sum = beta[0] * g[0][e];
-#pragma unroll
-                            for (int i = 1; i < N; ++i) sum = fmaf(beta[i], g[i][e], sum);
-                            o[e] = sum;
-                        }
-                        of[q] = pack_word<S>(o);
-                    }
-                    st16_stream(dF + t * row_bytes + v * 16, make_uint4(of[0], of[1], of[2], of[3]));
-#pragma unroll
-                    for (int i = 0; i < N; ++i) opaque(rg[i][j]);
-                    // partials of dbeta_i and dA[i][j]
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        float g[N][E], f[E];
-#pragma unroll
-                        for (int i = 0; i < N; ++i) unpack_word<S>(word(rg[i][j], q), g[i]);
-                        unpack_word<S>(word(rf[j], q), f);
-#pragma unroll
-                        for (int jj = 0; jj < N; ++jj) {
-                            float h[E];
-                            unpack_word<S>(word(rh[jj][j], q), h);
-#pragma unroll
-                            for (int i = 0; i < N; ++i)
-#pragma unroll
-                                for (int e = 0; e < E; ++e)
-                                    acc[N + i * N + jj] = fmaf(g[i][e], h[e], acc[N + i * N + jj]);
-                        }
-#pragma unroll
-                        for (int i = 0; i < N; ++i)
-#pragma unroll
-                            for (int e = 0; e < E; ++e) acc[i] = fmaf(g[i][e], f[e], acc[i]);
+                        uint8_t* dst = jj < N ? dH + r0 + jj * row_bytes : dF + t * row_bytes;
+                        st16_stream(dst + v * 16, make_uint4(oh[0], oh[1], oh[2], oh[3]));
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
             }
             if constexpr (PER_TOKEN) {
                 if constexpr (kAhead) {
-                    if (t + nb < T) fetch(t + nb);
-                }
-                block_sum_vec<M>(acc, red);
-                if (threadIdx.x < K) {
-                    const int c = threadIdx.x;
-                    float val = 0.0f;
+                    if (t + nb < T) {
+                        fetch(t + nb);
+                    } else {
 #pragma unroll
-                    for (int m = 0; m < M; ++m)
-                        if (c == N + m) val = acc[m];
-                    dw[t * K + c] = val;      // dalpha = 0 (post does not read alpha)
+                        for (int j = 0; j < VPT; ++j) clear(j);
+                    }
                 }
+                const float sum = block_sum_to<M>(acc, red);
+                // thread m < M holds sum m; the record is [dalpha = 0 (post does
+                // not read alpha) | dbeta | dA]
+                if ((int)threadIdx.x < N) dw[t * K + threadIdx.x] = 0.0f;
+                if ((int)threadIdx.x < M) dw[t * K + N + threadIdx.x] = sum;
 #pragma unroll
                 for (int m = 0; m < M; ++m) acc[m] = 0.0f;
             }
         }
         if constexpr (!PER_TOKEN) {
-            block_sum_vec<M>(acc, red);
-            if (threadIdx.x < M) {
-                float val = 0.0f;
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-                    if ((int)threadIdx.x == m) val = acc[m];
-                part[blk * M + threadIdx.x] = val;
-            }
+            const float sum = block_sum_to<M>(acc, red);
+            if ((int)threadIdx.x < M) part[blk * M + threadIdx.x] = sum;
         }
     }
 }
