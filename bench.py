@@ -198,7 +198,8 @@ def summarize_mfma(pmc_csv: str, kernel: str, workload: str, cmds: list):
     log(f"[bench] wrote {base}.json: MFMA busy {busy:.1%}, {flops / secs / 1e12:.1f} TFLOP/s")
 
 
-def summarize_counters(fetch_csv: str, write_csv: str, kernel: str, workload: str, cmds: list):
+def summarize_counters(fetch_csv: str, write_csv: str, kernel: str, workload: str, cmds: list,
+                       fold: bool = True):
     """Turn two rocprofv3 --pmc runs of this benchmark (FETCH_SIZE, then
     WRITE_SIZE; KiB per dispatch) into HBM bytes per launch of `kernel`.
 
@@ -240,7 +241,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, kernel: str, workload: st
            "post_mix": tr.post_bytes(wl.n, wl.d, wl.elem_bytes, per_tok),
            "weights": tr.weights_bytes(wl.n, wl.d, wl.elem_bytes),
            "post_pre_mix": tr.post_pre_bytes(wl.n, wl.d, wl.elem_bytes),
-           "post_mix_backward": tr.post_bwd_bytes(wl.n, wl.d, wl.elem_bytes),
+           "post_mix_backward": tr.post_bwd_bytes(wl.n, wl.d, wl.elem_bytes, h_grad=not fold),
            "pre_mix_backward": tr.pre_bwd_bytes(wl.n, wl.d, wl.elem_bytes, True),
            "weights_backward": tr.weights_bwd_bytes(wl.n, wl.d, wl.elem_bytes),
            "weights_backward_stream": tr.weights_bwd_stream_bytes(wl.n, wl.d, wl.elem_bytes)}[kernel] * wl.T
@@ -286,9 +287,13 @@ def main():
                     help="fuse each write-back with the next read-mix (chain: every layer; "
                          "static: one step is one fused layer boundary)")
     ap.add_argument("--backward", action="store_true",
-                    help="time the layer's gradients: post backward, pre backward accumulating "
-                         "into the same dH, shared-weight sums (static workloads); per-token "
-                         "records and the weight producer's gradient as well (dynamic)")
+                    help="time the layer's gradients: post backward (dF and its records), pre "
+                         "backward forming the whole dH, shared-weight sums (static workloads); "
+                         "per-token records and the weight producer's gradient as well (dynamic)")
+    ap.add_argument("--no-fold", action="store_true",
+                    help="with --backward: post backward writes its H gradient and the pre "
+                         "backward adds into it (by default post leaves dH to the pre backward, "
+                         "which forms the write-back's share from dH' itself)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph (torch.cuda.CUDAGraph) and time replays")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -301,7 +306,8 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, args.kernel, args.workload, args.command)
+        summarize_counters(*args.summarize_counters, args.kernel, args.workload, args.command,
+                           fold=not args.no_fold)
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma, args.kernel, args.workload, args.command)
@@ -376,6 +382,7 @@ def main():
     if wl.kind == "chain":
         recs = [dev(workloads.layer_record(wl, l)) for l in range(wl.layers + 1)]
 
+    fold = bool(args.backward) and not args.no_fold
     # algorithmic bytes per launch
     launch_bytes = {
         "pre_mix": traffic.pre_bytes(n, d, s, per_tok) * T,
@@ -384,7 +391,7 @@ def main():
         "weights": traffic.weights_bytes(n, d, s) * T,
         "sinkhorn": traffic.sinkhorn_bytes(n) * T,
         "block_tanh": 2 * d * s * T,
-        "post_mix_backward": traffic.post_bwd_bytes(n, d, s) * T,
+        "post_mix_backward": traffic.post_bwd_bytes(n, d, s, h_grad=not fold) * T,
         "pre_mix_backward": traffic.pre_bwd_bytes(n, d, s, True) * T,
         "weights_backward": traffic.weights_bwd_bytes(n, d, s) * T,
     }
@@ -420,13 +427,18 @@ def main():
         rec = (lambda b: b["w"]) if wl.kind == "dynamic" else (lambda b: w_static)
 
         def post_bwd(b):
-            # dH lands in b["O"]; the pre backward then accumulates into it
-            hc.post_mix_backward(b["G"], b["H"], b["F"], rec(b), dH=b["O"], dF=b["dF"],
-                                 dw=b["dwp"], workspace=b["ws"])
+            # dH lands in b["O"] and the pre backward accumulates into it; folded,
+            # the pre backward forms post's share of dH from dH' (b["G"]) itself
+            hc.post_mix_backward(b["G"], b["H"], b["F"], rec(b), dH=None if fold else b["O"],
+                                 dF=b["dF"], dw=b["dwp"], workspace=b["ws"], h_grad=not fold)
 
         def pre_bwd(b):
-            hc.pre_mix_backward(b["du"], b["H"], rec(b), gamma, wl.eps, dH_in=b["O"],
-                                out=b["O"], dw=b["dwq"], dgamma=b["dg"], workspace=b["ws"])
+            if fold:
+                hc.pre_mix_backward(b["du"], b["H"], rec(b), gamma, wl.eps, dH_out=b["G"],
+                                    out=b["O"], dw=b["dwq"], dgamma=b["dg"], workspace=b["ws"])
+            else:
+                hc.pre_mix_backward(b["du"], b["H"], rec(b), gamma, wl.eps, dH_in=b["O"],
+                                    out=b["O"], dw=b["dwq"], dgamma=b["dg"], workspace=b["ws"])
 
         def weights_bwd(b):
             # the records' gradient from post and pre, through the weight producer
@@ -558,7 +570,8 @@ def main():
     # dominant kernel = largest share of step time
     dom = max(kms, key=lambda k: kms[k] * launches[k])
     dom_gbps = launch_bytes[dom] / (kms[dom] * 1e-3) / 1e9
-    traffic_b = counter_traffic(dom, wl.name)
+    # the committed counters of the backward kernels are those of the folded pair
+    traffic_b = None if (args.backward and not fold) else counter_traffic(dom, wl.name)
 
     tokens_per_s = T / (ms_step * 1e-3)
     step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
@@ -577,7 +590,8 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs, identity-init weights + noise)",
         "config": {"workload": wl.name, "T": T, "n": n, "d": d, "weights": wl.kind,
                    "layers": wl.layers, "buffer_sets": sets, "fused": bool(args.fused),
-                   "graph": bool(args.graph), "backward": bool(args.backward)},
+                   "graph": bool(args.graph), "backward": bool(args.backward),
+                   "fold": fold},
         "us_per_layer": round(ms_step * 1e3 / wl.layers, 3),
         "hbm_gbps": round(step_gbps, 1),
         "frac_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),

@@ -83,7 +83,7 @@ const char* hc_status_str(hc_status s) {
     return "HC_ERR_UNKNOWN: unknown status code";
 }
 
-int32_t hc_abi_version(void) { return 2; }
+int32_t hc_abi_version(void) { return 3; }
 
 hc_status hc_pre_mix(const void* H, const float* w, int64_t w_stride, const float* gamma, float eps,
                      void* u, int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream) {
@@ -230,7 +230,7 @@ hc_status hc_post_mix_backward(const void* dH_out, const void* H, const void* F,
     const int K = record_len(n);
     if ((st = check_stride(w_stride, K, T)) != HC_OK) return st;
     if (T == 0) return HC_OK;
-    if (!dH_out || !H || !F || !w || !dH || !dF || !dw) return HC_ERR_NULL;
+    if (!dH_out || !H || !F || !w || !dF || !dw) return HC_ERR_NULL;     // dH may be NULL
     const bool shared = w_stride == 0;
     if (shared && !workspace) return HC_ERR_NULL;
     if (shared && workspace_bytes < hc_backward_workspace(T, n, d)) return HC_ERR_ARG;
@@ -240,7 +240,7 @@ hc_status hc_post_mix_backward(const void* dH_out, const void* H, const void* F,
         return HC_ERR_ALIGN;
     const int64_t s = elem_bytes(dt);
     const Span sG{dH_out, T * n * d * s}, sH{H, T * n * d * s}, sF{F, T * d * s},
-        sW{w, record_span(T, w_stride, K)}, sdH{dH, T * n * d * s}, sdF{dF, T * d * s},
+        sW{w, record_span(T, w_stride, K)}, sdH{dH, dH ? T * n * d * s : 0}, sdF{dF, T * d * s},
         sdw{dw, (shared ? 1 : T) * K * 4},
         sws{workspace, shared ? hc_backward_workspace(T, n, d) : 0};
     const Span ins[] = {sG, sH, sF, sW};
@@ -255,29 +255,32 @@ hc_status hc_post_mix_backward(const void* dH_out, const void* H, const void* F,
 }
 
 hc_status hc_pre_mix_backward(const void* du, const void* H, const float* w, int64_t w_stride,
-                              const float* gamma, float eps, const void* dH_in, void* dH,
-                              float* dw, float* dgamma, void* workspace, int64_t workspace_bytes,
-                              int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream) {
+                              const float* gamma, float eps, const void* dH_in, const void* dH_out,
+                              void* dH, float* dw, float* dgamma, void* workspace,
+                              int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
+                              void* stream) {
     if (!dtype_wide(dt)) return HC_ERR_DTYPE;
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
     const int K = record_len(n);
     if ((st = check_stride(w_stride, K, T)) != HC_OK) return st;
     if (!eps_ok(eps)) return HC_ERR_ARG;
+    if (dH_in && dH_out) return HC_ERR_ARG;     // at most one addend
     if (T == 0) return HC_OK;
     if (!du || !H || !w || !gamma || !dH || !dw || !dgamma || !workspace) return HC_ERR_NULL;
     if (workspace_bytes < hc_backward_workspace(T, n, d)) return HC_ERR_ARG;
     if (misaligned(du, 16) || misaligned(H, 16) || misaligned(gamma, 16) || misaligned(dH, 16) ||
-        misaligned(dH_in, 16) || misaligned(workspace, 16) || misaligned(w, 4) ||
-        misaligned(dw, 4) || misaligned(dgamma, 4))
+        misaligned(dH_in, 16) || misaligned(dH_out, 16) || misaligned(workspace, 16) ||
+        misaligned(w, 4) || misaligned(dw, 4) || misaligned(dgamma, 4))
         return HC_ERR_ALIGN;
     const int64_t s = elem_bytes(dt);
     const bool shared = w_stride == 0;
     const Span su{du, T * d * s}, sH{H, T * n * d * s}, sW{w, record_span(T, w_stride, K)},
         sg{gamma, int64_t(d) * 4}, sin{dH_in, dH_in ? T * n * d * s : 0}, sdH{dH, T * n * d * s},
         sdw{dw, (shared ? 1 : T) * K * 4}, sdg{dgamma, int64_t(d) * 4},
-        sws{workspace, hc_backward_workspace(T, n, d)};
-    const Span ins[] = {su, sH, sW, sg};
+        sws{workspace, hc_backward_workspace(T, n, d)},
+        sout{dH_out, dH_out ? T * n * d * s : 0};
+    const Span ins[] = {su, sH, sW, sg, sout};
     for (const Span& o : {sdH, sdw, sdg, sws})
         for (const Span& i : ins)
             if (overlap(o, i)) return HC_ERR_ALIAS;
@@ -287,8 +290,8 @@ hc_status hc_pre_mix_backward(const void* du, const void* H, const float* w, int
     if (overlap(sdH, sdw) || overlap(sdH, sdg) || overlap(sdH, sws) || overlap(sdw, sdg) ||
         overlap(sdw, sws) || overlap(sdg, sws))
         return HC_ERR_ALIAS;
-    return from_hip(hc::launch_pre_mix_backward(du, H, w, w_stride, gamma, eps, dH_in, dH, dw,
-                                                dgamma, workspace, T, n, d, dt,
+    return from_hip(hc::launch_pre_mix_backward(du, H, w, w_stride, gamma, eps, dH_in, dH_out, dH,
+                                                dw, dgamma, workspace, T, n, d, dt,
                                                 static_cast<hipStream_t>(stream)));
 }
 

@@ -150,8 +150,10 @@ inline int64_t post_group_of(int64_t T) {
 
 // PER_TOKEN: dw is [T][K], one block reduction per token.  Otherwise the
 // block's tokens are summed in registers and one partial record per block
-// goes to part[blk][M] (M = n + n^2: dbeta then dA).
-template <int N, typename S, int VPT, bool PER_TOKEN>
+// goes to part[blk][M] (M = n + n^2: dbeta then dA).  HG false: dH is not
+// written; the pre gradient forms A^T dH' itself (pre_bwd_kernel's dHo),
+// which saves writing dH here and reading it back there.
+template <int N, typename S, int VPT, bool PER_TOKEN, bool HG>
 __global__ __launch_bounds__(1024) void post_bwd_kernel(
     const uint8_t* __restrict__ dHo, const uint8_t* __restrict__ H, const uint8_t* __restrict__ F,
     const float* __restrict__ w, int64_t w_stride, uint8_t* __restrict__ dH,
@@ -243,16 +245,16 @@ __global__ __launch_bounds__(1024) void post_bwd_kernel(
                     // (kept apart by the scheduler: interleaving the two phases
                     // keeps every input and output live at once)
                     __builtin_amdgcn_sched_barrier(0);
-                    // dH_jj = sum_i A[i][jj] dH'_i and dF = sum_i beta_i dH'_i,
-                    // one output row at a time from the dH' vectors unpacked
-                    // once (the raw words die here)
+                    // dH_jj = sum_i A[i][jj] dH'_i (HG only) and dF = sum_i
+                    // beta_i dH'_i, one output row at a time from the dH'
+                    // vectors unpacked once (the raw words die here)
                     float g[N][4][E];
 #pragma unroll
                     for (int i = 0; i < N; ++i)
 #pragma unroll
                         for (int q = 0; q < 4; ++q) unpack_word<S>(word(rg[i][j], q), g[i][q]);
 #pragma unroll
-                    for (int jj = 0; jj <= N; ++jj) {
+                    for (int jj = HG ? 0 : N; jj <= N; ++jj) {
                         uint32_t oh[4];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
@@ -304,12 +306,14 @@ __global__ __launch_bounds__(1024) void post_bwd_kernel(
 // thread's columns stays in registers and goes to dg_part[blk][d] once;
 // dalpha goes per token and wave to da_part[t][wave][N] (PER_TOKEN; dw is
 // then filled by token_records_kernel) or is summed over the block's tokens
-// into da_part[blk][N].
-template <int N, typename S, int VPT, bool PER_TOKEN>
+// into da_part[blk][N].  dH gets dH_in added (when given), or with FOLD the
+// write-back's H gradient sum_i A[i][j] dH'_i, formed here from dHo (the
+// gradient at the write-back's output) and the same record.
+template <int N, typename S, int VPT, bool PER_TOKEN, bool FOLD>
 __global__ __launch_bounds__(1024) void pre_bwd_kernel(
     const uint8_t* __restrict__ du, const uint8_t* __restrict__ H, const float* __restrict__ w,
     int64_t w_stride, const float* __restrict__ gamma, float eps, const uint8_t* dH_in,
-    uint8_t* dH, float* __restrict__ dw, float* __restrict__ dg_part,
+    const uint8_t* dHo, uint8_t* dH, float* __restrict__ dw, float* __restrict__ dg_part,
     float* __restrict__ da_part, int64_t T, int d, int group) {
     constexpr int V = Store<S>::kElems, E = Word<S>::kElems;
     constexpr int K = 2 * N + N * N;
@@ -335,12 +339,17 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
 
         for (int64_t t = blk; t < T; t += nb) {
             const float* a = w + t * w_stride;
-            float alpha[N];
+            float alpha[N], A[N][N];
 #pragma unroll
             for (int i = 0; i < N; ++i) alpha[i] = a[i];
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+#pragma unroll
+                for (int k = 0; k < N; ++k) A[i][k] = FOLD ? a[2 * N + i * N + k] : 0.0f;
             const int64_t r0 = t * N * row_bytes;
-            // every load of the token first, dH_in included (it does not
-            // depend on the reduction)
+            // every load of the token first, dH_in or dH' included (they do
+            // not depend on the reduction)
+            const uint8_t* add = FOLD ? dHo : dH_in;
             uint4 rh[N][VPT], ru[VPT], rin[N][VPT];
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
@@ -352,7 +361,7 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
                 ru[j] = v < nvec ? ld16_stream(du + t * row_bytes + v * 16) : z;
 #pragma unroll
                 for (int i = 0; i < N; ++i)
-                    rin[i][j] = (dH_in && v < nvec) ? ld16_stream(dH_in + r0 + i * row_bytes + v * 16) : z;
+                    rin[i][j] = (add && v < nvec) ? ld16_stream(add + r0 + i * row_bytes + v * 16) : z;
             }
             // x = sum_i alpha_i H_i, dword by dword (recomputed the same way
             // after the reduction instead of being kept)
@@ -435,11 +444,24 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
                                 da[i] = fmaf(dx[q * E + e], h[e], da[i]);
                                 o[e] = alpha[i] * dx[q * E + e];
                             }
-                            if (dH_in) {
+                            if (!FOLD && dH_in) {
                                 float p[E];
                                 unpack_word<S>(word(rin[i][j], q), p);
 #pragma unroll
                                 for (int e = 0; e < E; ++e) o[e] += p[e];
+                            } else if constexpr (FOLD) {
+                                // + sum_k A[k][i] dH'_k, formed as the write-back's
+                                // gradient forms it, then one rounding
+                                float g[N][E];
+#pragma unroll
+                                for (int k = 0; k < N; ++k) unpack_word<S>(word(rin[k][j], q), g[k]);
+#pragma unroll
+                                for (int e = 0; e < E; ++e) {
+                                    float sum = A[0][i] * g[0][e];
+#pragma unroll
+                                    for (int k = 1; k < N; ++k) sum = fmaf(A[k][i], g[k][e], sum);
+                                    o[e] = fmaf(alpha[i], dx[q * E + e], sum);
+                                }
                             }
                             oh[q] = pack_word<S>(o);
                         }
@@ -608,36 +630,56 @@ hipError_t launch_sum_rows2(const SumJob* jobs, int njobs, hipStream_t s) {
 
 namespace {
 
-template <int N, typename S, int VPT>
-hipError_t post_bwd_go(RowCfg c, const void* dHo, const void* H, const void* F, const float* w,
-                       int64_t ws, void* dH, void* dF, float* dw, float* part, int64_t T, int d,
-                       int group, hipStream_t s) {
+template <int N, typename S, int VPT, bool HG>
+hipError_t post_bwd_go2(RowCfg c, const void* dHo, const void* H, const void* F, const float* w,
+                        int64_t ws, void* dH, void* dF, float* dw, float* part, int64_t T, int d,
+                        int group, hipStream_t s) {
     const dim3 grid = grid_of((T + group - 1) / group);
     if (ws != 0)
-        return launch(post_bwd_kernel<N, S, VPT, true>, grid, dim3(c.block), 0, s,
+        return launch(post_bwd_kernel<N, S, VPT, true, HG>, grid, dim3(c.block), 0, s,
                       static_cast<const uint8_t*>(dHo), static_cast<const uint8_t*>(H),
                       static_cast<const uint8_t*>(F), w, ws, static_cast<uint8_t*>(dH),
                       static_cast<uint8_t*>(dF), dw, part, T, d, group);
-    return launch(post_bwd_kernel<N, S, VPT, false>, grid, dim3(c.block), 0, s,
+    return launch(post_bwd_kernel<N, S, VPT, false, HG>, grid, dim3(c.block), 0, s,
                   static_cast<const uint8_t*>(dHo), static_cast<const uint8_t*>(H),
                   static_cast<const uint8_t*>(F), w, ws, static_cast<uint8_t*>(dH),
                   static_cast<uint8_t*>(dF), dw, part, T, d, group);
 }
 
 template <int N, typename S, int VPT>
-hipError_t pre_bwd_go(RowCfg c, const void* du, const void* H, const float* w, int64_t ws,
-                      const float* gamma, float eps, const void* dH_in, void* dH, float* dw,
-                      float* dg_part, float* da_part, int64_t T, int d, int group, hipStream_t s) {
+hipError_t post_bwd_go(RowCfg c, const void* dHo, const void* H, const void* F, const float* w,
+                       int64_t ws, void* dH, void* dF, float* dw, float* part, int64_t T, int d,
+                       int group, hipStream_t s) {
+    return dH ? post_bwd_go2<N, S, VPT, true>(c, dHo, H, F, w, ws, dH, dF, dw, part, T, d, group, s)
+              : post_bwd_go2<N, S, VPT, false>(c, dHo, H, F, w, ws, dH, dF, dw, part, T, d, group, s);
+}
+
+template <int N, typename S, int VPT, bool FOLD>
+hipError_t pre_bwd_go2(RowCfg c, const void* du, const void* H, const float* w, int64_t ws,
+                       const float* gamma, float eps, const void* dH_in, const void* dHo, void* dH,
+                       float* dw, float* dg_part, float* da_part, int64_t T, int d, int group,
+                       hipStream_t s) {
     const dim3 grid = grid_of((T + group - 1) / group);
     if (ws != 0)
-        return launch(pre_bwd_kernel<N, S, VPT, true>, grid, dim3(c.block), 0, s,
+        return launch(pre_bwd_kernel<N, S, VPT, true, FOLD>, grid, dim3(c.block), 0, s,
                       static_cast<const uint8_t*>(du), static_cast<const uint8_t*>(H), w, ws, gamma,
-                      eps, static_cast<const uint8_t*>(dH_in), static_cast<uint8_t*>(dH), dw,
-                      dg_part, da_part, T, d, group);
-    return launch(pre_bwd_kernel<N, S, VPT, false>, grid, dim3(c.block), 0, s,
+                      eps, static_cast<const uint8_t*>(dH_in), static_cast<const uint8_t*>(dHo),
+                      static_cast<uint8_t*>(dH), dw, dg_part, da_part, T, d, group);
+    return launch(pre_bwd_kernel<N, S, VPT, false, FOLD>, grid, dim3(c.block), 0, s,
                   static_cast<const uint8_t*>(du), static_cast<const uint8_t*>(H), w, ws, gamma,
-                  eps, static_cast<const uint8_t*>(dH_in), static_cast<uint8_t*>(dH), dw, dg_part,
-                  da_part, T, d, group);
+                  eps, static_cast<const uint8_t*>(dH_in), static_cast<const uint8_t*>(dHo),
+                  static_cast<uint8_t*>(dH), dw, dg_part, da_part, T, d, group);
+}
+
+template <int N, typename S, int VPT>
+hipError_t pre_bwd_go(RowCfg c, const void* du, const void* H, const float* w, int64_t ws,
+                      const float* gamma, float eps, const void* dH_in, const void* dHo, void* dH,
+                      float* dw, float* dg_part, float* da_part, int64_t T, int d, int group,
+                      hipStream_t s) {
+    return dHo ? pre_bwd_go2<N, S, VPT, true>(c, du, H, w, ws, gamma, eps, dH_in, dHo, dH, dw, dg_part,
+                                               da_part, T, d, group, s)
+               : pre_bwd_go2<N, S, VPT, false>(c, du, H, w, ws, gamma, eps, dH_in, dHo, dH, dw, dg_part,
+                                                da_part, T, d, group, s);
 }
 
 #define HC_BWD_VPT(FN, ...)                                  \
@@ -658,9 +700,11 @@ hipError_t post_bwd_vpt(RowCfg c, const void* dHo, const void* H, const void* F,
 
 template <int N, typename S>
 hipError_t pre_bwd_vpt(RowCfg c, const void* du, const void* H, const float* w, int64_t ws,
-                       const float* gamma, float eps, const void* dH_in, void* dH, float* dw,
-                       float* dg_part, float* da_part, int64_t T, int d, int group, hipStream_t s) {
-    HC_BWD_VPT(pre_bwd_go, du, H, w, ws, gamma, eps, dH_in, dH, dw, dg_part, da_part, T, d, group, s)
+                       const float* gamma, float eps, const void* dH_in, const void* dHo, void* dH,
+                       float* dw, float* dg_part, float* da_part, int64_t T, int d, int group,
+                       hipStream_t s) {
+    HC_BWD_VPT(pre_bwd_go, du, H, w, ws, gamma, eps, dH_in, dHo, dH, dw, dg_part, da_part, T, d, group,
+               s)
 }
 #undef HC_BWD_VPT
 
@@ -738,9 +782,9 @@ hipError_t launch_post_mix_backward(const void* dHo, const void* H, const void* 
 }
 
 hipError_t launch_pre_mix_backward(const void* du, const void* H, const float* w, int64_t w_stride,
-                                   const float* gamma, float eps, const void* dH_in, void* dH,
-                                   float* dw, float* dgamma, void* work, int64_t T, int n, int d,
-                                   int dt, hipStream_t s) {
+                                   const float* gamma, float eps, const void* dH_in, const void* dHo,
+                                   void* dH, float* dw, float* dgamma, void* work, int64_t T, int n,
+                                   int d, int dt, hipStream_t s) {
     const BwdSpace sp = bwd_space(T, n, d);
     float* ws = static_cast<float*>(work);
     const int group = (int)group_of(T);
@@ -749,9 +793,9 @@ hipError_t launch_pre_mix_backward(const void* du, const void* H, const float* w
     float* da_part = w_stride != 0 ? ws + sp.wp : ws + sp.rec;
     hipError_t e =
         dt == 0 ? pre_bwd_n<f32_t>(n, row_config(d / Store<f32_t>::kElems), du, H, w, w_stride,
-                                   gamma, eps, dH_in, dH, dw, dg_part, da_part, T, d, group, s)
+                                   gamma, eps, dH_in, dHo, dH, dw, dg_part, da_part, T, d, group, s)
                 : pre_bwd_n<bf16_t>(n, row_config(d / Store<bf16_t>::kElems), du, H, w, w_stride,
-                                    gamma, eps, dH_in, dH, dw, dg_part, da_part, T, d, group, s);
+                                    gamma, eps, dH_in, dHo, dH, dw, dg_part, da_part, T, d, group, s);
     if (e != hipSuccess) return e;
     const int K = 2 * n + n * n;
     if (w_stride != 0) {

@@ -53,9 +53,9 @@ hipError_t launch_post_mix_backward(const void* dHo, const void* H, const void* 
                                     int64_t w_stride, void* dH, void* dF, float* dw, void* work,
                                     int64_t T, int n, int d, int dt, hipStream_t s);
 hipError_t launch_pre_mix_backward(const void* du, const void* H, const float* w, int64_t w_stride,
-                                   const float* gamma, float eps, const void* dH_in, void* dH,
-                                   float* dw, float* dgamma, void* work, int64_t T, int n, int d,
-                                   int dt, hipStream_t s);
+                                   const float* gamma, float eps, const void* dH_in, const void* dHo,
+                                   void* dH, float* dw, float* dgamma, void* work, int64_t T, int n,
+                                   int d, int dt, hipStream_t s);
 int64_t backward_workspace_bytes(int64_t T, int n, int d);
 hipError_t launch_sum_records(const float* rec, int64_t T, int K, float* out, hipStream_t s);
 hipError_t launch_sinkhorn(const float* logits, float* w_out, int iters, int64_t T, int n,

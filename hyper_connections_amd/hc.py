@@ -46,8 +46,8 @@ _SIGS = {
     "hc_block_tanh": [_vp, _vp, _i64, _i32, _vp],
     "hc_post_mix_backward": [_vp, _vp, _vp, _fp, _i64, _vp, _vp, _fp, _vp, _i64, _i64, _i32, _i32,
                              _i32, _vp],
-    "hc_pre_mix_backward": [_vp, _vp, _fp, _i64, _fp, _f32, _vp, _vp, _fp, _fp, _vp, _i64, _i64,
-                            _i32, _i32, _i32, _vp],
+    "hc_pre_mix_backward": [_vp, _vp, _fp, _i64, _fp, _f32, _vp, _vp, _vp, _fp, _fp, _vp, _i64,
+                            _i64, _i32, _i32, _i32, _vp],
     "hc_sum_records": [_fp, _i64, _i32, _fp, _vp],
     "hc_weights_save": [_vp, _vp, _fp, _f32, _f32, _i32, _fp, _fp, _i64, _i64, _i32, _i32, _i32,
                         _vp],
@@ -299,10 +299,13 @@ def _grad_record(dw, T, K, ws_stride, device, what="dw"):
     return dw
 
 
-def post_mix_backward(dH_out, H, F, w, dH=None, dF=None, dw=None, workspace=None, stream=None):
+def post_mix_backward(dH_out, H, F, w, dH=None, dF=None, dw=None, workspace=None, stream=None,
+                      h_grad=True):
     """Gradients of post_mix: returns (dH, dF, dw).  dw has the shape of the
     weights: (K,) for a shared record (summed over tokens), (T, K) for
-    per-token records; entries [dalpha (0) | dbeta | dA]."""
+    per-token records; entries [dalpha (0) | dbeta | dA].  With
+    ``h_grad=False`` dH is not formed (None is returned for it): pass dH_out
+    to pre_mix_backward(dH_out=...) instead, which adds it there."""
     T, n, d, K = _H(H)
     ws = _record(w, T, K)
     _dev(dH_out, "dH_out")
@@ -311,24 +314,33 @@ def post_mix_backward(dH_out, H, F, w, dH=None, dF=None, dw=None, workspace=None
         raise ValueError("dH_out must match H")
     if F.dtype != H.dtype or tuple(F.shape) != (T, d):
         raise ValueError("F must match H's dtype and have shape (T, d)")
-    dH = torch.empty_like(H) if dH is None else _dev(dH, "dH")
+    if not h_grad:
+        if dH is not None:
+            raise ValueError("dH given with h_grad=False")
+    else:
+        dH = torch.empty_like(H) if dH is None else _dev(dH, "dH")
+        if dH.shape != H.shape or dH.dtype != H.dtype:
+            raise ValueError("dH does not match H")
     dF = torch.empty_like(F) if dF is None else _dev(dF, "dF")
-    if dH.shape != H.shape or dH.dtype != H.dtype or dF.shape != F.shape or dF.dtype != F.dtype:
-        raise ValueError("dH / dF do not match H / F")
+    if dF.shape != F.shape or dF.dtype != F.dtype:
+        raise ValueError("dF does not match F")
     dw = _grad_record(dw, T, K, ws, H.device)
     wk, wkb = (None, 0) if ws != 0 else _workspace(workspace, T, n, d, H.device)
     _call("hc_post_mix_backward", dH_out.data_ptr(), H.data_ptr(), F.data_ptr(), w.data_ptr(), ws,
-          dH.data_ptr(), dF.data_ptr(), dw.data_ptr(), wk.data_ptr() if wk is not None else None,
+          dH.data_ptr() if dH is not None else None, dF.data_ptr(), dw.data_ptr(),
+          wk.data_ptr() if wk is not None else None,
           wkb, T, n, d, _dt(H), _stream(stream))
     return dH, dF, dw
 
 
 def pre_mix_backward(du, H, w, gamma, eps: float = 1e-6, dH_in=None, out=None, dw=None,
-                     dgamma=None, workspace=None, stream=None):
+                     dgamma=None, workspace=None, stream=None, dH_out=None):
     """Gradients of pre_mix: returns (dH, dw, dgamma).  dH includes dH_in when
-    given (``out=dH_in`` accumulates in place); dw has the shape of the
-    weights ([dalpha | 0 | 0]); dgamma is summed over tokens.  Output
-    buffers and the workspace may be passed in."""
+    given (``out=dH_in`` accumulates in place), or, given dH_out (the
+    gradient at post_mix's output, after post_mix_backward(h_grad=False)),
+    the write-back's H gradient formed from it and the same records; dw has
+    the shape of the weights ([dalpha | 0 | 0]); dgamma is summed over
+    tokens.  Output buffers and the workspace may be passed in."""
     T, n, d, K = _H(H)
     ws = _record(w, T, K)
     _dev(du, "du")
@@ -337,10 +349,13 @@ def pre_mix_backward(du, H, w, gamma, eps: float = 1e-6, dH_in=None, out=None, d
         raise ValueError("du must match H's dtype and have shape (T, d)")
     if gamma.dtype != torch.float32 or tuple(gamma.shape) != (d,):
         raise ValueError("gamma must be float32 of shape (d,)")
-    if dH_in is not None:
-        _dev(dH_in, "dH_in")
-        if dH_in.dtype != H.dtype or dH_in.shape != H.shape:
-            raise ValueError("dH_in must match H")
+    if dH_in is not None and dH_out is not None:
+        raise ValueError("give at most one of dH_in and dH_out")
+    for name, x in (("dH_in", dH_in), ("dH_out", dH_out)):
+        if x is not None:
+            _dev(x, name)
+            if x.dtype != H.dtype or x.shape != H.shape:
+                raise ValueError(f"{name} must match H")
     dH = torch.empty_like(H) if out is None else _dev(out, "out")
     if dH.dtype != H.dtype or dH.shape != H.shape:
         raise ValueError("out must match H")
@@ -350,7 +365,8 @@ def pre_mix_backward(du, H, w, gamma, eps: float = 1e-6, dH_in=None, out=None, d
         raise ValueError(f"dgamma must be float32 of shape ({d},)")
     wk, wkb = _workspace(workspace, T, n, d, H.device)
     _call("hc_pre_mix_backward", du.data_ptr(), H.data_ptr(), w.data_ptr(), ws, gamma.data_ptr(),
-          float(eps), dH_in.data_ptr() if dH_in is not None else None, dH.data_ptr(),
+          float(eps), dH_in.data_ptr() if dH_in is not None else None,
+          dH_out.data_ptr() if dH_out is not None else None, dH.data_ptr(),
           dw.data_ptr(), dg.data_ptr(), wk.data_ptr(), wkb, T, n, d, _dt(H), _stream(stream))
     return dH, dw, dg
 

@@ -52,10 +52,10 @@ def post_pre_bytes(n: int, d: int, s: int, per_token_record: bool = False) -> in
     return (2 * n + 2) * d * s + rec
 
 
-def post_bwd_bytes(n: int, d: int, s: int) -> int:
-    """Gradient of post: read dH', H and F, write dH and dF and one gradient
-    record."""
-    return (3 * n + 2) * d * s + record_bytes(n)
+def post_bwd_bytes(n: int, d: int, s: int, h_grad: bool = True) -> int:
+    """Gradient of post: read dH', H and F, write dH (unless the pre gradient
+    forms it: h_grad False) and dF and one gradient record."""
+    return ((3 if h_grad else 2) * n + 2) * d * s + record_bytes(n)
 
 
 def pre_bwd_bytes(n: int, d: int, s: int, accumulate: bool = True) -> int:

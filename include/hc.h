@@ -180,7 +180,10 @@ int64_t hc_backward_workspace(int64_t T, int32_t n, int32_t d);
  *   dA[i][j] = sum_k dH_out_ik H_jk      dbeta_i = sum_k dH_out_ik F_k
  * [GLOSS] definition: the mixing is learned, so its weights take gradients.
  *   dH_out, H [T][n][d] dt; F [T][d] dt; w records as in hc_post_mix
- *   dH [T][n][d] dt, dF [T][d] dt: outputs (no overlap with anything)
+ *   dH [T][n][d] dt, dF [T][d] dt: outputs (no overlap with anything).
+ *      dH may be NULL: the H gradient is then not written, and
+ *      hc_pre_mix_backward, given the same dH_out and records, adds it to its
+ *      own dH (one write of dH and one read of it saved per layer).
  *   dw fp32, the shape of the weights: one record [dalpha | dbeta | dA]
  *      (dalpha = 0: post does not read alpha) when w_stride == 0, summed over
  *      the tokens in a fixed order; else [T][K], one record per token.
@@ -193,12 +196,18 @@ hc_status hc_post_mix_backward(const void* dH_out, const void* H, const void* F,
 
 /* Gradients of hc_pre_mix (RMSNorm and read-mix written out):
  *   dy = gamma * du, dx = r * (dy - x * r^2 * mean_k(dy_k x_k)),
- *   dH_i = alpha_i dx (+ dH_in_i), dalpha_i = sum_k dx_k H_ik,
+ *   dH_i = alpha_i dx (+ dH_in_i, or + sum_j A[j][i] dH_out_j),
+ *   dalpha_i = sum_k dx_k H_ik,
  *   dgamma_k = sum_t du_tk x_tk r_t,
  * with x and r = 1/sqrt(mean x^2 + eps) recomputed from H.
  *   du [T][d] dt; H [T][n][d] dt; w, gamma, eps as in hc_pre_mix
  *   dH_in [T][n][d] dt or NULL: added to dH (a layer's H feeds both pre and
  *     post, so this is where the two gradients meet); dH_in == dH allowed
+ *   dH_out [T][n][d] dt or NULL: the gradient at hc_post_mix's output, when
+ *     hc_post_mix_backward was called with dH = NULL; the write-back's H
+ *     gradient sum_j A[j][i] dH_out_j (A from the same records w) is then
+ *     formed here and added to dH before its one rounding.  At most one of
+ *     dH_in and dH_out (both: HC_ERR_ARG).
  *   dH [T][n][d] dt
  *   dw fp32, the shape of the weights: [dalpha | 0 | 0] summed over tokens
  *     when w_stride == 0, else [T][K] per token
@@ -207,9 +216,10 @@ hc_status hc_post_mix_backward(const void* dH_out, const void* H, const void* F,
  * Outputs may not overlap inputs, each other or the workspace (except
  * dH == dH_in); a short workspace is HC_ERR_ARG. */
 hc_status hc_pre_mix_backward(const void* du, const void* H, const float* w, int64_t w_stride,
-                              const float* gamma, float eps, const void* dH_in, void* dH,
-                              float* dw, float* dgamma, void* workspace, int64_t workspace_bytes,
-                              int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream);
+                              const float* gamma, float eps, const void* dH_in, const void* dH_out,
+                              void* dH, float* dw, float* dgamma, void* workspace,
+                              int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
+                              void* stream);
 
 /* Bytes of device workspace hc_weights_backward needs (0 for T <= 0 or
  * arguments out of range).  It holds the per-stream projections, per-token

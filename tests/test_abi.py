@@ -51,7 +51,7 @@ def test_status_strings(L):
         s = hc.status_str(code)
         assert s.startswith("HC_")
     assert hc.status_str(99).startswith("HC_ERR_UNKNOWN")
-    assert hc.abi_version() == 2
+    assert hc.abi_version() == 3
 
 
 def pre(L, H=P[0], w=P[1], ws=0, g=P[2], eps=1e-6, u=P[3], T=16, n=4, d=4096, dt=BF16):
@@ -137,18 +137,24 @@ def test_backward_validation(L):
     assert pb(dt=FP8) == DTYPE and pb(dt=FP8, T=0) == DTYPE
     assert pb(T=0) == OK and pb(T=0, dH=None) == OK
     assert pb(dF=None) == NULL and pb(ws=2) == SHAPE and pb(dH=P[4] + 8) == ALIGN
+    # dH may be NULL (the pre gradient then forms it); the rest is still checked
+    assert pb(dH=None, dF=None) == NULL and pb(dH=None, dF=P[0] + 16) == ALIAS
     assert pb(wk=None) == NULL and pb(wkb=ws_need - 1) == ARG and pb(wk=P[7] + 4) == ALIGN
     assert pb(dH=P[1]) == ALIAS and pb(dw=P[4] + 64) == ALIAS and pb(dF=P[0] + 16) == ALIAS
     assert pb(wk=P[6]) == ALIAS
     qb = lambda **k: L.hc_pre_mix_backward(  # noqa: E731
         k.get("du", P[0]), k.get("H", P[1]), k.get("w", P[2]), k.get("ws", 0), k.get("g", P[3]),
-        k.get("eps", 1e-6), k.get("din", None), k.get("dH", P[4]), k.get("dw", P[5]),
+        k.get("eps", 1e-6), k.get("din", None), k.get("dout", None), k.get("dH", P[4]), k.get("dw", P[5]),
         k.get("dg", P[6]), k.get("wk", P[7]), k.get("wkb", ws_need), k.get("T", 8), 4, 4096,
         k.get("dt", BF16), None)
     assert qb(dt=FP8) == DTYPE and qb(dt=FP8, T=0) == DTYPE
     assert qb(T=0) == OK and qb(eps=0.0) == ARG and qb(wkb=ws_need - 4) == ARG
     assert qb(wk=None) == NULL and qb(dg=P[6] + 2) == ALIGN and qb(wk=P[7] + 8) == ALIGN
     assert qb(din=P[4] + 16) == ALIAS and qb(dH=P[1]) == ALIAS and qb(wk=P[5]) == ALIAS
+    # dH_out: an input like H (at most one of dH_in and dH_out, checked first)
+    assert qb(din=P[0], dout=P[1]) == ARG and qb(din=P[0], dout=P[1], T=0) == ARG
+    assert qb(dout=P[0] + 8) == ALIGN and qb(dout=P[4]) == ALIAS and qb(dout=P[5] + 64) == ALIAS
+    assert qb(dout=P[7]) == ALIAS
     assert L.hc_sum_records(P[0], 10, 0, P[1], None) == SHAPE
     assert L.hc_sum_records(P[0], -1, 24, P[1], None) == ARG
     assert L.hc_sum_records(P[0], 10, 24, P[0] + 8, None) == ALIAS

@@ -109,6 +109,30 @@ def test_pre_backward_parity(dt, d, n, acc):
     grad_check(host(dg)[None, :], rdg[None, :], f"pre dgamma n={n} d={d}")
 
 
+@pytest.mark.parametrize("dt,d", SHAPES)
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_backward_fold_parity(dt, d, n):
+    """post_mix_backward without dH, then pre_mix_backward given dH_out: dH is
+    the write-back's H gradient plus the pre gradient, formed in one pass and
+    rounded once, so it meets the one-ulp bound; dF and the post records are
+    bitwise those of the unfolded call."""
+    rng = np.random.default_rng(d * 17 + n)
+    T = 11
+    H, F, G, du, w, g = case(rng, dt, T, n, d, per_token=(d % 2 == 0))
+    dH0, dF0, dw0 = hc.post_mix_backward(dev(G), dev(H), dev(F), dev(w))
+    none, dF, dwp = hc.post_mix_backward(dev(G), dev(H), dev(F), dev(w), h_grad=False)
+    assert none is None
+    assert np.array_equal(host(dF), host(dF0)) and np.array_equal(host(dwp), host(dw0))
+    dH, dwq, dg = hc.pre_mix_backward(dev(du), dev(H), dev(w), dev(g), 1e-6, dH_out=dev(G))
+    w64 = w.astype(np.float64)
+    rdH_post = oracle.post_mix_backward(G, H, F, w64)[0]
+    rdH, rdw, rdg = oracle.pre_mix_backward(du, H, w64, g, 1e-6, dH_in=rdH_post)
+    check(host(dH), rdH, f"folded dH n={n} d={d}")
+    # the pre records and dgamma do not depend on the addend
+    _, dwq0, dg0 = hc.pre_mix_backward(dev(du), dev(H), dev(w), dev(g), 1e-6)
+    assert np.array_equal(host(dwq), host(dwq0)) and np.array_equal(host(dg), host(dg0))
+
+
 def test_pre_backward_accumulates_in_place():
     rng = np.random.default_rng(3)
     H, F, G, du, w, g = case(rng, "bf16", 17, 4, 4096, per_token=True)
@@ -170,3 +194,31 @@ def test_static_layer_backward_full_size():
         sl = slice(t0, t0 + 1024)
         check(dFh[sl], r_post[1][sl], f"dF {t0}+")
         check(dHh[sl], r_pre[0][sl], f"dH {t0}+", one_ulp=False)
+
+
+def test_static_layer_backward_folded_full_size():
+    """The same static layer (T=8192, n=4, d=4096 bf16) through the folded
+    pair: post without dH, pre adding A^T dH' itself; every token of dH
+    against the oracle's exact sum at the one-ulp bound (one rounding), dF and
+    the shared records bitwise those of the unfolded pair."""
+    wl = workload("static-bf16")
+    inp = make_inputs(wl)
+    rng = np.random.default_rng(77)
+    T, n, d = wl.T, wl.n, wl.d
+    G = f32_to_bf16_bits(rng.standard_normal((T, n, d)).astype(np.float32))
+    du = f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    Hd, Fd, wd, gd, Gd = dev(inp["H"]), dev(inp["F"]), dev(inp["w"]), dev(inp["gamma"]), dev(G)
+    dH0, dF0, dwp0 = hc.post_mix_backward(Gd, Hd, Fd, wd)
+    _, dwq0, dg0 = hc.pre_mix_backward(dev(du), Hd, wd, gd, wl.eps, dH_in=dH0, out=dH0)
+    _, dF, dwp = hc.post_mix_backward(Gd, Hd, Fd, wd, h_grad=False)
+    dH, dwq, dg = hc.pre_mix_backward(dev(du), Hd, wd, gd, wl.eps, dH_out=Gd)
+    assert np.array_equal(host(dF), host(dF0)) and np.array_equal(host(dwp), host(dwp0))
+    assert np.array_equal(host(dwq), host(dwq0)) and np.array_equal(host(dg), host(dg0))
+    w64 = inp["w"].astype(np.float64)
+    oracle.set_threads(0)
+    r_post = oracle.post_mix_backward(G, inp["H"], inp["F"], w64)
+    r_pre = oracle.pre_mix_backward(du, inp["H"], w64, inp["gamma"], wl.eps, dH_in=r_post[0])
+    dHh = host(dH)
+    for t0 in range(0, T, 1024):
+        sl = slice(t0, t0 + 1024)
+        check(dHh[sl], r_pre[0][sl], f"folded dH {t0}+")

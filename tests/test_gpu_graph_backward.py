@@ -1,6 +1,7 @@
 """The backward calls inside a HIP graph (torch.cuda.CUDAGraph around the
 library's launches): a layer's gradients -- post, pre accumulating into the
-same dH, and the weight producer's -- captured once and replayed, with the
+same dH (or, folded, pre forming the whole dH from post's dH'), and the
+weight producer's -- captured once and replayed, with the
 outputs and workspaces overwritten by eager work before every replay, so each
 replay must rewrite everything it produces.  Every replay equals the eager
 calls bitwise (the library enqueues kernels only: no memsets, no host work)."""
@@ -24,8 +25,9 @@ def bf16(rng, shape, sd=1.0):
     return dev(f32_to_bf16_bits((sd * rng.standard_normal(shape)).astype(np.float32)))
 
 
+@pytest.mark.parametrize("fold", [False, True])
 @pytest.mark.parametrize("records", ["shared", "per-token"])
-def test_backward_graph_replays_equal_eager(records):
+def test_backward_graph_replays_equal_eager(records, fold):
     rng = np.random.default_rng(5 if records == "shared" else 6)
     T, n, d = 300, 4, 1024
     K = 2 * n + n * n
@@ -54,8 +56,14 @@ def test_backward_graph_replays_equal_eager(records):
     outs = [dH, dF, dg, dwp, dwq, dW, dws]
 
     def step():
-        hc.post_mix_backward(dHo, H, F, w, dH=dH, dF=dF, dw=dwp, workspace=wk)
-        hc.pre_mix_backward(du, H, w, gamma, 1e-6, dH_in=dH, out=dH, dw=dwq, dgamma=dg, workspace=wk)
+        if fold:
+            hc.post_mix_backward(dHo, H, F, w, dF=dF, dw=dwp, workspace=wk, h_grad=False)
+            hc.pre_mix_backward(du, H, w, gamma, 1e-6, dH_out=dHo, out=dH, dw=dwq, dgamma=dg,
+                                workspace=wk)
+        else:
+            hc.post_mix_backward(dHo, H, F, w, dH=dH, dF=dF, dw=dwp, workspace=wk)
+            hc.pre_mix_backward(du, H, w, gamma, 1e-6, dH_in=dH, out=dH, dw=dwq, dgamma=dg,
+                                workspace=wk)
         if per_token:
             hc.weights_backward(H, W, ws, 0.01, dwp, 1e-6, 0, dH_in=dH, out=dH, dW=dW,
                                 dw_static=dws, workspace=wwk, dw2=dwq, saved=saved)
