@@ -16,6 +16,10 @@
 // Pre:   u = gamma * x * r, r = (mean x^2 + eps)^(-1/2), x = sum_i alpha_i H_i:
 //   dy = gamma * du,  dx = r * (dy - x * r^2 * mean(dy * x)),
 //   dH_i = alpha_i dx,  dalpha_i = sum_k dx_k H_ik,  dgamma = sum_t du x r.
+// A layer's H feeds both, so its gradient is the sum of the two dH above.
+// Either post writes its share and pre adds into it, or (folded) post skips
+// it and pre forms sum_j A[j][i] dH'_j itself, which moves n rows per token
+// fewer and rounds once.
 //
 // Weight gradients take the shape of the weights: one record per token for
 // per-token weights (post: a workgroup reduction per token; pre: per-wave
