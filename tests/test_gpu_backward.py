@@ -222,3 +222,40 @@ def test_static_layer_backward_folded_full_size():
     for t0 in range(0, T, 1024):
         sl = slice(t0, t0 + 1024)
         check(dHh[sl], r_pre[0][sl], f"folded dH {t0}+")
+
+
+def test_dynamic_layer_backward_folded_full_size():
+    """The dynamic workload's shape (T=16384, n=4, d=4096 bf16) with one record
+    per token, drawn on the host: post without dH, pre forming the whole dH.
+    Every token of dH (one-ulp bound) and dF, the per-token dbeta/dA records,
+    dalpha (Cauchy-Schwarz bound) and dgamma against the oracle, in chunks of
+    2048 tokens (the gradients are per token, so a chunk is exact)."""
+    wl = workload("dynamic-bf16")
+    inp = make_inputs(wl)
+    assert "F" in inp
+    rng = np.random.default_rng(79)
+    T, n, d, K = wl.T, wl.n, wl.d, wl.K
+    w = (identity_record(n)[None, :] + 0.3 * rng.standard_normal((T, K))).astype(np.float32)
+    G = f32_to_bf16_bits(rng.standard_normal((T, n, d)).astype(np.float32))
+    du = f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    Hd, Fd, wd, Gd = dev(inp["H"]), dev(inp["F"]), dev(w), dev(G)
+    none, dF, dwp = hc.post_mix_backward(Gd, Hd, Fd, wd, h_grad=False)
+    dH, dwq, dg = hc.pre_mix_backward(dev(du), Hd, wd, dev(inp["gamma"]), wl.eps, dH_out=Gd)
+    assert none is None
+    dHh, dFh, dwph, dwqh, dgh = host(dH), host(dF), host(dwp), host(dwq), host(dg)
+    w64 = w.astype(np.float64)
+    oracle.set_threads(0)
+    rdg = np.zeros(d)
+    for t0 in range(0, T, 2048):
+        sl = slice(t0, t0 + 2048)
+        r_post = oracle.post_mix_backward(G[sl], inp["H"][sl], inp["F"][sl], w64[sl])
+        r_pre = oracle.pre_mix_backward(du[sl], inp["H"][sl], w64[sl], inp["gamma"], wl.eps,
+                                        dH_in=r_post[0])
+        check(dHh[sl], r_pre[0], f"folded dH {t0}+")
+        check(dFh[sl], r_post[1], f"dF {t0}+")
+        grad_check(dwph[sl][:, n:], r_post[2][:, n:], f"post records {t0}+")
+        assert np.all(dwph[sl][:, :n] == 0)
+        dalpha_check(dwqh[sl], r_pre[1], du[sl], inp["H"][sl], w[sl], inp["gamma"], wl.eps,
+                     f"dalpha {t0}+")
+        rdg += r_pre[2]
+    grad_check(dgh[None, :], rdg[None, :], "dgamma")
