@@ -233,6 +233,33 @@ __global__ __launch_bounds__(256) void wgrad_coef_kernel(
 
 // ---------------------------------------------------- streaming dH and dW pass
 
+// The four waves' partial dW (A x B tiles of f32x4, the same layout in every
+// wave: they share the workgroup's columns) added into wave 0's registers in
+// wave order, ((w0 + w1) + w2) + w3, through `lds` (3 * A * B * 256 floats),
+// so each workgroup writes one partial instead of four.
+template <int A, int B>
+__device__ __forceinline__ void sum_wave_partials(f32x4 (&acc)[A][B], float* lds) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (wave > 0) {
+#pragma unroll
+        for (int a = 0; a < A; ++a)
+#pragma unroll
+            for (int b = 0; b < B; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) lds[((((wave - 1) * A + a) * B + b) * 4 + j) * 64 + lane] = acc[a][b][j];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        for (int w = 0; w < 3; ++w)
+#pragma unroll
+            for (int a = 0; a < A; ++a)
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[a][b][j] += lds[(((w * A + a) * B + b) * 4 + j) * 64 + lane];
+    }
+}
+
 // fp32 storage (bf16 takes wgrad_mfma_kernel below).  One workgroup owns a
 // slice of CB = 16 V columns (16 lanes x one 16-byte vector) and a range of
 // tokens.  Each wave takes 4 tokens per step: lane l
@@ -244,7 +271,8 @@ __global__ __launch_bounds__(256) void wgrad_coef_kernel(
 // A[m = c][k = token] = dz (c = l % 16 + 16 q), B[k = token][n] = the lane's
 // hbar element e, so "virtual tile" e has output column (slice + n) V + e --
 // the lane's own columns, no shuffles.  Each wave keeps its partial dW
-// (2 x V tiles) and writes it to part[(split * 4 + wave)][K][d] at the end.
+// (2 x V tiles); at the end the workgroup's four are added (wave order) and
+// written to part[split][K][d].
 template <int N, typename S>
 __global__ __launch_bounds__(256) void wgrad_stream_kernel(
     const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, const float* __restrict__ dz,
@@ -254,6 +282,7 @@ __global__ __launch_bounds__(256) void wgrad_stream_kernel(
     constexpr int K = 2 * N + N * N;
     constexpr int CB = 16 * V;                       // columns per workgroup
     __shared__ __attribute__((aligned(16))) uint8_t wl[K * CB * SB];
+    __shared__ float wsum[3 * 2 * V * 256];          // sum_wave_partials
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, cl = lane & 15;
@@ -346,10 +375,11 @@ __global__ __launch_bounds__(256) void wgrad_stream_kernel(
             acc[1][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bv, acc[1][e], 0, 0, 0);
         }
     }
-    // this wave's partial: C[m = 4 g + j][n = cl] of tile (q, e) is
+    // the workgroup's partial: C[m = 4 g + j][n = cl] of tile (q, e) is
     // dW[c = 16 q + 4 g + j][column cv * V + e]
-    float* out = part + ((int64_t)blockIdx.y * 4 + wave) * K * (int64_t)d;
-    if (col_ok) {
+    sum_wave_partials(acc, wsum);
+    float* out = part + (int64_t)blockIdx.y * K * (int64_t)d;
+    if (wave == 0 && col_ok) {
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -408,6 +438,7 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(
     // B operands of the dhbar product: wl[(q * 16 + cl) * 32 + c] = W[c][8 (slice + cl) + q],
     // zero for c >= K and for columns past d
     __shared__ __attribute__((aligned(16))) uint16_t wl[8 * 16 * 32];
+    __shared__ float wsum[3 * MT * 8 * 256];         // sum_wave_partials
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, cl = lane & 15;
@@ -553,9 +584,10 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(
             }
         }
     }
-    // this wave's partial: element j of tile (m, q) is dW[c = 16 m + 4 g + j][8 cv + q]
-    float* out = part + ((int64_t)blockIdx.y * 4 + wave) * K * (int64_t)d;
-    if (col_ok) {
+    // the workgroup's partial: element j of tile (m, q) is dW[c = 16 m + 4 g + j][8 cv + q]
+    sum_wave_partials(acc, wsum);
+    float* out = part + (int64_t)blockIdx.y * K * (int64_t)d;
+    if (wave == 0 && col_ok) {
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -625,7 +657,7 @@ inline int64_t splits_of(int64_t T) {
 
 // Workspace layout (floats): P [T][n][K] | r [T][n] | dz [T][K] |
 // dw_static partials [coefficient workgroups][K] | ab [T][2n] | Sinkhorn
-// scratch [iters][T][16] | dW partials [4 splits][K][d] | the two sums'
+// scratch [iters][T][16] | dW partials [splits][K][d] | the two sums'
 // level scratch.  Every region starts 16-byte aligned.
 struct WgSpace {
     int64_t P, r, dz, dl, ab, scr, part, tmp, tmp2, total;
@@ -641,7 +673,7 @@ inline WgSpace wg_space(int64_t T, int n, int d, int iters) {
     w.ab = w.dl + up4(coef_blocks(T) * K);
     w.scr = w.ab + up4(T * 2 * n);
     w.part = w.scr + up4(int64_t(iters) * T * kSlot);
-    const int64_t rows = splits_of(T) * 4;
+    const int64_t rows = splits_of(T);
     w.tmp = w.part + up4(rows * K * d);
     w.tmp2 = w.tmp + up4(sum_rows_tmp_floats(rows, K * d));
     w.total = w.tmp2 + up4(sum_rows_tmp_floats(coef_blocks(T), K));
@@ -716,7 +748,7 @@ hipError_t launch_weights_backward(const void* H, const void* W, const float* w_
     if (e != hipSuccess) return e;
     // (4) fixed-order sums: dW over the partials, dw_static over the
     // coefficient workgroups' partials, in shared launches
-    const SumJob jobs[2] = {{ws + sp.part, splits * 4, K * d, ws + sp.tmp, dW, nullptr, 0},
+    const SumJob jobs[2] = {{ws + sp.part, splits, K * d, ws + sp.tmp, dW, nullptr, 0},
                            {ws + sp.dl, coef_blocks(T), K, ws + sp.tmp2, dws, nullptr, 0}};
     return launch_sum_rows2(jobs, 2, s);
 }
