@@ -29,3 +29,18 @@ def test_layer_bytes_are_14_state_units_at_n4():
     writes the state: (n+1) + (2n+1) = 3n+2 hidden-width vectors per token."""
     n, d, s = 4, 4096, 2
     assert traffic.pre_bytes(n, d, s) + traffic.post_bytes(n, d, s) == 14 * d * s == 114688
+
+
+def test_backward_bytes_count_each_row_moved():
+    """Backward rows per token at n = 4: post reads dH', H and F (2n+1) and
+    writes dH and dF (n+1), or only dF when the pre gradient forms dH; pre
+    reads du, H and dH_in or dH' (2n+1) and writes dH (n).  Folding removes
+    exactly the n rows of post's dH write from the layer."""
+    n, d, s = 4, 4096, 2
+    rec = traffic.record_bytes(n)
+    assert traffic.post_bwd_bytes(n, d, s) == (3 * n + 2) * d * s + rec == 114688 + rec
+    assert traffic.post_bwd_bytes(n, d, s, h_grad=False) == (2 * n + 2) * d * s + rec == 81920 + rec
+    assert traffic.pre_bwd_bytes(n, d, s, True) == (3 * n + 1) * d * s + rec == 106496 + rec
+    unfolded = traffic.post_bwd_bytes(n, d, s) + traffic.pre_bwd_bytes(n, d, s, True)
+    folded = traffic.post_bwd_bytes(n, d, s, h_grad=False) + traffic.pre_bwd_bytes(n, d, s, True)
+    assert unfolded - folded == n * d * s
