@@ -634,13 +634,24 @@ hipError_t launch_sum_rows2(const SumJob* jobs, int njobs, hipStream_t s) {
 
 namespace {
 
+// Per-token records: post's gradient runs fastest with at most 16 waves per
+// CU, two 512-thread workgroups, held there by an LDS request (160 KiB per
+// CU) that the kernel does not use.  Measured at 16384 tokens, n = 4, d =
+// 4096 bf16: two workgroups per CU 240.0 us, three (the register limit)
+// 248.7, one 267.0, four 262.6; shared records showed no difference.
+inline size_t post_token_lds(int block) {
+    const int per_cu = 16 / (block / 64);
+    return per_cu >= 2 ? (size_t)(160 * 1024) / (per_cu + 1) + 1024 : 0;
+}
+
 template <int N, typename S, int VPT, bool HG>
 hipError_t post_bwd_go2(RowCfg c, const void* dHo, const void* H, const void* F, const float* w,
                         int64_t ws, void* dH, void* dF, float* dw, float* part, int64_t T, int d,
                         int group, hipStream_t s) {
     const dim3 grid = grid_of((T + group - 1) / group);
     if (ws != 0)
-        return launch(post_bwd_kernel<N, S, VPT, true, HG>, grid, dim3(c.block), 0, s,
+        return launch(post_bwd_kernel<N, S, VPT, true, HG>, grid, dim3(c.block),
+                      post_token_lds(c.block), s,
                       static_cast<const uint8_t*>(dHo), static_cast<const uint8_t*>(H),
                       static_cast<const uint8_t*>(F), w, ws, static_cast<uint8_t*>(dH),
                       static_cast<uint8_t*>(dF), dw, part, T, d, group);
