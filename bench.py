@@ -7,7 +7,10 @@ A step is one pass of the path over one batch of synthetic tokens whose
 inputs are already resident in HBM:
   static-bf16   pre (read-mix + RMSNorm) then post (stream-mix + write-back)
                 with shared static weights; F is a given tensor (default)
-  dynamic-bf16  per-token weights (MFMA projection + tanh), then pre, post
+  dynamic-bf16  per-token weights: pre, then post fused with the projection
+                and tanh that form the next layer's records from H' on chip
+                (steady state of a layer loop; --weights-pass times the
+                separate weights kernel, pre and post instead)
   dynamic-fp8   the same with FP8 E4M3 H, W and F
   mhc-bf16      Sinkhorn records from per-token logits, then pre, post
   chain-bf16    78 layers of pre, tanh block, post (reported, not graded)
@@ -44,6 +47,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 KERNEL_SOURCES = {
     "pre_mix": "hc_rows.hip", "post_mix": "hc_rows.hip", "post_pre_mix": "hc_rows.hip",
+    "post_mix_weights": "hc_post_weights.hip",
     "block_tanh": "hc_rows.hip", "weights": "hc_weights.hip", "sinkhorn": "hc_weights.hip",
     "post_mix_backward": "hc_backward.hip", "pre_mix_backward": "hc_backward.hip",
     "sum_records": "hc_backward.hip", "weights_backward": "hc_weights_bwd.hip",
@@ -125,6 +129,7 @@ XCDS = 8
 
 # kernel name in the traces, where it differs from "<kernel>_kernel<"
 KERNEL_TAGS = {"post_mix_backward": "post_bwd_kernel<", "pre_mix_backward": "pre_bwd_kernel<",
+               "post_mix_weights": "post_weights_kernel<",
                "weights_backward_stream": "wgrad_mfma_kernel<"}
 
 
@@ -240,6 +245,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, kernel: str, workload: st
     alg = {"pre_mix": tr.pre_bytes(wl.n, wl.d, wl.elem_bytes, per_tok),
            "post_mix": tr.post_bytes(wl.n, wl.d, wl.elem_bytes, per_tok),
            "weights": tr.weights_bytes(wl.n, wl.d, wl.elem_bytes),
+           "post_mix_weights": tr.post_weights_bytes(wl.n, wl.d, wl.elem_bytes),
            "post_pre_mix": tr.post_pre_bytes(wl.n, wl.d, wl.elem_bytes),
            "post_mix_backward": tr.post_bwd_bytes(wl.n, wl.d, wl.elem_bytes, h_grad=not fold),
            "pre_mix_backward": tr.pre_bwd_bytes(wl.n, wl.d, wl.elem_bytes, True),
@@ -274,6 +280,46 @@ def summarize_counters(fetch_csv: str, write_csv: str, kernel: str, workload: st
         f"{traffic / alg:.4f} x algorithmic")
 
 
+def summarize_drift(drift_json: str, cmds: list):
+    """The 78-layer chain's per-layer parity and drift (written by
+    tests/test_gpu_chain.py with HC_DRIFT_OUT set) as
+    profiles/chain-bf16_drift.{json,md}."""
+    with open(drift_json) as fh:
+        rec = json.load(fh)
+    rec["commands"] = cmds
+    rows = rec["rows"]
+    d16 = [r["drift_vs_bf16_storing_fp64"] for r in rows]
+    d64 = [r["drift_vs_pure_fp64"] for r in rows]
+    rec["max_drift_vs_bf16_storing_fp64"] = max(d16)
+    rec["max_drift_vs_pure_fp64"] = max(d64)
+    base = os.path.join(PROFILES, "chain-bf16_drift")
+    with open(base + ".json", "w") as fh:
+        json.dump(rec, fh, indent=1)
+    with open(base + ".md", "w") as fh:
+        fh.write("# Per-layer parity and drift of the 78-layer chain (chain-bf16)\n\n")
+        fh.write(f"T = {rec['T']}, n = {rec['n']}, d = {rec['d']}, bf16 storage; "
+                 f"{rec['sample_tokens']} sampled tokens (tokens are independent, so the sample is "
+                 "exact for them).  Error metric: max |gpu - ref| / max(|ref|, rms of the "
+                 "reference row).\n\n")
+        fh.write("Commands (paths relative to the repository root):\n\n")
+        for c in cmds:
+            fh.write(f"    {c}\n")
+        fh.write("\nColumns: single-layer parity of pre, block and post with the oracle fed the "
+                 "GPU's own layer input (the pass criterion, bf16 tolerance 2e-2); drift of the "
+                 "GPU chain against an fp64 chain that stores u, F and H' to bf16 after every step "
+                 f"(bound {rec['drift_bound']}); drift against a pure fp64 chain with no store "
+                 "rounding (reported only).\n\n")
+        fh.write(f"Largest drift: {max(d16):.3g} against the bf16-storing chain, "
+                 f"{max(d64):.3g} against pure fp64.\n\n")
+        fh.write("| layer | parity pre | parity block | parity post | drift vs bf16-storing fp64 | "
+                 "drift vs pure fp64 |\n|---|---|---|---|---|---|\n")
+        for r in rows:
+            fh.write(f"| {r['layer']} | {r['parity_pre']:.3g} | {r['parity_block']:.3g} | "
+                     f"{r['parity_post']:.3g} | {r['drift_vs_bf16_storing_fp64']:.3g} | "
+                     f"{r['drift_vs_pure_fp64']:.3g} |\n")
+    log(f"[bench] wrote {base}.md: max drift {max(d16):.3g} (bf16-storing), {max(d64):.3g} (fp64)")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,12 +340,21 @@ def main():
                     help="with --backward: post backward writes its H gradient and the pre "
                          "backward adds into it (by default post leaves dH to the pre backward, "
                          "which forms the write-back's share from dH' itself)")
+    ap.add_argument("--weights-pass", action="store_true",
+                    help="dynamic workloads: a separate weights kernel reads H before pre and "
+                         "post (by default post forms the next layer's records)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph (torch.cuda.CUDAGraph) and time replays")
+    ap.add_argument("--all", metavar="OUT_JSONL",
+                    help="run the five configurations (tiny-f32, static-bf16, dynamic-bf16, "
+                         "mhc-bf16, chain-bf16) with parity, invariants and the oracle baseline, "
+                         "one JSON record per configuration into OUT_JSONL")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
     ap.add_argument("--summarize-mfma", metavar="PMC_CSV",
                     help="summarise a rocprofv3 --pmc run of MFMA/LDS counters into profiles/ and exit")
+    ap.add_argument("--summarize-drift", metavar="DRIFT_JSON",
+                    help="summarise the chain test's per-layer drift (HC_DRIFT_OUT) into profiles/ and exit")
     ap.add_argument("--kernel", default="post_mix", help="kernel for --summarize-counters/--summarize-mfma")
     ap.add_argument("--command", action="append", default=[],
                     help="profiling command to record in the summary (repeatable)")
@@ -312,6 +367,9 @@ def main():
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma, args.kernel, args.workload, args.command)
         return
+    if args.summarize_drift:
+        summarize_drift(args.summarize_drift, args.command)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this path runs on one GPU "
@@ -319,17 +377,35 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from hyper_connections_amd import hc, traffic, workloads
+    from hyper_connections_amd import hc
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     hc.lib()   # raises if the library is not built
 
-    wl = workloads.workload(args.workload)
+    if args.all:
+        run_all(args)
+        return
+    out, wl, inp = run_workload(args, args.workload)
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds,
+                                           one_thread_s=args.cpu_seconds / 2
+                                           if wl.name in ONE_THREAD_BASELINE else 0.0)
+    print(json.dumps(out), flush=True)
+
+
+def run_workload(args, name: str):
+    """Time one workload as the options ask; returns (the JSON record
+    without the CPU baseline, the workload, its host inputs)."""
+    import numpy as np
+    import torch
+
+    from hyper_connections_amd import hc, traffic, workloads
+
+    wl = workloads.workload(name)
     n, d, T, s = wl.n, wl.d, wl.T, wl.elem_bytes
     K = wl.K
 
@@ -388,6 +464,7 @@ def main():
         "pre_mix": traffic.pre_bytes(n, d, s, per_tok) * T,
         "post_mix": traffic.post_bytes(n, d, s, per_tok) * T,
         "post_pre_mix": traffic.post_pre_bytes(n, d, s) * T,
+        "post_mix_weights": traffic.post_weights_bytes(n, d, s) * T,
         "weights": traffic.weights_bytes(n, d, s) * T,
         "sinkhorn": traffic.sinkhorn_bytes(n) * T,
         "block_tanh": 2 * d * s * T,
@@ -457,10 +534,23 @@ def main():
     elif wl.kind == "static":
         ops = [("pre_mix", lambda b: hc.pre_mix(b["H"], w_static, gamma, wl.eps, out=b["u"])),
                ("post_mix", lambda b: hc.post_mix(b["H"], b["F"], w_static, out=b["O"]))]
-    elif wl.kind == "dynamic":
+    elif wl.kind == "dynamic" and args.weights_pass:
         ops = [("weights", lambda b: hc.weights(b["H"], Wp, ws, wl.scale, wl.eps, 0, out=b["w"])),
                ("pre_mix", lambda b: hc.pre_mix(b["H"], b["w"], gamma, wl.eps, out=b["u"])),
                ("post_mix", lambda b: hc.post_mix(b["H"], b["F"], b["w"], out=b["O"]))]
+    elif wl.kind == "dynamic":
+        # a layer at steady state: its records were formed by the previous
+        # layer's write-back; this write-back forms the next layer's (into the
+        # next buffer set, whose step comes next).  The first layer's records
+        # come from the weights kernel, untimed.
+        for i, b in enumerate(bufs):
+            hc.weights(b["H"], Wp, ws, wl.scale, wl.eps, 0, out=b["w"])
+            b["next"] = bufs[(i + 1) % sets]
+        torch.cuda.synchronize()
+        ops = [("pre_mix", lambda b: hc.pre_mix(b["H"], b["w"], gamma, wl.eps, out=b["u"])),
+               ("post_mix_weights", lambda b: hc.post_mix_weights(
+                   b["H"], b["F"], b["w"], Wp, ws, wl.scale, wl.eps, 0, out=b["O"],
+                   w_out=b["next"]["w"]))]
     elif wl.kind == "mhc":
         ops = [("sinkhorn", lambda b: hc.sinkhorn(b["logits"], n, wl.iters, out=b["w"])),
                ("pre_mix", lambda b: hc.pre_mix(b["H"], b["w"], gamma, wl.eps, out=b["u"])),
@@ -558,7 +648,14 @@ def main():
 
     hc_kernels = [k for k in kms if k != "block_tanh"]
     launches = {k: c // args.steps for k, c in bare.counts.items()}
-    step_bytes = sum(launch_bytes[k] * launches[k] for k in hc_kernels)
+    if args.backward or args.fused or wl.kind == "chain":
+        # the kernels' own bytes: a gradient step, a fused layer boundary, or
+        # the 78-layer chain (its tanh block left out)
+        step_bytes = sum(launch_bytes[k] * launches[k] for k in hc_kernels)
+    else:
+        # one layer of the method, graded on the bytes the method itself must
+        # move however the step is split into kernels
+        step_bytes = traffic.method_bytes(wl.kind, n, d, s) * T
     kernels = {}
     for k, ms in kms.items():
         gbps = launch_bytes[k] / (ms * 1e-3) / 1e9
@@ -591,8 +688,9 @@ def main():
         "config": {"workload": wl.name, "T": T, "n": n, "d": d, "weights": wl.kind,
                    "layers": wl.layers, "buffer_sets": sets, "fused": bool(args.fused),
                    "graph": bool(args.graph), "backward": bool(args.backward),
-                   "fold": fold},
+                   "fold": fold, "weights_pass": bool(args.weights_pass)},
         "us_per_layer": round(ms_step * 1e3 / wl.layers, 3),
+        "step_bytes": int(step_bytes),
         "hbm_gbps": round(step_gbps, 1),
         "frac_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "copy_gbps": round(copy_gbps, 1),
@@ -604,21 +702,31 @@ def main():
         "cpu_baseline": None,
     }
 
-    # ------------------------------------------------ oracle CPU baseline
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    return out, wl, inp
 
 
-def cpu_baseline(wl, inp, budget_s: float):
+def cpu_model() -> str:
+    """The host CPU's model name as the kernel reports it."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def oracle_rate(wl, inp, budget_s: float):
     """The oracle, as it stands, on the host cores: whole passes over the
-    workload's tokens (chunks of 1024) until the time budget is used."""
+    workload's tokens (chunks of 1024) until the time budget is used.
+    Returns (tokens/s, token passes, seconds)."""
     import numpy as np
 
     import oracle
     from hyper_connections_amd import workloads
 
-    threads = oracle.get_threads()
     chunk = 1024
     done, t0 = 0, time.perf_counter()
     layers = 0
@@ -656,10 +764,224 @@ def cpu_baseline(wl, inp, budget_s: float):
     rate = done / el
     if wl.kind == "chain":
         rate /= wl.layers   # one token through all layers
+    return rate, done, el
+
+
+# workloads whose CPU baseline also gets a one-thread run
+ONE_THREAD_BASELINE = ("tiny-f32", "static-bf16")
+
+
+def cpu_baseline(wl, inp, budget_s: float, one_thread_s: float = 0.0):
+    """The oracle CPU baseline: all host threads OpenMP gives it, plus (when
+    one_thread_s > 0) a run on one thread; the CPU model is recorded."""
+    import oracle
+
+    threads = oracle.get_threads()
+    rate, done, el = oracle_rate(wl, inp, budget_s)
     log(f"[bench] oracle CPU baseline: {done} token passes in {el:.1f}s on {threads} threads")
-    return {"value": round(rate, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} token passes of {wl.name} ({wl.T} tokens per full pass, chunks of "
-                      f"1024), fp64 oracle, {el:.1f}s wall"}
+    rec = {"value": round(rate, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{done} token passes of {wl.name} ({wl.T} tokens per full pass, chunks of "
+                     f"1024), fp64 oracle, {el:.1f}s wall",
+           "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+    if one_thread_s > 0:
+        oracle.set_threads(1)
+        try:
+            r1, d1, e1 = oracle_rate(wl, inp, one_thread_s)
+        finally:
+            oracle.set_threads(threads)
+        log(f"[bench] oracle CPU baseline, one thread: {d1} token passes in {e1:.1f}s")
+        rec["value_1_thread"] = round(r1, 1)
+        rec["sample_1_thread"] = f"{d1} token passes on 1 thread, {e1:.1f}s wall"
+    return rec
+
+
+# --------------------------------------------------------------- --all mode
+
+# the five configurations the metric is defined on, in order
+ALL_CONFIGS = ("tiny-f32", "static-bf16", "dynamic-bf16", "mhc-bf16", "chain-bf16")
+
+
+def _rel_err(got, ref) -> float:
+    """max |got - ref| / max(|ref|, rms of the reference row) (rows: last
+    axis); the error metric of the parity tests."""
+    import numpy as np
+    g, r = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    if g.size == 0:
+        return 0.0
+    rms = np.sqrt(np.mean(r * r, axis=-1, keepdims=True))
+    sc = np.maximum(np.abs(r), rms)
+    sc = np.where(sc == 0, 1.0, sc)
+    return float(np.max(np.abs(g - r) / sc))
+
+
+def verify(wl, inp) -> dict:
+    """One untimed pass of the workload's path on the GPU, compared with the
+    oracle: the largest error of every output over every token (the chain:
+    every layer on a 256-token sample, plus its drift against the
+    bf16-storing fp64 chain), and the workload's bit-exact invariants."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from hyper_connections_amd import hc, workloads
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        if a.dtype == np.uint8:
+            return torch.from_numpy(a).view(torch.float8_e4m3fn).cuda()
+        return torch.from_numpy(a.astype(np.float32)).cuda()
+
+    def host(t):
+        t = t.detach().contiguous().cpu()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        if t.dtype == torch.float8_e4m3fn:
+            return t.view(torch.uint8).numpy()
+        return t.numpy()
+
+    tol = {"f32": 1e-5, "bf16": 2e-2, "fp8": 2.0 ** -3}[wl.dtype]
+    errs, inv = {}, {}
+    g = inp["gamma"]
+    gd = dev(g)
+    chunk = 4096
+
+    def chunked(name, got_fn, ref_fn):
+        e = 0.0
+        for c0 in range(0, wl.T, chunk):
+            sl = slice(c0, min(wl.T, c0 + chunk))
+            e = max(e, _rel_err(oracle.widen(got_fn(sl)) if got_fn(sl).dtype != np.float32 or
+                                wl.dtype == "f32" else got_fn(sl), ref_fn(sl)))
+        errs[name] = e
+
+    if wl.kind in ("static", "dynamic", "mhc"):
+        H, Hd = inp["H"], dev(inp["H"])
+        if wl.kind == "static":
+            w = inp["w"]
+            wd = dev(w)
+            u = hc.pre_mix(Hd, wd, gd, wl.eps)
+            F = inp["F"] if "F" in inp else host(hc.block_tanh(u))
+            Fd = dev(F)
+            O = hc.post_mix(Hd, Fd, wd)
+            w64 = lambda sl: w.astype(np.float64)   # noqa: E731
+        elif wl.kind == "dynamic":
+            F, Fd = inp["F"], dev(inp["F"])
+            Wd, wsd = dev(inp["W"]), dev(inp["w_static"])
+            rec = hc.weights(Hd, Wd, wsd, wl.scale, wl.eps, 0)      # the first layer's records
+            u = hc.pre_mix(Hd, rec, gd, wl.eps)
+            O, rec2 = hc.post_mix_weights(Hd, Fd, rec, Wd, wsd, wl.scale, wl.eps, 0)
+            rh, r2h = host(rec), host(rec2)
+            errs["records"] = max(_rel_err(rh[c:c + chunk], oracle.weights(
+                H[c:c + chunk], inp["W"], inp["w_static"].astype(np.float64), wl.scale, wl.eps, 0))
+                for c in range(0, wl.T, chunk))
+            w64 = lambda sl: rh[sl].astype(np.float64)   # noqa: E731
+        else:
+            F, Fd = inp["F"], dev(inp["F"])
+            rec = hc.sinkhorn(dev(inp["logits"]), wl.n, wl.iters)
+            u = hc.pre_mix(Hd, rec, gd, wl.eps)
+            O = hc.post_mix(Hd, Fd, rec)
+            rh = host(rec)
+            errs["records"] = _rel_err(rh, oracle.sinkhorn(inp["logits"].astype(np.float64), wl.n,
+                                                           wl.iters))
+            A = rh[:, 2 * wl.n:].reshape(wl.T, wl.n, wl.n).astype(np.float64)
+            inv["column_sums_within_1e-6"] = bool(np.max(np.abs(A.sum(axis=1) - 1)) <= 1e-6)
+            w64 = lambda sl: rh[sl].astype(np.float64)   # noqa: E731
+        uh, Oh = host(u), host(O)
+        errs["u"] = max(_rel_err(oracle.widen(uh[c:c + chunk]), oracle.pre_mix(
+            H[c:c + chunk], w64(slice(c, c + chunk)), g, wl.eps)) for c in range(0, wl.T, chunk))
+        errs["H_out"] = max(_rel_err(oracle.widen(Oh[c:c + chunk]), oracle.post_mix(
+            H[c:c + chunk], F[c:c + chunk], w64(slice(c, c + chunk)))) for c in range(0, wl.T, chunk))
+        if wl.kind == "dynamic":
+            errs["next_records"] = max(_rel_err(r2h[c:c + chunk], oracle.weights(
+                Oh[c:c + chunk], inp["W"], inp["w_static"].astype(np.float64), wl.scale, wl.eps, 0))
+                for c in range(0, wl.T, chunk))
+            # W = 0: tanh(0) = 0, every record is w_static bitwise
+            Z = torch.zeros_like(Wd)
+            _, rz = hc.post_mix_weights(Hd[:256], Fd[:256], rec[:256], Z, wsd, wl.scale, wl.eps, 0)
+            inv["zero_projection_records_equal_w_static"] = bool(
+                np.array_equal(host(rz), np.broadcast_to(inp["w_static"], (256, wl.K))))
+        # identity invariants on copies of stream 0 (any workload's H)
+        x = H[:256, :1, :]
+        copies, one = dev(np.repeat(x, wl.n, axis=1)), dev(x.copy())
+        idn, id1 = dev(workloads.identity_record(wl.n)), dev(workloads.identity_record(1))
+        Fi = dev(np.ascontiguousarray(F[:256]))
+        post_n, post_1 = host(hc.post_mix(copies, Fi, idn)), host(hc.post_mix(one, Fi, id1))
+        ref_xf = (oracle.round_f32 if wl.dtype == "f32" else oracle.round_bf16)(
+            oracle.widen(x[:, 0, :]) + oracle.widen(F[:256]))
+        inv["identity_post_equals_stored_x_plus_F"] = bool(all(
+            np.array_equal(post_n[:, i, :], ref_xf) for i in range(wl.n)))
+        inv["identity_post_equals_one_stream"] = bool(np.array_equal(post_n[:, :1, :], post_1))
+        inv["alpha_e0_pre_equals_one_stream"] = bool(np.array_equal(
+            host(hc.pre_mix(copies, idn, gd, wl.eps)), host(hc.pre_mix(one, id1, gd, wl.eps))))
+    else:   # the chain: per-layer parity on a sample, drift, identity chain
+        Ha, Hb = dev(inp["H"]), torch.empty_like(dev(inp["H"]))
+        u = torch.empty((wl.T, wl.d), dtype=Ha.dtype, device="cuda")
+        F = torch.empty_like(u)
+        rng = np.random.default_rng(wl.seed)
+        idx = np.sort(rng.choice(wl.T, 256, replace=False))
+        ti = torch.from_numpy(idx).cuda()
+        Hb16 = inp["H"][idx]
+        ep, eb, eo, drift = 0.0, 0.0, 0.0, []
+        for layer in range(wl.layers):
+            w = workloads.layer_record(wl, layer)
+            w64, wd = w.astype(np.float64), dev(w)
+            hc.pre_mix(Ha, wd, gd, wl.eps, out=u)
+            hc.block_tanh(u, out=F)
+            hc.post_mix(Ha, F, wd, out=Hb)
+            Hin, us, Fs, Ho = host(Ha[ti]), host(u[ti]), host(F[ti]), host(Hb[ti])
+            ep = max(ep, _rel_err(oracle.widen(us), oracle.pre_mix(Hin, w64, g, wl.eps)))
+            eb = max(eb, _rel_err(oracle.widen(Fs), oracle.block_tanh(us)))
+            eo = max(eo, _rel_err(oracle.widen(Ho), oracle.post_mix(Hin, Fs, w64)))
+            uo = oracle.round_bf16(oracle.pre_mix(Hb16, w64, g, wl.eps))
+            Hb16 = oracle.round_bf16(oracle.post_mix(Hb16, oracle.round_bf16(oracle.block_tanh(uo)), w64))
+            drift.append(_rel_err(oracle.widen(Ho), oracle.widen(Hb16)))
+            Ha, Hb = Hb, Ha
+        errs.update({"u": ep, "F": eb, "H_out": eo})
+        inv["max_drift_vs_bf16_storing_fp64"] = max(drift)
+        inv["drift_at_last_layer"] = drift[-1]
+    tol_pass = all(v <= (1e-5 if k in ("records", "next_records") else tol) for k, v in errs.items())
+    return {"max_rel_err": {k: float(f"{v:.3g}") for k, v in errs.items()},
+            "tolerance": {"storage": tol, "records": 1e-5}, "parity_pass": bool(tol_pass),
+            "invariants": inv,
+            "invariants_pass": bool(all(v for v in inv.values() if isinstance(v, bool)))}
+
+
+def run_all(args):
+    """One record per configuration (tokens/s, algorithmic and counter
+    GB/s, largest error of every output, invariants, the oracle's rate) as
+    JSON lines into args.all; the headline configuration's record is the
+    one line printed on stdout."""
+    import copy
+
+    import torch
+
+    head = None
+    with open(args.all, "w") as fh:
+        for name in ALL_CONFIGS:
+            a = copy.copy(args)
+            a.workload = name
+            a.fused = a.backward = a.graph = a.weights_pass = False
+            out, wl, inp = run_workload(a, name)
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            out["verify"] = verify(wl, inp)
+            torch.cuda.empty_cache()
+            dom = out["roofline"]["kernel"]
+            tr = out["roofline"]["traffic"]
+            out["counter_gbps"] = (round(tr / (out["kernels"][dom]["us"] * 1e-6) / 1e9, 1)
+                                   if tr else None)
+            out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds,
+                                               one_thread_s=args.cpu_seconds / 2
+                                               if name in ONE_THREAD_BASELINE else 0.0)
+            log(f"[bench] {name}: {out['value']:.4g} tokens/s, {out['frac_hbm_peak']:.1%} of 8 TB/s, "
+                f"parity {out['verify']['parity_pass']}, invariants {out['verify']['invariants_pass']}")
+            fh.write(json.dumps(out) + "\n")
+            fh.flush()
+            if name == "static-bf16":
+                head = out
+            del inp
+    print(json.dumps(head), flush=True)
 
 
 if __name__ == "__main__":

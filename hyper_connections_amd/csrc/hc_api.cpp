@@ -10,6 +10,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 
 #include "hc_launch.h"
 
@@ -30,13 +31,13 @@ bool overlap(Span a, Span b) {
     return x < y + static_cast<uintptr_t>(b.bytes) && y < x + static_cast<uintptr_t>(a.bytes);
 }
 
-int elem_bytes(hc_dtype dt) { return dt == HC_F32 ? 4 : (dt == HC_FP8 ? 1 : 2); }
-int vec_elems(hc_dtype dt) { return 16 / elem_bytes(dt); }
+int elem_bytes(int dt) { return dt == HC_F32 ? 4 : (dt == HC_FP8 ? 1 : 2); }
+int vec_elems(int dt) { return 16 / elem_bytes(dt); }
 
 // The streaming calls (pre, post, post+pre, tanh block) take every storage
 // dtype; the weight producer and the gradients take fp32 and bf16.
-bool dtype_ok(hc_dtype dt) { return dt == HC_F32 || dt == HC_BF16 || dt == HC_FP8; }
-bool dtype_wide(hc_dtype dt) { return dt == HC_F32 || dt == HC_BF16; }
+bool dtype_ok(int dt) { return dt == HC_F32 || dt == HC_BF16 || dt == HC_FP8; }
+bool dtype_wide(int dt) { return dt == HC_F32 || dt == HC_BF16; }
 
 int record_len(int n) { return 2 * n + n * n; }
 
@@ -46,7 +47,7 @@ int64_t record_span(int64_t T, int64_t stride, int K) {
 }
 
 // Shape checks shared by the row kernels.  Order of checks: dtype, n, d, T.
-hc_status check_nd(int32_t n, int32_t d, int64_t T, hc_dtype dt) {
+hc_status check_nd(int32_t n, int32_t d, int64_t T, int dt) {
     if (!dtype_ok(dt)) return HC_ERR_DTYPE;
     if (n < 1 || n > HC_MAX_STREAMS) return HC_ERR_SHAPE;
     if (d < 1 || d > HC_MAX_HIDDEN || d % vec_elems(dt) != 0) return HC_ERR_SHAPE;
@@ -65,12 +66,23 @@ bool eps_ok(float eps) { return std::isfinite(eps) && eps > 0.0f; }
 
 hc_status from_hip(hipError_t e) { return e == hipSuccess ? HC_OK : HC_ERR_HIP; }
 
+// The value a C caller passed for an enum parameter.  C lets any int through
+// an enum type; in C++ reading an enum object that holds a value outside its
+// enumerators' range is undefined, so the argument is read through its bytes.
+template <typename E>
+int enum_value(const E& e) {
+    int v = 0;
+    static_assert(sizeof(E) == sizeof(int), "enum parameters are int-sized");
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
+
 }  // namespace
 
 extern "C" {
 
-const char* hc_status_str(hc_status s) {
-    switch (s) {
+const char* hc_status_str(hc_status status) {
+    switch (enum_value(status)) {
         case HC_OK: return "HC_OK: success";
         case HC_ERR_NULL: return "HC_ERR_NULL: a required pointer is NULL";
         case HC_ERR_SHAPE: return "HC_ERR_SHAPE: n, d or a stride is outside the supported set";
@@ -83,10 +95,11 @@ const char* hc_status_str(hc_status s) {
     return "HC_ERR_UNKNOWN: unknown status code";
 }
 
-int32_t hc_abi_version(void) { return 3; }
+int32_t hc_abi_version(void) { return 4; }
 
 hc_status hc_pre_mix(const void* H, const float* w, int64_t w_stride, const float* gamma, float eps,
-                     void* u, int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream) {
+                     void* u, int64_t T, int32_t n, int32_t d, hc_dtype dt_arg, void* stream) {
+    const int dt = enum_value(dt_arg);
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
     const int K = record_len(n);
@@ -105,7 +118,8 @@ hc_status hc_pre_mix(const void* H, const float* w, int64_t w_stride, const floa
 }
 
 hc_status hc_post_mix(const void* H, const void* F, const float* w, int64_t w_stride, void* H_out,
-                      int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream) {
+                      int64_t T, int32_t n, int32_t d, hc_dtype dt_arg, void* stream) {
+    const int dt = enum_value(dt_arg);
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
     const int K = record_len(n);
@@ -125,7 +139,8 @@ hc_status hc_post_mix(const void* H, const void* F, const float* w, int64_t w_st
 hc_status hc_post_pre_mix(const void* H, const void* F, const float* w, int64_t w_stride,
                           const float* w_next, int64_t w_next_stride, const float* gamma_next,
                           float eps, void* H_out, void* u_next, int64_t T, int32_t n, int32_t d,
-                          hc_dtype dt, void* stream) {
+                          hc_dtype dt_arg, void* stream) {
+    const int dt = enum_value(dt_arg);
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
     const int K = record_len(n);
@@ -152,7 +167,8 @@ hc_status hc_post_pre_mix(const void* H, const void* F, const float* w, int64_t 
 
 hc_status hc_weights(const void* H, const void* W, const float* w_static, float scale, float eps,
                      int32_t sinkhorn_iters, float* w_out, int64_t T, int32_t n, int32_t d,
-                     hc_dtype dt, void* stream) {
+                     hc_dtype dt_arg, void* stream) {
+    const int dt = enum_value(dt_arg);
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
     if (!eps_ok(eps) || !std::isfinite(scale)) return HC_ERR_ARG;
@@ -177,8 +193,9 @@ int64_t hc_weights_saved_bytes(int64_t T, int32_t n) {
 
 hc_status hc_weights_save(const void* H, const void* W, const float* w_static, float scale,
                           float eps, int32_t sinkhorn_iters, float* w_out, float* saved,
-                          int64_t saved_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
+                          int64_t saved_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt_arg,
                           void* stream) {
+    const int dt = enum_value(dt_arg);
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
     if (!eps_ok(eps) || !std::isfinite(scale)) return HC_ERR_ARG;
@@ -202,6 +219,45 @@ hc_status hc_weights_save(const void* H, const void* W, const float* w_static, f
                                             static_cast<hipStream_t>(stream)));
 }
 
+hc_status hc_post_mix_weights(const void* H, const void* F, const float* w, int64_t w_stride,
+                              const void* W, const float* w_static, float scale, float eps,
+                              int32_t sinkhorn_iters, void* H_out, float* w_out, float* saved,
+                              int64_t saved_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt_arg,
+                              void* stream) {
+    const int dt = enum_value(dt_arg);
+    if (dt != HC_BF16 && dt != HC_FP8) return HC_ERR_DTYPE;
+    hc_status st = check_nd(n, d, T, dt);
+    if (st != HC_OK) return st;
+    if (d > hc::post_weights_max_hidden(dt)) return HC_ERR_SHAPE;
+    const int K = record_len(n);
+    if ((st = check_stride(w_stride, K, T)) != HC_OK) return st;
+    if (!eps_ok(eps) || !std::isfinite(scale)) return HC_ERR_ARG;
+    if (sinkhorn_iters < 0 || sinkhorn_iters > HC_MAX_SINKHORN_ITERS) return HC_ERR_ARG;
+    if (T == 0) return HC_OK;
+    if (!H || !F || !w || !W || !w_static || !H_out || !w_out) return HC_ERR_NULL;
+    const int64_t need = saved ? hc_weights_saved_bytes(T, n) : 0;
+    if (saved && saved_bytes < need) return HC_ERR_ARG;
+    if (misaligned(H, 16) || misaligned(F, 16) || misaligned(H_out, 16) || misaligned(W, 16) ||
+        misaligned(w, 4) || misaligned(w_static, 4) || misaligned(w_out, 4) || misaligned(saved, 16))
+        return HC_ERR_ALIGN;
+    const int64_t s = elem_bytes(dt);
+    const Span sH{H, T * n * d * s}, sF{F, T * d * s}, sw{w, record_span(T, w_stride, K)},
+        sW{W, int64_t(K) * d * s}, sS{w_static, int64_t(K) * 4}, sO{H_out, T * n * d * s},
+        sR{w_out, T * K * 4}, sv{saved, need};
+    if ((H_out != H && overlap(sO, sH)) || overlap(sO, sF) || overlap(sO, sw) || overlap(sO, sW) ||
+        overlap(sO, sS))
+        return HC_ERR_ALIAS;
+    for (const Span& o : {sR, sv})
+        if (overlap(o, sH) || overlap(o, sF) || overlap(o, sw) || overlap(o, sW) || overlap(o, sS) ||
+            overlap(o, sO))
+            return HC_ERR_ALIAS;
+    if (overlap(sR, sv)) return HC_ERR_ALIAS;
+    return from_hip(hc::launch_post_mix_weights(
+        H, F, w, w_stride, W, w_static, scale, eps, sinkhorn_iters, H_out, w_out, saved,
+        saved ? saved + hc::saved_r_offset(T, n) : nullptr, T, n, d, dt,
+        static_cast<hipStream_t>(stream)));
+}
+
 hc_status hc_sinkhorn(const float* logits, float* w_out, int32_t iters, int64_t T, int32_t n,
                       void* stream) {
     if (n < 1 || n > HC_MAX_STREAMS) return HC_ERR_SHAPE;
@@ -223,7 +279,8 @@ int64_t hc_backward_workspace(int64_t T, int32_t n, int32_t d) {
 hc_status hc_post_mix_backward(const void* dH_out, const void* H, const void* F, const float* w,
                                int64_t w_stride, void* dH, void* dF, float* dw, void* workspace,
                                int64_t workspace_bytes, int64_t T, int32_t n, int32_t d,
-                               hc_dtype dt, void* stream) {
+                               hc_dtype dt_arg, void* stream) {
+    const int dt = enum_value(dt_arg);
     if (!dtype_wide(dt)) return HC_ERR_DTYPE;
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
@@ -257,8 +314,9 @@ hc_status hc_post_mix_backward(const void* dH_out, const void* H, const void* F,
 hc_status hc_pre_mix_backward(const void* du, const void* H, const float* w, int64_t w_stride,
                               const float* gamma, float eps, const void* dH_in, const void* dH_out,
                               void* dH, float* dw, float* dgamma, void* workspace,
-                              int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
+                              int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt_arg,
                               void* stream) {
+    const int dt = enum_value(dt_arg);
     if (!dtype_wide(dt)) return HC_ERR_DTYPE;
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
@@ -305,8 +363,9 @@ hc_status hc_weights_backward(const void* H, const void* W, const float* w_stati
                               float eps, int32_t sinkhorn_iters, const float* dw, const float* dw2,
                               const float* saved, const void* dH_in,
                               void* dH, float* dW, float* dw_static, void* workspace,
-                              int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
+                              int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt_arg,
                               void* stream) {
+    const int dt = enum_value(dt_arg);
     if (!dtype_wide(dt)) return HC_ERR_DTYPE;
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
@@ -371,13 +430,21 @@ hc_status hc_sinkhorn_backward(const float* logits, const float* dw, float* dlog
 hc_status hc_sum_records(const float* rec, int64_t T, int32_t K, float* out, void* stream) {
     if (K < 1 || K > 1024) return HC_ERR_SHAPE;
     if (T < 0 || T > kMaxBytes / 4 / K) return HC_ERR_ARG;
+    if (T == 0) {
+        // the sum over no tokens: zeros into `out` when it is given; `rec`
+        // is not read (an empty tensor has no storage) and may be NULL
+        if (!out) return HC_OK;
+        if (misaligned(out, 4)) return HC_ERR_ALIGN;
+        return from_hip(hc::launch_sum_records(rec, 0, K, out, static_cast<hipStream_t>(stream)));
+    }
     if (!rec || !out) return HC_ERR_NULL;
     if (misaligned(rec, 4) || misaligned(out, 4)) return HC_ERR_ALIGN;
     if (overlap(Span{rec, T * K * 4}, Span{out, int64_t(K) * 4})) return HC_ERR_ALIAS;
     return from_hip(hc::launch_sum_records(rec, T, K, out, static_cast<hipStream_t>(stream)));
 }
 
-hc_status hc_block_tanh(const void* u, void* F, int64_t count, hc_dtype dt, void* stream) {
+hc_status hc_block_tanh(const void* u, void* F, int64_t count, hc_dtype dt_arg, void* stream) {
+    const int dt = enum_value(dt_arg);
     if (!dtype_ok(dt)) return HC_ERR_DTYPE;
     if (count < 0 || count > kMaxBytes / 4) return HC_ERR_ARG;
     if (count % vec_elems(dt) != 0) return HC_ERR_SHAPE;

@@ -5,7 +5,8 @@
 //
 // Sources: hfviewer.com glossary "Hyper-connections (mHC)", definition (the
 // mixing before and after the block is learned, so its weights need
-// gradients; "richer gradient routing than one shared residual");
+// gradients, and the page credits the parallel streams with more paths for
+// gradients than a single residual offers);
 // learnaivisually.com "Tencent open-sources Hy4 Preview at 770B -- Identity
 // Hyper-Connections", section "Jargon", Residual connection (gradients take
 // the short path back through the residual).
@@ -777,13 +778,16 @@ int64_t backward_workspace_bytes(int64_t T, int n, int d) {
     return bwd_space(T, n, d).total * 4;
 }
 
-hipError_t launch_post_mix_backward(const void* dHo, const void* H, const void* F, const float* w,
-                                    int64_t w_stride, void* dH, void* dF, float* dw, void* work,
-                                    int64_t T, int n, int d, int dt, hipStream_t s) {
-    const BwdSpace sp = bwd_space(T, n, d);
-    float* ws = static_cast<float*>(work);
+namespace {
+
+// Post's gradient with its scratch given as two regions: the per-block
+// partial records (`part`, prows x M floats) and the levels of their sum
+// (`tmp`); both unused with per-token records.
+hipError_t post_backward_with(const void* dHo, const void* H, const void* F, const float* w,
+                              int64_t w_stride, void* dH, void* dF, float* dw, float* part,
+                              float* tmp, int64_t T, int n, int d, int dt, hipStream_t s) {
     const int group = w_stride != 0 ? 1 : (int)post_group_of(T);
-    float* part = w_stride != 0 ? nullptr : ws + sp.rec;
+    if (w_stride != 0) part = nullptr;
     hipError_t e =
         dt == 0 ? post_bwd_n<f32_t>(n, row_config(d / Store<f32_t>::kElems), dHo, H, F, w, w_stride,
                                     dH, dF, dw, part, T, d, group, s)
@@ -792,8 +796,20 @@ hipError_t launch_post_mix_backward(const void* dHo, const void* H, const void* 
     if (e != hipSuccess || w_stride != 0) return e;
     // shared record: dw = [0 (dalpha) | sum of the block partials]
     const int M = n + n * n;
-    const SumJob job = {part, sp.prows, M, ws + sp.tmp2, dw + n, dw, n};
+    const int64_t prows = (T + post_group_of(T) - 1) / post_group_of(T);
+    const SumJob job = {part, prows, M, tmp, dw + n, dw, n};
     return launch_sum_rows2(&job, 1, s);
+}
+
+}  // namespace
+
+hipError_t launch_post_mix_backward(const void* dHo, const void* H, const void* F, const float* w,
+                                    int64_t w_stride, void* dH, void* dF, float* dw, void* work,
+                                    int64_t T, int n, int d, int dt, hipStream_t s) {
+    const BwdSpace sp = bwd_space(T, n, d);
+    float* ws = static_cast<float*>(work);
+    return post_backward_with(dHo, H, F, w, w_stride, dH, dF, dw, ws ? ws + sp.rec : nullptr,
+                              ws ? ws + sp.tmp2 : nullptr, T, n, d, dt, s);
 }
 
 hipError_t launch_pre_mix_backward(const void* du, const void* H, const float* w, int64_t w_stride,

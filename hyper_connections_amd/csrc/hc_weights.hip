@@ -52,64 +52,6 @@ constexpr int kWaves = 4;    // waves per weights workgroup
 constexpr int kLV = 8;         // 16-byte vectors per lane per k-chunk
 constexpr int64_t kMaxGrid = 1 << 20;
 
-// ------------------------------------------------------------ mHC record
-
-// DPP quad permutes: swap neighbours (1,0,3,2) and pairs (2,3,0,1).
-__device__ __forceinline__ float quad_swap1(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float quad_swap2(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-}
-// Sum / max over the 4 lanes of a quad; every lane gets the same value (each
-// step adds the same two operands on both partners).
-__device__ __forceinline__ float quad_sum(float v) {
-    v += quad_swap1(v);
-    return v + quad_swap2(v);
-}
-__device__ __forceinline__ float quad_max(float v) {
-    v = fmaxf(v, quad_swap1(v));
-    return fmaxf(v, quad_swap2(v));
-}
-
-// The mHC transform of one token, spread over the 4 lanes of a quad: lane r
-// owns alpha_r, beta_r and row r of the n x n mix (lanes r >= N hold zeros
-// and take part only in the column sums).  On entry a, b and row[] are the
-// logits, on exit the weights:
-//   alpha = sigmoid(l_alpha), beta = sigmoid(l_beta),
-//   A = exp(l_A) normalised `iters` times, rows then columns.
-// With iters >= 1 the largest logit of A is subtracted before exp; the first
-// row division removes any common factor, so exact results are unchanged.
-// Must be called by all 4 lanes of the quad (no divergence around DPP).
-template <int N>
-__device__ __forceinline__ void mhc_quad(int r, float& a, float& b, float (&row)[N], int iters) {
-    const bool live = r < N;
-    a = 1.0f / (1.0f + expf(-a));
-    b = 1.0f / (1.0f + expf(-b));
-    float m = 0.0f;
-    if (iters > 0) {
-        m = live ? row[0] : -INFINITY;
-#pragma unroll
-        for (int j = 1; j < N; ++j) m = live ? fmaxf(m, row[j]) : m;
-        m = quad_max(m);
-    }
-#pragma unroll
-    for (int j = 0; j < N; ++j) row[j] = live ? expf(row[j] - m) : 0.0f;
-    for (int it = 0; it < iters; ++it) {
-        float s = row[0];
-#pragma unroll
-        for (int j = 1; j < N; ++j) s += row[j];
-        const float sd = live ? s : 1.0f;
-#pragma unroll
-        for (int j = 0; j < N; ++j) row[j] = row[j] / sd;
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-            const float c = quad_sum(row[j]);
-            row[j] = row[j] / c;
-        }
-    }
-}
-
 // --------------------------------------------------------------- sinkhorn
 
 // Four lanes per token (lane r owns row r); 64 tokens per 256-thread block.

@@ -21,12 +21,16 @@ block_tanh only):
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libhc.so")
+# HC_LIB names another build of the same library (the sanitizer test loads
+# one whose host code is built with AddressSanitizer); there is no fallback
+LIB_PATH = os.environ.get("HC_LIB") or os.path.join(_PKG, "libhc.so")
 
 HC_F32, HC_BF16, HC_FP8 = 0, 1, 2
 MAX_STREAMS = 4
@@ -54,6 +58,8 @@ _SIGS = {
     "hc_weights_backward": [_vp, _vp, _fp, _f32, _f32, _i32, _fp, _fp, _fp, _vp, _vp, _fp, _fp,
                             _vp, _i64, _i64, _i32, _i32, _i32, _vp],
     "hc_sinkhorn_backward": [_fp, _fp, _fp, _i32, _vp, _i64, _i64, _i32, _vp],
+    "hc_post_mix_weights": [_vp, _vp, _fp, _i64, _vp, _fp, _f32, _f32, _i32, _vp, _fp, _fp, _i64,
+                            _i64, _i32, _i32, _i32, _vp],
 }
 EXPORTS = tuple(_SIGS) + ("hc_status_str", "hc_abi_version", "hc_backward_workspace",
                           "hc_weights_backward_workspace", "hc_sinkhorn_backward_workspace",
@@ -114,6 +120,29 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _on_launch_stream(fn):
+    """Give `fn` its launch stream as the current stream.  Everything the
+    wrapper allocates (outputs, workspaces) then belongs to the stream its
+    kernels run on, so torch's caching allocator cannot hand that memory to
+    other work before those kernels are done.  `stream` may be a
+    torch.cuda.Stream or a raw hipStream_t handle; None means the current
+    stream."""
+    pos = list(inspect.signature(fn).parameters).index("stream")
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        if len(args) > pos:
+            stream, args = args[pos], args[:pos] + (None,) + args[pos + 1:]
+        else:
+            stream = kwargs.pop("stream", None)
+        if stream is None:
+            return fn(*args, **kwargs)
+        s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+        with torch.cuda.stream(s):
+            return fn(*args, **kwargs)
+    return wrapper
+
+
 def _dt(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return HC_BF16
@@ -154,6 +183,7 @@ def _H(H: torch.Tensor):
     return T, n, d, 2 * n + n * n
 
 
+@_on_launch_stream
 def pre_mix(H, w, gamma, eps: float = 1e-6, out=None, stream=None) -> torch.Tensor:
     """Block input u = RMSNorm_gamma(sum_i alpha_i H_i), shape (T, d)."""
     T, n, d, K = _H(H)
@@ -169,6 +199,7 @@ def pre_mix(H, w, gamma, eps: float = 1e-6, out=None, stream=None) -> torch.Tens
     return u
 
 
+@_on_launch_stream
 def post_mix(H, F, w, out=None, stream=None) -> torch.Tensor:
     """H'_i = sum_j A[i][j] H_j + beta_i F, shape (T, n, d).  ``out=H`` runs in place."""
     T, n, d, K = _H(H)
@@ -184,6 +215,7 @@ def post_mix(H, F, w, out=None, stream=None) -> torch.Tensor:
     return o
 
 
+@_on_launch_stream
 def post_pre_mix(H, F, w, w_next, gamma_next, eps: float = 1e-6, out=None, u_out=None,
                  stream=None):
     """Fused write-back of one layer and read-mix + RMSNorm of the next.
@@ -221,6 +253,7 @@ def _weights_args(H, W, w_static, out):
     return T, n, d, K, o
 
 
+@_on_launch_stream
 def weights(H, W, w_static, scale: float, eps: float = 1e-6, sinkhorn_iters: int = 0,
             out=None, stream=None) -> torch.Tensor:
     """Per-token weight records (T, K) float32 from the streams (see include/hc.h)."""
@@ -230,6 +263,7 @@ def weights(H, W, w_static, scale: float, eps: float = 1e-6, sinkhorn_iters: int
     return o
 
 
+@_on_launch_stream
 def weights_save(H, W, w_static, scale: float, eps: float = 1e-6, sinkhorn_iters: int = 0,
                  out=None, saved=None, stream=None):
     """weights() for a training forward: returns (records, saved), where saved
@@ -248,6 +282,42 @@ def weights_save(H, W, w_static, scale: float, eps: float = 1e-6, sinkhorn_iters
     return o, saved
 
 
+@_on_launch_stream
+def post_mix_weights(H, F, w, W, w_static, scale: float, eps: float = 1e-6,
+                     sinkhorn_iters: int = 0, out=None, w_out=None, saved=None, stream=None):
+    """The write-back of one layer fused with the next layer's per-token
+    weights: returns (H', w_next), H' = post_mix(H, F, w) (bitwise) and
+    w_next = weights(H', W, w_static, scale, eps, sinkhorn_iters) formed from
+    H' while it is on chip.  ``out=H`` runs in place.  ``saved`` (True, or a
+    float32 buffer of hc_weights_saved_bytes) also keeps the projections and
+    norms for weights_backward, and the result is (H', w_next, saved).
+    bf16 and FP8 storage, d <= 4096."""
+    T, n, d, K = _H(H)
+    ws = _record(w, T, K)
+    _dev(F, "F")
+    if F.dtype != H.dtype or tuple(F.shape) != (T, d):
+        raise ValueError("F must match H's dtype and have shape (T, d)")
+    o = torch.empty_like(H) if out is None else _dev(out, "out")
+    if o.dtype != H.dtype or o.shape != H.shape:
+        raise ValueError("out must match H")
+    W_, ro = W, w_out
+    T2, n2, d2, K2, ro = _weights_args(H, W_, w_static, ro)
+    keep = saved is not None and saved is not False
+    if saved is True:
+        saved = torch.empty(max(int(lib().hc_weights_saved_bytes(T, n)), 16) // 4,
+                            dtype=torch.float32, device=H.device)
+    if keep:
+        _dev(saved, "saved")
+        if saved.dtype != torch.float32:
+            raise ValueError("saved must be float32")
+    _call("hc_post_mix_weights", H.data_ptr(), F.data_ptr(), w.data_ptr(), ws, W.data_ptr(),
+          w_static.data_ptr(), float(scale), float(eps), int(sinkhorn_iters), o.data_ptr(),
+          ro.data_ptr(), saved.data_ptr() if keep else None, saved.numel() * 4 if keep else 0,
+          T, n, d, _dt(H), _stream(stream))
+    return (o, ro, saved) if keep else (o, ro)
+
+
+@_on_launch_stream
 def sinkhorn(logits, n: int, iters: int, out=None, stream=None) -> torch.Tensor:
     """mHC transform of per-token logit records (T, K) -> weight records (T, K)."""
     _dev(logits, "logits")
@@ -262,6 +332,7 @@ def sinkhorn(logits, n: int, iters: int, out=None, stream=None) -> torch.Tensor:
     return o
 
 
+@_on_launch_stream
 def block_tanh(u, out=None, stream=None) -> torch.Tensor:
     """Stand-in block F = tanh(u) (not part of the method)."""
     _dev(u, "u")
@@ -299,6 +370,7 @@ def _grad_record(dw, T, K, ws_stride, device, what="dw"):
     return dw
 
 
+@_on_launch_stream
 def post_mix_backward(dH_out, H, F, w, dH=None, dF=None, dw=None, workspace=None, stream=None,
                       h_grad=True):
     """Gradients of post_mix: returns (dH, dF, dw).  dw has the shape of the
@@ -333,6 +405,7 @@ def post_mix_backward(dH_out, H, F, w, dH=None, dF=None, dw=None, workspace=None
     return dH, dF, dw
 
 
+@_on_launch_stream
 def pre_mix_backward(du, H, w, gamma, eps: float = 1e-6, dH_in=None, out=None, dw=None,
                      dgamma=None, workspace=None, stream=None, dH_out=None):
     """Gradients of pre_mix: returns (dH, dw, dgamma).  dH includes dH_in when
@@ -371,6 +444,7 @@ def pre_mix_backward(du, H, w, gamma, eps: float = 1e-6, dH_in=None, out=None, d
     return dH, dw, dg
 
 
+@_on_launch_stream
 def sum_records(rec, out=None, stream=None):
     """Sum of per-token records over tokens: (T, K) float32 -> (K,)."""
     _dev(rec, "rec")
@@ -378,10 +452,13 @@ def sum_records(rec, out=None, stream=None):
         raise ValueError("rec must be float32 of shape (T, K)")
     T, K = rec.shape
     o = torch.empty(K, dtype=torch.float32, device=rec.device) if out is None else _dev(out, "out")
+    if o.dtype != torch.float32 or tuple(o.shape) != (K,):
+        raise ValueError(f"out must be float32 of shape ({K},)")
     _call("hc_sum_records", rec.data_ptr(), T, K, o.data_ptr(), _stream(stream))
     return o
 
 
+@_on_launch_stream
 def weights_backward(H, W, w_static, scale: float, dw, eps: float = 1e-6, sinkhorn_iters: int = 0,
                      dH_in=None, out=None, dW=None, dw_static=None, workspace=None, dw2=None,
                      saved=None, stream=None):
@@ -436,6 +513,7 @@ def weights_backward(H, W, w_static, scale: float, dw, eps: float = 1e-6, sinkho
     return dH, dW, dws
 
 
+@_on_launch_stream
 def sinkhorn_backward(logits, dw, n: int, iters: int, out=None, workspace=None, stream=None):
     """Gradient of sinkhorn: dL/dlogits (T, K) float32 from dL/dw (T, K)."""
     _dev(logits, "logits")

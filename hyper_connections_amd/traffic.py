@@ -35,9 +35,39 @@ def post_bytes(n: int, d: int, s: int, per_token_record: bool = False) -> int:
 
 
 def weights_bytes(n: int, d: int, s: int) -> int:
-    """Read H (n*d) and write one record; the K x d projection matrix is
-    shared by all tokens and not counted per token."""
+    """The separate weights kernel's own bytes: read H (n*d) and write one
+    record; the K x d projection matrix is shared by all tokens and not
+    counted per token.  This read of H is a second pass over the state that
+    the method does not need (see method_bytes), so it counts for the
+    kernel's own roofline, never towards a layer's."""
     return n * d * s + record_bytes(n)
+
+
+def method_bytes(kind: str, n: int, d: int, s: int) -> int:
+    """The bytes one layer of the method itself must move per token, the
+    figure a layer's time is graded on however its kernels are split:
+    pre reads H and writes u, post reads H and F and writes H'
+    ((3n + 2) d s), plus the weight records that leave the chip:
+      static   one shared record, not counted per token;
+      dynamic  the per-token record is formed while H is on chip; its mix
+               and write weights (n + n^2 fp32) are written once and read
+               once by the write-back;
+      mhc      the per-token logit record (K fp32) is read once.
+    A kernel split that moves more (a separate weights pass re-reading H,
+    a weight record written and read back) is charged against this."""
+    base = (3 * n + 2) * d * s
+    if kind == "dynamic":
+        return base + 2 * (n + n * n) * RECORD_BYTES_PER_ENTRY
+    if kind == "mhc":
+        return base + record_bytes(n)
+    return base
+
+
+def post_weights_bytes(n: int, d: int, s: int) -> int:
+    """Write-back fused with the next layer's weights: post's bytes with a
+    per-token record read, plus the next record written (H' is projected
+    from registers, not read back)."""
+    return post_bytes(n, d, s, True) + record_bytes(n)
 
 
 def sinkhorn_bytes(n: int) -> int:

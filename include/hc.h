@@ -146,6 +146,34 @@ hc_status hc_weights_save(const void* H, const void* W, const float* w_static, f
                           int64_t saved_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
                           void* stream);
 
+/* The write-back of one layer fused with the per-token weights of the next
+ * ([GLOSS] definition: mixing weights around every block; [EXPL] "What four
+ * streams cost per token": the cost is the n-fold state moved across each
+ * boundary, and a separate weights pass would read that state once more).
+ * Equivalent to
+ *   hc_post_mix(H, F, w, w_stride, H_out)                    then
+ *   hc_weights(H_out, W, w_static, scale, eps, sinkhorn_iters, w_out)
+ * (or hc_weights_save with `saved`), with H_out taken from registers instead
+ * of being read back: H_out is bitwise hc_post_mix's; w_out agrees with
+ * hc_weights on H_out to fp32 rounding (the projection's sums are taken in
+ * another order).  In a layer loop the records w_out feed the next layer's
+ * hc_pre_mix and hc_post_mix; only the first layer needs hc_weights.
+ *   H, F, w, w_stride, H_out   as hc_post_mix (H_out == H allowed)
+ *   W, w_static, scale, eps,
+ *   sinkhorn_iters, w_out      as hc_weights (W of the layer the records are
+ *                              for); w_out may not overlap anything
+ *   saved, saved_bytes         NULL/0, or the state hc_weights_save keeps
+ *                              (saved_bytes >= hc_weights_saved_bytes(T, n),
+ *                              16-byte aligned, no overlap): short is HC_ERR_ARG
+ * bf16 and FP8 storage only (HC_ERR_DTYPE otherwise).  W is held in
+ * registers for the whole call, which bounds the width: d <= 4096, else
+ * HC_ERR_SHAPE (use hc_post_mix and hc_weights beyond it). */
+hc_status hc_post_mix_weights(const void* H, const void* F, const float* w, int64_t w_stride,
+                              const void* W, const float* w_static, float scale, float eps,
+                              int32_t sinkhorn_iters, void* H_out, float* w_out, float* saved,
+                              int64_t saved_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
+                              void* stream);
+
 /* mHC step: make the stream mix doubly stochastic with Sinkhorn iterations
  * ([GLOSS] definition; [ATLAS] "Architecture concepts", mHC).  Per token:
  * alpha = sigmoid(l_alpha), beta = sigmoid(l_beta), A = exp(l_A) then `iters`
@@ -267,7 +295,9 @@ hc_status hc_sinkhorn_backward(const float* logits, const float* dw, float* dlog
 
 /* out[c] = sum over t of rec[t * K + c], c < K, summed in a fixed order:
  * turns per-token gradient records into the gradient of one shared record.
- *   rec [T][K] fp32, out [K] fp32 (no overlap), 1 <= K <= 1024. */
+ *   rec [T][K] fp32, out [K] fp32 (no overlap), 1 <= K <= 1024.
+ * At T == 0 the sum is empty: zeros are written to `out` if it is not NULL,
+ * and `rec` is not read (it may be NULL). */
 hc_status hc_sum_records(const float* rec, int64_t T, int32_t K, float* out, void* stream);
 
 /* Stand-in block used by the benchmarks and tests, not part of the method:

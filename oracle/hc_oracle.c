@@ -72,7 +72,10 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2 };
+/* Storage types of the inputs.  ORC_F64 holds values that were never
+ * rounded to a storage format: it lets a caller run the pure fp64 chain (no
+ * store rounding anywhere) that the per-layer drift is reported against. */
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2, ORC_F64 = 3 };
 
 /* FP8 E4M3 ("fn", the OCP 8-bit float): sign, 4 exponent bits with bias 7, 3
  * mantissa bits; no infinities; S.1111.111 is NaN; the largest finite value
@@ -94,6 +97,7 @@ static double orc_fp8_value(uint8_t b)
 static double orc_load(const void* p, int64_t idx, int dt)
 {
     if (dt == ORC_F32) return (double)((const float*)p)[idx];
+    if (dt == ORC_F64) return ((const double*)p)[idx];
     if (dt == ORC_FP8) return orc_fp8_value(((const uint8_t*)p)[idx]);
     uint32_t bits = (uint32_t)((const uint16_t*)p)[idx] << 16;
     float f;

@@ -6,8 +6,10 @@ imports the GPU library.
 
 Arrays are numpy arrays on the host.  Storage tensors (H, F, W, u) are passed
 in their storage type: ``np.float32`` for fp32, ``np.uint16`` holding bf16 bit
-patterns or ``np.uint8`` holding FP8 E4M3 codes.  Weight records, gains and logits are ``np.float64`` (callers
-widen fp32 values exactly).  Every result is returned unrounded in float64;
+patterns or ``np.uint8`` holding FP8 E4M3 codes; ``np.float64`` passes values
+that were never rounded to a storage format (the pure fp64 chain).  Weight
+records, gains and logits are ``np.float64`` (callers widen fp32 values
+exactly).  Every result is returned unrounded in float64;
 ``round_bf16`` / ``round_f32`` model a store to the storage type.
 
 Which passage each function follows is stated in ``hc_oracle.c``.
@@ -24,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hc_oracle.c")
 _SO = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, F64 = 0, 1, 2, 3
 
 _lib = None
 
@@ -86,8 +88,10 @@ def _dt(a: np.ndarray) -> int:
         return BF16
     if a.dtype == np.uint8:
         return FP8
-    raise TypeError(f"storage arrays must be float32, uint16 (bf16 bits) or uint8 (fp8 e4m3 "
-                    f"codes), got {a.dtype}")
+    if a.dtype == np.float64:
+        return F64     # unrounded values (the pure fp64 chain)
+    raise TypeError(f"storage arrays must be float32, uint16 (bf16 bits), uint8 (fp8 e4m3 "
+                    f"codes) or float64 (unrounded), got {a.dtype}")
 
 
 def _c(a: np.ndarray, dtype=None) -> np.ndarray:

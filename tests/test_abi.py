@@ -51,7 +51,7 @@ def test_status_strings(L):
         s = hc.status_str(code)
         assert s.startswith("HC_")
     assert hc.status_str(99).startswith("HC_ERR_UNKNOWN")
-    assert hc.abi_version() == 3
+    assert hc.abi_version() == 4
 
 
 def pre(L, H=P[0], w=P[1], ws=0, g=P[2], eps=1e-6, u=P[3], T=16, n=4, d=4096, dt=BF16):
@@ -158,6 +158,61 @@ def test_backward_validation(L):
     assert L.hc_sum_records(P[0], 10, 0, P[1], None) == SHAPE
     assert L.hc_sum_records(P[0], -1, 24, P[1], None) == ARG
     assert L.hc_sum_records(P[0], 10, 24, P[0] + 8, None) == ALIAS
+    # the empty sum: no pointer is needed and nothing is launched
+    assert L.hc_sum_records(None, 0, 24, None, None) == OK
+    assert L.hc_sum_records(P[0], 0, 24, None, None) == OK
+    assert L.hc_sum_records(None, 0, 0, None, None) == SHAPE
+    assert L.hc_sum_records(None, 10, 24, P[1], None) == NULL
+
+
+@pytest.mark.gpu
+def test_sum_records_binding_checks_out(L):
+    """The binding passes only a pointer for `out`: one of the wrong dtype or
+    size would let the kernel write past its end, so it is rejected first."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    rec = torch.zeros((4, 24), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        hc.sum_records(rec, out=torch.zeros(23, dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        hc.sum_records(rec, out=torch.zeros(24, dtype=torch.float64, device="cuda"))
+    # the empty sum writes zeros
+    o = torch.full((24,), 7.0, dtype=torch.float32, device="cuda")
+    hc.sum_records(torch.zeros((0, 24), dtype=torch.float32, device="cuda"), out=o)
+    assert torch.count_nonzero(o).item() == 0
+
+
+def test_post_mix_weights_validation(L):
+    """The fused write-back + next-layer weights call: its own limits (bf16 or
+    FP8, d <= 4096), the post_mix and weights checks, the optional saved
+    state, and every aliasing rule.  Every call here fails validation or has
+    T = 0, so nothing is launched (the pointers are fake)."""
+    K = 24
+    need = int(L.hc_weights_saved_bytes(16, 4))
+
+    def f(**k):
+        return L.hc_post_mix_weights(
+            k.get("H", P[0]), k.get("F", P[1]), k.get("w", P[2]), k.get("ws", 0), k.get("W", P[3]),
+            k.get("wst", P[4]), k.get("scale", 0.01), k.get("eps", 1e-6), k.get("it", 0),
+            k.get("O", P[5]), k.get("wo", P[6]), k.get("sv", None), k.get("svb", 0), k.get("T", 16),
+            k.get("n", 4), k.get("d", 4096), k.get("dt", BF16), None)
+    assert f(T=0) == OK and f(T=0, H=None) == OK and f(T=0, dt=FP8) == OK and f(T=0, ws=K) == OK
+    assert f(dt=F32) == DTYPE and f(dt=9) == DTYPE and f(dt=F32, T=0) == DTYPE
+    assert f(d=4104) == SHAPE and f(d=8192, dt=FP8) == SHAPE and f(d=12) == SHAPE and f(n=5) == SHAPE
+    assert f(ws=K - 1) == SHAPE
+    assert f(T=-1) == ARG and f(eps=0.0) == ARG and f(it=-1) == ARG and f(scale=float("inf")) == ARG
+    for name in ("H", "F", "w", "W", "wst", "O", "wo"):
+        assert f(**{name: None}) == NULL, name
+    assert f(H=P[0] + 8) == ALIGN and f(W=P[3] + 4) == ALIGN and f(wo=P[6] + 2) == ALIGN
+    # in place is allowed (checked on the GPU); any other overlap of an output is not
+    assert f(O=P[0] + 16) == ALIAS and f(O=P[1]) == ALIAS and f(O=P[3]) == ALIAS
+    assert f(wo=P[0] + 64) == ALIAS and f(wo=P[5] + 64) == ALIAS and f(wo=P[3]) == ALIAS
+    assert f(wo=P[2]) == ALIAS and f(wo=P[4]) == ALIAS
+    # the kept state: big enough, aligned, overlapping nothing
+    assert f(sv=P[7], svb=need - 4) == ARG
+    assert f(sv=P[7] + 4, svb=need) == ALIGN and f(sv=P[6], svb=need) == ALIAS
+    assert f(sv=P[5] + 16, svb=need) == ALIAS and f(sv=P[0], svb=need) == ALIAS
 
 
 def test_sinkhorn_validation(L):

@@ -230,3 +230,22 @@ def test_mhc_workload_full_size_every_token():
         w64 = w[sl].astype(np.float64)
         check(u[sl], oracle.pre_mix(inp["H"][sl], w64, inp["gamma"], wl.eps), f"pre {t0}+")
         check(Hp[sl], oracle.post_mix(inp["H"][sl], inp["F"][sl], w64), f"post {t0}+")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8", "f32"])
+def test_weights_mhc_configured_iterations_many_tokens(dt):
+    """mHC mode inside the weights kernel at the configured 20 iterations
+    ("a few Sinkhorn iterations": hfviewer glossary "Hyper-connections
+    (mHC)", definition) over 2048 tokens, logits of about unit scale (W ~
+    N(0, 0.03^2) on rows of unit RMS): every record against the oracle, and
+    every token's columns sum to 1 within 1e-6."""
+    n, d, T, K = 4, 4096, 2048, 24
+    rng = np.random.default_rng(2020)
+    H = storage(rng.standard_normal((T, n, d)).astype(np.float32), dt)
+    W = storage((0.03 * rng.standard_normal((K, d))).astype(np.float32), dt)
+    ws = (identity_record(n) + 0.1 * rng.standard_normal(K)).astype(np.float32)
+    got = host(hc.weights(dev(H), dev(W), dev(ws), 1.0, 1e-6, 20))
+    ref = oracle.weights(H, W, ws.astype(np.float64), 1.0, 1e-6, 20)
+    record_check(got, ref, f"mhc 20 iterations {dt}")
+    A = got[:, 2 * n:].reshape(T, n, n).astype(np.float64)
+    assert np.max(np.abs(A.sum(axis=1) - 1.0)) <= 1e-6

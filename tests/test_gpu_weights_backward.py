@@ -194,3 +194,19 @@ def test_weights_backward_saturated_tanh(dt, n):
         assert e <= 1e-4, f"saturated dH n={n} {dt}: {e:.3g} > 1e-4"
     grad_check(host(dW), rdW, f"saturated dW n={n} {dt}")
     grad_check(host(dws)[None], rdws[None], f"saturated dw_static n={n} {dt}")
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 4096), ("f32", 1024)])
+def test_weights_backward_mhc_configured_iterations_many_tokens(dt, d):
+    """The weight producer's gradient in mHC mode at the configured 20
+    iterations over 1024 tokens (several dW splits), logits of about unit
+    scale: dH, dW and dw_static against the oracle."""
+    n, T = 4, 1024
+    rng = np.random.default_rng(2021)
+    H, W, ws, dw = case(rng, dt, T, n, d, wsd=0.03 * (4096 / d) ** 0.5)
+    dH, dW, dws = hc.weights_backward(dev(H), dev(W), dev(ws), 1.0, dev(dw), 1e-6, 20)
+    rdH, rdW, rdws = oracle.weights_backward(H, W, ws.astype(np.float64), 1.0,
+                                             dw.astype(np.float64), 1e-6, 20)
+    check(host(dH), rdH, f"dH mhc 20 {dt}")
+    grad_check(host(dW), rdW, f"dW mhc 20 {dt}")
+    grad_check(host(dws)[None], rdws[None], f"dw_static mhc 20 {dt}")

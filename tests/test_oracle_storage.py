@@ -109,3 +109,27 @@ def test_fp8_storage_reads_like_its_values(orc, rng):
     assert np.array_equal(orc.pre_mix(H8, w, g), orc.pre_mix(H, w, g))
     assert np.array_equal(orc.post_mix(H8, F8, w), orc.post_mix(H, F, w))
     assert np.array_equal(orc.block_tanh(F8), orc.block_tanh(F))
+
+
+def test_f64_storage_reads_like_its_values(orc, rng):
+    """Unrounded float64 inputs (the pure fp64 chain) are read as they are:
+    values that fp32 holds exactly give bitwise what the fp32 array gives,
+    and values fp32 cannot hold reach the arithmetic unrounded."""
+    T, n, d, K = 5, 4, 24, 24
+    H = rng.standard_normal((T, n, d)).astype(np.float32)
+    F = rng.standard_normal((T, d)).astype(np.float32)
+    W = (0.1 * rng.standard_normal((K, d))).astype(np.float32)
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    g = rng.standard_normal(d).astype(np.float32)
+    H64, F64, W64 = H.astype(np.float64), F.astype(np.float64), W.astype(np.float64)
+    assert np.array_equal(orc.pre_mix(H64, w, g), orc.pre_mix(H, w, g))
+    assert np.array_equal(orc.post_mix(H64, F64, w), orc.post_mix(H, F, w))
+    assert np.array_equal(orc.weights(H64, W64, w[0], 0.5), orc.weights(H, W, w[0], 0.5))
+    assert np.array_equal(orc.widen(H64), H64)
+    # 1 + 2^-40 is not an fp32 value: with A = I, beta = 1 post adds it to F unrounded
+    one = np.zeros(K)
+    one[n:2 * n] = 1.0
+    one[2 * n:] = np.eye(n).ravel()
+    Hx = np.full((1, n, d), 1.0 + 2.0 ** -40)
+    out = orc.post_mix(Hx, np.zeros((1, d)), one)
+    assert np.all(out == 1.0 + 2.0 ** -40)
