@@ -47,7 +47,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 KERNEL_SOURCES = {
     "pre_mix": "hc_rows.hip", "post_mix": "hc_rows.hip", "post_pre_mix": "hc_rows.hip",
-    "post_mix_weights": "hc_post_weights.hip",
+    "post_mix_weights": "hc_post_weights.hip", "post_weights_pre_mix": "hc_post_weights.hip",
     "block_tanh": "hc_rows.hip", "weights": "hc_weights.hip", "sinkhorn": "hc_weights.hip",
     "post_mix_backward": "hc_backward.hip", "pre_mix_backward": "hc_backward.hip",
     "sum_records": "hc_backward.hip", "weights_backward": "hc_weights_bwd.hip",
@@ -342,7 +342,11 @@ def main():
                          "which forms the write-back's share from dH' itself)")
     ap.add_argument("--weights-pass", action="store_true",
                     help="dynamic workloads: a separate weights kernel reads H before pre and "
-                         "post (by default post forms the next layer's records)")
+                         "post (by default one kernel per layer boundary: the write-back, the "
+                         "next layer's records and its read-mix)")
+    ap.add_argument("--two-pass", action="store_true",
+                    help="dynamic workloads: this layer's read-mix, then the write-back fused "
+                         "with the next layer's records (two kernels per layer)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph (torch.cuda.CUDAGraph) and time replays")
     ap.add_argument("--all", metavar="OUT_JSONL",
@@ -465,6 +469,7 @@ def run_workload(args, name: str):
         "post_mix": traffic.post_bytes(n, d, s, per_tok) * T,
         "post_pre_mix": traffic.post_pre_bytes(n, d, s) * T,
         "post_mix_weights": traffic.post_weights_bytes(n, d, s) * T,
+        "post_weights_pre_mix": traffic.post_weights_pre_bytes(n, d, s) * T,
         "weights": traffic.weights_bytes(n, d, s) * T,
         "sinkhorn": traffic.sinkhorn_bytes(n) * T,
         "block_tanh": 2 * d * s * T,
@@ -540,17 +545,25 @@ def run_workload(args, name: str):
                ("post_mix", lambda b: hc.post_mix(b["H"], b["F"], b["w"], out=b["O"]))]
     elif wl.kind == "dynamic":
         # a layer at steady state: its records were formed by the previous
-        # layer's write-back; this write-back forms the next layer's (into the
-        # next buffer set, whose step comes next).  The first layer's records
-        # come from the weights kernel, untimed.
+        # layer boundary; this one forms the next layer's (into the next
+        # buffer set, whose step comes next).  The first layer's records come
+        # from the weights kernel, untimed.
         for i, b in enumerate(bufs):
             hc.weights(b["H"], Wp, ws, wl.scale, wl.eps, 0, out=b["w"])
             b["next"] = bufs[(i + 1) % sets]
         torch.cuda.synchronize()
-        ops = [("pre_mix", lambda b: hc.pre_mix(b["H"], b["w"], gamma, wl.eps, out=b["u"])),
-               ("post_mix_weights", lambda b: hc.post_mix_weights(
-                   b["H"], b["F"], b["w"], Wp, ws, wl.scale, wl.eps, 0, out=b["O"],
-                   w_out=b["next"]["w"]))]
+        if args.two_pass:
+            # this layer's read-mix, then the write-back with the next records
+            ops = [("pre_mix", lambda b: hc.pre_mix(b["H"], b["w"], gamma, wl.eps, out=b["u"])),
+                   ("post_mix_weights", lambda b: hc.post_mix_weights(
+                       b["H"], b["F"], b["w"], Wp, ws, wl.scale, wl.eps, 0, out=b["O"],
+                       w_out=b["next"]["w"]))]
+        else:
+            # one kernel per layer boundary: the write-back, the next layer's
+            # records and its read-mix (the block input u of the next layer)
+            ops = [("post_weights_pre_mix", lambda b: hc.post_weights_pre_mix(
+                b["H"], b["F"], b["w"], Wp, ws, wl.scale, gamma, wl.eps, wl.eps, 0, out=b["O"],
+                w_out=b["next"]["w"], u_out=b["u"]))]
     elif wl.kind == "mhc":
         ops = [("sinkhorn", lambda b: hc.sinkhorn(b["logits"], n, wl.iters, out=b["w"])),
                ("pre_mix", lambda b: hc.pre_mix(b["H"], b["w"], gamma, wl.eps, out=b["u"])),
@@ -648,14 +661,17 @@ def run_workload(args, name: str):
 
     hc_kernels = [k for k in kms if k != "block_tanh"]
     launches = {k: c // args.steps for k, c in bare.counts.items()}
-    if args.backward or args.fused or wl.kind == "chain":
-        # the kernels' own bytes: a gradient step, a fused layer boundary, or
-        # the 78-layer chain (its tanh block left out)
-        step_bytes = sum(launch_bytes[k] * launches[k] for k in hc_kernels)
+    # the kernels' own algorithmic bytes (a fused layer boundary moves less
+    # than the method's passes over the state)
+    kernel_bytes = sum(launch_bytes[k] * launches[k] for k in hc_kernels)
+    if args.backward or wl.kind == "chain":
+        # a gradient step, or the 78-layer chain (its tanh block left out)
+        step_bytes, basis = kernel_bytes, "kernels"
     else:
-        # one layer of the method, graded on the bytes the method itself must
-        # move however the step is split into kernels
-        step_bytes = traffic.method_bytes(wl.kind, n, d, s) * T
+        # one layer of the method (split into kernels, or one fused layer
+        # boundary at steady state), graded on the bytes the method itself
+        # moves when pre and post each pass over the state once
+        step_bytes, basis = traffic.method_bytes(wl.kind, n, d, s) * T, "method"
     kernels = {}
     for k, ms in kms.items():
         gbps = launch_bytes[k] / (ms * 1e-3) / 1e9
@@ -688,9 +704,13 @@ def run_workload(args, name: str):
         "config": {"workload": wl.name, "T": T, "n": n, "d": d, "weights": wl.kind,
                    "layers": wl.layers, "buffer_sets": sets, "fused": bool(args.fused),
                    "graph": bool(args.graph), "backward": bool(args.backward),
-                   "fold": fold, "weights_pass": bool(args.weights_pass)},
+                   "fold": fold, "weights_pass": bool(args.weights_pass),
+                   "two_pass": bool(args.two_pass)},
         "us_per_layer": round(ms_step * 1e3 / wl.layers, 3),
         "step_bytes": int(step_bytes),
+        "step_bytes_basis": basis,
+        "kernel_bytes": int(kernel_bytes),
+        "kernel_gbps": round(kernel_bytes / (ms_step * 1e-3) / 1e9, 1),
         "hbm_gbps": round(step_gbps, 1),
         "frac_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "copy_gbps": round(copy_gbps, 1),
@@ -870,8 +890,10 @@ def verify(wl, inp) -> dict:
             Wd, wsd = dev(inp["W"]), dev(inp["w_static"])
             rec = hc.weights(Hd, Wd, wsd, wl.scale, wl.eps, 0)      # the first layer's records
             u = hc.pre_mix(Hd, rec, gd, wl.eps)
-            O, rec2 = hc.post_mix_weights(Hd, Fd, rec, Wd, wsd, wl.scale, wl.eps, 0)
-            rh, r2h = host(rec), host(rec2)
+            # the timed layer boundary: write-back, next records, next read-mix
+            O, rec2, u2 = hc.post_weights_pre_mix(Hd, Fd, rec, Wd, wsd, wl.scale, gd, wl.eps,
+                                                  wl.eps, 0)
+            rh, r2h, u2h = host(rec), host(rec2), host(u2)
             errs["records"] = max(_rel_err(rh[c:c + chunk], oracle.weights(
                 H[c:c + chunk], inp["W"], inp["w_static"].astype(np.float64), wl.scale, wl.eps, 0))
                 for c in range(0, wl.T, chunk))
@@ -895,6 +917,9 @@ def verify(wl, inp) -> dict:
         if wl.kind == "dynamic":
             errs["next_records"] = max(_rel_err(r2h[c:c + chunk], oracle.weights(
                 Oh[c:c + chunk], inp["W"], inp["w_static"].astype(np.float64), wl.scale, wl.eps, 0))
+                for c in range(0, wl.T, chunk))
+            errs["next_u"] = max(_rel_err(oracle.widen(u2h[c:c + chunk]), oracle.pre_mix(
+                Oh[c:c + chunk], r2h[c:c + chunk].astype(np.float64), g, wl.eps))
                 for c in range(0, wl.T, chunk))
             # W = 0: tanh(0) = 0, every record is w_static bitwise
             Z = torch.zeros_like(Wd)
@@ -961,7 +986,7 @@ def run_all(args):
         for name in ALL_CONFIGS:
             a = copy.copy(args)
             a.workload = name
-            a.fused = a.backward = a.graph = a.weights_pass = False
+            a.fused = a.backward = a.graph = a.weights_pass = a.two_pass = False
             out, wl, inp = run_workload(a, name)
             torch.cuda.synchronize()
             torch.cuda.empty_cache()

@@ -95,7 +95,7 @@ const char* hc_status_str(hc_status status) {
     return "HC_ERR_UNKNOWN: unknown status code";
 }
 
-int32_t hc_abi_version(void) { return 4; }
+int32_t hc_abi_version(void) { return 5; }
 
 hc_status hc_pre_mix(const void* H, const float* w, int64_t w_stride, const float* gamma, float eps,
                      void* u, int64_t T, int32_t n, int32_t d, hc_dtype dt_arg, void* stream) {
@@ -219,12 +219,16 @@ hc_status hc_weights_save(const void* H, const void* W, const float* w_static, f
                                             static_cast<hipStream_t>(stream)));
 }
 
-hc_status hc_post_mix_weights(const void* H, const void* F, const float* w, int64_t w_stride,
-                              const void* W, const float* w_static, float scale, float eps,
-                              int32_t sinkhorn_iters, void* H_out, float* w_out, float* saved,
-                              int64_t saved_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt_arg,
-                              void* stream) {
-    const int dt = enum_value(dt_arg);
+namespace {
+
+// The write-back fused with the next layer's weights and, when u_next is
+// given, its read-mix (gamma_next, pre_eps); checks every argument first.
+hc_status post_weights(const void* H, const void* F, const float* w, int64_t w_stride,
+                       const void* W, const float* w_static, float scale, float eps,
+                       int32_t sinkhorn_iters, const float* gamma_next, float pre_eps, void* H_out,
+                       float* w_out, void* u_next, float* saved, int64_t saved_bytes, int64_t T,
+                       int32_t n, int32_t d, int dt, void* stream) {
+    const bool pre = u_next != nullptr || gamma_next != nullptr;
     if (dt != HC_BF16 && dt != HC_FP8) return HC_ERR_DTYPE;
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
@@ -232,30 +236,59 @@ hc_status hc_post_mix_weights(const void* H, const void* F, const float* w, int6
     const int K = record_len(n);
     if ((st = check_stride(w_stride, K, T)) != HC_OK) return st;
     if (!eps_ok(eps) || !std::isfinite(scale)) return HC_ERR_ARG;
+    if (pre && !eps_ok(pre_eps)) return HC_ERR_ARG;
     if (sinkhorn_iters < 0 || sinkhorn_iters > HC_MAX_SINKHORN_ITERS) return HC_ERR_ARG;
     if (T == 0) return HC_OK;
     if (!H || !F || !w || !W || !w_static || !H_out || !w_out) return HC_ERR_NULL;
+    if (pre && (!gamma_next || !u_next)) return HC_ERR_NULL;
     const int64_t need = saved ? hc_weights_saved_bytes(T, n) : 0;
     if (saved && saved_bytes < need) return HC_ERR_ARG;
     if (misaligned(H, 16) || misaligned(F, 16) || misaligned(H_out, 16) || misaligned(W, 16) ||
-        misaligned(w, 4) || misaligned(w_static, 4) || misaligned(w_out, 4) || misaligned(saved, 16))
+        misaligned(w, 4) || misaligned(w_static, 4) || misaligned(w_out, 4) ||
+        misaligned(saved, 16) || misaligned(u_next, 16) || misaligned(gamma_next, 16))
         return HC_ERR_ALIGN;
     const int64_t s = elem_bytes(dt);
     const Span sH{H, T * n * d * s}, sF{F, T * d * s}, sw{w, record_span(T, w_stride, K)},
         sW{W, int64_t(K) * d * s}, sS{w_static, int64_t(K) * 4}, sO{H_out, T * n * d * s},
-        sR{w_out, T * K * 4}, sv{saved, need};
+        sR{w_out, T * K * 4}, sv{saved, need}, sG{gamma_next, pre ? int64_t(d) * 4 : 0},
+        sU{u_next, pre ? T * d * s : 0};
     if ((H_out != H && overlap(sO, sH)) || overlap(sO, sF) || overlap(sO, sw) || overlap(sO, sW) ||
-        overlap(sO, sS))
+        overlap(sO, sS) || overlap(sO, sG))
         return HC_ERR_ALIAS;
-    for (const Span& o : {sR, sv})
+    for (const Span& o : {sR, sv, sU})
         if (overlap(o, sH) || overlap(o, sF) || overlap(o, sw) || overlap(o, sW) || overlap(o, sS) ||
-            overlap(o, sO))
+            overlap(o, sO) || overlap(o, sG))
             return HC_ERR_ALIAS;
-    if (overlap(sR, sv)) return HC_ERR_ALIAS;
+    if (overlap(sR, sv) || overlap(sR, sU) || overlap(sv, sU)) return HC_ERR_ALIAS;
     return from_hip(hc::launch_post_mix_weights(
-        H, F, w, w_stride, W, w_static, scale, eps, sinkhorn_iters, H_out, w_out, saved,
-        saved ? saved + hc::saved_r_offset(T, n) : nullptr, T, n, d, dt,
+        H, F, w, w_stride, W, w_static, scale, eps, sinkhorn_iters, gamma_next, pre_eps, H_out,
+        w_out, u_next, saved, saved ? saved + hc::saved_r_offset(T, n) : nullptr, T, n, d, dt,
         static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+hc_status hc_post_mix_weights(const void* H, const void* F, const float* w, int64_t w_stride,
+                              const void* W, const float* w_static, float scale, float eps,
+                              int32_t sinkhorn_iters, void* H_out, float* w_out, float* saved,
+                              int64_t saved_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt_arg,
+                              void* stream) {
+    return post_weights(H, F, w, w_stride, W, w_static, scale, eps, sinkhorn_iters, nullptr, 0.0f,
+                        H_out, w_out, nullptr, saved, saved_bytes, T, n, d, enum_value(dt_arg),
+                        stream);
+}
+
+hc_status hc_post_weights_pre_mix(const void* H, const void* F, const float* w, int64_t w_stride,
+                                  const void* W, const float* w_static, float scale, float eps,
+                                  int32_t sinkhorn_iters, const float* gamma_next, float pre_eps,
+                                  void* H_out, float* w_out, void* u_next, float* saved,
+                                  int64_t saved_bytes, int64_t T, int32_t n, int32_t d,
+                                  hc_dtype dt_arg, void* stream) {
+    // the read-mix half needs both of its buffers
+    if (T > 0 && (!gamma_next || !u_next)) return HC_ERR_NULL;
+    return post_weights(H, F, w, w_stride, W, w_static, scale, eps, sinkhorn_iters, gamma_next,
+                        pre_eps, H_out, w_out, u_next, saved, saved_bytes, T, n, d,
+                        enum_value(dt_arg), stream);
 }
 
 hc_status hc_sinkhorn(const float* logits, float* w_out, int32_t iters, int64_t T, int32_t n,

@@ -65,13 +65,16 @@ hipError_t launch_weights_raw(const void* H, const void* W, float eps, float* P,
 hipError_t launch_weights_save(const void* H, const void* W, const float* w_static, float scale,
                                float eps, int iters, float* w_out, float* P, float* r, int64_t T,
                                int n, int d, int dt, hipStream_t s);
-// Post fused with the next layer's per-token weights (W held in registers):
-// the largest d it takes for storage dtype dt (0: dt not taken).
+// Post fused with the next layer's per-token weights (W held in registers)
+// and, when u_out is not null, with the next layer's read-mix (gain gamma,
+// RMSNorm eps pre_eps): the largest d it takes for storage dtype dt (0: dt
+// not taken).
 int post_weights_max_hidden(int dt);
 hipError_t launch_post_mix_weights(const void* H, const void* F, const float* w, int64_t w_stride,
                                    const void* W, const float* w_static, float scale, float eps,
-                                   int iters, void* H_out, float* w_out, float* P, float* rn,
-                                   int64_t T, int n, int d, int dt, hipStream_t s);
+                                   int iters, const float* gamma, float pre_eps, void* H_out,
+                                   float* w_out, void* u_out, float* P, float* rn, int64_t T, int n,
+                                   int d, int dt, hipStream_t s);
 // The per-stream projections P [T][n][K] and norms r [T][n] the forward keeps
 // for the gradient pass: floats, r at saved_r_offset(T, n).
 int64_t saved_r_offset(int64_t T, int n);

@@ -57,7 +57,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxWaves = 8;    // 512-thread workgroups
 #ifndef PFD
-#define PFD 2
+#define PFD 1
 #endif
 
 // Value of lane J of this lane's quad (DPP quad_perm [J,J,J,J]); written
@@ -454,6 +454,10 @@ template <> struct FLoad<1> {
         return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
     }
     static __device__ __forceinline__ uint32_t w(T x, int i) { return x; }
+    static __device__ __forceinline__ T make(const uint32_t (&q)[1]) { return q[0]; }
+    static __device__ __forceinline__ void st(uint8_t* p, T x) {
+        __builtin_nontemporal_store(x, reinterpret_cast<uint32_t*>(p));
+    }
 };
 template <> struct FLoad<2> {
     typedef u32x2 T;
@@ -461,6 +465,10 @@ template <> struct FLoad<2> {
         return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
     }
     static __device__ __forceinline__ uint32_t w(T x, int i) { return i == 0 ? x.x : x.y; }
+    static __device__ __forceinline__ T make(const uint32_t (&q)[2]) { return T{q[0], q[1]}; }
+    static __device__ __forceinline__ void st(uint8_t* p, T x) {
+        __builtin_nontemporal_store(x, reinterpret_cast<T*>(p));
+    }
 };
 template <> struct FLoad<4> {
     typedef u32x4 T;
@@ -469,6 +477,10 @@ template <> struct FLoad<4> {
     }
     static __device__ __forceinline__ uint32_t w(T x, int i) {
         return i == 0 ? x.x : (i == 1 ? x.y : (i == 2 ? x.z : x.w));
+    }
+    static __device__ __forceinline__ T make(const uint32_t (&q)[4]) { return T{q[0], q[1], q[2], q[3]}; }
+    static __device__ __forceinline__ void st(uint8_t* p, T x) {
+        __builtin_nontemporal_store(x, reinterpret_cast<T*>(p));
     }
 };
 
@@ -499,29 +511,49 @@ constexpr int kRing = 32;   // tokens whose records wait in LDS before one store
 
 // FULL: every lane holds data (n = 4, the quads cover the row exactly and
 // fill the workgroup), so no lane needs a mask.
-template <int N, typename S, int VPL, int PF, bool FULL>
+//
+// PRE: the next layer's read-mix as well.  Its input is the stored H' of the
+// token, whose alpha is known only once the token's record is formed (after
+// the token's barrier, by the wave that forms the record), so the read-mix
+// runs two tokens behind the write-back: the rounded H' of every token is
+// parked in LDS (each lane its own vectors, three tokens deep), the record
+// wave parks alpha beside it, and two steps later every lane reads its share
+// of the row of every stream back (lane r of a quad takes the same bytes of
+// the row it loads of F), mixes them in hc_pre_mix's order and parks its
+// wave's sum of squares; the normalised u is stored a step after that, when
+// every wave's sum is visible.  One workgroup barrier per token, as without
+// the read-mix; the record ring is halved to leave the LDS for the parked H'.
+template <int N, typename S, int VPL, int PF, bool FULL, bool PRE>
 __global__ __launch_bounds__(512) void post_weights_kernel(
     const uint8_t* H, const uint8_t* __restrict__ F, const float* __restrict__ w,
     int64_t w_stride, const uint8_t* __restrict__ W, const float* __restrict__ w_static,
-    float scale, float eps, int iters, uint8_t* H_out, float* __restrict__ w_out,
+    float scale, float eps, int iters, const float* __restrict__ gamma, float pre_eps,
+    uint8_t* H_out, float* __restrict__ w_out, uint8_t* __restrict__ u_out,
     float* __restrict__ p_out, float* __restrict__ r_out, int64_t T, int d, int qn) {
     using Gm = PWGeom<N, S, VPL>;
     constexpr int K = Gm::K, G = Gm::G, V = Gm::V, KS = Gm::KS, NV = Gm::NV, NVP = Gm::NVP,
-                  FE = Gm::FE;
+                  FE = Gm::FE, FB = Gm::FB;
     constexpr int E = Word<S>::kElems;
     constexpr int RL = N + N * N;       // [beta | A], the part of a record the write-back reads
     constexpr int SV = N * K + N;       // kept state per token: projections and norms
+    constexpr int KP = kMaxWaves * 64 + 1;   // pitch of a parked vector index (16-byte units)
+    constexpr int RING = PRE ? kRing / 2 : kRing;
     // per token: the waves' row partials, double-buffered; per wave: the
     // finalising wave's sums and logits; the records (and kept state) of the
-    // last 2 kRing tokens; the current and next token's [beta | A]
+    // last 2 RING tokens; the current and next token's [beta | A]; with the
+    // read-mix, the parked H' and alpha of three tokens and the waves' sums
+    // of squares of two
     __shared__ __attribute__((aligned(16))) float part[2][kMaxWaves][4][Gm::SLOT];
     __shared__ float fin[kMaxWaves][Gm::SLOT + 32];
-    __shared__ float oring[2 * kRing][K];
-    __shared__ float pring[2 * kRing][SV];
+    __shared__ float oring[2 * RING][K];
+    __shared__ float pring[2 * RING][SV];
     __shared__ float recl[2][32];
+    __shared__ uint4 hkeep[PRE ? 3 * VPL * KP : 1];
+    __shared__ float alds[3][4];
+    __shared__ float upart[2][kMaxWaves];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nw = blockDim.x >> 6;
+    const int nw = FULL ? kMaxWaves : (int)(blockDim.x >> 6);
     const int r = lane & 3, Q = tid >> 2;
     const int nvec = d / V;
     const int64_t row_bytes = (int64_t)d * Gm::SB;
@@ -538,9 +570,9 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
         hoff[v] = hval[v] ? (int64_t)r * row_bytes + (int64_t)vi * 16 : 0;
     }
     // the quad's F bytes: lane r takes bytes [r FB, (r + 1) FB) of its vectors
-    const int fvi = Q + ((r * Gm::FB) / 16) * qn;
+    const int fvi = Q + ((r * FB) / 16) * qn;
     const bool fval = FULL || (Q < qn && fvi < nvec);
-    const int64_t foff = fval ? (int64_t)fvi * 16 + (r * Gm::FB) % 16 : 0;
+    const int64_t foff = fval ? (int64_t)fvi * 16 + (r * FB) % 16 : 0;
 
     // this lane's quarter of the quad's W slice: rows 4g + r at the quad's
     // positions, as bf16 MFMA operands (zero past K and past d)
@@ -556,6 +588,13 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
 #pragma unroll
             for (int s = 0; s < Op4<S>::kSteps; ++s) wb[g][v * Op4<S>::kSteps + s] = Op4<S>::get(x, s);
         }
+    }
+    // the read-mix gain at this lane's share of the row (the F positions)
+    float gm[FE];
+    if constexpr (PRE) {
+        const int64_t g0 = fval ? foff / Gm::SB : 0;
+#pragma unroll
+        for (int e = 0; e < FE; ++e) gm[e] = gamma[g0 + e];
     }
 
     // Rows PF tokens ahead.  The record's [beta | A] goes through LDS: every
@@ -591,16 +630,16 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
 
     // the records (and kept state) of ring block b, in one pass of all lanes
     auto flush = [&](int b, int count) {
-        const int base = (b * kRing) % (2 * kRing);
+        const int base = (b * RING) % (2 * RING);
         for (int e = tid; e < count * K; e += blockDim.x) {
             const int j = e / K, c = e % K;
-            const int64_t t = blockIdx.x + (int64_t)(b * kRing + j) * stride;
+            const int64_t t = blockIdx.x + (int64_t)(b * RING + j) * stride;
             w_out[t * K + c] = oring[base + j][c];
         }
         if (keep) {
             for (int e = tid; e < count * SV; e += blockDim.x) {
                 const int j = e / SV, c = e % SV;
-                const int64_t t = blockIdx.x + (int64_t)(b * kRing + j) * stride;
+                const int64_t t = blockIdx.x + (int64_t)(b * RING + j) * stride;
                 if (c < N * K) p_out[t * N * K + c] = pring[base + j][c];
                 else r_out[t * N + (c - N * K)] = pring[base + j][c];
             }
@@ -610,7 +649,8 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
     // The record of local token tf: its totals (the waves' row partials
     // added in a fixed order, all of a lane's loads issued before its adds),
     // norms, projections, z, then tanh or the mHC transform; into the ring
-    // (and the kept state).  One wave.
+    // (and the kept state).  One wave.  With the read-mix, its alpha is also
+    // parked for the read-mix two steps on (so the two agree bitwise).
     auto finish = [&](int tf) {
         float* tt = &fin[wave][0];
         float* lgs = tt + Gm::SLOT;
@@ -630,8 +670,9 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        float* orow = oring[tf % (2 * kRing)];
-        float* prow = pring[tf % (2 * kRing)];
+        float* orow = oring[tf % (2 * RING)];
+        float* prow = pring[tf % (2 * RING)];
+        float* arow = alds[tf % 3];
         float rs[N];
 #pragma unroll
         for (int i = 0; i < N; ++i) rs[i] = 1.0f / sqrtf(tt[i * NVP + NV - 1] / (float)d + eps);
@@ -647,7 +688,9 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
                 for (int i = 0; i < N; ++i) prow[i * K + lane] = pc[i];
             }
             if (iters == 0) {
-                orow[lane] = wst + scale * tanhf(z);
+                const float x = wst + scale * tanhf(z);
+                orow[lane] = x;
+                if (PRE && lane < N) arow[lane] = x;
             } else {
                 lgs[lane] = fmaf(scale, z, wst);
             }
@@ -669,6 +712,7 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
             mhc_quad<N>(r, a, b, row, iters);
             if (mine) {
                 orow[r] = a;
+                if constexpr (PRE) arow[r] = a;
                 orow[N + r] = b;
 #pragma unroll
                 for (int j = 0; j < N; ++j) orow[2 * N + r * N + j] = row[j];
@@ -676,13 +720,75 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
         }
     };
 
+    // The read-mix of local token tf from its parked H': this lane's FE
+    // positions of every stream (quad lane j's copy), x = sum_j alpha_j h_j
+    // in hc_pre_mix's order, and the wave's sum of x^2 into upart.
+    float xk[FE];
+    auto pre_mix = [&](int tf, const float (&al)[N]) {
+        typedef typename FLoad<VPL>::T FW;
+        const int vv = (r * FB) / 16, wo = ((r * FB) % 16) / 4;
+        const uint32_t* kp =
+            reinterpret_cast<const uint32_t*>(&hkeep[(tf % 3) * VPL * KP + vv * KP + 4 * Q]) + wo;
+        float h[N][FE];
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const FW x = *reinterpret_cast<const FW*>(kp + 4 * j);
+#pragma unroll
+            for (int q = 0; q < FE / E; ++q) unpack_word<S>(FLoad<VPL>::w(x, q), h[j] + q * E);
+        }
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < FE; ++e) {
+            float x = al[0] * h[0][e];
+#pragma unroll
+            for (int j = 1; j < N; ++j) x = fmaf(al[j], h[j][e], x);
+            xk[e] = x;
+            ss = fmaf(x, x, ss);
+        }
+        ss = wave_sum(fval ? ss : 0.0f);
+        if (lane == 0) upart[tf & 1][wave] = ss;
+    };
+    // u of local token tf from xk, once every wave's sum is visible
+    auto u_store = [&](int tf) {
+        float us[kMaxWaves];
+#pragma unroll
+        for (int i = 0; i < kMaxWaves; ++i) us[i] = i < nw ? upart[tf & 1][i] : 0.0f;
+        float s = us[0];
+#pragma unroll
+        for (int i = 1; i < kMaxWaves; ++i) s += us[i];
+        const float rr = 1.0f / sqrtf(s / (float)d + pre_eps);
+        uint32_t q[FB / 4];
+#pragma unroll
+        for (int k = 0; k < FB / 4; ++k) {
+            float o[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = gm[k * E + e] * (xk[k * E + e] * rr);
+            q[k] = pack_word<S>(o);
+        }
+        const int64_t t = blockIdx.x + (int64_t)tf * stride;
+        if (fval) FLoad<VPL>::st(u_out + t * row_bytes + foff, FLoad<VPL>::make(q));
+    };
+
     int tl = 0;   // tokens this workgroup has done
-    auto step = [&](auto kc, int64_t t) {
+    // one token; ST = how many earlier tokens there are, capped at 2 (the
+    // read-mix of the token two back needs two)
+    auto step = [&](auto kc, auto stc, int64_t t) {
         constexpr int k = decltype(kc)::value;
+        constexpr int ST = decltype(stc)::value;
         const int64_t ta = t + PF * stride;
         fetch<N, S, VPL>(sl[(k + PF) % (PF + 1)], H, F, ta, T, hoff, foff, row_bytes);
         rq[(k + PF) % (PF + 1)] = rec_load(ta);
         Slot<N, S, VPL>& cur = sl[k];
+
+        // the read-mix of the token two back (its alpha parked after the
+        // previous barrier), and the u of the one before it
+        if constexpr (PRE && ST >= 2) {
+            float al[N];
+#pragma unroll
+            for (int j = 0; j < N; ++j) al[j] = alds[(tl - 2) % 3][j];
+            if (tl >= 3) u_store(tl - 3);
+            pre_mix(tl - 2, al);
+        }
 
         // this lane's row of A and its beta, read from LDS a token ago
         float Ar[N], br = brn;
@@ -723,6 +829,7 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
             }
             o[v] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
             if (FULL || hval[v]) st16_stream(Ot + hoff[v], o[v]);
+            if constexpr (PRE) hkeep[(tl % 3) * VPL * KP + v * KP + tid] = o[v];
         }
 
         // the next layer's weights from the stored values: sums of squares
@@ -783,7 +890,7 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
 
         // the records in the ring up to the previous token are visible to
         // every lane from here on: store a full block of them
-        if (tl % kRing == 0 && tl > 0) flush(tl / kRing - 1, kRing);
+        if (tl % RING == 0 && tl > 0) flush(tl / RING - 1, RING);
 
         // the next token's row of A and beta, into registers now so that
         // its LDS latency is not on the next token's path
@@ -799,41 +906,77 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
         ++tl;
     };
 
-    // whole rounds of PF + 1 tokens with no test per token, then the rest
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
     int64_t t0 = blockIdx.x;
-    for (; t0 + PF * stride < T; t0 += (PF + 1) * stride) {
-        step(std::integral_constant<int, 0>{}, t0);
-        if constexpr (PF >= 1) step(std::integral_constant<int, 1>{}, t0 + stride);
-        if constexpr (PF >= 2) step(std::integral_constant<int, 2>{}, t0 + 2 * stride);
+    if (t0 + PF * stride < T) {
+        // the first round: with the read-mix, its tokens have fewer than two
+        // earlier ones
+        step(I0{}, I0{}, t0);
+        if constexpr (PF >= 1) step(I1{}, I1{}, t0 + stride);
+        if constexpr (PF >= 2) step(I2{}, I2{}, t0 + 2 * stride);
+        t0 += (PF + 1) * stride;
+        // whole rounds of PF + 1 tokens with no test per token, then the rest
+        for (; t0 + PF * stride < T; t0 += (PF + 1) * stride) {
+            step(I0{}, I2{}, t0);
+            if constexpr (PF >= 1) step(I1{}, I2{}, t0 + stride);
+            if constexpr (PF >= 2) step(I2{}, I2{}, t0 + 2 * stride);
+        }
+        if (t0 < T) step(I0{}, I2{}, t0);
+        if constexpr (PF >= 1) {
+            if (t0 + stride < T) step(I1{}, I2{}, t0 + stride);
+        }
+        if constexpr (PF >= 2) {
+            if (t0 + 2 * stride < T) step(I2{}, I2{}, t0 + 2 * stride);
+        }
+    } else {
+        // fewer than PF + 1 tokens (the grid never exceeds T, so at least one)
+        step(I0{}, I0{}, t0);
+        if constexpr (PF >= 1) {
+            if (t0 + stride < T) step(I1{}, I1{}, t0 + stride);
+        }
     }
-    if (t0 < T) step(std::integral_constant<int, 0>{}, t0);
-    if constexpr (PF >= 1) {
-        if (t0 + stride < T) step(std::integral_constant<int, 1>{}, t0 + stride);
-    }
-    if constexpr (PF >= 2) {
-        if (t0 + 2 * stride < T) step(std::integral_constant<int, 2>{}, t0 + 2 * stride);
+    if constexpr (PRE) {
+        // the read-mix of the last two tokens and the u of the last three,
+        // each once what it reads is visible
+        float al[N];
+        if (tl >= 2) {
+#pragma unroll
+            for (int j = 0; j < N; ++j) al[j] = alds[(tl - 2) % 3][j];
+            if (tl >= 3) u_store(tl - 3);
+            pre_mix(tl - 2, al);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < N; ++j) al[j] = alds[(tl - 1) % 3][j];
+        if (tl >= 2) u_store(tl - 2);
+        pre_mix(tl - 1, al);
+        __syncthreads();
+        u_store(tl - 1);
     }
     // every record not yet stored, once the last one is visible
     __syncthreads();
-    // blocks flushed in the loop: at steps m kRing <= tl - 1, m >= 1
-    const int done = tl >= 1 ? ((tl - 1) / kRing) * kRing : 0;
-    for (int b = done / kRing; b * kRing < tl; ++b)
-        flush(b, (tl - b * kRing) < kRing ? tl - b * kRing : kRing);
+    // blocks flushed in the loop: at steps m RING <= tl - 1, m >= 1
+    const int done = tl >= 1 ? ((tl - 1) / RING) * RING : 0;
+    for (int b = done / RING; b * RING < tl; ++b)
+        flush(b, (tl - b * RING) < RING ? tl - b * RING : RING);
 }
 
-template <int N, typename S, int VPL, int PF>
+template <int N, typename S, int VPL, int PF, bool PRE>
 hipError_t go(const void* H, const void* F, const float* w, int64_t w_stride, const void* W,
-              const float* w_static, float scale, float eps, int iters, void* H_out, float* w_out,
-              float* P, float* rn, int64_t T, int d, hipStream_t s) {
+              const float* w_static, float scale, float eps, int iters, const float* gamma,
+              float pre_eps, void* H_out, float* w_out, void* u_out, float* P, float* rn, int64_t T,
+              int d, hipStream_t s) {
     const int nvec = d / Store<S>::kElems;
     const int qn = (nvec + VPL - 1) / VPL;
     const int block = (4 * qn + 63) / 64 * 64;
     const bool full = N == 4 && qn * VPL == nvec && 4 * qn == block;
     void (*kernel)(const uint8_t*, const uint8_t*, const float*, int64_t, const uint8_t*, const float*,
-                   float, float, int, uint8_t*, float*, float*, float*, int64_t, int, int) =
-        post_weights_kernel<N, S, VPL, PF, false>;
+                   float, float, int, const float*, float, uint8_t*, float*, uint8_t*, float*, float*,
+                   int64_t, int, int) = post_weights_kernel<N, S, VPL, PF, false, PRE>;
     if constexpr (N == 4) {
-        if (full) kernel = post_weights_kernel<N, S, VPL, PF, true>;
+        if (full) kernel = post_weights_kernel<N, S, VPL, PF, true, PRE>;
     }
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -847,18 +990,34 @@ hipError_t go(const void* H, const void* F, const float* w, int64_t w_stride, co
     const dim3 grid((unsigned)(T < resident ? T : resident));
     return launch(kernel, grid, dim3(block), 0, s, static_cast<const uint8_t*>(H),
                   static_cast<const uint8_t*>(F), w, w_stride, static_cast<const uint8_t*>(W), w_static,
-                  scale, eps, iters, static_cast<uint8_t*>(H_out), w_out, P, rn, T, d, qn);
+                  scale, eps, iters, gamma, pre_eps, static_cast<uint8_t*>(H_out), w_out,
+                  static_cast<uint8_t*>(u_out), P, rn, T, d, qn);
+}
+
+struct PWArgs {
+    const void* H; const void* F; const float* w; int64_t w_stride; const void* W;
+    const float* w_static; float scale; float eps; int iters; const float* gamma; float pre_eps;
+    void* H_out; float* w_out; void* u_out; float* P; float* rn; int64_t T; int d; hipStream_t s;
+};
+
+template <int N, typename S, int VPL>
+hipError_t go_pre(const PWArgs& a) {
+    if (a.u_out != nullptr)
+        return go<N, S, VPL, PFD, true>(a.H, a.F, a.w, a.w_stride, a.W, a.w_static, a.scale, a.eps,
+                                        a.iters, a.gamma, a.pre_eps, a.H_out, a.w_out, a.u_out, a.P,
+                                        a.rn, a.T, a.d, a.s);
+    return go<N, S, VPL, PFD, false>(a.H, a.F, a.w, a.w_stride, a.W, a.w_static, a.scale, a.eps,
+                                     a.iters, nullptr, 0.0f, a.H_out, a.w_out, nullptr, a.P, a.rn,
+                                     a.T, a.d, a.s);
 }
 
 template <typename S, int VPL>
-hipError_t by_n(int n, const void* H, const void* F, const float* w, int64_t w_stride, const void* W,
-                const float* w_static, float scale, float eps, int iters, void* H_out, float* w_out,
-                float* P, float* rn, int64_t T, int d, hipStream_t s) {
+hipError_t by_n(int n, const PWArgs& a) {
     switch (n) {
-        case 1: return go<1, S, VPL, PFD>(H, F, w, w_stride, W, w_static, scale, eps, iters, H_out, w_out, P, rn, T, d, s);
-        case 2: return go<2, S, VPL, PFD>(H, F, w, w_stride, W, w_static, scale, eps, iters, H_out, w_out, P, rn, T, d, s);
-        case 3: return go<3, S, VPL, PFD>(H, F, w, w_stride, W, w_static, scale, eps, iters, H_out, w_out, P, rn, T, d, s);
-        case 4: return go<4, S, VPL, PFD>(H, F, w, w_stride, W, w_static, scale, eps, iters, H_out, w_out, P, rn, T, d, s);
+        case 1: return go_pre<1, S, VPL>(a);
+        case 2: return go_pre<2, S, VPL>(a);
+        case 3: return go_pre<3, S, VPL>(a);
+        case 4: return go_pre<4, S, VPL>(a);
     }
     return hipErrorInvalidValue;
 }
@@ -873,21 +1032,21 @@ int post_weights_max_hidden(int dt) {
 
 hipError_t launch_post_mix_weights(const void* H, const void* F, const float* w, int64_t w_stride,
                                    const void* W, const float* w_static, float scale, float eps,
-                                   int iters, void* H_out, float* w_out, float* P, float* rn,
-                                   int64_t T, int n, int d, int dt, hipStream_t s) {
+                                   int iters, const float* gamma, float pre_eps, void* H_out,
+                                   float* w_out, void* u_out, float* P, float* rn, int64_t T, int n,
+                                   int d, int dt, hipStream_t s) {
+    const PWArgs a = {H, F, w, w_stride, W, w_static, scale, eps, iters, gamma, pre_eps,
+                      H_out, w_out, u_out, P, rn, T, d, s};
     // vectors per lane: as few as fill at most 128 quads (512 threads)
     if (dt == 2) {
         const int nvec = d / Store<fp8_t>::kElems;
-        if (nvec <= 128)
-            return by_n<fp8_t, 1>(n, H, F, w, w_stride, W, w_static, scale, eps, iters, H_out, w_out, P, rn, T, d, s);
-        return by_n<fp8_t, 2>(n, H, F, w, w_stride, W, w_static, scale, eps, iters, H_out, w_out, P, rn, T, d, s);
+        if (nvec <= 128) return by_n<fp8_t, 1>(n, a);
+        return by_n<fp8_t, 2>(n, a);
     }
     const int nvec = d / Store<bf16_t>::kElems;
-    if (nvec <= 128)
-        return by_n<bf16_t, 1>(n, H, F, w, w_stride, W, w_static, scale, eps, iters, H_out, w_out, P, rn, T, d, s);
-    if (nvec <= 256)
-        return by_n<bf16_t, 2>(n, H, F, w, w_stride, W, w_static, scale, eps, iters, H_out, w_out, P, rn, T, d, s);
-    return by_n<bf16_t, 4>(n, H, F, w, w_stride, W, w_static, scale, eps, iters, H_out, w_out, P, rn, T, d, s);
+    if (nvec <= 128) return by_n<bf16_t, 1>(n, a);
+    if (nvec <= 256) return by_n<bf16_t, 2>(n, a);
+    return by_n<bf16_t, 4>(n, a);
 }
 
 }  // namespace hc

@@ -60,6 +60,8 @@ _SIGS = {
     "hc_sinkhorn_backward": [_fp, _fp, _fp, _i32, _vp, _i64, _i64, _i32, _vp],
     "hc_post_mix_weights": [_vp, _vp, _fp, _i64, _vp, _fp, _f32, _f32, _i32, _vp, _fp, _fp, _i64,
                             _i64, _i32, _i32, _i32, _vp],
+    "hc_post_weights_pre_mix": [_vp, _vp, _fp, _i64, _vp, _fp, _f32, _f32, _i32, _fp, _f32, _vp,
+                                _fp, _vp, _fp, _i64, _i64, _i32, _i32, _i32, _vp],
 }
 EXPORTS = tuple(_SIGS) + ("hc_status_str", "hc_abi_version", "hc_backward_workspace",
                           "hc_weights_backward_workspace", "hc_sinkhorn_backward_workspace",
@@ -315,6 +317,47 @@ def post_mix_weights(H, F, w, W, w_static, scale: float, eps: float = 1e-6,
           ro.data_ptr(), saved.data_ptr() if keep else None, saved.numel() * 4 if keep else 0,
           T, n, d, _dt(H), _stream(stream))
     return (o, ro, saved) if keep else (o, ro)
+
+
+@_on_launch_stream
+def post_weights_pre_mix(H, F, w, W, w_static, scale: float, gamma_next, eps: float = 1e-6,
+                         pre_eps: float = 1e-6, sinkhorn_iters: int = 0, out=None, w_out=None,
+                         u_out=None, saved=None, stream=None):
+    """The whole layer boundary in one pass: returns (H', w_next, u_next),
+    H' = post_mix(H, F, w) (bitwise), w_next = the next layer's per-token
+    weights from H' (as post_mix_weights), u_next = pre_mix(H', w_next,
+    gamma_next, pre_eps) to one unit in the last place.  ``out=H`` runs in
+    place; ``saved`` as post_mix_weights (the result then ends with it).
+    bf16 and FP8 storage, d <= 4096."""
+    T, n, d, K = _H(H)
+    ws = _record(w, T, K)
+    _dev(F, "F")
+    if F.dtype != H.dtype or tuple(F.shape) != (T, d):
+        raise ValueError("F must match H's dtype and have shape (T, d)")
+    _dev(gamma_next, "gamma_next")
+    if gamma_next.dtype != torch.float32 or tuple(gamma_next.shape) != (d,):
+        raise ValueError("gamma_next must be float32 of shape (d,)")
+    o = torch.empty_like(H) if out is None else _dev(out, "out")
+    if o.dtype != H.dtype or o.shape != H.shape:
+        raise ValueError("out must match H")
+    u = torch.empty((T, d), dtype=H.dtype, device=H.device) if u_out is None else _dev(u_out, "u_out")
+    if u.dtype != H.dtype or tuple(u.shape) != (T, d):
+        raise ValueError("u_out must match H's dtype and have shape (T, d)")
+    _, _, _, _, ro = _weights_args(H, W, w_static, w_out)
+    keep = saved is not None and saved is not False
+    if saved is True:
+        saved = torch.empty(max(int(lib().hc_weights_saved_bytes(T, n)), 16) // 4,
+                            dtype=torch.float32, device=H.device)
+    if keep:
+        _dev(saved, "saved")
+        if saved.dtype != torch.float32:
+            raise ValueError("saved must be float32")
+    _call("hc_post_weights_pre_mix", H.data_ptr(), F.data_ptr(), w.data_ptr(), ws, W.data_ptr(),
+          w_static.data_ptr(), float(scale), float(eps), int(sinkhorn_iters),
+          gamma_next.data_ptr(), float(pre_eps), o.data_ptr(), ro.data_ptr(), u.data_ptr(),
+          saved.data_ptr() if keep else None, saved.numel() * 4 if keep else 0, T, n, d, _dt(H),
+          _stream(stream))
+    return (o, ro, u, saved) if keep else (o, ro, u)
 
 
 @_on_launch_stream

@@ -70,6 +70,13 @@ def post_weights_bytes(n: int, d: int, s: int) -> int:
     return post_bytes(n, d, s, True) + record_bytes(n)
 
 
+def post_weights_pre_bytes(n: int, d: int, s: int) -> int:
+    """The whole layer boundary with per-token weights in one pass: read H
+    and F, write H' and the next block input u; the per-token [beta | A]
+    read and the next record written (alpha is used from the chip)."""
+    return (2 * n + 2) * d * s + (n + n * n) * RECORD_BYTES_PER_ENTRY + record_bytes(n)
+
+
 def sinkhorn_bytes(n: int) -> int:
     """Read one logit record, write one weight record."""
     return 2 * record_bytes(n)

@@ -197,6 +197,33 @@ hc_status hc_post_pre_mix(const void* H, const void* F, const float* w, int64_t 
                           const float* gamma_next, float eps, void* H_out, void* u_next,
                           int64_t T, int32_t n, int32_t d, hc_dtype dt, void* stream);
 
+/* The whole layer boundary with per-token weights in one pass: the
+ * write-back of one layer, the next layer's per-token weights from its
+ * result, and the next layer's read-mix + RMSNorm with those weights
+ * ([GLOSS] definition: learned mixing before and after every block; [EXPL]
+ * "What four streams cost per token": every layer boundary hands the n-fold
+ * state across, and this moves it once: H and F in, H' and u out).
+ * Equivalent to
+ *   hc_post_mix_weights(H, F, w, w_stride, W, w_static, scale, eps,
+ *                       sinkhorn_iters, H_out, w_out, saved, saved_bytes)
+ *   hc_pre_mix(H_out, w_out, K, gamma_next, pre_eps, u_next)
+ * with H_out bitwise hc_post_mix's and w_out as hc_post_mix_weights gives
+ * it.  u_next uses the alpha stored in w_out and H_out as stored (rounded);
+ * it agrees with that hc_pre_mix call to the rounding of the RMSNorm sum
+ * (added in another order), i.e. to one unit in the last place of dt.
+ *   arguments as hc_post_mix_weights, plus
+ *   gamma_next    [d] fp32, 16-byte aligned: the next read-mix's RMSNorm gain
+ *   pre_eps       its RMSNorm epsilon (> 0, finite)
+ *   u_next        [T][d] in dt, 16-byte aligned, overlapping nothing
+ * Errors as hc_post_mix_weights; gamma_next or u_next NULL (T > 0) is
+ * HC_ERR_NULL; a bad pre_eps is HC_ERR_ARG. */
+hc_status hc_post_weights_pre_mix(const void* H, const void* F, const float* w, int64_t w_stride,
+                                  const void* W, const float* w_static, float scale, float eps,
+                                  int32_t sinkhorn_iters, const float* gamma_next, float pre_eps,
+                                  void* H_out, float* w_out, void* u_next, float* saved,
+                                  int64_t saved_bytes, int64_t T, int32_t n, int32_t d,
+                                  hc_dtype dt, void* stream);
+
 /* Bytes of device workspace the backward calls need for T tokens of width d
  * with n streams (0 for T <= 0).  The caller owns it; it holds partial sums
  * (per workgroup, or per token and wave for per-token records) and every

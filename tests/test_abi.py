@@ -17,7 +17,7 @@ OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, ARG = 0, 1, 2, 3, 4, 5, 6
 BF16, F32, FP8 = hc.HC_BF16, hc.HC_F32, hc.HC_FP8
 
 # fake, never dereferenced device addresses (16-byte aligned, far apart)
-P = [0x10000000 * (i + 1) for i in range(8)]
+P = [0x10000000 * (i + 1) for i in range(10)]
 MiB = 1 << 20
 
 
@@ -51,7 +51,7 @@ def test_status_strings(L):
         s = hc.status_str(code)
         assert s.startswith("HC_")
     assert hc.status_str(99).startswith("HC_ERR_UNKNOWN")
-    assert hc.abi_version() == 4
+    assert hc.abi_version() == 5
 
 
 def pre(L, H=P[0], w=P[1], ws=0, g=P[2], eps=1e-6, u=P[3], T=16, n=4, d=4096, dt=BF16):
@@ -213,6 +213,33 @@ def test_post_mix_weights_validation(L):
     assert f(sv=P[7], svb=need - 4) == ARG
     assert f(sv=P[7] + 4, svb=need) == ALIGN and f(sv=P[6], svb=need) == ALIAS
     assert f(sv=P[5] + 16, svb=need) == ALIAS and f(sv=P[0], svb=need) == ALIAS
+
+
+def test_post_weights_pre_mix_validation(L):
+    """The whole layer boundary: every check of hc_post_mix_weights, plus the
+    read-mix's gain and output (present, aligned, overlapping nothing) and
+    its epsilon.  Nothing is launched (fake pointers, or T = 0)."""
+    K = 24
+    need = int(L.hc_weights_saved_bytes(16, 4))
+
+    def f(**k):
+        return L.hc_post_weights_pre_mix(
+            k.get("H", P[0]), k.get("F", P[1]), k.get("w", P[2]), k.get("ws", 0), k.get("W", P[3]),
+            k.get("wst", P[4]), k.get("scale", 0.01), k.get("eps", 1e-6), k.get("it", 0),
+            k.get("g", P[8]), k.get("peps", 1e-6), k.get("O", P[5]), k.get("wo", P[6]),
+            k.get("u", P[9]), k.get("sv", None), k.get("svb", 0), k.get("T", 16), k.get("n", 4),
+            k.get("d", 4096), k.get("dt", BF16), None)
+    assert f(T=0) == OK and f(T=0, g=None, u=None) == OK and f(T=0, dt=FP8) == OK
+    assert f(dt=F32) == DTYPE and f(d=4104) == SHAPE and f(ws=K - 1) == SHAPE
+    assert f(peps=0.0) == ARG and f(peps=float("nan")) == ARG and f(eps=0.0) == ARG
+    for name in ("H", "F", "w", "W", "wst", "O", "wo", "g", "u"):
+        assert f(**{name: None}) == NULL, name
+    assert f(g=P[8] + 4) == ALIGN and f(u=P[9] + 8) == ALIGN
+    # u overlaps nothing; gamma is not overwritten by any output
+    assert f(u=P[0]) == ALIAS and f(u=P[1] + 16) == ALIAS and f(u=P[5]) == ALIAS
+    assert f(u=P[6]) == ALIAS and f(u=P[8]) == ALIAS and f(u=P[2]) == ALIAS
+    assert f(O=P[8]) == ALIAS and f(wo=P[8]) == ALIAS
+    assert f(sv=P[9], svb=need) == ALIAS and f(sv=P[7], svb=need - 4) == ARG
 
 
 def test_sinkhorn_validation(L):
