@@ -344,6 +344,37 @@ hc_status hc_post_mix_backward(const void* dH_out, const void* H, const void* F,
                                                  T, n, d, dt, static_cast<hipStream_t>(stream)));
 }
 
+hc_status hc_post_mix_backward_noalloc(const void* dH_out, const void* H, const void* F,
+                                       const float* w, int64_t w_stride, void* dH, void* dF,
+                                       float* dw, int64_t T, int32_t n, int32_t d, hc_dtype dt_arg,
+                                       void* stream) {
+    const int dt = enum_value(dt_arg);
+    if (!dtype_wide(dt)) return HC_ERR_DTYPE;
+    hc_status st = check_nd(n, d, T, dt);
+    if (st != HC_OK) return st;
+    const int K = record_len(n);
+    if ((st = check_stride(w_stride, K, T)) != HC_OK) return st;
+    if (T == 0) return HC_OK;
+    if (!dH_out || !H || !F || !w || !dF || !dw) return HC_ERR_NULL;     // dH may be NULL
+    const bool shared = w_stride == 0;
+    if (shared && hc::post_backward_scratch_bytes(T, n) > hc::post_backward_scratch_max_bytes())
+        return HC_ERR_ARG;
+    if (misaligned(dH_out, 16) || misaligned(H, 16) || misaligned(F, 16) || misaligned(dH, 16) ||
+        misaligned(dF, 16) || misaligned(w, 4) || misaligned(dw, 4))
+        return HC_ERR_ALIGN;
+    const int64_t s = elem_bytes(dt);
+    const Span sG{dH_out, T * n * d * s}, sH{H, T * n * d * s}, sF{F, T * d * s},
+        sW{w, record_span(T, w_stride, K)}, sdH{dH, dH ? T * n * d * s : 0}, sdF{dF, T * d * s},
+        sdw{dw, (shared ? 1 : T) * K * 4};
+    const Span ins[] = {sG, sH, sF, sW};
+    for (const Span& o : {sdH, sdF, sdw})
+        for (const Span& i : ins)
+            if (overlap(o, i)) return HC_ERR_ALIAS;
+    if (overlap(sdH, sdF) || overlap(sdH, sdw) || overlap(sdF, sdw)) return HC_ERR_ALIAS;
+    return from_hip(hc::launch_post_mix_backward_noalloc(dH_out, H, F, w, w_stride, dH, dF, dw, T, n,
+                                                         d, dt, static_cast<hipStream_t>(stream)));
+}
+
 hc_status hc_pre_mix_backward(const void* du, const void* H, const float* w, int64_t w_stride,
                               const float* gamma, float eps, const void* dH_in, const void* dH_out,
                               void* dH, float* dw, float* dgamma, void* workspace,

@@ -32,6 +32,8 @@
 //
 // Both kernels stream rows like the forward ones (one 16-byte vector per
 // thread per stream, all loads of a token issued first).
+#include <mutex>
+
 #include "hc_device.h"
 #include "hc_launch.h"
 
@@ -801,6 +803,40 @@ hipError_t post_backward_with(const void* dHo, const void* H, const void* F, con
     return launch_sum_rows2(&job, 1, s);
 }
 
+// The allocation-free variant's scratch: one array per GPU for the life of
+// the process, shared by every call on that GPU (calls that overlap on one
+// GPU race for it).  Host code never passes the array's name to a kernel
+// (in host code it is a host-side stand-in, not a device address); it
+// passes the device address that hipGetSymbolAddress returns for the
+// current device, looked up once per device.
+constexpr int64_t kScratchBytes = int64_t(1) << 20;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+hipError_t scratch_on_current_device(float** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = p;
+    });
+    if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+    *out = static_cast<float*>(g_scratch_ptr[dev]);
+    return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_post_mix_backward(const void* dHo, const void* H, const void* F, const float* w,
@@ -810,6 +846,32 @@ hipError_t launch_post_mix_backward(const void* dHo, const void* H, const void* 
     float* ws = static_cast<float*>(work);
     return post_backward_with(dHo, H, F, w, w_stride, dH, dF, dw, ws ? ws + sp.rec : nullptr,
                               ws ? ws + sp.tmp2 : nullptr, T, n, d, dt, s);
+}
+
+int64_t post_backward_scratch_bytes(int64_t T, int n) {
+    if (T <= 0 || n <= 0) return 0;
+    const int64_t M = n + int64_t(n) * n;
+    const int64_t prows = (T + post_group_of(T) - 1) / post_group_of(T);
+    return (prows * M + sum_rows_tmp_floats(prows, M)) * 4;
+}
+
+int64_t post_backward_scratch_max_bytes() { return kScratchBytes; }
+
+hipError_t launch_post_mix_backward_noalloc(const void* dHo, const void* H, const void* F,
+                                            const float* w, int64_t w_stride, void* dH, void* dF,
+                                            float* dw, int64_t T, int n, int d, int dt, hipStream_t s) {
+    float* part = nullptr;
+    float* tmp = nullptr;
+    if (w_stride == 0) {
+        float* base = nullptr;
+        const hipError_t e = scratch_on_current_device(&base);
+        if (e != hipSuccess) return e;
+        const int64_t M = n + int64_t(n) * n;
+        const int64_t prows = (T + post_group_of(T) - 1) / post_group_of(T);
+        part = base;
+        tmp = base + prows * M;
+    }
+    return post_backward_with(dHo, H, F, w, w_stride, dH, dF, dw, part, tmp, T, n, d, dt, s);
 }
 
 hipError_t launch_pre_mix_backward(const void* du, const void* H, const float* w, int64_t w_stride,

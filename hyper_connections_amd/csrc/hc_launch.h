@@ -57,6 +57,13 @@ hipError_t launch_pre_mix_backward(const void* du, const void* H, const float* w
                                    void* dH, float* dw, float* dgamma, void* work, int64_t T, int n,
                                    int d, int dt, hipStream_t s);
 int64_t backward_workspace_bytes(int64_t T, int n, int d);
+// The post gradient with its scratch in the library's own per-GPU array
+// (nothing allocated): bytes it needs, and the array's size.
+int64_t post_backward_scratch_bytes(int64_t T, int n);
+int64_t post_backward_scratch_max_bytes();
+hipError_t launch_post_mix_backward_noalloc(const void* dHo, const void* H, const void* F,
+                                            const float* w, int64_t w_stride, void* dH, void* dF,
+                                            float* dw, int64_t T, int n, int d, int dt, hipStream_t s);
 hipError_t launch_sum_records(const float* rec, int64_t T, int K, float* out, hipStream_t s);
 hipError_t launch_sinkhorn(const float* logits, float* w_out, int iters, int64_t T, int n,
                            hipStream_t s);

@@ -60,6 +60,8 @@ _SIGS = {
     "hc_sinkhorn_backward": [_fp, _fp, _fp, _i32, _vp, _i64, _i64, _i32, _vp],
     "hc_post_mix_weights": [_vp, _vp, _fp, _i64, _vp, _fp, _f32, _f32, _i32, _vp, _fp, _fp, _i64,
                             _i64, _i32, _i32, _i32, _vp],
+    "hc_post_mix_backward_noalloc": [_vp, _vp, _vp, _fp, _i64, _vp, _vp, _fp, _i64, _i32, _i32,
+                                     _i32, _vp],
     "hc_post_weights_pre_mix": [_vp, _vp, _fp, _i64, _vp, _fp, _f32, _f32, _i32, _fp, _f32, _vp,
                                 _fp, _vp, _fp, _i64, _i64, _i32, _i32, _i32, _vp],
 }
@@ -445,6 +447,38 @@ def post_mix_backward(dH_out, H, F, w, dH=None, dF=None, dw=None, workspace=None
           dH.data_ptr() if dH is not None else None, dF.data_ptr(), dw.data_ptr(),
           wk.data_ptr() if wk is not None else None,
           wkb, T, n, d, _dt(H), _stream(stream))
+    return dH, dF, dw
+
+
+@_on_launch_stream
+def post_mix_backward_noalloc(dH_out, H, F, w, dH=None, dF=None, dw=None, stream=None,
+                              h_grad=True):
+    """post_mix_backward without a workspace: the library's own per-GPU
+    scratch array holds a shared record's partial sums, so the call allocates
+    nothing when the outputs are given.  Calls that overlap on one GPU race
+    for that array."""
+    T, n, d, K = _H(H)
+    ws = _record(w, T, K)
+    _dev(dH_out, "dH_out")
+    _dev(F, "F")
+    if dH_out.dtype != H.dtype or dH_out.shape != H.shape:
+        raise ValueError("dH_out must match H")
+    if F.dtype != H.dtype or tuple(F.shape) != (T, d):
+        raise ValueError("F must match H's dtype and have shape (T, d)")
+    if not h_grad:
+        if dH is not None:
+            raise ValueError("dH given with h_grad=False")
+    else:
+        dH = torch.empty_like(H) if dH is None else _dev(dH, "dH")
+        if dH.shape != H.shape or dH.dtype != H.dtype:
+            raise ValueError("dH does not match H")
+    dF = torch.empty_like(F) if dF is None else _dev(dF, "dF")
+    if dF.shape != F.shape or dF.dtype != F.dtype:
+        raise ValueError("dF does not match F")
+    dw = _grad_record(dw, T, K, ws, H.device)
+    _call("hc_post_mix_backward_noalloc", dH_out.data_ptr(), H.data_ptr(), F.data_ptr(),
+          w.data_ptr(), ws, dH.data_ptr() if dH is not None else None, dF.data_ptr(),
+          dw.data_ptr(), T, n, d, _dt(H), _stream(stream))
     return dH, dF, dw
 
 

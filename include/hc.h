@@ -34,7 +34,9 @@
  *    stream reproduce the ordinary residual x + f(x) bitwise ([EXPL]
  *    "Jargon", Identity initialization).
  *  - Every pointer is device memory owned by the caller.  The library
- *    allocates nothing and keeps no state; calls are thread-safe.
+ *    allocates nothing and keeps no state, and calls are thread-safe; the one
+ *    exception is hc_post_mix_backward_noalloc, whose scratch is a fixed
+ *    array per GPU that overlapping calls on one GPU share.
  *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  Work
  *    is enqueued and the call returns without synchronising.
  *  - All arguments are validated before anything is launched; a failed check
@@ -248,6 +250,22 @@ hc_status hc_post_mix_backward(const void* dH_out, const void* H, const void* F,
                                int64_t w_stride, void* dH, void* dF, float* dw,
                                void* workspace, int64_t workspace_bytes, int64_t T,
                                int32_t n, int32_t d, hc_dtype dt, void* stream);
+
+/* hc_post_mix_backward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same gradients, bitwise, with no workspace argument.  A
+ * shared record's partial sums go to the library's own scratch array, one
+ * per GPU, 1 MiB, held until the process ends (at n <= 4 every T fits; a
+ * larger need is HC_ERR_ARG).  Calls on one GPU share that array, and each
+ * call overwrites what the last left there: calls that overlap on one GPU
+ * (concurrent streams, several host threads) race and must be serialised by
+ * the caller.  Per-token records use no scratch.  Arguments, layouts and
+ * errors otherwise as hc_post_mix_backward. */
+hc_status hc_post_mix_backward_noalloc(const void* dH_out, const void* H, const void* F,
+                                       const float* w, int64_t w_stride, void* dH, void* dF,
+                                       float* dw, int64_t T, int32_t n, int32_t d, hc_dtype dt,
+                                       void* stream);
+
 
 /* Gradients of hc_pre_mix (RMSNorm and read-mix written out):
  *   dy = gamma * du, dx = r * (dy - x * r^2 * mean_k(dy_k x_k)),
