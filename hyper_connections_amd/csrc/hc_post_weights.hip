@@ -548,6 +548,7 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
     __shared__ float oring[2 * RING][K];
     __shared__ float pring[2 * RING][SV];
     __shared__ float recl[2][32];
+    __shared__ float wsl[32];
     __shared__ uint4 hkeep[PRE ? 3 * VPL * KP : 1];
     __shared__ float alds[3][4];
     __shared__ float upart[2][kMaxWaves];
@@ -607,7 +608,10 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
     // the static part of output lane (loaded once: a load in the loop would
     // wait behind the prefetch)
     const float wst = w_static[lane < K ? lane : K - 1];
-    auto rec_load = [&](int64_t t) {
+    // (every helper below is forced inline: a call would save the live
+    // registers to scratch and wait for every load in flight, the prefetch
+    // included)
+    auto rec_load = [&](int64_t t) __attribute__((always_inline)) {
         const int64_t tc = t < T ? t : T - 1;
         return w[tc * w_stride + N + rl];
     };
@@ -619,6 +623,7 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
         rq[k] = rec_load(blockIdx.x + k * stride);
     }
     if (rec_lane) recl[0][lane] = rq[0];
+    if (tid < K) wsl[tid] = w_static[tid];
     __syncthreads();
     float Arn[N], brn;
     {
@@ -629,7 +634,7 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
     }
 
     // the records (and kept state) of ring block b, in one pass of all lanes
-    auto flush = [&](int b, int count) {
+    auto flush = [&](int b, int count) __attribute__((always_inline)) {
         const int base = (b * RING) % (2 * RING);
         for (int e = tid; e < count * K; e += blockDim.x) {
             const int j = e / K, c = e % K;
@@ -651,7 +656,7 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
     // norms, projections, z, then tanh or the mHC transform; into the ring
     // (and the kept state).  One wave.  With the read-mix, its alpha is also
     // parked for the read-mix two steps on (so the two agree bitwise).
-    auto finish = [&](int tf) {
+    auto finish = [&](int tf) __attribute__((always_inline)) {
         float* tt = &fin[wave][0];
         float* lgs = tt + Gm::SLOT;
         for (int j = lane; j < Gm::SLOT; j += 64) {
@@ -720,11 +725,71 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
         }
     };
 
+    // The tanh-mode record of local token tf, outputs 4g + c of column class
+    // c, by one wave (four waves share a token's record).  Two lanes per
+    // total: lane q (< 32) adds the partials of slots 0..15, lane q + 32 those
+    // of slots 16..31, each in slot order, and the halves are added across
+    // the wave halves.  Totals: the N sums of squares, then P_i[4g + c].
+    auto finish_c = [&](int tf, int c) __attribute__((always_inline)) {
+        constexpr int NT = N + G * N;
+        float* tt = &fin[wave][0];
+        const int q = lane & 31, half = lane >> 5;
+        const int j = q < N ? q * NVP + NV - 1 : c * NVP + (q < NT ? q - N : 0);
+        float x[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int sidx = 16 * half + k;
+            const float y = part[tf & 1][sidx >> 2][sidx & 3][j];
+            x[k] = (FULL || (sidx >> 2) < nw) ? y : 0.0f;
+        }
+        float v = x[0];
+#pragma unroll
+        for (int k = 1; k < 16; ++k) v += x[k];
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                         false);
+        v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        if (lane < NT) tt[lane] = v;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float* orow = oring[tf % (2 * RING)];
+        float* prow = pring[tf % (2 * RING)];
+        float rs[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) rs[i] = 1.0f / sqrtf(tt[i] / (float)d + eps);
+        const int g = lane, o = 4 * lane + c;
+        if (g < G && o < K) {
+            const float* pc = tt + N + g * N;
+            float z = rs[0] * pc[0];
+#pragma unroll
+            for (int i = 1; i < N; ++i) z = fmaf(rs[i], pc[i], z);
+            z = z / (float)N;
+            if (keep) {
+#pragma unroll
+                for (int i = 0; i < N; ++i) prow[i * K + o] = pc[i];
+            }
+            const float rec = wsl[o] + scale * tanhf(z);
+            orow[o] = rec;
+            if (PRE && o < N) alds[tf % 3][o] = rec;
+        }
+        if (keep && c == 0 && lane < N) prow[N * K + lane] = rs[lane];
+    };
+    // the record of local token tf: four waves in tanh mode, one in mHC mode
+    auto finish_any = [&](int tf) __attribute__((always_inline)) {
+        if (iters == 0) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (c < K && wave == (tf + c) % nw) finish_c(tf, c);
+        } else if (wave == tf % nw) {
+            finish(tf);
+        }
+    };
+
     // The read-mix of local token tf from its parked H': this lane's FE
     // positions of every stream (quad lane j's copy), x = sum_j alpha_j h_j
     // in hc_pre_mix's order, and the wave's sum of x^2 into upart.
     float xk[FE];
-    auto pre_mix = [&](int tf, const float (&al)[N]) {
+    auto pre_mix = [&](int tf, const float (&al)[N]) __attribute__((always_inline)) {
         typedef typename FLoad<VPL>::T FW;
         const int vv = (r * FB) / 16, wo = ((r * FB) % 16) / 4;
         const uint32_t* kp =
@@ -749,7 +814,7 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
         if (lane == 0) upart[tf & 1][wave] = ss;
     };
     // u of local token tf from xk, once every wave's sum is visible
-    auto u_store = [&](int tf) {
+    auto u_store = [&](int tf) __attribute__((always_inline)) {
         float us[kMaxWaves];
 #pragma unroll
         for (int i = 0; i < kMaxWaves; ++i) us[i] = i < nw ? upart[tf & 1][i] : 0.0f;
@@ -772,7 +837,7 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
     int tl = 0;   // tokens this workgroup has done
     // one token; ST = how many earlier tokens there are, capped at 2 (the
     // read-mix of the token two back needs two)
-    auto step = [&](auto kc, auto stc, int64_t t) {
+    auto step = [&](auto kc, auto stc, int64_t t) __attribute__((always_inline)) {
         constexpr int k = decltype(kc)::value;
         constexpr int ST = decltype(stc)::value;
         const int64_t ta = t + PF * stride;
@@ -901,8 +966,8 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
             for (int j = 0; j < N; ++j) Arn[j] = r < N ? rlds[N + r * N + j] : 0.0f;
         }
 
-        // this token's record, by one wave (a different one each token)
-        if (wave == tl % nw) finish(tl);
+        // this token's record
+        finish_any(tl);
         ++tl;
     };
 

@@ -32,11 +32,13 @@ from hyper_connections_amd.workloads import identity_record, layer_record, make_
 pytestmark = pytest.mark.gpu
 
 SAMPLE = 256
-# Drift against the bf16-storing fp64 chain.  Measured on MI355X over the 78
-# layers on this sample: rising from 0 (layer 1 is one rounding apart at
-# most) to a maximum recorded in profiles/chain-bf16_drift.md; the bound is
-# about twice that maximum.
-DRIFT_BOUND = 0.1
+# Drift against the bf16-storing fp64 chain (single-layer parity is the pass
+# criterion; the end-to-end drift, which compounds fp32-against-fp64
+# rounding over 78 layers, is bounded and reported).  Measured on MI355X
+# over the 78 layers on this sample: rising from 0 at layer 1 to 0.020
+# (0.033 against pure fp64), per layer in profiles/chain-bf16_drift.md;
+# the bound is twice that maximum.
+DRIFT_BOUND = 0.04
 
 
 @pytest.fixture(autouse=True)
