@@ -33,8 +33,20 @@ def test_code_text_sees_code_changes():
 def test_committed_counter_summaries_name_known_kernels():
     import glob
     import json
-    for path in glob.glob(os.path.join(ROOT, "profiles", "*.json")):
+    paths = (glob.glob(os.path.join(ROOT, "profiles", "*_counters.json")) +
+             glob.glob(os.path.join(ROOT, "profiles", "*_mfma.json")))
+    assert paths
+    for path in paths:
         with open(path) as fh:
             rec = json.load(fh)
         assert rec["kernel"] in bench.KERNEL_SOURCES, path
         assert len(rec["source_sha"]) == 16, path
+
+
+def test_committed_drift_summary_is_within_its_bound():
+    import json
+    with open(os.path.join(ROOT, "profiles", "chain-bf16_drift.json")) as fh:
+        rec = json.load(fh)
+    assert len(rec["rows"]) == rec["layers"] == 78
+    drift = [r["drift_vs_bf16_storing_fp64"] for r in rec["rows"]]
+    assert max(drift) == rec["max_drift_vs_bf16_storing_fp64"] <= rec["drift_bound"]
