@@ -338,6 +338,39 @@ def summarize_drift(drift_json: str, cmds: list):
     log(f"[bench] wrote {base}.md: max drift {max(d16):.3g} (bf16-storing), {max(d64):.3g} (fp64)")
 
 
+def summarize_margins(margins_json: str, cmds: list):
+    """The gradient checks' achieved errors (written by the backward tests
+    with HC_MARGIN_OUT set) as profiles/backward_margins.{json,md}: how far
+    below its tolerance every check passed."""
+    with open(margins_json) as fh:
+        rows = json.load(fh)
+    for r in rows:
+        r["ratio"] = r["error"] / r["tolerance"]
+    rows.sort(key=lambda r: -r["ratio"])
+    rec = {"checks": len(rows), "commands": cmds, "worst_ratio": rows[0]["ratio"] if rows else None,
+           "rows": rows}
+    base = os.path.join(PROFILES, "backward_margins")
+    with open(base + ".json", "w") as fh:
+        json.dump(rec, fh, indent=0)
+    ratios = sorted(r["ratio"] for r in rows)
+    q = lambda f: ratios[min(len(ratios) - 1, int(f * len(ratios)))]  # noqa: E731
+    with open(base + ".md", "w") as fh:
+        fh.write("# Achieved errors of the gradient checks\n\n")
+        fh.write("Every gradient record, dgamma, dW and dw_static check of the backward parity "
+                 "tests (error metric: max |gpu - ref| / max(|ref|, rms of the reference row); "
+                 "dalpha of pre against its Cauchy-Schwarz bound), with the tolerance it is "
+                 "held to.\n\nCommands (paths relative to the repository root):\n\n")
+        for c in cmds:
+            fh.write(f"    {c}\n")
+        fh.write(f"\n{len(rows)} checks.  Error / tolerance: median {q(0.5):.3g}, 90th percentile "
+                 f"{q(0.9):.3g}, largest {ratios[-1]:.3g}.\n\n")
+        fh.write("The 30 closest to their tolerance:\n\n| check | error | tolerance | ratio |\n"
+                 "|---|---|---|---|\n")
+        for r in rows[:30]:
+            fh.write(f"| {r['check']} | {r['error']:.3g} | {r['tolerance']:.0e} | {r['ratio']:.3g} |\n")
+    log(f"[bench] wrote {base}.md: {len(rows)} checks, largest error/tolerance {ratios[-1]:.3g}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -377,6 +410,9 @@ def main():
                     help="summarise a rocprofv3 --pmc run of MFMA/LDS counters into profiles/ and exit")
     ap.add_argument("--summarize-drift", metavar="DRIFT_JSON",
                     help="summarise the chain test's per-layer drift (HC_DRIFT_OUT) into profiles/ and exit")
+    ap.add_argument("--summarize-margins", metavar="MARGINS_JSON",
+                    help="summarise the gradient checks' achieved errors (HC_MARGIN_OUT) into "
+                         "profiles/ and exit")
     ap.add_argument("--kernel", default="post_mix", help="kernel for --summarize-counters/--summarize-mfma")
     ap.add_argument("--command", action="append", default=[],
                     help="profiling command to record in the summary (repeatable)")
@@ -391,6 +427,9 @@ def main():
         return
     if args.summarize_drift:
         summarize_drift(args.summarize_drift, args.command)
+        return
+    if args.summarize_margins:
+        summarize_margins(args.summarize_margins, args.command)
         return
 
     if args.gpus != 1:

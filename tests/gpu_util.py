@@ -30,6 +30,18 @@ TOL_BF16_ULP = 2.0 ** -8
 TOL_FP8 = 2.0 ** -3
 TOL_RECORD = 1e-5      # fp32 weight records (any storage dtype of H)
 
+# With HC_MARGIN_OUT set to a path, every gradient check's achieved error
+# and its tolerance are collected and written there as JSON at the end of
+# the session (tests/conftest.py), so the margin is visible and not only
+# the pass or fail.
+MARGINS: list = []
+
+
+def record_margin(what: str, err: float, tol: float) -> None:
+    import os
+    if os.environ.get("HC_MARGIN_OUT"):
+        MARGINS.append({"check": what, "error": float(err), "tolerance": float(tol)})
+
 
 def need_gpu():
     if not torch.cuda.is_available():

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import check, dev, host, need_gpu, rel_err
+from gpu_util import check, dev, host, need_gpu, rel_err, record_margin
 from hyper_connections_amd import hc
 from hyper_connections_amd.workloads import f32_to_bf16_bits, identity_record, make_inputs, workload
 
@@ -29,6 +29,7 @@ def storage(x, dt):
 
 def grad_check(got, ref, what):
     e = rel_err(np.asarray(got, np.float64), np.asarray(ref, np.float64))
+    record_margin(what, e, TOL_GRAD)
     assert e <= TOL_GRAD, f"{what}: {e:.3g} > {TOL_GRAD}"
 
 
@@ -50,6 +51,7 @@ def dalpha_check(got, ref, du, H, w, g, eps, what):
     if got.shape[0] == 1:          # shared record: summed over tokens
         bound = bound.sum(axis=0, keepdims=True)
     e = np.max(np.abs(got - ref) / np.maximum(bound, 1e-30))
+    record_margin(what + " (of the Cauchy-Schwarz bound)", e, 1e-5)
     assert e <= 1e-5, f"{what}: {e:.3g} of the Cauchy-Schwarz bound"
 
 

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import check, dev, host, need_gpu, rel_err
+from gpu_util import check, dev, host, need_gpu, rel_err, record_margin
 from hyper_connections_amd import hc
 from hyper_connections_amd.workloads import f32_to_bf16_bits, identity_record, make_inputs, workload
 
@@ -29,6 +29,7 @@ def storage(x, dt):
 
 def grad_check(got, ref, what):
     e = rel_err(np.asarray(got, np.float64), np.asarray(ref, np.float64))
+    record_margin(what, e, TOL_GRAD)
     assert e <= TOL_GRAD, f"{what}: {e:.3g} > {TOL_GRAD}"
 
 
@@ -191,6 +192,7 @@ def test_weights_backward_saturated_tanh(dt, n):
         check(host(dH), rdH, f"saturated dH n={n} {dt}")
     else:
         e = rel_err(host(dH), rdH)
+        record_margin(f"saturated dH n={n} {dt}", e, 1e-4)
         assert e <= 1e-4, f"saturated dH n={n} {dt}: {e:.3g} > 1e-4"
     grad_check(host(dW), rdW, f"saturated dW n={n} {dt}")
     grad_check(host(dws)[None], rdws[None], f"saturated dw_static n={n} {dt}")
