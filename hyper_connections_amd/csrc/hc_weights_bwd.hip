@@ -231,6 +231,77 @@ __global__ __launch_bounds__(256) void wgrad_coef_kernel(
     }
 }
 
+// The tanh-mode coefficients with four lanes per token: lane q of a quad
+// takes outputs c = q, q + 4, ... (dz_c, its share of dl and of
+// s_i = sum_c P_ic dz_c, the quad adding the shares), so a 256-thread
+// workgroup covers the 64 tokens that one wave covers in wgrad_coef_kernel
+// and the same dl_part rows come out; the loads of a token's P row are
+// spread over four lanes.  dz is bitwise wgrad_coef_kernel's; s_i, and so
+// b_i, are added in another order.  The workgroup's dl sums go through LDS
+// in token order.
+template <int N>
+__global__ __launch_bounds__(256) void wgrad_coef4_kernel(
+    const float* __restrict__ P, const float* __restrict__ r, const float* __restrict__ dw,
+    const float* __restrict__ dw2, float scale, float* __restrict__ dz,
+    float* __restrict__ dl_part, float* __restrict__ ab, int64_t T, int d) {
+    constexpr int K = 2 * N + N * N;
+    constexpr int J = (K + 3) / 4;                  // outputs per lane
+    __shared__ float dlw[J][4][64];
+    const int q = threadIdx.x & 3, tk = threadIdx.x >> 2;
+    float dls[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) dls[j] = 0.0f;
+    for (int64_t b = blockIdx.x; b * 64 < T; b += gridDim.x) {
+        const int64_t t = b * 64 + tk;
+        const bool ok = t < T;
+        const int64_t tc = ok ? t : T - 1;
+        const float* p = P + tc * N * K;
+        float ri[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) ri[i] = r[tc * N + i];
+        float si[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) si[i] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int c = q + 4 * j;
+            const int cc = c < K ? c : K - 1;
+            // z as the forward kernel forms it: sum_i r_i P_ic in stream order, / n
+            float v = ri[0] * p[cc];
+#pragma unroll
+            for (int i = 1; i < N; ++i) v = fmaf(ri[i], p[i * K + cc], v);
+            const float z = v / (float)N;
+            const float g = dw2 ? dw[tc * K + cc] + dw2[tc * K + cc] : dw[tc * K + cc];
+            const float gz = g * scale * dtanh(z);
+            const bool live = ok && c < K;
+            if (live) dz[t * K + c] = gz;
+            dls[j] += live ? g : 0.0f;
+#pragma unroll
+            for (int i = 0; i < N; ++i) si[i] = fmaf(p[i * K + cc], live ? gz : 0.0f, si[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < N; ++i) si[i] = quad_sum(si[i]);
+        if (ok && q < N) {
+            float sq = si[0];
+#pragma unroll
+            for (int i = 1; i < N; ++i) sq = q == i ? si[i] : sq;
+            const float rq = ri[q];
+            ab[t * 2 * N + q] = rq / (float)N;
+            ab[t * 2 * N + N + q] = -(rq * rq * rq) * sq / ((float)N * (float)d);
+        }
+    }
+    // the workgroup's dl: each output's 64 token lanes added in token order
+#pragma unroll
+    for (int j = 0; j < J; ++j) dlw[j][q][tk] = dls[j];
+    __syncthreads();
+    if (threadIdx.x < K) {
+        const int c = threadIdx.x, j = c / 4, qq = c % 4;
+        float v = dlw[j][qq][0];
+        for (int k = 1; k < 64; ++k) v += dlw[j][qq][k];
+        dl_part[(int64_t)blockIdx.x * K + c] = v;
+    }
+}
+
 // ---------------------------------------------------- streaming dH and dW pass
 
 // The four waves' partial dW (A x B tiles of f32x4, the same layout in every
@@ -613,7 +684,11 @@ template <int N>
 hipError_t coef_go(const float* P, const float* r, const float* dw, const float* dw2, const float* ws,
                    float scale, int iters, float* scr, float* dz, float* dl_part, float* ab, int64_t T,
                    int d, hipStream_t s) {
-    // one wave per workgroup: 16384 tokens still reach every CU
+    // 64 tokens per workgroup either way (the dl_part rows): one lane per
+    // token for the mHC transform, four for tanh
+    if (iters == 0)
+        return launch(wgrad_coef4_kernel<N>, dim3((unsigned)coef_blocks(T)), dim3(256), 0, s, P, r,
+                      dw, dw2, scale, dz, dl_part, ab, T, d);
     return launch(wgrad_coef_kernel<N>, dim3((unsigned)coef_blocks(T)), dim3(64), 0, s, P, r, dw, dw2,
                   ws, scale, iters, scr, dz, dl_part, ab, T, d);
 }
