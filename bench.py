@@ -264,7 +264,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, kernel: str, workload: st
            "weights": tr.weights_bytes(wl.n, wl.d, wl.elem_bytes),
            "post_mix_weights": tr.post_weights_bytes(wl.n, wl.d, wl.elem_bytes),
            "post_weights_pre_mix": tr.post_weights_pre_bytes(wl.n, wl.d, wl.elem_bytes),
-           "post_pre_mix": tr.post_pre_bytes(wl.n, wl.d, wl.elem_bytes),
+           "post_pre_mix": tr.post_pre_bytes(wl.n, wl.d, wl.elem_bytes, per_tok),
            "post_mix_backward": tr.post_bwd_bytes(wl.n, wl.d, wl.elem_bytes, h_grad=not fold),
            "pre_mix_backward": tr.pre_bwd_bytes(wl.n, wl.d, wl.elem_bytes, True),
            "weights_backward": tr.weights_bwd_bytes(wl.n, wl.d, wl.elem_bytes),
@@ -451,6 +451,18 @@ def main():
         run_all(args)
         return
     out, wl, inp = run_workload(args, args.workload)
+    if wl.kind in ("static", "mhc") and not (args.fused or args.backward or args.graph):
+        # the same layer at steady state in a layer loop, one fused boundary
+        # (this layer's write-back and the next read-mix) per layer: reported
+        # beside the headline step, which is this layer's pre then post
+        import copy
+        a = copy.copy(args)
+        a.fused = True
+        f, _, _ = run_workload(a, args.workload)
+        out["fused_boundary"] = {k: f[k] for k in ("value", "ms_per_step", "hbm_gbps", "frac_hbm_peak",
+                                                   "step_gbps", "frac_step_bytes_peak")}
+        out["fused_boundary"]["kernels"] = {k: v["us"] for k, v in f["kernels"].items()}
+        del f
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds,
                                            one_thread_s=args.cpu_seconds / 2
@@ -524,7 +536,7 @@ def run_workload(args, name: str):
     launch_bytes = {
         "pre_mix": traffic.pre_bytes(n, d, s, per_tok) * T,
         "post_mix": traffic.post_bytes(n, d, s, per_tok) * T,
-        "post_pre_mix": traffic.post_pre_bytes(n, d, s) * T,
+        "post_pre_mix": traffic.post_pre_bytes(n, d, s, per_tok) * T,
         "post_mix_weights": traffic.post_weights_bytes(n, d, s) * T,
         "post_weights_pre_mix": traffic.post_weights_pre_bytes(n, d, s) * T,
         "weights": traffic.weights_bytes(n, d, s) * T,
@@ -621,6 +633,17 @@ def run_workload(args, name: str):
             ops = [("post_weights_pre_mix", lambda b: hc.post_weights_pre_mix(
                 b["H"], b["F"], b["w"], Wp, ws, wl.scale, gamma, wl.eps, wl.eps, 0, out=b["O"],
                 w_out=b["next"]["w"], u_out=b["u"]))]
+    elif wl.kind == "mhc" and args.fused:
+        # a layer boundary at steady state: the next layer's records from its
+        # logits, then this layer's write-back fused with the next read-mix
+        # (this layer's records were formed by the previous boundary)
+        for i, b in enumerate(bufs):
+            hc.sinkhorn(b["logits"], n, wl.iters, out=b["w"])
+            b["next"] = bufs[(i + 1) % sets]
+        torch.cuda.synchronize()
+        ops = [("sinkhorn", lambda b: hc.sinkhorn(b["next"]["logits"], n, wl.iters, out=b["next"]["w"])),
+               ("post_pre_mix", lambda b: hc.post_pre_mix(b["H"], b["F"], b["w"], b["next"]["w"], gamma,
+                                                          wl.eps, out=b["O"], u_out=b["u"]))]
     elif wl.kind == "mhc":
         ops = [("sinkhorn", lambda b: hc.sinkhorn(b["logits"], n, wl.iters, out=b["w"])),
                ("pre_mix", lambda b: hc.pre_mix(b["H"], b["w"], gamma, wl.eps, out=b["u"])),
