@@ -31,7 +31,12 @@
 //    12% faster on MI355X.  So the rows are loaded that way and each half
 //    chunk passes through a per-wave LDS buffer into the A layout.
 //  - B operand: W staged through LDS one k-chunk at a time (shared by the
-//    four waves; rows >= K and k >= d are zero), 16 bytes of row padding.
+//    four waves; rows >= K and k >= d are zero).
+//  - Both LDS buffers pad their rows by 32 bytes.  With 16 bytes the
+//    row-strided 16-byte reads of 16 lanes conflicted: measured on MI355X,
+//    bank-conflict cycles were 34% of the LDS active cycles (16 bytes on
+//    both), 15% (32 on W only), 26% (32 on the transpose only) and 0.9% (32
+//    on both).
 //  - C: one 16x16 tile per 16 outputs (two tiles for K = 24).
 //  - Epilogue through LDS (the wave's transpose buffer): the C tile and the
 //    row sums of squares are combined per token, then tanh or the mHC
@@ -143,13 +148,13 @@ struct WeightsGeom {
     static constexpr int TPW = 16 / N;                // tokens per wave
     static constexpr int V = Store<S>::kElems;        // elements per vector
     static constexpr int KC = 4 * kLV * V;            // k per chunk
-    static constexpr int RS = KC * Store<S>::kBytes + 16;  // LDS row pitch (bytes)
+    static constexpr int RS = KC * Store<S>::kBytes + 32;  // LDS row pitch (bytes)
     static constexpr int WBYTES = NT * 16 * RS;       // one W chunk in LDS
     static constexpr int PIECES = KC * Store<S>::kBytes / 16;  // 16-byte pieces per W row
     static constexpr int CPITCH = NT * 16 + 1;        // epilogue C row pitch (floats)
     static constexpr int EPI = 16 * CPITCH + 16 + TPW * K;  // floats per wave
     static constexpr int KH = KC * Store<S>::kBytes / 2;     // bytes per row per half chunk
-    static constexpr int TP = KH + 16;                // transpose row pitch (bytes)
+    static constexpr int TP = KH + 32;                // transpose row pitch (bytes)
     static constexpr int TBYTES = 16 * TP;            // transpose buffer per wave
     static_assert(EPI * 4 <= TBYTES, "the epilogue reuses the transpose buffer");
 };
@@ -197,7 +202,7 @@ __global__ __launch_bounds__(kWThreads) void weights_kernel(
         // 16 lanes each of rows 4s .. 4s+3 (lane -> row 4s + lane/16, 16-byte
         // piece lane%16), i.e. 256 contiguous bytes per row.  The MFMA A
         // operand wants lane -> row lane%16, so each half chunk is passed
-        // through the wave's LDS buffer (rows padded by 16 bytes: the
+        // through the wave's LDS buffer (rows padded so that the
         // row-strided reads are conflict-free).
         const int lrow = lane >> 4, lpiece = lane & 15;
         for (int c = 0; c < nchunks; ++c) {
