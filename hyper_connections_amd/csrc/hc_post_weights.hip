@@ -560,6 +560,11 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
     const int64_t row_bytes = (int64_t)d * Gm::SB;
     const int64_t stride = gridDim.x;
     const bool keep = p_out != nullptr;
+    // the norms 1/sqrt(sum/d + eps) use the hardware reciprocal square root
+    // (v_rsq_f32, about one ulp) on the sum scaled by 1/d: a few
+    // instructions where the rounded division and square root took about
+    // forty, once per stream for the records and once per token for u
+    const float inv_d = 1.0f / (float)d;
 
     // which of this lane's loads carry data, and from where
     bool hval[VPL];
@@ -680,7 +685,7 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
         float* arow = alds[tf % 3];
         float rs[N];
 #pragma unroll
-        for (int i = 0; i < N; ++i) rs[i] = 1.0f / sqrtf(tt[i * NVP + NV - 1] / (float)d + eps);
+        for (int i = 0; i < N; ++i) rs[i] = __builtin_amdgcn_rsqf(fmaf(tt[i * NVP + NV - 1], inv_d, eps));
         if (lane < K) {
             // output c lives in column class c % 4, group c / 4
             const float* pc = tt + (lane & 3) * NVP + (lane >> 2) * N;
@@ -756,7 +761,7 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
         float* prow = pring[tf % (2 * RING)];
         float rs[N];
 #pragma unroll
-        for (int i = 0; i < N; ++i) rs[i] = 1.0f / sqrtf(tt[i] / (float)d + eps);
+        for (int i = 0; i < N; ++i) rs[i] = __builtin_amdgcn_rsqf(fmaf(tt[i], inv_d, eps));
         const int g = lane, o = 4 * lane + c;
         if (g < G && o < K) {
             const float* pc = tt + N + g * N;
@@ -821,7 +826,7 @@ __global__ __launch_bounds__(512) void post_weights_kernel(
         float s = us[0];
 #pragma unroll
         for (int i = 1; i < kMaxWaves; ++i) s += us[i];
-        const float rr = 1.0f / sqrtf(s / (float)d + pre_eps);
+        const float rr = __builtin_amdgcn_rsqf(fmaf(s, inv_d, pre_eps));
         uint32_t q[FB / 4];
 #pragma unroll
         for (int k = 0; k < FB / 4; ++k) {
