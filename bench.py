@@ -56,7 +56,7 @@ KERNEL_SOURCES = {
     "block_tanh": "hc_rows.hip", "weights": "hc_weights.hip", "sinkhorn": "hc_weights.hip",
     "post_mix_backward": "hc_backward.hip", "pre_mix_backward": "hc_backward.hip",
     "sum_records": "hc_backward.hip", "weights_backward": "hc_weights_bwd.hip",
-    "weights_backward_stream": "hc_weights_bwd.hip",
+    "weights_backward_stream": "hc_weights_bwd.hip", "post_pre_mix_backward": "hc_backward.hip",
 }
 
 
@@ -136,6 +136,7 @@ XCDS = 8
 # the part of a kernel's name that picks it out of a trace (the boundary
 # kernel with and without the read-mix differ in the last template argument)
 KERNEL_TAGS = {"post_mix_backward": "post_bwd_kernel<", "pre_mix_backward": "pre_bwd_kernel<",
+               "post_pre_mix_backward": "post_pre_bwd_kernel<",
                "post_mix_weights": "post_weights_kernel<",
                "post_weights_pre_mix": "post_weights_kernel<",
                "weights_backward_stream": "wgrad_mfma_kernel<"}
@@ -145,7 +146,8 @@ KERNEL_LAST_ARG = {"post_mix_weights": "false>", "post_weights_pre_mix": "true>"
 def kernel_match(kernel: str, name: str) -> bool:
     """Whether a trace's kernel name is `kernel`'s."""
     tag = KERNEL_TAGS.get(kernel, f"{kernel}_kernel<")
-    if tag not in name:
+    # the whole identifier: pre_bwd_kernel is not post_pre_bwd_kernel
+    if f"::{tag}" not in name and not name.startswith(tag):
         return False
     last = KERNEL_LAST_ARG.get(kernel)
     return last is None or f" {last}(" in name
@@ -268,6 +270,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, kernel: str, workload: st
            "post_mix_backward": tr.post_bwd_bytes(wl.n, wl.d, wl.elem_bytes, h_grad=not fold),
            "pre_mix_backward": tr.pre_bwd_bytes(wl.n, wl.d, wl.elem_bytes, True),
            "weights_backward": tr.weights_bwd_bytes(wl.n, wl.d, wl.elem_bytes),
+           "post_pre_mix_backward": tr.post_pre_bwd_bytes(wl.n, wl.d, wl.elem_bytes),
            "weights_backward_stream": tr.weights_bwd_stream_bytes(wl.n, wl.d, wl.elem_bytes)}[kernel] * wl.T
     rec = {"kernel": kernel, "workload": workload, "source_sha": source_sha(kernel),
            "dispatches": {"FETCH_SIZE": len(fk), "WRITE_SIZE": len(wk)},
@@ -382,7 +385,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--fused", action="store_true",
                     help="fuse each write-back with the next read-mix (chain: every layer; "
-                         "static: one step is one fused layer boundary)")
+                         "static: one step is one fused layer boundary; static with --backward: "
+                         "one step is that boundary's gradient in one pass)")
     ap.add_argument("--backward", action="store_true",
                     help="time the layer's gradients: post backward (dF and its records), pre "
                          "backward forming the whole dH, shared-weight sums (static workloads); "
@@ -451,6 +455,17 @@ def main():
         run_all(args)
         return
     out, wl, inp = run_workload(args, args.workload)
+    if wl.kind == "static" and args.backward and not (args.fused or args.no_fold or args.graph):
+        # the same gradients at steady state in a stack of layers: one pass per
+        # layer boundary, reported beside the layer's separate post and pre
+        # gradients
+        import copy
+        a = copy.copy(args)
+        a.fused = True
+        f, _, _ = run_workload(a, args.workload)
+        out["fused_boundary"] = {k: f[k] for k in ("value", "ms_per_step", "hbm_gbps", "frac_hbm_peak")}
+        out["fused_boundary"]["kernels"] = {k: v["us"] for k, v in f["kernels"].items()}
+        del f
     if wl.kind in ("static", "mhc") and not (args.fused or args.backward or args.graph):
         # the same layer at steady state in a layer loop, one fused boundary
         # (this layer's write-back and the next read-mix) per layer: reported
@@ -545,6 +560,7 @@ def run_workload(args, name: str):
         "post_mix_backward": traffic.post_bwd_bytes(n, d, s, h_grad=not fold) * T,
         "pre_mix_backward": traffic.pre_bwd_bytes(n, d, s, True) * T,
         "weights_backward": traffic.weights_bwd_bytes(n, d, s) * T,
+        "post_pre_mix_backward": traffic.post_pre_bwd_bytes(n, d, s) * T,
     }
 
     if args.backward:
@@ -600,6 +616,14 @@ def run_workload(args, name: str):
         ops = [("post_mix_backward", post_bwd), ("pre_mix_backward", pre_bwd)]
         if wl.kind == "dynamic":
             ops.append(("weights_backward", weights_bwd))
+        elif args.fused:
+            # one layer boundary's gradient at steady state in a stack: this
+            # layer's read-mix and the previous layer's write-back in one pass
+            # (dH' arrives from the next boundary's call; H' is recomputed)
+            ops = [("post_pre_mix_backward", lambda b: hc.post_pre_mix_backward(
+                b["G"], b["du"], b["H"], b["F"], w_static, w_static, gamma, wl.eps, out=b["O"],
+                dF=b["dF"], dw=b["dwp"], dw_next=b["dwq"], dgamma_next=b["dg"],
+                workspace=b["ws"]))]
     # the kernels of one step, in order: (name, launch on buffer set b)
     elif wl.kind == "static" and args.fused:
         # one layer boundary: write-back of this layer fused with the next read-mix

@@ -95,7 +95,7 @@ const char* hc_status_str(hc_status status) {
     return "HC_ERR_UNKNOWN: unknown status code";
 }
 
-int32_t hc_abi_version(void) { return 5; }
+int32_t hc_abi_version(void) { return 6; }
 
 hc_status hc_pre_mix(const void* H, const float* w, int64_t w_stride, const float* gamma, float eps,
                      void* u, int64_t T, int32_t n, int32_t d, hc_dtype dt_arg, void* stream) {
@@ -415,6 +415,60 @@ hc_status hc_pre_mix_backward(const void* du, const void* H, const float* w, int
     return from_hip(hc::launch_pre_mix_backward(du, H, w, w_stride, gamma, eps, dH_in, dH_out, dH,
                                                 dw, dgamma, workspace, T, n, d, dt,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+hc_status hc_post_pre_mix_backward(const void* dH_out, const void* du_next, const void* H,
+                                   const void* F, const float* w, int64_t w_stride,
+                                   const float* w_next, int64_t w_next_stride,
+                                   const float* gamma_next, float eps, void* dH, void* dF, float* dw,
+                                   float* dw_next, float* dgamma_next, void* workspace,
+                                   int64_t workspace_bytes, int64_t T, int32_t n, int32_t d,
+                                   hc_dtype dt_arg, void* stream) {
+    const int dt = enum_value(dt_arg);
+    if (!dtype_wide(dt)) return HC_ERR_DTYPE;
+    hc_status st = check_nd(n, d, T, dt);
+    if (st != HC_OK) return st;
+    const int K = record_len(n);
+    if ((st = check_stride(w_stride, K, T)) != HC_OK) return st;
+    if ((st = check_stride(w_next_stride, K, T)) != HC_OK) return st;
+    if (w_stride != w_next_stride) return HC_ERR_ARG;   // both shared or both per token
+    if (!eps_ok(eps)) return HC_ERR_ARG;
+    if (T == 0) return HC_OK;
+    if (!dH_out || !du_next || !H || !F || !w || !w_next || !gamma_next || !dH || !dF || !dw ||
+        !dw_next || !dgamma_next || !workspace)
+        return HC_ERR_NULL;
+    if (workspace_bytes < hc_backward_workspace(T, n, d)) return HC_ERR_ARG;
+    if (misaligned(dH_out, 16) || misaligned(du_next, 16) || misaligned(H, 16) ||
+        misaligned(F, 16) || misaligned(gamma_next, 16) || misaligned(dH, 16) ||
+        misaligned(dF, 16) || misaligned(workspace, 16) || misaligned(w, 4) ||
+        misaligned(w_next, 4) || misaligned(dw, 4) || misaligned(dw_next, 4) ||
+        misaligned(dgamma_next, 4))
+        return HC_ERR_ALIGN;
+    const int64_t s = elem_bytes(dt);
+    const bool shared = w_stride == 0;
+    const Span sO{dH_out, T * n * d * s}, su{du_next, T * d * s}, sH{H, T * n * d * s},
+        sF{F, T * d * s}, sW{w, record_span(T, w_stride, K)},
+        sW2{w_next, record_span(T, w_next_stride, K)}, sg{gamma_next, int64_t(d) * 4},
+        sdH{dH, T * n * d * s}, sdF{dF, T * d * s}, sdw{dw, (shared ? 1 : T) * K * 4},
+        sdw2{dw_next, (shared ? 1 : T) * K * 4}, sdg{dgamma_next, int64_t(d) * 4},
+        sws{workspace, hc_backward_workspace(T, n, d)};
+    // dH == dH_out is allowed (every element is read before the same thread
+    // writes it); any other overlap of an output is an error
+    if (dH != dH_out && overlap(sdH, sO)) return HC_ERR_ALIAS;
+    for (const Span& i : {su, sH, sF, sW, sW2, sg})
+        if (overlap(sdH, i)) return HC_ERR_ALIAS;
+    const Span outs[] = {sdF, sdw, sdw2, sdg, sws};
+    for (const Span& o : outs) {
+        for (const Span& i : {sO, su, sH, sF, sW, sW2, sg, sdH})
+            if (overlap(o, i)) return HC_ERR_ALIAS;
+    }
+    for (int a = 0; a < 5; ++a)
+        for (int b = a + 1; b < 5; ++b)
+            if (overlap(outs[a], outs[b])) return HC_ERR_ALIAS;
+    return from_hip(hc::launch_post_pre_mix_backward(dH_out, du_next, H, F, w, w_next, w_stride,
+                                                     gamma_next, eps, dH, dF, dw, dw_next,
+                                                     dgamma_next, workspace, T, n, d, dt,
+                                                     static_cast<hipStream_t>(stream)));
 }
 
 int64_t hc_weights_backward_workspace(int64_t T, int32_t n, int32_t d, int32_t sinkhorn_iters) {

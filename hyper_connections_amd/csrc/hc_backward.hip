@@ -92,10 +92,12 @@ __device__ __forceinline__ void halve(const float* in, float* out, bool upper) {
 // sums meet in LDS (24 floats per wave in `red`) and are added in wave order.
 // About 80 instructions for 20 values, against 7 or 8 per value for one
 // reduction per value.
+// wave_sums_to is the part inside one wave: the wave's sum of value m goes to
+// out[m] (m < M), stored by the lane that holds it.
 template <int M>
-__device__ __forceinline__ float block_sum_to(const float (&v)[M], float* red) {
-    static_assert(M <= 24, "block_sum_to takes at most 24 values");
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+__device__ __forceinline__ void wave_sums_to(const float (&v)[M], float* out) {
+    static_assert(M <= 24, "wave_sums_to takes at most 24 values");
+    const int lane = threadIdx.x & 63;
     const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
     constexpr int LA = (M + 1) / 2, LB = (LA + 1) / 2, LC = (LB + 1) / 2;
     float a[LA], b[LB], c[LC];
@@ -113,8 +115,15 @@ __device__ __forceinline__ float block_sum_to(const float (&v)[M], float* red) {
     if (lane < 16 && !(lane & 1)) {
         const int g = (b1 ? 4 : 0) + (b2 ? 2 : 0) + (b3 ? 1 : 0);
 #pragma unroll
-        for (int k = 0; k < LC; ++k) red[wave * 24 + 8 * k + g] = c[k];
+        for (int k = 0; k < LC; ++k)
+            if (8 * k + g < M) out[8 * k + g] = c[k];
     }
+}
+
+template <int M>
+__device__ __forceinline__ float block_sum_to(const float (&v)[M], float* red) {
+    const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    wave_sums_to<M>(v, red + wave * 24);
     __syncthreads();
     float s = 0.0f;
     if ((int)threadIdx.x < M) {
@@ -323,7 +332,6 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
     const uint8_t* dHo, uint8_t* dH, float* __restrict__ dw, float* __restrict__ dg_part,
     float* __restrict__ da_part, int64_t T, int d, int group) {
     constexpr int V = Store<S>::kElems, E = Word<S>::kElems;
-    constexpr int K = 2 * N + N * N;
     __shared__ float red[16 * (N > 2 ? N : 2)];   // block_sum_vec<2> and <N>
     const int B = blockDim.x;
     const int nvec = d / V;
@@ -516,6 +524,250 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
     }
 }
 
+// ------------------------------------------------ layer boundary backward
+
+// The gradient of hc_post_pre_mix (one layer's write-back and the next
+// layer's read-mix + RMSNorm) in one pass.  Per token, with beta and A from
+// w and alpha from wn:
+//   H' = A H + beta F, recomputed in the forward's order and rounded as it
+//     is stored, so bitwise the H' that the forward wrote (not read back);
+//   x = sum_i alpha_i H'_i, r and dx as in pre_bwd_kernel;
+//   G_i = dHo_i + alpha_i dx, the whole gradient at H' (the next layer's
+//     write-back sends dHo), in fp32 registers only;
+//   dH_j = sum_i A[i][j] G_i and dF = sum_i beta_i G_i, the rows written;
+//   dalpha_i = dx . H'_i, dbeta_i = G_i . F, dA[i][j] = G_i . H_j and
+//   dgamma = sum_t du x r.
+// Rows per token: H, F, dHo and du in, dH and dF out (3n + 3), against
+// 5n + 3 for post_bwd_kernel without dH followed by pre_bwd_kernel with the
+// fold, which read H twice and read dHo twice.
+//
+// Record partials come in record order [dalpha | dbeta | dA] (K values).
+// PER_TOKEN: per token and wave, rpart[t][wave][K], added in wave order by
+// boundary_records_kernel (no block reduction per token).  Otherwise summed
+// over the block's tokens in registers: dalpha to rpart[blk][n], the rest to
+// rpart[nb * n + blk * M] (nb blocks, M = n + n^2).
+template <int N, typename S, int VPT, bool PER_TOKEN>
+__global__ __launch_bounds__(1024) void post_pre_bwd_kernel(
+    const uint8_t* __restrict__ dHo, const uint8_t* __restrict__ du, const uint8_t* __restrict__ H,
+    const uint8_t* __restrict__ F, const float* __restrict__ w, const float* __restrict__ wn,
+    int64_t w_stride, const float* __restrict__ gamma, float eps, uint8_t* __restrict__ dH,
+    uint8_t* __restrict__ dF, float* __restrict__ dg_part, float* __restrict__ rpart, int64_t T,
+    int d, int group) {
+    constexpr int V = Store<S>::kElems, E = Word<S>::kElems;
+    constexpr int K = 2 * N + N * N;
+    constexpr int M = N + N * N;
+    __shared__ float red[16 * 24];          // block_sum_vec<2> and block_sum_to<K>
+    // With one vector per thread the rounded H' waits for the second phase in
+    // dynamic LDS, [stream][word][thread] (16 n bytes per thread; each thread
+    // reads back only what it wrote, so no barrier): at n = 4 that keeps the
+    // kernel within 128 VGPRs without spills.  With more vectors per thread
+    // it stays in registers.
+    constexpr bool kLds = VPT == 1;
+    extern __shared__ uint32_t hol[];
+    const int B = blockDim.x;
+    const int nvec = d / V;
+    const int64_t row_bytes = (int64_t)d * Store<S>::kBytes;
+    const int wave = threadIdx.x >> 6, nw = B >> 6;
+
+    // tokens blk, blk + nb, ... as in the other gradient kernels
+    const int64_t nb = (T + group - 1) / group;
+    for (int64_t blk = blockIdx.x; blk < nb; blk += gridDim.x) {
+        float dgp[VPT][V];
+#pragma unroll
+        for (int j = 0; j < VPT; ++j)
+#pragma unroll
+            for (int e = 0; e < V; ++e) dgp[j][e] = 0.0f;
+        float acc[K];
+#pragma unroll
+        for (int m = 0; m < K; ++m) acc[m] = 0.0f;
+
+        for (int64_t t = blk; t < T; t += nb) {
+            const float* rec = w + t * w_stride;
+            const float* recn = wn + t * w_stride;
+            float alpha[N], beta[N], A[N][N];
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                alpha[i] = recn[i];
+                beta[i] = rec[N + i];
+            }
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+#pragma unroll
+                for (int k = 0; k < N; ++k) A[i][k] = rec[2 * N + i * N + k];
+            const int64_t r0 = t * N * row_bytes;
+            // every load of the token first
+            uint4 rh[N][VPT], rg[N][VPT], rf[VPT], ru[VPT];
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+                const int v = threadIdx.x + j * B;
+                const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < N; ++i)
+                    rh[i][j] = v < nvec ? ld16_stream(H + r0 + i * row_bytes + v * 16) : z;
+                rf[j] = v < nvec ? ld16_stream(F + t * row_bytes + v * 16) : z;
+#pragma unroll
+                for (int i = 0; i < N; ++i)
+                    rg[i][j] = v < nvec ? ld16_stream(dHo + r0 + i * row_bytes + v * 16) : z;
+                ru[j] = v < nvec ? ld16_stream(du + t * row_bytes + v * 16) : z;
+            }
+            // H' as the forward stores it, and the RMSNorm gradient's two sums
+            uint4 ro[N][VPT];
+            float s2[2] = {0.0f, 0.0f};
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+                const int v = threadIdx.x + j * B;
+                uint32_t o[N][4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float h[N][E], f[E];
+#pragma unroll
+                    for (int i = 0; i < N; ++i) unpack_word<S>(word(rh[i][j], q), h[i]);
+                    unpack_word<S>(word(rf[j], q), f);
+#pragma unroll
+                    for (int i = 0; i < N; ++i) {
+                        float y[E];
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            float sum = A[i][0] * h[0][e];
+#pragma unroll
+                            for (int k = 1; k < N; ++k) sum = fmaf(A[i][k], h[k][e], sum);
+                            y[e] = fmaf(beta[i], f[e], sum);
+                        }
+                        o[i][q] = pack_word<S>(y);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < N; ++i) {
+                    if constexpr (kLds) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) hol[(i * 4 + q) * B + threadIdx.x] = o[i][q];
+                    } else {
+                        ro[i][j] = make_uint4(o[i][0], o[i][1], o[i][2], o[i][3]);
+                    }
+                }
+                if (v < nvec) {
+                    float g[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if ((q * E) % 4 == 0) unpack<f32_t>(ld16(gamma + v * V + q * E), g);
+                        float x[E], yr[E], ug[E];
+                        unpack_word<S>(o[0][q], yr);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) x[e] = alpha[0] * yr[e];
+#pragma unroll
+                        for (int i = 1; i < N; ++i) {
+                            unpack_word<S>(o[i][q], yr);
+#pragma unroll
+                            for (int e = 0; e < E; ++e) x[e] = fmaf(alpha[i], yr[e], x[e]);
+                        }
+                        unpack_word<S>(word(ru[j], q), ug);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            s2[0] = fmaf(x[e], x[e], s2[0]);
+                            s2[1] = fmaf(g[(q * E) % 4 + e] * ug[e], x[e], s2[1]);
+                        }
+                    }
+                }
+            }
+            block_sum_vec<2>(s2, red);
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+#pragma unroll
+                for (int i = 0; i < N; ++i) {
+                    opaque(rh[i][j]);
+                    opaque(rg[i][j]);
+                    if constexpr (!kLds) opaque(ro[i][j]);
+                }
+                opaque(rf[j]);
+                opaque(ru[j]);
+            }
+            const float r = 1.0f / sqrtf(s2[0] / (float)d + eps);
+            const float c2 = r * r * s2[1] / (float)d;
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+                const int v = threadIdx.x + j * B;
+                if (v < nvec) {
+                    float g[4];
+                    uint32_t oh[N][4], of[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if ((q * E) % 4 == 0) unpack<f32_t>(ld16(gamma + v * V + q * E), g);
+                        float h[N][E], ho[N][E], gr[N][E], f[E], ug[E];
+#pragma unroll
+                        for (int i = 0; i < N; ++i) {
+                            unpack_word<S>(word(rh[i][j], q), h[i]);
+                            unpack_word<S>(kLds ? hol[(i * 4 + q) * B + threadIdx.x] : word(ro[i][j], q), ho[i]);
+                            unpack_word<S>(word(rg[i][j], q), gr[i]);
+                        }
+                        unpack_word<S>(word(rf[j], q), f);
+                        unpack_word<S>(word(ru[j], q), ug);
+                        float o[N][E], ofe[E];
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            float x = alpha[0] * ho[0][e];
+#pragma unroll
+                            for (int i = 1; i < N; ++i) x = fmaf(alpha[i], ho[i][e], x);
+                            const float dx = r * (g[(q * E) % 4 + e] * ug[e] - x * c2);
+                            dgp[j][q * E + e] = fmaf(ug[e], x * r, dgp[j][q * E + e]);
+                            float G[N];
+#pragma unroll
+                            for (int i = 0; i < N; ++i) {
+                                acc[i] = fmaf(dx, ho[i][e], acc[i]);
+                                G[i] = fmaf(alpha[i], dx, gr[i][e]);
+                                acc[N + i] = fmaf(G[i], f[e], acc[N + i]);
+#pragma unroll
+                                for (int k = 0; k < N; ++k)
+                                    acc[2 * N + i * N + k] = fmaf(G[i], h[k][e], acc[2 * N + i * N + k]);
+                            }
+#pragma unroll
+                            for (int k = 0; k < N; ++k) {
+                                float sum = A[0][k] * G[0];
+#pragma unroll
+                                for (int i = 1; i < N; ++i) sum = fmaf(A[i][k], G[i], sum);
+                                o[k][e] = sum;
+                            }
+                            float sum = beta[0] * G[0];
+#pragma unroll
+                            for (int i = 1; i < N; ++i) sum = fmaf(beta[i], G[i], sum);
+                            ofe[e] = sum;
+                        }
+#pragma unroll
+                        for (int k = 0; k < N; ++k) oh[k][q] = pack_word<S>(o[k]);
+                        of[q] = pack_word<S>(ofe);
+                    }
+#pragma unroll
+                    for (int k = 0; k < N; ++k)
+                        st16_stream(dH + r0 + k * row_bytes + v * 16,
+                                    make_uint4(oh[k][0], oh[k][1], oh[k][2], oh[k][3]));
+                    st16_stream(dF + t * row_bytes + v * 16, make_uint4(of[0], of[1], of[2], of[3]));
+                }
+            }
+            if constexpr (PER_TOKEN) {
+                wave_sums_to<K>(acc, rpart + (t * nw + wave) * K);
+#pragma unroll
+                for (int m = 0; m < K; ++m) acc[m] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int v = threadIdx.x + j * B;
+            if (v < nvec) {
+#pragma unroll
+                for (int q = 0; q < V / 4; ++q)
+                    st16(dg_part + blk * (int64_t)d + v * V + 4 * q,
+                         make_uint4(__float_as_uint(dgp[j][4 * q]), __float_as_uint(dgp[j][4 * q + 1]),
+                                    __float_as_uint(dgp[j][4 * q + 2]), __float_as_uint(dgp[j][4 * q + 3])));
+            }
+        }
+        if constexpr (!PER_TOKEN) {
+            const float sum = block_sum_to<K>(acc, red);
+            const int m = threadIdx.x;
+            if (m < N) rpart[blk * N + m] = sum;
+            else if (m < K) rpart[nb * N + blk * M + (m - N)] = sum;
+        }
+    }
+}
+
 // One level of a column sum: out[s][c] = sum of in[r][c] over the rows r of
 // segment s (kSumRows rows each), in row order; a thread per column.  The
 // final level of a sum may also clear `zero` (nzero floats: record entries
@@ -529,10 +781,10 @@ struct SumLevel {
     int nzero;
 };
 
-// Up to two independent sums per launch (blockIdx.z picks one), so that the
+// Up to three independent sums per launch (blockIdx.z picks one), so that the
 // short sums of a backward call share launches.
-__global__ __launch_bounds__(256) void sum_rows_kernel(SumLevel a, SumLevel b) {
-    const SumLevel& j = blockIdx.z == 0 ? a : b;
+__global__ __launch_bounds__(256) void sum_rows_kernel(SumLevel a, SumLevel b, SumLevel c) {
+    const SumLevel& j = blockIdx.z == 0 ? a : blockIdx.z == 1 ? b : c;
     if (blockIdx.x == 0 && blockIdx.y == 0)
         for (int i = threadIdx.x; i < j.nzero; i += 256) j.zero[i] = 0.0f;
     const int64_t r0 = (int64_t)blockIdx.y * kSumRows;
@@ -589,24 +841,49 @@ __global__ __launch_bounds__(256) void token_records_kernel(const float* __restr
     }
 }
 
+// The layer boundary's per-token records from its per-wave partials
+// part[t][wave][K] (added in wave order): dw[t] = [0 | dbeta | dA] for the
+// write-back's records, dwn[t] = [dalpha | 0 | 0] for the read-mix's.
+__global__ __launch_bounds__(256) void boundary_records_kernel(const float* __restrict__ part,
+                                                               int nw, int n, int K, int64_t T,
+                                                               float* __restrict__ dw,
+                                                               float* __restrict__ dwn) {
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < T * K;
+         e += (int64_t)gridDim.x * 256) {
+        const int64_t t = e / K;
+        const int c = (int)(e % K);
+        const float* p = part + t * nw * K + c;
+        float s = p[0];
+        for (int w = 1; w < nw; ++w) s += p[w * K];
+        dw[e] = c < n ? 0.0f : s;
+        dwn[e] = c < n ? s : 0.0f;
+    }
+}
+
 // ----------------------------------------------------------------- dispatch
 
 inline dim3 grid_of(int64_t blocks) { return dim3((unsigned)(blocks < kMaxGridB ? blocks : kMaxGridB)); }
 
 }  // namespace
 
-// Deterministic column sums, up to two at once: every level folds kSumRows
+// Deterministic column sums, up to three at once: every level folds kSumRows
 // rows into one (rows -> ceil(rows / 64) rows in tmp -> ... -> out), so the
 // order depends only on the shapes.  Each job's tmp holds
 // sum_rows_tmp_floats(rows, cols) floats; the jobs' levels share launches.
-hipError_t launch_sum_rows2(const SumJob* jobs, int njobs, hipStream_t s) {
-    SumJob j[2] = {jobs[0], njobs > 1 ? jobs[1] : jobs[0]};
-    bool done[2] = {false, njobs < 2};
-    while (!(done[0] && done[1])) {
-        SumLevel lv[2];
-        int idx[2], nz = 0;
+hipError_t launch_sum_rows(const SumJob* jobs, int njobs, hipStream_t s) {
+    constexpr int kJobs = 3;
+    if (njobs < 1 || njobs > kJobs) return hipErrorInvalidValue;
+    SumJob j[kJobs];
+    bool done[kJobs];
+    for (int k = 0; k < kJobs; ++k) {
+        j[k] = jobs[k < njobs ? k : 0];
+        done[k] = k >= njobs;
+    }
+    while (!(done[0] && done[1] && done[2])) {
+        SumLevel lv[kJobs];
+        int idx[kJobs], nz = 0;
         unsigned gx = 1, gy = 1;
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < kJobs; ++k) {
             if (done[k]) continue;
             const int64_t segs = (j[k].rows + kSumRows - 1) / kSumRows;
             const bool last = segs <= 1;
@@ -618,7 +895,7 @@ hipError_t launch_sum_rows2(const SumJob* jobs, int njobs, hipStream_t s) {
             gy = y > gy ? y : gy;
         }
         hipError_t e = launch(sum_rows_kernel, dim3(gx, gy, (unsigned)nz), dim3(256), 0, s, lv[0],
-                              nz > 1 ? lv[1] : lv[0]);
+                              nz > 1 ? lv[1] : lv[0], nz > 2 ? lv[2] : lv[0]);
         if (e != hipSuccess) return e;
         for (int q = 0; q < nz; ++q) {
             SumJob& x = j[idx[q]];
@@ -724,6 +1001,28 @@ hipError_t pre_bwd_vpt(RowCfg c, const void* du, const void* H, const float* w, 
     HC_BWD_VPT(pre_bwd_go, du, H, w, ws, gamma, eps, dH_in, dHo, dH, dw, dg_part, da_part, T, d, group,
                s)
 }
+template <int N, typename S, int VPT>
+hipError_t post_pre_bwd_go(RowCfg c, const void* dHo, const void* du, const void* H, const void* F,
+                           const float* w, const float* wn, int64_t ws, const float* gamma,
+                           float eps, void* dH, void* dF, float* dg_part, float* rpart, int64_t T,
+                           int d, int group, hipStream_t s) {
+    const dim3 grid = grid_of((T + group - 1) / group);
+    auto* k = ws != 0 ? post_pre_bwd_kernel<N, S, VPT, true> : post_pre_bwd_kernel<N, S, VPT, false>;
+    const size_t lds = VPT == 1 ? (size_t)N * 16 * c.block : 0;     // the parked H'
+    return launch(k, grid, dim3(c.block), lds, s, static_cast<const uint8_t*>(dHo),
+                  static_cast<const uint8_t*>(du), static_cast<const uint8_t*>(H),
+                  static_cast<const uint8_t*>(F), w, wn, ws, gamma, eps, static_cast<uint8_t*>(dH),
+                  static_cast<uint8_t*>(dF), dg_part, rpart, T, d, group);
+}
+
+template <int N, typename S>
+hipError_t post_pre_bwd_vpt(RowCfg c, const void* dHo, const void* du, const void* H, const void* F,
+                            const float* w, const float* wn, int64_t ws, const float* gamma,
+                            float eps, void* dH, void* dF, float* dg_part, float* rpart, int64_t T,
+                            int d, int group, hipStream_t s) {
+    HC_BWD_VPT(post_pre_bwd_go, dHo, du, H, F, w, wn, ws, gamma, eps, dH, dF, dg_part, rpart, T, d,
+               group, s)
+}
 #undef HC_BWD_VPT
 
 template <typename S, typename... A>
@@ -733,6 +1032,17 @@ hipError_t post_bwd_n(int n, A... a) {
         case 2: return post_bwd_vpt<2, S>(a...);
         case 3: return post_bwd_vpt<3, S>(a...);
         case 4: return post_bwd_vpt<4, S>(a...);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename S, typename... A>
+hipError_t post_pre_bwd_n(int n, A... a) {
+    switch (n) {
+        case 1: return post_pre_bwd_vpt<1, S>(a...);
+        case 2: return post_pre_bwd_vpt<2, S>(a...);
+        case 3: return post_pre_bwd_vpt<3, S>(a...);
+        case 4: return post_pre_bwd_vpt<4, S>(a...);
     }
     return hipErrorInvalidValue;
 }
@@ -748,11 +1058,15 @@ hipError_t pre_bwd_n(int n, A... a) {
     return hipErrorInvalidValue;
 }
 
-// Workspace layout for T tokens of width d with n streams (floats):
+// Workspace layout for T tokens of width d with n streams (floats), shared
+// by every gradient call here:
 //   [rows][d]   dgamma partials         (rows = blocks = ceil(T / group))
-//   [rows][M]   record partials         (M = n + n^2 >= the n of dalpha)
-//   tmp         second-level rows of either sum (ceil(rows / 64) * max(d, M),
-//               plus a third level, bounded by 2 * ceil(rows / 64) * max(d, M))
+//   [rr][K]     record partials         (post: M = n + n^2 per row; pre: n;
+//               the layer boundary: n and M, K = 2n + n^2 in all)
+//   tmp         the levels of the dgamma sum (sum_rows_tmp_floats(rows, d))
+//   tmp2        the levels of the record sums (sum_rows_tmp_floats(rr, K):
+//               the floats it needs grow linearly with the columns)
+//   wp          per-token, per-wave partials (T x 16 waves x K at most)
 struct BwdSpace {
     int64_t rows, prows, dg, rec, tmp, tmp2, wp, total;   // offsets and total, in floats
 };
@@ -760,16 +1074,16 @@ inline BwdSpace bwd_space(int64_t T, int n, int d) {
     BwdSpace b;
     const int64_t g = group_of(T);
     b.rows = (T + g - 1) / g;
-    const int64_t M = n + int64_t(n) * n;
+    const int64_t K = 2 * n + int64_t(n) * n;
     b.dg = 0;
     b.rec = b.rows * d;
     const int64_t pg = post_group_of(T);
     b.prows = (T + pg - 1) / pg;                          // post's partial records
     const int64_t rr = b.prows > b.rows ? b.prows : b.rows;
-    b.tmp = b.rec + rr * M;                               // the dgamma sum's levels
+    b.tmp = b.rec + rr * K;                               // the dgamma sum's levels
     b.tmp2 = b.tmp + sum_rows_tmp_floats(b.rows, d);      // the record sums' levels
-    b.wp = b.tmp2 + sum_rows_tmp_floats(rr, M);           // pre's per-wave partials, per token
-    b.total = b.wp + T * 16 * n;
+    b.wp = b.tmp2 + sum_rows_tmp_floats(rr, K);           // per-token, per-wave partials
+    b.total = b.wp + T * 16 * K;
     return b;
 }
 
@@ -800,7 +1114,7 @@ hipError_t post_backward_with(const void* dHo, const void* H, const void* F, con
     const int M = n + n * n;
     const int64_t prows = (T + post_group_of(T) - 1) / post_group_of(T);
     const SumJob job = {part, prows, M, tmp, dw + n, dw, n};
-    return launch_sum_rows2(&job, 1, s);
+    return launch_sum_rows(&job, 1, s);
 }
 
 // The allocation-free variant's scratch: one array per GPU for the life of
@@ -902,7 +1216,43 @@ hipError_t launch_pre_mix_backward(const void* du, const void* H, const float* w
     // 0 (dbeta, dA)], in the same launches
     const SumJob jobs[2] = {{dg_part, sp.rows, d, ws + sp.tmp, dgamma, nullptr, 0},
                             {da_part, sp.rows, n, ws + sp.tmp2, dw, dw + n, K - n}};
-    return launch_sum_rows2(jobs, w_stride != 0 ? 1 : 2, s);
+    return launch_sum_rows(jobs, w_stride != 0 ? 1 : 2, s);
+}
+
+hipError_t launch_post_pre_mix_backward(const void* dHo, const void* du, const void* H, const void* F,
+                                        const float* w, const float* wn, int64_t w_stride,
+                                        const float* gamma, float eps, void* dH, void* dF, float* dw,
+                                        float* dwn, float* dgamma, void* work, int64_t T, int n,
+                                        int d, int dt, hipStream_t s) {
+    const BwdSpace sp = bwd_space(T, n, d);
+    float* ws = static_cast<float*>(work);
+    const int group = (int)group_of(T);
+    float* dg_part = ws + sp.dg;
+    // record partials: per token and wave, or per workgroup
+    float* rpart = w_stride != 0 ? ws + sp.wp : ws + sp.rec;
+    const RowCfg c = row_config(d / (dt == 0 ? Store<f32_t>::kElems : Store<bf16_t>::kElems));
+    hipError_t e =
+        dt == 0 ? post_pre_bwd_n<f32_t>(n, c, dHo, du, H, F, w, wn, w_stride, gamma, eps, dH, dF,
+                                        dg_part, rpart, T, d, group, s)
+                : post_pre_bwd_n<bf16_t>(n, c, dHo, du, H, F, w, wn, w_stride, gamma, eps, dH, dF,
+                                         dg_part, rpart, T, d, group, s);
+    if (e != hipSuccess) return e;
+    const int K = 2 * n + n * n, M = n + n * n;
+    const SumJob dg_job = {dg_part, sp.rows, d, ws + sp.tmp, dgamma, nullptr, 0};
+    if (w_stride != 0) {
+        const int64_t blocks = (T * K + 255) / 256;
+        e = launch(boundary_records_kernel, grid_of(blocks), dim3(256), 0, s,
+                   static_cast<const float*>(rpart), c.block / 64, n, K, T, dw, dwn);
+        if (e != hipSuccess) return e;
+        return launch_sum_rows(&dg_job, 1, s);
+    }
+    // shared records: dwn = [sum of the dalpha partials | 0], dw = [0 | sums
+    // of the dbeta and dA partials], in the dgamma sum's launches
+    const SumJob jobs[3] = {dg_job,
+                            {rpart, sp.rows, n, ws + sp.tmp2, dwn, dwn + n, K - n},
+                            {rpart + sp.rows * n, sp.rows, M,
+                             ws + sp.tmp2 + sum_rows_tmp_floats(sp.rows, n), dw + n, dw, n}};
+    return launch_sum_rows(jobs, 3, s);
 }
 
 int64_t sum_rows_tmp_floats(int64_t rows, int64_t cols) {

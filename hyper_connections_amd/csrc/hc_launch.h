@@ -56,6 +56,11 @@ hipError_t launch_pre_mix_backward(const void* du, const void* H, const float* w
                                    const float* gamma, float eps, const void* dH_in, const void* dHo,
                                    void* dH, float* dw, float* dgamma, void* work, int64_t T, int n,
                                    int d, int dt, hipStream_t s);
+hipError_t launch_post_pre_mix_backward(const void* dHo, const void* du, const void* H, const void* F,
+                                        const float* w, const float* wn, int64_t w_stride,
+                                        const float* gamma, float eps, void* dH, void* dF, float* dw,
+                                        float* dwn, float* dgamma, void* work, int64_t T, int n,
+                                        int d, int dt, hipStream_t s);
 int64_t backward_workspace_bytes(int64_t T, int n, int d);
 // The post gradient with its scratch in the library's own per-GPU array
 // (nothing allocated): bytes it needs, and the array's size.
@@ -99,8 +104,8 @@ struct SumJob {
     float* zero;
     int nzero;
 };
-// One or two independent sums; their levels share launches.
-hipError_t launch_sum_rows2(const SumJob* jobs, int njobs, hipStream_t s);
+// One to three independent sums; their levels share launches.
+hipError_t launch_sum_rows(const SumJob* jobs, int njobs, hipStream_t s);
 int64_t weights_backward_workspace_bytes(int64_t T, int n, int d, int iters);
 int64_t sinkhorn_backward_workspace_bytes(int64_t T, int iters);
 hipError_t launch_weights_backward(const void* H, const void* W, const float* w_static, float scale,

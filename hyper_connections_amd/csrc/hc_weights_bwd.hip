@@ -825,7 +825,7 @@ hipError_t launch_weights_backward(const void* H, const void* W, const float* w_
     // coefficient workgroups' partials, in shared launches
     const SumJob jobs[2] = {{ws + sp.part, splits, K * d, ws + sp.tmp, dW, nullptr, 0},
                            {ws + sp.dl, coef_blocks(T), K, ws + sp.tmp2, dws, nullptr, 0}};
-    return launch_sum_rows2(jobs, 2, s);
+    return launch_sum_rows(jobs, 2, s);
 }
 
 }  // namespace hc

@@ -52,6 +52,8 @@ _SIGS = {
                              _i32, _vp],
     "hc_pre_mix_backward": [_vp, _vp, _fp, _i64, _fp, _f32, _vp, _vp, _vp, _fp, _fp, _vp, _i64,
                             _i64, _i32, _i32, _i32, _vp],
+    "hc_post_pre_mix_backward": [_vp, _vp, _vp, _vp, _fp, _i64, _fp, _i64, _fp, _f32, _vp, _vp,
+                                 _fp, _fp, _fp, _vp, _i64, _i64, _i32, _i32, _i32, _vp],
     "hc_sum_records": [_fp, _i64, _i32, _fp, _vp],
     "hc_weights_save": [_vp, _vp, _fp, _f32, _f32, _i32, _fp, _fp, _i64, _i64, _i32, _i32, _i32,
                         _vp],
@@ -519,6 +521,47 @@ def pre_mix_backward(du, H, w, gamma, eps: float = 1e-6, dH_in=None, out=None, d
           dH_out.data_ptr() if dH_out is not None else None, dH.data_ptr(),
           dw.data_ptr(), dg.data_ptr(), wk.data_ptr(), wkb, T, n, d, _dt(H), _stream(stream))
     return dH, dw, dg
+
+
+@_on_launch_stream
+def post_pre_mix_backward(dH_out, du_next, H, F, w, w_next, gamma_next, eps: float = 1e-6,
+                          out=None, dF=None, dw=None, dw_next=None, dgamma_next=None,
+                          workspace=None, stream=None):
+    """Gradients of post_pre_mix (one layer boundary): returns (dH, dF, dw,
+    dw_next, dgamma_next).  dH_out is the gradient at H' from the next layer's
+    write-back (not from the read-mix, whose share is formed here from
+    du_next); H' is recomputed from H, F and w.  dw ([0 | dbeta | dA]) and
+    dw_next ([dalpha | 0 | 0]) have the shape of w and w_next, which must be
+    both shared or both per token.  ``out=dH_out`` writes dH in place."""
+    T, n, d, K = _H(H)
+    ws = _record(w, T, K)
+    ws2 = _record(w_next, T, K, "w_next")
+    if ws != ws2:
+        raise ValueError("w and w_next must be both shared (K,) or both per token (T, K)")
+    for name, x, shape in (("dH_out", dH_out, tuple(H.shape)), ("du_next", du_next, (T, d)),
+                           ("F", F, (T, d))):
+        _dev(x, name)
+        if x.dtype != H.dtype or tuple(x.shape) != shape:
+            raise ValueError(f"{name} must match H's dtype and have shape {shape}")
+    _dev(gamma_next, "gamma_next")
+    if gamma_next.dtype != torch.float32 or tuple(gamma_next.shape) != (d,):
+        raise ValueError("gamma_next must be float32 of shape (d,)")
+    dH = torch.empty_like(H) if out is None else _dev(out, "out")
+    f = torch.empty((T, d), dtype=H.dtype, device=H.device) if dF is None else _dev(dF, "dF")
+    if dH.dtype != H.dtype or dH.shape != H.shape or f.dtype != H.dtype or tuple(f.shape) != (T, d):
+        raise ValueError("out / dF do not match H")
+    dw = _grad_record(dw, T, K, ws, H.device)
+    dwn = _grad_record(dw_next, T, K, ws, H.device, "dw_next")
+    dg = (torch.empty(d, dtype=torch.float32, device=H.device) if dgamma_next is None
+          else _dev(dgamma_next, "dgamma_next"))
+    if dg.dtype != torch.float32 or tuple(dg.shape) != (d,):
+        raise ValueError(f"dgamma_next must be float32 of shape ({d},)")
+    wk, wkb = _workspace(workspace, T, n, d, H.device)
+    _call("hc_post_pre_mix_backward", dH_out.data_ptr(), du_next.data_ptr(), H.data_ptr(),
+          F.data_ptr(), w.data_ptr(), ws, w_next.data_ptr(), ws2, gamma_next.data_ptr(),
+          float(eps), dH.data_ptr(), f.data_ptr(), dw.data_ptr(), dwn.data_ptr(), dg.data_ptr(),
+          wk.data_ptr(), wkb, T, n, d, _dt(H), _stream(stream))
+    return dH, f, dw, dwn, dg
 
 
 @_on_launch_stream

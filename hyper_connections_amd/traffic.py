@@ -102,6 +102,14 @@ def pre_bwd_bytes(n: int, d: int, s: int, accumulate: bool = True) -> int:
     return (2 * n + 1 + (n if accumulate else 0)) * d * s + record_bytes(n)
 
 
+def post_pre_bwd_bytes(n: int, d: int, s: int) -> int:
+    """Gradient of one layer boundary (write-back and next read-mix) in one
+    pass: read dH', du, H and F, write dH and dF ((3n + 3) d s; H' is
+    recomputed, not read), and the two gradient records (as in the separate
+    calls, whose rows total (5n + 3) d s)."""
+    return (3 * n + 3) * d * s + 2 * record_bytes(n)
+
+
 def weights_bwd_bytes(n: int, d: int, s: int) -> int:
     """Gradient of the per-token weights: read H, read the incoming dH and
     write dH once each, plus two gradient records read (from pre and post).

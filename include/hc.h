@@ -294,6 +294,44 @@ hc_status hc_pre_mix_backward(const void* du, const void* H, const float* w, int
                               int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
                               void* stream);
 
+/* Gradients of hc_post_pre_mix (the write-back of one layer and the read-mix
+ * + RMSNorm of the next) in one pass over the streams: the backward of one
+ * layer boundary.  [GLOSS] definition (the mixing before and after every
+ * block is learned, so its weights take gradients); [EXPL] "What four
+ * streams cost per token" (the n-fold state crosses every boundary, and here
+ * it crosses once: H, F, dH_out and du_next in, dH and dF out).
+ * With H' = hc_post_mix(H, F, w) recomputed bitwise as the forward stored it
+ * (H' is not an argument) and x, r, dx the read-mix's (hc_pre_mix_backward,
+ * with alpha from w_next and gamma_next):
+ *   G_i = dH_out_i + alpha_i dx      the whole gradient at H' (fp32, not stored)
+ *   dH_j = sum_i A[i][j] G_i         dF = sum_i beta_i G_i
+ *   dw      = [0 | dbeta | dA],      dbeta_i = G_i . F,  dA[i][j] = G_i . H_j
+ *   dw_next = [dalpha | 0 | 0],      dalpha_i = dx . H'_i
+ *   dgamma_next = sum_t du_next x r
+ * i.e. hc_post_mix_backward(G, H, F, w) and hc_pre_mix_backward(du_next, H',
+ * w_next) with G formed in registers.  dH_out is the gradient at H' from
+ * everything after the call except the read-mix: in a stack of layers, the
+ * dH that the next boundary's call (or the last write-back's
+ * hc_post_mix_backward) returned.
+ *   dH_out [T][n][d] dt; du_next [T][d] dt; H [T][n][d] dt; F [T][d] dt
+ *   w, w_stride, w_next, w_next_stride as in hc_post_pre_mix, both shared
+ *     (stride 0) or both per token (stride K); unequal strides: HC_ERR_ARG
+ *   gamma_next [d] fp32, eps > 0: the read-mix's RMSNorm
+ *   dH [T][n][d] dt (dH == dH_out allowed), dF [T][d] dt
+ *   dw, dw_next fp32 in the shape of w and w_next, dgamma_next [d] fp32,
+ *     summed over tokens in a fixed order (deterministic)
+ *   workspace >= hc_backward_workspace(T, n, d) bytes, 16-byte aligned.
+ * Alignment as the other gradient calls; any other overlap of an output with
+ * an input, another output or the workspace is HC_ERR_ALIAS; fp32 and bf16
+ * only (HC_ERR_DTYPE for HC_FP8). */
+hc_status hc_post_pre_mix_backward(const void* dH_out, const void* du_next, const void* H,
+                                   const void* F, const float* w, int64_t w_stride,
+                                   const float* w_next, int64_t w_next_stride,
+                                   const float* gamma_next, float eps, void* dH, void* dF, float* dw,
+                                   float* dw_next, float* dgamma_next, void* workspace,
+                                   int64_t workspace_bytes, int64_t T, int32_t n, int32_t d,
+                                   hc_dtype dt, void* stream);
+
 /* Bytes of device workspace hc_weights_backward needs (0 for T <= 0 or
  * arguments out of range).  It holds the per-stream projections, per-token
  * coefficients, Sinkhorn intermediates (16 floats per token per iteration)

@@ -17,7 +17,7 @@ OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, ARG = 0, 1, 2, 3, 4, 5, 6
 BF16, F32, FP8 = hc.HC_BF16, hc.HC_F32, hc.HC_FP8
 
 # fake, never dereferenced device addresses (16-byte aligned, far apart)
-P = [0x10000000 * (i + 1) for i in range(10)]
+P = [0x10000000 * (i + 1) for i in range(14)]
 MiB = 1 << 20
 
 
@@ -51,7 +51,7 @@ def test_status_strings(L):
         s = hc.status_str(code)
         assert s.startswith("HC_")
     assert hc.status_str(99).startswith("HC_ERR_UNKNOWN")
-    assert hc.abi_version() == 5
+    assert hc.abi_version() == 6
 
 
 def pre(L, H=P[0], w=P[1], ws=0, g=P[2], eps=1e-6, u=P[3], T=16, n=4, d=4096, dt=BF16):
@@ -263,6 +263,39 @@ def test_binding_rejects_host_tensors():
     H = torch.zeros(2, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         hc.pre_mix(H, torch.zeros(24), torch.ones(64))
+
+
+def test_post_pre_mix_backward_validation(L):
+    """The layer boundary's gradient: dtype, shapes, strides (both shared or
+    both per token), workspace size, NULLs, alignment, and overlaps (dH may
+    be dH_out itself, nothing else may overlap).  Nothing is launched."""
+    need = L.hc_backward_workspace(8, 4, 4096)
+
+    def f(**k):
+        return L.hc_post_pre_mix_backward(
+            k.get("go", P[0]), k.get("du", P[1]), k.get("H", P[2]), k.get("F", P[3]),
+            k.get("w", P[4]), k.get("ws", 0), k.get("wn", P[5]), k.get("wns", 0), k.get("g", P[6]),
+            k.get("eps", 1e-6), k.get("dH", P[7]), k.get("dF", P[8]), k.get("dw", P[9]),
+            k.get("dwn", P[10]), k.get("dg", P[11]), k.get("wk", P[12]), k.get("wkb", need),
+            k.get("T", 8), k.get("n", 4), k.get("d", 4096), k.get("dt", BF16), None)
+    assert f(T=0) == OK and f(T=0, go=None, dH=None) == OK
+    assert f(dt=FP8) == DTYPE and f(dt=FP8, T=0) == DTYPE and f(dt=5) == DTYPE
+    assert f(n=5) == SHAPE and f(d=4100) == SHAPE and f(ws=3) == SHAPE and f(wns=23) == SHAPE
+    # equal per-token strides pass that check (and stop at the next one here)
+    assert f(ws=24, wns=0) == ARG and f(ws=0, wns=24) == ARG and f(ws=24, wns=24, dg=None) == NULL
+    assert f(eps=0.0) == ARG and f(T=-2) == ARG and f(wkb=need - 1) == ARG
+    for name in ("go", "du", "H", "F", "w", "wn", "g", "dH", "dF", "dw", "dwn", "dg", "wk"):
+        assert f(**{name: None}) == NULL, name
+    for name in ("go", "du", "H", "F", "g", "dH", "dF", "wk"):
+        assert f(**{name: P[13] + 8}) == ALIGN, name
+    for name in ("w", "wn", "dw", "dwn", "dg"):
+        assert f(**{name: P[13] + 2}) == ALIGN, name
+    # (dH == dH_out, in place, is allowed: the GPU tests run it) a partial
+    # overlap with dH_out is not
+    assert f(dH=P[0] + 16) == ALIAS
+    assert f(dH=P[2]) == ALIAS and f(dH=P[1]) == ALIAS and f(dF=P[3]) == ALIAS
+    assert f(dF=P[0] + 64) == ALIAS and f(dw=P[5]) == ALIAS and f(dwn=P[9]) == ALIAS
+    assert f(dg=P[6]) == ALIAS and f(wk=P[7]) == ALIAS and f(dF=P[7] + 16) == ALIAS
 
 
 def test_weights_backward_validation(L):

@@ -1,0 +1,311 @@
+"""GPU parity of the layer boundary's gradient (hc_post_pre_mix_backward: the
+write-back of one layer and the read-mix + RMSNorm of the next in one pass)
+against the oracle, through the C ABI.
+
+The expected values chain the oracle's own gradients: H' = post_mix(H, F, w)
+stored in the storage type, then pre_mix_backward(du, H', w_next) with the
+gradient from the next write-back added (G, the whole gradient at H', never
+rounded), then post_mix_backward(G, H, F, w).  Tolerances as the other
+gradient tests: dH and dF one rounding (storage tolerance, one ulp); records
+1e-4 of their RMS; dalpha against its Cauchy-Schwarz bound; dgamma 1e-4."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import check, dev, host, need_gpu
+from hyper_connections_amd import hc
+from hyper_connections_amd.workloads import f32_to_bf16_bits, identity_record, make_inputs, workload
+from test_gpu_backward import SHAPES, dalpha_check, grad_check, storage
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def boundary_case(rng, dt, T, n, d, per_token):
+    K = 2 * n + n * n
+    H = storage(rng.standard_normal((T, n, d)).astype(np.float32), dt)
+    F = storage(rng.standard_normal((T, d)).astype(np.float32), dt)
+    G = storage(rng.standard_normal((T, n, d)).astype(np.float32), dt)
+    du = storage(rng.standard_normal((T, d)).astype(np.float32), dt)
+    shape = (T, K) if per_token else (K,)
+    w = (np.broadcast_to(identity_record(n), shape) + 0.3 * rng.standard_normal(shape)).astype(np.float32)
+    wn = (np.broadcast_to(identity_record(n), shape) + 0.3 * rng.standard_normal(shape)).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    H, F = unambiguous(H, F, w)
+    return H, F, G, du, w, wn, g
+
+
+def _midpoint_risk(H, F, w, n):
+    """Where the exact H' = post_mix(H, F, w) lies within the error of an fp32
+    evaluation of its n + 1 terms ((n + 2) 2^-24 of the sum of their
+    magnitudes) of a bf16 rounding midpoint (the oracle on H, F, w)."""
+    Hp = oracle.post_mix(H, F, w)
+    size = oracle.post_mix(H & 0x7FFF, F & 0x7FFF, np.abs(w))
+    r = oracle.widen(oracle.round_bf16(Hp))
+    a = np.abs(Hp)
+    step = np.ldexp(1.0, np.frexp(a)[1] - 8)     # the bf16 step at |H'|
+    return (step / 2 - np.abs(Hp - r) <= (n + 2) * 2.0 ** -24 * size) & (a > 0)
+
+
+def unambiguous(H, F, w, chunk=2048, move_h=True):
+    """The inputs with F (then H) moved by one bf16 step wherever the exact
+    H' lies so close to a bf16 rounding midpoint that the forward's fp32
+    evaluation may round it the other way.  Elsewhere the H' the forward
+    stores is the oracle's rounded H', so the expected gradients are those
+    of the H' the kernels recompute.  bf16 only (an fp32 store differs by
+    fp32 ulps, far below every gradient tolerance).  move_h=False moves F
+    only."""
+    if H.dtype != np.uint16:
+        return H, F
+    H, F = H.copy(), F.copy()
+    T, n, d = H.shape
+    w64 = np.asarray(w, np.float64)
+    for t0 in range(0, T, chunk):
+        sl = slice(t0, t0 + chunk)
+        bad = _midpoint_risk(H[sl], F[sl], w64[sl] if w64.ndim == 2 else w64, n)
+        t, i, k = np.nonzero(bad)
+        t = t + t0
+        for it in range(16):
+            if t.size == 0:
+                break
+            if it % 2 == 0 or not move_h:
+                F[t, k] += 1
+            else:
+                H[t, (i + it // 2) % n, k] += 1
+            # recheck the moved columns only: token t, column k, every stream
+            tk = np.unique(np.stack([t, k], axis=1), axis=0)
+            t, k = tk[:, 0], tk[:, 1]
+            wt = w64[t] if w64.ndim == 2 else w64
+            sub = _midpoint_risk(np.ascontiguousarray(H[t, :, k][:, :, None]),
+                                 np.ascontiguousarray(F[t, k][:, None]), wt, n)
+            m, i, _ = np.nonzero(sub)
+            t, k = t[m], k[m]
+        else:
+            raise AssertionError("could not move the inputs off the rounding midpoints")
+    return H, F
+
+
+def oracle_boundary(G, du, H, F, w, wn, g, eps):
+    """The oracle's gradients of one boundary: (dH, dF, dw per token,
+    dw_next per token, dgamma, H' as stored)."""
+    w64, wn64 = w.astype(np.float64), wn.astype(np.float64)
+    Hp = oracle.post_mix(H, F, w64)
+    Hs = oracle.round_bf16(Hp) if H.dtype == np.uint16 else oracle.round_f32(Hp)
+    Gt, rdwn, rdg = oracle.pre_mix_backward(du, Hs, wn64, g, eps, dH_in=oracle.widen(G))
+    rdH, rdF, rdw = oracle.post_mix_backward(Gt, oracle.widen(H), oracle.widen(F), w64)
+    return rdH, rdF, rdw, rdwn, rdg, Hs
+
+
+def compare(got, ref, du, Hs, wn, g, eps, n, what):
+    dH, dF, dw, dwn, dg = (host(x) for x in got)
+    rdH, rdF, rdw, rdwn, rdg = ref
+    K = 2 * n + n * n
+    check(dH, rdH, f"{what} dH")
+    check(dF, rdF, f"{what} dF")
+    shared = dw.ndim == 1
+    if shared:
+        rdw, rdwn = rdw.sum(axis=0), rdwn.sum(axis=0)
+    dw2, rdw2 = dw.reshape(-1, K), rdw.reshape(-1, K)
+    assert np.all(dw2[:, :n] == 0), f"{what}: dw's dalpha slots must be 0"
+    grad_check(dw2[:, n:], rdw2[:, n:], f"{what} dbeta, dA")
+    dalpha_check(dwn, rdwn, du, Hs, wn, g, eps, f"{what} dalpha")
+    assert np.all(dwn.reshape(-1, K)[:, n:] == 0), f"{what}: dw_next's dbeta, dA slots must be 0"
+    grad_check(dg[None, :], rdg[None, :], f"{what} dgamma")
+
+
+@pytest.mark.parametrize("dt,d", SHAPES + [("bf16", 8192)])
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("per_token", [False, True])
+def test_boundary_backward_parity(dt, d, n, per_token):
+    """Every launch shape (1..4 vectors per thread, ragged rows; d = 8192 bf16
+    is the largest workgroup with one vector per thread, whose H' takes 16n KiB
+    of LDS), n = 1..4, shared and per-token records; T = 19 spans several
+    dgamma groups with a partial last one."""
+    rng = np.random.default_rng(d * 7 + n * 3 + per_token)
+    T = 19
+    H, F, G, du, w, wn, g = boundary_case(rng, dt, T, n, d, per_token)
+    got = hc.post_pre_mix_backward(dev(G), dev(du), dev(H), dev(F), dev(w), dev(wn), dev(g), 1e-6)
+    ref = oracle_boundary(G, du, H, F, w, wn, g, 1e-6)
+    compare(got, ref[:5], du, ref[5], wn, g, 1e-6, n, f"{dt} d={d} n={n} per_token={per_token}")
+
+
+@pytest.mark.parametrize("per_token", [False, True])
+def test_boundary_backward_dgamma_bitwise_pre(per_token):
+    """dgamma is bitwise hc_pre_mix_backward's on the H' that hc_post_mix
+    stores: the same per-thread sums over the same token groups, so any
+    element of the recomputed H' that differed from the stored one would
+    show.  (dalpha is summed in another order; it is checked against the
+    oracle.)"""
+    rng = np.random.default_rng(5 + per_token)
+    T, n, d = 300, 4, 4096
+    H, F, G, du, w, wn, g = boundary_case(rng, "bf16", T, n, d, per_token)
+    Hd, Fd, wd, wnd, gd, dud = dev(H), dev(F), dev(w), dev(wn), dev(g), dev(du)
+    _, _, _, _, dg = hc.post_pre_mix_backward(dev(G), dud, Hd, Fd, wd, wnd, gd, 1e-6)
+    Hs = hc.post_mix(Hd, Fd, wd)
+    _, _, dg_pre = hc.pre_mix_backward(dud, Hs, wnd, gd, 1e-6)
+    assert np.array_equal(host(dg), host(dg_pre))
+
+
+def test_boundary_backward_in_place_and_deterministic():
+    """dH may overwrite dH_out (what a stack of layers does with one gradient
+    buffer); two calls give the same bits."""
+    rng = np.random.default_rng(9)
+    T, n, d = 257, 4, 4096
+    H, F, G, du, w, wn, g = boundary_case(rng, "bf16", T, n, d, False)
+    args = (dev(du), dev(H), dev(F), dev(w), dev(wn), dev(g), 1e-6)
+    ref = [host(x) for x in hc.post_pre_mix_backward(dev(G), *args)]
+    again = [host(x) for x in hc.post_pre_mix_backward(dev(G), *args)]
+    for a, b in zip(ref, again):
+        assert np.array_equal(a, b)
+    buf = dev(G)
+    ptr = buf.data_ptr()
+    out = hc.post_pre_mix_backward(buf, *args, out=buf)
+    assert out[0].data_ptr() == ptr
+    for a, b in zip(ref, out):
+        assert np.array_equal(a, host(b))
+
+
+def test_boundary_backward_through_a_stack():
+    """Four layers with shared records and given block outputs F_l (fp32
+    storage, T = 64, d = 4096): the gradient at the input streams and every
+    layer's dF, records and dgamma, from the library's backward schedule (the
+    last write-back's hc_post_mix_backward, one boundary call per inner
+    boundary writing dH in place, the first read-mix's hc_pre_mix_backward)
+    against the oracle's chain of the same steps.  fp32, because a bf16 chain
+    stores the gradient between layers: the records, sums over 2^18 products,
+    would then carry that rounding (about 2^-9 of their size), which the
+    single-boundary tests above keep out."""
+    rng = np.random.default_rng(21)
+    L, T, n, d, eps = 4, 64, 4, 4096, 1e-6
+    K = 2 * n + n * n
+    bf = lambda a: a.astype(np.float32)  # noqa: E731
+    H0 = bf(rng.standard_normal((T, n, d)))
+    Fs = [bf(rng.standard_normal((T, d))) for _ in range(L)]
+    dus = [bf(rng.standard_normal((T, d))) for _ in range(L)]
+    dHL = bf(rng.standard_normal((T, n, d)))
+    ws = [(identity_record(n) + 0.05 * rng.standard_normal(K)).astype(np.float32) for _ in range(L)]
+    gs = [(1 + 0.1 * rng.standard_normal(d)).astype(np.float32) for _ in range(L)]
+
+    # the oracle: stored streams of every layer, then the backward chain in fp64
+    Hs = [H0]
+    for l in range(L - 1):
+        _, Fs[l] = unambiguous(Hs[l], Fs[l], ws[l], move_h=False)
+        Hs.append(oracle.round_f32(oracle.post_mix(Hs[l], Fs[l], ws[l].astype(np.float64))))
+    r_dF, r_dw, r_dg = [None] * L, [np.zeros(K) for _ in range(L)], [None] * L
+    gH, r_dF[L - 1], rw = oracle.post_mix_backward(oracle.widen(dHL), oracle.widen(Hs[L - 1]),
+                                                  oracle.widen(Fs[L - 1]),
+                                                  ws[L - 1].astype(np.float64))
+    r_dw[L - 1] += rw.sum(axis=0)
+    for l in range(L - 1, 0, -1):
+        Gt, rwn, r_dg[l] = oracle.pre_mix_backward(dus[l], Hs[l], ws[l].astype(np.float64), gs[l],
+                                                   eps, dH_in=gH)
+        r_dw[l] += rwn.sum(axis=0)
+        gH, r_dF[l - 1], rw = oracle.post_mix_backward(Gt, oracle.widen(Hs[l - 1]),
+                                                       oracle.widen(Fs[l - 1]),
+                                                       ws[l - 1].astype(np.float64))
+        r_dw[l - 1] += rw.sum(axis=0)
+    r_dH0, rwn, r_dg[0] = oracle.pre_mix_backward(dus[0], H0, ws[0].astype(np.float64), gs[0], eps,
+                                                  dH_in=gH)
+    r_dw[0] += rwn.sum(axis=0)
+
+    # the library: its own forward streams, then the backward schedule
+    Hd = [dev(H0)]
+    for l in range(L - 1):
+        Hd.append(hc.post_mix(Hd[l], dev(Fs[l]), dev(ws[l])))
+    wd, gd = [dev(x) for x in ws], [dev(x) for x in gs]
+    dF, dw, dg = [None] * L, [np.zeros(K, np.float32) for _ in range(L)], [None] * L
+    buf, dF[L - 1], w_post = hc.post_mix_backward(dev(dHL), Hd[L - 1], dev(Fs[L - 1]), wd[L - 1])
+    dw[L - 1] += host(w_post)
+    for l in range(L - 1, 0, -1):
+        buf, dF[l - 1], w_post, w_pre, dg[l] = hc.post_pre_mix_backward(
+            buf, dev(dus[l]), Hd[l - 1], dev(Fs[l - 1]), wd[l - 1], wd[l], gd[l], eps, out=buf)
+        dw[l - 1] += host(w_post)
+        dw[l] += host(w_pre)
+    dH0, w_pre, dg[0] = hc.pre_mix_backward(dev(dus[0]), Hd[0], wd[0], gd[0], eps, dH_in=buf)
+    dw[0] += host(w_pre)
+
+    check(host(dH0), r_dH0, "stack dH0")
+    for l in range(L):
+        check(host(dF[l]), r_dF[l], f"stack dF layer {l}")
+        grad_check(dw[l][None, n:], r_dw[l][None, n:], f"stack dbeta, dA layer {l}")
+        dalpha_check(dw[l][None, :], r_dw[l][None, :], dus[l], Hs[l], ws[l], gs[l], eps,
+                     f"stack dalpha layer {l}")
+        grad_check(host(dg[l])[None, :], r_dg[l][None, :], f"stack dgamma layer {l}")
+
+
+@pytest.mark.timeout(600)
+def test_static_boundary_backward_full_size():
+    """The static workload's shape (T=8192, n=4, d=4096 bf16, shared records):
+    every token of dH and dF, the shared records and dgamma against the
+    oracle's chain."""
+    wl = workload("static-bf16")
+    inp = make_inputs(wl)
+    rng = np.random.default_rng(81)
+    T, n, d, K = wl.T, wl.n, wl.d, wl.K
+    wn = (identity_record(n) + 0.05 * rng.standard_normal(K)).astype(np.float32)
+    G = f32_to_bf16_bits(rng.standard_normal((T, n, d)).astype(np.float32))
+    du = f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    oracle.set_threads(0)
+    H, F = unambiguous(inp["H"], inp["F"], inp["w"])
+    got = hc.post_pre_mix_backward(dev(G), dev(du), dev(H), dev(F), dev(inp["w"]),
+                                   dev(wn), dev(inp["gamma"]), wl.eps)
+    ref = oracle_boundary(G, du, H, F, inp["w"], wn, inp["gamma"], wl.eps)
+    dH, dF = host(got[0]), host(got[1])
+    for t0 in range(0, T, 1024):
+        sl = slice(t0, t0 + 1024)
+        check(dH[sl], ref[0][sl], f"dH {t0}+")
+        check(dF[sl], ref[1][sl], f"dF {t0}+")
+    dw, dwn = host(got[2]), host(got[3])
+    assert np.all(dw[:n] == 0) and np.all(dwn[n:] == 0)
+    grad_check(dw[None, n:], ref[2].sum(axis=0)[None, n:], "shared dbeta, dA")
+    dalpha_check(dwn[None, :], ref[3].sum(axis=0)[None, :], du, ref[5], wn, inp["gamma"], wl.eps,
+                 "shared dalpha")
+    grad_check(host(got[4])[None, :], ref[4][None, :], "dgamma")
+
+
+@pytest.mark.timeout(900)
+def test_per_token_boundary_backward_full_size():
+    """The dynamic workload's shape (T=16384, n=4, d=4096 bf16) with one record
+    per token drawn on the host: every token's dH, dF, records, and dgamma,
+    against the oracle in chunks of 2048 tokens (gradients per token, so a
+    chunk is exact; dgamma is summed over the chunks)."""
+    wl = workload("dynamic-bf16")
+    inp = make_inputs(wl)
+    rng = np.random.default_rng(83)
+    T, n, d, K = wl.T, wl.n, wl.d, wl.K
+    w = (identity_record(n)[None, :] + 0.3 * rng.standard_normal((T, K))).astype(np.float32)
+    wn = (identity_record(n)[None, :] + 0.3 * rng.standard_normal((T, K))).astype(np.float32)
+    G = f32_to_bf16_bits(rng.standard_normal((T, n, d)).astype(np.float32))
+    du = f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    oracle.set_threads(0)
+    H, F = unambiguous(inp["H"], inp["F"], w)
+    got = [host(x) for x in hc.post_pre_mix_backward(dev(G), dev(du), dev(H), dev(F),
+                                                     dev(w), dev(wn), dev(inp["gamma"]), wl.eps)]
+    rdg = np.zeros(d)
+    for t0 in range(0, T, 2048):
+        sl = slice(t0, t0 + 2048)
+        ref = oracle_boundary(G[sl], du[sl], H[sl], F[sl], w[sl], wn[sl], inp["gamma"], wl.eps)
+        check(got[0][sl], ref[0], f"dH {t0}+")
+        check(got[1][sl], ref[1], f"dF {t0}+")
+        assert np.all(got[2][sl][:, :n] == 0) and np.all(got[3][sl][:, n:] == 0)
+        grad_check(got[2][sl][:, n:], ref[2][:, n:], f"dbeta, dA {t0}+")
+        dalpha_check(got[3][sl], ref[3], du[sl], ref[5], wn[sl], inp["gamma"], wl.eps,
+                     f"dalpha {t0}+")
+        rdg += ref[4]
+    grad_check(got[4][None, :], rdg[None, :], "dgamma")
+
+
+def test_boundary_backward_rejects():
+    rng = np.random.default_rng(1)
+    H, F, G, du, w, wn, g = boundary_case(rng, "bf16", 8, 4, 4096, False)
+    wt = np.broadcast_to(w, (8, 24)).copy()
+    with pytest.raises(ValueError):
+        hc.post_pre_mix_backward(dev(G), dev(du), dev(H), dev(F), dev(wt), dev(wn), dev(g))
+    fp8 = np.zeros((8, 4, 4096), np.uint8)
+    with pytest.raises((ValueError, RuntimeError)):
+        hc.post_pre_mix_backward(dev(fp8), dev(fp8[:, 0]), dev(fp8), dev(fp8[:, 0]), dev(w), dev(wn),
+                                 dev(g))
