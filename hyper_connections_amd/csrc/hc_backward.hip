@@ -558,12 +558,14 @@ __global__ __launch_bounds__(1024) void post_pre_bwd_kernel(
     constexpr int M = N + N * N;
     __shared__ float red[16 * 24];          // block_sum_vec<2> and block_sum_to<K>
     // With one vector per thread the rounded H' waits for the second phase in
-    // dynamic LDS, [stream][word][thread] (16 n bytes per thread; each thread
-    // reads back only what it wrote, so no barrier): at n = 4 that keeps the
-    // kernel within 128 VGPRs without spills.  With more vectors per thread
-    // it stays in registers.
+    // dynamic LDS, [wave][stream][word][lane] (16 n bytes per thread; each
+    // thread reads back only what it wrote, so no barrier; a wave's accesses
+    // are consecutive words, and the offsets are constants): at n = 4 that
+    // keeps the kernel within 128 VGPRs.  With more vectors per thread it
+    // stays in registers.
     constexpr bool kLds = VPT == 1;
     extern __shared__ uint32_t hol[];
+    uint32_t* const hl = hol + (threadIdx.x >> 6) * (N * 4 * 64) + (threadIdx.x & 63);
     const int B = blockDim.x;
     const int nvec = d / V;
     const int64_t row_bytes = (int64_t)d * Store<S>::kBytes;
@@ -640,7 +642,7 @@ __global__ __launch_bounds__(1024) void post_pre_bwd_kernel(
                 for (int i = 0; i < N; ++i) {
                     if constexpr (kLds) {
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) hol[(i * 4 + q) * B + threadIdx.x] = o[i][q];
+                        for (int q = 0; q < 4; ++q) hl[(i * 4 + q) * 64] = o[i][q];
                     } else {
                         ro[i][j] = make_uint4(o[i][0], o[i][1], o[i][2], o[i][3]);
                     }
@@ -696,7 +698,7 @@ __global__ __launch_bounds__(1024) void post_pre_bwd_kernel(
 #pragma unroll
                         for (int i = 0; i < N; ++i) {
                             unpack_word<S>(word(rh[i][j], q), h[i]);
-                            unpack_word<S>(kLds ? hol[(i * 4 + q) * B + threadIdx.x] : word(ro[i][j], q), ho[i]);
+                            unpack_word<S>(kLds ? hl[(i * 4 + q) * 64] : word(ro[i][j], q), ho[i]);
                             unpack_word<S>(word(rg[i][j], q), gr[i]);
                         }
                         unpack_word<S>(word(rf[j], q), f);
