@@ -1,8 +1,8 @@
 """The binding on a side stream: every wrapper allocates its outputs and
 workspaces on the stream its kernels run on, so that torch's caching
 allocator cannot hand that memory to other work while the kernels still run.
-Each gradient (post, pre, the weight producer) and the fused write-back is
-run on a side stream, with other work queued on the current stream that
+Each gradient (post, pre, the weight producer, the layer boundary's) and the
+fused write-backs are run on a side stream, with other work queued on the current stream that
 reuses freed memory meanwhile, and compared bitwise with the same call on
 the current stream."""
 import numpy as np
@@ -43,7 +43,8 @@ def churn():
         del x
 
 
-@pytest.mark.parametrize("which", ["post", "pre", "weights", "post_weights"])
+@pytest.mark.parametrize("which", ["post", "pre", "weights", "post_weights", "boundary",
+                                   "boundary_per_token", "post_weights_pre"])
 def test_side_stream_equals_current_stream(which):
     H, F, G, du, w, wt, g, W, ws, dw = inputs()
 
@@ -54,6 +55,12 @@ def test_side_stream_equals_current_stream(which):
             return hc.pre_mix_backward(du, H, w, g, 1e-6, stream=stream)
         if which == "weights":
             return hc.weights_backward(H, W, ws, 0.01, dw, 1e-6, 0, stream=stream)
+        if which == "boundary":
+            return hc.post_pre_mix_backward(G, du, H, F, w, w, g, 1e-6, stream=stream)
+        if which == "boundary_per_token":
+            return hc.post_pre_mix_backward(G, du, H, F, wt, wt, g, 1e-6, stream=stream)
+        if which == "post_weights_pre":
+            return hc.post_weights_pre_mix(H, F, wt, W, ws, 0.01, g, stream=stream)
         return hc.post_mix_weights(H, F, wt, W, ws, 0.01, 1e-6, 0, stream=stream)
 
     ref = [host(x) for x in run(None)]
