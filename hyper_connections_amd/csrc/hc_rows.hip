@@ -305,6 +305,17 @@ __global__ __launch_bounds__(1024) void post_pre_mix_kernel(
 
 // ------------------------------------------------------------ tanh block
 
+// tanh from the hardware base-2 exponential and reciprocal (each about one
+// ulp): tanh|x| = (1 - t) / (1 + t) with t = 2^(-2|x| log2 e), sign restored.
+// The error is a few fp32 ulps of the result, and about 1e-7 absolute near 0
+// where 1 - t cancels; the stored F is rounded to its storage type anyway.
+// tanh(+-inf) = +-1 and NaN stays NaN.  About a third of the instructions of
+// the library tanhf, which made the kernel bound by its arithmetic.
+__device__ __forceinline__ float tanh_fast(float x) {
+    const float t = __builtin_amdgcn_exp2f(-2.88539008177792681f * fabsf(x));   // 2 log2(e)
+    return copysignf((1.0f - t) * __builtin_amdgcn_rcpf(1.0f + t), x);
+}
+
 template <typename S>
 __global__ __launch_bounds__(256) void block_tanh_kernel(const uint8_t* __restrict__ u,
                                                          uint8_t* __restrict__ F, int64_t nvec) {
@@ -314,7 +325,7 @@ __global__ __launch_bounds__(256) void block_tanh_kernel(const uint8_t* __restri
         float x[V];
         unpack<S>(ld16_stream(u + v * 16), x);
 #pragma unroll
-        for (int e = 0; e < V; ++e) x[e] = tanhf(x[e]);
+        for (int e = 0; e < V; ++e) x[e] = tanh_fast(x[e]);
         st16_stream(F + v * 16, pack<S>(x));
     }
 }
