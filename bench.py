@@ -57,6 +57,7 @@ KERNEL_SOURCES = {
     "post_mix_backward": "hc_backward.hip", "pre_mix_backward": "hc_backward.hip",
     "sum_records": "hc_backward.hip", "weights_backward": "hc_weights_bwd.hip",
     "weights_backward_stream": "hc_weights_bwd.hip", "post_pre_mix_backward": "hc_backward.hip",
+    "sinkhorn_backward": "hc_weights_bwd.hip",
 }
 
 
@@ -560,12 +561,14 @@ def run_workload(args, name: str):
         "post_mix_backward": traffic.post_bwd_bytes(n, d, s, h_grad=not fold) * T,
         "pre_mix_backward": traffic.pre_bwd_bytes(n, d, s, True) * T,
         "weights_backward": traffic.weights_bwd_bytes(n, d, s) * T,
-        "post_pre_mix_backward": traffic.post_pre_bwd_bytes(n, d, s) * T,
+        "post_pre_mix_backward": traffic.post_pre_bwd_bytes(n, d, s, per_tok) * T,
+        "sinkhorn_backward": traffic.sinkhorn_bwd_bytes(n) * T,
     }
 
     if args.backward:
-        if wl.kind not in ("static", "dynamic") or wl.dtype == "fp8":
-            raise SystemExit("--backward is defined for the static and dynamic bf16/fp32 workloads")
+        if wl.kind not in ("static", "dynamic", "mhc") or wl.dtype == "fp8":
+            raise SystemExit("--backward is defined for the static, dynamic and mhc bf16/fp32 "
+                             "workloads")
         rng = np.random.default_rng(wl.seed + 1)
         G0 = dev(workloads.to_storage(rng.standard_normal((T, n, d), dtype=np.float32), wl.dtype))
         du0 = dev(workloads.to_storage(rng.standard_normal((T, d), dtype=np.float32), wl.dtype))
@@ -591,7 +594,20 @@ def run_workload(args, name: str):
                 b["dws"] = torch.empty(K, dtype=torch.float32, device="cuda")
                 b["wws"] = torch.empty(wws_bytes, dtype=torch.uint8, device="cuda")
             torch.cuda.synchronize()
-        rec = (lambda b: b["w"]) if wl.kind == "dynamic" else (lambda b: w_static)
+        if wl.kind == "mhc":
+            # a layer boundary at steady state in a stack of mHC layers: the
+            # write-back's records (this set's logits) and the next read-mix's
+            # (the next set's) come from Sinkhorn (untimed); gradients per token
+            sbytes = max(int(hc.lib().hc_sinkhorn_backward_workspace(T, wl.iters)), 16)
+            for i, b in enumerate(bufs):
+                hc.sinkhorn(b["logits"], n, wl.iters, out=b["w"])
+                b["next"] = bufs[(i + 1) % sets]
+                b["dwp"] = torch.empty((T, K), dtype=torch.float32, device="cuda")
+                b["dwq"] = torch.empty((T, K), dtype=torch.float32, device="cuda")
+                b["dl"] = torch.empty((T, K), dtype=torch.float32, device="cuda")
+                b["sws"] = torch.empty(sbytes, dtype=torch.uint8, device="cuda")
+            torch.cuda.synchronize()
+        rec = (lambda b: b["w"]) if wl.kind in ("dynamic", "mhc") else (lambda b: w_static)
 
         def post_bwd(b):
             # dH lands in b["O"] and the pre backward accumulates into it; folded,
@@ -616,6 +632,18 @@ def run_workload(args, name: str):
         ops = [("post_mix_backward", post_bwd), ("pre_mix_backward", pre_bwd)]
         if wl.kind == "dynamic":
             ops.append(("weights_backward", weights_bwd))
+        elif wl.kind == "mhc":
+            # the boundary's gradient in one pass, then the next layer's logit
+            # gradient through Sinkhorn from its two record gradients: this
+            # call's read-mix part and the write-back part that the next
+            # boundary's call (another buffer set here) produced
+            ops = [("post_pre_mix_backward", lambda b: hc.post_pre_mix_backward(
+                       b["G"], b["du"], b["H"], b["F"], b["w"], b["next"]["w"], gamma, wl.eps,
+                       out=b["O"], dF=b["dF"], dw=b["dwp"], dw_next=b["dwq"], dgamma_next=b["dg"],
+                       workspace=b["ws"])),
+                   ("sinkhorn_backward", lambda b: hc.sinkhorn_backward(
+                       b["next"]["logits"], b["dwq"], n, wl.iters, out=b["dl"],
+                       workspace=b["sws"], dw2=b["next"]["dwp"]))]
         elif args.fused:
             # one layer boundary's gradient at steady state in a stack: this
             # layer's read-mix and the previous layer's write-back in one pass

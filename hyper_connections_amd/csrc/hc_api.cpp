@@ -95,7 +95,7 @@ const char* hc_status_str(hc_status status) {
     return "HC_ERR_UNKNOWN: unknown status code";
 }
 
-int32_t hc_abi_version(void) { return 6; }
+int32_t hc_abi_version(void) { return 7; }
 
 hc_status hc_pre_mix(const void* H, const float* w, int64_t w_stride, const float* gamma, float eps,
                      void* u, int64_t T, int32_t n, int32_t d, hc_dtype dt_arg, void* stream) {
@@ -523,9 +523,9 @@ int64_t hc_sinkhorn_backward_workspace(int64_t T, int32_t iters) {
     return hc::sinkhorn_backward_workspace_bytes(T, iters);
 }
 
-hc_status hc_sinkhorn_backward(const float* logits, const float* dw, float* dlogits, int32_t iters,
-                               void* workspace, int64_t workspace_bytes, int64_t T, int32_t n,
-                               void* stream) {
+hc_status hc_sinkhorn_backward(const float* logits, const float* dw, const float* dw2,
+                               float* dlogits, int32_t iters, void* workspace,
+                               int64_t workspace_bytes, int64_t T, int32_t n, void* stream) {
     if (n < 1 || n > HC_MAX_STREAMS) return HC_ERR_SHAPE;
     if (T < 0 || iters < 0 || iters > HC_MAX_SINKHORN_ITERS) return HC_ERR_ARG;
     const int K = record_len(n);
@@ -535,13 +535,15 @@ hc_status hc_sinkhorn_backward(const float* logits, const float* dw, float* dlog
     const int64_t need = hc_sinkhorn_backward_workspace(T, iters);
     if (need > 0 && !workspace) return HC_ERR_NULL;
     if (workspace_bytes < need) return HC_ERR_ARG;
-    if (misaligned(logits, 4) || misaligned(dw, 4) || misaligned(dlogits, 4) ||
-        (need > 0 && misaligned(workspace, 4)))
+    if (misaligned(logits, 4) || misaligned(dw, 4) || misaligned(dw2, 4) ||
+        misaligned(dlogits, 4) || (need > 0 && misaligned(workspace, 4)))
         return HC_ERR_ALIGN;
-    const Span sl{logits, T * K * 4}, sg{dw, T * K * 4}, so{dlogits, T * K * 4}, sws{workspace, need};
-    if (overlap(so, sl) || overlap(so, sg) || overlap(sws, sl) || overlap(sws, sg) || overlap(sws, so))
+    const Span sl{logits, T * K * 4}, sg{dw, T * K * 4}, sg2{dw2, dw2 ? T * K * 4 : 0},
+        so{dlogits, T * K * 4}, sws{workspace, need};
+    if (overlap(so, sl) || overlap(so, sg) || overlap(so, sg2) || overlap(sws, sl) ||
+        overlap(sws, sg) || overlap(sws, sg2) || overlap(sws, so))
         return HC_ERR_ALIAS;
-    return from_hip(hc::launch_sinkhorn_backward(logits, dw, dlogits, iters, workspace, T, n,
+    return from_hip(hc::launch_sinkhorn_backward(logits, dw, dw2, dlogits, iters, workspace, T, n,
                                                  static_cast<hipStream_t>(stream)));
 }
 

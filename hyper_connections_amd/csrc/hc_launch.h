@@ -113,7 +113,8 @@ hipError_t launch_weights_backward(const void* H, const void* W, const float* w_
                                    const float* saved, const void* dH_in,
                                    void* dH, float* dW, float* dws, void* work, int64_t T, int n,
                                    int d, int dt, hipStream_t s);
-hipError_t launch_sinkhorn_backward(const float* logits, const float* dw, float* dlogits, int iters,
-                                    void* work, int64_t T, int n, hipStream_t s);
+hipError_t launch_sinkhorn_backward(const float* logits, const float* dw, const float* dw2,
+                                    float* dlogits, int iters, void* work, int64_t T, int n,
+                                    hipStream_t s);
 
 }  // namespace hc

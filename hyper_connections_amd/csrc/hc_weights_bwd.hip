@@ -144,6 +144,7 @@ __device__ void mhc_record_bwd(const float* l, const float* g, float* dl, int it
 template <int N>
 __global__ __launch_bounds__(256) void sinkhorn_bwd_kernel(const float* __restrict__ logits,
                                                            const float* __restrict__ dw,
+                                                           const float* __restrict__ dw2,
                                                            float* __restrict__ dlogits, int iters,
                                                            float* __restrict__ scr, int64_t T) {
     constexpr int K = 2 * N + N * N;
@@ -153,7 +154,9 @@ __global__ __launch_bounds__(256) void sinkhorn_bwd_kernel(const float* __restri
 #pragma unroll
         for (int c = 0; c < K; ++c) {
             l[c] = logits[t * K + c];
-            g[c] = dw[t * K + c];
+            // dw2: the records' gradient from a second consumer (the read-mix
+            // and the write-back of a layer use the same record)
+            g[c] = dw2 ? dw[t * K + c] + dw2[t * K + c] : dw[t * K + c];
         }
         mhc_record_bwd<N>(l, g, out, iters, scr + t * kSlot, T * kSlot);
 #pragma unroll
@@ -773,16 +776,17 @@ int64_t sinkhorn_backward_workspace_bytes(int64_t T, int iters) {
     return int64_t(iters) * T * kSlot * 4;
 }
 
-hipError_t launch_sinkhorn_backward(const float* logits, const float* dw, float* dlogits, int iters,
-                                    void* work, int64_t T, int n, hipStream_t s) {
+hipError_t launch_sinkhorn_backward(const float* logits, const float* dw, const float* dw2,
+                                    float* dlogits, int iters, void* work, int64_t T, int n,
+                                    hipStream_t s) {
     const int64_t blocks = (T + 63) / 64;
     const dim3 grid((unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid));
     float* scr = static_cast<float*>(work);
     switch (n) {
-        case 1: return launch(sinkhorn_bwd_kernel<1>, grid, dim3(64), 0, s, logits, dw, dlogits, iters, scr, T);
-        case 2: return launch(sinkhorn_bwd_kernel<2>, grid, dim3(64), 0, s, logits, dw, dlogits, iters, scr, T);
-        case 3: return launch(sinkhorn_bwd_kernel<3>, grid, dim3(64), 0, s, logits, dw, dlogits, iters, scr, T);
-        case 4: return launch(sinkhorn_bwd_kernel<4>, grid, dim3(64), 0, s, logits, dw, dlogits, iters, scr, T);
+        case 1: return launch(sinkhorn_bwd_kernel<1>, grid, dim3(64), 0, s, logits, dw, dw2, dlogits, iters, scr, T);
+        case 2: return launch(sinkhorn_bwd_kernel<2>, grid, dim3(64), 0, s, logits, dw, dw2, dlogits, iters, scr, T);
+        case 3: return launch(sinkhorn_bwd_kernel<3>, grid, dim3(64), 0, s, logits, dw, dw2, dlogits, iters, scr, T);
+        case 4: return launch(sinkhorn_bwd_kernel<4>, grid, dim3(64), 0, s, logits, dw, dw2, dlogits, iters, scr, T);
     }
     return hipErrorInvalidValue;
 }

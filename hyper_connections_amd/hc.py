@@ -59,7 +59,7 @@ _SIGS = {
                         _vp],
     "hc_weights_backward": [_vp, _vp, _fp, _f32, _f32, _i32, _fp, _fp, _fp, _vp, _vp, _fp, _fp,
                             _vp, _i64, _i64, _i32, _i32, _i32, _vp],
-    "hc_sinkhorn_backward": [_fp, _fp, _fp, _i32, _vp, _i64, _i64, _i32, _vp],
+    "hc_sinkhorn_backward": [_fp, _fp, _fp, _fp, _i32, _vp, _i64, _i64, _i32, _vp],
     "hc_post_mix_weights": [_vp, _vp, _fp, _i64, _vp, _fp, _f32, _f32, _i32, _vp, _fp, _fp, _i64,
                             _i64, _i32, _i32, _i32, _vp],
     "hc_post_mix_backward_noalloc": [_vp, _vp, _vp, _fp, _i64, _vp, _vp, _fp, _i64, _i32, _i32,
@@ -634,8 +634,11 @@ def weights_backward(H, W, w_static, scale: float, dw, eps: float = 1e-6, sinkho
 
 
 @_on_launch_stream
-def sinkhorn_backward(logits, dw, n: int, iters: int, out=None, workspace=None, stream=None):
-    """Gradient of sinkhorn: dL/dlogits (T, K) float32 from dL/dw (T, K)."""
+def sinkhorn_backward(logits, dw, n: int, iters: int, out=None, workspace=None, stream=None,
+                      dw2=None):
+    """Gradient of sinkhorn: dL/dlogits (T, K) float32 from dL/dw (T, K),
+    plus dw2 when given (the records' gradient from a second call, e.g. the
+    read-mix's and the write-back's of one layer)."""
     _dev(logits, "logits")
     _dev(dw, "dw")
     K = 2 * n + n * n
@@ -643,13 +646,18 @@ def sinkhorn_backward(logits, dw, n: int, iters: int, out=None, workspace=None, 
         raise ValueError(f"logits must be float32 of shape (T, {K})")
     if dw.dtype != torch.float32 or dw.shape != logits.shape:
         raise ValueError("dw must match logits")
+    if dw2 is not None:
+        _dev(dw2, "dw2")
+        if dw2.dtype != torch.float32 or dw2.shape != logits.shape:
+            raise ValueError("dw2 must match logits")
     T = logits.shape[0]
     o = torch.empty_like(logits) if out is None else _dev(out, "out")
     need = int(lib().hc_sinkhorn_backward_workspace(T, int(iters)))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=logits.device)
     _dev(workspace, "workspace")
-    _call("hc_sinkhorn_backward", logits.data_ptr(), dw.data_ptr(), o.data_ptr(), int(iters),
+    _call("hc_sinkhorn_backward", logits.data_ptr(), dw.data_ptr(),
+          dw2.data_ptr() if dw2 is not None else None, o.data_ptr(), int(iters),
           workspace.data_ptr(), workspace.numel() * workspace.element_size(), T, n,
           _stream(stream))
     return o

@@ -102,12 +102,21 @@ def pre_bwd_bytes(n: int, d: int, s: int, accumulate: bool = True) -> int:
     return (2 * n + 1 + (n if accumulate else 0)) * d * s + record_bytes(n)
 
 
-def post_pre_bwd_bytes(n: int, d: int, s: int) -> int:
+def post_pre_bwd_bytes(n: int, d: int, s: int, per_token_record: bool = False) -> int:
     """Gradient of one layer boundary (write-back and next read-mix) in one
     pass: read dH', du, H and F, write dH and dF ((3n + 3) d s; H' is
     recomputed, not read), and the two gradient records (as in the separate
-    calls, whose rows total (5n + 3) d s)."""
-    return (3 * n + 3) * d * s + 2 * record_bytes(n)
+    calls, whose rows total (5n + 3) d s); per-token records also read the
+    two weight records."""
+    return (3 * n + 3) * d * s + (4 if per_token_record else 2) * record_bytes(n)
+
+
+def sinkhorn_bwd_bytes(n: int, two_gradients: bool = True) -> int:
+    """Gradient of the mHC transform per token: read the logit record and the
+    record gradient (two of them when they come from two calls), write the
+    logit gradient.  Not counted: the workspace that keeps the matrix entering
+    every iteration (64 B per iteration, written and read back)."""
+    return (4 if two_gradients else 3) * record_bytes(n)
 
 
 def weights_bwd_bytes(n: int, d: int, s: int) -> int:

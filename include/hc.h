@@ -368,13 +368,15 @@ hc_status hc_weights_backward(const void* H, const void* W, const float* w_stati
 int64_t hc_sinkhorn_backward_workspace(int64_t T, int32_t iters);
 
 /* Gradient of hc_sinkhorn: dlogits [T][K] from dw = dL/dw [T][K] (both fp32,
- * stride K).  Each token's forward is re-run keeping the matrix entering
- * every iteration in the workspace; the row and column steps are undone in
- * reverse, then exp and the sigmoids.  dlogits may not overlap the inputs or
- * the workspace. */
-hc_status hc_sinkhorn_backward(const float* logits, const float* dw, float* dlogits, int32_t iters,
-                               void* workspace, int64_t workspace_bytes, int64_t T, int32_t n,
-                               void* stream);
+ * stride K), plus dw2 [T][K] when not NULL (a layer's records feed its
+ * read-mix and its write-back, whose gradients arrive from two calls: e.g.
+ * the dw_next of one hc_post_pre_mix_backward and the dw of the next).  Each
+ * token's forward is re-run keeping the matrix entering every iteration in
+ * the workspace; the row and column steps are undone in reverse, then exp and
+ * the sigmoids.  dlogits may not overlap the inputs or the workspace. */
+hc_status hc_sinkhorn_backward(const float* logits, const float* dw, const float* dw2,
+                               float* dlogits, int32_t iters, void* workspace,
+                               int64_t workspace_bytes, int64_t T, int32_t n, void* stream);
 
 /* out[c] = sum over t of rec[t * K + c], c < K, summed in a fixed order:
  * turns per-token gradient records into the gradient of one shared record.

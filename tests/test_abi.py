@@ -51,7 +51,7 @@ def test_status_strings(L):
         s = hc.status_str(code)
         assert s.startswith("HC_")
     assert hc.status_str(99).startswith("HC_ERR_UNKNOWN")
-    assert hc.abi_version() == 6
+    assert hc.abi_version() == 7
 
 
 def pre(L, H=P[0], w=P[1], ws=0, g=P[2], eps=1e-6, u=P[3], T=16, n=4, d=4096, dt=BF16):
@@ -343,9 +343,11 @@ def test_sinkhorn_backward_validation(L):
     need = L.hc_sinkhorn_backward_workspace(100, 20)
     assert need == 100 * 20 * 64 and L.hc_sinkhorn_backward_workspace(100, 0) == 0
     f = lambda **k: L.hc_sinkhorn_backward(  # noqa: E731
-        k.get("l", P[0]), k.get("g", P[1]), k.get("o", P[2]), k.get("it", 20), k.get("wk", P[3]),
-        k.get("wkb", need), k.get("T", 100), k.get("n", 4), None)
+        k.get("l", P[0]), k.get("g", P[1]), k.get("g2", None), k.get("o", P[2]), k.get("it", 20),
+        k.get("wk", P[3]), k.get("wkb", need), k.get("T", 100), k.get("n", 4), None)
     assert f(T=0) == OK
     assert f(n=5) == SHAPE and f(it=-1) == ARG and f(T=-2) == ARG and f(wkb=need - 4) == ARG
     assert f(l=None) == NULL and f(wk=None) == NULL
     assert f(o=P[0] + 4) == ALIAS and f(wk=P[1]) == ALIAS and f(o=P[2] + 2) == ALIGN
+    # dw2: optional, an input like dw
+    assert f(g2=P[4] + 2) == ALIGN and f(g2=P[2] + 64) == ALIAS and f(g2=P[3]) == ALIAS

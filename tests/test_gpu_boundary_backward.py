@@ -299,6 +299,44 @@ def test_per_token_boundary_backward_full_size():
     grad_check(got[4][None, :], rdg[None, :], "dgamma")
 
 
+def test_mhc_boundary_backward_through_sinkhorn():
+    """A layer boundary with mHC records (n = 4, d = 4096 bf16, 20 Sinkhorn
+    iterations, T = 512): the write-back's and the read-mix's records from
+    their logits, the boundary's gradient in one pass, then the read-mix
+    layer's logit gradient through Sinkhorn from its two record gradients
+    (the boundary's dalpha and a write-back part given as dw2), against the
+    oracle's chain of the same steps.  The beta and A columns see the same
+    dw2 on both sides (1e-4 of the row's RMS); the alpha columns carry the
+    boundary's dalpha, held to 1e-5 of its Cauchy-Schwarz bound times the
+    sigmoid's largest slope (1/4), as dalpha is."""
+    rng = np.random.default_rng(31)
+    T, n, d, K, it, eps = 512, 4, 4096, 24, 20, 1e-6
+    lg_w = rng.standard_normal((T, K))
+    lg = rng.standard_normal((T, K)).astype(np.float32)
+    w = oracle.sinkhorn(lg_w, n, it).astype(np.float32)
+    wn = oracle.sinkhorn(lg.astype(np.float64), n, it).astype(np.float32)
+    bf = lambda *sh: f32_to_bf16_bits(rng.standard_normal(sh).astype(np.float32))  # noqa: E731
+    H, F, G, du = bf(T, n, d), bf(T, d), bf(T, n, d), bf(T, d)
+    g = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    dw2 = rng.standard_normal((T, K)).astype(np.float32)
+    H, F = unambiguous(H, F, w)
+    _, _, _, dwn, _ = hc.post_pre_mix_backward(dev(G), dev(du), dev(H), dev(F), dev(w), dev(wn),
+                                               dev(g), eps)
+    dl = host(hc.sinkhorn_backward(dev(lg), dwn, n, it, dw2=dev(dw2)))
+    ref = oracle_boundary(G, du, H, F, w, wn, g, eps)
+    rdl = oracle.sinkhorn_backward(lg.astype(np.float64), ref[3] + dw2.astype(np.float64), n, it)
+    grad_check(dl[:, n:], rdl[:, n:], "mHC dlogits, beta and A")
+    # the Cauchy-Schwarz bound of dalpha, |dx| |H'_i|, per token and stream
+    Hs = oracle.widen(ref[5])
+    x = np.einsum("ti,tid->td", wn[:, :n].astype(np.float64), Hs)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps)
+    dy = g[None, :] * oracle.widen(du)
+    dx = r * (dy - x * r * r * np.mean(dy * x, axis=1, keepdims=True))
+    bound = np.linalg.norm(dx, axis=1)[:, None] * np.linalg.norm(Hs, axis=2)
+    e = np.max(np.abs(dl[:, :n] - rdl[:, :n]) / (0.25 * bound))
+    assert e <= 1e-5, f"mHC dlogits, alpha: {e:.3g} of the bound"
+
+
 def test_boundary_backward_rejects():
     rng = np.random.default_rng(1)
     H, F, G, du, w, wn, g = boundary_case(rng, "bf16", 8, 4, 4096, False)

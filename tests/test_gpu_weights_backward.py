@@ -111,6 +111,21 @@ def test_sinkhorn_backward_parity(n, iters):
     grad_check(got, ref, f"dlogits n={n} iters={iters}")
 
 
+@pytest.mark.parametrize("n", [1, 4])
+def test_sinkhorn_backward_two_gradients(n):
+    """dw2 (the records' gradient from a second call) is added to dw: against
+    the oracle's gradient of dw + dw2, at the configured 20 iterations."""
+    rng = np.random.default_rng(n * 7 + 1)
+    T, K = 1000, 2 * n + n * n
+    lg = rng.standard_normal((T, K)).astype(np.float32)
+    dw = rng.standard_normal((T, K)).astype(np.float32)
+    dw2 = rng.standard_normal((T, K)).astype(np.float32)
+    got = host(hc.sinkhorn_backward(dev(lg), dev(dw), n, 20, dw2=dev(dw2)))
+    ref = oracle.sinkhorn_backward(lg.astype(np.float64),
+                                   dw.astype(np.float64) + dw2.astype(np.float64), n, 20)
+    grad_check(got, ref, f"dlogits from two gradients n={n}")
+
+
 def test_dynamic_workload_backward_full_size():
     """T=16384, n=4, d=4096 bf16 (the dynamic workload): dH of every token,
     dW and dw_static over all tokens, against the oracle (run in chunks of
