@@ -77,21 +77,25 @@ __device__ void mhc_record_bwd(const float* l, const float* g, float* dl, int it
         float* dst = scr + it * stride;
 #pragma unroll
         for (int e = 0; e < NN; ++e) dst[e] = M[e];
+        // one correctly rounded reciprocal per sum, then products (a division
+        // per entry cost about ten instructions each, the bulk of this loop)
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             float s = M[i * N];
 #pragma unroll
             for (int j = 1; j < N; ++j) s += M[i * N + j];
+            const float inv = 1.0f / s;
 #pragma unroll
-            for (int j = 0; j < N; ++j) M[i * N + j] = M[i * N + j] / s;
+            for (int j = 0; j < N; ++j) M[i * N + j] *= inv;
         }
 #pragma unroll
         for (int j = 0; j < N; ++j) {
             float s = M[j];
 #pragma unroll
             for (int i = 1; i < N; ++i) s += M[i * N + j];
+            const float inv = 1.0f / s;
 #pragma unroll
-            for (int i = 0; i < N; ++i) M[i * N + j] = M[i * N + j] / s;
+            for (int i = 0; i < N; ++i) M[i * N + j] *= inv;
         }
     }
     float G[NN];
@@ -102,30 +106,31 @@ __device__ void mhc_record_bwd(const float* l, const float* g, float* dl, int it
         float R[NN], rs[N], cs[N];
 #pragma unroll
         for (int e = 0; e < NN; ++e) R[e] = src[e];
+        // the reciprocals of the row sums and column sums (rs, cs hold 1/sum)
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             float s = R[i * N];
 #pragma unroll
             for (int j = 1; j < N; ++j) s += R[i * N + j];
-            rs[i] = s;
+            rs[i] = 1.0f / s;
 #pragma unroll
-            for (int j = 0; j < N; ++j) R[i * N + j] = R[i * N + j] / s;
+            for (int j = 0; j < N; ++j) R[i * N + j] *= rs[i];
         }
 #pragma unroll
         for (int j = 0; j < N; ++j) {
             float s = R[j];
 #pragma unroll
             for (int i = 1; i < N; ++i) s += R[i * N + j];
-            cs[j] = s;
+            cs[j] = 1.0f / s;
         }
         // column step: C_ij = R_ij / cs_j
 #pragma unroll
         for (int j = 0; j < N; ++j) {
             float s = 0.0f;
 #pragma unroll
-            for (int i = 0; i < N; ++i) s = fmaf(G[i * N + j], R[i * N + j] / cs[j], s);
+            for (int i = 0; i < N; ++i) s = fmaf(G[i * N + j], R[i * N + j] * cs[j], s);
 #pragma unroll
-            for (int i = 0; i < N; ++i) G[i * N + j] = (G[i * N + j] - s) / cs[j];
+            for (int i = 0; i < N; ++i) G[i * N + j] = (G[i * N + j] - s) * cs[j];
         }
         // row step: R_ij = M_ij / rs_i
 #pragma unroll
@@ -134,7 +139,7 @@ __device__ void mhc_record_bwd(const float* l, const float* g, float* dl, int it
 #pragma unroll
             for (int j = 0; j < N; ++j) s = fmaf(G[i * N + j], R[i * N + j], s);
 #pragma unroll
-            for (int j = 0; j < N; ++j) G[i * N + j] = (G[i * N + j] - s) / rs[i];
+            for (int j = 0; j < N; ++j) G[i * N + j] = (G[i * N + j] - s) * rs[i];
         }
     }
 #pragma unroll
