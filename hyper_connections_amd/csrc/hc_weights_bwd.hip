@@ -146,26 +146,141 @@ __device__ void mhc_record_bwd(const float* l, const float* g, float* dl, int it
     for (int e = 0; e < NN; ++e) dl[2 * N + e] = G[e] * M0[e];
 }
 
-template <int N>
-__global__ __launch_bounds__(256) void sinkhorn_bwd_kernel(const float* __restrict__ logits,
-                                                           const float* __restrict__ dw,
-                                                           const float* __restrict__ dw2,
-                                                           float* __restrict__ dlogits, int iters,
-                                                           float* __restrict__ scr, int64_t T) {
+// hc_sinkhorn_backward: the same gradient with four lanes per token.  Lane r
+// of a quad holds row r of the 4 x 4 matrix (rows r >= N hold zeros and
+// stay zero) and alpha_r, beta_r.  Row sums are the lane's own; column sums
+// and the column step's dot products are added over the quad by two DPP
+// exchanges (lanes l ^ 1, then l ^ 2), which every lane of the quad adds in
+// an order that gives the same bits.  Four times the lanes of the
+// one-thread form, so 32768 tokens fill 2048 waves instead of 512; the
+// scratch layout is the same (row r of the matrix entering an iteration at
+// floats 4r .. 4r + 3 of the token's slot).
+__device__ __forceinline__ float quad_swap1(float x) {      // quad_perm [1, 0, 3, 2]
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_swap2(float x) {      // quad_perm [2, 3, 0, 1]
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_add(float x) {
+    x += quad_swap1(x);
+    return x + quad_swap2(x);
+}
+__device__ __forceinline__ float quad_max(float x) {
+    x = fmaxf(x, quad_swap1(x));
+    return fmaxf(x, quad_swap2(x));
+}
+
+// IMAX > 0: at most IMAX iterations, whose matrices stay in registers (a
+// row of 4 floats per lane and iteration) instead of the scratch; the
+// iteration loops are unrolled with their index known, and the scratch is
+// not touched.  IMAX = 0: any count, through the scratch.
+template <int N, int IMAX>
+__global__ __launch_bounds__(256) void sinkhorn_bwd_quad_kernel(const float* __restrict__ logits,
+                                                                const float* __restrict__ dw,
+                                                                const float* __restrict__ dw2,
+                                                                float* __restrict__ dlogits,
+                                                                int iters, float* __restrict__ scr,
+                                                                int64_t T) {
     constexpr int K = 2 * N + N * N;
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < T;
-         t += (int64_t)gridDim.x * blockDim.x) {
-        float l[K], g[K], out[K];
+    const int r = threadIdx.x & 3;
+    const bool row = r < N;
+    const int64_t step = ((int64_t)gridDim.x * blockDim.x) >> 2;
+    // a quad's four lanes share t, so they run (and exchange) together
+    for (int64_t t = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 2; t < T; t += step) {
+        const float* lt = logits + t * K;
+        const float* gt = dw + t * K;
+        const float* g2 = dw2 ? dw2 + t * K : nullptr;
+        float* ot = dlogits + t * K;
+        if (row) {
 #pragma unroll
-        for (int c = 0; c < K; ++c) {
-            l[c] = logits[t * K + c];
-            // dw2: the records' gradient from a second consumer (the read-mix
-            // and the write-back of a layer use the same record)
-            g[c] = dw2 ? dw[t * K + c] + dw2[t * K + c] : dw[t * K + c];
+            for (int h = 0; h < 2; ++h) {
+                const int c = h * N + r;
+                const float g = g2 ? gt[c] + g2[c] : gt[c];
+                ot[c] = g * dsigmoid(lt[c]);
+            }
         }
-        mhc_record_bwd<N>(l, g, out, iters, scr + t * kSlot, T * kSlot);
+        float l[N], G[N], M[N], M0[N];
 #pragma unroll
-        for (int c = 0; c < K; ++c) dlogits[t * K + c] = out[c];
+        for (int j = 0; j < N; ++j) {
+            const int c = 2 * N + r * N + j;
+            l[j] = row ? lt[c] : -INFINITY;
+            G[j] = row ? (g2 ? gt[c] + g2[c] : gt[c]) : 0.0f;
+        }
+        float m = 0.0f;
+        if (iters > 0) {
+            float mx = l[0];
+#pragma unroll
+            for (int j = 1; j < N; ++j) mx = fmaxf(mx, l[j]);
+            m = quad_max(mx);
+        }
+#pragma unroll
+        for (int j = 0; j < N; ++j) M0[j] = M[j] = row ? expf(l[j] - m) : 0.0f;
+        const int64_t stride = T * kSlot;
+        float* slot = scr + t * kSlot + 4 * r;
+        float keep[IMAX > 0 ? IMAX : 1][N];
+        auto forward = [&](int it) __attribute__((always_inline)) {
+            if constexpr (IMAX > 0) {
+#pragma unroll
+                for (int j = 0; j < N; ++j) keep[IMAX > 0 ? it : 0][j] = M[j];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) slot[it * stride + j] = j < N ? M[j] : 0.0f;
+            }
+            if (row) {
+                float s = M[0];
+#pragma unroll
+                for (int j = 1; j < N; ++j) s += M[j];
+                const float inv = 1.0f / s;
+#pragma unroll
+                for (int j = 0; j < N; ++j) M[j] *= inv;
+            }
+#pragma unroll
+            for (int j = 0; j < N; ++j) M[j] *= 1.0f / quad_add(M[j]);
+        };
+        auto backward = [&](int it) __attribute__((always_inline)) {
+            float R[N];
+#pragma unroll
+            for (int j = 0; j < N; ++j) R[j] = IMAX > 0 ? keep[IMAX > 0 ? it : 0][j] : slot[it * stride + j];
+            float rs = 0.0f;
+            if (row) {
+                float s = R[0];
+#pragma unroll
+                for (int j = 1; j < N; ++j) s += R[j];
+                rs = 1.0f / s;
+#pragma unroll
+                for (int j = 0; j < N; ++j) R[j] *= rs;
+            }
+            // column step: C_ij = R_ij / cs_j
+#pragma unroll
+            for (int j = 0; j < N; ++j) {
+                const float ci = 1.0f / quad_add(R[j]);
+                const float s = quad_add(G[j] * (R[j] * ci));
+                G[j] = row ? (G[j] - s) * ci : 0.0f;
+            }
+            // row step: R_ij = M_ij / rs_i
+            if (row) {
+                float s = 0.0f;
+#pragma unroll
+                for (int j = 0; j < N; ++j) s = fmaf(G[j], R[j], s);
+#pragma unroll
+                for (int j = 0; j < N; ++j) G[j] = (G[j] - s) * rs;
+            }
+        };
+        if constexpr (IMAX > 0) {
+#pragma unroll
+            for (int it = 0; it < IMAX; ++it)
+                if (it < iters) forward(it);
+#pragma unroll
+            for (int it = IMAX - 1; it >= 0; --it)
+                if (it < iters) backward(it);
+        } else {
+            for (int it = 0; it < iters; ++it) forward(it);
+            for (int it = iters - 1; it >= 0; --it) backward(it);
+        }
+        if (row) {
+#pragma unroll
+            for (int j = 0; j < N; ++j) ot[2 * N + r * N + j] = G[j] * M0[j];
+        }
     }
 }
 
@@ -784,15 +899,25 @@ int64_t sinkhorn_backward_workspace_bytes(int64_t T, int iters) {
 hipError_t launch_sinkhorn_backward(const float* logits, const float* dw, const float* dw2,
                                     float* dlogits, int iters, void* work, int64_t T, int n,
                                     hipStream_t s) {
-    const int64_t blocks = (T + 63) / 64;
+    // four lanes per token, 64 tokens per 256-thread workgroup
+    const int64_t blocks = (4 * T + 255) / 256;
     const dim3 grid((unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid));
     float* scr = static_cast<float*>(work);
+    // up to kKeep iterations keep their matrices in registers
+    constexpr int kKeep = 20;
+    const bool reg = iters <= kKeep;
+#define HC_SKB(NN)                                                                              \
+    return reg ? launch(sinkhorn_bwd_quad_kernel<NN, kKeep>, grid, dim3(256), 0, s, logits, dw, \
+                        dw2, dlogits, iters, scr, T)                                            \
+               : launch(sinkhorn_bwd_quad_kernel<NN, 0>, grid, dim3(256), 0, s, logits, dw, dw2, \
+                        dlogits, iters, scr, T);
     switch (n) {
-        case 1: return launch(sinkhorn_bwd_kernel<1>, grid, dim3(64), 0, s, logits, dw, dw2, dlogits, iters, scr, T);
-        case 2: return launch(sinkhorn_bwd_kernel<2>, grid, dim3(64), 0, s, logits, dw, dw2, dlogits, iters, scr, T);
-        case 3: return launch(sinkhorn_bwd_kernel<3>, grid, dim3(64), 0, s, logits, dw, dw2, dlogits, iters, scr, T);
-        case 4: return launch(sinkhorn_bwd_kernel<4>, grid, dim3(64), 0, s, logits, dw, dw2, dlogits, iters, scr, T);
+        case 1: HC_SKB(1)
+        case 2: HC_SKB(2)
+        case 3: HC_SKB(3)
+        case 4: HC_SKB(4)
     }
+#undef HC_SKB
     return hipErrorInvalidValue;
 }
 
