@@ -21,6 +21,12 @@
 // Either post writes its share and pre adds into it, or (folded) post skips
 // it and pre forms sum_j A[j][i] dH'_j itself, which moves n rows per token
 // fewer and rounds once.
+// In a stack of layers the write-back of one layer and the read-mix of the
+// next meet at the same H' (the forward's fused boundary), and
+// post_pre_bwd_kernel takes both gradients there in one pass: it recomputes
+// H' from the write-back's inputs, adds the read-mix's share to the
+// gradient arriving at H', and applies the write-back's gradient to the sum
+// without storing it.
 //
 // Weight gradients take the shape of the weights: one record per token for
 // per-token weights (post: a workgroup reduction per token; pre: per-wave
@@ -30,7 +36,7 @@
 // the caller's workspace, and summed over blocks by sum_rows_kernel in a
 // fixed order (64 rows per level), so every result is deterministic.
 //
-// Both kernels stream rows like the forward ones (one 16-byte vector per
+// The kernels stream rows like the forward ones (one 16-byte vector per
 // thread per stream, all loads of a token issued first).
 #include <mutex>
 
