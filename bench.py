@@ -57,7 +57,7 @@ KERNEL_SOURCES = {
     "post_mix_backward": "hc_backward.hip", "pre_mix_backward": "hc_backward.hip",
     "sum_records": "hc_backward.hip", "weights_backward": "hc_weights_bwd.hip",
     "weights_backward_stream": "hc_weights_bwd.hip", "post_pre_mix_backward": "hc_backward.hip",
-    "sinkhorn_backward": "hc_weights_bwd.hip",
+    "sinkhorn_backward": "hc_weights_bwd.hip", "pre_mix_records": "hc_backward.hip",
 }
 
 
@@ -137,11 +137,12 @@ XCDS = 8
 # the part of a kernel's name that picks it out of a trace (the boundary
 # kernel with and without the read-mix differ in the last template argument)
 KERNEL_TAGS = {"post_mix_backward": "post_bwd_kernel<", "pre_mix_backward": "pre_bwd_kernel<",
-               "post_pre_mix_backward": "post_pre_bwd_kernel<",
+               "post_pre_mix_backward": "post_pre_bwd_kernel<", "pre_mix_records": "pre_bwd_kernel<",
                "post_mix_weights": "post_weights_kernel<",
                "post_weights_pre_mix": "post_weights_kernel<",
                "weights_backward_stream": "wgrad_mfma_kernel<"}
-KERNEL_LAST_ARG = {"post_mix_weights": "false>", "post_weights_pre_mix": "true>"}
+KERNEL_LAST_ARG = {"post_mix_weights": "false>", "post_weights_pre_mix": "true>",
+                   "pre_mix_backward": "true>", "pre_mix_records": "false>"}
 
 
 def kernel_match(kernel: str, name: str) -> bool:
@@ -386,8 +387,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--fused", action="store_true",
                     help="fuse each write-back with the next read-mix (chain: every layer; "
-                         "static: one step is one fused layer boundary; static with --backward: "
-                         "one step is that boundary's gradient in one pass)")
+                         "static: one step is one fused layer boundary; with --backward (static, "
+                         "dynamic): one step is a layer boundary's gradient in one pass)")
     ap.add_argument("--backward", action="store_true",
                     help="time the layer's gradients: post backward (dF and its records), pre "
                          "backward forming the whole dH, shared-weight sums (static workloads); "
@@ -456,10 +457,10 @@ def main():
         run_all(args)
         return
     out, wl, inp = run_workload(args, args.workload)
-    if wl.kind == "static" and args.backward and not (args.fused or args.no_fold or args.graph):
+    if wl.kind in ("static", "dynamic") and args.backward and not (args.fused or args.no_fold or args.graph):
         # the same gradients at steady state in a stack of layers: one pass per
         # layer boundary, reported beside the layer's separate post and pre
-        # gradients
+        # (and weight producer) gradients
         import copy
         a = copy.copy(args)
         a.fused = True
@@ -563,6 +564,7 @@ def run_workload(args, name: str):
         "weights_backward": traffic.weights_bwd_bytes(n, d, s) * T,
         "post_pre_mix_backward": traffic.post_pre_bwd_bytes(n, d, s, per_tok) * T,
         "sinkhorn_backward": traffic.sinkhorn_bwd_bytes(n) * T,
+        "pre_mix_records": traffic.pre_records_bytes(n, d, s) * T,
     }
 
     if args.backward:
@@ -630,7 +632,31 @@ def run_workload(args, name: str):
                                 dw2=b["dwq"], saved=b["saved"])
 
         ops = [("post_mix_backward", post_bwd), ("pre_mix_backward", pre_bwd)]
-        if wl.kind == "dynamic":
+        if wl.kind == "dynamic" and args.fused:
+            # a layer at steady state in a stack, one pass per boundary: this
+            # layer's dalpha (its read-mix records, dH not formed), the weight
+            # producer's gradient added in place to the gradient arriving at
+            # this layer's streams (from the next boundary's call), then the
+            # boundary's gradient, which adds the read-mix's share itself and
+            # applies the previous layer's write-back gradient.  The next
+            # buffer set stands for this layer's streams and records, this set
+            # for the previous layer's.
+            for i, b in enumerate(bufs):
+                b["next"] = bufs[(i + 1) % sets]
+                b["dwq2"] = torch.empty((T, K), dtype=torch.float32, device="cuda")
+                b["dg2"] = torch.empty(d, dtype=torch.float32, device="cuda")
+            ops = [("pre_mix_records", lambda b: hc.pre_mix_backward(
+                       b["du"], b["next"]["H"], b["next"]["w"], gamma, wl.eps, h_grad=False,
+                       dw=b["dwq"], dgamma=b["dg"], workspace=b["ws"])),
+                   ("weights_backward", lambda b: hc.weights_backward(
+                       b["next"]["H"], Wp, ws, wl.scale, b["dwq"], wl.eps, 0, dH_in=b["G"],
+                       out=b["G"], dW=b["dW"], dw_static=b["dws"], workspace=b["wws"],
+                       dw2=b["next"]["dwp"], saved=b["next"]["saved"])),
+                   ("post_pre_mix_backward", lambda b: hc.post_pre_mix_backward(
+                       b["G"], b["du"], b["H"], b["F"], b["w"], b["next"]["w"], gamma, wl.eps,
+                       out=b["O"], dF=b["dF"], dw=b["dwp"], dw_next=b["dwq2"],
+                       dgamma_next=b["dg2"], workspace=b["ws"]))]
+        elif wl.kind == "dynamic":
             ops.append(("weights_backward", weights_bwd))
         elif wl.kind == "mhc":
             # the boundary's gradient in one pass, then the next layer's logit

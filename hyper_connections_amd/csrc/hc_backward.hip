@@ -331,7 +331,10 @@ __global__ __launch_bounds__(1024) void post_bwd_kernel(
 // into da_part[blk][N].  dH gets dH_in added (when given), or with FOLD the
 // write-back's H gradient sum_i A[i][j] dH'_i, formed here from dHo (the
 // gradient at the write-back's output) and the same record.
-template <int N, typename S, int VPT, bool PER_TOKEN, bool FOLD>
+// HG false: dH is not written (dH == NULL); the records and dgamma come out
+// bitwise as with it (per-token weights produced from H need dalpha before
+// the layer's dH can be formed).
+template <int N, typename S, int VPT, bool PER_TOKEN, bool FOLD, bool HG = true>
 __global__ __launch_bounds__(1024) void pre_bwd_kernel(
     const uint8_t* __restrict__ du, const uint8_t* __restrict__ H, const float* __restrict__ w,
     int64_t w_stride, const float* __restrict__ gamma, float eps, const uint8_t* dH_in,
@@ -465,6 +468,7 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
                                 da[i] = fmaf(dx[q * E + e], h[e], da[i]);
                                 o[e] = alpha[i] * dx[q * E + e];
                             }
+                            if constexpr (!HG) continue;
                             if (!FOLD && dH_in) {
                                 float p[E];
                                 unpack_word<S>(word(rin[i][j], q), p);
@@ -486,7 +490,8 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
                             }
                             oh[q] = pack_word<S>(o);
                         }
-                        st16_stream(dH + r0 + i * row_bytes + v * 16, make_uint4(oh[0], oh[1], oh[2], oh[3]));
+                        if constexpr (HG)
+                            st16_stream(dH + r0 + i * row_bytes + v * 16, make_uint4(oh[0], oh[1], oh[2], oh[3]));
                     }
                 }
             }
@@ -957,18 +962,18 @@ hipError_t post_bwd_go(RowCfg c, const void* dHo, const void* H, const void* F, 
               : post_bwd_go2<N, S, VPT, false>(c, dHo, H, F, w, ws, dH, dF, dw, part, T, d, group, s);
 }
 
-template <int N, typename S, int VPT, bool FOLD>
+template <int N, typename S, int VPT, bool FOLD, bool HG = true>
 hipError_t pre_bwd_go2(RowCfg c, const void* du, const void* H, const float* w, int64_t ws,
                        const float* gamma, float eps, const void* dH_in, const void* dHo, void* dH,
                        float* dw, float* dg_part, float* da_part, int64_t T, int d, int group,
                        hipStream_t s) {
     const dim3 grid = grid_of((T + group - 1) / group);
     if (ws != 0)
-        return launch(pre_bwd_kernel<N, S, VPT, true, FOLD>, grid, dim3(c.block), 0, s,
+        return launch(pre_bwd_kernel<N, S, VPT, true, FOLD, HG>, grid, dim3(c.block), 0, s,
                       static_cast<const uint8_t*>(du), static_cast<const uint8_t*>(H), w, ws, gamma,
                       eps, static_cast<const uint8_t*>(dH_in), static_cast<const uint8_t*>(dHo),
                       static_cast<uint8_t*>(dH), dw, dg_part, da_part, T, d, group);
-    return launch(pre_bwd_kernel<N, S, VPT, false, FOLD>, grid, dim3(c.block), 0, s,
+    return launch(pre_bwd_kernel<N, S, VPT, false, FOLD, HG>, grid, dim3(c.block), 0, s,
                   static_cast<const uint8_t*>(du), static_cast<const uint8_t*>(H), w, ws, gamma,
                   eps, static_cast<const uint8_t*>(dH_in), static_cast<const uint8_t*>(dHo),
                   static_cast<uint8_t*>(dH), dw, dg_part, da_part, T, d, group);
@@ -979,6 +984,9 @@ hipError_t pre_bwd_go(RowCfg c, const void* du, const void* H, const float* w, i
                       const float* gamma, float eps, const void* dH_in, const void* dHo, void* dH,
                       float* dw, float* dg_part, float* da_part, int64_t T, int d, int group,
                       hipStream_t s) {
+    if (!dH)   // records and dgamma only (no addend: the API checks)
+        return pre_bwd_go2<N, S, VPT, false, false>(c, du, H, w, ws, gamma, eps, nullptr, nullptr,
+                                                    nullptr, dw, dg_part, da_part, T, d, group, s);
     return dHo ? pre_bwd_go2<N, S, VPT, true>(c, du, H, w, ws, gamma, eps, dH_in, dHo, dH, dw, dg_part,
                                                da_part, T, d, group, s)
                : pre_bwd_go2<N, S, VPT, false>(c, du, H, w, ws, gamma, eps, dH_in, dHo, dH, dw, dg_part,

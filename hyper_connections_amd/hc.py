@@ -486,13 +486,14 @@ def post_mix_backward_noalloc(dH_out, H, F, w, dH=None, dF=None, dw=None, stream
 
 @_on_launch_stream
 def pre_mix_backward(du, H, w, gamma, eps: float = 1e-6, dH_in=None, out=None, dw=None,
-                     dgamma=None, workspace=None, stream=None, dH_out=None):
+                     dgamma=None, workspace=None, stream=None, dH_out=None, h_grad=True):
     """Gradients of pre_mix: returns (dH, dw, dgamma).  dH includes dH_in when
     given (``out=dH_in`` accumulates in place), or, given dH_out (the
     gradient at post_mix's output, after post_mix_backward(h_grad=False)),
     the write-back's H gradient formed from it and the same records; dw has
     the shape of the weights ([dalpha | 0 | 0]); dgamma is summed over
-    tokens.  Output buffers and the workspace may be passed in."""
+    tokens.  h_grad=False computes dw and dgamma only (dH is None; no
+    addend).  Output buffers and the workspace may be passed in."""
     T, n, d, K = _H(H)
     ws = _record(w, T, K)
     _dev(du, "du")
@@ -508,9 +509,14 @@ def pre_mix_backward(du, H, w, gamma, eps: float = 1e-6, dH_in=None, out=None, d
             _dev(x, name)
             if x.dtype != H.dtype or x.shape != H.shape:
                 raise ValueError(f"{name} must match H")
-    dH = torch.empty_like(H) if out is None else _dev(out, "out")
-    if dH.dtype != H.dtype or dH.shape != H.shape:
-        raise ValueError("out must match H")
+    if h_grad:
+        dH = torch.empty_like(H) if out is None else _dev(out, "out")
+        if dH.dtype != H.dtype or dH.shape != H.shape:
+            raise ValueError("out must match H")
+    else:
+        if dH_in is not None or dH_out is not None or out is not None:
+            raise ValueError("h_grad=False takes no dH_in, dH_out or out")
+        dH = None
     dw = _grad_record(dw, T, K, ws, H.device)
     dg = torch.empty(d, dtype=torch.float32, device=H.device) if dgamma is None else _dev(dgamma, "dgamma")
     if dg.dtype != torch.float32 or tuple(dg.shape) != (d,):
@@ -518,7 +524,8 @@ def pre_mix_backward(du, H, w, gamma, eps: float = 1e-6, dH_in=None, out=None, d
     wk, wkb = _workspace(workspace, T, n, d, H.device)
     _call("hc_pre_mix_backward", du.data_ptr(), H.data_ptr(), w.data_ptr(), ws, gamma.data_ptr(),
           float(eps), dH_in.data_ptr() if dH_in is not None else None,
-          dH_out.data_ptr() if dH_out is not None else None, dH.data_ptr(),
+          dH_out.data_ptr() if dH_out is not None else None,
+          dH.data_ptr() if dH is not None else None,
           dw.data_ptr(), dg.data_ptr(), wk.data_ptr(), wkb, T, n, d, _dt(H), _stream(stream))
     return dH, dw, dg
 

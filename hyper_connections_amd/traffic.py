@@ -119,6 +119,12 @@ def sinkhorn_bwd_bytes(n: int, two_gradients: bool = True) -> int:
     return (4 if two_gradients else 3) * record_bytes(n)
 
 
+def pre_records_bytes(n: int, d: int, s: int) -> int:
+    """The read-mix's record gradient alone (dH not formed): read du and H,
+    write one gradient record."""
+    return (n + 1) * d * s + record_bytes(n)
+
+
 def weights_bwd_bytes(n: int, d: int, s: int) -> int:
     """Gradient of the per-token weights: read H, read the incoming dH and
     write dH once each, plus two gradient records read (from pre and post).

@@ -281,7 +281,10 @@ hc_status hc_post_mix_backward_noalloc(const void* dH_out, const void* H, const 
  *     gradient sum_j A[j][i] dH_out_j (A from the same records w) is then
  *     formed here and added to dH before its one rounding.  At most one of
  *     dH_in and dH_out (both: HC_ERR_ARG).
- *   dH [T][n][d] dt
+ *   dH [T][n][d] dt, or NULL: then only dw and dgamma are computed (bitwise
+ *     the same as with dH), and dH_in and dH_out must be NULL (HC_ERR_ARG):
+ *     for weights produced from H, whose gradient needs dalpha before the
+ *     layer's dH is formed
  *   dw fp32, the shape of the weights: [dalpha | 0 | 0] summed over tokens
  *     when w_stride == 0, else [T][K] per token
  *   dgamma [d] fp32, summed over tokens in a fixed order (deterministic)

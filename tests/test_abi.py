@@ -155,6 +155,9 @@ def test_backward_validation(L):
     assert qb(din=P[0], dout=P[1]) == ARG and qb(din=P[0], dout=P[1], T=0) == ARG
     assert qb(dout=P[0] + 8) == ALIGN and qb(dout=P[4]) == ALIAS and qb(dout=P[5] + 64) == ALIAS
     assert qb(dout=P[7]) == ALIAS
+    # dH NULL: records and dgamma only, so no addend may be given
+    assert qb(dH=None, din=P[0] + 64) == ARG and qb(dH=None, dout=P[1] + 64) == ARG
+    assert qb(dH=None, T=0) == OK and qb(dH=None, dg=None) == NULL
     assert L.hc_sum_records(P[0], 10, 0, P[1], None) == SHAPE
     assert L.hc_sum_records(P[0], -1, 24, P[1], None) == ARG
     assert L.hc_sum_records(P[0], 10, 24, P[0] + 8, None) == ALIAS

@@ -135,6 +135,17 @@ def test_backward_fold_parity(dt, d, n):
     assert np.array_equal(host(dwq), host(dwq0)) and np.array_equal(host(dg), host(dg0))
 
 
+@pytest.mark.parametrize("per_token", [False, True])
+def test_pre_backward_records_only(per_token):
+    """dH = NULL: the records and dgamma alone, bitwise those of the full call."""
+    rng = np.random.default_rng(6 + per_token)
+    H, F, G, du, w, g = case(rng, "bf16", 300, 4, 4096, per_token=per_token)
+    dH, dw, dg = hc.pre_mix_backward(dev(du), dev(H), dev(w), dev(g), 1e-6, h_grad=False)
+    assert dH is None
+    _, dw0, dg0 = hc.pre_mix_backward(dev(du), dev(H), dev(w), dev(g), 1e-6)
+    assert np.array_equal(host(dw), host(dw0)) and np.array_equal(host(dg), host(dg0))
+
+
 def test_pre_backward_accumulates_in_place():
     rng = np.random.default_rng(3)
     H, F, G, du, w, g = case(rng, "bf16", 17, 4, 4096, per_token=True)
