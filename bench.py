@@ -634,7 +634,8 @@ def run_workload(args, name: str):
         ops = [("post_mix_backward", post_bwd), ("pre_mix_backward", pre_bwd)]
         if wl.kind == "dynamic" and args.fused:
             # a layer at steady state in a stack, one pass per boundary: this
-            # layer's dalpha (its read-mix records, dH not formed), the weight
+            # layer's dalpha (its read-mix records, dH and dgamma not formed:
+            # the boundary's call forms dgamma), the weight
             # producer's gradient added in place to the gradient arriving at
             # this layer's streams (from the next boundary's call), then the
             # boundary's gradient, which adds the read-mix's share itself and
@@ -647,7 +648,7 @@ def run_workload(args, name: str):
                 b["dg2"] = torch.empty(d, dtype=torch.float32, device="cuda")
             ops = [("pre_mix_records", lambda b: hc.pre_mix_backward(
                        b["du"], b["next"]["H"], b["next"]["w"], gamma, wl.eps, h_grad=False,
-                       dw=b["dwq"], dgamma=b["dg"], workspace=b["ws"])),
+                       g_grad=False, dw=b["dwq"], workspace=b["ws"])),
                    ("weights_backward", lambda b: hc.weights_backward(
                        b["next"]["H"], Wp, ws, wl.scale, b["dwq"], wl.eps, 0, dH_in=b["G"],
                        out=b["G"], dW=b["dW"], dw_static=b["dws"], workspace=b["wws"],

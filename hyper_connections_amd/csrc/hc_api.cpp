@@ -390,7 +390,8 @@ hc_status hc_pre_mix_backward(const void* du, const void* H, const float* w, int
     if (dH_in && dH_out) return HC_ERR_ARG;     // at most one addend
     if (!dH && (dH_in || dH_out)) return HC_ERR_ARG;   // an addend needs the dH it adds into
     if (T == 0) return HC_OK;
-    if (!du || !H || !w || !gamma || !dw || !dgamma || !workspace) return HC_ERR_NULL;
+    if (!du || !H || !w || !gamma || !dw || !workspace) return HC_ERR_NULL;
+    if (!dgamma && dH) return HC_ERR_NULL;             // dgamma may be left out only with dH
     if (workspace_bytes < hc_backward_workspace(T, n, d)) return HC_ERR_ARG;
     if (misaligned(du, 16) || misaligned(H, 16) || misaligned(gamma, 16) || misaligned(dH, 16) ||
         misaligned(dH_in, 16) || misaligned(dH_out, 16) || misaligned(workspace, 16) ||
@@ -401,7 +402,7 @@ hc_status hc_pre_mix_backward(const void* du, const void* H, const float* w, int
     const Span su{du, T * d * s}, sH{H, T * n * d * s}, sW{w, record_span(T, w_stride, K)},
         sg{gamma, int64_t(d) * 4}, sin{dH_in, dH_in ? T * n * d * s : 0},
         sdH{dH, dH ? T * n * d * s : 0},
-        sdw{dw, (shared ? 1 : T) * K * 4}, sdg{dgamma, int64_t(d) * 4},
+        sdw{dw, (shared ? 1 : T) * K * 4}, sdg{dgamma, dgamma ? int64_t(d) * 4 : 0},
         sws{workspace, hc_backward_workspace(T, n, d)},
         sout{dH_out, dH_out ? T * n * d * s : 0};
     const Span ins[] = {su, sH, sW, sg, sout};

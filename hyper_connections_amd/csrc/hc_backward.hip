@@ -510,11 +510,12 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
                 for (int i = 0; i < N; ++i) dab[i] += da[i];
             }
         }
-        // the block's partials: dgamma of its columns, dalpha (shared record)
+        // the block's partials: dgamma of its columns (unless not asked for),
+        // dalpha (shared record)
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
             const int v = threadIdx.x + j * B;
-            if (v < nvec) {
+            if (v < nvec && dg_part) {
 #pragma unroll
                 for (int q = 0; q < V / 4; ++q)
                     st16(dg_part + blk * (int64_t)d + v * V + 4 * q,
@@ -1210,8 +1211,12 @@ hipError_t launch_pre_mix_backward(const void* du, const void* H, const float* w
                                    int d, int dt, hipStream_t s) {
     const BwdSpace sp = bwd_space(T, n, d);
     float* ws = static_cast<float*>(work);
-    const int group = (int)group_of(T);
-    float* dg_part = ws + sp.dg;
+    // dalpha alone with per-token records (no dH, no dgamma): no per-block
+    // row of partials to keep, so one token per workgroup, as the forward
+    // read-mix runs
+    const bool alone = !dgamma && w_stride != 0;
+    const int group = alone ? 1 : (int)group_of(T);
+    float* dg_part = dgamma ? ws + sp.dg : nullptr;
     // dalpha: per-workgroup partials (shared record), or per token and wave
     float* da_part = w_stride != 0 ? ws + sp.wp : ws + sp.rec;
     hipError_t e =
@@ -1232,6 +1237,8 @@ hipError_t launch_pre_mix_backward(const void* du, const void* H, const float* w
     // 0 (dbeta, dA)], in the same launches
     const SumJob jobs[2] = {{dg_part, sp.rows, d, ws + sp.tmp, dgamma, nullptr, 0},
                             {da_part, sp.rows, n, ws + sp.tmp2, dw, dw + n, K - n}};
+    if (!dgamma)
+        return w_stride != 0 ? hipSuccess : launch_sum_rows(jobs + 1, 1, s);
     return launch_sum_rows(jobs, w_stride != 0 ? 1 : 2, s);
 }
 

@@ -486,14 +486,16 @@ def post_mix_backward_noalloc(dH_out, H, F, w, dH=None, dF=None, dw=None, stream
 
 @_on_launch_stream
 def pre_mix_backward(du, H, w, gamma, eps: float = 1e-6, dH_in=None, out=None, dw=None,
-                     dgamma=None, workspace=None, stream=None, dH_out=None, h_grad=True):
+                     dgamma=None, workspace=None, stream=None, dH_out=None, h_grad=True,
+                     g_grad=True):
     """Gradients of pre_mix: returns (dH, dw, dgamma).  dH includes dH_in when
     given (``out=dH_in`` accumulates in place), or, given dH_out (the
     gradient at post_mix's output, after post_mix_backward(h_grad=False)),
     the write-back's H gradient formed from it and the same records; dw has
     the shape of the weights ([dalpha | 0 | 0]); dgamma is summed over
     tokens.  h_grad=False computes dw and dgamma only (dH is None; no
-    addend).  Output buffers and the workspace may be passed in."""
+    addend); with g_grad=False as well, dw alone (dgamma is None).  Output
+    buffers and the workspace may be passed in."""
     T, n, d, K = _H(H)
     ws = _record(w, T, K)
     _dev(du, "du")
@@ -518,15 +520,21 @@ def pre_mix_backward(du, H, w, gamma, eps: float = 1e-6, dH_in=None, out=None, d
             raise ValueError("h_grad=False takes no dH_in, dH_out or out")
         dH = None
     dw = _grad_record(dw, T, K, ws, H.device)
-    dg = torch.empty(d, dtype=torch.float32, device=H.device) if dgamma is None else _dev(dgamma, "dgamma")
-    if dg.dtype != torch.float32 or tuple(dg.shape) != (d,):
-        raise ValueError(f"dgamma must be float32 of shape ({d},)")
+    if not g_grad and h_grad:
+        raise ValueError("g_grad=False needs h_grad=False")
+    if g_grad:
+        dg = torch.empty(d, dtype=torch.float32, device=H.device) if dgamma is None else _dev(dgamma, "dgamma")
+        if dg.dtype != torch.float32 or tuple(dg.shape) != (d,):
+            raise ValueError(f"dgamma must be float32 of shape ({d},)")
+    else:
+        dg = None
     wk, wkb = _workspace(workspace, T, n, d, H.device)
     _call("hc_pre_mix_backward", du.data_ptr(), H.data_ptr(), w.data_ptr(), ws, gamma.data_ptr(),
           float(eps), dH_in.data_ptr() if dH_in is not None else None,
           dH_out.data_ptr() if dH_out is not None else None,
           dH.data_ptr() if dH is not None else None,
-          dw.data_ptr(), dg.data_ptr(), wk.data_ptr(), wkb, T, n, d, _dt(H), _stream(stream))
+          dw.data_ptr(), dg.data_ptr() if dg is not None else None, wk.data_ptr(), wkb, T, n, d,
+          _dt(H), _stream(stream))
     return dH, dw, dg
 
 

@@ -120,8 +120,8 @@ def sinkhorn_bwd_bytes(n: int, two_gradients: bool = True) -> int:
 
 
 def pre_records_bytes(n: int, d: int, s: int) -> int:
-    """The read-mix's record gradient alone (dH not formed): read du and H,
-    write one gradient record."""
+    """The read-mix's record gradient alone (dH and dgamma not formed): read
+    du and H, write one gradient record."""
     return (n + 1) * d * s + record_bytes(n)
 
 

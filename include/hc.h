@@ -284,7 +284,9 @@ hc_status hc_post_mix_backward_noalloc(const void* dH_out, const void* H, const 
  *   dH [T][n][d] dt, or NULL: then only dw and dgamma are computed (bitwise
  *     the same as with dH), and dH_in and dH_out must be NULL (HC_ERR_ARG):
  *     for weights produced from H, whose gradient needs dalpha before the
- *     layer's dH is formed
+ *     layer's dH is formed.  With dH NULL, dgamma may be NULL too (dalpha
+ *     alone: hc_post_pre_mix_backward forms dgamma at the same boundary);
+ *     dgamma NULL with dH given is HC_ERR_NULL
  *   dw fp32, the shape of the weights: [dalpha | 0 | 0] summed over tokens
  *     when w_stride == 0, else [T][K] per token
  *   dgamma [d] fp32, summed over tokens in a fixed order (deterministic)

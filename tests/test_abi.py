@@ -157,7 +157,8 @@ def test_backward_validation(L):
     assert qb(dout=P[7]) == ALIAS
     # dH NULL: records and dgamma only, so no addend may be given
     assert qb(dH=None, din=P[0] + 64) == ARG and qb(dH=None, dout=P[1] + 64) == ARG
-    assert qb(dH=None, T=0) == OK and qb(dH=None, dg=None) == NULL
+    assert qb(dH=None, T=0) == OK and qb(dg=None) == NULL   # dgamma left out only with dH
+    assert qb(dH=None, dg=None, wk=None) == NULL
     assert L.hc_sum_records(P[0], 10, 0, P[1], None) == SHAPE
     assert L.hc_sum_records(P[0], -1, 24, P[1], None) == ARG
     assert L.hc_sum_records(P[0], 10, 24, P[0] + 8, None) == ALIAS

@@ -144,6 +144,16 @@ def test_pre_backward_records_only(per_token):
     assert dH is None
     _, dw0, dg0 = hc.pre_mix_backward(dev(du), dev(H), dev(w), dev(g), 1e-6)
     assert np.array_equal(host(dw), host(dw0)) and np.array_equal(host(dg), host(dg0))
+    # dalpha alone (no dgamma): one token per workgroup for per-token
+    # records; the same sums per token and wave, so the same bits
+    _, dw1, dg1 = hc.pre_mix_backward(dev(du), dev(H), dev(w), dev(g), 1e-6, h_grad=False,
+                                      g_grad=False)
+    assert dg1 is None
+    if per_token:
+        assert np.array_equal(host(dw1), host(dw0))
+    else:
+        rdw = oracle.pre_mix_backward(du, H, w.astype(np.float64), g, 1e-6)[1].sum(axis=0)
+        dalpha_check(host(dw1), rdw, du, H, w, g, 1e-6, "pre dalpha alone")
 
 
 def test_pre_backward_accumulates_in_place():
