@@ -272,7 +272,8 @@ def summarize_counters(fetch_csv: str, write_csv: str, kernel: str, workload: st
            "post_mix_backward": tr.post_bwd_bytes(wl.n, wl.d, wl.elem_bytes, h_grad=not fold),
            "pre_mix_backward": tr.pre_bwd_bytes(wl.n, wl.d, wl.elem_bytes, True),
            "weights_backward": tr.weights_bwd_bytes(wl.n, wl.d, wl.elem_bytes),
-           "post_pre_mix_backward": tr.post_pre_bwd_bytes(wl.n, wl.d, wl.elem_bytes),
+           "post_pre_mix_backward": tr.post_pre_bwd_bytes(wl.n, wl.d, wl.elem_bytes, per_tok),
+           "pre_mix_records": tr.pre_records_bytes(wl.n, wl.d, wl.elem_bytes),
            "weights_backward_stream": tr.weights_bwd_stream_bytes(wl.n, wl.d, wl.elem_bytes)}[kernel] * wl.T
     rec = {"kernel": kernel, "workload": workload, "source_sha": source_sha(kernel),
            "dispatches": {"FETCH_SIZE": len(fk), "WRITE_SIZE": len(wk)},
