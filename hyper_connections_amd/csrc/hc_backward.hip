@@ -551,7 +551,7 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
 //   dgamma = sum_t du x r.
 // Rows per token: H, F, dHo and du in, dH and dF out (3n + 3), against
 // 5n + 3 for post_bwd_kernel without dH followed by pre_bwd_kernel with the
-// fold, which read H twice and read dHo twice.
+// fold, which also read the stored H' and read dHo twice.
 //
 // Record partials come in record order [dalpha | dbeta | dA] (K values).
 // PER_TOKEN: per token and wave, rpart[t][wave][K], added in wave order by
