@@ -50,3 +50,23 @@ def test_committed_drift_summary_is_within_its_bound():
     assert len(rec["rows"]) == rec["layers"] == 78
     drift = [r["drift_vs_bf16_storing_fp64"] for r in rec["rows"]]
     assert max(drift) == rec["max_drift_vs_bf16_storing_fp64"] <= rec["drift_bound"]
+
+
+def test_kernel_match_tells_the_kernels_apart():
+    """Trace and counter rows are attributed by the whole kernel identifier
+    and, where one template serves two entry points, its last argument."""
+    ns = "void hc::(anonymous namespace)::"
+    tail = "(unsigned char const*, float const*)"
+    names = {
+        "pre_mix_backward": ns + "pre_bwd_kernel<4, hc::bf16_t, 1, true, true, true>" + tail,
+        "pre_mix_records": ns + "pre_bwd_kernel<4, hc::bf16_t, 1, true, false, false>" + tail,
+        "post_pre_mix_backward": ns + "post_pre_bwd_kernel<4, hc::bf16_t, 1, false>" + tail,
+        "post_mix_backward": ns + "post_bwd_kernel<4, hc::bf16_t, 1, false, false>" + tail,
+        "pre_mix": ns + "pre_mix_kernel<4, hc::bf16_t, 1>" + tail,
+        "post_pre_mix": ns + "post_pre_mix_kernel<4, hc::bf16_t, 1>" + tail,
+        "post_weights_pre_mix": ns + "post_weights_kernel<4, hc::bf16_t, 4, 1, true, true>" + tail,
+        "post_mix_weights": ns + "post_weights_kernel<4, hc::bf16_t, 4, 1, true, false>" + tail,
+    }
+    for kernel, name in names.items():
+        hits = [k for k in names if bench.kernel_match(k, name)]
+        assert hits == [kernel], (kernel, hits)
