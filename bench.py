@@ -58,6 +58,9 @@ KERNEL_SOURCES = {
     "sum_records": "hc_backward.hip", "weights_backward": "hc_weights_bwd.hip",
     "weights_backward_stream": "hc_weights_bwd.hip", "post_pre_mix_backward": "hc_backward.hip",
     "sinkhorn_backward": "hc_weights_bwd.hip", "pre_mix_records": "hc_backward.hip",
+    "weights_backward_terms": "hc_weights_bwd.hip",
+    "weights_backward_terms_stream": "hc_weights_bwd.hip",
+    "post_pre_mix_backward_terms": "hc_backward.hip",
 }
 
 
@@ -140,9 +143,13 @@ KERNEL_TAGS = {"post_mix_backward": "post_bwd_kernel<", "pre_mix_backward": "pre
                "post_pre_mix_backward": "post_pre_bwd_kernel<", "pre_mix_records": "pre_bwd_kernel<",
                "post_mix_weights": "post_weights_kernel<",
                "post_weights_pre_mix": "post_weights_kernel<",
-               "weights_backward_stream": "wgrad_mfma_kernel<"}
+               "weights_backward_stream": "wgrad_mfma_kernel<",
+               "weights_backward_terms_stream": "wgrad_mfma_kernel<",
+               "post_pre_mix_backward_terms": "post_pre_bwd_kernel<"}
 KERNEL_LAST_ARG = {"post_mix_weights": "false>", "post_weights_pre_mix": "true>",
-                   "pre_mix_backward": "true>", "pre_mix_records": "false>"}
+                   "pre_mix_backward": "true>", "pre_mix_records": "false>",
+                   "post_pre_mix_backward": "false>", "post_pre_mix_backward_terms": "true>",
+                   "weights_backward_stream": "false>", "weights_backward_terms_stream": "true>"}
 
 
 def kernel_match(kernel: str, name: str) -> bool:
@@ -274,7 +281,10 @@ def summarize_counters(fetch_csv: str, write_csv: str, kernel: str, workload: st
            "weights_backward": tr.weights_bwd_bytes(wl.n, wl.d, wl.elem_bytes),
            "post_pre_mix_backward": tr.post_pre_bwd_bytes(wl.n, wl.d, wl.elem_bytes, per_tok),
            "pre_mix_records": tr.pre_records_bytes(wl.n, wl.d, wl.elem_bytes),
-           "weights_backward_stream": tr.weights_bwd_stream_bytes(wl.n, wl.d, wl.elem_bytes)}[kernel] * wl.T
+           "weights_backward_stream": tr.weights_bwd_stream_bytes(wl.n, wl.d, wl.elem_bytes),
+           "post_pre_mix_backward_terms": tr.post_pre_bwd_terms_bytes(wl.n, wl.d, wl.elem_bytes),
+           # the stream pass of the factors' form: read H, write dhbar
+           "weights_backward_terms_stream": wl.n * wl.d * wl.elem_bytes + 4 * wl.d}[kernel] * wl.T
     rec = {"kernel": kernel, "workload": workload, "source_sha": source_sha(kernel),
            "dispatches": {"FETCH_SIZE": len(fk), "WRITE_SIZE": len(wk)},
            "fetch_kib_per_dispatch": round(fetch_kib, 3), "write_kib_per_dispatch": round(write_kib, 3),
@@ -398,6 +408,10 @@ def main():
                     help="with --backward: post backward writes its H gradient and the pre "
                          "backward adds into it (by default post leaves dH to the pre backward, "
                          "which forms the write-back's share from dH' itself)")
+    ap.add_argument("--no-terms", action="store_true",
+                    help="dynamic --backward --fused: add the weight producer's gradient in place "
+                         "to the gradient arriving at the layer's streams (by default the producer "
+                         "returns dhbar and its coefficients and the boundary's call adds them)")
     ap.add_argument("--weights-pass", action="store_true",
                     help="dynamic workloads: a separate weights kernel reads H before pre and "
                          "post (by default one kernel per layer boundary: the write-back, the "
@@ -566,6 +580,8 @@ def run_workload(args, name: str):
         "post_pre_mix_backward": traffic.post_pre_bwd_bytes(n, d, s, per_tok) * T,
         "sinkhorn_backward": traffic.sinkhorn_bwd_bytes(n) * T,
         "pre_mix_records": traffic.pre_records_bytes(n, d, s) * T,
+        "weights_backward_terms": traffic.weights_bwd_terms_bytes(n, d, s) * T,
+        "post_pre_mix_backward_terms": traffic.post_pre_bwd_terms_bytes(n, d, s) * T,
     }
 
     if args.backward:
@@ -647,6 +663,26 @@ def run_workload(args, name: str):
                 b["next"] = bufs[(i + 1) % sets]
                 b["dwq2"] = torch.empty((T, K), dtype=torch.float32, device="cuda")
                 b["dg2"] = torch.empty(d, dtype=torch.float32, device="cuda")
+                if not args.no_terms:
+                    b["dhb"] = torch.empty((T, d), dtype=torch.float32, device="cuda")
+                    b["coef"] = torch.empty((T, 2 * n), dtype=torch.float32, device="cuda")
+            if not args.no_terms:
+                # the weight producer's gradient as its two factors (dhbar and
+                # per-token coefficients), added at H' by the boundary's call,
+                # instead of being added in place to the gradient arriving at
+                # this layer's streams: 28 rows per token instead of 32
+                ops = [("pre_mix_records", lambda b: hc.pre_mix_backward(
+                           b["du"], b["next"]["H"], b["next"]["w"], gamma, wl.eps, h_grad=False,
+                           g_grad=False, dw=b["dwq"], workspace=b["ws"])),
+                       ("weights_backward_terms", lambda b: hc.weights_backward_terms(
+                           b["next"]["H"], Wp, ws, wl.scale, b["dwq"], wl.eps, 0, dhbar=b["dhb"],
+                           coef=b["coef"], dW=b["dW"], dw_static=b["dws"], workspace=b["wws"],
+                           dw2=b["next"]["dwp"], saved=b["next"]["saved"])),
+                       ("post_pre_mix_backward_terms", lambda b: hc.post_pre_mix_backward(
+                           b["G"], b["du"], b["H"], b["F"], b["w"], b["next"]["w"], gamma, wl.eps,
+                           out=b["O"], dF=b["dF"], dw=b["dwp"], dw_next=b["dwq2"],
+                           dgamma_next=b["dg2"], workspace=b["ws"], terms=(b["dhb"], b["coef"])))]
+        if wl.kind == "dynamic" and args.fused and args.no_terms:
             ops = [("pre_mix_records", lambda b: hc.pre_mix_backward(
                        b["du"], b["next"]["H"], b["next"]["w"], gamma, wl.eps, h_grad=False,
                        g_grad=False, dw=b["dwq"], workspace=b["ws"])),
@@ -658,6 +694,8 @@ def run_workload(args, name: str):
                        b["G"], b["du"], b["H"], b["F"], b["w"], b["next"]["w"], gamma, wl.eps,
                        out=b["O"], dF=b["dF"], dw=b["dwp"], dw_next=b["dwq2"],
                        dgamma_next=b["dg2"], workspace=b["ws"]))]
+        elif wl.kind == "dynamic" and args.fused:
+            pass
         elif wl.kind == "dynamic":
             ops.append(("weights_backward", weights_bwd))
         elif wl.kind == "mhc":
@@ -866,7 +904,9 @@ def run_workload(args, name: str):
                    "layers": wl.layers, "buffer_sets": sets, "fused": bool(args.fused),
                    "graph": bool(args.graph), "backward": bool(args.backward),
                    "fold": fold, "weights_pass": bool(args.weights_pass),
-                   "two_pass": bool(args.two_pass)},
+                   "two_pass": bool(args.two_pass),
+                   "terms": bool(wl.kind == "dynamic" and args.backward and args.fused
+                                 and not args.no_terms)},
         "us_per_layer": round(ms_step * 1e3 / wl.layers, 3),
         # what the step's kernels move (algorithmic: every input read once,
         # every output written once), per step and per second

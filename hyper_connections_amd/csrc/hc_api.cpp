@@ -95,7 +95,7 @@ const char* hc_status_str(hc_status status) {
     return "HC_ERR_UNKNOWN: unknown status code";
 }
 
-int32_t hc_abi_version(void) { return 7; }
+int32_t hc_abi_version(void) { return 8; }
 
 hc_status hc_pre_mix(const void* H, const float* w, int64_t w_stride, const float* gamma, float eps,
                      void* u, int64_t T, int32_t n, int32_t d, hc_dtype dt_arg, void* stream) {
@@ -420,14 +420,17 @@ hc_status hc_pre_mix_backward(const void* du, const void* H, const float* w, int
                                                 static_cast<hipStream_t>(stream)));
 }
 
-hc_status hc_post_pre_mix_backward(const void* dH_out, const void* du_next, const void* H,
-                                   const void* F, const float* w, int64_t w_stride,
-                                   const float* w_next, int64_t w_next_stride,
-                                   const float* gamma_next, float eps, void* dH, void* dF, float* dw,
-                                   float* dw_next, float* dgamma_next, void* workspace,
-                                   int64_t workspace_bytes, int64_t T, int32_t n, int32_t d,
-                                   hc_dtype dt_arg, void* stream) {
-    const int dt = enum_value(dt_arg);
+namespace {
+
+// hc_post_pre_mix_backward, and with the weight producer's terms (dhbar and
+// coef not NULL: per-token records only) hc_post_pre_mix_backward_terms.
+hc_status post_pre_backward(const void* dH_out, const void* du_next, const void* H, const void* F,
+                            const float* w, int64_t w_stride, const float* w_next,
+                            int64_t w_next_stride, const float* gamma_next, float eps, void* dH,
+                            void* dF, float* dw, float* dw_next, float* dgamma_next,
+                            const float* dhbar, const float* coef, bool terms, void* workspace,
+                            int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, int dt,
+                            void* stream) {
     if (!dtype_wide(dt)) return HC_ERR_DTYPE;
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
@@ -435,11 +438,14 @@ hc_status hc_post_pre_mix_backward(const void* dH_out, const void* du_next, cons
     if ((st = check_stride(w_stride, K, T)) != HC_OK) return st;
     if ((st = check_stride(w_next_stride, K, T)) != HC_OK) return st;
     if (w_stride != w_next_stride) return HC_ERR_ARG;   // both shared or both per token
+    if (terms && w_stride == 0) return HC_ERR_ARG;     // the producer's records are per token
     if (!eps_ok(eps)) return HC_ERR_ARG;
     if (T == 0) return HC_OK;
     if (!dH_out || !du_next || !H || !F || !w || !w_next || !gamma_next || !dH || !dF || !dw ||
         !dw_next || !dgamma_next || !workspace)
         return HC_ERR_NULL;
+    if (terms && (!dhbar || !coef)) return HC_ERR_NULL;
+    if (misaligned(dhbar, 16) || misaligned(coef, 4)) return HC_ERR_ALIGN;
     if (workspace_bytes < hc_backward_workspace(T, n, d)) return HC_ERR_ARG;
     if (misaligned(dH_out, 16) || misaligned(du_next, 16) || misaligned(H, 16) ||
         misaligned(F, 16) || misaligned(gamma_next, 16) || misaligned(dH, 16) ||
@@ -454,15 +460,16 @@ hc_status hc_post_pre_mix_backward(const void* dH_out, const void* du_next, cons
         sW2{w_next, record_span(T, w_next_stride, K)}, sg{gamma_next, int64_t(d) * 4},
         sdH{dH, T * n * d * s}, sdF{dF, T * d * s}, sdw{dw, (shared ? 1 : T) * K * 4},
         sdw2{dw_next, (shared ? 1 : T) * K * 4}, sdg{dgamma_next, int64_t(d) * 4},
-        sws{workspace, hc_backward_workspace(T, n, d)};
+        sws{workspace, hc_backward_workspace(T, n, d)},
+        sdb{dhbar, terms ? T * d * 4 : 0}, sco{coef, terms ? T * 2 * n * 4 : 0};
     // dH == dH_out is allowed (every element is read before the same thread
     // writes it); any other overlap of an output is an error
     if (dH != dH_out && overlap(sdH, sO)) return HC_ERR_ALIAS;
-    for (const Span& i : {su, sH, sF, sW, sW2, sg})
+    for (const Span& i : {su, sH, sF, sW, sW2, sg, sdb, sco})
         if (overlap(sdH, i)) return HC_ERR_ALIAS;
     const Span outs[] = {sdF, sdw, sdw2, sdg, sws};
     for (const Span& o : outs) {
-        for (const Span& i : {sO, su, sH, sF, sW, sW2, sg, sdH})
+        for (const Span& i : {sO, su, sH, sF, sW, sW2, sg, sdH, sdb, sco})
             if (overlap(o, i)) return HC_ERR_ALIAS;
     }
     for (int a = 0; a < 5; ++a)
@@ -471,7 +478,36 @@ hc_status hc_post_pre_mix_backward(const void* dH_out, const void* du_next, cons
     return from_hip(hc::launch_post_pre_mix_backward(dH_out, du_next, H, F, w, w_next, w_stride,
                                                      gamma_next, eps, dH, dF, dw, dw_next,
                                                      dgamma_next, workspace, T, n, d, dt,
-                                                     static_cast<hipStream_t>(stream)));
+                                                     static_cast<hipStream_t>(stream),
+                                                     terms ? dhbar : nullptr,
+                                                     terms ? coef : nullptr));
+}
+
+}  // namespace
+
+hc_status hc_post_pre_mix_backward(const void* dH_out, const void* du_next, const void* H,
+                                   const void* F, const float* w, int64_t w_stride,
+                                   const float* w_next, int64_t w_next_stride,
+                                   const float* gamma_next, float eps, void* dH, void* dF, float* dw,
+                                   float* dw_next, float* dgamma_next, void* workspace,
+                                   int64_t workspace_bytes, int64_t T, int32_t n, int32_t d,
+                                   hc_dtype dt, void* stream) {
+    return post_pre_backward(dH_out, du_next, H, F, w, w_stride, w_next, w_next_stride, gamma_next,
+                             eps, dH, dF, dw, dw_next, dgamma_next, nullptr, nullptr, false,
+                             workspace, workspace_bytes, T, n, d, enum_value(dt), stream);
+}
+
+hc_status hc_post_pre_mix_backward_terms(const void* dH_out, const void* du_next, const void* H,
+                                         const void* F, const float* w, int64_t w_stride,
+                                         const float* w_next, int64_t w_next_stride,
+                                         const float* gamma_next, float eps, const float* dhbar,
+                                         const float* coef, void* dH, void* dF, float* dw,
+                                         float* dw_next, float* dgamma_next, void* workspace,
+                                         int64_t workspace_bytes, int64_t T, int32_t n, int32_t d,
+                                         hc_dtype dt, void* stream) {
+    return post_pre_backward(dH_out, du_next, H, F, w, w_stride, w_next, w_next_stride, gamma_next,
+                             eps, dH, dF, dw, dw_next, dgamma_next, dhbar, coef, true, workspace,
+                             workspace_bytes, T, n, d, enum_value(dt), stream);
 }
 
 int64_t hc_weights_backward_workspace(int64_t T, int32_t n, int32_t d, int32_t sinkhorn_iters) {
@@ -480,32 +516,46 @@ int64_t hc_weights_backward_workspace(int64_t T, int32_t n, int32_t d, int32_t s
     return hc::weights_backward_workspace_bytes(T, n, d, sinkhorn_iters);
 }
 
-hc_status hc_weights_backward(const void* H, const void* W, const float* w_static, float scale,
-                              float eps, int32_t sinkhorn_iters, const float* dw, const float* dw2,
-                              const float* saved, const void* dH_in,
-                              void* dH, float* dW, float* dw_static, void* workspace,
-                              int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt_arg,
-                              void* stream) {
-    const int dt = enum_value(dt_arg);
+namespace {
+
+// hc_weights_backward (terms false: dH out), or hc_weights_backward_terms
+// (dhbar and coef out; dH_in and dH NULL).
+hc_status weights_backward(const void* H, const void* W, const float* w_static, float scale,
+                           float eps, int32_t sinkhorn_iters, const float* dw, const float* dw2,
+                           const float* saved, const void* dH_in, void* dH, float* dhbar,
+                           float* coef, bool terms, float* dW, float* dw_static, void* workspace,
+                           int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, int dt,
+                           void* stream) {
     if (!dtype_wide(dt)) return HC_ERR_DTYPE;
     hc_status st = check_nd(n, d, T, dt);
     if (st != HC_OK) return st;
     if (!eps_ok(eps) || !std::isfinite(scale)) return HC_ERR_ARG;
     if (sinkhorn_iters < 0 || sinkhorn_iters > HC_MAX_SINKHORN_ITERS) return HC_ERR_ARG;
     if (T == 0) return HC_OK;
-    if (!H || !W || !w_static || !dw || !dH || !dW || !dw_static || !workspace) return HC_ERR_NULL;
+    if (!H || !W || !w_static || !dw || !dW || !dw_static || !workspace) return HC_ERR_NULL;
+    if (terms ? (!dhbar || !coef) : !dH) return HC_ERR_NULL;
+    if (terms && (dH || dH_in)) return HC_ERR_ARG;
     const int64_t need = hc_weights_backward_workspace(T, n, d, sinkhorn_iters);
     if (workspace_bytes < need) return HC_ERR_ARG;
     if (misaligned(H, 16) || misaligned(W, 16) || misaligned(dH, 16) || misaligned(dH_in, 16) ||
         misaligned(workspace, 16) || misaligned(w_static, 4) || misaligned(dw, 4) ||
-        misaligned(dW, 4) || misaligned(dw_static, 4) || misaligned(dw2, 4) || misaligned(saved, 16))
+        misaligned(dW, 4) || misaligned(dw_static, 4) || misaligned(dw2, 4) || misaligned(saved, 16) ||
+        misaligned(dhbar, 16) || misaligned(coef, 4))
         return HC_ERR_ALIGN;
     const int K = record_len(n);
     const int64_t s = elem_bytes(dt);
+    // the terms' two outputs take dH's place in the checks below: dhbar
+    // [T][d] fp32 and coef [T][2n] fp32, which may not overlap each other
+    const Span sdb{dhbar, terms ? T * d * 4 : 0}, sco{coef, terms ? T * 2 * n * 4 : 0};
+    if (overlap(sdb, sco)) return HC_ERR_ALIAS;
     const Span sH{H, T * n * d * s}, sW{W, int64_t(K) * d * s}, sS{w_static, int64_t(K) * 4},
         sg{dw, T * K * 4}, sg2{dw2, dw2 ? T * K * 4 : 0}, sin{dH_in, dH_in ? T * n * d * s : 0},
-        sdH{dH, T * n * d * s}, sdW{dW, int64_t(K) * d * 4}, sds{dw_static, int64_t(K) * 4},
+        sdH = terms ? Span{dhbar, T * d * 4} : Span{dH, T * n * d * s},
+        sdW{dW, int64_t(K) * d * 4}, sds{dw_static, int64_t(K) * 4},
         sws{workspace, need}, ssv{saved, saved ? hc_weights_saved_bytes(T, n) : 0};
+    if (terms)
+        for (const Span& i : {sH, sW, sS, sg, sg2, ssv, sdW, sds, sws})
+            if (overlap(sco, i)) return HC_ERR_ALIAS;
     const Span ins[] = {sH, sW, sS, sg, sg2, ssv};
     for (const Span& o : {sdH, sdW, sds, sws})
         for (const Span& i : ins)
@@ -518,7 +568,32 @@ hc_status hc_weights_backward(const void* H, const void* W, const float* w_stati
         return HC_ERR_ALIAS;
     return from_hip(hc::launch_weights_backward(H, W, w_static, scale, eps, sinkhorn_iters, dw, dw2,
                                                 saved, dH_in, dH, dW, dw_static, workspace, T, n, d, dt,
-                                                static_cast<hipStream_t>(stream)));
+                                                static_cast<hipStream_t>(stream),
+                                                terms ? dhbar : nullptr, terms ? coef : nullptr));
+}
+
+}  // namespace
+
+hc_status hc_weights_backward(const void* H, const void* W, const float* w_static, float scale,
+                              float eps, int32_t sinkhorn_iters, const float* dw, const float* dw2,
+                              const float* saved, const void* dH_in,
+                              void* dH, float* dW, float* dw_static, void* workspace,
+                              int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
+                              void* stream) {
+    return weights_backward(H, W, w_static, scale, eps, sinkhorn_iters, dw, dw2, saved, dH_in, dH,
+                            nullptr, nullptr, false, dW, dw_static, workspace, workspace_bytes, T, n,
+                            d, enum_value(dt), stream);
+}
+
+hc_status hc_weights_backward_terms(const void* H, const void* W, const float* w_static,
+                                    float scale, float eps, int32_t sinkhorn_iters, const float* dw,
+                                    const float* dw2, const float* saved, float* dhbar, float* coef,
+                                    float* dW, float* dw_static, void* workspace,
+                                    int64_t workspace_bytes, int64_t T, int32_t n, int32_t d,
+                                    hc_dtype dt, void* stream) {
+    return weights_backward(H, W, w_static, scale, eps, sinkhorn_iters, dw, dw2, saved, nullptr,
+                            nullptr, dhbar, coef, true, dW, dw_static, workspace, workspace_bytes, T,
+                            n, d, enum_value(dt), stream);
 }
 
 int64_t hc_sinkhorn_backward_workspace(int64_t T, int32_t iters) {

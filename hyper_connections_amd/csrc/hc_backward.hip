@@ -558,14 +558,22 @@ __global__ __launch_bounds__(1024) void pre_bwd_kernel(
 // boundary_records_kernel (no block reduction per token).  Otherwise summed
 // over the block's tokens in registers: dalpha to rpart[blk][n], the rest to
 // rpart[nb * n + blk * M] (nb blocks, M = n + n^2).
-template <int N, typename S, int VPT, bool PER_TOKEN>
+//
+// WT (with per-token records produced from H' by the weight producer): the
+// producer's share of the gradient at H' is added to G as well,
+//   G_i += a_i dhbar + b_i H'_i,
+// from dhb [T][d] fp32 (dhbar = W^T dz) and coef [T][2n] = (a_i | b_i), which
+// the weight producer's gradient pass wrote instead of a dH row per stream
+// (hc_weights_bwd.hip); H'_i is the recomputed H' already in hand.
+template <int N, typename S, int VPT, bool PER_TOKEN, bool WT = false>
 __global__ __launch_bounds__(1024) void post_pre_bwd_kernel(
     const uint8_t* __restrict__ dHo, const uint8_t* __restrict__ du, const uint8_t* __restrict__ H,
     const uint8_t* __restrict__ F, const float* __restrict__ w, const float* __restrict__ wn,
     int64_t w_stride, const float* __restrict__ gamma, float eps, uint8_t* __restrict__ dH,
     uint8_t* __restrict__ dF, float* __restrict__ dg_part, float* __restrict__ rpart, int64_t T,
-    int d, int group) {
+    int d, int group, const float* __restrict__ dhb, const float* __restrict__ coef) {
     constexpr int V = Store<S>::kElems, E = Word<S>::kElems;
+    constexpr int DV = V / 4;               // 16-byte vectors of dhbar per stream vector
     constexpr int K = 2 * N + N * N;
     constexpr int M = N + N * N;
     __shared__ float red[16 * 24];          // block_sum_vec<2> and block_sum_to<K>
@@ -579,6 +587,10 @@ __global__ __launch_bounds__(1024) void post_pre_bwd_kernel(
     extern __shared__ uint32_t hol[];
     uint32_t* const hl = hol + (threadIdx.x >> 6) * (N * 4 * 64) + (threadIdx.x & 63);
     const int B = blockDim.x;
+    // WT with one vector per thread: dhbar waits for the second phase in the
+    // same way, after the whole block's H' ([wave][element][lane], V words
+    // per thread)
+    uint32_t* const dl = hol + (B >> 6) * (N * 4 * 64) + (threadIdx.x >> 6) * (V * 64) + (threadIdx.x & 63);
     const int nvec = d / V;
     const int64_t row_bytes = (int64_t)d * Store<S>::kBytes;
     const int wave = threadIdx.x >> 6, nw = B >> 6;
@@ -608,9 +620,17 @@ __global__ __launch_bounds__(1024) void post_pre_bwd_kernel(
             for (int i = 0; i < N; ++i)
 #pragma unroll
                 for (int k = 0; k < N; ++k) A[i][k] = rec[2 * N + i * N + k];
+            float ca[N], cb[N];
+            if constexpr (WT) {
+#pragma unroll
+                for (int i = 0; i < N; ++i) {
+                    ca[i] = coef[t * 2 * N + i];
+                    cb[i] = coef[t * 2 * N + N + i];
+                }
+            }
             const int64_t r0 = t * N * row_bytes;
             // every load of the token first
-            uint4 rh[N][VPT], rg[N][VPT], rf[VPT], ru[VPT];
+            uint4 rh[N][VPT], rg[N][VPT], rf[VPT], ru[VPT], rd[VPT][WT ? DV : 1];
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
                 const int v = threadIdx.x + j * B;
@@ -623,6 +643,11 @@ __global__ __launch_bounds__(1024) void post_pre_bwd_kernel(
                 for (int i = 0; i < N; ++i)
                     rg[i][j] = v < nvec ? ld16_stream(dHo + r0 + i * row_bytes + v * 16) : z;
                 ru[j] = v < nvec ? ld16_stream(du + t * row_bytes + v * 16) : z;
+                if constexpr (WT) {
+#pragma unroll
+                    for (int q = 0; q < DV; ++q)
+                        rd[j][q] = v < nvec ? ld16_stream(reinterpret_cast<const uint8_t*>(dhb + t * d + v * V) + 16 * q) : z;
+                }
             }
             // H' as the forward stores it, and the RMSNorm gradient's two sums
             uint4 ro[N][VPT];
@@ -659,6 +684,10 @@ __global__ __launch_bounds__(1024) void post_pre_bwd_kernel(
                         ro[i][j] = make_uint4(o[i][0], o[i][1], o[i][2], o[i][3]);
                     }
                 }
+                if constexpr (WT && kLds) {
+#pragma unroll
+                    for (int el = 0; el < V; ++el) dl[el * 64] = word(rd[j][el / 4], el % 4);
+                }
                 if (v < nvec) {
                     float g[4];
 #pragma unroll
@@ -694,6 +723,10 @@ __global__ __launch_bounds__(1024) void post_pre_bwd_kernel(
                 }
                 opaque(rf[j]);
                 opaque(ru[j]);
+                if constexpr (WT && !kLds) {
+#pragma unroll
+                    for (int q = 0; q < DV; ++q) opaque(rd[j][q]);
+                }
             }
             const float r = 1.0f / sqrtf(s2[0] / (float)d + eps);
             const float c2 = r * r * s2[1] / (float)d;
@@ -728,6 +761,12 @@ __global__ __launch_bounds__(1024) void post_pre_bwd_kernel(
                             for (int i = 0; i < N; ++i) {
                                 acc[i] = fmaf(dx, ho[i][e], acc[i]);
                                 G[i] = fmaf(alpha[i], dx, gr[i][e]);
+                                if constexpr (WT) {
+                                    const int el = q * E + e;          // element of the vector
+                                    const float hd = __uint_as_float(
+                                        kLds ? dl[el * 64] : word(rd[j][(el / 4) % DV], el % 4));
+                                    G[i] = fmaf(cb[i], ho[i][e], fmaf(ca[i], hd, G[i]));
+                                }
                                 acc[N + i] = fmaf(G[i], f[e], acc[N + i]);
 #pragma unroll
                                 for (int k = 0; k < N; ++k)
@@ -1022,23 +1061,26 @@ template <int N, typename S, int VPT>
 hipError_t post_pre_bwd_go(RowCfg c, const void* dHo, const void* du, const void* H, const void* F,
                            const float* w, const float* wn, int64_t ws, const float* gamma,
                            float eps, void* dH, void* dF, float* dg_part, float* rpart, int64_t T,
-                           int d, int group, hipStream_t s) {
+                           int d, int group, const float* dhb, const float* coef, hipStream_t s) {
     const dim3 grid = grid_of((T + group - 1) / group);
-    auto* k = ws != 0 ? post_pre_bwd_kernel<N, S, VPT, true> : post_pre_bwd_kernel<N, S, VPT, false>;
-    const size_t lds = VPT == 1 ? (size_t)N * 16 * c.block : 0;     // the parked H'
+    // the weight producer's terms come only with per-token records
+    auto* k = dhb ? post_pre_bwd_kernel<N, S, VPT, true, true>
+              : ws != 0 ? post_pre_bwd_kernel<N, S, VPT, true> : post_pre_bwd_kernel<N, S, VPT, false>;
+    // the parked H', and with the producer's terms dhbar (V floats per thread)
+    const size_t lds = VPT == 1 ? ((size_t)N * 16 + (dhb ? Store<S>::kElems * 4 : 0)) * c.block : 0;
     return launch(k, grid, dim3(c.block), lds, s, static_cast<const uint8_t*>(dHo),
                   static_cast<const uint8_t*>(du), static_cast<const uint8_t*>(H),
                   static_cast<const uint8_t*>(F), w, wn, ws, gamma, eps, static_cast<uint8_t*>(dH),
-                  static_cast<uint8_t*>(dF), dg_part, rpart, T, d, group);
+                  static_cast<uint8_t*>(dF), dg_part, rpart, T, d, group, dhb, coef);
 }
 
 template <int N, typename S>
 hipError_t post_pre_bwd_vpt(RowCfg c, const void* dHo, const void* du, const void* H, const void* F,
                             const float* w, const float* wn, int64_t ws, const float* gamma,
                             float eps, void* dH, void* dF, float* dg_part, float* rpart, int64_t T,
-                            int d, int group, hipStream_t s) {
+                            int d, int group, const float* dhb, const float* coef, hipStream_t s) {
     HC_BWD_VPT(post_pre_bwd_go, dHo, du, H, F, w, wn, ws, gamma, eps, dH, dF, dg_part, rpart, T, d,
-               group, s)
+               group, dhb, coef, s)
 }
 #undef HC_BWD_VPT
 
@@ -1246,7 +1288,8 @@ hipError_t launch_post_pre_mix_backward(const void* dHo, const void* du, const v
                                         const float* w, const float* wn, int64_t w_stride,
                                         const float* gamma, float eps, void* dH, void* dF, float* dw,
                                         float* dwn, float* dgamma, void* work, int64_t T, int n,
-                                        int d, int dt, hipStream_t s) {
+                                        int d, int dt, hipStream_t s, const float* dhb,
+                                        const float* coef) {
     const BwdSpace sp = bwd_space(T, n, d);
     float* ws = static_cast<float*>(work);
     const int group = (int)group_of(T);
@@ -1256,9 +1299,9 @@ hipError_t launch_post_pre_mix_backward(const void* dHo, const void* du, const v
     const RowCfg c = row_config(d / (dt == 0 ? Store<f32_t>::kElems : Store<bf16_t>::kElems));
     hipError_t e =
         dt == 0 ? post_pre_bwd_n<f32_t>(n, c, dHo, du, H, F, w, wn, w_stride, gamma, eps, dH, dF,
-                                        dg_part, rpart, T, d, group, s)
+                                        dg_part, rpart, T, d, group, dhb, coef, s)
                 : post_pre_bwd_n<bf16_t>(n, c, dHo, du, H, F, w, wn, w_stride, gamma, eps, dH, dF,
-                                         dg_part, rpart, T, d, group, s);
+                                         dg_part, rpart, T, d, group, dhb, coef, s);
     if (e != hipSuccess) return e;
     const int K = 2 * n + n * n, M = n + n * n;
     const SumJob dg_job = {dg_part, sp.rows, d, ws + sp.tmp, dgamma, nullptr, 0};

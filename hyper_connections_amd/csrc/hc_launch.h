@@ -60,7 +60,8 @@ hipError_t launch_post_pre_mix_backward(const void* dHo, const void* du, const v
                                         const float* w, const float* wn, int64_t w_stride,
                                         const float* gamma, float eps, void* dH, void* dF, float* dw,
                                         float* dwn, float* dgamma, void* work, int64_t T, int n,
-                                        int d, int dt, hipStream_t s);
+                                        int d, int dt, hipStream_t s, const float* dhb = nullptr,
+                                        const float* coef = nullptr);
 int64_t backward_workspace_bytes(int64_t T, int n, int d);
 // The post gradient with its scratch in the library's own per-GPU array
 // (nothing allocated): bytes it needs, and the array's size.
@@ -108,11 +109,14 @@ struct SumJob {
 hipError_t launch_sum_rows(const SumJob* jobs, int njobs, hipStream_t s);
 int64_t weights_backward_workspace_bytes(int64_t T, int n, int d, int iters);
 int64_t sinkhorn_backward_workspace_bytes(int64_t T, int iters);
+// With dhbar (and coef) given, the stream pass writes dhbar = W^T dz [T][d]
+// and the coefficients (a_i | b_i) [T][2n] instead of dH (dH_in, dH unused).
 hipError_t launch_weights_backward(const void* H, const void* W, const float* w_static, float scale,
                                    float eps, int iters, const float* dw, const float* dw2,
                                    const float* saved, const void* dH_in,
                                    void* dH, float* dW, float* dws, void* work, int64_t T, int n,
-                                   int d, int dt, hipStream_t s);
+                                   int d, int dt, hipStream_t s, float* dhbar = nullptr,
+                                   float* coef = nullptr);
 hipError_t launch_sinkhorn_backward(const float* logits, const float* dw, const float* dw2,
                                     float* dlogits, int iters, void* work, int64_t T, int n,
                                     hipStream_t s);

@@ -467,11 +467,16 @@ __device__ __forceinline__ void sum_wave_partials(f32x4 (&acc)[A][B], float* lds
 // the lane's own columns, no shuffles.  Each wave keeps its partial dW
 // (2 x V tiles); at the end the workgroup's four are added (wave order) and
 // written to part[split][K][d].
-template <int N, typename S>
+//
+// TERMS: dH is not formed; the lane's dhbar values are written to dhbar
+// [T][d] (fp32) instead, for a later pass that holds H_i to add
+// a_i dhbar + b_i H_i itself (dH_in and dH unused).
+template <int N, typename S, bool TERMS = false>
 __global__ __launch_bounds__(256) void wgrad_stream_kernel(
     const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, const float* __restrict__ dz,
     const float* __restrict__ ab, const float* __restrict__ r, const uint8_t* dH_in,
-    uint8_t* dH, float* __restrict__ part, int64_t T, int d, int64_t tok_per_split) {
+    uint8_t* dH, float* __restrict__ part, int64_t T, int d, int64_t tok_per_split,
+    float* __restrict__ dhbar) {
     constexpr int V = Store<S>::kElems, SB = Store<S>::kBytes;
     constexpr int K = 2 * N + N * N;
     constexpr int CB = 16 * V;                       // columns per workgroup
@@ -510,7 +515,8 @@ __global__ __launch_bounds__(256) void wgrad_stream_kernel(
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             rh[i] = live ? ld16_stream(H + r0 + i * row_bytes) : make_uint4(0, 0, 0, 0);
-            rin[i] = (live && dH_in) ? ld16_stream(dH_in + r0 + i * row_bytes) : make_uint4(0, 0, 0, 0);
+            rin[i] = (!TERMS && live && dH_in) ? ld16_stream(dH_in + r0 + i * row_bytes)
+                                               : make_uint4(0, 0, 0, 0);
         }
         const int64_t tt = ok ? t : t_begin;
         float gz[K];
@@ -546,13 +552,24 @@ __global__ __launch_bounds__(256) void wgrad_stream_kernel(
                 hb[e] = fmaf(ri[i], h[e], hb[e]);
                 o[e] = fmaf(ai[i], dhb[e], bi[i] * h[e]);
             }
-            if (dH_in) {
-                float p[V];
-                unpack<S>(rin[i], p);
+            if constexpr (!TERMS) {
+                if (dH_in) {
+                    float p[V];
+                    unpack<S>(rin[i], p);
 #pragma unroll
-                for (int e = 0; e < V; ++e) o[e] += p[e];
+                    for (int e = 0; e < V; ++e) o[e] += p[e];
+                }
+                if (live) st16_stream(dH + r0 + i * row_bytes, pack<S>(o));
             }
-            if (live) st16_stream(dH + r0 + i * row_bytes, pack<S>(o));
+        }
+        if constexpr (TERMS) {
+            if (live) {
+#pragma unroll
+                for (int q = 0; q < V / 4; ++q)
+                    st16_stream(dhbar + t * d + (int64_t)cv * V + 4 * q,
+                                make_uint4(__float_as_uint(dhb[4 * q]), __float_as_uint(dhb[4 * q + 1]),
+                                           __float_as_uint(dhb[4 * q + 2]), __float_as_uint(dhb[4 * q + 3])));
+            }
         }
 #pragma unroll
         for (int e = 0; e < V; ++e) hb[e] = hb[e] / (float)N;
@@ -618,11 +635,16 @@ __device__ __forceinline__ Split2 split_bf16x2(float x0, float x1) {
     return {h, pack_bf16x2(x0 - lo_bf16(h), x1 - hi_bf16(h))};
 }
 
-template <int N, bool IN>
+// TERMS (IN false): no dH; the lane's dhbar values (8 columns of each of
+// its 4 tokens) go to dhbar [T][d] fp32 instead, for the pass that adds
+// a_i dhbar + b_i H_i where it holds H_i.
+template <int N, bool IN, bool TERMS = false>
 __global__ __launch_bounds__(256) void wgrad_mfma_kernel(
     const uint8_t* __restrict__ H, const uint8_t* __restrict__ W, const float* __restrict__ dz,
     const float* __restrict__ ab, const float* __restrict__ r, const uint8_t* dH_in,
-    uint8_t* dH, float* __restrict__ part, int64_t T, int d, int64_t tok_per_split) {
+    uint8_t* dH, float* __restrict__ part, int64_t T, int d, int64_t tok_per_split,
+    float* __restrict__ dhbar) {
+    static_assert(!(IN && TERMS), "the terms take no incoming dH");
     // the fp32 kernel's signature: this one takes hbar's weights from ab (a_i =
     // r_i / n) and deals its steps round robin, so r and the split size go unused
     (void)r;
@@ -739,11 +761,23 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(
                     }
                     hb[j][2 * k] = fmaf(L.a[i], h0, hb[j][2 * k]);
                     hb[j][2 * k + 1] = fmaf(L.a[i], h1, hb[j][2 * k + 1]);
-                    o0 = fmaf(L.b[i], h0, fmaf(L.a[i], dhb[2 * k][j], o0));
-                    o1 = fmaf(L.b[i], h1, fmaf(L.a[i], dhb[2 * k + 1][j], o1));
-                    ow[k] = pack_bf16x2(o0, o1);
+                    if constexpr (!TERMS) {
+                        o0 = fmaf(L.b[i], h0, fmaf(L.a[i], dhb[2 * k][j], o0));
+                        o1 = fmaf(L.b[i], h1, fmaf(L.a[i], dhb[2 * k + 1][j], o1));
+                        ow[k] = pack_bf16x2(o0, o1);
+                    }
                 }
-                if (ok && col_ok) st16_stream(dH + r0 + i * row_bytes, make_uint4(ow[0], ow[1], ow[2], ow[3]));
+                if constexpr (!TERMS)
+                    if (ok && col_ok) st16_stream(dH + r0 + i * row_bytes, make_uint4(ow[0], ow[1], ow[2], ow[3]));
+            }
+            if constexpr (TERMS) {
+                if (ok && col_ok) {
+                    float* o = dhbar + t * d + (int64_t)cv * 8;
+                    st16_stream(o, make_uint4(__float_as_uint(dhb[0][j]), __float_as_uint(dhb[1][j]),
+                                              __float_as_uint(dhb[2][j]), __float_as_uint(dhb[3][j])));
+                    st16_stream(o + 4, make_uint4(__float_as_uint(dhb[4][j]), __float_as_uint(dhb[5][j]),
+                                                  __float_as_uint(dhb[6][j]), __float_as_uint(dhb[7][j])));
+                }
             }
 #pragma unroll
             for (int q = 0; q < 8; ++q) hb[j][q] = ok ? hb[j][q] : 0.0f;
@@ -819,28 +853,29 @@ hipError_t coef_go(const float* P, const float* r, const float* dw, const float*
 template <int N, typename S>
 hipError_t stream_go(const void* H, const void* W, const float* dz, const float* ab, const float* r,
                      const void* dH_in, void* dH, float* part, int64_t T, int d, int splits,
-                     int64_t tps, hipStream_t s) {
+                     int64_t tps, float* dhbar, hipStream_t s) {
     const int nvec = d / Store<S>::kElems;
     const dim3 grid((unsigned)((nvec + 15) / 16), (unsigned)splits);
     void (*kernel)(const uint8_t*, const uint8_t*, const float*, const float*, const float*,
-                   const uint8_t*, uint8_t*, float*, int64_t, int, int64_t) =
-        !std::is_same<S, bf16_t>::value ? wgrad_stream_kernel<N, S>
+                   const uint8_t*, uint8_t*, float*, int64_t, int, int64_t, float*) =
+        !std::is_same<S, bf16_t>::value ? (dhbar ? wgrad_stream_kernel<N, S, true> : wgrad_stream_kernel<N, S>)
+        : dhbar                          ? wgrad_mfma_kernel<N, false, true>
         : dH_in                          ? wgrad_mfma_kernel<N, true>
                                          : wgrad_mfma_kernel<N, false>;
     return launch(kernel, grid, dim3(256), 0, s, static_cast<const uint8_t*>(H),
                   static_cast<const uint8_t*>(W), dz, ab, r, static_cast<const uint8_t*>(dH_in),
-                  static_cast<uint8_t*>(dH), part, T, d, tps);
+                  static_cast<uint8_t*>(dH), part, T, d, tps, dhbar);
 }
 
 template <typename S>
 hipError_t stream_by_n(int n, const void* H, const void* W, const float* dz, const float* ab,
                        const float* r, const void* dH_in, void* dH, float* part, int64_t T, int d,
-                       int splits, int64_t tps, hipStream_t s) {
+                       int splits, int64_t tps, float* dhbar, hipStream_t s) {
     switch (n) {
-        case 1: return stream_go<1, S>(H, W, dz, ab, r, dH_in, dH, part, T, d, splits, tps, s);
-        case 2: return stream_go<2, S>(H, W, dz, ab, r, dH_in, dH, part, T, d, splits, tps, s);
-        case 3: return stream_go<3, S>(H, W, dz, ab, r, dH_in, dH, part, T, d, splits, tps, s);
-        case 4: return stream_go<4, S>(H, W, dz, ab, r, dH_in, dH, part, T, d, splits, tps, s);
+        case 1: return stream_go<1, S>(H, W, dz, ab, r, dH_in, dH, part, T, d, splits, tps, dhbar, s);
+        case 2: return stream_go<2, S>(H, W, dz, ab, r, dH_in, dH, part, T, d, splits, tps, dhbar, s);
+        case 3: return stream_go<3, S>(H, W, dz, ab, r, dH_in, dH, part, T, d, splits, tps, dhbar, s);
+        case 4: return stream_go<4, S>(H, W, dz, ab, r, dH_in, dH, part, T, d, splits, tps, dhbar, s);
     }
     return hipErrorInvalidValue;
 }
@@ -925,10 +960,13 @@ hipError_t launch_weights_backward(const void* H, const void* W, const float* w_
                                    float eps, int iters, const float* dw, const float* dw2,
                                    const float* saved, const void* dH_in,
                                    void* dH, float* dW, float* dws, void* work, int64_t T, int n,
-                                   int d, int dt, hipStream_t s) {
+                                   int d, int dt, hipStream_t s, float* dhbar, float* coef) {
     const WgSpace sp = wg_space(T, n, d, iters);
     float* ws = static_cast<float*>(work);
     const int K = 2 * n + n * n;
+    // the coefficients (a_i | b_i): the caller's buffer when the terms are
+    // returned, else the workspace
+    float* const ab = dhbar ? coef : ws + sp.ab;
     // (1) per-stream projections and row norms: kept by the forward, or
     // computed again
     const float* Pp = saved ? saved : ws + sp.P;
@@ -940,20 +978,20 @@ hipError_t launch_weights_backward(const void* H, const void* W, const float* w_
     }
     // (2) per-token coefficients
     switch (n) {
-        case 1: e = coef_go<1>(Pp, rp, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
-        case 2: e = coef_go<2>(Pp, rp, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
-        case 3: e = coef_go<3>(Pp, rp, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
-        case 4: e = coef_go<4>(Pp, rp, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ws + sp.ab, T, d, s); break;
+        case 1: e = coef_go<1>(Pp, rp, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ab, T, d, s); break;
+        case 2: e = coef_go<2>(Pp, rp, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ab, T, d, s); break;
+        case 3: e = coef_go<3>(Pp, rp, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ab, T, d, s); break;
+        case 4: e = coef_go<4>(Pp, rp, dw, dw2, w_static, scale, iters, ws + sp.scr, ws + sp.dz, ws + sp.dl, ab, T, d, s); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
     // (3) dH and the dW partials
     const int64_t splits = splits_of(T);
     const int64_t tps = (T + splits - 1) / splits;
-    e = dt == 0 ? stream_by_n<f32_t>(n, H, W, ws + sp.dz, ws + sp.ab, rp, dH_in, dH, ws + sp.part,
-                                     T, d, (int)splits, tps, s)
-                : stream_by_n<bf16_t>(n, H, W, ws + sp.dz, ws + sp.ab, rp, dH_in, dH,
-                                      ws + sp.part, T, d, (int)splits, tps, s);
+    e = dt == 0 ? stream_by_n<f32_t>(n, H, W, ws + sp.dz, ab, rp, dH_in, dH, ws + sp.part,
+                                     T, d, (int)splits, tps, dhbar, s)
+                : stream_by_n<bf16_t>(n, H, W, ws + sp.dz, ab, rp, dH_in, dH,
+                                      ws + sp.part, T, d, (int)splits, tps, dhbar, s);
     if (e != hipSuccess) return e;
     // (4) fixed-order sums: dW over the partials, dw_static over the
     // coefficient workgroups' partials, in shared launches

@@ -54,6 +54,11 @@ _SIGS = {
                             _i64, _i32, _i32, _i32, _vp],
     "hc_post_pre_mix_backward": [_vp, _vp, _vp, _vp, _fp, _i64, _fp, _i64, _fp, _f32, _vp, _vp,
                                  _fp, _fp, _fp, _vp, _i64, _i64, _i32, _i32, _i32, _vp],
+    "hc_post_pre_mix_backward_terms": [_vp, _vp, _vp, _vp, _fp, _i64, _fp, _i64, _fp, _f32, _fp,
+                                       _fp, _vp, _vp, _fp, _fp, _fp, _vp, _i64, _i64, _i32, _i32,
+                                       _i32, _vp],
+    "hc_weights_backward_terms": [_vp, _vp, _fp, _f32, _f32, _i32, _fp, _fp, _fp, _fp, _fp, _fp,
+                                  _fp, _vp, _i64, _i64, _i32, _i32, _i32, _vp],
     "hc_sum_records": [_fp, _i64, _i32, _fp, _vp],
     "hc_weights_save": [_vp, _vp, _fp, _f32, _f32, _i32, _fp, _fp, _i64, _i64, _i32, _i32, _i32,
                         _vp],
@@ -541,18 +546,30 @@ def pre_mix_backward(du, H, w, gamma, eps: float = 1e-6, dH_in=None, out=None, d
 @_on_launch_stream
 def post_pre_mix_backward(dH_out, du_next, H, F, w, w_next, gamma_next, eps: float = 1e-6,
                           out=None, dF=None, dw=None, dw_next=None, dgamma_next=None,
-                          workspace=None, stream=None):
+                          workspace=None, stream=None, terms=None):
     """Gradients of post_pre_mix (one layer boundary): returns (dH, dF, dw,
     dw_next, dgamma_next).  dH_out is the gradient at H' from the next layer's
     write-back (not from the read-mix, whose share is formed here from
     du_next); H' is recomputed from H, F and w.  dw ([0 | dbeta | dA]) and
     dw_next ([dalpha | 0 | 0]) have the shape of w and w_next, which must be
-    both shared or both per token.  ``out=dH_out`` writes dH in place."""
+    both shared or both per token.  ``out=dH_out`` writes dH in place.
+    ``terms=(dhbar, coef)`` from weights_backward_terms (per-token records
+    only) adds the weight producer's gradient a_i dhbar + b_i H'_i at H'."""
     T, n, d, K = _H(H)
     ws = _record(w, T, K)
     ws2 = _record(w_next, T, K, "w_next")
     if ws != ws2:
         raise ValueError("w and w_next must be both shared (K,) or both per token (T, K)")
+    if terms is not None:
+        if ws == 0:
+            raise ValueError("terms come with per-token records (T, K)")
+        dhbar, coef = terms
+        _dev(dhbar, "dhbar")
+        _dev(coef, "coef")
+        if dhbar.dtype != torch.float32 or tuple(dhbar.shape) != (T, d) or not dhbar.is_contiguous():
+            raise ValueError(f"dhbar must be contiguous float32 of shape ({T}, {d})")
+        if coef.dtype != torch.float32 or tuple(coef.shape) != (T, 2 * n) or not coef.is_contiguous():
+            raise ValueError(f"coef must be contiguous float32 of shape ({T}, {2 * n})")
     for name, x, shape in (("dH_out", dH_out, tuple(H.shape)), ("du_next", du_next, (T, d)),
                            ("F", F, (T, d))):
         _dev(x, name)
@@ -572,10 +589,17 @@ def post_pre_mix_backward(dH_out, du_next, H, F, w, w_next, gamma_next, eps: flo
     if dg.dtype != torch.float32 or tuple(dg.shape) != (d,):
         raise ValueError(f"dgamma_next must be float32 of shape ({d},)")
     wk, wkb = _workspace(workspace, T, n, d, H.device)
-    _call("hc_post_pre_mix_backward", dH_out.data_ptr(), du_next.data_ptr(), H.data_ptr(),
-          F.data_ptr(), w.data_ptr(), ws, w_next.data_ptr(), ws2, gamma_next.data_ptr(),
-          float(eps), dH.data_ptr(), f.data_ptr(), dw.data_ptr(), dwn.data_ptr(), dg.data_ptr(),
-          wk.data_ptr(), wkb, T, n, d, _dt(H), _stream(stream))
+    if terms is None:
+        _call("hc_post_pre_mix_backward", dH_out.data_ptr(), du_next.data_ptr(), H.data_ptr(),
+              F.data_ptr(), w.data_ptr(), ws, w_next.data_ptr(), ws2, gamma_next.data_ptr(),
+              float(eps), dH.data_ptr(), f.data_ptr(), dw.data_ptr(), dwn.data_ptr(), dg.data_ptr(),
+              wk.data_ptr(), wkb, T, n, d, _dt(H), _stream(stream))
+    else:
+        _call("hc_post_pre_mix_backward_terms", dH_out.data_ptr(), du_next.data_ptr(), H.data_ptr(),
+              F.data_ptr(), w.data_ptr(), ws, w_next.data_ptr(), ws2, gamma_next.data_ptr(),
+              float(eps), dhbar.data_ptr(), coef.data_ptr(), dH.data_ptr(), f.data_ptr(),
+              dw.data_ptr(), dwn.data_ptr(), dg.data_ptr(), wk.data_ptr(), wkb, T, n, d, _dt(H),
+              _stream(stream))
     return dH, f, dw, dwn, dg
 
 
@@ -646,6 +670,57 @@ def weights_backward(H, W, w_static, scale: float, dw, eps: float = 1e-6, sinkho
           dws.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
           T, n, d, _dt(H), _stream(stream))
     return dH, dW, dws
+
+
+@_on_launch_stream
+def weights_backward_terms(H, W, w_static, scale: float, dw, eps: float = 1e-6,
+                           sinkhorn_iters: int = 0, dhbar=None, coef=None, dW=None, dw_static=None,
+                           workspace=None, dw2=None, saved=None, stream=None):
+    """weights_backward without dH: returns (dhbar, coef, dW, dw_static) with
+    dhbar (T, d) float32 = W^T dz per token and coef (T, 2n) float32 = (a | b),
+    so that the gradient reaching stream i is a_i dhbar + b_i H_i (for
+    post_pre_mix_backward(..., terms=(dhbar, coef)))."""
+    T, n, d, K = _H(H)
+    for name, x in (("W", W), ("w_static", w_static), ("dw", dw)):
+        _dev(x, name)
+    if W.dtype != H.dtype or tuple(W.shape) != (K, d):
+        raise ValueError(f"W must match H's dtype and have shape ({K}, {d})")
+    if w_static.dtype != torch.float32 or tuple(w_static.shape) != (K,):
+        raise ValueError(f"w_static must be float32 of shape ({K},)")
+    if dw.dtype != torch.float32 or tuple(dw.shape) != (T, K):
+        raise ValueError(f"dw must be float32 of shape ({T}, {K})")
+    if dw2 is not None:
+        _dev(dw2, "dw2")
+        if dw2.dtype != torch.float32 or tuple(dw2.shape) != (T, K):
+            raise ValueError(f"dw2 must be float32 of shape ({T}, {K})")
+    if saved is not None:
+        _dev(saved, "saved")
+        if saved.dtype != torch.float32 or saved.numel() * 4 < int(lib().hc_weights_saved_bytes(T, n)):
+            raise ValueError("saved must be the float32 buffer weights_save filled")
+    dhb = torch.empty((T, d), dtype=torch.float32, device=H.device) if dhbar is None else _dev(dhbar, "dhbar")
+    co = torch.empty((T, 2 * n), dtype=torch.float32, device=H.device) if coef is None else _dev(coef, "coef")
+    if dhb.dtype != torch.float32 or tuple(dhb.shape) != (T, d) or not dhb.is_contiguous():
+        raise ValueError(f"dhbar must be contiguous float32 of shape ({T}, {d})")
+    if co.dtype != torch.float32 or tuple(co.shape) != (T, 2 * n) or not co.is_contiguous():
+        raise ValueError(f"coef must be contiguous float32 of shape ({T}, {2 * n})")
+    dW = torch.empty((K, d), dtype=torch.float32, device=H.device) if dW is None else _dev(dW, "dW")
+    dws = (torch.empty(K, dtype=torch.float32, device=H.device) if dw_static is None
+           else _dev(dw_static, "dw_static"))
+    if dW.dtype != torch.float32 or tuple(dW.shape) != (K, d):
+        raise ValueError(f"dW must be float32 of shape ({K}, {d})")
+    if dws.dtype != torch.float32 or tuple(dws.shape) != (K,):
+        raise ValueError(f"dw_static must be float32 of shape ({K},)")
+    need = int(lib().hc_weights_backward_workspace(T, n, d, int(sinkhorn_iters)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=H.device)
+    _dev(workspace, "workspace")
+    _call("hc_weights_backward_terms", H.data_ptr(), W.data_ptr(), w_static.data_ptr(), float(scale),
+          float(eps), int(sinkhorn_iters), dw.data_ptr(),
+          dw2.data_ptr() if dw2 is not None else None,
+          saved.data_ptr() if saved is not None else None, dhb.data_ptr(), co.data_ptr(),
+          dW.data_ptr(), dws.data_ptr(), workspace.data_ptr(),
+          workspace.numel() * workspace.element_size(), T, n, d, _dt(H), _stream(stream))
+    return dhb, co, dW, dws
 
 
 @_on_launch_stream

@@ -134,6 +134,21 @@ def weights_bwd_bytes(n: int, d: int, s: int) -> int:
     return 3 * n * d * s + 2 * record_bytes(n)
 
 
+def weights_bwd_terms_bytes(n: int, d: int, s: int) -> int:
+    """Gradient of the per-token weights returned as its factors: read H once,
+    write dhbar (d fp32) and the coefficients (2n fp32), plus the two gradient
+    records read.  The projections and norms kept by the forward are not
+    counted, as in weights_bwd_bytes."""
+    return n * d * s + 4 * d + 4 * 2 * n + 2 * record_bytes(n)
+
+
+def post_pre_bwd_terms_bytes(n: int, d: int, s: int) -> int:
+    """The layer boundary's gradient with the weight producer's factors added
+    at H': post_pre_bwd_bytes with per-token records, plus dhbar (d fp32) and
+    the coefficients (2n fp32) read."""
+    return post_pre_bwd_bytes(n, d, s, True) + 4 * d + 4 * 2 * n
+
+
 def weights_bwd_stream_bytes(n: int, d: int, s: int) -> int:
     """The streaming pass of the weights gradient alone: read H and the
     incoming dH, write dH (the per-token coefficients it reads, K + 2n floats,

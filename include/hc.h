@@ -337,6 +337,31 @@ hc_status hc_post_pre_mix_backward(const void* dH_out, const void* du_next, cons
                                    int64_t workspace_bytes, int64_t T, int32_t n, int32_t d,
                                    hc_dtype dt, void* stream);
 
+/* hc_post_pre_mix_backward at a boundary whose next layer's records are
+ * produced from H' by the weight producer (hc_post_mix_weights,
+ * hc_post_weights_pre_mix; [GLOSS] definition: the weight producers are
+ * learned, so their gradient reaches the streams they read).  The producer's
+ * share of the gradient at H' is added inside the pass instead of arriving in
+ * dH_out:
+ *   G_i = dH_out_i + alpha_i dx + a_i dhbar + b_i H'_i
+ * with dhbar and (a_i | b_i) from hc_weights_backward_terms for the records
+ * w_next and H' (H' recomputed here bitwise as the forward stored it).  Per
+ * token this reads one fp32 row (dhbar) where the producer's own dH pass
+ * would read and write n rows of dH.
+ *   dhbar [T][d] fp32, 16-byte aligned; coef [T][2n] fp32 = (a_1..a_n |
+ *     b_1..b_n) per token: inputs, which no output may overlap
+ *   w and w_next per token (stride K): shared records are HC_ERR_ARG
+ *   every other argument, output and error as hc_post_pre_mix_backward;
+ *   dhbar or coef NULL is HC_ERR_NULL. */
+hc_status hc_post_pre_mix_backward_terms(const void* dH_out, const void* du_next, const void* H,
+                                         const void* F, const float* w, int64_t w_stride,
+                                         const float* w_next, int64_t w_next_stride,
+                                         const float* gamma_next, float eps, const float* dhbar,
+                                         const float* coef, void* dH, void* dF, float* dw,
+                                         float* dw_next, float* dgamma_next, void* workspace,
+                                         int64_t workspace_bytes, int64_t T, int32_t n, int32_t d,
+                                         hc_dtype dt, void* stream);
+
 /* Bytes of device workspace hc_weights_backward needs (0 for T <= 0 or
  * arguments out of range).  It holds the per-stream projections, per-token
  * coefficients, Sinkhorn intermediates (16 floats per token per iteration)
@@ -367,6 +392,26 @@ hc_status hc_weights_backward(const void* H, const void* W, const float* w_stati
                               void* dH, float* dW, float* dw_static, void* workspace,
                               int64_t workspace_bytes, int64_t T, int32_t n, int32_t d, hc_dtype dt,
                               void* stream);
+
+/* hc_weights_backward without dH: the gradient reaching H is returned as
+ * its two factors, for a later pass that holds H_i to form
+ *   dH_i = a_i dhbar + b_i H_i
+ * itself (hc_post_pre_mix_backward_terms) instead of this call reading and
+ * writing n rows of dH per token ([GLOSS] definition, as hc_weights_backward;
+ * [EXPL] "What four streams cost per token": the n-fold state is what each
+ * pass moves).
+ *   dhbar [T][d] fp32 out = W^T dz per token, 16-byte aligned
+ *   coef [T][2n] fp32 out = (a_1..a_n | b_1..b_n), a_i = r_i / n,
+ *     b_i = -r_i^3 (H_i . dhbar) / (n d)
+ *   dW, dw_static and every input, the workspace and the errors as
+ *     hc_weights_backward (dhbar, coef take dH's place: NULL is HC_ERR_NULL,
+ *     overlap with anything is HC_ERR_ALIAS).  fp32 and bf16 storage only. */
+hc_status hc_weights_backward_terms(const void* H, const void* W, const float* w_static,
+                                    float scale, float eps, int32_t sinkhorn_iters, const float* dw,
+                                    const float* dw2, const float* saved, float* dhbar, float* coef,
+                                    float* dW, float* dw_static, void* workspace,
+                                    int64_t workspace_bytes, int64_t T, int32_t n, int32_t d,
+                                    hc_dtype dt, void* stream);
 
 /* Bytes of device workspace hc_sinkhorn_backward needs: 64 per token per
  * iteration (0 for iters == 0). */

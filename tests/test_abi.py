@@ -51,7 +51,7 @@ def test_status_strings(L):
         s = hc.status_str(code)
         assert s.startswith("HC_")
     assert hc.status_str(99).startswith("HC_ERR_UNKNOWN")
-    assert hc.abi_version() == 7
+    assert hc.abi_version() == 8
 
 
 def pre(L, H=P[0], w=P[1], ws=0, g=P[2], eps=1e-6, u=P[3], T=16, n=4, d=4096, dt=BF16):
@@ -325,6 +325,47 @@ def test_weights_backward_validation(L):
     assert f(din=P[4] + 16) == ALIAS and f(dws=P[5] + 64) == ALIAS
     assert f(g2=P[3] + 2) == ALIGN and f(g2=P[4]) == ALIAS             # dw2 under dH
     assert f(sv=P[3] + 4) == ALIGN and f(sv=P[4] + 64) == ALIAS and f(sv=P[7]) == ALIAS
+
+
+def test_post_pre_mix_backward_terms_validation(L):
+    """The boundary's gradient with the weight producer's factors: per-token
+    records only, dhbar and coef required, aligned, and overlapping no
+    output; the rest as the plain call.  Nothing is launched."""
+    need = L.hc_backward_workspace(8, 4, 4096)
+
+    def f(**k):
+        return L.hc_post_pre_mix_backward_terms(
+            k.get("go", P[0]), k.get("du", P[1]), k.get("H", P[2]), k.get("F", P[3]),
+            k.get("w", P[4]), k.get("ws", 24), k.get("wn", P[5]), k.get("wns", 24), k.get("g", P[6]),
+            k.get("eps", 1e-6), k.get("db", P[12] + 4 * MiB), k.get("co", P[13]), k.get("dH", P[7]),
+            k.get("dF", P[8]), k.get("dw", P[9]), k.get("dwn", P[10]), k.get("dg", P[11]),
+            k.get("wk", P[12]), k.get("wkb", need), k.get("T", 8), k.get("n", 4), k.get("d", 4096),
+            k.get("dt", BF16), None)
+    assert f(T=0) == OK and f(T=0, db=None, co=None) == OK
+    assert f(ws=0, wns=0) == ARG                       # shared records take no terms
+    assert f(dt=FP8) == DTYPE and f(n=5) == SHAPE
+    assert f(db=None) == NULL and f(co=None) == NULL and f(dg=None) == NULL
+    assert f(db=P[12] + 4 * MiB + 8) == ALIGN and f(co=P[13] + 2) == ALIGN
+    assert f(dH=P[12] + 4 * MiB) == ALIAS and f(dF=P[13]) == ALIAS and f(wk=P[13]) == ALIAS
+    assert f(dw=P[12] + 4 * MiB + 64) == ALIAS
+
+
+def test_weights_backward_terms_validation(L):
+    need = L.hc_weights_backward_workspace(64, 4, 4096, 0)
+    f = lambda **k: L.hc_weights_backward_terms(  # noqa: E731
+        k.get("H", P[0]), k.get("W", P[1]), k.get("ws", P[2]), k.get("scale", 0.01),
+        k.get("eps", 1e-6), k.get("it", 0), k.get("g", P[3]), k.get("g2", None), k.get("sv", None),
+        k.get("db", P[4]), k.get("co", P[8]), k.get("dW", P[5]), k.get("dws", P[6]),
+        k.get("wk", P[7]), k.get("wkb", need), k.get("T", 64), k.get("n", 4), k.get("d", 4096),
+        k.get("dt", BF16), None)
+    assert f(T=0) == OK and f(T=0, db=None, co=None) == OK
+    assert f(dt=FP8) == DTYPE and f(n=0) == SHAPE and f(d=100) == SHAPE
+    assert f(eps=0.0) == ARG and f(it=-1) == ARG and f(wkb=need - 1) == ARG
+    assert f(db=None) == NULL and f(co=None) == NULL and f(dW=None) == NULL
+    assert f(db=P[4] + 8) == ALIGN and f(co=P[8] + 2) == ALIGN
+    # dhbar over an input, coef over dhbar, coef over the workspace or an output
+    assert f(db=P[0]) == ALIAS and f(co=P[4] + 64) == ALIAS and f(co=P[7]) == ALIAS
+    assert f(co=P[5]) == ALIAS and f(co=P[3]) == ALIAS and f(dW=P[4] + 64) == ALIAS
 
 
 def test_weights_save_validation(L):

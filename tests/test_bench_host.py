@@ -60,7 +60,10 @@ def test_kernel_match_tells_the_kernels_apart():
     names = {
         "pre_mix_backward": ns + "pre_bwd_kernel<4, hc::bf16_t, 1, true, true, true>" + tail,
         "pre_mix_records": ns + "pre_bwd_kernel<4, hc::bf16_t, 1, true, false, false>" + tail,
-        "post_pre_mix_backward": ns + "post_pre_bwd_kernel<4, hc::bf16_t, 1, false>" + tail,
+        "post_pre_mix_backward": ns + "post_pre_bwd_kernel<4, hc::bf16_t, 1, true, false>" + tail,
+        "post_pre_mix_backward_terms": ns + "post_pre_bwd_kernel<4, hc::bf16_t, 1, true, true>" + tail,
+        "weights_backward_stream": ns + "wgrad_mfma_kernel<4, true, false>" + tail,
+        "weights_backward_terms_stream": ns + "wgrad_mfma_kernel<4, false, true>" + tail,
         "post_mix_backward": ns + "post_bwd_kernel<4, hc::bf16_t, 1, false, false>" + tail,
         "pre_mix": ns + "pre_mix_kernel<4, hc::bf16_t, 1>" + tail,
         "post_pre_mix": ns + "post_pre_mix_kernel<4, hc::bf16_t, 1>" + tail,
