@@ -771,12 +771,16 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(
                     if (ok && col_ok) st16_stream(dH + r0 + i * row_bytes, make_uint4(ow[0], ow[1], ow[2], ow[3]));
             }
             if constexpr (TERMS) {
+                // the lane's 32 bytes go out as two 16-byte halves, each
+                // store instruction covering every other 16 bytes of the
+                // row's 512; as ordinary (cached) stores the halves meet in
+                // L2 and each line is written to HBM whole
                 if (ok && col_ok) {
                     float* o = dhbar + t * d + (int64_t)cv * 8;
-                    st16_stream(o, make_uint4(__float_as_uint(dhb[0][j]), __float_as_uint(dhb[1][j]),
-                                              __float_as_uint(dhb[2][j]), __float_as_uint(dhb[3][j])));
-                    st16_stream(o + 4, make_uint4(__float_as_uint(dhb[4][j]), __float_as_uint(dhb[5][j]),
-                                                  __float_as_uint(dhb[6][j]), __float_as_uint(dhb[7][j])));
+                    st16(o, make_uint4(__float_as_uint(dhb[0][j]), __float_as_uint(dhb[1][j]),
+                                       __float_as_uint(dhb[2][j]), __float_as_uint(dhb[3][j])));
+                    st16(o + 4, make_uint4(__float_as_uint(dhb[4][j]), __float_as_uint(dhb[5][j]),
+                                           __float_as_uint(dhb[6][j]), __float_as_uint(dhb[7][j])));
                 }
             }
 #pragma unroll
