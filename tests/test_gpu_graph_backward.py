@@ -89,14 +89,16 @@ def test_backward_graph_replays_equal_eager(records, fold):
         _ = (H.float() * 2).sum().item()   # eager work between replays
 
 
-@pytest.mark.parametrize("records", ["shared", "per-token"])
+@pytest.mark.parametrize("records", ["shared", "per-token", "per-token-terms"])
 def test_boundary_backward_graph_replays_equal_eager(records):
     """One layer boundary's gradient in one pass, captured and replayed: with
     shared records the boundary call alone; with per-token records produced
     from the streams the whole schedule (the read-mix's dalpha alone, the
-    weight producer's gradient onto the arriving gradient, the boundary
+    weight producer's gradient onto the arriving gradient, or as its factors
+    (dhbar, coefficients) that the boundary call adds, then the boundary
     call).  Outputs and workspaces are overwritten before every replay."""
-    rng = np.random.default_rng(7 if records == "shared" else 8)
+    rng = np.random.default_rng({"shared": 7, "per-token": 8, "per-token-terms": 9}[records])
+    terms = records == "per-token-terms"
     T, n, d = 300, 4, 1024
     K = 2 * n + n * n
     H, F, H2 = bf16(rng, (T, n, d)), bf16(rng, (T, d)), bf16(rng, (T, n, d))
@@ -104,7 +106,7 @@ def test_boundary_backward_graph_replays_equal_eager(records):
     gamma = dev((1 + 0.1 * rng.standard_normal(d)).astype(np.float32))
     ws = dev((identity_record(n) + 0.05 * rng.standard_normal(K)).astype(np.float32))
     W = bf16(rng, (K, d), 0.02)
-    per_token = records == "per-token"
+    per_token = records != "shared"
     if per_token:
         w, _ = hc.weights_save(H, W, ws, 0.01, 1e-6, 0)
         w2, saved2 = hc.weights_save(H2, W, ws, 0.01, 1e-6, 0)
@@ -125,18 +127,27 @@ def test_boundary_backward_graph_replays_equal_eager(records):
     wk2 = torch.empty_like(wk)
     wwk = torch.empty(int(hc.lib().hc_weights_backward_workspace(T, n, d, 0)), dtype=torch.uint8,
                       device="cuda")
-    outs = [dH, dF, dwp, dwn, dg] + ([dalpha, Gw, dW, dws] if per_token else [])
+    dhb = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    coef = torch.empty((T, 2 * n), dtype=torch.float32, device="cuda")
+    outs = [dH, dF, dwp, dwn, dg] + ([dalpha, dW, dws] if per_token else [])
+    outs += [dhb, coef] if terms else ([Gw] if per_token else [])
 
     def step():
         arriving = G
         if per_token:
             hc.pre_mix_backward(du, H2, w2, gamma, 1e-6, h_grad=False, g_grad=False, dw=dalpha,
                                 workspace=wk2)
+        if terms:
+            hc.weights_backward_terms(H2, W, ws, 0.01, dalpha, 1e-6, 0, dhbar=dhb, coef=coef,
+                                      dW=dW, dw_static=dws, workspace=wwk, dw2=post_part,
+                                      saved=saved2)
+        elif per_token:
             hc.weights_backward(H2, W, ws, 0.01, dalpha, 1e-6, 0, dH_in=G, out=Gw, dW=dW,
                                 dw_static=dws, workspace=wwk, dw2=post_part, saved=saved2)
             arriving = Gw
         hc.post_pre_mix_backward(arriving, du, H, F, w, w2, gamma, 1e-6, out=dH, dF=dF, dw=dwp,
-                                 dw_next=dwn, dgamma_next=dg, workspace=wk)
+                                 dw_next=dwn, dgamma_next=dg, workspace=wk,
+                                 terms=(dhb, coef) if terms else None)
 
     step()
     torch.cuda.synchronize()

@@ -1,8 +1,9 @@
 """The binding on a side stream: every wrapper allocates its outputs and
 workspaces on the stream its kernels run on, so that torch's caching
 allocator cannot hand that memory to other work while the kernels still run.
-Each gradient (post, pre, the weight producer, the layer boundary's) and the
-fused write-backs are run on a side stream, with other work queued on the current stream that
+Each gradient (post, pre, the weight producer, also as its factors, the
+layer boundary's, also adding them) and the fused write-backs are run on a
+side stream, with other work queued on the current stream that
 reuses freed memory meanwhile, and compared bitwise with the same call on
 the current stream."""
 import numpy as np
@@ -44,9 +45,11 @@ def churn():
 
 
 @pytest.mark.parametrize("which", ["post", "pre", "weights", "post_weights", "boundary",
-                                   "boundary_per_token", "post_weights_pre"])
+                                   "boundary_per_token", "post_weights_pre", "weights_terms",
+                                   "boundary_terms"])
 def test_side_stream_equals_current_stream(which):
     H, F, G, du, w, wt, g, W, ws, dw = inputs()
+    terms = hc.weights_backward_terms(H, W, ws, 0.01, dw)[:2] if which == "boundary_terms" else None
 
     def run(stream):
         if which == "post":
@@ -61,6 +64,13 @@ def test_side_stream_equals_current_stream(which):
             return hc.post_pre_mix_backward(G, du, H, F, wt, wt, g, 1e-6, stream=stream)
         if which == "post_weights_pre":
             return hc.post_weights_pre_mix(H, F, wt, W, ws, 0.01, g, stream=stream)
+        if which == "weights_terms":
+            return hc.weights_backward_terms(H, W, ws, 0.01, dw, 1e-6, 0, stream=stream)
+        if which == "boundary_terms":
+            # the factors come from the current stream's call; the side stream
+            # waits for them before it starts (below)
+            return hc.post_pre_mix_backward(G, du, H, F, wt, wt, g, 1e-6, stream=stream,
+                                            terms=terms)
         return hc.post_mix_weights(H, F, wt, W, ws, 0.01, 1e-6, 0, stream=stream)
 
     ref = [host(x) for x in run(None)]
