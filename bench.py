@@ -930,6 +930,15 @@ def run_workload(args, name: str):
         "cpu_baseline": None,
     }
 
+    if basis == "method" and len(hc_kernels) == 1 and launches[dom] == 1 and step_bytes != kernel_bytes:
+        # one kernel does the whole layer (a fused layer boundary at steady
+        # state): the rate at which it does the method's work, on the bytes
+        # the method's own passes would move for the same tokens
+        method_gbps = step_bytes / (kms[dom] * 1e-3) / 1e9
+        out["roofline"]["method_bytes_per_launch"] = int(step_bytes)
+        out["roofline"]["method_achieved"] = round(method_gbps, 1)
+        out["roofline"]["method_frac"] = round(method_gbps / HBM_PEAK_GBPS, 4)
+
     return out, wl, inp
 
 
