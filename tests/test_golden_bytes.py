@@ -44,3 +44,24 @@ def test_backward_bytes_count_each_row_moved():
     unfolded = traffic.post_bwd_bytes(n, d, s) + traffic.pre_bwd_bytes(n, d, s, True)
     folded = traffic.post_bwd_bytes(n, d, s, h_grad=False) + traffic.pre_bwd_bytes(n, d, s, True)
     assert unfolded - folded == n * d * s
+
+
+def test_weight_producer_factors_bytes():
+    """The dynamic layer's backward per token at n = 4, d = 4096, bf16, one
+    pass per boundary.  With the producer's gradient added in place: dalpha
+    alone (H and du, n + 1 rows), the producer (H, dH in, dH out: 3n rows)
+    and the boundary (3n + 3 rows): 32 rows.  As its factors: the producer
+    reads H (n rows) and writes dhbar (d fp32, two bf16 rows) and 2n
+    coefficients; the boundary reads them too: 28 rows, 12.4% fewer bytes."""
+    n, d, s = 4, 4096, 2
+    rec = traffic.record_bytes(n)
+    coef = 4 * 2 * n
+    assert traffic.weights_bwd_terms_bytes(n, d, s) == n * d * s + 4 * d + coef + 2 * rec == 49376
+    assert (traffic.post_pre_bwd_terms_bytes(n, d, s)
+            == traffic.post_pre_bwd_bytes(n, d, s, True) + 4 * d + coef == 139680)
+    alone = traffic.pre_records_bytes(n, d, s)
+    in_place = alone + traffic.weights_bwd_bytes(n, d, s) + traffic.post_pre_bwd_bytes(n, d, s, True)
+    factors = (alone + traffic.weights_bwd_terms_bytes(n, d, s)
+               + traffic.post_pre_bwd_terms_bytes(n, d, s))
+    assert in_place == 262816 and factors == 230112
+    assert in_place - factors == 4 * d * s - 2 * coef
